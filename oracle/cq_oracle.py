@@ -1,0 +1,381 @@
+"""CPU oracle for the Cactus-Quants (CQ) rotated-codebook quantizer.
+
+TEST INFRASTRUCTURE ONLY.  This module is the plain, slow reference the HIP
+library is checked against.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import it; the product path
+(``rotated_codebook_bit_amd``) never does, and this module imports nothing from
+the product path.  It shares no code, table or constant generator with the
+HIP library.
+
+Everything is computed in float64 NumPy, step by step in the order the pages
+describe, with dense matrices where the pages use dense matrices.  Sources
+(page title, then section):
+
+* "Cactus Quants CQ2-bit Quantization: Extreme Compression for Edge LLMs"
+  (called *CQ2 overview* below): §Group-wise Weight Partitioning,
+  §Hadamard Rotation, §Optimized Codebook Design,
+  §The CQ2-bit Implementation Pipeline.
+* "How CQ2-bit Quantization Contributes to Needle 2's Small Footprint"
+  (*Footprint*): §Hadamard Rotation, §Static Codebook Quantization,
+  §Per-Group Storage Breakdown, §Binary Serialization.
+* "Performance Differences Between 2-Bit and 4-Bit Quantization in Needle"
+  (*2-bit vs 4-bit*): §Quantization Error and Accuracy Impact,
+  §Practical Code Comparison.
+* "How Quantization Codebooks Are Trained in Cactus Quants: Lloyd-Max on
+  Gaussian Data" (*Codebook training*): §Gaussian Sampling and
+  Initialization, §Iterative Refinement of Quantization Levels,
+  §Ternary Special Case Handling, §Production Codebook Generation and Caching.
+
+Readings where the pages are silent or ambiguous are listed in the design doc;
+the ones that shape this file are repeated next to the code they affect.
+
+Parity pins: every public function here is pinned by ``tests/test_oracle_*.py``
+against closed forms, textbook values, brute force or hand-worked examples.
+No function is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# Ternary case: the pages give the 3-level codebook explicitly instead of
+# training it (*Codebook training*, §Ternary Special Case Handling).
+TERNARY = 158  # bit-width code for the "1.58-bit" three-level codebook
+TERNARY_LEVELS = (-1.2240064, 0.0, 1.2240064)
+
+GROUP = 128  # default group size (*CQ2 overview*, §Group-wise Weight Partitioning)
+LLOYD_SAMPLES = 400_000  # (*Codebook training*, §Gaussian Sampling and Initialization)
+LLOYD_ITERS = 200  # (*Codebook training*, §Iterative Refinement of Quantization Levels)
+
+
+# ---------------------------------------------------------------------------
+# Codebook
+# ---------------------------------------------------------------------------
+
+def n_levels(bits: int) -> int:
+    """Number of codebook levels: 3 for the ternary code, else 2**bits."""
+    if bits == TERNARY:
+        return 3
+    if bits not in (1, 2, 3, 4):
+        raise ValueError(f"unsupported bit-width {bits}")
+    return 1 << bits
+
+
+def storage_bits(bits: int) -> int:
+    """Bits stored per index.  The three ternary codes use a 2-bit field
+    (reading: the pages describe no trit packing)."""
+    return 2 if bits == TERNARY else n_levels(bits).bit_length() - 1
+
+
+def lloyd_max(samples: np.ndarray, levels: int, iters: int = LLOYD_ITERS) -> np.ndarray:
+    """1-D Lloyd-Max (k-means) on a sample set, as *Codebook training*
+    §Gaussian Sampling and Initialization and §Iterative Refinement of
+    Quantization Levels describe it.
+
+    * The samples are sorted; the initial level k is the sample at the
+      quantile position floor((k + 1/2) * n / L) of the sorted array.
+    * Each iteration puts the decision boundaries at the midpoints of
+      neighbouring levels, gives every sample to the cell whose lower
+      boundary it strictly exceeds (a sample equal to a boundary stays in the
+      lower cell), and moves every level to the mean of its cell.
+    * A cell left empty keeps its previous level (reading: the pages do not
+      say; it never happens for L <= 16 with this initialisation).
+    * The levels are returned sorted ascending.
+    """
+    x = np.sort(np.asarray(samples, dtype=np.float64).ravel())
+    n = x.size
+    if n < levels:
+        raise ValueError("need at least as many samples as levels")
+    pos = ((2 * np.arange(levels, dtype=np.int64) + 1) * n) // (2 * levels)
+    c = x[pos].copy()
+    for _ in range(iters):
+        edges = 0.5 * (c[:-1] + c[1:])
+        # Cell k holds the sorted samples in [start[k], start[k+1]).  A sample
+        # belongs to cell #{edges < sample}, so cell k starts after the last
+        # sample that is <= edges[k-1].
+        start = np.concatenate(([0], np.searchsorted(x, edges, side="right"), [n]))
+        for k in range(levels):
+            lo, hi = start[k], start[k + 1]
+            if hi > lo:
+                c[k] = x[lo:hi].mean()
+    return np.sort(c)
+
+
+def codebook(bits: int, samples: np.ndarray | None = None,
+             iters: int = LLOYD_ITERS) -> np.ndarray:
+    """Codebook levels in N(0,1) units (float64), before any group scaling.
+
+    Ternary returns the fixed three levels; every other width runs
+    :func:`lloyd_max` on ``samples`` (the caller draws them: the pages use
+    400,000 standard-normal draws from a seeded generator).
+    """
+    if bits == TERNARY:
+        return np.array(TERNARY_LEVELS, dtype=np.float64)
+    if samples is None:
+        raise ValueError("Lloyd-Max codebooks need the Gaussian samples")
+    return lloyd_max(samples, n_levels(bits), iters)
+
+
+def runtime_levels(levels: np.ndarray) -> np.ndarray:
+    """The levels as the quantizer uses them at run time: rounded to float32
+    (the pages turn the NumPy table into a device array, *Footprint*
+    §Hadamard Rotation), returned as exact float64 copies of those floats."""
+    return np.asarray(levels, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def thresholds(levels32: np.ndarray) -> np.ndarray:
+    """Decision thresholds: midpoints of neighbouring levels (*Codebook
+    training* §Iterative Refinement).  Exact in float64 for float32 levels."""
+    c = np.asarray(levels32, dtype=np.float64)
+    return 0.5 * (c[:-1] + c[1:])
+
+
+# ---------------------------------------------------------------------------
+# Hadamard rotation
+# ---------------------------------------------------------------------------
+
+def sylvester(g: int) -> np.ndarray:
+    """The +-1 Sylvester-Hadamard matrix of order g (a power of two), built by
+    repeated Kronecker doubling [[H, H], [H, -H]]."""
+    if g < 1 or g & (g - 1):
+        raise ValueError("group size must be a power of two")
+    h = np.ones((1, 1), dtype=np.float64)
+    while h.shape[0] < g:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def hadamard(g: int) -> np.ndarray:
+    """Orthonormal Walsh-Hadamard matrix H/sqrt(g) (*CQ2 overview* §Hadamard
+    Rotation; *Footprint* §Hadamard Rotation).  Reading: Sylvester natural
+    order.  It is symmetric and its own inverse."""
+    return sylvester(g) / math.sqrt(g)
+
+
+# ---------------------------------------------------------------------------
+# Quantize / dequantize
+# ---------------------------------------------------------------------------
+
+def to_groups(w: np.ndarray, g: int = GROUP) -> tuple[np.ndarray, int, int]:
+    """Zero-pad the last axis to a multiple of g and cut it into groups
+    (*CQ2 overview* §The CQ2-bit Implementation Pipeline, step 1).
+
+    Returns (X, R, D): X has shape (R * ceil(D/g), g) in row-major group
+    order, R is the product of the leading dimensions, D the last dimension.
+    """
+    w = np.asarray(w, dtype=np.float64)
+    if w.ndim == 0:
+        raise ValueError("need at least one dimension")
+    d = w.shape[-1]
+    r = int(np.prod(w.shape[:-1], dtype=np.int64)) if w.ndim > 1 else 1
+    w2 = w.reshape(r, d)
+    ng = -(-d // g)
+    padded = np.zeros((r, ng * g), dtype=np.float64)
+    padded[:, :d] = w2
+    return padded.reshape(r * ng, g), r, d
+
+
+class Quantized:
+    """Result of :func:`quantize` (all arrays in row-major group order).
+
+    idx    int64  [R, ng, g]   codebook index per element
+    z      f64    [R, ng, g]   normalised rotated value the index was chosen from
+    norm   f64    [R, ng]      unrounded group L2 norm
+    norm16 uint16 [R, ng]      IEEE binary16 bits of the stored norm
+    """
+
+    def __init__(self, idx, z, norm, norm16, rows, cols, bits, g, levels32):
+        self.idx, self.z, self.norm, self.norm16 = idx, z, norm, norm16
+        self.rows, self.cols, self.bits, self.g = rows, cols, bits, g
+        self.levels32 = levels32
+
+    @property
+    def packed(self) -> np.ndarray:
+        return pack(self.idx, storage_bits(self.bits))
+
+
+def fp16_bits(x: np.ndarray) -> np.ndarray:
+    """IEEE binary16 bit pattern of float64 values, round-to-nearest-even,
+    converted directly from float64 (NumPy's double->half conversion)."""
+    with np.errstate(over="ignore"):  # norms above 65504 store +Inf
+        return np.asarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def quantize(w: np.ndarray, bits: int, levels: np.ndarray, g: int = GROUP) -> Quantized:
+    """CQ quantize, following *CQ2 overview* §The CQ2-bit Implementation
+    Pipeline (steps 1-4) and *Footprint* §Per-Group Storage Breakdown.
+
+    1. pad the last axis with zeros to a multiple of g, cut into groups;
+    2. rotate every group by the orthonormal Hadamard matrix (dense product);
+    3. take the group's L2 norm n and normalise: z = sqrt(g) * y / n
+       (equivalently unit-norm components against levels / sqrt(g),
+       *Codebook training* §Production Codebook Generation and Caching);
+       a zero group gives z = 0 (reading: the pages do not say);
+    4. index = number of thresholds strictly below z (nearest level; an exact
+       tie goes to the lower level);
+    5. store the index and the norm rounded to binary16.
+
+    ``levels`` are in N(0,1) units; they are rounded to float32 first
+    (:func:`runtime_levels`).
+    """
+    levels32 = runtime_levels(levels)
+    if levels32.size != n_levels(bits):
+        raise ValueError("codebook size does not match the bit-width")
+    t = thresholds(levels32)
+    x, r, d = to_groups(w, g)
+    y = x @ hadamard(g)
+    n = np.sqrt(np.sum(y * y, axis=1))
+    z = np.zeros_like(y)
+    nz = n > 0
+    z[nz] = math.sqrt(g) * y[nz] / n[nz, None]
+    idx = np.searchsorted(t, z, side="left").astype(np.int64)
+    ng = x.shape[0] // r if r else 0
+    shape3 = (r, ng, g)
+    return Quantized(idx.reshape(shape3), z.reshape(shape3), n.reshape(r, ng),
+                     fp16_bits(n).reshape(r, ng), r, d, bits, g, levels32)
+
+
+def dequantize_groups(idx: np.ndarray, norm16: np.ndarray, levels: np.ndarray,
+                      g: int = GROUP) -> np.ndarray:
+    """Reconstructed groups (float64, shape [..., g]) from indices and stored
+    binary16 norms: look up the float32 levels, scale by norm/sqrt(g), rotate
+    back by the Hadamard matrix (*CQ2 overview* §The CQ2-bit Implementation
+    Pipeline, steps 4-5)."""
+    levels32 = runtime_levels(levels)
+    idx = np.asarray(idx, dtype=np.int64)
+    n = np.asarray(norm16, dtype=np.uint16).view(np.float16).astype(np.float64)
+    q = levels32[idx] * (n[..., None] / math.sqrt(g))
+    return q @ hadamard(g)
+
+
+def dequantize(packed: np.ndarray, norm16: np.ndarray, rows: int, cols: int,
+               bits: int, levels: np.ndarray, g: int = GROUP) -> np.ndarray:
+    """Dequantize packed storage to a float64 [rows, cols] matrix; the pad
+    columns are dropped (*CQ2 overview* §The CQ2-bit Implementation Pipeline,
+    step 6)."""
+    ng = -(-cols // g)
+    idx = unpack(packed, storage_bits(bits), g).reshape(rows, ng, g)
+    xh = dequantize_groups(idx, np.asarray(norm16).reshape(rows, ng), levels, g)
+    return xh.reshape(rows, ng * g)[:, :cols]
+
+
+# ---------------------------------------------------------------------------
+# Packing
+# ---------------------------------------------------------------------------
+
+def pack(idx: np.ndarray, sbits: int) -> np.ndarray:
+    """Pack indices into bytes: within each group, index j occupies bits
+    [sbits*j, sbits*j + sbits) of a little-endian bit stream (least
+    significant bit first).  Reading of *Footprint* §Binary Serialization,
+    which says only that consecutive weights are packed into bytes.
+
+    idx has shape [..., g]; the result has shape [..., g * sbits / 8]."""
+    idx = np.asarray(idx, dtype=np.int64)
+    g = idx.shape[-1]
+    if (g * sbits) % 8:
+        raise ValueError("group does not fill whole bytes")
+    bits = (idx[..., :, None] >> np.arange(sbits)) & 1  # [..., g, sbits]
+    stream = bits.reshape(idx.shape[:-1] + (g * sbits,)).astype(np.uint8)
+    return np.packbits(stream, axis=-1, bitorder="little")
+
+
+def unpack(packed: np.ndarray, sbits: int, g: int = GROUP) -> np.ndarray:
+    """Inverse of :func:`pack`: bytes [..., g*sbits/8] -> indices [..., g]."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    nbytes = g * sbits // 8
+    flat = packed.reshape(-1, nbytes)
+    stream = np.unpackbits(flat, axis=-1, bitorder="little").astype(np.int64)
+    stream = stream.reshape(flat.shape[0], g, sbits)
+    idx = np.sum(stream << np.arange(sbits), axis=-1)
+    return idx.reshape(packed.shape[:-1] + (g,)) if packed.ndim > 1 else idx.reshape(g)
+
+
+# ---------------------------------------------------------------------------
+# Dequantize-matvec
+# ---------------------------------------------------------------------------
+
+def matvec(packed: np.ndarray, norm16: np.ndarray, n_out: int, k: int, bits: int,
+           levels: np.ndarray, x: np.ndarray, g: int = GROUP) -> np.ndarray:
+    """y = x . W_hat^T in float64, with W_hat the dequantized [n_out, k]
+    matrix (the forward product of *2-bit vs 4-bit* §Practical Code
+    Comparison applied to quantized weights).  x is [batch, k]."""
+    w_hat = dequantize(packed, norm16, n_out, k, bits, levels, g)
+    return np.asarray(x, dtype=np.float64) @ w_hat.T
+
+
+def matvec_rotated(packed: np.ndarray, norm16: np.ndarray, n_out: int, k: int,
+                   bits: int, levels: np.ndarray, x: np.ndarray,
+                   g: int = GROUP) -> np.ndarray:
+    """Second route to the same product, used to check :func:`matvec`:
+    because the orthonormal Hadamard matrix is symmetric and its own inverse,
+    x_g . W_hat_g = (norm/sqrt(g)) * <x_g H, levels[idx]> for every group.
+    Requires k to be a multiple of g."""
+    if k % g:
+        raise ValueError("k must be a multiple of the group size")
+    ng = k // g
+    levels32 = runtime_levels(levels)
+    idx = unpack(packed, storage_bits(bits), g).reshape(n_out, ng, g)
+    n = np.asarray(norm16, dtype=np.uint16).reshape(n_out, ng).view(np.float16)
+    q = levels32[idx] * (n.astype(np.float64)[..., None] / math.sqrt(g))
+    xr = np.asarray(x, dtype=np.float64).reshape(-1, ng, g) @ hadamard(g)
+    return np.einsum("bgj,rgj->br", xr, q)
+
+
+# ---------------------------------------------------------------------------
+# Size accounting and error reports
+# ---------------------------------------------------------------------------
+
+def model_bytes(shapes, bits: int, g: int = GROUP) -> int:
+    """Storage size of a set of tensors: per group, g*sbits/8 bytes of packed
+    indices plus one binary16 norm, nothing else (*Footprint* §Per-Group
+    Storage Breakdown).  A tensor of shape (..., D) has prod(leading) *
+    ceil(D/g) groups; padded groups count in full."""
+    sb = storage_bits(bits)
+    total = 0
+    for shape in shapes:
+        shape = tuple(int(s) for s in shape)
+        d = shape[-1]
+        r = int(np.prod(shape[:-1], dtype=np.int64)) if len(shape) > 1 else 1
+        groups = r * (-(-d // g))
+        total += groups * (g * sb // 8 + 2)
+    return total
+
+
+def relative_mse(w: np.ndarray, w_hat: np.ndarray) -> float:
+    """||W - W_hat||_F^2 / ||W||_F^2 (the distortion measure of *2-bit vs
+    4-bit* §Quantization Error and Accuracy Impact, read as a mean-square
+    ratio)."""
+    w = np.asarray(w, dtype=np.float64)
+    e = w - np.asarray(w_hat, dtype=np.float64)
+    return float(np.sum(e * e) / np.sum(w * w))
+
+
+def fake_quant(w: np.ndarray, bits: int, levels: np.ndarray, g: int = GROUP,
+               rotate: bool = True) -> np.ndarray:
+    """Quantize then reconstruct with the unrounded norm, as the pages'
+    quantizer returns its result (*CQ2 overview* §The CQ2-bit Implementation
+    Pipeline).  ``rotate=False`` replaces the Hadamard matrix by the identity
+    (the no-rotation ablation used to show the rotation's effect)."""
+    levels32 = runtime_levels(levels)
+    t = thresholds(levels32)
+    x, r, d = to_groups(w, g)
+    h = hadamard(g) if rotate else np.eye(g)
+    y = x @ h
+    n = np.sqrt(np.sum(y * y, axis=1))
+    z = np.zeros_like(y)
+    nz = n > 0
+    z[nz] = math.sqrt(g) * y[nz] / n[nz, None]
+    idx = np.searchsorted(t, z, side="left")
+    xh = (levels32[idx] * (n[:, None] / math.sqrt(g))) @ h.T
+    ng = x.shape[0] // r
+    return xh.reshape(r, ng * g)[:, :d].reshape(np.shape(w))
+
+
+def threshold_distance(z: np.ndarray, levels: np.ndarray) -> np.ndarray:
+    """Distance (z units) from each normalised value to its nearest decision
+    threshold; used to decide which index differences are admissible."""
+    t = thresholds(runtime_levels(levels))
+    z = np.asarray(z, dtype=np.float64)
+    return np.min(np.abs(z[..., None] - t), axis=-1)
