@@ -1,0 +1,267 @@
+"""Benchmark of the CQ hot path on one MI355X.
+
+One step is one pass of the whole path over the 7B-shaped model (bf16,
+6,607,077,376 parameters in one flat device buffer, 2-bit codebook, G=128):
+
+  1. quantize the whole model in one launch (bf16 -> packed 2-bit + fp16 norms);
+  2. dequantize the whole model in one launch (-> float32);
+  3. dequant-matvec at batch 1 through every packed matrix (225 calls, each
+     rotating its activation and dotting it with the looked-up levels).
+
+Prints one JSON line.  `value` is model parameters per second over the whole
+step (wall clock, inputs resident in HBM).  Per-kernel times come from HIP
+events recorded on the stream the kernels run on.  The CPU oracle is timed on
+a bounded sample (one 4096x4096 tensor through the same three steps).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+       python bench.py --copy-only   (plain device copy, for counter scaling)
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CQ2 quantize+dequantize Gparams/s and % of HBM peak GB/s (1×MI355X)"
+HBM_PEAK_GBS = 8000.0
+BITS = 2
+G = 128
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama7b.json")
+KERNEL_SOURCES = ["rotated_codebook_bit_amd/csrc/quantize.hip",
+                  "rotated_codebook_bit_amd/csrc/dequantize.hip",
+                  "rotated_codebook_bit_amd/csrc/matvec.hip"]
+
+
+def sources_digest() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-only", action="store_true", help="only run a plain 4 GiB device copy")
+    return ap.parse_args()
+
+
+def copy_only(torch):
+    n = 1 << 30  # 4 GiB of float32
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    print(json.dumps({"copy_bytes_each_way": 4 * n, "ms": ms,
+                      "GBps_read_plus_write": 2 * 4 * n / ms / 1e6}), flush=True)
+
+
+def cpu_baseline() -> dict:
+    """The oracle as it stands, on one 4096x4096 tensor: quantize, dequantize,
+    matvec at batch 1 (the per-tensor work of one step)."""
+    from oracle import cq_oracle as O
+    from rotated_codebook_bit_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        blas_threads = os.cpu_count() or 1
+    import rotated_codebook_bit_amd as cq
+    levels = cq.codebook(BITS)
+    rng = np.random.default_rng(0)
+    w = W.bf16_round((rng.standard_normal((4096, 4096)) * 0.02).astype(np.float32)).astype(np.float64)
+    x = rng.standard_normal((1, 4096))
+    t0 = time.perf_counter()
+    q = O.quantize(w, BITS, levels)
+    w_hat = O.dequantize(q.packed, q.norm16, 4096, 4096, BITS, levels)
+    _ = x @ w_hat.T
+    dt = time.perf_counter() - t0
+    params = w.size
+    return {"value": round(params / dt / 1e9, 6), "unit": "Gparams/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"one 4096x4096 bf16-valued tensor (16.8M params) through quantize, "
+                      f"dequantize and a batch-1 matvec, float64 NumPy, {dt:.1f} s; "
+                      f"host cpu_count={os.cpu_count()}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus "
+              f"{args.gpus}).  Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_only:
+        copy_only(torch)
+        return
+
+    import rotated_codebook_bit_amd as cq
+    from rotated_codebook_bit_amd import workloads as W
+
+    levels = cq.codebook(BITS)
+    shapes = W.llama7b_shapes()
+    log("generating the 7B-shaped bf16 model on the device")
+    buf, offsets = W.llama7b_device("cuda")
+    params = buf.numel()
+    n_groups = params // G
+    w2 = buf.view(n_groups, G)
+    packed = torch.empty((n_groups, G * BITS // 8), dtype=torch.uint8, device="cuda")
+    norms = torch.empty((n_groups,), dtype=torch.float16, device="cuda")
+    out = torch.empty((n_groups, G), dtype=torch.float32, device="cuda")
+    kmax = max(c for _, c in shapes)
+    nmax = max(r for r, _ in shapes)
+    xg = torch.Generator(device="cuda")
+    xg.manual_seed(1)
+    x = torch.randn((1, kmax), generator=xg, device="cuda", dtype=torch.float32)
+    y = torch.empty((1, nmax), dtype=torch.float32, device="cuda")
+    # Per-tensor views of the packed model (groups never straddle tensors:
+    # every column count is a multiple of 128).
+    views = []
+    for i, (r, c) in enumerate(shapes):
+        g0, g1 = int(offsets[i]) // G, int(offsets[i + 1]) // G
+        views.append((packed[g0:g1], norms[g0:g1], r, c))
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        cq.quantize(w2, BITS, levels, packed=packed.view(n_groups, 1, -1),
+                    norms=norms.view(n_groups, 1))
+        if ev:
+            ev[1].record(stream)
+        cq.dequantize(packed, norms, n_groups, G, BITS, levels, out=out)
+        if ev:
+            ev[2].record(stream)
+        for p, nv, r, c in views:
+            cq.dequant_matvec(p, nv, r, c, BITS, levels, x[:, :c].contiguous() if c != kmax else x,
+                              y=y[:, :r])
+        if ev:
+            ev[3].record(stream)
+
+    # x[:, :c] for c < kmax: make the activations contiguous once.
+    xs = {c: x[:, :c].contiguous() for _, c in shapes}
+
+    def step2(ev=None):
+        if ev:
+            ev[0].record(stream)
+        cq.quantize(w2, BITS, levels, packed=packed.view(n_groups, 1, -1),
+                    norms=norms.view(n_groups, 1))
+        if ev:
+            ev[1].record(stream)
+        cq.dequantize(packed, norms, n_groups, G, BITS, levels, out=out)
+        if ev:
+            ev[2].record(stream)
+        for p, nv, r, c in views:
+            cq.dequant_matvec(p, nv, r, c, BITS, levels, xs[c], y=y[:, :r])
+        if ev:
+            ev[3].record(stream)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step2()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step2(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+    tq = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    tdq = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    tmv = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+
+    sb = BITS
+    q_bytes = params * 2 + n_groups * (G * sb // 8) + n_groups * 2
+    dq_bytes = n_groups * (G * sb // 8) + n_groups * 2 + params * 4
+    mv_bytes = n_groups * (G * sb // 8 + 2) + sum(c * 4 + r * 4 for r, c in shapes)
+
+    def gbs(b, ms):
+        return b / (ms * 1e-3) / 1e9
+
+    phases = {
+        "quantize": {"ms": round(tq, 4), "Gparams_per_s": round(params / tq / 1e6, 1),
+                     "GB_per_s": round(gbs(q_bytes, tq), 1), "bytes": q_bytes,
+                     "frac_hbm_peak": round(gbs(q_bytes, tq) / HBM_PEAK_GBS, 4)},
+        "dequantize_f32": {"ms": round(tdq, 4), "Gparams_per_s": round(params / tdq / 1e6, 1),
+                           "GB_per_s": round(gbs(dq_bytes, tdq), 1), "bytes": dq_bytes,
+                           "frac_hbm_peak": round(gbs(dq_bytes, tdq) / HBM_PEAK_GBS, 4)},
+        "matvec_pass_b1": {"ms": round(tmv, 4), "calls": len(shapes),
+                           "GB_per_s": round(gbs(mv_bytes, tmv), 1), "bytes": mv_bytes},
+        "quantize_plus_dequantize_Gparams_per_s": round(params / (tq + tdq) / 1e6, 1),
+    }
+    dom = "dequantize_f32" if tdq >= tq else "quantize"
+    dom_kernel = {"dequantize_f32": "dequantize_contig<2, false>", "quantize": "quantize_contig<4, true>"}
+    ach = gbs(phases[dom]["bytes"], phases[dom]["ms"])
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            t = json.load(open(TRAFFIC_FILE))
+            if t.get("sources_digest") == sources_digest() and dom in t.get("kernels", {}):
+                traffic = t["kernels"][dom]["hbm_bytes_per_launch"]
+        except Exception:
+            traffic = None
+    roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": dom_kernel[dom], "bytes_per_launch": phases[dom]["bytes"]}
+    result = {
+        "metric": METRIC,
+        "value": round(params / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "Gparams/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "llama7b-shaped: 32x[4x(4096x4096), 2x(4096x11008), 11008x4096] + "
+                               "32000x4096, bf16 N(0,0.02^2), 6,607,077,376 params, bits=2, G=128",
+                   "step": "quantize (1 launch) + dequantize to f32 (1 launch) + batch-1 "
+                           "dequant-matvec through all 225 matrices",
+                   "parallelism": "single GPU"},
+        "phases": phases,
+        "roofline": roofline,
+        "sources_digest": sources_digest(),
+    }
+    del out, buf
+    torch.cuda.empty_cache()
+    if not args.no_cpu:
+        log("timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

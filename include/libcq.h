@@ -1,0 +1,166 @@
+/*
+ * libcq - Cactus-Quants (CQ) rotated-codebook weight quantizer for AMD
+ * MI355X (gfx950).  C ABI.
+ *
+ * The method (sources are web pages, cited by title and section):
+ *   - weights are cut into groups of G = 128 consecutive values along the
+ *     last axis, the last group of a row zero-padded
+ *     ("Cactus Quants CQ2-bit Quantization: Extreme Compression for Edge
+ *     LLMs", section Group-wise Weight Partitioning);
+ *   - each group is rotated by the orthonormal Walsh-Hadamard matrix
+ *     (same page, section Hadamard Rotation);
+ *   - the rotated values are normalised by the group's L2 norm and snapped to
+ *     the nearest level of a fixed Lloyd-Max codebook for N(0,1), whose levels
+ *     are used divided by sqrt(G)
+ *     ("How Quantization Codebooks Are Trained in Cactus Quants: Lloyd-Max on
+ *     Gaussian Data", sections Iterative Refinement of Quantization Levels and
+ *     Production Codebook Generation and Caching);
+ *   - storage is the packed indices plus one binary16 norm per group
+ *     ("How CQ2-bit Quantization Contributes to Needle 2's Small Footprint",
+ *     sections Per-Group Storage Breakdown and Binary Serialization);
+ *   - dequantization looks the levels up, rescales and rotates back
+ *     (first page, section The CQ2-bit Implementation Pipeline).
+ *
+ * Conventions shared by every call
+ *   - Pointers are DEVICE pointers unless the argument says "host".
+ *   - A tensor of any rank is passed as rows x cols: rows is the product of
+ *     the leading dimensions, cols the last (grouping) dimension.  Rows are
+ *     contiguous, row-major.
+ *   - bits is one of CQ_TERNARY, 2, 3, 4 (1 is accepted by the host-only
+ *     calls).  Storage bits per index (sbits): 2 for CQ_TERNARY, else bits.
+ *   - Packed layout: packed[rows][ceil(cols/G)][G*sbits/8] bytes; inside a
+ *     group, index j occupies bits [sbits*j, sbits*j + sbits) of a
+ *     little-endian bit stream (least significant bit first).  Groups are in
+ *     row-major order.
+ *   - Norm layout: norms[rows][ceil(cols/G)], IEEE binary16 bit patterns,
+ *     round to nearest even from the float32 norm; norms above 65504 store
+ *     +Inf.
+ *   - levels (host, nullable where stated): n_levels float32 codebook levels
+ *     in N(0,1) units (before the 1/sqrt(G) scaling), strictly ascending.
+ *     n_levels must be 3 for CQ_TERNARY and 2^bits otherwise.
+ *   - group_size must be 128 for device calls; host-only calls take any power
+ *     of two up to 4096.
+ *   - Device calls validate every argument first, then enqueue their kernels
+ *     on `stream` (a hipStream_t; NULL = the null stream) and return without
+ *     waiting.  On a validation error nothing is enqueued.  Asynchronous
+ *     faults surface at the caller's next synchronisation.  Buffers must stay
+ *     alive until the stream has passed the call.
+ *   - rows*cols == 0 (or n_out*k == 0) is a successful no-op.
+ *   - Alignment: w, out, packed, x, y must be 16-byte aligned; norms 2-byte.
+ *   - Inputs and outputs must not overlap.  Non-finite inputs give
+ *     unspecified but deterministic results.
+ *   - Return value: CQ_OK (0) or a negative cq_status.  cq_last_error()
+ *     returns a thread-local message for the last failing call.
+ *   - Ownership: the caller owns every buffer.  The library keeps no pointer
+ *     after a call returns.
+ */
+#ifndef LIBCQ_H
+#define LIBCQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CQ_OK = 0,
+  CQ_ERR_NULL = -1,        /* a required pointer is NULL */
+  CQ_ERR_ARG = -2,         /* bad bits, sizes, dtype, levels or overlap */
+  CQ_ERR_ALIGN = -3,       /* misaligned pointer */
+  CQ_ERR_UNSUPPORTED = -4, /* valid request this build does not implement */
+  CQ_ERR_HIP = -5          /* a HIP runtime call or kernel launch failed */
+} cq_status;
+
+typedef enum { CQ_F32 = 0, CQ_BF16 = 1 } cq_dtype;
+
+/* Bit-width code of the three-level ("1.58-bit") codebook
+ * ("How Quantization Codebooks Are Trained in Cactus Quants", section Ternary
+ * Special Case Handling). */
+#define CQ_TERNARY 158
+#define CQ_GROUP 128
+#define CQ_MAX_LEVELS 16
+
+/* Sizes of the quantized form of one rows x cols tensor.
+ * n_groups = rows * ceil(cols / group_size);
+ * packed_bytes = n_groups * group_size * sbits / 8.  Host only, pure.
+ * Either output pointer may be NULL. */
+int cq_layout(int64_t rows, int64_t cols, int bits, int group_size,
+              int64_t* n_groups, int64_t* packed_bytes);
+
+/* Storage size of a set of tensors: for every group, group_size*sbits/8 bytes
+ * of indices plus 2 bytes of binary16 norm, and nothing else
+ * ("How CQ2-bit Quantization Contributes to Needle 2's Small Footprint",
+ * section Per-Group Storage Breakdown).  rows/cols are host arrays of
+ * n_tensors entries.  Padded groups count in full.  Host only, pure. */
+int cq_model_bytes(int n_tensors, const int64_t* rows, const int64_t* cols,
+                   int bits, int group_size, uint64_t* bytes_out);
+
+/* Codebook levels in N(0,1) units, written as float32 to levels_out (host,
+ * room for CQ_MAX_LEVELS), count to *n_levels (host).
+ * CQ_TERNARY returns the fixed levels -1.2240064, 0, 1.2240064
+ * ("How Quantization Codebooks Are Trained in Cactus Quants", section Ternary
+ * Special Case Handling) and ignores samples.  Other widths run 1-D Lloyd-Max
+ * (k-means) with 2^bits levels on the n_samples host samples (double), as the
+ * same page describes in sections Gaussian Sampling and Initialization and
+ * Iterative Refinement of Quantization Levels: sort, quantile initialisation
+ * at sorted position floor((k + 1/2) n / L), then `iters` rounds of midpoint
+ * boundaries, assignment (a sample equal to a boundary goes to the lower
+ * cell) and cell means; an empty cell keeps its level; result sorted.  The
+ * pages draw 400,000 standard-normal samples and run 200 iterations.
+ * Host only; the samples array is not modified. */
+int cq_codebook(int bits, const double* samples, int64_t n_samples, int iters,
+                float* levels_out, int* n_levels);
+
+/* Quantize w (rows x cols, dtype w_dtype = CQ_F32 or CQ_BF16) into packed
+ * indices and binary16 norms (layouts above).  levels (host, required):
+ * n_levels float32 levels.  Each group's index j is the number of decision
+ * thresholds (midpoints of neighbouring levels) strictly below
+ * sqrt(G) * y_j / ||y|| (y the rotated group); an all-zero group uses 0 for
+ * that value.  The decision is taken in float32; values within about 1e-6
+ * of a threshold may land on either side. */
+int cq_quantize(const void* w, int w_dtype, int64_t rows, int64_t cols,
+                int bits, int group_size, const float* levels, int n_levels,
+                uint8_t* packed, uint16_t* norms, void* stream);
+
+/* Dequantize packed indices + binary16 norms to out (rows x cols, dtype
+ * out_dtype = CQ_F32 or CQ_BF16, pad columns not written):
+ * x_hat = (norm / G) * H * levels[idx] with H the +-1 Sylvester-Hadamard
+ * matrix, which equals (norm/sqrt(G)) * levels[idx] times the orthonormal
+ * Hadamard matrix.  Computed in float32 (bf16 output rounds to nearest
+ * even).  levels (host, required). */
+int cq_dequantize(const uint8_t* packed, const uint16_t* norms, int64_t rows,
+                  int64_t cols, int bits, int group_size, const float* levels,
+                  int n_levels, void* out, int out_dtype, void* stream);
+
+/* y = x . W_hat^T for the quantized n_out x k matrix W (packed + norms as
+ * produced by cq_quantize with rows = n_out, cols = k), x float32
+ * [batch][k], y float32 [batch][n_out].  k must be a multiple of G
+ * (CQ_ERR_UNSUPPORTED otherwise), batch >= 1.  The activations are rotated
+ * once per group and dotted with the looked-up levels: because the
+ * orthonormal Hadamard matrix is symmetric and its own inverse,
+ * x_g . W_hat_g = (norm / G) * <H x_g, levels[idx]> with H the +-1
+ * Sylvester-Hadamard matrix.  float32 accumulation.  The library takes
+ * batch*k*4 bytes of
+ * stream-ordered device memory (hipMallocAsync / hipFreeAsync on `stream`)
+ * for the rotated activations. */
+int cq_dequant_matvec(const uint8_t* packed, const uint16_t* norms, int64_t n_out,
+                      int64_t k, int bits, int group_size, const float* levels,
+                      int n_levels, const float* x, int64_t batch, float* y,
+                      void* stream);
+
+/* Static description of a status code. */
+const char* cq_status_str(int status);
+
+/* Thread-local detail message of the last failing call on this thread
+ * ("" if none). */
+const char* cq_last_error(void);
+
+/* Library version string. */
+const char* cq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBCQ_H */

@@ -1,0 +1,207 @@
+"""Python binding of libcq, the CQ rotated-codebook quantizer for MI355X.
+
+Thin ctypes marshalling over the C ABI declared in ``include/libcq.h``: the
+names match the C entry points without the ``cq_`` prefix.  Every step of the
+computation runs in libcq's HIP kernels; PyTorch only provides device memory
+and the current stream.  There is no fallback: if ``libcq.so`` is missing or
+a call fails, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "TERNARY", "GROUP", "CQError", "lib", "storage_bits", "n_levels", "layout",
+    "model_bytes", "codebook", "quantize", "dequantize", "dequant_matvec",
+]
+
+TERNARY = 158
+GROUP = 128
+F32, BF16 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcq.so")
+_lib = None
+
+
+class CQError(RuntimeError):
+    """A libcq call returned an error status."""
+
+    def __init__(self, func: str, status: int, detail: str):
+        super().__init__(f"{func}: {detail} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libcq.so (built in place by ``rotated_codebook_bit_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run `python -m rotated_codebook_bit_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        L.cq_layout.argtypes = [i64, i64, i32, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        L.cq_model_bytes.argtypes = [i32, ctypes.POINTER(i64), ctypes.POINTER(i64), i32, i32,
+                                     ctypes.POINTER(ctypes.c_uint64)]
+        L.cq_codebook.argtypes = [i32, ctypes.POINTER(ctypes.c_double), i64, i32,
+                                  ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
+        L.cq_quantize.argtypes = [vp, i32, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_float), i32,
+                                  vp, vp, vp]
+        L.cq_dequantize.argtypes = [vp, vp, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_float), i32,
+                                    vp, i32, vp]
+        L.cq_dequant_matvec.argtypes = [vp, vp, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_float),
+                                        i32, vp, i64, vp, vp]
+        for name in ("cq_layout", "cq_model_bytes", "cq_codebook", "cq_quantize", "cq_dequantize",
+                     "cq_dequant_matvec"):
+            getattr(L, name).restype = i32
+        L.cq_status_str.argtypes = [i32]
+        L.cq_status_str.restype = ctypes.c_char_p
+        L.cq_last_error.argtypes = []
+        L.cq_last_error.restype = ctypes.c_char_p
+        L.cq_version.argtypes = []
+        L.cq_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(func: str, status: int) -> None:
+    if status != 0:
+        L = lib()
+        detail = L.cq_last_error().decode() or L.cq_status_str(status).decode()
+        raise CQError(func, status, detail)
+
+
+def storage_bits(bits: int) -> int:
+    return 2 if bits == TERNARY else int(bits)
+
+
+def n_levels(bits: int) -> int:
+    return 3 if bits == TERNARY else 1 << int(bits)
+
+
+def _levels_arg(levels) -> tuple[np.ndarray, ctypes.POINTER(ctypes.c_float)]:
+    arr = np.ascontiguousarray(np.asarray(levels, dtype=np.float32))
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+def _stream_ptr(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+# -- host-only calls ------------------------------------------------------------
+
+def layout(rows: int, cols: int, bits: int, group_size: int = GROUP) -> tuple[int, int]:
+    """(n_groups, packed_bytes) of a rows x cols tensor."""
+    ng, pb = ctypes.c_int64(), ctypes.c_int64()
+    _check("cq_layout", lib().cq_layout(rows, cols, bits, group_size, ctypes.byref(ng),
+                                        ctypes.byref(pb)))
+    return ng.value, pb.value
+
+
+def model_bytes(shapes, bits: int, group_size: int = GROUP) -> int:
+    """Storage bytes of a list of tensor shapes (last axis is the grouped one)."""
+    rows, cols = [], []
+    for shape in shapes:
+        shape = tuple(int(s) for s in shape)
+        cols.append(shape[-1])
+        rows.append(int(np.prod(shape[:-1], dtype=np.int64)) if len(shape) > 1 else 1)
+    n = len(rows)
+    r = (ctypes.c_int64 * max(n, 1))(*rows)
+    c = (ctypes.c_int64 * max(n, 1))(*cols)
+    out = ctypes.c_uint64()
+    _check("cq_model_bytes", lib().cq_model_bytes(n, r, c, bits, group_size, ctypes.byref(out)))
+    return out.value
+
+
+def codebook(bits: int, samples=None, iters: int = 200) -> np.ndarray:
+    """float32 codebook levels in N(0,1) units.  ``samples`` (float64) are the
+    Lloyd-Max training draws; None uses the standard 400,000 seed-0 draws."""
+    if samples is None and bits != TERNARY:
+        from .workloads import lloyd_samples
+        samples = lloyd_samples()
+    s = np.ascontiguousarray(np.zeros(0) if samples is None else samples, dtype=np.float64)
+    out = (ctypes.c_float * 16)()
+    n = ctypes.c_int()
+    _check("cq_codebook", lib().cq_codebook(bits, s.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                            s.size, iters, out, ctypes.byref(n)))
+    return np.array(out[:n.value], dtype=np.float32)
+
+
+# -- device calls ---------------------------------------------------------------
+
+def _rows_cols(shape) -> tuple[int, int]:
+    cols = int(shape[-1])
+    rows = int(np.prod(shape[:-1], dtype=np.int64)) if len(shape) > 1 else 1
+    return rows, cols
+
+
+def quantize(w, bits: int, levels, group_size: int = GROUP, packed=None, norms=None, stream=None):
+    """Quantize a CUDA tensor (float32 or bfloat16, any rank; the last axis is
+    grouped).  Returns (packed uint8 [rows, ngroups, G*sbits/8],
+    norms float16 [rows, ngroups]) on w's device."""
+    import torch
+    if w.dtype == torch.float32:
+        dt = F32
+    elif w.dtype == torch.bfloat16:
+        dt = BF16
+    else:
+        raise TypeError(f"unsupported dtype {w.dtype}")
+    if not w.is_contiguous():
+        raise ValueError("w must be contiguous")
+    rows, cols = _rows_cols(w.shape)
+    ng = -(-cols // group_size) if cols else 0
+    pb = group_size * storage_bits(bits) // 8
+    if packed is None:
+        packed = torch.empty((rows, ng, pb), dtype=torch.uint8, device=w.device)
+    if norms is None:
+        norms = torch.empty((rows, ng), dtype=torch.float16, device=w.device)
+    lv, lvp = _levels_arg(levels)
+    _check("cq_quantize", lib().cq_quantize(_ptr(w), dt, rows, cols, bits, group_size, lvp, lv.size,
+                                            _ptr(packed), _ptr(norms), _stream_ptr(stream)))
+    return packed, norms
+
+
+def dequantize(packed, norms, rows: int, cols: int, bits: int, levels, out_dtype=None,
+               group_size: int = GROUP, out=None, stream=None):
+    """Dequantize to a [rows, cols] CUDA tensor (float32 by default, or
+    bfloat16)."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    dt = {torch.float32: F32, torch.bfloat16: BF16}[out_dtype]
+    if out is None:
+        out = torch.empty((rows, cols), dtype=out_dtype, device=packed.device)
+    lv, lvp = _levels_arg(levels)
+    _check("cq_dequantize", lib().cq_dequantize(_ptr(packed), _ptr(norms), rows, cols, bits,
+                                                group_size, lvp, lv.size, _ptr(out), dt,
+                                                _stream_ptr(stream)))
+    return out
+
+
+def dequant_matvec(packed, norms, n_out: int, k: int, bits: int, levels, x, group_size: int = GROUP,
+                   y=None, stream=None):
+    """y = x . W_hat^T with W the quantized n_out x k matrix; x float32
+    [batch, k] on the device.  Returns float32 [batch, n_out]."""
+    import torch
+    if x.dtype != torch.float32 or not x.is_contiguous():
+        raise TypeError("x must be a contiguous float32 tensor")
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError(f"x must be [batch, {k}], got {tuple(x.shape)}")
+    x2 = x
+    batch = x2.shape[0]
+    if y is None:
+        y = torch.empty((batch, n_out), dtype=torch.float32, device=x.device)
+    lv, lvp = _levels_arg(levels)
+    _check("cq_dequant_matvec", lib().cq_dequant_matvec(_ptr(packed), _ptr(norms), n_out, k, bits,
+                                                        group_size, lvp, lv.size, _ptr(x2), batch,
+                                                        _ptr(y), _stream_ptr(stream)))
+    return y

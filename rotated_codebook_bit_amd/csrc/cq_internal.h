@@ -1,0 +1,52 @@
+// Internal interface between the host library (libcq_host.cpp) and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cq {
+
+constexpr int kGroup = 128;       // elements per group
+constexpr int kWave = 64;         // lanes per wavefront (gfx950)
+constexpr int kMaxLevels = 16;
+
+// Per-call constants of the quantize kernels, derived on the host from the
+// float32 levels.  Thresholds are midpoints of neighbouring float32 levels,
+// computed in double and rounded once to float32.  They are in z units
+// (z = rotated value / group norm * sqrt(G) = unnormalised butterfly output /
+// group norm), so the kernels compare the unnormalised butterfly output Y
+// against threshold * norm.
+struct QuantParams {
+  float thr[kMaxLevels - 1];  // L-1 thresholds (binary-search widths: L = 8, 16)
+  // Two-compare decision for L = 3 and L = 4 (see quantize.hip):
+  float mu;     // centre of the outer pair of thresholds
+  float delta;  // half distance between the outer pair
+  float hmid;   // L = 4: middle threshold minus mu; L = 3: delta
+  int n_levels;
+};
+
+struct LevelTable {
+  float c[kMaxLevels];  // float32 levels in N(0,1) units
+  int n_levels;
+};
+
+// Launchers (return hipError_t of the launch).  All sizes already validated.
+hipError_t launch_quantize(const void* w, bool bf16, int64_t rows, int64_t cols,
+                           const QuantParams& p, uint8_t* packed, uint16_t* norms,
+                           hipStream_t stream);
+
+hipError_t launch_dequantize(const uint8_t* packed, const uint16_t* norms,
+                             int64_t rows, int64_t cols, int sbits,
+                             const LevelTable& lv, void* out, bool bf16_out,
+                             hipStream_t stream);
+
+hipError_t launch_rotate_rows(const float* x, int64_t n_groups, float* xr,
+                              hipStream_t stream);
+
+hipError_t launch_matvec(const uint8_t* packed, const uint16_t* norms,
+                         int64_t n_out, int64_t k, int sbits,
+                         const LevelTable& lv, const float* xr, int64_t batch,
+                         float* y, hipStream_t stream);
+
+}  // namespace cq

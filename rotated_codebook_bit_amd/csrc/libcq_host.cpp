@@ -1,0 +1,326 @@
+// libcq host side: argument validation, layout and size accounting, the
+// Lloyd-Max codebook, per-call constants, and kernel dispatch.
+//
+// Method sources (web pages, by title and section):
+//   "Cactus Quants CQ2-bit Quantization: Extreme Compression for Edge LLMs"
+//       - Group-wise Weight Partitioning; The CQ2-bit Implementation Pipeline
+//   "How CQ2-bit Quantization Contributes to Needle 2's Small Footprint"
+//       - Per-Group Storage Breakdown; Binary Serialization
+//   "How Quantization Codebooks Are Trained in Cactus Quants: Lloyd-Max on
+//    Gaussian Data"
+//       - Gaussian Sampling and Initialization; Iterative Refinement of
+//         Quantization Levels; Ternary Special Case Handling
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "../../include/libcq.h"
+#include "cq_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// Levels of a bit-width; -1 if unsupported.
+int levels_for_bits(int bits, bool host_only) {
+  if (bits == CQ_TERNARY) return 3;
+  if (bits == 2 || bits == 3 || bits == 4) return 1 << bits;
+  if (bits == 1 && host_only) return 2;
+  return -1;
+}
+
+int storage_bits(int bits) { return bits == CQ_TERNARY ? 2 : bits; }
+
+int check_bits(int bits, bool host_only, int* n_levels) {
+  int l = levels_for_bits(bits, host_only);
+  if (l < 0) return fail(CQ_ERR_ARG, "unsupported bits=%d", bits);
+  if (n_levels) *n_levels = l;
+  return CQ_OK;
+}
+
+int check_group(int group_size, bool device) {
+  if (device) {
+    if (group_size != cq::kGroup)
+      return fail(CQ_ERR_UNSUPPORTED, "group_size=%d: device kernels support 128", group_size);
+  } else if (!is_pow2(group_size) || group_size > 4096) {
+    return fail(CQ_ERR_ARG, "group_size=%d must be a power of two <= 4096", group_size);
+  }
+  return CQ_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  auto x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na && nb && x < y + nb && y < x + na;
+}
+
+int check_levels(const float* levels, int n_levels, int expect) {
+  if (!levels) return fail(CQ_ERR_NULL, "levels is NULL");
+  if (n_levels != expect)
+    return fail(CQ_ERR_ARG, "n_levels=%d, this bit-width needs %d", n_levels, expect);
+  for (int i = 0; i < n_levels; ++i) {
+    if (!std::isfinite(levels[i])) return fail(CQ_ERR_ARG, "levels[%d] is not finite", i);
+    if (i && !(levels[i] > levels[i - 1]))
+      return fail(CQ_ERR_ARG, "levels must be strictly ascending (index %d)", i);
+  }
+  return CQ_OK;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Decision constants for the quantize kernels.  The index of a value z is
+// the number of midpoint thresholds strictly below it.  For three and four
+// levels the kernels decide with two compares around the centre mu of the
+// outer thresholds (half width delta):
+//   high bit h = [z - mu > hmid]       (hmid = t_mid - mu; three levels: delta)
+//   q          = [|z - mu| > delta]    (outside the outer pair)
+//   four levels: low bit = NOT (q XOR h);  three levels: low bit = NOT q.
+cq::QuantParams make_quant_params(const float* levels, int n_levels) {
+  cq::QuantParams p{};
+  p.n_levels = n_levels;
+  double t[cq::kMaxLevels - 1];
+  for (int i = 0; i + 1 < n_levels; ++i) {
+    t[i] = 0.5 * (static_cast<double>(levels[i]) + static_cast<double>(levels[i + 1]));
+    p.thr[i] = static_cast<float>(t[i]);
+  }
+  if (n_levels == 3) {
+    double mu = 0.5 * (t[0] + t[1]), d = 0.5 * (t[1] - t[0]);
+    p.mu = static_cast<float>(mu);
+    p.delta = static_cast<float>(d);
+    p.hmid = static_cast<float>(d);
+  } else if (n_levels == 4) {
+    double mu = 0.5 * (t[0] + t[2]), d = 0.5 * (t[2] - t[0]);
+    p.mu = static_cast<float>(mu);
+    p.delta = static_cast<float>(d);
+    p.hmid = static_cast<float>(t[1] - mu);
+  }
+  return p;
+}
+
+cq::LevelTable make_table(const float* levels, int n_levels) {
+  cq::LevelTable t{};
+  t.n_levels = n_levels;
+  for (int i = 0; i < n_levels; ++i) t.c[i] = levels[i];
+  return t;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(CQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return CQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cq_version(void) { return "libcq 0.1 (gfx950)"; }
+
+const char* cq_last_error(void) { return g_last_error; }
+
+const char* cq_status_str(int status) {
+  switch (status) {
+    case CQ_OK: return "ok";
+    case CQ_ERR_NULL: return "null pointer";
+    case CQ_ERR_ARG: return "invalid argument";
+    case CQ_ERR_ALIGN: return "misaligned pointer";
+    case CQ_ERR_UNSUPPORTED: return "unsupported";
+    case CQ_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int cq_layout(int64_t rows, int64_t cols, int bits, int group_size, int64_t* n_groups,
+              int64_t* packed_bytes) {
+  g_last_error[0] = 0;
+  int rc;
+  if ((rc = check_bits(bits, true, nullptr))) return rc;
+  if ((rc = check_group(group_size, false))) return rc;
+  if (rows < 0 || cols < 0) return fail(CQ_ERR_ARG, "negative size");
+  int64_t g = rows * ceil_div(cols, group_size);
+  if (n_groups) *n_groups = g;
+  if (packed_bytes) *packed_bytes = g * (group_size * storage_bits(bits) / 8);
+  return CQ_OK;
+}
+
+int cq_model_bytes(int n_tensors, const int64_t* rows, const int64_t* cols, int bits,
+                   int group_size, uint64_t* bytes_out) {
+  g_last_error[0] = 0;
+  int rc;
+  if (!bytes_out) return fail(CQ_ERR_NULL, "bytes_out is NULL");
+  if (n_tensors < 0) return fail(CQ_ERR_ARG, "n_tensors < 0");
+  if (n_tensors > 0 && (!rows || !cols)) return fail(CQ_ERR_NULL, "rows/cols is NULL");
+  if ((rc = check_bits(bits, true, nullptr))) return rc;
+  if ((rc = check_group(group_size, false))) return rc;
+  const uint64_t per_group = static_cast<uint64_t>(group_size) * storage_bits(bits) / 8 + 2;
+  uint64_t total = 0;
+  for (int i = 0; i < n_tensors; ++i) {
+    if (rows[i] < 0 || cols[i] < 0) return fail(CQ_ERR_ARG, "tensor %d has a negative size", i);
+    total += static_cast<uint64_t>(rows[i]) * static_cast<uint64_t>(ceil_div(cols[i], group_size)) *
+             per_group;
+  }
+  *bytes_out = total;
+  return CQ_OK;
+}
+
+int cq_codebook(int bits, const double* samples, int64_t n_samples, int iters, float* levels_out,
+                int* n_levels) {
+  g_last_error[0] = 0;
+  int L, rc;
+  if (!levels_out || !n_levels) return fail(CQ_ERR_NULL, "levels_out/n_levels is NULL");
+  if ((rc = check_bits(bits, true, &L))) return rc;
+  if (bits == CQ_TERNARY) {
+    static const float kTernary[3] = {-1.2240064f, 0.0f, 1.2240064f};
+    std::memcpy(levels_out, kTernary, sizeof(kTernary));
+    *n_levels = 3;
+    return CQ_OK;
+  }
+  if (!samples) return fail(CQ_ERR_NULL, "samples is NULL");
+  if (n_samples < L) return fail(CQ_ERR_ARG, "need at least %d samples", L);
+  if (iters < 0) return fail(CQ_ERR_ARG, "iters < 0");
+  for (int64_t i = 0; i < n_samples; ++i)
+    if (!std::isfinite(samples[i])) return fail(CQ_ERR_ARG, "sample %lld is not finite", (long long)i);
+
+  // 1-D k-means on the sorted samples.  Cells are contiguous runs of the
+  // sorted array, so each round needs only the L-1 split positions.
+  std::vector<double> x(samples, samples + n_samples);
+  std::sort(x.begin(), x.end());
+  const int64_t n = n_samples;
+  std::vector<double> c(L);
+  for (int k = 0; k < L; ++k) c[k] = x[((2 * static_cast<int64_t>(k) + 1) * n) / (2 * L)];
+  std::vector<int64_t> start(L + 1);
+  for (int it = 0; it < iters; ++it) {
+    start[0] = 0;
+    start[L] = n;
+    for (int k = 1; k < L; ++k) {
+      const double edge = 0.5 * (c[k - 1] + c[k]);
+      // First sample strictly above the boundary: a sample equal to the
+      // boundary stays in the lower cell.
+      start[k] = std::upper_bound(x.begin(), x.end(), edge) - x.begin();
+    }
+    for (int k = 0; k < L; ++k) {
+      const int64_t lo = start[k], hi = start[k + 1];
+      if (hi <= lo) continue;  // empty cell keeps its level
+      long double s = 0.0L;
+      for (int64_t i = lo; i < hi; ++i) s += x[i];
+      c[k] = static_cast<double>(s / static_cast<long double>(hi - lo));
+    }
+  }
+  std::sort(c.begin(), c.end());
+  for (int k = 0; k < L; ++k) levels_out[k] = static_cast<float>(c[k]);
+  *n_levels = L;
+  return CQ_OK;
+}
+
+int cq_quantize(const void* w, int w_dtype, int64_t rows, int64_t cols, int bits, int group_size,
+                const float* levels, int n_levels, uint8_t* packed, uint16_t* norms,
+                void* stream) {
+  g_last_error[0] = 0;
+  int L, rc;
+  if ((rc = check_bits(bits, false, &L))) return rc;
+  if (w_dtype != CQ_F32 && w_dtype != CQ_BF16) return fail(CQ_ERR_ARG, "unknown w_dtype %d", w_dtype);
+  if (rows < 0 || cols < 0) return fail(CQ_ERR_ARG, "negative size");
+  if ((rc = check_group(group_size, true))) return rc;
+  if ((rc = check_levels(levels, n_levels, L))) return rc;
+  if (rows == 0 || cols == 0) return CQ_OK;
+  if (!w || !packed || !norms) return fail(CQ_ERR_NULL, "w/packed/norms is NULL");
+  if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(norms, 2))
+    return fail(CQ_ERR_ALIGN, "w and packed need 16-byte, norms 2-byte alignment");
+  const int64_t ng = rows * ceil_div(cols, group_size);
+  const size_t in_bytes = static_cast<size_t>(rows * cols) * (w_dtype == CQ_F32 ? 4 : 2);
+  const size_t pk_bytes = static_cast<size_t>(ng) * group_size * storage_bits(bits) / 8;
+  const size_t nm_bytes = static_cast<size_t>(ng) * 2;
+  if (overlap(w, in_bytes, packed, pk_bytes) || overlap(w, in_bytes, norms, nm_bytes) ||
+      overlap(packed, pk_bytes, norms, nm_bytes))
+    return fail(CQ_ERR_ARG, "input and output buffers overlap");
+  const cq::QuantParams p = make_quant_params(levels, L);
+  return hip_status(cq::launch_quantize(w, w_dtype == CQ_BF16, rows, cols, p, packed, norms,
+                                        static_cast<hipStream_t>(stream)),
+                    "quantize launch");
+}
+
+int cq_dequantize(const uint8_t* packed, const uint16_t* norms, int64_t rows, int64_t cols,
+                  int bits, int group_size, const float* levels, int n_levels, void* out,
+                  int out_dtype, void* stream) {
+  g_last_error[0] = 0;
+  int L, rc;
+  if ((rc = check_bits(bits, false, &L))) return rc;
+  if (out_dtype != CQ_F32 && out_dtype != CQ_BF16)
+    return fail(CQ_ERR_ARG, "unknown out_dtype %d", out_dtype);
+  if (rows < 0 || cols < 0) return fail(CQ_ERR_ARG, "negative size");
+  if ((rc = check_group(group_size, true))) return rc;
+  if ((rc = check_levels(levels, n_levels, L))) return rc;
+  if (rows == 0 || cols == 0) return CQ_OK;
+  if (!packed || !norms || !out) return fail(CQ_ERR_NULL, "packed/norms/out is NULL");
+  if (!aligned(out, 16) || !aligned(packed, 16) || !aligned(norms, 2))
+    return fail(CQ_ERR_ALIGN, "out and packed need 16-byte, norms 2-byte alignment");
+  const int64_t ng = rows * ceil_div(cols, group_size);
+  const size_t out_bytes = static_cast<size_t>(rows * cols) * (out_dtype == CQ_F32 ? 4 : 2);
+  const size_t pk_bytes = static_cast<size_t>(ng) * group_size * storage_bits(bits) / 8;
+  if (overlap(out, out_bytes, packed, pk_bytes) || overlap(out, out_bytes, norms, ng * 2))
+    return fail(CQ_ERR_ARG, "input and output buffers overlap");
+  const cq::LevelTable lv = make_table(levels, L);
+  return hip_status(cq::launch_dequantize(packed, norms, rows, cols, storage_bits(bits), lv, out,
+                                          out_dtype == CQ_BF16, static_cast<hipStream_t>(stream)),
+                    "dequantize launch");
+}
+
+int cq_dequant_matvec(const uint8_t* packed, const uint16_t* norms, int64_t n_out, int64_t k,
+                      int bits, int group_size, const float* levels, int n_levels, const float* x,
+                      int64_t batch, float* y, void* stream) {
+  g_last_error[0] = 0;
+  int L, rc;
+  if ((rc = check_bits(bits, false, &L))) return rc;
+  if (n_out < 0 || k < 0) return fail(CQ_ERR_ARG, "negative size");
+  if (batch < 1) return fail(CQ_ERR_ARG, "batch must be >= 1");
+  if ((rc = check_group(group_size, true))) return rc;
+  if (k % group_size) return fail(CQ_ERR_UNSUPPORTED, "k=%lld is not a multiple of %d", (long long)k, group_size);
+  if ((rc = check_levels(levels, n_levels, L))) return rc;
+  if (n_out == 0) return CQ_OK;
+  if (!y) return fail(CQ_ERR_NULL, "y is NULL");
+  if (!aligned(y, 16)) return fail(CQ_ERR_ALIGN, "y needs 16-byte alignment");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const cq::LevelTable lv = make_table(levels, L);
+  if (k == 0) {  // empty rows: the kernel writes zeros and reads nothing else
+    return hip_status(cq::launch_matvec(nullptr, nullptr, n_out, 0, storage_bits(bits), lv, nullptr,
+                                        batch, y, s),
+                      "matvec launch");
+  }
+  if (!packed || !norms || !x) return fail(CQ_ERR_NULL, "packed/norms/x is NULL");
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(norms, 2))
+    return fail(CQ_ERR_ALIGN, "x, packed need 16-byte, norms 2-byte alignment");
+  const int64_t ng = n_out * (k / group_size);
+  const size_t y_bytes = static_cast<size_t>(batch * n_out) * 4;
+  const size_t pk_bytes = static_cast<size_t>(ng) * group_size * storage_bits(bits) / 8;
+  if (overlap(y, y_bytes, packed, pk_bytes) || overlap(y, y_bytes, norms, ng * 2) ||
+      overlap(y, y_bytes, x, static_cast<size_t>(batch * k) * 4))
+    return fail(CQ_ERR_ARG, "input and output buffers overlap");
+  float* xr = nullptr;
+  const size_t xr_bytes = static_cast<size_t>(batch * k) * sizeof(float);
+  if ((rc = hip_status(hipMallocAsync(reinterpret_cast<void**>(&xr), xr_bytes, s), "workspace alloc")))
+    return rc;
+  rc = hip_status(cq::launch_rotate_rows(x, batch * (k / group_size), xr, s), "rotate launch");
+  if (!rc)
+    rc = hip_status(cq::launch_matvec(packed, norms, n_out, k, storage_bits(bits), lv, xr, batch, y, s),
+                    "matvec launch");
+  int rc2 = hip_status(hipFreeAsync(xr, s), "workspace free");
+  return rc ? rc : rc2;
+}
+
+}  // extern "C"

@@ -1,0 +1,445 @@
+// CQ quantize kernels for gfx950.
+//
+// Method (web pages, by title and section):
+//   "Cactus Quants CQ2-bit Quantization: Extreme Compression for Edge LLMs",
+//     Group-wise Weight Partitioning (groups of 128 along the last axis, the
+//     last group zero-padded), Hadamard Rotation, The CQ2-bit Implementation
+//     Pipeline (pad, rotate, normalise, nearest level);
+//   "How Quantization Codebooks Are Trained in Cactus Quants",
+//     Iterative Refinement of Quantization Levels (decision boundaries are
+//     the midpoints of neighbouring levels), Production Codebook Generation
+//     and Caching (levels divided by sqrt(G), i.e. z = sqrt(G) y / ||y||
+//     compared against N(0,1) levels);
+//   "How CQ2-bit Quantization Contributes to Needle 2's Small Footprint",
+//     Per-Group Storage Breakdown (indices + one fp16 norm per group).
+//
+// Mapping to the hardware
+//   * One lane owns one whole group: all 7 butterfly stages of the 128-point
+//     Walsh-Hadamard transform run in that lane's registers, with no
+//     cross-lane traffic, and the group norm is a per-lane sum.
+//   * A wave handles a batch of 64 consecutive groups.  The batch is copied
+//     into a wave-private LDS buffer by direct-to-LDS loads
+//     (global_load_lds_dwordx4): every load instruction moves 1 KiB of
+//     contiguous HBM, so reads are fully coalesced although each lane later
+//     needs a 256-byte (bf16) or 512-byte (fp32) stretch.  Each lane then reads
+//     its group with ds_read_b128; chunk c of group g sits in physical chunk
+//     slot c ^ (g & 15), which makes every such read conflict-free.
+//   * The load of the next batch is issued right after the current batch has
+//     been read out of LDS, so it overlaps the arithmetic.
+//   * The butterfly is unnormalised (Y = H x with the +-1 Sylvester matrix).
+//     z = sqrt(G) * (Y / sqrt(G)) / n = Y / n, so instead of dividing, the
+//     thresholds are multiplied by the group norm n once per group.
+//   * Three and four levels: two compares per element.  With mu the centre
+//     and delta the half width of the outer pair of thresholds, and the
+//     shifted value Y' = Y - mu*n,
+//        h = [Y' > hmid*n],  q = [|Y'| > delta*n],
+//        four levels: index = 2h + NOT(q XOR h);  three levels: 2h + NOT q.
+//     Subtracting mu*n from every Y is the same as subtracting it from the
+//     first element of the group before the transform (H maps e_0 to the
+//     all-ones vector), so the shift costs one operation per group.
+//   * Eight and sixteen levels: binary search over thresholds held in VGPRs.
+//   * Bits are shifted into the packed word with add-with-carry from the
+//     compare mask (acc = 2 acc + bit), LSB-first order per the ABI, so a
+//     decision bit costs one compare and one add.
+
+#include "cq_internal.h"
+
+namespace cq {
+namespace kq {
+
+constexpr int kWaves = 4;
+constexpr int kBlock = kWaves * kWave;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0)
+
+template <int L>
+struct Shape {
+  static constexpr int sbits = (L <= 4) ? 2 : (L == 8 ? 3 : 4);
+  static constexpr int words = kGroup * sbits / 32;  // packed dwords per group
+};
+
+// Butterfly stages 2..7 (pairs at distance 2..64) in place; stage 1
+// (distance 1) is done by the loader while the data is unpacked.
+__device__ __forceinline__ void butterfly_from_stage2(float (&y)[kGroup]) {
+#pragma unroll
+  for (int h = 2; h < kGroup; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < kGroup; i += 2 * h) {
+#pragma unroll
+      for (int j = i; j < i + h; ++j) {
+        const float a = y[j], b = y[j + h];
+        y[j] = a + b;
+        y[j + h] = a - b;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t bit(bool b) { return b ? 1u : 0u; }
+
+// acc * 2 + b in one add-with-carry whose carry-in is the wave's compare
+// mask: the compare writes the mask straight into an SGPR pair and
+// v_addc_co_u32 adds each lane's bit.  (Written as plain C++ the compiler
+// materialises each bit with a select and merges it with shifts and ORs,
+// about three times the instructions.)
+__device__ __forceinline__ uint32_t shift_in(uint32_t acc, bool b) {
+  const uint64_t mask = __builtin_amdgcn_ballot_w64(b);
+  uint32_t r;
+  uint64_t carry_out;
+  asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(acc), "s"(mask));
+  return r;
+}
+
+// Index by binary search over 7 thresholds (8 levels).
+__device__ __forceinline__ uint32_t search8(float v, const float (&T)[kMaxLevels - 1]) {
+  const bool b2 = v > T[3];
+  const bool b1 = v > (b2 ? T[5] : T[1]);
+  const float lo = b1 ? T[2] : T[0], hi = b1 ? T[6] : T[4];
+  const bool b0 = v > (b2 ? hi : lo);
+  return (bit(b2) << 2) | (bit(b1) << 1) | bit(b0);
+}
+
+// Index bits (b3, b2, b1, b0) by binary search over 15 thresholds.
+__device__ __forceinline__ void search16(float v, const float (&T)[kMaxLevels - 1], bool& b3,
+                                         bool& b2, bool& b1, bool& b0) {
+  b3 = v > T[7];
+  b2 = v > (b3 ? T[11] : T[3]);
+  const float p0 = b3 ? T[9] : T[1], p1 = b3 ? T[13] : T[5];
+  b1 = v > (b2 ? p1 : p0);
+  const float r0 = b3 ? T[8] : T[0], r1 = b3 ? T[10] : T[2];
+  const float r2 = b3 ? T[12] : T[4], r3 = b3 ? T[14] : T[6];
+  const float s0 = b2 ? r2 : r0, s1 = b2 ? r3 : r1;
+  b0 = v > (b1 ? s1 : s0);
+}
+
+// Everything after stage 1: shift, stages 2..7, decisions, packing.
+// y holds the stage-1 outputs, S the sum of squares of the group.
+template <int L>
+__device__ __forceinline__ uint16_t finish_group(float (&y)[kGroup], float S, const QuantParams& p,
+                                                 uint32_t (&words)[Shape<L>::words]) {
+  const float n = __builtin_sqrtf(S);
+  // An all-zero group has z = 0: deciding with scale 1 compares 0 against
+  // the thresholds themselves.
+  const float ns = S > 0.0f ? n : 1.0f;
+  if constexpr (L == 3 || L == 4) {
+    const float sh = p.mu * ns;
+    y[0] -= sh;
+    y[1] -= sh;
+  }
+  butterfly_from_stage2(y);
+
+  if constexpr (L == 3 || L == 4) {
+    const float A = p.hmid * ns, D = p.delta * ns;
+#pragma unroll
+    for (int wd = 0; wd < 8; ++wd) {
+      uint32_t acc = 0;
+#pragma unroll
+      for (int pos = 15; pos >= 0; --pos) {
+        const float v = y[16 * wd + pos];
+        acc = shift_in(acc, v > A);
+        acc = shift_in(acc, __builtin_fabsf(v) > D);
+      }
+      if constexpr (L == 4)
+        acc ^= ((acc >> 1) & 0x55555555u) ^ 0x55555555u;
+      else
+        acc ^= 0x55555555u;
+      words[wd] = acc;
+    }
+  } else if constexpr (L == 8) {
+    float T[kMaxLevels - 1];
+#pragma unroll
+    for (int i = 0; i < 7; ++i) T[i] = p.thr[i] * ns;
+#pragma unroll
+    for (int i = 0; i < Shape<L>::words; ++i) words[i] = 0;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      const uint32_t idx = search8(y[j], T);
+      const int pos = 3 * j, wd = pos >> 5, off = pos & 31;
+      words[wd] |= idx << off;
+      if (off > 29) words[wd + 1] |= idx >> (32 - off);
+    }
+  } else {
+    float T[kMaxLevels - 1];
+#pragma unroll
+    for (int i = 0; i < 15; ++i) T[i] = p.thr[i] * ns;
+#pragma unroll
+    for (int wd = 0; wd < 16; ++wd) {
+      uint32_t acc = 0;
+#pragma unroll
+      for (int pos = 7; pos >= 0; --pos) {
+        bool b3, b2, b1, b0;
+        search16(y[8 * wd + pos], T, b3, b2, b1, b0);
+        acc = shift_in(acc, b3);
+        acc = shift_in(acc, b2);
+        acc = shift_in(acc, b1);
+        acc = shift_in(acc, b0);
+      }
+      words[wd] = acc;
+    }
+  }
+  const _Float16 h = static_cast<_Float16>(n);
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+template <int L>
+__device__ __forceinline__ void store_group(uint8_t* __restrict__ packed, uint16_t* __restrict__ norms,
+                                            int64_t g, const uint32_t (&words)[Shape<L>::words],
+                                            uint16_t n16) {
+  constexpr int W = Shape<L>::words;
+  uint4* dst = reinterpret_cast<uint4*>(packed + g * (W * 4));
+#pragma unroll
+  for (int i = 0; i < W / 4; ++i)
+    dst[i] = make_uint4(words[4 * i], words[4 * i + 1], words[4 * i + 2], words[4 * i + 3]);
+  norms[g] = n16;
+}
+
+// Stage 1 from one 32-bit word holding elements 2i (low half) and 2i+1.
+__device__ __forceinline__ void stage1_bf16(uint32_t u, float& s, float& d, float& acc) {
+  const float a = __builtin_bit_cast(float, u << 16);
+  const float b = __builtin_bit_cast(float, u & 0xFFFF0000u);
+  s = a + b;
+  d = a - b;
+  acc = __builtin_fmaf(a, a, acc);
+  acc = __builtin_fmaf(b, b, acc);
+}
+
+// Buffer resource over [base, base + bytes): loads past the end return zero
+// and stores past the end are dropped by the hardware, which handles the
+// last, partial batch without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// Groups of batch bt that exist (64 except for the last batch).
+__device__ __forceinline__ int valid_in_batch(int64_t bt, int64_t n_groups) {
+  const int64_t left = n_groups - bt * kWave;
+  return static_cast<int>(left < kWave ? left : kWave);
+}
+
+// DMA of batch bt into the wave's LDS buffer (see quantize_contig).
+template <int GB, int NI, int R>
+__device__ __forceinline__ void issue_batch(const uint8_t* __restrict__ w, int64_t bt,
+                                            int64_t n_groups, uint8_t* buf,
+                                            const uint32_t (&lane_part)[R]) {
+  // Buffer-resource builtins exist only for the GPU target; the host pass
+  // needs nothing but the kernel's signature for its launch stub.
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto src = make_rsrc(w + bt * kWave * GB, valid_in_batch(bt, n_groups) * GB);
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_ptr_t)(buf + i * 1024), 16,
+                                             i * 1024 + lane_part[i % R], 0, 0, 0);
+#endif
+}
+
+// Packed words and norm of every lane's group of batch bt.
+template <int L>
+__device__ __forceinline__ void store_batch(uint8_t* __restrict__ packed, uint16_t* __restrict__ norms,
+                                            int64_t bt, int64_t n_groups, int lane,
+                                            const uint32_t (&words)[Shape<L>::words], uint16_t n16) {
+  constexpr int PB = Shape<L>::words * 4;
+#if defined(__HIP_DEVICE_COMPILE__)  // GPU-only builtins, as in issue_batch
+  const int nv = valid_in_batch(bt, n_groups);
+  const auto dst = make_rsrc(packed + bt * kWave * PB, nv * PB);
+#pragma unroll
+  for (int i = 0; i < PB / 16; ++i) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = {words[4 * i], words[4 * i + 1], words[4 * i + 2], words[4 * i + 3]};
+    __builtin_amdgcn_raw_buffer_store_b128(v, dst, lane * PB + 16 * i, 0, 0);
+  }
+  const auto ndst = make_rsrc(norms + bt * kWave, nv * 2);
+  __builtin_amdgcn_raw_buffer_store_b16(n16, ndst, lane * 2, 0, 0);
+#endif
+}
+
+// Fast path: every group is 128 contiguous elements (cols % 128 == 0).
+//
+// Per iteration a wave reads its 64 groups out of LDS, stores the results of
+// its previous batch, issues the DMA of its next batch into the same buffer,
+// and computes.  The compiler waits for the direct-to-LDS loads (with a full
+// vmcnt(0)) right before the next LDS reads; deferring the stores by one
+// iteration means that wait finds only long-finished stores in flight.
+template <int L, bool BF16>
+__global__ void __launch_bounds__(kBlock, 2)
+quantize_contig(const uint8_t* __restrict__ w, int64_t n_groups, QuantParams p,
+                uint8_t* __restrict__ packed, uint16_t* __restrict__ norms) {
+  constexpr int GB = BF16 ? 256 : 512;  // input bytes per group
+  constexpr int CPG = GB / 16;          // 16-byte chunks per group
+  constexpr int WAVE_BYTES = kWave * GB;
+  constexpr int NI = WAVE_BYTES / 1024;  // 1 KiB load instructions per batch
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * WAVE_BYTES];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  uint8_t* const buf = lds + wave * WAVE_BYTES;
+  const int64_t n_batches = (n_groups + kWave - 1) / kWave;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
+  int64_t batch = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  if (batch >= n_batches) return;
+
+  // Load instruction i, lane l fills LDS slot 64 i + l (16 bytes each): group
+  // gs = GPI*i + q with q = l / CPG, physical chunk cl = l % CPG, which holds
+  // logical chunk cl ^ (gs & 15).  Since q < GPI and GPI*i is a multiple of
+  // GPI, cl ^ (gs & 15) = (cl ^ q) ^ ((GPI*i) & 15), so the source offset is
+  // 1024*i plus a lane part that repeats every R = 16/GPI instructions.
+  constexpr int GPI = kWave / CPG;  // groups per load instruction
+  constexpr int R = 16 / GPI;
+  uint32_t lane_part[R];
+  {
+    const int q = lane / CPG, cl = lane % CPG;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      lane_part[r] = static_cast<uint32_t>(q * GB + 16 * ((cl ^ q) ^ ((GPI * r) & 15)));
+  }
+
+
+
+  // This lane's group occupies bytes [lane*GB, lane*GB + GB) of the buffer;
+  // logical chunk c sits at (lane*GB + 16*(lane & 15)) ^ (16*c).
+  const uint32_t rd_base = static_cast<uint32_t>(lane * GB + 16 * (lane & 15));
+
+
+
+  uint32_t words[Shape<L>::words];
+  uint16_t n16 = 0;
+  int64_t prev = -1;  // batch whose results are waiting in words / n16
+  issue_batch<GB, NI, R>(w, batch, n_groups, buf, lane_part);
+  for (;;) {
+    uint32_t raw[GB / 4];
+#pragma unroll
+    for (int c = 0; c < CPG; ++c) {
+      const uint4 v = *reinterpret_cast<const uint4*>(buf + (rd_base ^ (16u * c)));
+      raw[4 * c] = v.x;
+      raw[4 * c + 1] = v.y;
+      raw[4 * c + 2] = v.z;
+      raw[4 * c + 3] = v.w;
+    }
+    wait_lgkm0();  // the buffer is free once every lane has its group
+    // Keep the deferred stores (and the next DMA) after the LDS reads, i.e.
+    // after the loop-head wait, instead of letting them float above it.
+    asm volatile("" ::: "memory");
+    if (prev >= 0) store_batch<L>(packed, norms, prev, n_groups, lane, words, n16);
+    const int64_t next = batch + stride;
+    if (next < n_batches) issue_batch<GB, NI, R>(w, next, n_groups, buf, lane_part);
+
+    float y[kGroup];
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    if constexpr (BF16) {
+#pragma unroll
+      for (int i = 0; i < 64; i += 4) {
+        stage1_bf16(raw[i], y[2 * i], y[2 * i + 1], s0);
+        stage1_bf16(raw[i + 1], y[2 * i + 2], y[2 * i + 3], s1);
+        stage1_bf16(raw[i + 2], y[2 * i + 4], y[2 * i + 5], s2);
+        stage1_bf16(raw[i + 3], y[2 * i + 6], y[2 * i + 7], s3);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 128; i += 4) {
+        const float a0 = __builtin_bit_cast(float, raw[i]), b0 = __builtin_bit_cast(float, raw[i + 1]);
+        const float a1 = __builtin_bit_cast(float, raw[i + 2]), b1 = __builtin_bit_cast(float, raw[i + 3]);
+        y[i] = a0 + b0;
+        y[i + 1] = a0 - b0;
+        y[i + 2] = a1 + b1;
+        y[i + 3] = a1 - b1;
+        s0 = __builtin_fmaf(a0, a0, s0);
+        s1 = __builtin_fmaf(b0, b0, s1);
+        s2 = __builtin_fmaf(a1, a1, s2);
+        s3 = __builtin_fmaf(b1, b1, s3);
+      }
+    }
+    n16 = finish_group<L>(y, (s0 + s1) + (s2 + s3), p, words);
+    prev = batch;
+    batch = next;
+    if (batch >= n_batches) break;
+  }
+  store_batch<L>(packed, norms, prev, n_groups, lane, words, n16);
+}
+
+// General path: rows whose length is not a multiple of 128; the last group
+// of each row is zero-padded.  Each lane gathers its own group.
+template <int L, bool BF16>
+__global__ void __launch_bounds__(kBlock)
+quantize_ragged(const uint8_t* __restrict__ w, int64_t rows, int64_t cols, QuantParams p,
+                uint8_t* __restrict__ packed, uint16_t* __restrict__ norms) {
+  const int64_t ngr = (cols + kGroup - 1) / kGroup;
+  const int64_t n_groups = rows * ngr;
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  if (g >= n_groups) return;
+  const int64_t row = g / ngr, gi = g - row * ngr;
+  const int64_t col0 = gi * kGroup;
+  const int64_t valid = cols - col0 < kGroup ? cols - col0 : kGroup;
+  const int64_t base = row * cols + col0;
+  float x[kGroup];
+#pragma unroll
+  for (int j = 0; j < kGroup; ++j) {
+    float v = 0.0f;
+    if (j < valid) {
+      if constexpr (BF16) {
+        const uint16_t b = reinterpret_cast<const uint16_t*>(w)[base + j];
+        v = __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);
+      } else {
+        v = reinterpret_cast<const float*>(w)[base + j];
+      }
+    }
+    x[j] = v;
+  }
+  float y[kGroup];
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < kGroup; i += 2) {
+    y[i] = x[i] + x[i + 1];
+    y[i + 1] = x[i] - x[i + 1];
+    s0 = __builtin_fmaf(x[i], x[i], s0);
+    s1 = __builtin_fmaf(x[i + 1], x[i + 1], s1);
+  }
+  uint32_t words[Shape<L>::words];
+  const uint16_t n16 = finish_group<L>(y, s0 + s1, p, words);
+  store_group<L>(packed, norms, g, words, n16);
+}
+
+template <int L, bool BF16>
+hipError_t launch_l(const void* w, int64_t rows, int64_t cols, const QuantParams& p,
+                    uint8_t* packed, uint16_t* norms, hipStream_t s) {
+  const uint8_t* wb = static_cast<const uint8_t*>(w);
+  if (cols % kGroup == 0) {
+    const int64_t n_groups = rows * (cols / kGroup);
+    const int64_t n_batches = (n_groups + kWave - 1) / kWave;
+    // Enough resident waves to keep every CU busy; each wave loops over
+    // batches so the next load overlaps the current arithmetic.
+    const int64_t want = (n_batches + kWaves - 1) / kWaves;
+    const int blocks = static_cast<int>(want < 2048 ? want : 2048);
+    hipLaunchKernelGGL((quantize_contig<L, BF16>), dim3(blocks), dim3(kBlock), 0, s, wb, n_groups,
+                       p, packed, norms);
+  } else {
+    const int64_t n_groups = rows * ((cols + kGroup - 1) / kGroup);
+    const int blocks = static_cast<int>((n_groups + kBlock - 1) / kBlock);
+    hipLaunchKernelGGL((quantize_ragged<L, BF16>), dim3(blocks), dim3(kBlock), 0, s, wb, rows,
+                       cols, p, packed, norms);
+  }
+  return hipGetLastError();
+}
+
+template <int L>
+hipError_t launch_dtype(const void* w, bool bf16, int64_t rows, int64_t cols, const QuantParams& p,
+                        uint8_t* packed, uint16_t* norms, hipStream_t s) {
+  return bf16 ? launch_l<L, true>(w, rows, cols, p, packed, norms, s)
+              : launch_l<L, false>(w, rows, cols, p, packed, norms, s);
+}
+
+}  // namespace kq
+
+hipError_t launch_quantize(const void* w, bool bf16, int64_t rows, int64_t cols,
+                           const QuantParams& p, uint8_t* packed, uint16_t* norms,
+                           hipStream_t stream) {
+  switch (p.n_levels) {
+    case 3: return kq::launch_dtype<3>(w, bf16, rows, cols, p, packed, norms, stream);
+    case 4: return kq::launch_dtype<4>(w, bf16, rows, cols, p, packed, norms, stream);
+    case 8: return kq::launch_dtype<8>(w, bf16, rows, cols, p, packed, norms, stream);
+    case 16: return kq::launch_dtype<16>(w, bf16, rows, cols, p, packed, norms, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace cq

@@ -1,0 +1,115 @@
+"""Comparison rules between libcq (GPU) results and the oracle.
+
+* Indices: bit-exact, except elements whose normalised value lies within
+  BAND = 1e-5 (z units, oracle float64) of a decision threshold; there either
+  neighbouring index is correct.  Such mismatches are counted and must number
+  at most MAX_FRAC = 1e-6 of the elements checked.
+* Norms (binary16): bit-exact, except where the oracle's float64 norm lies
+  within 1e-6 relative of a binary16 rounding midpoint; there either
+  neighbour is correct (the GPU rounds its float32 norm).
+* Dequantized values: |x_gpu - x_ref| <= 1e-5 * RMS_g per element, with
+  RMS_g = norm16 / sqrt(G) of the element's group.
+* Matvec: |y_gpu - y_ref| <= 1e-5 * ||x_b|| * ||W_hat_r|| per element.
+
+The oracle is only ever given inputs that came from the seeded generators or
+from the oracle itself, never from the GPU.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from oracle import cq_oracle as O
+
+BAND = 1e-5
+MAX_FRAC = 1e-6
+NORM_REL = 1e-6
+DEQ_TOL = 1e-5
+MV_TOL = 1e-5
+
+
+class Report(dict):
+    def line(self) -> str:
+        return " ".join(f"{k}={v}" for k, v in self.items())
+
+
+def _fp16_value(bits: np.ndarray) -> np.ndarray:
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def check_indices(idx_gpu: np.ndarray, q: O.Quantized, enforce_count: bool = True) -> Report:
+    """Every mismatch must be in band and to a neighbouring level; with
+    enforce_count the number of mismatches is capped here, else the caller
+    applies the cap to a whole workload (see check_count)."""
+    idx_gpu = np.asarray(idx_gpu).reshape(q.idx.shape)
+    mism = idx_gpu != q.idx
+    n = int(mism.sum())
+    total = q.idx.size
+    rep = Report(elements=total, index_mismatches=n)
+    if n:
+        dist = O.threshold_distance(q.z[mism], q.levels32)
+        assert np.all(dist <= BAND), f"index mismatch outside the band: max dist {dist.max():.3g}"
+        assert np.all(np.abs(idx_gpu[mism] - q.idx[mism]) == 1), "mismatch is not a neighbouring level"
+        rep["max_band_dist"] = float(dist.max())
+    if enforce_count:
+        check_count(n, total)
+    return rep
+
+
+def check_count(mismatches: int, elements: int) -> None:
+    allowed = math.floor(MAX_FRAC * elements)
+    assert mismatches <= allowed, (f"{mismatches} in-band mismatches > {allowed} allowed "
+                                   f"({MAX_FRAC:g} of {elements})")
+
+
+def check_norms(norm16_gpu: np.ndarray, q: O.Quantized) -> Report:
+    g = np.asarray(norm16_gpu).view(np.uint16).reshape(q.norm16.shape)
+    diff = g != q.norm16
+    n = int(diff.sum())
+    rep = Report(groups=q.norm16.size, norm_mismatches=n)
+    if n:
+        ref = q.norm[diff]
+        a = _fp16_value(g[diff])
+        b = _fp16_value(q.norm16[diff])
+        # The two values must be binary16 neighbours and the exact norm must
+        # sit within NORM_REL of their midpoint.
+        step = np.abs(g[diff].astype(np.int64) - q.norm16[diff].astype(np.int64))
+        assert np.all(step == 1), "norms differ by more than one binary16 step"
+        mid = 0.5 * (a + b)
+        assert np.all(np.abs(ref - mid) <= NORM_REL * ref), "norm mismatch away from a rounding midpoint"
+    return rep
+
+
+def check_quantize(packed_gpu: np.ndarray, norms_gpu: np.ndarray, q: O.Quantized,
+                   enforce_count: bool = True) -> Report:
+    sb = O.storage_bits(q.bits)
+    idx = O.unpack(np.asarray(packed_gpu).reshape(-1, q.g * sb // 8), sb, q.g)
+    rep = check_indices(idx, q, enforce_count)
+    rep.update(check_norms(norms_gpu, q))
+    return rep
+
+
+def check_dequant(out_gpu: np.ndarray, ref: np.ndarray, norm16: np.ndarray, rows: int, cols: int,
+                  g: int = O.GROUP) -> Report:
+    """out_gpu and ref are [rows, cols]; norm16 [rows, ceil(cols/g)]."""
+    out = np.asarray(out_gpu, dtype=np.float64).reshape(rows, cols)
+    ng = -(-cols // g)
+    rms = _fp16_value(norm16).reshape(rows, ng) / math.sqrt(g)
+    tol = np.repeat(rms, g, axis=1)[:, :cols] * DEQ_TOL
+    err = np.abs(out - ref)
+    bad = err > tol
+    assert not bad.any(), (f"{int(bad.sum())} dequantized values off by more than 1e-5 RMS; worst "
+                           f"{float((err / np.maximum(tol / DEQ_TOL, 1e-300)).max()):.3g} RMS")
+    scaled = err / np.where(tol > 0, tol / DEQ_TOL, 1.0)
+    return Report(values=out.size, max_err_rms=float(scaled.max()) if out.size else 0.0)
+
+
+def check_matvec(y_gpu: np.ndarray, y_ref: np.ndarray, x: np.ndarray, w_hat: np.ndarray) -> Report:
+    x = np.asarray(x, dtype=np.float64)
+    scale = np.linalg.norm(x, axis=1)[:, None] * np.linalg.norm(w_hat, axis=1)[None, :]
+    err = np.abs(np.asarray(y_gpu, dtype=np.float64) - y_ref)
+    rel = err / np.where(scale > 0, scale, 1.0)
+    assert np.all(err <= MV_TOL * scale), f"matvec error {rel.max():.3g} of ||x|| ||w|| > {MV_TOL:g}"
+    return Report(outputs=err.size, max_err_scaled=float(rel.max()))

@@ -1,0 +1,190 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/libcq.h declares, its host-only calls agree with the oracle, and
+every argument-validation error is returned before any HIP call (so fake
+device pointers are safe here)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import rotated_codebook_bit_amd as cq
+from oracle import cq_oracle as O
+from rotated_codebook_bit_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libcq.h")
+
+OK, E_NULL, E_ARG, E_ALIGN, E_UNSUP = 0, -1, -2, -3, -4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cq_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = cq.lib()
+    names = declared_functions()
+    assert {"cq_quantize", "cq_dequantize", "cq_dequant_matvec", "cq_model_bytes"} <= set(names)
+    for name in names:
+        assert hasattr(L, name), name
+    assert L.cq_version().decode().startswith("libcq")
+
+
+def test_status_strings():
+    L = cq.lib()
+    for s in (OK, E_NULL, E_ARG, E_ALIGN, E_UNSUP, -5):
+        assert L.cq_status_str(s)
+    assert L.cq_status_str(-99) == b"unknown status"
+
+
+# -- host-only calls vs the oracle ------------------------------------------------
+
+@pytest.mark.parametrize("bits", [O.TERNARY, 1, 2, 3, 4])
+def test_codebook_equals_oracle_float32(bits, lloyd_samples, oracle_levels):
+    got = cq.codebook(bits, lloyd_samples)
+    want = O.runtime_levels(oracle_levels[bits]).astype(np.float32)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_codebook_iterations_and_tiny_example(lloyd_samples):
+    import json
+    ex = json.load(open(os.path.join(ROOT, "tests", "golden", "hand_examples.json")))["lloyd_tiny"]
+    # 1 level-bit = 2 levels, the tiny hand example
+    got = cq.codebook(1, np.array(ex["samples"]), iters=10)
+    np.testing.assert_allclose(got, np.float32(ex["result"]), rtol=0, atol=0)
+    got0 = cq.codebook(1, np.array(ex["samples"]), iters=0)
+    np.testing.assert_array_equal(got0, np.float32(ex["init"]))
+
+
+def test_layout_and_model_bytes():
+    assert cq.layout(300, 1000, 2) == (2400, 2400 * 32)
+    assert cq.layout(7, 128, 3) == (7, 7 * 48)
+    assert cq.layout(0, 5, 4) == (0, 0)
+    shapes = [s for _, s in W.needle2_shapes()]
+    for bits in (O.TERNARY, 1, 2, 3, 4):
+        assert cq.model_bytes(shapes, bits) == O.model_bytes(shapes, bits)
+    assert cq.model_bytes(shapes, 2) == 12_162_752
+    for g in (32, 64, 256):
+        assert cq.model_bytes([(3, 1000)], 2, g) == O.model_bytes([(3, 1000)], 2, g)
+    assert cq.model_bytes([], 2) == 0
+    assert cq.model_bytes([(2, 3, 129)], 4) == O.model_bytes([(2, 3, 129)], 4)
+
+
+def test_llama7b_byte_counts():
+    shapes = W.llama7b_shapes()
+    params = sum(r * c for r, c in shapes)
+    assert params == 6_607_077_376
+    assert cq.model_bytes(shapes, 2) == 1_651_769_344 + 103_235_584
+
+
+# -- validation (no HIP call is reached) ---------------------------------------
+
+F = ctypes.POINTER(ctypes.c_float)
+FAKE = ctypes.c_void_p(0x100000)      # never dereferenced: validation fails first
+FAKE2 = ctypes.c_void_p(0x900000)
+FAKE3 = ctypes.c_void_p(0x1100000)
+
+
+def _levels(n):
+    arr = np.linspace(-1.5, 1.5, n).astype(np.float32)
+    return arr, arr.ctypes.data_as(F)
+
+
+def quant(w=FAKE, dt=0, rows=4, cols=256, bits=2, g=128, levels=None, nl=None, packed=FAKE2,
+          norms=FAKE3):
+    lv, lp = _levels(4 if nl is None else nl) if levels is None else levels
+    if nl is None:
+        nl = lv.size
+    return cq.lib().cq_quantize(w, dt, rows, cols, bits, g, lp, nl, packed, norms, None)
+
+
+def test_quantize_validation():
+    L = cq.lib()
+    assert quant(bits=5) == E_ARG
+    assert quant(bits=1) == E_ARG               # host-only width
+    assert quant(dt=7) == E_ARG
+    assert quant(rows=-1) == E_ARG
+    assert quant(g=64) == E_UNSUP
+    assert quant(nl=3) == E_ARG                 # 2 bits needs 4 levels
+    bad = np.array([0.0, 0.0, 1.0, 2.0], dtype=np.float32)
+    assert quant(levels=(bad, bad.ctypes.data_as(F))) == E_ARG
+    nan = np.array([0.0, np.nan, 1.0, 2.0], dtype=np.float32)
+    assert quant(levels=(nan, nan.ctypes.data_as(F))) == E_ARG
+    assert quant(levels=(np.zeros(4, np.float32), None)) == E_NULL
+    assert quant(w=None) == E_NULL
+    assert quant(packed=None) == E_NULL
+    assert quant(w=ctypes.c_void_p(0x100004)) == E_ALIGN
+    assert quant(norms=ctypes.c_void_p(0x1100001)) == E_ALIGN
+    assert quant(packed=ctypes.c_void_p(0x100010)) == E_ARG   # overlaps w
+    assert L.cq_last_error()
+    # empty tensors are a no-op even with NULL pointers
+    assert quant(rows=0, w=None, packed=None, norms=None) == OK
+    assert quant(cols=0, w=None, packed=None, norms=None) == OK
+
+
+def test_dequantize_validation():
+    L = cq.lib()
+    lv, lp = _levels(8)
+
+    def deq(packed=FAKE, norms=FAKE2, rows=4, cols=256, bits=3, g=128, out=FAKE3, dt=0, nl=8):
+        return L.cq_dequantize(packed, norms, rows, cols, bits, g, lp, nl, out, dt, None)
+
+    assert deq(dt=2) == E_ARG
+    assert deq(bits=7) == E_ARG
+    assert deq(g=256) == E_UNSUP
+    assert deq(nl=4) == E_ARG
+    assert deq(out=None) == E_NULL
+    assert deq(out=ctypes.c_void_p(0x1100008)) == E_ALIGN
+    assert deq(out=ctypes.c_void_p(0x100000 + 64)) == E_ARG      # overlaps packed
+    assert deq(rows=0, packed=None, norms=None, out=None) == OK
+
+
+def test_matvec_validation():
+    L = cq.lib()
+    lv, lp = _levels(4)
+
+    def mv(packed=FAKE, norms=FAKE2, n_out=8, k=256, bits=2, x=ctypes.c_void_p(0x2100000), batch=1,
+           y=ctypes.c_void_p(0x3100000), g=128, nl=4):
+        return L.cq_dequant_matvec(packed, norms, n_out, k, bits, g, lp, nl, x, batch, y, None)
+
+    assert mv(k=200) == E_UNSUP
+    assert mv(batch=0) == E_ARG
+    assert mv(bits=158, nl=4) == E_ARG
+    assert mv(x=None) == E_NULL
+    assert mv(y=None) == E_NULL
+    assert mv(x=ctypes.c_void_p(0x2100004)) == E_ALIGN
+    assert mv(y=ctypes.c_void_p(0x2100000)) == E_ARG              # y overlaps x
+    assert mv(n_out=0, packed=None, norms=None, x=None, y=None) == OK
+
+
+def test_host_call_validation():
+    L = cq.lib()
+    out = (ctypes.c_float * 16)()
+    n = ctypes.c_int()
+    assert L.cq_codebook(2, None, 10, 200, out, ctypes.byref(n)) == E_NULL
+    s = np.zeros(3)
+    assert L.cq_codebook(2, s.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), 3, 200, out,
+                         ctypes.byref(n)) == E_ARG        # fewer samples than levels
+    assert L.cq_codebook(9, None, 0, 200, out, ctypes.byref(n)) == E_ARG
+    assert L.cq_codebook(158, None, 0, 0, out, ctypes.byref(n)) == OK and n.value == 3
+    ng = ctypes.c_int64()
+    assert L.cq_layout(1, 1, 2, 96, ctypes.byref(ng), None) == E_ARG
+    assert L.cq_layout(-1, 1, 2, 128, ctypes.byref(ng), None) == E_ARG
+    r = (ctypes.c_int64 * 1)(-5)
+    c = (ctypes.c_int64 * 1)(5)
+    b = ctypes.c_uint64()
+    assert L.cq_model_bytes(1, r, c, 2, 128, ctypes.byref(b)) == E_ARG
+    assert L.cq_model_bytes(1, None, None, 2, 128, ctypes.byref(b)) == E_NULL
+    assert L.cq_model_bytes(1, r, c, 2, 128, None) == E_NULL
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(cq, "_lib", None)
+    monkeypatch.setattr(cq, "LIB_PATH", "/nonexistent/libcq.so")
+    with pytest.raises(ImportError):
+        cq.lib()

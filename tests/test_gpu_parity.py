@@ -1,0 +1,288 @@
+"""GPU parity: libcq's HIP kernels against the CPU oracle, through the C ABI.
+
+Workloads follow the pages' own (random matrices, the 45.5M-parameter model,
+a 7B-shaped model); inputs come from the seeded generators in
+rotated_codebook_bit_amd.workloads.  Each case prints its name before it
+touches the GPU.
+"""
+
+import math
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+from oracle import cq_oracle as O
+from rotated_codebook_bit_amd import workloads as W
+from parity import check_count, check_dequant, check_matvec, check_quantize
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import rotated_codebook_bit_amd as cq  # noqa: E402
+
+DEV = "cuda"
+ALL_BITS = [O.TERNARY, 2, 3, 4]
+
+
+def say(msg):
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def levels(lloyd_samples):
+    # Both sides use the same float32 levels: libcq's own Lloyd-Max run (the
+    # ABI tests pin it to the oracle's bit for bit).
+    return {b: cq.codebook(b, lloyd_samples) for b in ALL_BITS}
+
+
+def to_dev_f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def to_dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def gpu_quantize(w_dev, bits, lv):
+    packed, norms = cq.quantize(w_dev, bits, lv)
+    return host(packed), host(norms.view(torch.int16)).view(np.uint16)
+
+
+def run_case(name, w_host64, w_dev, bits, lv, deq=True):
+    """Quantize on both sides, compare; dequantize the oracle's packed data on
+    the GPU and compare; compare the two round trips."""
+    rows, cols = w_host64.reshape(-1, w_host64.shape[-1]).shape
+    say(f"{name}: quantize bits={bits} shape={tuple(w_host64.shape)}")
+    q = O.quantize(w_host64, bits, lv)
+    packed, norms = gpu_quantize(w_dev, bits, lv)
+    rep = check_quantize(packed, norms, q)
+    if deq:
+        say(f"{name}: dequantize oracle packing bits={bits}")
+        ref = O.dequantize(q.packed, q.norm16, rows, cols, bits, lv)
+        p_dev = torch.from_numpy(q.packed.reshape(rows, -1)).to(DEV)
+        n_dev = torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16)
+        out = host(cq.dequantize(p_dev, n_dev, rows, cols, bits, lv))
+        rep.update(check_dequant(out, ref, q.norm16, rows, cols))
+        # Round trip: GPU quantize -> GPU dequantize vs the oracle's chain, on
+        # groups whose indices and norm agree.
+        say(f"{name}: round trip bits={bits}")
+        rt = host(cq.dequantize(torch.from_numpy(packed).to(DEV),
+                                torch.from_numpy(norms.view(np.int16)).to(DEV).view(torch.float16),
+                                rows, cols, bits, lv))
+        sb = O.storage_bits(bits)
+        same = (O.unpack(packed.reshape(-1, 16 * sb), sb).reshape(q.idx.shape) == q.idx).all(-1)
+        same &= norms.reshape(q.norm16.shape) == q.norm16
+        cols_ok = np.repeat(same, O.GROUP, axis=1)[:, :cols]
+        err = np.abs(rt.astype(np.float64) - ref)
+        rms = np.repeat(q.norm16.view(np.float16).astype(np.float64), O.GROUP, axis=1)[:, :cols]
+        assert np.all(err[cols_ok] <= 1e-5 * rms[cols_ok] / math.sqrt(O.GROUP))
+        rep["roundtrip_groups_compared"] = int(same.sum())
+    say(f"{name}: {rep.line()}")
+    return rep
+
+
+# -- the small fp32 matrix ----------------------------------------------------------
+
+def test_small_matrix_2bit(levels):
+    w = W.small()
+    run_case("small", w.astype(np.float64), to_dev_f32(w), 2, levels[2])
+
+
+@pytest.mark.parametrize("bits", ALL_BITS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(1000, 384), (77, 1000), (3, 1, 130), (1, 128), (1, 1)])
+def test_bits_dtypes_shapes(bits, dtype, shape, levels):
+    rng = np.random.default_rng(zlib.crc32(repr((bits, dtype, shape)).encode()))
+    w = (rng.standard_normal(shape) * 0.02).astype(np.float32)
+    if dtype == "bf16":
+        b = W.f32_to_bf16_bits(w)
+        run_case(f"{dtype}{shape}", W.bf16_bits_to_f32(b).astype(np.float64), to_dev_bf16(b), bits,
+                 levels[bits])
+    else:
+        run_case(f"{dtype}{shape}", w.astype(np.float64), to_dev_f32(w), bits, levels[bits])
+
+
+def test_special_groups(levels):
+    """Zero groups, constant groups, power-of-two scaled copies, huge values
+    whose norm overflows binary16 (stored as +Inf)."""
+    rng = np.random.default_rng(5)
+    base = rng.standard_normal((1, 128))
+    w = np.concatenate([np.zeros((1, 128)), np.full((1, 128), 0.25), base, base * 2.0 ** 10,
+                        np.full((1, 128), -3.0), np.full((1, 128), 1e5)], axis=0).astype(np.float32)
+    for bits in ALL_BITS:
+        say(f"special groups bits={bits}")
+        q = O.quantize(w.astype(np.float64), bits, levels[bits])
+        packed, norms = gpu_quantize(to_dev_f32(w), bits, levels[bits])
+        check_quantize(packed, norms, q)
+        assert norms[-1, 0] == 0x7C00 and norms[0, 0] == 0
+
+
+def test_empty_inputs(levels):
+    for shape in [(0, 128), (5, 0), (0,)]:
+        w = torch.zeros(shape, dtype=torch.float32, device=DEV)
+        p, n = cq.quantize(w, 2, levels[2])
+        assert p.numel() == 0 and n.numel() == 0
+    out = cq.dequantize(torch.zeros((0, 32), dtype=torch.uint8, device=DEV),
+                        torch.zeros((0, 1), dtype=torch.float16, device=DEV), 0, 128, 2, levels[2])
+    assert out.shape == (0, 128)
+    y = cq.dequant_matvec(torch.zeros((4, 0), dtype=torch.uint8, device=DEV),
+                          torch.zeros((4, 0), dtype=torch.float16, device=DEV), 4, 0, 2, levels[2],
+                          torch.zeros((2, 0), dtype=torch.float32, device=DEV))
+    assert host(y).shape == (2, 4) and not host(y).any()
+
+
+def test_deterministic(levels):
+    w = to_dev_bf16(W.f32_to_bf16_bits((np.random.default_rng(3).standard_normal((512, 4096)) * 0.02)
+                                       .astype(np.float32)))
+    say("determinism")
+    a = gpu_quantize(w, 2, levels[2])
+    b = gpu_quantize(w, 2, levels[2])
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_bf16_output(levels):
+    lv = levels[2]
+    w = W.small()
+    q = O.quantize(w.astype(np.float64), 2, lv)
+    ref = O.dequantize(q.packed, q.norm16, 256, 512, 2, lv)
+    say("dequantize to bf16")
+    out = cq.dequantize(torch.from_numpy(q.packed.reshape(256, -1)).to(DEV),
+                        torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16),
+                        256, 512, 2, lv, out_dtype=torch.bfloat16)
+    got = W.bf16_bits_to_f32(host(out.view(torch.int16)).view(np.uint16)).astype(np.float64)
+    # bf16 rounding of a float32 value within 1e-5 RMS of the reference.
+    ulp = np.abs(W.bf16_round(ref.astype(np.float32)).astype(np.float64) - ref) + 1e-300
+    rms = np.repeat(q.norm16.view(np.float16).astype(np.float64), 128, axis=1) / math.sqrt(128)
+    assert np.all(np.abs(got - ref) <= 2 * np.abs(ref) * 2.0 ** -8 + 1e-5 * rms)
+
+
+# -- the 45.5M-parameter set --------------------------------------------------------
+
+def test_needle2_set(levels):
+    lv = levels[2]
+    tensors = W.needle2()
+    total = mism = elems = 0
+    for name, w in tensors:
+        say(f"needle2 {name} {w.shape}")
+        q = O.quantize(w.astype(np.float64), 2, lv)
+        packed, norms = gpu_quantize(to_dev_f32(w), 2, lv)
+        rep = check_quantize(packed, norms, q, enforce_count=False)
+        mism += rep["index_mismatches"]
+        elems += rep["elements"]
+        total += packed.nbytes + norms.nbytes
+    say(f"needle2 set: {mism} in-band index mismatches in {elems} elements")
+    check_count(mism, elems)  # the cap applies to the whole parameter set
+    assert total == cq.model_bytes([w.shape for _, w in tensors], 2) == 12_162_752
+    # dequantize + round trip on the padded tensor and one full layer tensor
+    for name, w in (tensors[-1], tensors[5]):
+        run_case(f"needle2 {name}", w.astype(np.float64), to_dev_f32(w), 2, lv)
+
+
+# -- bit-width sweep on the heavy-tailed 4096x4096 bf16 matrix ------------------------
+
+@pytest.mark.parametrize("bits", ALL_BITS)
+def test_sweep_4096(bits, levels):
+    b = W.sweep_bits()
+    w64 = W.bf16_bits_to_f32(b).astype(np.float64)
+    rep = run_case("sweep4096", w64, to_dev_bf16(b), bits, levels[bits])
+    rot = O.relative_mse(w64, O.fake_quant(w64, bits, levels[bits]))
+    say(f"sweep4096 bits={bits} rel_mse={rot:.4f} rel_err={math.sqrt(rot):.4f}")
+    assert rep["elements"] == 4096 * 4096
+
+
+# -- 7B-shaped model, one flat launch, sampled checks --------------------------------
+
+def test_llama7b_flat_sampled(levels):
+    lv = levels[2]
+    say("llama7b: generate 6.6G bf16 params on the device")
+    buf, offsets = W.llama7b_device(DEV)
+    n_groups = buf.numel() // 128
+    w2 = buf.view(n_groups, 128)
+    say(f"llama7b: quantize {n_groups} groups in one launch")
+    packed, norms = cq.quantize(w2, 2, lv)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    sample = np.unique(np.concatenate([
+        rng.choice(n_groups, 30_000, replace=False),
+        np.arange(n_groups - 300, n_groups),                  # the final, partial batches
+        np.arange(int(offsets[4]) // 128, int(offsets[5]) // 128),  # one full 4096x11008 tensor
+    ]))
+    idx_dev = torch.from_numpy(sample).to(DEV)
+    x = W.bf16_bits_to_f32(host(w2.index_select(0, idx_dev).view(torch.int16)).view(np.uint16))
+    say(f"llama7b: oracle on {sample.size} sampled groups")
+    q = O.quantize(x.astype(np.float64), 2, lv)
+    p = host(packed.view(n_groups, 32).index_select(0, idx_dev))
+    n = host(norms.view(n_groups).view(torch.int16).index_select(0, idx_dev)).view(np.uint16)
+    rep = check_quantize(p.reshape(-1, 1, 32), n.reshape(-1, 1), q)
+    say(f"llama7b quantize: {rep.line()}")
+    say("llama7b: dequantize whole model to fp32")
+    out = cq.dequantize(packed.view(n_groups, 32), norms.view(n_groups, 1), n_groups, 128, 2, lv)
+    got = host(out.index_select(0, idx_dev))
+    del out
+    ref = O.dequantize(q.packed, q.norm16, sample.size, 128, 2, lv)
+    same = np.all(O.unpack(p, 2) == q.idx[:, 0], axis=1) & (n == q.norm16[:, 0])
+    rms = q.norm16[:, 0].view(np.float16).astype(np.float64) / math.sqrt(128)
+    err = np.abs(got.astype(np.float64) - ref)
+    assert np.all(err[same] <= 1e-5 * rms[same, None])
+    say(f"llama7b round trip: groups compared {int(same.sum())} of {sample.size}")
+
+
+# -- dequant-matvec 11008x4096 ------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def matvec_weight(levels):
+    lv = levels[2]
+    b = W.matvec_weight_bits()
+    w64 = W.bf16_bits_to_f32(b).astype(np.float64)
+    q = O.quantize(w64, 2, lv)
+    return b, q
+
+
+def test_matvec_weight_quantize(matvec_weight, levels):
+    b, q = matvec_weight
+    say("matvec weight: quantize 11008x4096 bf16")
+    packed, norms = gpu_quantize(to_dev_bf16(b), 2, levels[2])
+    say(f"matvec weight: {check_quantize(packed, norms, q).line()}")
+
+
+@pytest.mark.parametrize("batch", [1, 8, 3, 11])
+def test_matvec(batch, matvec_weight, levels):
+    lv = levels[2]
+    _, q = matvec_weight
+    n_out, k = 11008, 4096
+    x = W.matvec_x(batch)
+    say(f"matvec batch={batch}")
+    w_hat = O.dequantize(q.packed, q.norm16, n_out, k, 2, lv)
+    y_ref = x.astype(np.float64) @ w_hat.T
+    y = host(cq.dequant_matvec(torch.from_numpy(q.packed.reshape(n_out, -1)).to(DEV),
+                               torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16),
+                               n_out, k, 2, lv, to_dev_f32(x)))
+    say(f"matvec batch={batch}: {check_matvec(y, y_ref, x, w_hat).line()}")
+
+
+@pytest.mark.parametrize("bits", [O.TERNARY, 3, 4])
+@pytest.mark.parametrize("n_out,k", [(37, 11008), (300, 384)])
+def test_matvec_bits_shapes(bits, n_out, k, levels):
+    lv = levels[bits]
+    rng = np.random.default_rng(n_out + k + bits)
+    w = rng.standard_normal((n_out, k)) * 0.02
+    q = O.quantize(w, bits, lv)
+    x = rng.standard_normal((2, k)).astype(np.float32)
+    w_hat = O.dequantize(q.packed, q.norm16, n_out, k, bits, lv)
+    y_ref = x.astype(np.float64) @ w_hat.T
+    say(f"matvec bits={bits} {n_out}x{k}")
+    y = host(cq.dequant_matvec(torch.from_numpy(q.packed.reshape(n_out, -1)).to(DEV),
+                               torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16),
+                               n_out, k, bits, lv, to_dev_f32(x)))
+    check_matvec(y, y_ref, x, w_hat)
