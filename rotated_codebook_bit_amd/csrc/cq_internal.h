@@ -31,6 +31,17 @@ struct LevelTable {
   int n_levels;
 };
 
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+// Blocks for a persistent grid-stride kernel: `per_cu` resident blocks on
+// every compute unit, but no more than there is work for.
+inline int persistent_blocks(int64_t work_blocks, int per_cu) {
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * per_cu;
+  const int64_t b = work_blocks < cap ? work_blocks : cap;
+  return static_cast<int>(b > 0 ? b : 1);
+}
+
 // Launchers (return hipError_t of the launch).  All sizes already validated.
 hipError_t launch_quantize(const void* w, bool bf16, int64_t rows, int64_t cols,
                            const QuantParams& p, uint8_t* packed, uint16_t* norms,

@@ -26,6 +26,7 @@ namespace kd {
 
 constexpr int kWaves = 4;
 constexpr int kBlock = kWaves * kWave;
+constexpr int kBlocksPerCu = 2;
 
 __device__ __forceinline__ void butterfly(float (&y)[kGroup]) {
 #pragma unroll
@@ -73,7 +74,8 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Reconstruct one group into y (float32, already scaled).
+// Reconstruct one group into y (float32, already scaled), generic form:
+// per-element level lookup, then the 7 butterfly stages.
 template <int SB>
 __device__ __forceinline__ void reconstruct(const uint32_t (&words)[4 * SB], uint16_t n16,
                                             const float* lut, float (&y)[kGroup]) {
@@ -85,46 +87,195 @@ __device__ __forceinline__ void reconstruct(const uint32_t (&words)[4 * SB], uin
   for (int j = 0; j < kGroup; ++j) y[j] *= s;
 }
 
+// Butterfly stages with pair distance >= h0 (the earlier ones are done).
+template <int H0>
+__device__ __forceinline__ void butterfly_from(float (&y)[kGroup]) {
+#pragma unroll
+  for (int h = H0; h < kGroup; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < kGroup; i += 2 * h) {
+#pragma unroll
+      for (int j = i; j < i + h; ++j) {
+        const float a = y[j], b = y[j + h];
+        y[j] = a + b;
+        y[j + h] = a - b;
+      }
+    }
+  }
+}
+
+// Byte table: a packed byte holds E = 8 / SB consecutive indices (E = 4 at 2
+// bits, 2 at 4 bits).  Entry b is the unnormalised E-point Walsh-Hadamard
+// transform of the levels its indices select, so one table read replaces E
+// lookups and the first log2(E) butterfly stages.  The adds are the same
+// float32 operations, in the same order, as running those stages in
+// registers.
+template <int SB>
+struct ByteTable {
+  static constexpr int E = 8 / SB;
+  static __device__ __forceinline__ void fill(float* tab, const LevelTable& lv, int t) {
+    if (t >= 256) return;
+    float q[4];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = (t >> (SB * e)) & ((1 << SB) - 1);
+      q[e] = i < lv.n_levels ? lv.c[i] : 0.0f;
+    }
+    if constexpr (E == 4) {
+      const float a0 = q[0] + q[1], a1 = q[0] - q[1], a2 = q[2] + q[3], a3 = q[2] - q[3];
+      tab[4 * t] = a0 + a2;
+      tab[4 * t + 1] = a1 + a3;
+      tab[4 * t + 2] = a0 - a2;
+      tab[4 * t + 3] = a1 - a3;
+    } else {
+      tab[2 * t] = q[0] + q[1];
+      tab[2 * t + 1] = q[0] - q[1];
+    }
+  }
+  // Byte k (0..G*SB/8-1) of the group's packed bits.
+  static __device__ __forceinline__ uint32_t byte_at(const uint32_t (&words)[4 * SB], int k) {
+    return (words[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+  }
+  static __device__ __forceinline__ void decode(const uint32_t (&words)[4 * SB], const float* tab,
+                                                float (&y)[kGroup]) {
+#pragma unroll
+    for (int k = 0; k < kGroup / E; ++k) {
+      const uint32_t b = byte_at(words, k);
+      if constexpr (E == 4) {
+        const float4 v = *reinterpret_cast<const float4*>(tab + 4 * b);
+        y[4 * k] = v.x;
+        y[4 * k + 1] = v.y;
+        y[4 * k + 2] = v.z;
+        y[4 * k + 3] = v.w;
+      } else {
+        const float2 v = *reinterpret_cast<const float2*>(tab + 2 * b);
+        y[2 * k] = v.x;
+        y[2 * k + 1] = v.y;
+      }
+    }
+  }
+};
+
+template <int SB>
+struct TableSize {
+  static constexpr int floats = SB == 3 ? kMaxLevels : 256 * (8 / SB);
+};
+
+template <int SB>
+__device__ __forceinline__ void fill_table(float* tab, const LevelTable& lv, int t) {
+  if constexpr (SB == 3) {
+    if (t < kMaxLevels) tab[t] = t < lv.n_levels ? lv.c[t] : 0.0f;
+  } else {
+    ByteTable<SB>::fill(tab, lv, t);
+  }
+}
+
+template <int SB>
+__device__ __forceinline__ void reconstruct_fast(const uint32_t (&words)[4 * SB], uint16_t n16,
+                                                 const float* tab, float (&y)[kGroup]) {
+  if constexpr (SB == 3) {
+    reconstruct<SB>(words, n16, tab, y);
+  } else {
+    ByteTable<SB>::decode(words, tab, y);
+    butterfly_from<ByteTable<SB>::E>(y);
+    const float s = half_to_float(n16) * (1.0f / kGroup);
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) y[j] *= s;
+  }
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// Packed words and norm of every lane's group of batch bt (zeros past the
+// end: buffer loads outside the resource return 0).
+template <int SB>
+__device__ __forceinline__ void fetch_batch(const uint8_t* __restrict__ packed,
+                                            const uint16_t* __restrict__ norms, int64_t bt,
+                                            int nv, int lane, uint32_t (&words)[4 * SB],
+                                            uint16_t& n16) {
+#if defined(__HIP_DEVICE_COMPILE__)  // buffer builtins exist only for the GPU target
+  constexpr int PB = 16 * SB;  // packed bytes per group
+  const auto src = make_rsrc(packed + bt * kWave * PB, nv * PB);
+#pragma unroll
+  for (int i = 0; i < SB; ++i) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(src, lane * PB + 16 * i, 0, 0);
+    words[4 * i] = v.x;
+    words[4 * i + 1] = v.y;
+    words[4 * i + 2] = v.z;
+    words[4 * i + 3] = v.w;
+  }
+  const auto nsrc = make_rsrc(norms + bt * kWave, nv * 2);
+  n16 = __builtin_amdgcn_raw_buffer_load_b16(nsrc, lane * 2, 0, 0);
+#endif
+}
+
+__device__ __forceinline__ void store16(const uint4& v, __amdgpu_buffer_rsrc_t dst, uint32_t voff,
+                                        uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(w, dst, voff, soff, 0);
+#endif
+}
+
 // Fast path: cols % 128 == 0, so group g's output is 128 contiguous values.
+// The next batch's packed words and norm are loaded into registers while the
+// current batch is computed.  Stores go through a per-batch buffer resource
+// so the lanes past the end of the last batch are dropped by the hardware.
 template <int SB, bool BF16OUT>
-__global__ void __launch_bounds__(kBlock)
+__global__ void __launch_bounds__(kBlock, 2)
 dequantize_contig(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
                   int64_t n_groups, LevelTable lv, uint8_t* __restrict__ out) {
   constexpr int OB = BF16OUT ? 2 : 4;        // output bytes per element
+  constexpr int GOB = kGroup * OB;           // output bytes per group
   constexpr int PB = 32 * OB;                // bytes per group per phase
   constexpr int CPP = PB / 16;               // 16-byte chunks per group per phase
   constexpr int GPB = 256 / PB;              // groups per 256-byte LDS row
+  constexpr int GPI = kWave / CPP;           // groups per store instruction
   constexpr int WAVE_BYTES = kWave * PB;
   constexpr int NI = WAVE_BYTES / 1024;      // store instructions per phase
-  __shared__ float lut[kMaxLevels];
+  __shared__ __attribute__((aligned(16))) float tab[TableSize<SB>::floats];
   __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * WAVE_BYTES];
-  if (threadIdx.x < kMaxLevels) lut[threadIdx.x] = threadIdx.x < lv.n_levels ? lv.c[threadIdx.x] : 0.0f;
+  fill_table<SB>(tab, lv, threadIdx.x);
   __syncthreads();
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   uint8_t* const buf = lds + wave * WAVE_BYTES;
   const int64_t n_batches = (n_groups + kWave - 1) / kWave;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
+  int64_t batch = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  if (batch >= n_batches) return;
+
+  // LDS write: this lane's chunk c of a phase goes to slot c ^ swz_w.
   const int swz_w = (lane / GPB) & (CPP - 1);
+  // Store instruction i moves groups GPI*i + lane/CPP, chunk lane % CPP.
+  const int gq = lane / CPP, cc = lane % CPP;
+  const uint32_t st_lane = static_cast<uint32_t>(gq * GOB + 16 * cc);
 
-  for (int64_t batch = static_cast<int64_t>(blockIdx.x) * kWaves + wave; batch < n_batches;
-       batch += stride) {
-    const int64_t g0 = batch * kWave;
-    const int64_t g = g0 + lane;
-    const bool valid = g < n_groups;
+  auto nvalid = [&](int64_t bt) __attribute__((always_inline)) {
+    const int64_t left = n_groups - bt * kWave;
+    return static_cast<int>(left < kWave ? left : kWave);
+  };
+  uint32_t nwords[4 * SB];
+  uint16_t nn16 = 0;
+  fetch_batch<SB>(packed, norms, batch, nvalid(batch), lane, nwords, nn16);
+  for (;;) {
     uint32_t words[4 * SB];
-    uint16_t n16 = 0;
-    if (valid) {
-      load_indices<SB>(packed, g, words);
-      n16 = norms[g];
-    } else {
 #pragma unroll
-      for (int i = 0; i < 4 * SB; ++i) words[i] = 0;
-    }
-    float y[kGroup];
-    reconstruct<SB>(words, n16, lut, y);
+    for (int i = 0; i < 4 * SB; ++i) words[i] = nwords[i];
+    const uint16_t n16 = nn16;
+    const int64_t next = batch + stride;
+    const int nv = nvalid(batch);
+    if (next < n_batches) fetch_batch<SB>(packed, norms, next, nvalid(next), lane, nwords, nn16);
 
+    float y[kGroup];
+    reconstruct_fast<SB>(words, n16, tab, y);
+
+    const auto dst = make_rsrc(out + batch * kWave * GOB, nv * GOB);
 #pragma unroll
     for (int ph = 0; ph < 4; ++ph) {
       // Scatter this lane's 32 values of the phase into the swizzled buffer.
@@ -147,14 +298,14 @@ dequantize_contig(const uint8_t* __restrict__ packed, const uint16_t* __restrict
       // Gather 16-byte chunks so consecutive lanes write consecutive bytes.
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const int slot = i * kWave + lane;
-        const int gs = slot / CPP, c = slot % CPP;
+        const int gs = GPI * i + gq;
         const int sw = (gs / GPB) & (CPP - 1);
-        const uint4 v = *reinterpret_cast<const uint4*>(buf + gs * PB + 16 * (c ^ sw));
-        if (g0 + gs < n_groups)
-          *reinterpret_cast<uint4*>(out + (g0 + gs) * (kGroup * OB) + ph * PB + 16 * c) = v;
+        const uint4 v = *reinterpret_cast<const uint4*>(buf + gs * PB + 16 * (cc ^ sw));
+        store16(v, dst, st_lane + ph * PB, static_cast<uint32_t>(GPI * i * GOB));
       }
     }
+    batch = next;
+    if (batch >= n_batches) break;
   }
 }
 
@@ -164,8 +315,8 @@ template <int SB, bool BF16OUT>
 __global__ void __launch_bounds__(kBlock)
 dequantize_ragged(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
                   int64_t rows, int64_t cols, LevelTable lv, uint8_t* __restrict__ out) {
-  __shared__ float lut[kMaxLevels];
-  if (threadIdx.x < kMaxLevels) lut[threadIdx.x] = threadIdx.x < lv.n_levels ? lv.c[threadIdx.x] : 0.0f;
+  __shared__ __attribute__((aligned(16))) float tab[TableSize<SB>::floats];
+  fill_table<SB>(tab, lv, threadIdx.x);
   __syncthreads();
   const int64_t ngr = (cols + kGroup - 1) / kGroup;
   const int64_t g = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
@@ -175,7 +326,7 @@ dequantize_ragged(const uint8_t* __restrict__ packed, const uint16_t* __restrict
   uint32_t words[4 * SB];
   load_indices<SB>(packed, g, words);
   float y[kGroup];
-  reconstruct<SB>(words, norms[g], lut, y);
+  reconstruct_fast<SB>(words, norms[g], tab, y);
   const int64_t base = row * cols + col0;
 #pragma unroll
   for (int j = 0; j < kGroup; ++j) {
@@ -195,8 +346,7 @@ hipError_t launch_sb(const uint8_t* packed, const uint16_t* norms, int64_t rows,
   if (cols % kGroup == 0) {
     const int64_t n_groups = rows * (cols / kGroup);
     const int64_t n_batches = (n_groups + kWave - 1) / kWave;
-    const int64_t want = (n_batches + kWaves - 1) / kWaves;
-    const int blocks = static_cast<int>(want < 4096 ? want : 4096);
+    const int blocks = persistent_blocks((n_batches + kWaves - 1) / kWaves, kBlocksPerCu);
     hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT>), dim3(blocks), dim3(kBlock), 0, s, packed,
                        norms, n_groups, lv, ob);
   } else {

@@ -128,6 +128,23 @@ int hip_status(hipError_t e, const char* what) {
 
 }  // namespace
 
+namespace cq {
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+}  // namespace cq
+
 extern "C" {
 
 const char* cq_version(void) { return "libcq 0.1 (gfx950)"; }

@@ -49,6 +49,7 @@ namespace kq {
 
 constexpr int kWaves = 4;
 constexpr int kBlock = kWaves * kWave;
+constexpr int kBlocksPerCu = 2;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -195,14 +196,24 @@ __device__ __forceinline__ void store_group(uint8_t* __restrict__ packed, uint16
   norms[g] = n16;
 }
 
-// Stage 1 from one 32-bit word holding elements 2i (low half) and 2i+1.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// acc + a.lo * a.lo + a.hi * a.hi for a packed bf16 pair, in float32
+// (v_dot2c_f32_bf16): the sum of squares of two elements in one instruction,
+// straight from the packed pair.  The bf16 squares are exact in float32.
+__device__ __forceinline__ float sumsq2_bf16(uint32_t a, float acc) {
+  const bf16x2_t v = __builtin_bit_cast(bf16x2_t, a);
+  return __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
+}
+
+// Stage 1 from one 32-bit word holding elements 2i (low half) and 2i+1, plus
+// the pair's contribution to the sum of squares.
 __device__ __forceinline__ void stage1_bf16(uint32_t u, float& s, float& d, float& acc) {
   const float a = __builtin_bit_cast(float, u << 16);
   const float b = __builtin_bit_cast(float, u & 0xFFFF0000u);
   s = a + b;
   d = a - b;
-  acc = __builtin_fmaf(a, a, acc);
-  acc = __builtin_fmaf(b, b, acc);
+  acc = sumsq2_bf16(u, acc);
 }
 
 // Buffer resource over [base, base + bytes): loads past the end return zero
@@ -406,10 +417,10 @@ hipError_t launch_l(const void* w, int64_t rows, int64_t cols, const QuantParams
   if (cols % kGroup == 0) {
     const int64_t n_groups = rows * (cols / kGroup);
     const int64_t n_batches = (n_groups + kWave - 1) / kWave;
-    // Enough resident waves to keep every CU busy; each wave loops over
-    // batches so the next load overlaps the current arithmetic.
-    const int64_t want = (n_batches + kWaves - 1) / kWaves;
-    const int blocks = static_cast<int>(want < 2048 ? want : 2048);
+    // One resident grid (two blocks per CU, the occupancy the kernel is
+    // built for); each wave loops over batches so the next batch's DMA
+    // overlaps the current arithmetic.
+    const int blocks = persistent_blocks((n_batches + kWaves - 1) / kWaves, kBlocksPerCu);
     hipLaunchKernelGGL((quantize_contig<L, BF16>), dim3(blocks), dim3(kBlock), 0, s, wb, n_groups,
                        p, packed, norms);
   } else {
