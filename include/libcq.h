@@ -140,14 +140,38 @@ int cq_dequantize(const uint8_t* packed, const uint16_t* norms, int64_t rows,
  * once per group and dotted with the looked-up levels: because the
  * orthonormal Hadamard matrix is symmetric and its own inverse,
  * x_g . W_hat_g = (norm / G) * <H x_g, levels[idx]> with H the +-1
- * Sylvester-Hadamard matrix.  float32 accumulation.  The library takes
- * batch*k*4 bytes of
- * stream-ordered device memory (hipMallocAsync / hipFreeAsync on `stream`)
- * for the rotated activations. */
+ * Sylvester-Hadamard matrix.  float32 accumulation in a fixed order
+ * (deterministic).  Same as cq_dequant_matvec_many with one matrix, whose
+ * notes on workspace memory apply. */
 int cq_dequant_matvec(const uint8_t* packed, const uint16_t* norms, int64_t n_out,
                       int64_t k, int bits, int group_size, const float* levels,
                       int n_levels, const float* x, int64_t batch, float* y,
                       void* stream);
+
+/* One matrix of cq_dequant_matvec_many (all pointers device pointers):
+ * y [batch][n_out] = x [batch][k] . W_hat^T with W given by packed/norms as
+ * cq_quantize produced them for rows = n_out, cols = k. */
+typedef struct {
+  const uint8_t* packed;
+  const uint16_t* norms;
+  int64_t n_out;
+  int64_t k;
+  const float* x;
+  float* y;
+} cq_matvec_desc;
+
+/* cq_dequant_matvec for n matrices (descs: host array) that share bits,
+ * levels and batch: the whole set runs as one activation-rotation launch and
+ * one product launch per 8 batch rows, e.g. every weight matrix of a model
+ * for one decode step ("How Needle 2 Model Compresses to a Single Binary",
+ * section Stage 3: the runtime decodes the packed tensors on the fly).
+ * Each descriptor is validated as cq_dequant_matvec validates its arguments
+ * (the first failing one is reported; nothing is enqueued then).  Takes
+ * sum(batch*k)*4 bytes plus a small descriptor table of stream-ordered
+ * device memory (hipMallocAsync / hipFreeAsync on `stream`).  Results are
+ * deterministic (fixed reduction order). */
+int cq_dequant_matvec_many(int n, const cq_matvec_desc* descs, int bits, int group_size,
+                           const float* levels, int n_levels, int64_t batch, void* stream);
 
 /* Static description of a status code. */
 const char* cq_status_str(int status);

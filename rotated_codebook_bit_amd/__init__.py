@@ -16,7 +16,7 @@ import numpy as np
 
 __all__ = [
     "TERNARY", "GROUP", "CQError", "lib", "storage_bits", "n_levels", "layout",
-    "model_bytes", "codebook", "quantize", "dequantize", "dequant_matvec",
+    "model_bytes", "codebook", "quantize", "dequantize", "dequant_matvec", "dequant_matvec_many",
 ]
 
 TERNARY = 158
@@ -34,6 +34,12 @@ class CQError(RuntimeError):
     def __init__(self, func: str, status: int, detail: str):
         super().__init__(f"{func}: {detail} (status {status})")
         self.status = status
+
+
+class MatvecDesc(ctypes.Structure):
+    """cq_matvec_desc: one matrix of cq_dequant_matvec_many."""
+    _fields_ = [("packed", ctypes.c_void_p), ("norms", ctypes.c_void_p), ("n_out", ctypes.c_int64),
+                ("k", ctypes.c_int64), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
 
 
 def lib() -> ctypes.CDLL:
@@ -55,8 +61,10 @@ def lib() -> ctypes.CDLL:
                                     vp, i32, vp]
         L.cq_dequant_matvec.argtypes = [vp, vp, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_float),
                                         i32, vp, i64, vp, vp]
+        L.cq_dequant_matvec_many.argtypes = [i32, ctypes.POINTER(MatvecDesc), i32, i32,
+                                             ctypes.POINTER(ctypes.c_float), i32, i64, vp]
         for name in ("cq_layout", "cq_model_bytes", "cq_codebook", "cq_quantize", "cq_dequantize",
-                     "cq_dequant_matvec"):
+                     "cq_dequant_matvec", "cq_dequant_matvec_many"):
             getattr(L, name).restype = i32
         L.cq_status_str.argtypes = [i32]
         L.cq_status_str.restype = ctypes.c_char_p
@@ -205,3 +213,19 @@ def dequant_matvec(packed, norms, n_out: int, k: int, bits: int, levels, x, grou
                                                         group_size, lvp, lv.size, _ptr(x2), batch,
                                                         _ptr(y), _stream_ptr(stream)))
     return y
+
+
+def dequant_matvec_many(items, bits: int, levels, batch: int, group_size: int = GROUP, stream=None):
+    """Run y = x . W_hat^T for every (packed, norms, n_out, k, x, y) in items
+    as one call (the y tensors, float32 [batch, n_out], are written in place).
+    Returns the list of y tensors."""
+    n = len(items)
+    arr = (MatvecDesc * max(n, 1))()
+    for i, (packed, norms, n_out, k, x, y) in enumerate(items):
+        arr[i] = MatvecDesc(packed.data_ptr() if packed.numel() else 0,
+                            norms.data_ptr() if norms.numel() else 0, n_out, k,
+                            x.data_ptr() if x.numel() else 0, y.data_ptr() if y.numel() else 0)
+    lv, lvp = _levels_arg(levels)
+    _check("cq_dequant_matvec_many", lib().cq_dequant_matvec_many(n, arr, bits, group_size, lvp, lv.size,
+                                                                  batch, _stream_ptr(stream)))
+    return [it[5] for it in items]

@@ -52,12 +52,44 @@ hipError_t launch_dequantize(const uint8_t* packed, const uint16_t* norms,
                              const LevelTable& lv, void* out, bool bf16_out,
                              hipStream_t stream);
 
-hipError_t launch_rotate_rows(const float* x, int64_t n_groups, float* xr,
-                              hipStream_t stream);
+// One matrix of a dequant-matvec call (device-side descriptor).
+struct MatvecDesc {
+  const uint8_t* packed;  // [n_out][k / 128][128 * sbits / 8]
+  const uint16_t* norms;  // [n_out][k / 128]
+  const float* x;         // [batch][k]
+  float* y;               // [batch][n_out]
+  int64_t n_out;
+  int64_t k;
+  int64_t xr_offset;      // float offset of this matrix's rotated x in the workspace
+};
 
-hipError_t launch_matvec(const uint8_t* packed, const uint16_t* norms,
-                         int64_t n_out, int64_t k, int sbits,
-                         const LevelTable& lv, const float* xr, int64_t batch,
-                         float* y, hipStream_t stream);
+// Descriptors are written to device memory by a small kernel that receives
+// them as kernel arguments, kDescPerInit at a time (no host-to-device copy,
+// so the call stays asynchronous).
+constexpr int kDescPerInit = 24;
+struct DescChunk {
+  MatvecDesc d[kDescPerInit];
+  int64_t gstart[kDescPerInit + 1];   // rotate-kernel group prefix
+  int64_t bstart0[kDescPerInit + 1];  // product-kernel block prefix, full batch chunks
+  int64_t bstart1[kDescPerInit + 1];  // same, for the last (partial) batch chunk
+  int count;                          // descriptors in this chunk
+  int first;                          // index of d[0] in the table
+  int last_chunk;                     // 1: also write the sentinel entries [count]
+};
+
+hipError_t launch_table_init(const DescChunk& c, MatvecDesc* table, int64_t* gstart,
+                             int64_t* bstart0, int64_t* bstart1, hipStream_t stream);
+
+// Rows per product-kernel block for a batch chunk of nb rows.
+int matvec_rows_per_block(int nb);
+
+hipError_t launch_rotate(const MatvecDesc* table, const int64_t* gstart, int n, int64_t total_groups,
+                         float* xr, hipStream_t stream);
+
+hipError_t launch_matvec(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks,
+                         int sbits, const LevelTable& lv, const float* xr, int64_t b0, int nb,
+                         hipStream_t stream);
+
+hipError_t launch_zero(float* y, int64_t count, hipStream_t stream);
 
 }  // namespace cq

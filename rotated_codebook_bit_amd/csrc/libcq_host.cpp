@@ -301,42 +301,105 @@ int cq_dequantize(const uint8_t* packed, const uint16_t* norms, int64_t rows, in
 int cq_dequant_matvec(const uint8_t* packed, const uint16_t* norms, int64_t n_out, int64_t k,
                       int bits, int group_size, const float* levels, int n_levels, const float* x,
                       int64_t batch, float* y, void* stream) {
+  const cq_matvec_desc d{packed, norms, n_out, k, x, y};
+  return cq_dequant_matvec_many(1, &d, bits, group_size, levels, n_levels, batch, stream);
+}
+
+int cq_dequant_matvec_many(int n, const cq_matvec_desc* descs, int bits, int group_size,
+                           const float* levels, int n_levels, int64_t batch, void* stream) {
   g_last_error[0] = 0;
   int L, rc;
   if ((rc = check_bits(bits, false, &L))) return rc;
-  if (n_out < 0 || k < 0) return fail(CQ_ERR_ARG, "negative size");
+  if (n < 0) return fail(CQ_ERR_ARG, "n < 0");
   if (batch < 1) return fail(CQ_ERR_ARG, "batch must be >= 1");
   if ((rc = check_group(group_size, true))) return rc;
-  if (k % group_size) return fail(CQ_ERR_UNSUPPORTED, "k=%lld is not a multiple of %d", (long long)k, group_size);
   if ((rc = check_levels(levels, n_levels, L))) return rc;
-  if (n_out == 0) return CQ_OK;
-  if (!y) return fail(CQ_ERR_NULL, "y is NULL");
-  if (!aligned(y, 16)) return fail(CQ_ERR_ALIGN, "y needs 16-byte alignment");
+  if (n == 0) return CQ_OK;
+  if (!descs) return fail(CQ_ERR_NULL, "descs is NULL");
+  const int sb = storage_bits(bits);
+  for (int i = 0; i < n; ++i) {
+    const cq_matvec_desc& d = descs[i];
+    if (d.n_out < 0 || d.k < 0) return fail(CQ_ERR_ARG, "matrix %d: negative size", i);
+    if (d.k % group_size)
+      return fail(CQ_ERR_UNSUPPORTED, "matrix %d: k=%lld is not a multiple of %d", i, (long long)d.k,
+                  group_size);
+    if (d.n_out == 0) continue;
+    if (!d.y) return fail(CQ_ERR_NULL, "matrix %d: y is NULL", i);
+    if (!aligned(d.y, 16)) return fail(CQ_ERR_ALIGN, "matrix %d: y needs 16-byte alignment", i);
+    if (d.k == 0) continue;
+    if (!d.packed || !d.norms || !d.x) return fail(CQ_ERR_NULL, "matrix %d: packed/norms/x is NULL", i);
+    if (!aligned(d.x, 16) || !aligned(d.packed, 16) || !aligned(d.norms, 2))
+      return fail(CQ_ERR_ALIGN, "matrix %d: x, packed need 16-byte, norms 2-byte alignment", i);
+    const int64_t ng = d.n_out * (d.k / group_size);
+    const size_t y_bytes = static_cast<size_t>(batch * d.n_out) * 4;
+    const size_t pk_bytes = static_cast<size_t>(ng) * group_size * sb / 8;
+    if (overlap(d.y, y_bytes, d.packed, pk_bytes) || overlap(d.y, y_bytes, d.norms, ng * 2) ||
+        overlap(d.y, y_bytes, d.x, static_cast<size_t>(batch * d.k) * 4))
+      return fail(CQ_ERR_ARG, "matrix %d: input and output buffers overlap", i);
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const cq::LevelTable lv = make_table(levels, L);
-  if (k == 0) {  // empty rows: the kernel writes zeros and reads nothing else
-    return hip_status(cq::launch_matvec(nullptr, nullptr, n_out, 0, storage_bits(bits), lv, nullptr,
-                                        batch, y, s),
-                      "matvec launch");
+
+  // Matrices with k = 0 produce zeros; the rest go to the descriptor table.
+  std::vector<cq::MatvecDesc> act;
+  for (int i = 0; i < n; ++i) {
+    const cq_matvec_desc& d = descs[i];
+    if (d.n_out == 0) continue;
+    if (d.k == 0) {
+      if ((rc = hip_status(cq::launch_zero(d.y, batch * d.n_out, s), "zero launch"))) return rc;
+      continue;
+    }
+    act.push_back(cq::MatvecDesc{d.packed, d.norms, d.x, d.y, d.n_out, d.k, 0});
   }
-  if (!packed || !norms || !x) return fail(CQ_ERR_NULL, "packed/norms/x is NULL");
-  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(norms, 2))
-    return fail(CQ_ERR_ALIGN, "x, packed need 16-byte, norms 2-byte alignment");
-  const int64_t ng = n_out * (k / group_size);
-  const size_t y_bytes = static_cast<size_t>(batch * n_out) * 4;
-  const size_t pk_bytes = static_cast<size_t>(ng) * group_size * storage_bits(bits) / 8;
-  if (overlap(y, y_bytes, packed, pk_bytes) || overlap(y, y_bytes, norms, ng * 2) ||
-      overlap(y, y_bytes, x, static_cast<size_t>(batch * k) * 4))
-    return fail(CQ_ERR_ARG, "input and output buffers overlap");
-  float* xr = nullptr;
-  const size_t xr_bytes = static_cast<size_t>(batch * k) * sizeof(float);
-  if ((rc = hip_status(hipMallocAsync(reinterpret_cast<void**>(&xr), xr_bytes, s), "workspace alloc")))
+  if (act.empty()) return CQ_OK;
+  const int na = static_cast<int>(act.size());
+  // Batch rows go through the product kernel in chunks of at most 8.
+  const int nb_full = static_cast<int>(batch < 8 ? batch : 8);
+  const int nb_last = static_cast<int>(batch - 8 * ((batch - 1) / 8));
+  const int rb0 = cq::matvec_rows_per_block(nb_full), rb1 = cq::matvec_rows_per_block(nb_last);
+  std::vector<int64_t> gstart(na + 1), bstart0(na + 1), bstart1(na + 1);
+  int64_t xr_floats = 0;
+  for (int i = 0; i < na; ++i) {
+    act[i].xr_offset = xr_floats;
+    xr_floats += batch * act[i].k;
+    gstart[i + 1] = gstart[i] + batch * (act[i].k / group_size);
+    bstart0[i + 1] = bstart0[i] + (act[i].n_out + rb0 - 1) / rb0;
+    bstart1[i + 1] = bstart1[i] + (act[i].n_out + rb1 - 1) / rb1;
+  }
+  auto round_up = [](size_t v) { return (v + 255) & ~size_t(255); };
+  const size_t table_b = round_up(na * sizeof(cq::MatvecDesc));
+  const size_t start_b = round_up((na + 1) * sizeof(int64_t));
+  const size_t ws_bytes = table_b + 3 * start_b + static_cast<size_t>(xr_floats) * sizeof(float);
+  uint8_t* ws = nullptr;
+  if ((rc = hip_status(hipMallocAsync(reinterpret_cast<void**>(&ws), ws_bytes, s), "workspace alloc")))
     return rc;
-  rc = hip_status(cq::launch_rotate_rows(x, batch * (k / group_size), xr, s), "rotate launch");
-  if (!rc)
-    rc = hip_status(cq::launch_matvec(packed, norms, n_out, k, storage_bits(bits), lv, xr, batch, y, s),
+  auto* table = reinterpret_cast<cq::MatvecDesc*>(ws);
+  auto* g_dev = reinterpret_cast<int64_t*>(ws + table_b);
+  auto* b0_dev = reinterpret_cast<int64_t*>(ws + table_b + start_b);
+  auto* b1_dev = reinterpret_cast<int64_t*>(ws + table_b + 2 * start_b);
+  auto* xr = reinterpret_cast<float*>(ws + table_b + 3 * start_b);
+  for (int first = 0; first < na && !rc; first += cq::kDescPerInit) {
+    cq::DescChunk c{};
+    c.first = first;
+    c.count = na - first < cq::kDescPerInit ? na - first : cq::kDescPerInit;
+    c.last_chunk = first + c.count == na ? 1 : 0;
+    for (int i = 0; i < c.count; ++i) c.d[i] = act[first + i];
+    for (int i = 0; i < c.count + c.last_chunk; ++i) {
+      c.gstart[i] = gstart[first + i];
+      c.bstart0[i] = bstart0[first + i];
+      c.bstart1[i] = bstart1[first + i];
+    }
+    rc = hip_status(cq::launch_table_init(c, table, g_dev, b0_dev, b1_dev, s), "table launch");
+  }
+  if (!rc) rc = hip_status(cq::launch_rotate(table, g_dev, na, gstart[na], xr, s), "rotate launch");
+  for (int64_t b0 = 0; b0 < batch && !rc; b0 += 8) {
+    const int nb = static_cast<int>(batch - b0 < 8 ? batch - b0 : 8);
+    const bool full = nb == nb_full;
+    rc = hip_status(cq::launch_matvec(table, full ? b0_dev : b1_dev, na, full ? bstart0[na] : bstart1[na],
+                                      sb, lv, xr, b0, nb, s),
                     "matvec launch");
-  int rc2 = hip_status(hipFreeAsync(xr, s), "workspace free");
+  }
+  const int rc2 = hip_status(hipFreeAsync(ws, s), "workspace free");
   return rc ? rc : rc2;
 }
 

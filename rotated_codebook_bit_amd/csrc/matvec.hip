@@ -1,4 +1,5 @@
-// CQ dequantize-matvec kernels for gfx950: y = x . W_hat^T.
+// CQ dequantize-matvec kernels for gfx950: y = x . W_hat^T for one or many
+// quantized matrices.
 //
 // The pages use the quantized weights in an ordinary forward product
 // ("Performance Differences Between 2-Bit and 4-Bit Quantization in Needle",
@@ -10,16 +11,21 @@
 // for every group g of a row
 //     x_g . W_hat_g = (norm_g / G) * < H x_g , levels[idx_g] >
 // with H the +-1 Sylvester matrix.  So the activations are rotated once per
-// (batch row, group) by rotate_rows, and the main kernel never applies a
-// per-weight inverse rotation: it looks the level up and accumulates.
+// (batch row, group) by rotate_kernel, and the product kernel never applies
+// a per-weight inverse rotation: it looks the levels up and accumulates.
 //
-// Main kernel mapping: a lane owns 16 consecutive columns of a 1024-column
-// tile and keeps the rotated activations of those columns (16 per batch row)
-// in registers; a wave handles RW rows, walking the tiles, and keeps RW x NB
-// per-lane partial sums.  The cross-lane reduction happens once per row at
-// the end.  Packed bits of 16 consecutive columns are 4 (2-bit), 6 (3-bit)
-// or 8 (4-bit) bytes, so one wave instruction reads 256-512 contiguous bytes
-// of a row.
+// Both kernels read a table of matrix descriptors in device memory, so any
+// number of matrices (a whole model's decode step) runs as two launches.
+//
+// Product kernel mapping: a block (4 waves) owns RB consecutive rows of one
+// matrix.  Thread t owns 16-column chunks t, t + 256, ... of the row (one
+// 4096-column pass per 256 chunks) and keeps the rotated activations of its
+// chunk in registers for the whole pass; for every row it loads the 4 (2-bit)
+// / 6 (3-bit) / 8 (4-bit) bytes of codes of its chunk (a wave instruction
+// reads 256-512 contiguous bytes of the row), decodes four (2-bit) or two
+// (4-bit) levels per LDS read from a byte table, and accumulates NB partial
+// sums per row.  The block reduces its RB x NB partials through LDS in a
+// fixed order, so results are deterministic.
 
 #include "cq_internal.h"
 
@@ -28,23 +34,43 @@ namespace km {
 
 constexpr int kWaves = 4;
 constexpr int kBlock = kWaves * kWave;
-constexpr int kRowsPerWave = 4;
-constexpr int kTile = 16 * kWave;  // columns per tile
+constexpr int kChunk = 16;              // columns per thread per pass
+constexpr int kPass = kChunk * kBlock;  // columns per pass (4096)
 
 __device__ __forceinline__ float half_to_float(uint16_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, h));
 }
 
-// xr[g][:] = H x[g][:] for n_groups consecutive 128-value groups.
+// Index of the descriptor whose [start[d], start[d+1]) range holds v
+// (start ascending, start[0] = 0, start[n] = total, v < total).
+__device__ __forceinline__ int find_desc(const int64_t* __restrict__ start, int n, int64_t v) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (start[mid] <= v)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+// xr[m][b][g][:] = H x[m][b][g][:] for every 128-value group of every
+// matrix's activations; one thread per group.
 __global__ void __launch_bounds__(kBlock)
-rotate_rows_kernel(const float* __restrict__ x, int64_t n_groups, float* __restrict__ xr) {
+rotate_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restrict__ gstart, int n,
+              float* __restrict__ xr) {
   const int64_t g = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-  if (g >= n_groups) return;
+  if (g >= gstart[n]) return;
+  const int d = find_desc(gstart, n, g);
+  const MatvecDesc& m = table[d];
+  const int64_t local = g - gstart[d];  // group within the matrix's batch*k/128
+  const float* src = m.x + local * kGroup;
+  float* dst = xr + m.xr_offset + local * kGroup;
   float y[kGroup];
-  const float4* src = reinterpret_cast<const float4*>(x + g * kGroup);
 #pragma unroll
   for (int i = 0; i < kGroup / 4; ++i) {
-    const float4 v = src[i];
+    const float4 v = reinterpret_cast<const float4*>(src)[i];
     y[4 * i] = v.x;
     y[4 * i + 1] = v.y;
     y[4 * i + 2] = v.z;
@@ -62,21 +88,15 @@ rotate_rows_kernel(const float* __restrict__ x, int64_t n_groups, float* __restr
       }
     }
   }
-  float4* dst = reinterpret_cast<float4*>(xr + g * kGroup);
 #pragma unroll
-  for (int i = 0; i < kGroup / 4; ++i) dst[i] = make_float4(y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]);
+  for (int i = 0; i < kGroup / 4; ++i)
+    reinterpret_cast<float4*>(dst)[i] = make_float4(y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
-}
-
-// Packed bits of the 16 columns starting at column c0 (c0 % 16 == 0) of a
+// Packed codes of the 16 columns starting at column c0 (c0 % 16 == 0) of a
 // row, as a 64-bit value with column c0+e at bits [SB*e, SB*e + SB).
 template <int SB>
-__device__ __forceinline__ uint64_t load_bits16(const uint8_t* __restrict__ row_ptr, int64_t c0) {
+__device__ __forceinline__ uint64_t load_codes16(const uint8_t* __restrict__ row_ptr, int64_t c0) {
   if constexpr (SB == 2) {
     return *reinterpret_cast<const uint32_t*>(row_ptr + c0 / 4);
   } else if constexpr (SB == 4) {
@@ -90,34 +110,86 @@ __device__ __forceinline__ uint64_t load_bits16(const uint8_t* __restrict__ row_
   }
 }
 
-template <int SB, int NB>
+// Level table in LDS.  2 bits: entry b (a code byte) holds the 4 levels its
+// four 2-bit codes select; 4 bits: entry b holds the 2 levels of its two
+// nibbles; 3 bits: plain 8-entry table.
+template <int SB>
+struct Levels {
+  static constexpr int floats = SB == 2 ? 1024 : (SB == 4 ? 512 : kMaxLevels);
+  static __device__ __forceinline__ float lev(const LevelTable& lv, int i) {
+    return i < lv.n_levels ? lv.c[i] : 0.0f;
+  }
+  static __device__ __forceinline__ void fill(float* tab, const LevelTable& lv, int t) {
+    if constexpr (SB == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tab[4 * t + e] = lev(lv, (t >> (2 * e)) & 3);
+    } else if constexpr (SB == 4) {
+      tab[2 * t] = lev(lv, t & 15);
+      tab[2 * t + 1] = lev(lv, t >> 4);
+    } else {
+      if (t < kMaxLevels) tab[t] = lev(lv, t);
+    }
+  }
+  // Levels of the 16 codes into v[16].
+  static __device__ __forceinline__ void decode(uint64_t codes, const float* tab, float (&v)[16]) {
+    if constexpr (SB == 2) {
+      const uint32_t c = static_cast<uint32_t>(codes);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 f = *reinterpret_cast<const float4*>(tab + 4 * ((c >> (8 * q)) & 0xFFu));
+        v[4 * q] = f.x;
+        v[4 * q + 1] = f.y;
+        v[4 * q + 2] = f.z;
+        v[4 * q + 3] = f.w;
+      }
+    } else if constexpr (SB == 4) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float2 f = *reinterpret_cast<const float2*>(tab + 2 * ((codes >> (8 * q)) & 0xFFu));
+        v[2 * q] = f.x;
+        v[2 * q + 1] = f.y;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] = tab[(codes >> (3 * e)) & 7u];
+    }
+  }
+};
+
+// RB rows x NB batch rows per block; RB * NB <= 32 keeps the accumulators
+// and the activations of a chunk (16 * NB) in registers.
+template <int SB, int NB, int RB>
 __global__ void __launch_bounds__(kBlock)
-matvec_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms, int64_t n_out,
-              int64_t k, LevelTable lv, const float* __restrict__ xr, int64_t batch, int64_t b0,
-              float* __restrict__ y) {
-  __shared__ float lut[kMaxLevels];
-  if (threadIdx.x < kMaxLevels) lut[threadIdx.x] = threadIdx.x < lv.n_levels ? lv.c[threadIdx.x] : 0.0f;
+matvec_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restrict__ bstart, int n,
+              LevelTable lv, const float* __restrict__ xr, int64_t b0) {
+  __shared__ __attribute__((aligned(16))) float tab[Levels<SB>::floats];
+  __shared__ float red[RB * NB][kBlock + 1];
+  Levels<SB>::fill(tab, lv, threadIdx.x);
   __syncthreads();
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWaves + threadIdx.x / kWave;
-  const int64_t r0 = wave * kRowsPerWave;
-  if (r0 >= n_out) return;
+
+  const int64_t blk = blockIdx.x;
+  const int d = find_desc(bstart, n, blk);
+  const MatvecDesc& m = table[d];
+  const int64_t n_out = m.n_out, k = m.k;
+  const int64_t row0 = (blk - bstart[d]) * RB;
   const int64_t row_bytes = k * SB / 8;
   const int64_t ngr = k / kGroup;
+  const float* x_rot = xr + m.xr_offset;
+  const int t = threadIdx.x;
 
-  float acc[kRowsPerWave][NB];
+  float acc[RB][NB];
 #pragma unroll
-  for (int r = 0; r < kRowsPerWave; ++r)
+  for (int r = 0; r < RB; ++r)
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[r][b] = 0.0f;
 
-  for (int64_t t0 = 0; t0 < k; t0 += kTile) {
-    const int64_t c0 = t0 + 16 * lane;
+  for (int64_t p0 = 0; p0 < k; p0 += kPass) {
+    const int64_t c0 = p0 + kChunk * t;
     if (c0 < k) {
       float xv[NB][16];
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const float4* src = reinterpret_cast<const float4*>(xr + (b0 + b) * k + c0);
+        const float4* src = reinterpret_cast<const float4*>(x_rot + (b0 + b) * k + c0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float4 v = src[i];
@@ -127,88 +199,140 @@ matvec_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ n
           xv[b][4 * i + 3] = v.w;
         }
       }
+      // All rows' codes and norms are loaded before any is used, so a thread
+      // keeps RB loads in flight.  Rows past the end re-read the last row;
+      // their sums are never stored.
+      uint64_t codes[RB];
+      float scale[RB];
 #pragma unroll
-      for (int r = 0; r < kRowsPerWave; ++r) {
-        const int64_t row = r0 + r;
-        if (row < n_out) {
-          const uint64_t bits = load_bits16<SB>(packed + row * row_bytes, c0);
-          const float s = half_to_float(norms[row * ngr + c0 / kGroup]) * (1.0f / kGroup);
-          float part[NB];
+      for (int r = 0; r < RB; ++r) {
+        const int64_t row = row0 + r < n_out ? row0 + r : n_out - 1;
+        codes[r] = load_codes16<SB>(m.packed + row * row_bytes, c0);
+        scale[r] = half_to_float(m.norms[row * ngr + c0 / kGroup]) * (1.0f / kGroup);
+      }
 #pragma unroll
-          for (int b = 0; b < NB; ++b) part[b] = 0.0f;
+      for (int r = 0; r < RB; ++r) {
+        float v[16];
+        Levels<SB>::decode(codes[r], tab, v);
+        float part[NB];
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const float v = lut[(bits >> (SB * e)) & ((1u << SB) - 1u)];
+        for (int b = 0; b < NB; ++b) part[b] = 0.0f;
 #pragma unroll
-            for (int b = 0; b < NB; ++b) part[b] = __builtin_fmaf(v, xv[b][e], part[b]);
-          }
+        for (int e = 0; e < 16; ++e)
 #pragma unroll
-          for (int b = 0; b < NB; ++b) acc[r][b] = __builtin_fmaf(s, part[b], acc[r][b]);
-        }
+          for (int b = 0; b < NB; ++b) part[b] = __builtin_fmaf(v[e], xv[b][e], part[b]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[r][b] = __builtin_fmaf(scale[r], part[b], acc[r][b]);
       }
     }
   }
+
+  // Block reduction in a fixed order: thread t's partials go to column t of
+  // `red`; thread t then sums value t / 8 over columns 32*(t%8) .. 32*(t%8)+31
+  // and the 8 threads of a value combine by shuffles.
 #pragma unroll
-  for (int r = 0; r < kRowsPerWave; ++r) {
+  for (int r = 0; r < RB; ++r)
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const float v = wave_sum(acc[r][b]);
-      const int64_t row = r0 + r;
-      if (lane == 0 && row < n_out) y[(b0 + b) * n_out + row] = v;
-    }
+    for (int b = 0; b < NB; ++b) red[r * NB + b][t] = acc[r][b];
+  __syncthreads();
+  constexpr int V = RB * NB;  // values to reduce (<= 32)
+  const int vi = t / 8, part = t % 8;
+  float s = 0.0f;
+  if (vi < V) {
+#pragma unroll 8
+    for (int i = 0; i < 32; ++i) s += red[vi][32 * part + i];
+  }
+  s += __shfl_xor(s, 1, kWave);
+  s += __shfl_xor(s, 2, kWave);
+  s += __shfl_xor(s, 4, kWave);
+  if (vi < V && part == 0) {
+    const int r = vi / NB, b = vi % NB;
+    const int64_t row = row0 + r;
+    if (row < n_out) m.y[(b0 + b) * n_out + row] = s;
   }
 }
 
+// Writes a chunk of descriptors (received as kernel arguments) to the table.
+__global__ void table_init_kernel(DescChunk c, MatvecDesc* __restrict__ table,
+                                  int64_t* __restrict__ gstart, int64_t* __restrict__ bstart0,
+                                  int64_t* __restrict__ bstart1) {
+  const int i = threadIdx.x;
+  if (i < c.count) table[c.first + i] = c.d[i];
+  if (i < c.count + c.last_chunk) {
+    gstart[c.first + i] = c.gstart[i];
+    bstart0[c.first + i] = c.bstart0[i];
+    bstart1[c.first + i] = c.bstart1[i];
+  }
+}
+
+// y[i] = 0 for i < count (matrices whose k is 0: an empty sum).
+__global__ void __launch_bounds__(kBlock) zero_kernel(float* __restrict__ y, int64_t count) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  if (i < count) y[i] = 0.0f;
+}
+
 template <int SB, int NB>
-hipError_t launch_nb(const uint8_t* packed, const uint16_t* norms, int64_t n_out, int64_t k,
-                     const LevelTable& lv, const float* xr, int64_t batch, int64_t b0, float* y,
-                     hipStream_t s) {
-  const int64_t waves = (n_out + kRowsPerWave - 1) / kRowsPerWave;
-  const int blocks = static_cast<int>((waves + kWaves - 1) / kWaves);
-  hipLaunchKernelGGL((matvec_kernel<SB, NB>), dim3(blocks), dim3(kBlock), 0, s, packed, norms, n_out,
-                     k, lv, xr, batch, b0, y);
+hipError_t launch_nb(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks,
+                     const LevelTable& lv, const float* xr, int64_t b0, hipStream_t s) {
+  constexpr int RB = 32 / (NB <= 1 ? 1 : NB <= 2 ? 2 : NB <= 4 ? 4 : 8);
+  hipLaunchKernelGGL((matvec_kernel<SB, NB, RB>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock),
+                     0, s, table, bstart, n, lv, xr, b0);
   return hipGetLastError();
 }
 
 template <int SB>
-hipError_t launch_sb(const uint8_t* packed, const uint16_t* norms, int64_t n_out, int64_t k,
-                     const LevelTable& lv, const float* xr, int64_t batch, float* y, hipStream_t s) {
-  for (int64_t b0 = 0; b0 < batch; b0 += 8) {
-    const int64_t nb = batch - b0 < 8 ? batch - b0 : 8;
-    hipError_t e;
-    switch (nb) {
-      case 1: e = launch_nb<SB, 1>(packed, norms, n_out, k, lv, xr, batch, b0, y, s); break;
-      case 2: e = launch_nb<SB, 2>(packed, norms, n_out, k, lv, xr, batch, b0, y, s); break;
-      case 3: e = launch_nb<SB, 3>(packed, norms, n_out, k, lv, xr, batch, b0, y, s); break;
-      case 4: e = launch_nb<SB, 4>(packed, norms, n_out, k, lv, xr, batch, b0, y, s); break;
-      case 5: e = launch_nb<SB, 5>(packed, norms, n_out, k, lv, xr, batch, b0, y, s); break;
-      case 6: e = launch_nb<SB, 6>(packed, norms, n_out, k, lv, xr, batch, b0, y, s); break;
-      case 7: e = launch_nb<SB, 7>(packed, norms, n_out, k, lv, xr, batch, b0, y, s); break;
-      default: e = launch_nb<SB, 8>(packed, norms, n_out, k, lv, xr, batch, b0, y, s); break;
-    }
-    if (e != hipSuccess) return e;
+hipError_t launch_sb(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks,
+                     const LevelTable& lv, const float* xr, int64_t b0, int nb, hipStream_t s) {
+  switch (nb) {
+    case 1: return launch_nb<SB, 1>(table, bstart, n, blocks, lv, xr, b0, s);
+    case 2: return launch_nb<SB, 2>(table, bstart, n, blocks, lv, xr, b0, s);
+    case 3: return launch_nb<SB, 3>(table, bstart, n, blocks, lv, xr, b0, s);
+    case 4: return launch_nb<SB, 4>(table, bstart, n, blocks, lv, xr, b0, s);
+    case 5: return launch_nb<SB, 5>(table, bstart, n, blocks, lv, xr, b0, s);
+    case 6: return launch_nb<SB, 6>(table, bstart, n, blocks, lv, xr, b0, s);
+    case 7: return launch_nb<SB, 7>(table, bstart, n, blocks, lv, xr, b0, s);
+    default: return launch_nb<SB, 8>(table, bstart, n, blocks, lv, xr, b0, s);
   }
-  return hipSuccess;
 }
 
 }  // namespace km
 
-hipError_t launch_rotate_rows(const float* x, int64_t n_groups, float* xr, hipStream_t stream) {
-  if (n_groups <= 0) return hipSuccess;
-  const int blocks = static_cast<int>((n_groups + km::kBlock - 1) / km::kBlock);
-  hipLaunchKernelGGL(km::rotate_rows_kernel, dim3(blocks), dim3(km::kBlock), 0, stream, x, n_groups, xr);
+int matvec_rows_per_block(int nb) { return 32 / (nb <= 1 ? 1 : nb <= 2 ? 2 : nb <= 4 ? 4 : 8); }
+
+hipError_t launch_rotate(const MatvecDesc* table, const int64_t* gstart, int n, int64_t total_groups,
+                         float* xr, hipStream_t stream) {
+  if (total_groups <= 0) return hipSuccess;
+  const int64_t blocks = (total_groups + km::kBlock - 1) / km::kBlock;
+  hipLaunchKernelGGL(km::rotate_kernel, dim3(static_cast<unsigned>(blocks)), dim3(km::kBlock), 0,
+                     stream, table, gstart, n, xr);
   return hipGetLastError();
 }
 
-hipError_t launch_matvec(const uint8_t* packed, const uint16_t* norms, int64_t n_out, int64_t k,
-                         int sbits, const LevelTable& lv, const float* xr, int64_t batch, float* y,
+hipError_t launch_matvec(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks,
+                         int sbits, const LevelTable& lv, const float* xr, int64_t b0, int nb,
                          hipStream_t stream) {
+  if (blocks <= 0) return hipSuccess;
   switch (sbits) {
-    case 2: return km::launch_sb<2>(packed, norms, n_out, k, lv, xr, batch, y, stream);
-    case 3: return km::launch_sb<3>(packed, norms, n_out, k, lv, xr, batch, y, stream);
-    case 4: return km::launch_sb<4>(packed, norms, n_out, k, lv, xr, batch, y, stream);
+    case 2: return km::launch_sb<2>(table, bstart, n, blocks, lv, xr, b0, nb, stream);
+    case 3: return km::launch_sb<3>(table, bstart, n, blocks, lv, xr, b0, nb, stream);
+    case 4: return km::launch_sb<4>(table, bstart, n, blocks, lv, xr, b0, nb, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_table_init(const DescChunk& c, MatvecDesc* table, int64_t* gstart,
+                             int64_t* bstart0, int64_t* bstart1, hipStream_t stream) {
+  hipLaunchKernelGGL(km::table_init_kernel, dim3(1), dim3(kDescPerInit + 1), 0, stream, c, table, gstart,
+                     bstart0, bstart1);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(float* y, int64_t count, hipStream_t stream) {
+  if (count <= 0) return hipSuccess;
+  const int64_t blocks = (count + km::kBlock - 1) / km::kBlock;
+  hipLaunchKernelGGL(km::zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(km::kBlock), 0, stream,
+                     y, count);
+  return hipGetLastError();
 }
 
 }  // namespace cq

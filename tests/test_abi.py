@@ -188,3 +188,25 @@ def test_python_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(cq, "LIB_PATH", "/nonexistent/libcq.so")
     with pytest.raises(ImportError):
         cq.lib()
+
+
+def test_matvec_many_validation():
+    L = cq.lib()
+    lv, lp = _levels(4)
+    D = cq.MatvecDesc
+
+    def many(descs, n=None, batch=1, bits=2, nl=4):
+        arr = (D * max(len(descs), 1))(*descs)
+        return L.cq_dequant_matvec_many(len(descs) if n is None else n, arr if descs else None, bits, 128,
+                                        lp, nl, batch, None)
+
+    good = D(0x100000, 0x900000, 8, 256, 0x2100000, 0x3100000)
+    assert many([], n=0) == OK
+    assert many([good], n=-1) == E_ARG
+    assert L.cq_dequant_matvec_many(1, None, 2, 128, lp, 4, 1, None) == E_NULL
+    assert many([good], batch=0) == E_ARG
+    assert many([good, D(0x100000, 0x900000, 8, 200, 0x2100000, 0x3100000)]) == E_UNSUP
+    assert many([good, D(0x100000, 0x900000, 8, 256, 0x2100000, 0)]) == E_NULL
+    assert many([D(0x100000, 0x900000, 8, 256, 0x2100004, 0x3100000)]) == E_ALIGN
+    assert many([D(0x100000, 0x900000, 8, 256, 0x2100000, 0x2100000)]) == E_ARG   # y overlaps x
+    assert many([D(0, 0, 0, 256, 0, 0)]) == OK                                    # empty matrix

@@ -286,3 +286,49 @@ def test_matvec_bits_shapes(bits, n_out, k, levels):
                                torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16),
                                n_out, k, bits, lv, to_dev_f32(x)))
     check_matvec(y, y_ref, x, w_hat)
+
+
+@pytest.mark.parametrize("batch", [1, 2, 8, 9])
+def test_matvec_many(batch, levels):
+    """Several matrices of mixed shapes in one call, including an empty k, a
+    row count that is not a multiple of the rows per block, k = 128 and k
+    spanning three 4096-column passes."""
+    lv = levels[2]
+    shapes = [(100, 512), (37, 11008), (64, 128), (5, 0), (1, 4096), (300, 384)]
+    rng = np.random.default_rng(40 + batch)
+    items, refs = [], []
+    for n_out, k in shapes:
+        w = rng.standard_normal((n_out, k)) * 0.02
+        q = O.quantize(w, 2, lv) if k else None
+        x = rng.standard_normal((batch, k)).astype(np.float32)
+        if k:
+            w_hat = O.dequantize(q.packed, q.norm16, n_out, k, 2, lv)
+            p_dev = torch.from_numpy(q.packed.reshape(n_out, -1)).to(DEV)
+            n_dev = torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16)
+        else:
+            w_hat = np.zeros((n_out, 0))
+            p_dev = torch.zeros((n_out, 0), dtype=torch.uint8, device=DEV)
+            n_dev = torch.zeros((n_out, 0), dtype=torch.float16, device=DEV)
+        y = torch.full((batch, n_out), float("nan"), dtype=torch.float32, device=DEV)
+        items.append((p_dev, n_dev, n_out, k, to_dev_f32(x), y))
+        refs.append((x, w_hat))
+    say(f"matvec_many batch={batch}")
+    cq.dequant_matvec_many(items, 2, lv, batch)
+    for (x, w_hat), it in zip(refs, items):
+        y = host(it[5])
+        if w_hat.shape[1] == 0:
+            assert not y.any()
+        else:
+            check_matvec(y, x.astype(np.float64) @ w_hat.T, x, w_hat)
+
+
+def test_matvec_deterministic(matvec_weight, levels):
+    lv = levels[2]
+    _, q = matvec_weight
+    p_dev = torch.from_numpy(q.packed.reshape(11008, -1)).to(DEV)
+    n_dev = torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16)
+    x = to_dev_f32(W.matvec_x(8))
+    say("matvec determinism")
+    a = host(cq.dequant_matvec(p_dev, n_dev, 11008, 4096, 2, lv, x))
+    b = host(cq.dequant_matvec(p_dev, n_dev, 11008, 4096, 2, lv, x))
+    assert np.array_equal(a, b)
