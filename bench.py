@@ -12,7 +12,8 @@ One step is one pass of the whole path over the 7B-shaped model (bf16,
 Prints one JSON line.  `value` is model parameters per second over the whole
 step (wall clock, inputs resident in HBM).  Per-kernel times come from HIP
 events recorded on the stream the kernels run on.  The CPU oracle is timed on
-a bounded sample (one 4096x4096 tensor through the same three steps).
+a bounded sample (one transformer layer and the embedding, 333M params,
+through the same three steps).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        python bench.py --copy-only   (plain device copy, for counter scaling)
@@ -82,8 +83,10 @@ def copy_only(torch):
 
 
 def cpu_baseline() -> dict:
-    """The oracle as it stands, on one 4096x4096 tensor: quantize, dequantize,
-    matvec at batch 1 (the per-tensor work of one step)."""
+    """The oracle as it stands, on one transformer layer of the 7B-shaped
+    model plus its embedding (4 x 4096x4096, 2 x 4096x11008, 11008x4096,
+    32000x4096 = 333,447,168 params): quantize, dequantize and a batch-1
+    matvec per tensor, the per-tensor work of one step."""
     from oracle import cq_oracle as O
     from rotated_codebook_bit_amd import workloads as W
     try:
@@ -94,19 +97,26 @@ def cpu_baseline() -> dict:
     import rotated_codebook_bit_amd as cq
     levels = cq.codebook(BITS)
     rng = np.random.default_rng(0)
-    w = W.bf16_round((rng.standard_normal((4096, 4096)) * 0.02).astype(np.float32)).astype(np.float64)
-    x = rng.standard_normal((1, 4096))
-    t0 = time.perf_counter()
-    q = O.quantize(w, BITS, levels)
-    w_hat = O.dequantize(q.packed, q.norm16, 4096, 4096, BITS, levels)
-    _ = x @ w_hat.T
-    dt = time.perf_counter() - t0
-    params = w.size
+    shapes = W.llama7b_shapes()
+    layer = shapes[:7] + shapes[-1:]
+    params = 0
+    dt = 0.0
+    for r, c in layer:
+        w = W.bf16_round((rng.standard_normal((r, c)) * 0.02).astype(np.float32)).astype(np.float64)
+        x = rng.standard_normal((1, c))
+        t0 = time.perf_counter()
+        q = O.quantize(w, BITS, levels)
+        w_hat = O.dequantize(q.packed, q.norm16, r, c, BITS, levels)
+        _ = x @ w_hat.T
+        dt += time.perf_counter() - t0
+        params += w.size
+        del w, q, w_hat
     return {"value": round(params / dt / 1e9, 6), "unit": "Gparams/s", "cores": int(blas_threads),
             "kind": "oracle",
-            "sample": f"one 4096x4096 bf16-valued tensor (16.8M params) through quantize, "
-                      f"dequantize and a batch-1 matvec, float64 NumPy, {dt:.1f} s; "
-                      f"host cpu_count={os.cpu_count()}"}
+            "sample": f"one 7B-shaped transformer layer + the embedding ({params:,} bf16-valued "
+                      f"params, 8 tensors) "
+                      f"through quantize, dequantize and a batch-1 matvec, float64 NumPy, "
+                      f"{dt:.1f} s timed; host cpu_count={os.cpu_count()}"}
 
 
 def main():

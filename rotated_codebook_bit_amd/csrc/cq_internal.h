@@ -27,9 +27,19 @@ struct QuantParams {
 };
 
 struct LevelTable {
-  float c[kMaxLevels];  // float32 levels in N(0,1) units
+  float c[kMaxLevels];  // float32 levels in N(0,1) units; entries >= n_levels are 0
   int n_levels;
 };
+
+// lv.c[i] for a per-thread index i, by an unrolled select over constant
+// indices: the levels stay in scalar registers (a dynamic index into the
+// kernel-argument struct would become serialized memory loads).
+__device__ __forceinline__ float level_at(const LevelTable& lv, int i) {
+  float v = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kMaxLevels; ++j) v = (i == j) ? lv.c[j] : v;
+  return v;
+}
 
 // Compute units of the current device (cached per device).
 int device_cu_count();

@@ -26,7 +26,9 @@ namespace kd {
 
 constexpr int kWaves = 4;
 constexpr int kBlock = kWaves * kWave;
-constexpr int kBlocksPerCu = 2;
+// One resident block per CU measured faster than two for this store-heavy
+// kernel (fewer concurrent write streams).
+constexpr int kBlocksPerCu = 1;
 
 __device__ __forceinline__ void butterfly(float (&y)[kGroup]) {
 #pragma unroll
@@ -119,7 +121,7 @@ struct ByteTable {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int i = (t >> (SB * e)) & ((1 << SB) - 1);
-      q[e] = i < lv.n_levels ? lv.c[i] : 0.0f;
+      q[e] = level_at(lv, i);
     }
     if constexpr (E == 4) {
       const float a0 = q[0] + q[1], a1 = q[0] - q[1], a2 = q[2] + q[3], a3 = q[2] - q[3];
@@ -164,7 +166,7 @@ struct TableSize {
 template <int SB>
 __device__ __forceinline__ void fill_table(float* tab, const LevelTable& lv, int t) {
   if constexpr (SB == 3) {
-    if (t < kMaxLevels) tab[t] = t < lv.n_levels ? lv.c[t] : 0.0f;
+    if (t < kMaxLevels) tab[t] = level_at(lv, t);
   } else {
     ByteTable<SB>::fill(tab, lv, t);
   }

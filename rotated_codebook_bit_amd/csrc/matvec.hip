@@ -116,9 +116,7 @@ __device__ __forceinline__ uint64_t load_codes16(const uint8_t* __restrict__ row
 template <int SB>
 struct Levels {
   static constexpr int floats = SB == 2 ? 1024 : (SB == 4 ? 512 : kMaxLevels);
-  static __device__ __forceinline__ float lev(const LevelTable& lv, int i) {
-    return i < lv.n_levels ? lv.c[i] : 0.0f;
-  }
+  static __device__ __forceinline__ float lev(const LevelTable& lv, int i) { return level_at(lv, i); }
   static __device__ __forceinline__ void fill(float* tab, const LevelTable& lv, int t) {
     if constexpr (SB == 2) {
 #pragma unroll
@@ -166,89 +164,94 @@ matvec_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restrict__ 
   __shared__ float red[RB * NB][kBlock + 1];
   Levels<SB>::fill(tab, lv, threadIdx.x);
   __syncthreads();
-
-  const int64_t blk = blockIdx.x;
-  const int d = find_desc(bstart, n, blk);
-  const MatvecDesc& m = table[d];
-  const int64_t n_out = m.n_out, k = m.k;
-  const int64_t row0 = (blk - bstart[d]) * RB;
-  const int64_t row_bytes = k * SB / 8;
-  const int64_t ngr = k / kGroup;
-  const float* x_rot = xr + m.xr_offset;
   const int t = threadIdx.x;
+  const int64_t total = bstart[n];
 
-  float acc[RB][NB];
-#pragma unroll
-  for (int r = 0; r < RB; ++r)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[r][b] = 0.0f;
+  // Each block walks row blocks blk, blk + gridDim.x, ... (one when the grid
+  // covers them all, as launched).
+  for (int64_t blk = blockIdx.x; blk < total; blk += gridDim.x) {
+    const int d = find_desc(bstart, n, blk);
+    const MatvecDesc& m = table[d];
+    const int64_t n_out = m.n_out, k = m.k;
+    const int64_t row0 = (blk - bstart[d]) * RB;
+    const int64_t row_bytes = k * SB / 8;
+    const int64_t ngr = k / kGroup;
+    const float* x_rot = xr + m.xr_offset;
 
-  for (int64_t p0 = 0; p0 < k; p0 += kPass) {
-    const int64_t c0 = p0 + kChunk * t;
-    if (c0 < k) {
-      float xv[NB][16];
+    float acc[RB][NB];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const float4* src = reinterpret_cast<const float4*>(x_rot + (b0 + b) * k + c0);
+    for (int r = 0; r < RB; ++r)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float4 v = src[i];
-          xv[b][4 * i] = v.x;
-          xv[b][4 * i + 1] = v.y;
-          xv[b][4 * i + 2] = v.z;
-          xv[b][4 * i + 3] = v.w;
+      for (int b = 0; b < NB; ++b) acc[r][b] = 0.0f;
+
+    for (int64_t p0 = 0; p0 < k; p0 += kPass) {
+      const int64_t c0 = p0 + kChunk * t;
+      if (c0 < k) {
+        float xv[NB][16];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const float4* src = reinterpret_cast<const float4*>(x_rot + (b0 + b) * k + c0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float4 v = src[i];
+            xv[b][4 * i] = v.x;
+            xv[b][4 * i + 1] = v.y;
+            xv[b][4 * i + 2] = v.z;
+            xv[b][4 * i + 3] = v.w;
+          }
+        }
+        // All rows' codes and norms are loaded before any is used, so a
+        // thread keeps RB loads in flight.  Rows past the end re-read the
+        // last row; their sums are never stored.
+        uint64_t codes[RB];
+        float scale[RB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          const int64_t row = row0 + r < n_out ? row0 + r : n_out - 1;
+          codes[r] = load_codes16<SB>(m.packed + row * row_bytes, c0);
+          scale[r] = half_to_float(m.norms[row * ngr + c0 / kGroup]) * (1.0f / kGroup);
+        }
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          float v[16];
+          Levels<SB>::decode(codes[r], tab, v);
+          float part[NB];
+#pragma unroll
+          for (int b = 0; b < NB; ++b) part[b] = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) part[b] = __builtin_fmaf(v[e], xv[b][e], part[b]);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) acc[r][b] = __builtin_fmaf(scale[r], part[b], acc[r][b]);
         }
       }
-      // All rows' codes and norms are loaded before any is used, so a thread
-      // keeps RB loads in flight.  Rows past the end re-read the last row;
-      // their sums are never stored.
-      uint64_t codes[RB];
-      float scale[RB];
-#pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        const int64_t row = row0 + r < n_out ? row0 + r : n_out - 1;
-        codes[r] = load_codes16<SB>(m.packed + row * row_bytes, c0);
-        scale[r] = half_to_float(m.norms[row * ngr + c0 / kGroup]) * (1.0f / kGroup);
-      }
-#pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        float v[16];
-        Levels<SB>::decode(codes[r], tab, v);
-        float part[NB];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) part[b] = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-#pragma unroll
-          for (int b = 0; b < NB; ++b) part[b] = __builtin_fmaf(v[e], xv[b][e], part[b]);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) acc[r][b] = __builtin_fmaf(scale[r], part[b], acc[r][b]);
-      }
     }
-  }
 
-  // Block reduction in a fixed order: thread t's partials go to column t of
-  // `red`; thread t then sums value t / 8 over columns 32*(t%8) .. 32*(t%8)+31
-  // and the 8 threads of a value combine by shuffles.
+    // Block reduction in a fixed order: thread t's partials go to column t
+    // of `red`; thread t then sums value t / 8 over columns 32*(t%8) ..
+    // 32*(t%8)+31 and the 8 threads of a value combine by shuffles.
 #pragma unroll
-  for (int r = 0; r < RB; ++r)
+    for (int r = 0; r < RB; ++r)
 #pragma unroll
-    for (int b = 0; b < NB; ++b) red[r * NB + b][t] = acc[r][b];
-  __syncthreads();
-  constexpr int V = RB * NB;  // values to reduce (<= 32)
-  const int vi = t / 8, part = t % 8;
-  float s = 0.0f;
-  if (vi < V) {
+      for (int b = 0; b < NB; ++b) red[r * NB + b][t] = acc[r][b];
+    __syncthreads();
+    constexpr int V = RB * NB;  // values to reduce (<= 32)
+    const int vi = t / 8, part = t % 8;
+    float s = 0.0f;
+    if (vi < V) {
 #pragma unroll 8
-    for (int i = 0; i < 32; ++i) s += red[vi][32 * part + i];
-  }
-  s += __shfl_xor(s, 1, kWave);
-  s += __shfl_xor(s, 2, kWave);
-  s += __shfl_xor(s, 4, kWave);
-  if (vi < V && part == 0) {
-    const int r = vi / NB, b = vi % NB;
-    const int64_t row = row0 + r;
-    if (row < n_out) m.y[(b0 + b) * n_out + row] = s;
+      for (int i = 0; i < 32; ++i) s += red[vi][32 * part + i];
+    }
+    s += __shfl_xor(s, 1, kWave);
+    s += __shfl_xor(s, 2, kWave);
+    s += __shfl_xor(s, 4, kWave);
+    if (vi < V && part == 0) {
+      const int r = vi / NB, b = vi % NB;
+      const int64_t row = row0 + r;
+      if (row < n_out) m.y[(b0 + b) * n_out + row] = s;
+    }
+    __syncthreads();  // `red` is rewritten by the next row block
   }
 }
 
@@ -275,8 +278,10 @@ template <int SB, int NB>
 hipError_t launch_nb(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks,
                      const LevelTable& lv, const float* xr, int64_t b0, hipStream_t s) {
   constexpr int RB = 32 / (NB <= 1 ? 1 : NB <= 2 ? 2 : NB <= 4 ? 4 : 8);
-  hipLaunchKernelGGL((matvec_kernel<SB, NB, RB>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock),
-                     0, s, table, bstart, n, lv, xr, b0);
+  // One block per row block: the blocks are short, and letting the hardware
+  // refill free slots measured faster than a resident grid that loops.
+  hipLaunchKernelGGL((matvec_kernel<SB, NB, RB>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
+                     s, table, bstart, n, lv, xr, b0);
   return hipGetLastError();
 }
 
