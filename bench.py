@@ -216,6 +216,25 @@ def main():
                            "GB_per_s": round(gbs(mv_bytes, tmv), 1), "bytes": mv_bytes},
         "quantize_plus_dequantize_Gparams_per_s": round(params / (tq + tdq) / 1e6, 1),
     }
+    # Fused fake quantization (quantize + reconstruct, bf16 -> bf16, one
+    # launch over the whole model), timed on its own after the step.
+    fq_out = torch.empty_like(buf)
+    for _ in range(2):
+        cq.fake_quant(buf, BITS, levels, out=fq_out)
+    fe = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in fe:
+        e[0].record(stream)
+        cq.fake_quant(buf, BITS, levels, out=fq_out)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    tfq = float(np.mean([e[0].elapsed_time(e[1]) for e in fe]))
+    fq_bytes = params * 2 * 2
+    del fq_out
+    phases["fake_quant_bf16_extra"] = {
+        "ms": round(tfq, 4), "Gparams_per_s": round(params / tfq / 1e6, 1),
+        "GB_per_s": round(gbs(fq_bytes, tfq), 1), "bytes": fq_bytes,
+        "frac_hbm_peak": round(gbs(fq_bytes, tfq) / HBM_PEAK_GBS, 4),
+        "note": "not part of the step; bf16 in, bf16 out, one launch"}
     dom = "dequantize_f32" if tdq >= tq else "quantize"
     dom_kernel = {"dequantize_f32": "dequantize_contig<2, false>", "quantize": "quantize_contig<4, true>"}
     ach = gbs(phases[dom]["bytes"], phases[dom]["ms"])

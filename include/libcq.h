@@ -133,6 +133,24 @@ int cq_dequantize(const uint8_t* packed, const uint16_t* norms, int64_t rows,
                   int64_t cols, int bits, int group_size, const float* levels,
                   int n_levels, void* out, int out_dtype, void* stream);
 
+/* Fake quantization: out = the reconstruction of w after quantization, in
+ * one pass with no packed intermediate.  This is the quantize-then-rebuild
+ * transform of "Cactus Quants CQ2-bit Quantization: Extreme Compression for
+ * Edge LLMs", section The CQ2-bit Implementation Pipeline, and the forward
+ * of its straight-through estimator (same page, section Training with
+ * Quantization).  Indices are chosen exactly as cq_quantize chooses them;
+ * the reconstruction is x_hat = (n / G) * H * levels[idx] with n the float32
+ * group norm BEFORE binary16 rounding (so it differs from cq_dequantize of
+ * cq_quantize's output by that rounding, at most 2^-11 relative per group).
+ * w and out are rows x cols in w_dtype / out_dtype (CQ_F32 or CQ_BF16; bf16
+ * output rounds to nearest even), both 16-byte aligned.  out == w with
+ * w_dtype == out_dtype (in place) is allowed: every group is read in full
+ * before it is written.  Any other overlap is CQ_ERR_ARG.  levels (host,
+ * required). */
+int cq_fake_quant(const void* w, int w_dtype, int64_t rows, int64_t cols, int bits,
+                  int group_size, const float* levels, int n_levels, void* out, int out_dtype,
+                  void* stream);
+
 /* y = x . W_hat^T for the quantized n_out x k matrix W (packed + norms as
  * produced by cq_quantize with rows = n_out, cols = k), x float32
  * [batch][k], y float32 [batch][n_out].  k must be a multiple of G

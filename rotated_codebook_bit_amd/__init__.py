@@ -59,12 +59,14 @@ def lib() -> ctypes.CDLL:
                                   vp, vp, vp]
         L.cq_dequantize.argtypes = [vp, vp, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_float), i32,
                                     vp, i32, vp]
+        L.cq_fake_quant.argtypes = [vp, i32, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_float), i32,
+                                    vp, i32, vp]
         L.cq_dequant_matvec.argtypes = [vp, vp, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_float),
                                         i32, vp, i64, vp, vp]
         L.cq_dequant_matvec_many.argtypes = [i32, ctypes.POINTER(MatvecDesc), i32, i32,
                                              ctypes.POINTER(ctypes.c_float), i32, i64, vp]
         for name in ("cq_layout", "cq_model_bytes", "cq_codebook", "cq_quantize", "cq_dequantize",
-                     "cq_dequant_matvec", "cq_dequant_matvec_many"):
+                     "cq_fake_quant", "cq_dequant_matvec", "cq_dequant_matvec_many"):
             getattr(L, name).restype = i32
         L.cq_status_str.argtypes = [i32]
         L.cq_status_str.restype = ctypes.c_char_p
@@ -191,6 +193,29 @@ def dequantize(packed, norms, rows: int, cols: int, bits: int, levels, out_dtype
     lv, lvp = _levels_arg(levels)
     _check("cq_dequantize", lib().cq_dequantize(_ptr(packed), _ptr(norms), rows, cols, bits,
                                                 group_size, lvp, lv.size, _ptr(out), dt,
+                                                _stream_ptr(stream)))
+    return out
+
+
+def fake_quant(w, bits: int, levels, out_dtype=None, group_size: int = GROUP, out=None,
+               stream=None):
+    """Quantize and reconstruct a CUDA tensor in one pass (float32 or
+    bfloat16 in, float32 or bfloat16 out, w's shape; default out dtype = w's).
+    ``out=w`` fake-quantizes in place."""
+    import torch
+    dts = {torch.float32: F32, torch.bfloat16: BF16}
+    if w.dtype not in dts:
+        raise TypeError(f"unsupported dtype {w.dtype}")
+    if not w.is_contiguous():
+        raise ValueError("w must be contiguous")
+    if out is None:
+        out = torch.empty(w.shape, dtype=w.dtype if out_dtype is None else out_dtype, device=w.device)
+    if out.dtype not in dts or not out.is_contiguous() or out.numel() != w.numel():
+        raise ValueError("out must be a contiguous float32/bfloat16 tensor of w's size")
+    rows, cols = _rows_cols(w.shape)
+    lv, lvp = _levels_arg(levels)
+    _check("cq_fake_quant", lib().cq_fake_quant(_ptr(w), dts[w.dtype], rows, cols, bits, group_size,
+                                                lvp, lv.size, _ptr(out), dts[out.dtype],
                                                 _stream_ptr(stream)))
     return out
 

@@ -57,6 +57,10 @@ hipError_t launch_quantize(const void* w, bool bf16, int64_t rows, int64_t cols,
                            const QuantParams& p, uint8_t* packed, uint16_t* norms,
                            hipStream_t stream);
 
+hipError_t launch_fake_quant(const void* w, bool bf16_in, int64_t rows, int64_t cols,
+                             const QuantParams& p, const LevelTable& lv, void* out, bool bf16_out,
+                             hipStream_t stream);
+
 hipError_t launch_dequantize(const uint8_t* packed, const uint16_t* norms,
                              int64_t rows, int64_t cols, int sbits,
                              const LevelTable& lv, void* out, bool bf16_out,

@@ -272,6 +272,34 @@ int cq_quantize(const void* w, int w_dtype, int64_t rows, int64_t cols, int bits
                     "quantize launch");
 }
 
+int cq_fake_quant(const void* w, int w_dtype, int64_t rows, int64_t cols, int bits,
+                  int group_size, const float* levels, int n_levels, void* out, int out_dtype,
+                  void* stream) {
+  g_last_error[0] = 0;
+  int L, rc;
+  if ((rc = check_bits(bits, false, &L))) return rc;
+  if (w_dtype != CQ_F32 && w_dtype != CQ_BF16) return fail(CQ_ERR_ARG, "unknown w_dtype %d", w_dtype);
+  if (out_dtype != CQ_F32 && out_dtype != CQ_BF16)
+    return fail(CQ_ERR_ARG, "unknown out_dtype %d", out_dtype);
+  if (rows < 0 || cols < 0) return fail(CQ_ERR_ARG, "negative size");
+  if ((rc = check_group(group_size, true))) return rc;
+  if ((rc = check_levels(levels, n_levels, L))) return rc;
+  if (rows == 0 || cols == 0) return CQ_OK;
+  if (!w || !out) return fail(CQ_ERR_NULL, "w/out is NULL");
+  if (!aligned(w, 16) || !aligned(out, 16))
+    return fail(CQ_ERR_ALIGN, "w and out need 16-byte alignment");
+  const size_t in_bytes = static_cast<size_t>(rows * cols) * (w_dtype == CQ_F32 ? 4 : 2);
+  const size_t out_bytes = static_cast<size_t>(rows * cols) * (out_dtype == CQ_F32 ? 4 : 2);
+  const bool in_place = w == out && w_dtype == out_dtype;
+  if (!in_place && overlap(w, in_bytes, out, out_bytes))
+    return fail(CQ_ERR_ARG, "w and out overlap (only out == w with equal dtypes is allowed)");
+  const cq::QuantParams p = make_quant_params(levels, L);
+  const cq::LevelTable lv = make_table(levels, L);
+  return hip_status(cq::launch_fake_quant(w, w_dtype == CQ_BF16, rows, cols, p, lv, out,
+                                          out_dtype == CQ_BF16, static_cast<hipStream_t>(stream)),
+                    "fake-quant launch");
+}
+
 int cq_dequantize(const uint8_t* packed, const uint16_t* norms, int64_t rows, int64_t cols,
                   int bits, int group_size, const float* levels, int n_levels, void* out,
                   int out_dtype, void* stream) {

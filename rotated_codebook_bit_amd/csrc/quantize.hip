@@ -115,14 +115,15 @@ __device__ __forceinline__ void search16(float v, const float (&T)[kMaxLevels - 
   b0 = v > (b1 ? s1 : s0);
 }
 
-// Everything after stage 1: shift, stages 2..7, decisions, packing.
-// y holds the stage-1 outputs, S the sum of squares of the group.
+// Stages after stage 1: the shift used by the two-compare decision, then
+// butterfly stages 2..7.  y holds the stage-1 outputs, S the sum of squares
+// of the group.  Returns the group norm; *ns is the scale the decisions use
+// (the norm, or 1 for an all-zero group, whose z is 0: deciding with scale 1
+// compares 0 against the thresholds themselves).
 template <int L>
-__device__ __forceinline__ uint16_t finish_group(float (&y)[kGroup], float S, const QuantParams& p,
-                                                 uint32_t (&words)[Shape<L>::words]) {
+__device__ __forceinline__ float forward_group(float (&y)[kGroup], float S, const QuantParams& p,
+                                               float* ns_out) {
   const float n = __builtin_sqrtf(S);
-  // An all-zero group has z = 0: deciding with scale 1 compares 0 against
-  // the thresholds themselves.
   const float ns = S > 0.0f ? n : 1.0f;
   if constexpr (L == 3 || L == 4) {
     const float sh = p.mu * ns;
@@ -130,7 +131,17 @@ __device__ __forceinline__ uint16_t finish_group(float (&y)[kGroup], float S, co
     y[1] -= sh;
   }
   butterfly_from_stage2(y);
+  *ns_out = ns;
+  return n;
+}
 
+// Everything after stage 1: shift, stages 2..7, decisions, packing.
+// y holds the stage-1 outputs, S the sum of squares of the group.
+template <int L>
+__device__ __forceinline__ uint16_t finish_group(float (&y)[kGroup], float S, const QuantParams& p,
+                                                 uint32_t (&words)[Shape<L>::words]) {
+  float ns;
+  const float n = forward_group<L>(y, S, p, &ns);
   if constexpr (L == 3 || L == 4) {
     const float A = p.hmid * ns, D = p.delta * ns;
 #pragma unroll
@@ -410,6 +421,298 @@ quantize_ragged(const uint8_t* __restrict__ w, int64_t rows, int64_t cols, Quant
   store_group<L>(packed, norms, g, words, n16);
 }
 
+// ---------------------------------------------------------------------------
+// Fused fake quantization: quantize, then reconstruct with the unrounded
+// float32 norm, with no packed intermediate (the pages' quantizer returns the
+// reconstructed tensor: "Cactus Quants CQ2-bit Quantization: Extreme
+// Compression for Edge LLMs", section The CQ2-bit Implementation Pipeline;
+// it is the forward of the straight-through estimator, section Training with
+// Quantization).
+// x_hat = (n / G) * H levels[idx]  (n unrounded; 1/G = 2^-7 is exact).
+// ---------------------------------------------------------------------------
+
+// y[j] <- level of element j's decision (N(0,1) units), in place.
+template <int L>
+__device__ __forceinline__ void levels_in_place(float (&y)[kGroup], float ns, const QuantParams& p,
+                                                const LevelTable& lv, const float* lut) {
+  if constexpr (L == 3 || L == 4) {
+    const float A = p.hmid * ns, D = p.delta * ns;
+    // Four levels: index = 2h + NOT(q XOR h); three levels: 2h + NOT q.
+    const float lo = lv.c[0], mid = lv.c[1], hi = lv.c[L - 1], mid2 = lv.c[L == 4 ? 2 : 1];
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      const float v = y[j];
+      const bool h = v > A, q = __builtin_fabsf(v) > D;
+      y[j] = q ? (h ? hi : lo) : (h ? mid2 : mid);
+    }
+  } else if constexpr (L == 8) {
+    float T[kMaxLevels - 1];
+#pragma unroll
+    for (int i = 0; i < 7; ++i) T[i] = p.thr[i] * ns;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) y[j] = lut[search8(y[j], T)];
+  } else {
+    float T[kMaxLevels - 1];
+#pragma unroll
+    for (int i = 0; i < 15; ++i) T[i] = p.thr[i] * ns;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      bool b3, b2, b1, b0;
+      search16(y[j], T, b3, b2, b1, b0);
+      y[j] = lut[(bit(b3) << 3) | (bit(b2) << 2) | (bit(b1) << 1) | bit(b0)];
+    }
+  }
+}
+
+__device__ __forceinline__ void butterfly_all(float (&y)[kGroup]) {
+#pragma unroll
+  for (int i = 0; i < kGroup; i += 2) {
+    const float a = y[i], b = y[i + 1];
+    y[i] = a + b;
+    y[i + 1] = a - b;
+  }
+  butterfly_from_stage2(y);
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ void store16(const uint4& v, __amdgpu_buffer_rsrc_t dst, uint32_t voff,
+                                        uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)  // buffer builtins exist only for the GPU target
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(w, dst, voff, soff, 0);
+#endif
+}
+
+// Stage 1 and the sum of squares from the raw words of one group.
+template <bool BF16>
+__device__ __forceinline__ float stage1_group(const uint32_t (&raw)[BF16 ? 64 : 128], float (&y)[kGroup]) {
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  if constexpr (BF16) {
+#pragma unroll
+    for (int i = 0; i < 64; i += 4) {
+      stage1_bf16(raw[i], y[2 * i], y[2 * i + 1], s0);
+      stage1_bf16(raw[i + 1], y[2 * i + 2], y[2 * i + 3], s1);
+      stage1_bf16(raw[i + 2], y[2 * i + 4], y[2 * i + 5], s2);
+      stage1_bf16(raw[i + 3], y[2 * i + 6], y[2 * i + 7], s3);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 128; i += 4) {
+      const float a0 = __builtin_bit_cast(float, raw[i]), b0 = __builtin_bit_cast(float, raw[i + 1]);
+      const float a1 = __builtin_bit_cast(float, raw[i + 2]), b1 = __builtin_bit_cast(float, raw[i + 3]);
+      y[i] = a0 + b0;
+      y[i + 1] = a0 - b0;
+      y[i + 2] = a1 + b1;
+      y[i + 3] = a1 - b1;
+      s0 = __builtin_fmaf(a0, a0, s0);
+      s1 = __builtin_fmaf(b0, b0, s1);
+      s2 = __builtin_fmaf(a1, a1, s2);
+      s3 = __builtin_fmaf(b1, b1, s3);
+    }
+  }
+  return (s0 + s1) + (s2 + s3);
+}
+
+// Fast path (cols % 128 == 0).  Input as in quantize_contig (DMA into a
+// wave-private LDS buffer, next batch issued right after the current one is
+// read out); the reconstructed groups leave through a second, smaller LDS
+// buffer in phases of 32 bytes per group so that consecutive lanes store
+// consecutive bytes.
+template <int L, bool BF16IN, bool BF16OUT>
+__global__ void __launch_bounds__(kBlock, 2)
+fakequant_contig(const uint8_t* __restrict__ w, int64_t n_groups, QuantParams p, LevelTable lv,
+                 uint8_t* __restrict__ out) {
+  constexpr int GB = BF16IN ? 256 : 512;  // input bytes per group
+  constexpr int CPG = GB / 16;
+  constexpr int WAVE_BYTES = kWave * GB;
+  constexpr int NI = WAVE_BYTES / 1024;
+  constexpr int OB = BF16OUT ? 2 : 4;     // output bytes per element
+  constexpr int GOB = kGroup * OB;        // output bytes per group
+  constexpr int PB = 32;                  // bytes per group per phase
+  constexpr int PE = PB / OB;             // elements per group per phase
+  constexpr int CPP = PB / 16;            // 16-byte chunks per group per phase
+  constexpr int GPB = 256 / PB;           // groups per 256-byte LDS row
+  constexpr int GPO = kWave / CPP;        // groups per store instruction
+  constexpr int OWB = kWave * PB;         // output staging bytes per wave
+  constexpr int NIO = OWB / 1024;         // store instructions per phase
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * WAVE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t olds[kWaves * OWB];
+  __shared__ float lut[kMaxLevels];
+  if (threadIdx.x < kMaxLevels) lut[threadIdx.x] = level_at(lv, threadIdx.x);
+  __syncthreads();
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  uint8_t* const buf = lds + wave * WAVE_BYTES;
+  uint8_t* const obuf = olds + wave * OWB;
+  const int64_t n_batches = (n_groups + kWave - 1) / kWave;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
+  int64_t batch = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  if (batch >= n_batches) return;
+
+  constexpr int GPI = kWave / CPG;
+  constexpr int R = 16 / GPI;
+  uint32_t lane_part[R];
+  {
+    const int q = lane / CPG, cl = lane % CPG;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      lane_part[r] = static_cast<uint32_t>(q * GB + 16 * ((cl ^ q) ^ ((GPI * r) & 15)));
+  }
+  const uint32_t rd_base = static_cast<uint32_t>(lane * GB + 16 * (lane & 15));
+  const int swz_w = (lane / GPB) & (CPP - 1);
+  const int gq = lane / CPP, cc = lane % CPP;
+  const uint32_t st_lane = static_cast<uint32_t>(gq * GOB + 16 * cc);
+
+  issue_batch<GB, NI, R>(w, batch, n_groups, buf, lane_part);
+  for (;;) {
+    uint32_t raw[GB / 4];
+#pragma unroll
+    for (int c = 0; c < CPG; ++c) {
+      const uint4 v = *reinterpret_cast<const uint4*>(buf + (rd_base ^ (16u * c)));
+      raw[4 * c] = v.x;
+      raw[4 * c + 1] = v.y;
+      raw[4 * c + 2] = v.z;
+      raw[4 * c + 3] = v.w;
+    }
+    wait_lgkm0();
+    asm volatile("" ::: "memory");
+    const int64_t next = batch + stride;
+    if (next < n_batches) issue_batch<GB, NI, R>(w, next, n_groups, buf, lane_part);
+
+    float y[kGroup];
+    const float S = stage1_group<BF16IN>(raw, y);
+    float ns;
+    const float n = forward_group<L>(y, S, p, &ns);
+    levels_in_place<L>(y, ns, p, lv, lut);
+    butterfly_all(y);
+    const float sc = n * (1.0f / kGroup);
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) y[j] *= sc;
+
+    const auto dst = make_rsrc(out + batch * kWave * GOB, valid_in_batch(batch, n_groups) * GOB);
+#pragma unroll
+    for (int ph = 0; ph < kGroup / PE; ++ph) {
+#pragma unroll
+      for (int c = 0; c < CPP; ++c) {
+        uint4 v;
+        if constexpr (BF16OUT) {
+          const int e = PE * ph + 8 * c;
+          v.x = f32_to_bf16_rne(y[e]) | (f32_to_bf16_rne(y[e + 1]) << 16);
+          v.y = f32_to_bf16_rne(y[e + 2]) | (f32_to_bf16_rne(y[e + 3]) << 16);
+          v.z = f32_to_bf16_rne(y[e + 4]) | (f32_to_bf16_rne(y[e + 5]) << 16);
+          v.w = f32_to_bf16_rne(y[e + 6]) | (f32_to_bf16_rne(y[e + 7]) << 16);
+        } else {
+          const int e = PE * ph + 4 * c;
+          v = make_uint4(__builtin_bit_cast(uint32_t, y[e]), __builtin_bit_cast(uint32_t, y[e + 1]),
+                         __builtin_bit_cast(uint32_t, y[e + 2]), __builtin_bit_cast(uint32_t, y[e + 3]));
+        }
+        *reinterpret_cast<uint4*>(obuf + lane * PB + 16 * (c ^ swz_w)) = v;
+      }
+#pragma unroll
+      for (int i = 0; i < NIO; ++i) {
+        const int gs = GPO * i + gq;
+        const int sw = (gs / GPB) & (CPP - 1);
+        const uint4 v = *reinterpret_cast<const uint4*>(obuf + gs * PB + 16 * (cc ^ sw));
+        store16(v, dst, st_lane + ph * PB, static_cast<uint32_t>(GPO * i * GOB));
+      }
+    }
+    batch = next;
+    if (batch >= n_batches) break;
+  }
+}
+
+// General path: rows of any length; each lane gathers its own group and
+// writes its valid columns.
+template <int L, bool BF16IN, bool BF16OUT>
+__global__ void __launch_bounds__(kBlock)
+fakequant_ragged(const uint8_t* __restrict__ w, int64_t rows, int64_t cols, QuantParams p,
+                 LevelTable lv, uint8_t* __restrict__ out) {
+  __shared__ float lut[kMaxLevels];
+  if (threadIdx.x < kMaxLevels) lut[threadIdx.x] = level_at(lv, threadIdx.x);
+  __syncthreads();
+  const int64_t ngr = (cols + kGroup - 1) / kGroup;
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  if (g >= rows * ngr) return;
+  const int64_t row = g / ngr, col0 = (g - row * ngr) * kGroup;
+  const int64_t valid = cols - col0 < kGroup ? cols - col0 : kGroup;
+  const int64_t base = row * cols + col0;
+  float x[kGroup];
+#pragma unroll
+  for (int j = 0; j < kGroup; ++j) {
+    float v = 0.0f;
+    if (j < valid) {
+      if constexpr (BF16IN) {
+        const uint16_t b = reinterpret_cast<const uint16_t*>(w)[base + j];
+        v = __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);
+      } else {
+        v = reinterpret_cast<const float*>(w)[base + j];
+      }
+    }
+    x[j] = v;
+  }
+  float y[kGroup];
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < kGroup; i += 2) {
+    y[i] = x[i] + x[i + 1];
+    y[i + 1] = x[i] - x[i + 1];
+    s0 = __builtin_fmaf(x[i], x[i], s0);
+    s1 = __builtin_fmaf(x[i + 1], x[i + 1], s1);
+  }
+  float ns;
+  const float n = forward_group<L>(y, s0 + s1, p, &ns);
+  levels_in_place<L>(y, ns, p, lv, lut);
+  butterfly_all(y);
+  const float sc = n * (1.0f / kGroup);
+#pragma unroll
+  for (int j = 0; j < kGroup; ++j) {
+    if (j < valid) {
+      const float v = y[j] * sc;
+      if constexpr (BF16OUT)
+        reinterpret_cast<uint16_t*>(out)[base + j] = static_cast<uint16_t>(f32_to_bf16_rne(v));
+      else
+        reinterpret_cast<float*>(out)[base + j] = v;
+    }
+  }
+}
+
+template <int L, bool BF16IN, bool BF16OUT>
+hipError_t launch_fq(const void* w, int64_t rows, int64_t cols, const QuantParams& p,
+                     const LevelTable& lv, void* out, hipStream_t s) {
+  const uint8_t* wb = static_cast<const uint8_t*>(w);
+  uint8_t* ob = static_cast<uint8_t*>(out);
+  if (cols % kGroup == 0) {
+    const int64_t n_groups = rows * (cols / kGroup);
+    const int64_t n_batches = (n_groups + kWave - 1) / kWave;
+    const int blocks = persistent_blocks((n_batches + kWaves - 1) / kWaves, BF16IN ? kBlocksPerCu : 1);
+    hipLaunchKernelGGL((fakequant_contig<L, BF16IN, BF16OUT>), dim3(blocks), dim3(kBlock), 0, s, wb,
+                       n_groups, p, lv, ob);
+  } else {
+    const int64_t n_groups = rows * ((cols + kGroup - 1) / kGroup);
+    const int blocks = static_cast<int>((n_groups + kBlock - 1) / kBlock);
+    hipLaunchKernelGGL((fakequant_ragged<L, BF16IN, BF16OUT>), dim3(blocks), dim3(kBlock), 0, s, wb, rows,
+                       cols, p, lv, ob);
+  }
+  return hipGetLastError();
+}
+
+template <int L>
+hipError_t launch_fq_types(const void* w, bool bf16_in, int64_t rows, int64_t cols,
+                           const QuantParams& p, const LevelTable& lv, void* out, bool bf16_out,
+                           hipStream_t s) {
+  if (bf16_in)
+    return bf16_out ? launch_fq<L, true, true>(w, rows, cols, p, lv, out, s)
+                    : launch_fq<L, true, false>(w, rows, cols, p, lv, out, s);
+  return bf16_out ? launch_fq<L, false, true>(w, rows, cols, p, lv, out, s)
+                  : launch_fq<L, false, false>(w, rows, cols, p, lv, out, s);
+}
+
 template <int L, bool BF16>
 hipError_t launch_l(const void* w, int64_t rows, int64_t cols, const QuantParams& p,
                     uint8_t* packed, uint16_t* norms, hipStream_t s) {
@@ -440,6 +743,18 @@ hipError_t launch_dtype(const void* w, bool bf16, int64_t rows, int64_t cols, co
 }
 
 }  // namespace kq
+
+hipError_t launch_fake_quant(const void* w, bool bf16_in, int64_t rows, int64_t cols,
+                             const QuantParams& p, const LevelTable& lv, void* out, bool bf16_out,
+                             hipStream_t stream) {
+  switch (p.n_levels) {
+    case 3: return kq::launch_fq_types<3>(w, bf16_in, rows, cols, p, lv, out, bf16_out, stream);
+    case 4: return kq::launch_fq_types<4>(w, bf16_in, rows, cols, p, lv, out, bf16_out, stream);
+    case 8: return kq::launch_fq_types<8>(w, bf16_in, rows, cols, p, lv, out, bf16_out, stream);
+    case 16: return kq::launch_fq_types<16>(w, bf16_in, rows, cols, p, lv, out, bf16_out, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_quantize(const void* w, bool bf16, int64_t rows, int64_t cols,
                            const QuantParams& p, uint8_t* packed, uint16_t* norms,

@@ -10,6 +10,12 @@
 * Dequantized values: |x_gpu - x_ref| <= 1e-5 * RMS_g per element, with
   RMS_g = norm16 / sqrt(G) of the element's group.
 * Matvec: |y_gpu - y_ref| <= 1e-5 * ||x_b|| * ||W_hat_r|| per element.
+* Fake quantization: the GPU's indices are read back from its output
+  (H x_hat * sqrt(G) / n recovers levels[idx] for full groups) and checked
+  under the index rule; values |x_gpu - x_ref| <= 1e-5 * n / sqrt(G) per
+  element, plus (n / G) * (largest level gap) for each in-band element of the
+  group (one flipped index moves every element of its group by exactly
+  (n / G) * gap), plus one bf16 rounding for bf16 output.
 
 The oracle is only ever given inputs that came from the seeded generators or
 from the oracle itself, never from the GPU.
@@ -113,3 +119,55 @@ def check_matvec(y_gpu: np.ndarray, y_ref: np.ndarray, x: np.ndarray, w_hat: np.
     rel = err / np.where(scale > 0, scale, 1.0)
     assert np.all(err <= MV_TOL * scale), f"matvec error {rel.max():.3g} of ||x|| ||w|| > {MV_TOL:g}"
     return Report(outputs=err.size, max_err_scaled=float(rel.max()))
+
+
+def check_fake_quant(out_gpu: np.ndarray, w64: np.ndarray, bits: int, levels: np.ndarray,
+                     out_bf16: bool = False, enforce_count: bool = True) -> Report:
+    """out_gpu: the GPU reconstruction of w64 (any shape, w64's size)."""
+    g = O.GROUP
+    w2 = np.asarray(w64, dtype=np.float64).reshape(-1, np.shape(w64)[-1])
+    rows, cols = w2.shape
+    ng = -(-cols // g)
+    ref = O.fake_quant(w2, bits, levels)
+    q = O.quantize(w2, bits, levels)
+    lv32 = O.runtime_levels(levels)
+    out = np.asarray(out_gpu, dtype=np.float64).reshape(rows, cols)
+    n = q.norm
+    inband = (O.threshold_distance(q.z, lv32) <= BAND).sum(-1)
+    gap = float(np.max(np.diff(lv32)))
+
+    def by_group(a):
+        full = np.zeros((rows, ng * g))
+        full[:, :cols] = a
+        return full.reshape(rows, ng, g)
+
+    err = by_group(np.abs(out - ref)).max(-1)
+    tol = DEQ_TOL * n / math.sqrt(g) + inband * (n / g) * gap
+    if out_bf16:
+        tol = tol * (1 + 2.0 ** -8) + 2.0 ** -8 * by_group(np.abs(ref)).max(-1)
+    bad = err > tol
+    assert not bad.any(), (f"{int(bad.sum())} groups off by more than the bound; worst "
+                           f"{float((err / np.maximum(tol, 1e-300)).max()):.3g}x")
+    zero = n == 0
+    assert not by_group(out)[zero].any(), "a zero group must reconstruct to zeros"
+    rep = Report(values=out.size, groups_with_band=int((inband > 0).sum()))
+
+    nfull = ng if cols % g == 0 else ng - 1
+    if nfull > 0:
+        xg = out[:, :nfull * g].reshape(rows, nfull, g)
+        nn = n[:, :nfull]
+        c_hat = (xg @ O.hadamard(g)) * (math.sqrt(g) / np.where(nn > 0, nn, 1.0))[..., None]
+        idx_ref = q.idx[:, :nfull]
+        idx_gpu = np.argmin(np.abs(c_hat[..., None] - lv32), axis=-1)
+        idx_gpu[zero[:, :nfull]] = idx_ref[zero[:, :nfull]]
+        mism = idx_gpu != idx_ref
+        m = int(mism.sum())
+        if m:
+            dist = O.threshold_distance(q.z[:, :nfull][mism], lv32)
+            assert np.all(dist <= BAND), f"index mismatch outside the band: max dist {dist.max():.3g}"
+            assert np.all(np.abs(idx_gpu[mism] - idx_ref[mism]) == 1), "mismatch is not a neighbour"
+        rep["index_mismatches"] = m
+        rep["indices_read_back"] = int(idx_ref.size)
+        if enforce_count:
+            check_count(m, idx_ref.size)
+    return rep

@@ -29,7 +29,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = cq.lib()
     names = declared_functions()
-    assert {"cq_quantize", "cq_dequantize", "cq_dequant_matvec", "cq_model_bytes"} <= set(names)
+    assert {"cq_quantize", "cq_dequantize", "cq_dequant_matvec", "cq_model_bytes",
+            "cq_fake_quant"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
     assert L.cq_version().decode().startswith("libcq")
@@ -210,3 +211,25 @@ def test_matvec_many_validation():
     assert many([D(0x100000, 0x900000, 8, 256, 0x2100004, 0x3100000)]) == E_ALIGN
     assert many([D(0x100000, 0x900000, 8, 256, 0x2100000, 0x2100000)]) == E_ARG   # y overlaps x
     assert many([D(0, 0, 0, 256, 0, 0)]) == OK                                    # empty matrix
+
+
+def test_fake_quant_validation():
+    L = cq.lib()
+    lv, lp = _levels(4)
+
+    def fq(w=FAKE, dt=1, rows=4, cols=256, bits=2, g=128, nl=4, out=FAKE2, odt=0):
+        return L.cq_fake_quant(w, dt, rows, cols, bits, g, lp if nl == 4 else _levels(nl)[1], nl,
+                               out, odt, None)
+
+    assert fq(dt=3) == E_ARG
+    assert fq(odt=-1) == E_ARG
+    assert fq(bits=1) == E_ARG
+    assert fq(g=32) == E_UNSUP
+    assert fq(nl=8) == E_ARG
+    assert fq(rows=-2) == E_ARG
+    assert fq(w=None) == E_NULL
+    assert fq(out=None) == E_NULL
+    assert fq(out=ctypes.c_void_p(0x900008)) == E_ALIGN
+    assert fq(out=ctypes.c_void_p(0x100000 + 1024)) == E_ARG        # partial overlap
+    assert fq(out=FAKE, dt=1, odt=0) == E_ARG                          # in place, dtypes differ
+    assert fq(rows=0, w=None, out=None) == OK

@@ -15,7 +15,7 @@ import pytest
 
 from oracle import cq_oracle as O
 from rotated_codebook_bit_amd import workloads as W
-from parity import check_count, check_dequant, check_matvec, check_quantize
+from parity import check_count, check_dequant, check_fake_quant, check_matvec, check_quantize
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -332,3 +332,97 @@ def test_matvec_deterministic(matvec_weight, levels):
     a = host(cq.dequant_matvec(p_dev, n_dev, 11008, 4096, 2, lv, x))
     b = host(cq.dequant_matvec(p_dev, n_dev, 11008, 4096, 2, lv, x))
     assert np.array_equal(a, b)
+
+
+# -- fused fake quantization --------------------------------------------------------
+
+def _w(shape, seed, dtype):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal(shape) * 0.02).astype(np.float32)
+    if dtype == "bf16":
+        b = W.f32_to_bf16_bits(w)
+        return W.bf16_bits_to_f32(b).astype(np.float64), to_dev_bf16(b)
+    return w.astype(np.float64), to_dev_f32(w)
+
+
+def _out_host(t):
+    if t.dtype == torch.bfloat16:
+        return W.bf16_bits_to_f32(host(t.view(torch.int16)).view(np.uint16)).astype(np.float64)
+    return host(t).astype(np.float64)
+
+
+@pytest.mark.parametrize("bits", ALL_BITS)
+@pytest.mark.parametrize("dtypes", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"), ("f32", "bf16")])
+@pytest.mark.parametrize("shape", [(600, 512), (33, 1000), (2, 3, 130), (1, 1)])
+def test_fake_quant(bits, dtypes, shape, levels):
+    din, dout = dtypes
+    w64, w_dev = _w(shape, zlib.crc32(repr(("fq", bits, dtypes, shape)).encode()), din)
+    odt = torch.bfloat16 if dout == "bf16" else torch.float32
+    say(f"fake_quant bits={bits} {din}->{dout} shape={shape}")
+    out = cq.fake_quant(w_dev, bits, levels[bits], out_dtype=odt)
+    assert tuple(out.shape) == shape and out.dtype == odt
+    rep = check_fake_quant(_out_host(out), w64, bits, levels[bits], out_bf16=dout == "bf16")
+    say(f"fake_quant: {rep.line()}")
+
+
+def test_fake_quant_in_place_and_special(levels):
+    rng = np.random.default_rng(6)
+    base = rng.standard_normal((1, 128))
+    w = np.concatenate([np.zeros((1, 128)), np.full((1, 128), 0.25), base, base * 2.0 ** 10,
+                        np.full((1, 128), -3.0), np.full((1, 128), 1e5),
+                        rng.standard_normal((250, 128)) * 0.02], axis=0).astype(np.float32)
+    for bits in ALL_BITS:
+        say(f"fake_quant special groups, in place, bits={bits}")
+        w_dev = to_dev_f32(w)
+        out = cq.fake_quant(w_dev, bits, levels[bits], out=w_dev)
+        assert out.data_ptr() == w_dev.data_ptr()
+        check_fake_quant(_out_host(out), w.astype(np.float64), bits, levels[bits])
+        # The norm overflowing binary16 does not matter here: the unrounded
+        # norm is used.
+        assert np.isfinite(_out_host(out)).all()
+
+
+def test_fake_quant_matches_quantize_decisions(levels):
+    """Fake quantization makes the same decisions as quantize: on a 4096 x 4096
+    bf16 matrix, the indices read back from its output agree with the packed
+    indices wherever no element lies within the band of a threshold."""
+    lv = levels[2]
+    w64, w_dev = _w((4096, 4096), 11, "bf16")
+    say("fake_quant vs quantize decisions 4096x4096")
+    out = _out_host(cq.fake_quant(w_dev, 2, lv, out_dtype=torch.float32))
+    rep = check_fake_quant(out, w64, 2, lv, enforce_count=False)
+    check_count(rep["index_mismatches"], rep["indices_read_back"])
+    packed, norms = gpu_quantize(w_dev, 2, lv)
+    idx_q = O.unpack(packed.reshape(-1, 32), 2).reshape(4096, 32, 128)
+    c_hat = (out.reshape(4096, 32, 128) @ O.hadamard(128))
+    n = np.sqrt(np.sum(c_hat ** 2, axis=-1, keepdims=True))
+    lv32 = O.runtime_levels(lv)
+    # scale-free read-back: the reconstructed level vector up to its norm
+    unit = lv32[idx_q]
+    unit = unit / np.sqrt(np.sum(unit ** 2, axis=-1, keepdims=True))
+    same = np.abs(c_hat / n - unit).max(-1) < 1e-4
+    assert same.mean() > 1 - 1e-4, f"only {same.mean():.6f} of groups match quantize"
+    say(f"fake_quant vs quantize: {rep.line()} groups_equal={same.mean():.6f}")
+
+
+def test_fake_quant_empty(levels):
+    for shape in [(0, 128), (5, 0)]:
+        w = torch.zeros(shape, dtype=torch.bfloat16, device=DEV)
+        assert cq.fake_quant(w, 2, levels[2]).shape == shape
+
+
+def test_fake_quant_llama7b_layer_sampled(levels):
+    """The largest single tensor of the 7B-shaped model (32000 x 4096, bf16):
+    whole-tensor launch, 2048 sampled rows checked against the oracle."""
+    lv = levels[2]
+    g = torch.Generator(device=DEV)
+    g.manual_seed(123)
+    w_dev = (torch.randn((32000, 4096), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    say("fake_quant 32000x4096 bf16 -> bf16")
+    out = cq.fake_quant(w_dev, 2, lv)
+    rows = np.sort(np.random.default_rng(7).choice(32000, 2048, replace=False))
+    ridx = torch.from_numpy(rows).to(DEV)
+    w_s = W.bf16_bits_to_f32(host(w_dev[ridx].view(torch.int16)).view(np.uint16)).astype(np.float64)
+    rep = check_fake_quant(_out_host(out[ridx]), w_s, 2, lv, out_bf16=True, enforce_count=False)
+    check_count(rep["index_mismatches"], rep["indices_read_back"])
+    say(f"fake_quant llama7b sampled: {rep.line()}")

@@ -225,3 +225,44 @@ def test_model_bytes_matches_packed_sizes(oracle_levels):
     for bits in BITS:
         q = O.quantize(w, bits, oracle_levels[bits])
         assert q.packed.nbytes + q.norm16.nbytes == O.model_bytes([w.shape], bits)
+
+
+# -- fake quant (quantize then reconstruct with the unrounded norm) ----------------
+
+@pytest.mark.parametrize("bits", [O.TERNARY, 2, 3, 4])
+def test_fake_quant_equals_stored_round_trip_when_norm_is_fp16_exact(bits, oracle_levels):
+    """Groups whose norm is exactly representable in binary16 reconstruct the
+    same with the stored and the unrounded norm: 64 entries of +-2 and 64
+    zeros have norm exactly 16."""
+    levels = oracle_levels[bits]
+    rs = np.random.RandomState(21)
+    w = np.zeros((6, 128))
+    for r in range(6):
+        pos = rs.permutation(128)[:64]
+        w[r, pos] = rs.choice([-2.0, 2.0], size=64)
+    q = O.quantize(w, bits, levels)
+    assert np.all(q.norm == 16.0)
+    rt = O.dequantize(q.packed, q.norm16, 6, 128, bits, levels)
+    # Same formula; only the float64 summation order of the two products differs.
+    np.testing.assert_allclose(O.fake_quant(w, bits, levels), rt, rtol=1e-13, atol=1e-15)
+
+
+def test_fake_quant_constant_group_closed_form(oracle_levels):
+    levels = oracle_levels[2]
+    c = O.runtime_levels(levels)
+    a = 0.3
+    n = a * math.sqrt(128)
+    m = int(np.sum(O.thresholds(c) < 0))
+    xh = O.fake_quant(np.full((1, 128), a), 2, levels)[0]
+    expect = np.full(128, (n / 128) * (c[-1] - c[m]))
+    expect[0] = (n / 128) * (c[-1] + 127 * c[m])
+    np.testing.assert_allclose(xh, expect, rtol=1e-13)
+
+
+def test_fake_quant_shape_and_padding(oracle_levels):
+    w = np.random.RandomState(22).randn(2, 3, 200)
+    out = O.fake_quant(w, 2, oracle_levels[2])
+    assert out.shape == w.shape
+    wp = np.zeros((2, 3, 256))
+    wp[..., :200] = w
+    np.testing.assert_array_equal(out, O.fake_quant(wp, 2, oracle_levels[2])[..., :200])
