@@ -343,6 +343,35 @@ def model_bytes(shapes, bits: int, g: int = GROUP) -> int:
     return total
 
 
+def serialize(quantized) -> np.ndarray:
+    """Serialized weights of a sequence of quantized tensors, in the order of
+    *Footprint* §Binary Serialization: the packed indices of every tensor,
+    tensor after tensor, followed by every tensor's binary16 norms
+    (little-endian), in the same tensor order.  No header and no padding
+    (reading: the norms of all tensors follow all the indices)."""
+    parts = [np.asarray(q.packed, dtype=np.uint8).ravel() for q in quantized]
+    parts += [np.asarray(q.norm16, dtype=np.uint16).astype("<u2").view(np.uint8).ravel()
+              for q in quantized]
+    return np.concatenate(parts) if parts else np.zeros(0, dtype=np.uint8)
+
+
+def blob_offsets(shapes, bits: int, g: int = GROUP):
+    """(packed_offsets, norm_offsets, total) of :func:`serialize`'s output for
+    tensors of the given shapes: byte offsets of each tensor's indices and
+    norms, and the total size (which equals :func:`model_bytes`)."""
+    sb = storage_bits(bits)
+    packed, norms = [], []
+    for shape in shapes:
+        shape = tuple(int(s) for s in shape)
+        r = int(np.prod(shape[:-1], dtype=np.int64)) if len(shape) > 1 else 1
+        groups = r * (-(-shape[-1] // g))
+        packed.append(groups * g * sb // 8)
+        norms.append(groups * 2)
+    p_off = [sum(packed[:i]) for i in range(len(packed))]
+    n_off = [sum(packed) + sum(norms[:i]) for i in range(len(norms))]
+    return p_off, n_off, sum(packed) + sum(norms)
+
+
 def relative_mse(w: np.ndarray, w_hat: np.ndarray) -> float:
     """||W - W_hat||_F^2 / ||W||_F^2 (the distortion measure of *2-bit vs
     4-bit* §Quantization Error and Accuracy Impact, read as a mean-square
