@@ -235,6 +235,58 @@ def main():
         "GB_per_s": round(gbs(fq_bytes, tfq), 1), "bytes": fq_bytes,
         "frac_hbm_peak": round(gbs(fq_bytes, tfq) / HBM_PEAK_GBS, 4),
         "note": "not part of the step; bf16 in, bf16 out, one launch"}
+    # Quantize as 225 back-to-back per-tensor calls on one stream (launch
+    # gaps and small-tensor tails), against the one flat launch above.
+    def per_tensor():
+        for i, (r, c) in enumerate(shapes):
+            o0, o1 = int(offsets[i]), int(offsets[i + 1])
+            g0, g1 = o0 // G, o1 // G
+            cq.quantize(buf[o0:o1].view(r, c), BITS, levels, packed=packed[g0:g1].view(r, c // G, -1),
+                        norms=norms[g0:g1].view(r, c // G))
+    per_tensor()
+    torch.cuda.synchronize()
+    pe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    reps = 3
+    pe[0].record(stream)
+    for _ in range(reps):
+        per_tensor()
+    pe[1].record(stream)
+    torch.cuda.synchronize()
+    tpt = pe[0].elapsed_time(pe[1]) / reps
+    phases["quantize_225_calls_extra"] = {
+        "ms": round(tpt, 4), "GB_per_s": round(gbs(q_bytes, tpt), 1),
+        "note": "the same quantize as 225 per-tensor calls; not part of the step"}
+
+    # The same 225 tensors through one multi-tensor call, writing the
+    # serialized blob (all packed indices, then all norms).
+    tviews = [buf[int(offsets[i]):int(offsets[i + 1])].view(r, c) for i, (r, c) in enumerate(shapes)]
+    blob, _ = cq.quantize_many(tviews, BITS, levels)
+    torch.cuda.synchronize()
+    pe[0].record(stream)
+    for _ in range(reps):
+        cq.quantize_many(tviews, BITS, levels, blob=blob, views=False)
+    pe[1].record(stream)
+    torch.cuda.synchronize()
+    tqm = pe[0].elapsed_time(pe[1]) / reps
+    phases["quantize_many_1_call_extra"] = {
+        "ms": round(tqm, 4), "GB_per_s": round(gbs(q_bytes, tqm), 1),
+        "note": "the same quantize as one cq_quantize_many call over the 225 tensors, writing the "
+                "serialized blob; not part of the step"}
+    del blob
+
+    # Practical ceiling in the same process: a 4 GiB device-to-device copy.
+    src = torch.empty(1 << 30, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ce[0].record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    ce[1].record(stream)
+    torch.cuda.synchronize()
+    tcopy = ce[0].elapsed_time(ce[1]) / 5
+    copy_gbs = 2 * src.numel() * 4 / (tcopy * 1e-3) / 1e9
+    del src, dst
     dom = "dequantize_f32" if tdq >= tq else "quantize"
     dom_kernel = {"dequantize_f32": "dequantize_contig<2, false>", "quantize": "quantize_contig<4, true>"}
     ach = gbs(phases[dom]["bytes"], phases[dom]["ms"])
@@ -248,7 +300,9 @@ def main():
             traffic = None
     roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": dom_kernel[dom], "bytes_per_launch": phases[dom]["bytes"]}
+                "kernel": dom_kernel[dom], "bytes_per_launch": phases[dom]["bytes"],
+                "copy_4GiB_GB_per_s": round(copy_gbs, 1),
+                "frac_of_copy": round(ach / copy_gbs, 4)}
     result = {
         "metric": METRIC,
         "value": round(params / (ms_step * 1e-3) / 1e9, 2),

@@ -39,7 +39,7 @@
  *     in N(0,1) units (before the 1/sqrt(G) scaling), strictly ascending.
  *     n_levels must be 3 for CQ_TERNARY and 2^bits otherwise.
  *   - group_size must be 128 for device calls; host-only calls take any power
- *     of two up to 4096.
+ *     of two from 8 to 4096 (so a group's packed indices fill whole bytes).
  *   - Device calls validate every argument first, then enqueue their kernels
  *     on `stream` (a hipStream_t; NULL = the null stream) and return without
  *     waiting.  On a validation error nothing is enqueued.  Asynchronous
@@ -132,6 +132,63 @@ int cq_quantize(const void* w, int w_dtype, int64_t rows, int64_t cols,
 int cq_dequantize(const uint8_t* packed, const uint16_t* norms, int64_t rows,
                   int64_t cols, int bits, int group_size, const float* levels,
                   int n_levels, void* out, int out_dtype, void* stream);
+
+/* Serialized layout of n_tensors quantized tensors (rows/cols host arrays),
+ * in the order of "How CQ2-bit Quantization Contributes to Needle 2's Small
+ * Footprint", section Binary Serialization: the packed indices of every
+ * tensor, tensor after tensor, then the binary16 norms of every tensor in the
+ * same order, with no header and no padding.  Writes the byte offset of
+ * tensor i's packed indices to packed_offsets[i] and of its norms to
+ * norm_offsets[i] (host arrays of n_tensors entries, each may be NULL) and
+ * the blob size to *total_bytes (may be NULL), which equals cq_model_bytes.
+ * With group_size 128 every offset is a multiple of 16 (packed) or 2
+ * (norms), so a 16-byte aligned blob can take cq_quantize_many's outputs
+ * directly.  Host only, pure. */
+int cq_blob_layout(int n_tensors, const int64_t* rows, const int64_t* cols, int bits,
+                   int group_size, int64_t* packed_offsets, int64_t* norm_offsets,
+                   int64_t* total_bytes);
+
+/* One tensor of cq_quantize_many (device pointers, layouts as cq_quantize). */
+typedef struct {
+  const void* w;     /* rows x cols, the call's w_dtype */
+  int64_t rows;
+  int64_t cols;
+  uint8_t* packed;   /* [rows][ceil(cols/G)][G*sbits/8] */
+  uint16_t* norms;   /* [rows][ceil(cols/G)] */
+} cq_quant_desc;
+
+/* cq_quantize over n tensors (descs: host array) sharing w_dtype, bits and
+ * levels, e.g. every weight of a model, in one call: one launch for all the
+ * tensors whose cols is a multiple of G plus one for the others, instead of
+ * one launch per tensor (a parameter tree quantized as in "Cactus Quants
+ * CQ2-bit Quantization: Extreme Compression for Edge LLMs", section The
+ * CQ2-bit Implementation Pipeline).  Results are identical to cq_quantize on
+ * each tensor.  Pointing packed/norms at the offsets of cq_blob_layout writes
+ * the serialized blob in place.  Every descriptor is validated as
+ * cq_quantize validates its arguments (the first failing tensor is reported;
+ * nothing is enqueued then); no output may overlap another output or any
+ * input of the call (CQ_ERR_ARG).  Empty tensors are skipped.  Takes
+ * 48 bytes per tensor of stream-ordered device memory for the descriptor
+ * table (hipMallocAsync / hipFreeAsync on `stream`). */
+int cq_quantize_many(int n, const cq_quant_desc* descs, int w_dtype, int bits, int group_size,
+                     const float* levels, int n_levels, void* stream);
+
+/* One tensor of cq_dequantize_many (device pointers, layouts as
+ * cq_dequantize). */
+typedef struct {
+  const uint8_t* packed;
+  const uint16_t* norms;
+  int64_t rows;
+  int64_t cols;
+  void* out;         /* rows x cols, the call's out_dtype */
+} cq_dequant_desc;
+
+/* cq_dequantize over n tensors (descs: host array) in one call, the inverse
+ * of cq_quantize_many (for example all tensors of a serialized blob).  Same
+ * launch structure, validation, overlap rule and workspace as
+ * cq_quantize_many; results identical to cq_dequantize on each tensor. */
+int cq_dequantize_many(int n, const cq_dequant_desc* descs, int bits, int group_size,
+                       const float* levels, int n_levels, int out_dtype, void* stream);
 
 /* Fake quantization: out = the reconstruction of w after quantization, in
  * one pass with no packed intermediate.  This is the quantize-then-rebuild

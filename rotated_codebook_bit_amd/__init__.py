@@ -17,6 +17,7 @@ import numpy as np
 __all__ = [
     "TERNARY", "GROUP", "CQError", "lib", "storage_bits", "n_levels", "layout",
     "model_bytes", "codebook", "quantize", "dequantize", "dequant_matvec", "dequant_matvec_many",
+    "fake_quant", "blob_layout", "quantize_many", "dequantize_many",
 ]
 
 TERNARY = 158
@@ -34,6 +35,18 @@ class CQError(RuntimeError):
     def __init__(self, func: str, status: int, detail: str):
         super().__init__(f"{func}: {detail} (status {status})")
         self.status = status
+
+
+class QuantDesc(ctypes.Structure):
+    """cq_quant_desc: one tensor of cq_quantize_many."""
+    _fields_ = [("w", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("packed", ctypes.c_void_p), ("norms", ctypes.c_void_p)]
+
+
+class DequantDesc(ctypes.Structure):
+    """cq_dequant_desc: one tensor of cq_dequantize_many."""
+    _fields_ = [("packed", ctypes.c_void_p), ("norms", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("out", ctypes.c_void_p)]
 
 
 class MatvecDesc(ctypes.Structure):
@@ -59,6 +72,12 @@ def lib() -> ctypes.CDLL:
                                   vp, vp, vp]
         L.cq_dequantize.argtypes = [vp, vp, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_float), i32,
                                     vp, i32, vp]
+        L.cq_blob_layout.argtypes = [i32, ctypes.POINTER(i64), ctypes.POINTER(i64), i32, i32,
+                                     ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        L.cq_quantize_many.argtypes = [i32, ctypes.POINTER(QuantDesc), i32, i32, i32,
+                                       ctypes.POINTER(ctypes.c_float), i32, vp]
+        L.cq_dequantize_many.argtypes = [i32, ctypes.POINTER(DequantDesc), i32, i32,
+                                         ctypes.POINTER(ctypes.c_float), i32, i32, vp]
         L.cq_fake_quant.argtypes = [vp, i32, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_float), i32,
                                     vp, i32, vp]
         L.cq_dequant_matvec.argtypes = [vp, vp, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_float),
@@ -66,7 +85,8 @@ def lib() -> ctypes.CDLL:
         L.cq_dequant_matvec_many.argtypes = [i32, ctypes.POINTER(MatvecDesc), i32, i32,
                                              ctypes.POINTER(ctypes.c_float), i32, i64, vp]
         for name in ("cq_layout", "cq_model_bytes", "cq_codebook", "cq_quantize", "cq_dequantize",
-                     "cq_fake_quant", "cq_dequant_matvec", "cq_dequant_matvec_many"):
+                     "cq_fake_quant", "cq_dequant_matvec", "cq_dequant_matvec_many", "cq_blob_layout",
+                     "cq_quantize_many", "cq_dequantize_many"):
             getattr(L, name).restype = i32
         L.cq_status_str.argtypes = [i32]
         L.cq_status_str.restype = ctypes.c_char_p
@@ -254,3 +274,82 @@ def dequant_matvec_many(items, bits: int, levels, batch: int, group_size: int = 
     _check("cq_dequant_matvec_many", lib().cq_dequant_matvec_many(n, arr, bits, group_size, lvp, lv.size,
                                                                   batch, _stream_ptr(stream)))
     return [it[5] for it in items]
+
+
+def blob_layout(shapes, bits: int, group_size: int = GROUP):
+    """Offsets of the serialized form (all packed indices, then all norms) of
+    tensors with the given shapes: (packed_offsets, norm_offsets, total)."""
+    dims = [_rows_cols(tuple(sh)) for sh in shapes]
+    n = len(dims)
+    rows = (ctypes.c_int64 * max(n, 1))(*[r for r, _ in dims])
+    cols = (ctypes.c_int64 * max(n, 1))(*[c for _, c in dims])
+    po = (ctypes.c_int64 * max(n, 1))()
+    no = (ctypes.c_int64 * max(n, 1))()
+    total = ctypes.c_int64()
+    _check("cq_blob_layout", lib().cq_blob_layout(n, rows, cols, bits, group_size, po, no,
+                                                  ctypes.byref(total)))
+    return list(po)[:n], list(no)[:n], total.value
+
+
+def quantize_many(ws, bits: int, levels, blob=None, group_size: int = GROUP, stream=None,
+                  views: bool = True):
+    """Quantize a list of CUDA tensors (all float32 or all bfloat16) in one
+    call, writing the serialized blob (uint8, all packed indices then all
+    norms).  Returns (blob, [(packed [rows, ng, G*sbits/8], norms float16
+    [rows, ng]) views into the blob, one per tensor]); with views=False the
+    list is empty (blob_layout gives the offsets)."""
+    import torch
+    if not ws:
+        return torch.zeros(0, dtype=torch.uint8), []
+    dt = {torch.float32: F32, torch.bfloat16: BF16}.get(ws[0].dtype)
+    if dt is None or any(w.dtype != ws[0].dtype for w in ws):
+        raise TypeError("all tensors must be float32, or all bfloat16")
+    if any(not w.is_contiguous() for w in ws):
+        raise ValueError("tensors must be contiguous")
+    po, no, total = blob_layout([tuple(w.shape) for w in ws], bits, group_size)
+    if blob is None:
+        blob = torch.empty(total, dtype=torch.uint8, device=ws[0].device)
+    if blob.dtype != torch.uint8 or blob.numel() != total or not blob.is_contiguous():
+        raise ValueError(f"blob must be a contiguous uint8 tensor of {total} bytes")
+    pb = group_size * storage_bits(bits) // 8
+    base = blob.data_ptr() if total else 0
+    out_views = []
+    arr = (QuantDesc * len(ws))()
+    for i, w in enumerate(ws):
+        rows, cols = _rows_cols(tuple(w.shape))
+        ng = -(-cols // group_size) if cols else 0
+        empty = rows * cols == 0
+        arr[i] = QuantDesc(0 if empty else w.data_ptr(), rows, cols, 0 if empty else base + po[i],
+                           0 if empty else base + no[i])
+        if views:
+            pk = blob[po[i]:po[i] + rows * ng * pb].view(rows, ng, pb)
+            nm = blob[no[i]:no[i] + 2 * rows * ng].view(torch.float16).view(rows, ng)
+            out_views.append((pk, nm))
+    lv, lvp = _levels_arg(levels)
+    _check("cq_quantize_many", lib().cq_quantize_many(len(ws), arr, dt, bits, group_size, lvp, lv.size,
+                                                      _stream_ptr(stream)))
+    return blob, out_views
+
+
+def dequantize_many(items, bits: int, levels, out_dtype=None, outs=None, group_size: int = GROUP,
+                    stream=None):
+    """Dequantize every (packed, norms, rows, cols) of items in one call.
+    Returns the list of [rows, cols] outputs (float32 by default, or
+    bfloat16; ``outs`` supplies them)."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    dt = {torch.float32: F32, torch.bfloat16: BF16}[out_dtype]
+    if outs is None:
+        dev = items[0][0].device if items else "cpu"
+        outs = [torch.empty((r, c), dtype=out_dtype, device=dev) for _, _, r, c in items]
+    arr = (DequantDesc * max(len(items), 1))()
+    for i, ((packed, norms, rows, cols), out) in enumerate(zip(items, outs)):
+        if out.dtype != out_dtype or out.numel() != rows * cols or not out.is_contiguous():
+            raise ValueError(f"outs[{i}] must be a contiguous {out_dtype} tensor of {rows}x{cols}")
+        arr[i] = DequantDesc(packed.data_ptr() if packed.numel() else 0,
+                             norms.data_ptr() if norms.numel() else 0, rows, cols,
+                             out.data_ptr() if out.numel() else 0)
+    lv, lvp = _levels_arg(levels)
+    _check("cq_dequantize_many", lib().cq_dequantize_many(len(items), arr, bits, group_size, lvp,
+                                                          lv.size, dt, _stream_ptr(stream)))
+    return outs

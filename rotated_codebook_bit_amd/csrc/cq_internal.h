@@ -66,6 +66,70 @@ hipError_t launch_dequantize(const uint8_t* packed, const uint16_t* norms,
                              const LevelTable& lv, void* out, bool bf16_out,
                              hipStream_t stream);
 
+// ---- Multi-tensor codec calls ----------------------------------------------
+
+// One tensor of a multi-tensor quantize / dequantize call (device-side
+// descriptors, 40 bytes each).
+struct QuantDesc {
+  const uint8_t* w;  // rows x cols input (f32 or bf16)
+  uint8_t* packed;
+  uint16_t* norms;
+  int64_t rows, cols;
+};
+struct DequantDesc {
+  const uint8_t* packed;
+  const uint16_t* norms;
+  uint8_t* out;  // rows x cols output (f32 or bf16)
+  int64_t rows, cols;
+};
+
+// A device table of n descriptors plus the prefix start[0..n] of their work
+// units (64-group batches on the fast path, groups on the ragged path):
+// descriptor d owns units [start[d], start[d+1]).
+template <class D>
+struct TensorTable {
+  const D* desc;
+  const int64_t* start;
+  int n;
+};
+
+// Read-only table entry read through the constant address space: with a
+// wave-uniform address this is a scalar load (tracked apart from the vector
+// memory counter, so it never waits for the wave's loads and stores in
+// flight); with a per-lane address the compiler falls back to a vector load.
+template <class T>
+__device__ __forceinline__ T load_const(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
+// Last d in [lo, n) with start[d] <= v (start ascending, start[lo] <= v <
+// start[n]).
+__device__ __forceinline__ int find_unit(const int64_t* __restrict__ start, int lo, int n, int64_t v) {
+  int hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (load_const(start + mid) <= v)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+// Copies `bytes` (a multiple of 4) host bytes to device memory at dst with
+// kernel launches that carry them as arguments: asynchronous, and the host
+// buffer may be reused as soon as the call returns.
+hipError_t upload(const void* src, size_t bytes, void* dst, hipStream_t stream);
+
+hipError_t launch_quantize_many(bool bf16, const QuantParams& p, TensorTable<QuantDesc> contig,
+                                int64_t contig_batches, TensorTable<QuantDesc> ragged,
+                                int64_t ragged_groups, hipStream_t stream);
+
+hipError_t launch_dequantize_many(int sbits, const LevelTable& lv, bool bf16_out,
+                                  TensorTable<DequantDesc> contig, int64_t contig_batches,
+                                  TensorTable<DequantDesc> ragged, int64_t ragged_groups,
+                                  hipStream_t stream);
+
 // One matrix of a dequant-matvec call (device-side descriptor).
 struct MatvecDesc {
   const uint8_t* packed;  // [n_out][k / 128][128 * sbits / 8]

@@ -227,10 +227,48 @@ __device__ __forceinline__ void store16(const uint4& v, __amdgpu_buffer_rsrc_t d
 // The next batch's packed words and norm are loaded into registers while the
 // current batch is computed.  Stores go through a per-batch buffer resource
 // so the lanes past the end of the last batch are dropped by the hardware.
-template <int SB, bool BF16OUT>
+//
+// One launch covers one tensor (MANY = false) or a table of tensors whose
+// column counts are multiples of 128 (MANY = true, batches of each tensor
+// numbered consecutively).
+struct DequantJob {
+  const uint8_t* packed;
+  const uint16_t* norms;
+  uint8_t* out;
+  int64_t n_groups;
+  TensorTable<DequantDesc> t;
+  int64_t n_batches;
+};
+
+// Inputs and output of one 64-group batch: local batch bt of a tensor with
+// n_groups groups.
+struct DBatch {
+  const uint8_t* packed;
+  const uint16_t* norms;
+  uint8_t* out;
+  int64_t bt;
+  int64_t n_groups;
+  __device__ int nvalid() const {
+    const int64_t left = n_groups - bt * kWave;
+    return static_cast<int>(left < kWave ? left : kWave);
+  }
+};
+
+template <bool MANY>
+__device__ __forceinline__ DBatch resolve(const DequantJob& j, int64_t b, int& d) {
+  if constexpr (!MANY) {
+    return DBatch{j.packed, j.norms, j.out, b, j.n_groups};
+  } else {
+    d = find_unit(j.t.start, d, j.t.n, b);
+    const DequantDesc* q = j.t.desc + d;  // field by field: scalar loads
+    return DBatch{load_const(&q->packed), load_const(&q->norms), load_const(&q->out),
+                  b - load_const(j.t.start + d), load_const(&q->rows) * (load_const(&q->cols) / kGroup)};
+  }
+}
+
+template <int SB, bool BF16OUT, bool MANY>
 __global__ void __launch_bounds__(kBlock, 2)
-dequantize_contig(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
-                  int64_t n_groups, LevelTable lv, uint8_t* __restrict__ out) {
+dequantize_contig(DequantJob job, LevelTable lv) {
   constexpr int OB = BF16OUT ? 2 : 4;        // output bytes per element
   constexpr int GOB = kGroup * OB;           // output bytes per group
   constexpr int PB = 32 * OB;                // bytes per group per phase
@@ -247,10 +285,11 @@ dequantize_contig(const uint8_t* __restrict__ packed, const uint16_t* __restrict
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   uint8_t* const buf = lds + wave * WAVE_BYTES;
-  const int64_t n_batches = (n_groups + kWave - 1) / kWave;
+  const int64_t n_batches = job.n_batches;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
   int64_t batch = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
   if (batch >= n_batches) return;
+  int d = 0;
 
   // LDS write: this lane's chunk c of a phase goes to slot c ^ swz_w.
   const int swz_w = (lane / GPB) & (CPP - 1);
@@ -258,26 +297,27 @@ dequantize_contig(const uint8_t* __restrict__ packed, const uint16_t* __restrict
   const int gq = lane / CPP, cc = lane % CPP;
   const uint32_t st_lane = static_cast<uint32_t>(gq * GOB + 16 * cc);
 
-  auto nvalid = [&](int64_t bt) __attribute__((always_inline)) {
-    const int64_t left = n_groups - bt * kWave;
-    return static_cast<int>(left < kWave ? left : kWave);
-  };
   uint32_t nwords[4 * SB];
   uint16_t nn16 = 0;
-  fetch_batch<SB>(packed, norms, batch, nvalid(batch), lane, nwords, nn16);
+  DBatch cur = resolve<MANY>(job, batch, d);
+  fetch_batch<SB>(cur.packed, cur.norms, cur.bt, cur.nvalid(), lane, nwords, nn16);
   for (;;) {
     uint32_t words[4 * SB];
 #pragma unroll
     for (int i = 0; i < 4 * SB; ++i) words[i] = nwords[i];
     const uint16_t n16 = nn16;
     const int64_t next = batch + stride;
-    const int nv = nvalid(batch);
-    if (next < n_batches) fetch_batch<SB>(packed, norms, next, nvalid(next), lane, nwords, nn16);
+    const int nv = cur.nvalid();
+    DBatch nxt = cur;
+    if (next < n_batches) {
+      nxt = resolve<MANY>(job, next, d);
+      fetch_batch<SB>(nxt.packed, nxt.norms, nxt.bt, nxt.nvalid(), lane, nwords, nn16);
+    }
 
     float y[kGroup];
     reconstruct_fast<SB>(words, n16, tab, y);
 
-    const auto dst = make_rsrc(out + batch * kWave * GOB, nv * GOB);
+    const auto dst = make_rsrc(cur.out + cur.bt * kWave * GOB, nv * GOB);
 #pragma unroll
     for (int ph = 0; ph < 4; ++ph) {
       // Scatter this lane's 32 values of the phase into the swizzled buffer.
@@ -306,6 +346,7 @@ dequantize_contig(const uint8_t* __restrict__ packed, const uint16_t* __restrict
         store16(v, dst, st_lane + ph * PB, static_cast<uint32_t>(GPI * i * GOB));
       }
     }
+    cur = nxt;
     batch = next;
     if (batch >= n_batches) break;
   }
@@ -313,15 +354,30 @@ dequantize_contig(const uint8_t* __restrict__ packed, const uint16_t* __restrict
 
 // General path: rows of any length; each lane writes its own group's valid
 // columns.
-template <int SB, bool BF16OUT>
+// With MANY, thread g of the launch takes group g of the concatenation of the
+// table's tensors (t.start holds group prefixes); the plain arguments are
+// ignored.
+template <int SB, bool BF16OUT, bool MANY>
 __global__ void __launch_bounds__(kBlock)
 dequantize_ragged(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
-                  int64_t rows, int64_t cols, LevelTable lv, uint8_t* __restrict__ out) {
+                  int64_t rows, int64_t cols, LevelTable lv, uint8_t* __restrict__ out,
+                  TensorTable<DequantDesc> t, int64_t total) {
   __shared__ __attribute__((aligned(16))) float tab[TableSize<SB>::floats];
   fill_table<SB>(tab, lv, threadIdx.x);
   __syncthreads();
+  int64_t g = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  if constexpr (MANY) {
+    if (g >= total) return;
+    const int d = find_unit(t.start, 0, t.n, g);
+    const DequantDesc q = t.desc[d];
+    packed = q.packed;
+    norms = q.norms;
+    out = q.out;
+    rows = q.rows;
+    cols = q.cols;
+    g -= t.start[d];
+  }
   const int64_t ngr = (cols + kGroup - 1) / kGroup;
-  const int64_t g = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
   if (g >= rows * ngr) return;
   const int64_t row = g / ngr, col0 = (g - row * ngr) * kGroup;
   const int64_t valid = cols - col0 < kGroup ? cols - col0 : kGroup;
@@ -349,15 +405,42 @@ hipError_t launch_sb(const uint8_t* packed, const uint16_t* norms, int64_t rows,
     const int64_t n_groups = rows * (cols / kGroup);
     const int64_t n_batches = (n_groups + kWave - 1) / kWave;
     const int blocks = persistent_blocks((n_batches + kWaves - 1) / kWaves, kBlocksPerCu);
-    hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT>), dim3(blocks), dim3(kBlock), 0, s, packed,
-                       norms, n_groups, lv, ob);
+    const DequantJob job{packed, norms, ob, n_groups, TensorTable<DequantDesc>{nullptr, nullptr, 0},
+                         n_batches};
+    hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT, false>), dim3(blocks), dim3(kBlock), 0, s, job, lv);
   } else {
     const int64_t n_groups = rows * ((cols + kGroup - 1) / kGroup);
     const int blocks = static_cast<int>((n_groups + kBlock - 1) / kBlock);
-    hipLaunchKernelGGL((dequantize_ragged<SB, BF16OUT>), dim3(blocks), dim3(kBlock), 0, s, packed,
-                       norms, rows, cols, lv, ob);
+    hipLaunchKernelGGL((dequantize_ragged<SB, BF16OUT, false>), dim3(blocks), dim3(kBlock), 0, s, packed,
+                       norms, rows, cols, lv, ob, TensorTable<DequantDesc>{nullptr, nullptr, 0}, int64_t{0});
   }
   return hipGetLastError();
+}
+
+template <int SB, bool BF16OUT>
+hipError_t launch_many_sb(const LevelTable& lv, TensorTable<DequantDesc> contig, int64_t contig_batches,
+                          TensorTable<DequantDesc> ragged, int64_t ragged_groups, hipStream_t s) {
+  if (contig_batches > 0) {
+    const int blocks = persistent_blocks((contig_batches + kWaves - 1) / kWaves, kBlocksPerCu);
+    const DequantJob job{nullptr, nullptr, nullptr, 0, contig, contig_batches};
+    hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT, true>), dim3(blocks), dim3(kBlock), 0, s, job, lv);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (ragged_groups > 0) {
+    const int blocks = static_cast<int>((ragged_groups + kBlock - 1) / kBlock);
+    hipLaunchKernelGGL((dequantize_ragged<SB, BF16OUT, true>), dim3(blocks), dim3(kBlock), 0, s, nullptr,
+                       nullptr, int64_t{0}, int64_t{0}, lv, nullptr, ragged, ragged_groups);
+  }
+  return hipGetLastError();
+}
+
+template <int SB>
+hipError_t launch_many_out(const LevelTable& lv, bool bf16_out, TensorTable<DequantDesc> contig,
+                           int64_t contig_batches, TensorTable<DequantDesc> ragged, int64_t ragged_groups,
+                           hipStream_t s) {
+  return bf16_out ? launch_many_sb<SB, true>(lv, contig, contig_batches, ragged, ragged_groups, s)
+                  : launch_many_sb<SB, false>(lv, contig, contig_batches, ragged, ragged_groups, s);
 }
 
 template <int SB>
@@ -376,6 +459,18 @@ hipError_t launch_dequantize(const uint8_t* packed, const uint16_t* norms, int64
     case 2: return kd::launch_out<2>(packed, norms, rows, cols, lv, out, bf16_out, stream);
     case 3: return kd::launch_out<3>(packed, norms, rows, cols, lv, out, bf16_out, stream);
     case 4: return kd::launch_out<4>(packed, norms, rows, cols, lv, out, bf16_out, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_dequantize_many(int sbits, const LevelTable& lv, bool bf16_out,
+                                  TensorTable<DequantDesc> contig, int64_t contig_batches,
+                                  TensorTable<DequantDesc> ragged, int64_t ragged_groups,
+                                  hipStream_t stream) {
+  switch (sbits) {
+    case 2: return kd::launch_many_out<2>(lv, bf16_out, contig, contig_batches, ragged, ragged_groups, stream);
+    case 3: return kd::launch_many_out<3>(lv, bf16_out, contig, contig_batches, ragged, ragged_groups, stream);
+    case 4: return kd::launch_many_out<4>(lv, bf16_out, contig, contig_batches, ragged, ragged_groups, stream);
     default: return hipErrorInvalidValue;
   }
 }

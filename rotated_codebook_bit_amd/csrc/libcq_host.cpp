@@ -58,8 +58,9 @@ int check_group(int group_size, bool device) {
   if (device) {
     if (group_size != cq::kGroup)
       return fail(CQ_ERR_UNSUPPORTED, "group_size=%d: device kernels support 128", group_size);
-  } else if (!is_pow2(group_size) || group_size > 4096) {
-    return fail(CQ_ERR_ARG, "group_size=%d must be a power of two <= 4096", group_size);
+  } else if (!is_pow2(group_size) || group_size < 8 || group_size > 4096) {
+    // From 8 up, a group's packed indices fill whole bytes at every width.
+    return fail(CQ_ERR_ARG, "group_size=%d must be a power of two in [8, 4096]", group_size);
   }
   return CQ_OK;
 }
@@ -84,6 +85,83 @@ int check_levels(const float* levels, int n_levels, int expect) {
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Byte range [lo, hi) of one buffer of a multi-tensor call.
+struct Span {
+  uintptr_t lo, hi;
+  int tensor;
+};
+
+Span span(const void* p, size_t bytes, int tensor) {
+  const auto a = reinterpret_cast<uintptr_t>(p);
+  return Span{a, a + bytes, tensor};
+}
+
+// Index of a tensor whose buffers conflict (two outputs overlap, or an input
+// overlaps an output), or -1.  Inputs may overlap each other.
+int first_conflict(std::vector<Span> outs, const std::vector<Span>& ins) {
+  std::sort(outs.begin(), outs.end(), [](const Span& a, const Span& b) { return a.lo < b.lo; });
+  for (size_t i = 1; i < outs.size(); ++i)
+    if (outs[i].lo < outs[i - 1].hi) return outs[i].tensor;
+  for (const Span& in : ins) {
+    // The last output starting before the input ends is the only candidate:
+    // outputs are disjoint and sorted.
+    auto it = std::lower_bound(outs.begin(), outs.end(), in.hi,
+                               [](const Span& o, uintptr_t v) { return o.lo < v; });
+    if (it != outs.begin() && std::prev(it)->hi > in.lo) return in.tensor;
+  }
+  return -1;
+}
+
+int hip_status(hipError_t e, const char* what);
+
+// Device table of one multi-tensor call: descriptors of the fast-path
+// (cols % 128 == 0) and ragged tensors, with their work-unit prefixes, in one
+// stream-ordered allocation.
+template <class D>
+struct ManyTables {
+  std::vector<D> contig, ragged;
+  std::vector<int64_t> bstart{0}, gstart{0};  // 64-group batches / groups
+  uint8_t* ws = nullptr;
+  cq::TensorTable<D> tc{}, tr{};
+
+  void add(const D& d, int64_t n_groups, bool fast) {
+    if (fast) {
+      contig.push_back(d);
+      bstart.push_back(bstart.back() + ceil_div(n_groups, cq::kWave));
+    } else {
+      ragged.push_back(d);
+      gstart.push_back(gstart.back() + n_groups);
+    }
+  }
+  bool empty() const { return contig.empty() && ragged.empty(); }
+
+  // Allocates the workspace on `s` and uploads the tables.
+  int upload(hipStream_t s) {
+    auto up = [](size_t v) { return (v + 255) & ~size_t(255); };
+    const size_t b0 = up(contig.size() * sizeof(D)), b1 = up(bstart.size() * 8);
+    const size_t b2 = up(ragged.size() * sizeof(D)), b3 = up(gstart.size() * 8);
+    int rc = hip_status(hipMallocAsync(reinterpret_cast<void**>(&ws), b0 + b1 + b2 + b3, s),
+                        "table alloc");
+    if (rc) return rc;
+    auto* dc = reinterpret_cast<D*>(ws);
+    auto* sc = reinterpret_cast<int64_t*>(ws + b0);
+    auto* dr = reinterpret_cast<D*>(ws + b0 + b1);
+    auto* sr = reinterpret_cast<int64_t*>(ws + b0 + b1 + b2);
+    tc = cq::TensorTable<D>{dc, sc, static_cast<int>(contig.size())};
+    tr = cq::TensorTable<D>{dr, sr, static_cast<int>(ragged.size())};
+    if (!contig.empty()) {
+      rc = hip_status(cq::upload(contig.data(), contig.size() * sizeof(D), dc, s), "table upload");
+      if (!rc) rc = hip_status(cq::upload(bstart.data(), bstart.size() * 8, sc, s), "table upload");
+    }
+    if (!rc && !ragged.empty()) {
+      rc = hip_status(cq::upload(ragged.data(), ragged.size() * sizeof(D), dr, s), "table upload");
+      if (!rc) rc = hip_status(cq::upload(gstart.data(), gstart.size() * 8, sr, s), "table upload");
+    }
+    return rc;
+  }
+  int release(hipStream_t s) { return ws ? hip_status(hipFreeAsync(ws, s), "table free") : CQ_OK; }
+};
 
 // Decision constants for the quantize kernels.  The index of a value z is
 // the number of midpoint thresholds strictly below it.  For three and four
@@ -270,6 +348,119 @@ int cq_quantize(const void* w, int w_dtype, int64_t rows, int64_t cols, int bits
   return hip_status(cq::launch_quantize(w, w_dtype == CQ_BF16, rows, cols, p, packed, norms,
                                         static_cast<hipStream_t>(stream)),
                     "quantize launch");
+}
+
+int cq_quantize_many(int n, const cq_quant_desc* descs, int w_dtype, int bits, int group_size,
+                     const float* levels, int n_levels, void* stream) {
+  g_last_error[0] = 0;
+  int L, rc;
+  if ((rc = check_bits(bits, false, &L))) return rc;
+  if (w_dtype != CQ_F32 && w_dtype != CQ_BF16) return fail(CQ_ERR_ARG, "unknown w_dtype %d", w_dtype);
+  if (n < 0) return fail(CQ_ERR_ARG, "n < 0");
+  if ((rc = check_group(group_size, true))) return rc;
+  if ((rc = check_levels(levels, n_levels, L))) return rc;
+  if (n == 0) return CQ_OK;
+  if (!descs) return fail(CQ_ERR_NULL, "descs is NULL");
+  const size_t esz = w_dtype == CQ_F32 ? 4 : 2;
+  const int sb = storage_bits(bits);
+  ManyTables<cq::QuantDesc> t;
+  std::vector<Span> outs, ins;
+  for (int i = 0; i < n; ++i) {
+    const cq_quant_desc& d = descs[i];
+    if (d.rows < 0 || d.cols < 0) return fail(CQ_ERR_ARG, "tensor %d: negative size", i);
+    if (d.rows == 0 || d.cols == 0) continue;
+    if (!d.w || !d.packed || !d.norms) return fail(CQ_ERR_NULL, "tensor %d: w/packed/norms is NULL", i);
+    if (!aligned(d.w, 16) || !aligned(d.packed, 16) || !aligned(d.norms, 2))
+      return fail(CQ_ERR_ALIGN, "tensor %d: w and packed need 16-byte, norms 2-byte alignment", i);
+    const int64_t ng = d.rows * ceil_div(d.cols, group_size);
+    ins.push_back(span(d.w, static_cast<size_t>(d.rows * d.cols) * esz, i));
+    outs.push_back(span(d.packed, static_cast<size_t>(ng) * group_size * sb / 8, i));
+    outs.push_back(span(d.norms, static_cast<size_t>(ng) * 2, i));
+    t.add(cq::QuantDesc{static_cast<const uint8_t*>(d.w), d.packed, d.norms, d.rows, d.cols}, ng,
+          d.cols % group_size == 0);
+  }
+  const int bad = first_conflict(outs, ins);
+  if (bad >= 0) return fail(CQ_ERR_ARG, "tensor %d: buffers overlap another buffer of the call", bad);
+  if (t.empty()) return CQ_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const cq::QuantParams p = make_quant_params(levels, L);
+  rc = t.upload(s);
+  if (!rc)
+    rc = hip_status(cq::launch_quantize_many(w_dtype == CQ_BF16, p, t.tc, t.bstart.back(), t.tr,
+                                             t.gstart.back(), s),
+                    "quantize launch");
+  const int rc2 = t.release(s);
+  return rc ? rc : rc2;
+}
+
+int cq_dequantize_many(int n, const cq_dequant_desc* descs, int bits, int group_size,
+                       const float* levels, int n_levels, int out_dtype, void* stream) {
+  g_last_error[0] = 0;
+  int L, rc;
+  if ((rc = check_bits(bits, false, &L))) return rc;
+  if (out_dtype != CQ_F32 && out_dtype != CQ_BF16)
+    return fail(CQ_ERR_ARG, "unknown out_dtype %d", out_dtype);
+  if (n < 0) return fail(CQ_ERR_ARG, "n < 0");
+  if ((rc = check_group(group_size, true))) return rc;
+  if ((rc = check_levels(levels, n_levels, L))) return rc;
+  if (n == 0) return CQ_OK;
+  if (!descs) return fail(CQ_ERR_NULL, "descs is NULL");
+  const size_t esz = out_dtype == CQ_F32 ? 4 : 2;
+  const int sb = storage_bits(bits);
+  ManyTables<cq::DequantDesc> t;
+  std::vector<Span> outs, ins;
+  for (int i = 0; i < n; ++i) {
+    const cq_dequant_desc& d = descs[i];
+    if (d.rows < 0 || d.cols < 0) return fail(CQ_ERR_ARG, "tensor %d: negative size", i);
+    if (d.rows == 0 || d.cols == 0) continue;
+    if (!d.packed || !d.norms || !d.out) return fail(CQ_ERR_NULL, "tensor %d: packed/norms/out is NULL", i);
+    if (!aligned(d.out, 16) || !aligned(d.packed, 16) || !aligned(d.norms, 2))
+      return fail(CQ_ERR_ALIGN, "tensor %d: out and packed need 16-byte, norms 2-byte alignment", i);
+    const int64_t ng = d.rows * ceil_div(d.cols, group_size);
+    ins.push_back(span(d.packed, static_cast<size_t>(ng) * group_size * sb / 8, i));
+    ins.push_back(span(d.norms, static_cast<size_t>(ng) * 2, i));
+    outs.push_back(span(d.out, static_cast<size_t>(d.rows * d.cols) * esz, i));
+    t.add(cq::DequantDesc{d.packed, d.norms, static_cast<uint8_t*>(d.out), d.rows, d.cols}, ng,
+          d.cols % group_size == 0);
+  }
+  const int bad = first_conflict(outs, ins);
+  if (bad >= 0) return fail(CQ_ERR_ARG, "tensor %d: buffers overlap another buffer of the call", bad);
+  if (t.empty()) return CQ_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const cq::LevelTable lv = make_table(levels, L);
+  rc = t.upload(s);
+  if (!rc)
+    rc = hip_status(cq::launch_dequantize_many(sb, lv, out_dtype == CQ_BF16, t.tc, t.bstart.back(), t.tr,
+                                               t.gstart.back(), s),
+                    "dequantize launch");
+  const int rc2 = t.release(s);
+  return rc ? rc : rc2;
+}
+
+int cq_blob_layout(int n_tensors, const int64_t* rows, const int64_t* cols, int bits, int group_size,
+                   int64_t* packed_offsets, int64_t* norm_offsets, int64_t* total_bytes) {
+  g_last_error[0] = 0;
+  int rc;
+  if (n_tensors < 0) return fail(CQ_ERR_ARG, "n_tensors < 0");
+  if (n_tensors > 0 && (!rows || !cols)) return fail(CQ_ERR_NULL, "rows/cols is NULL");
+  if ((rc = check_bits(bits, true, nullptr))) return rc;
+  if ((rc = check_group(group_size, false))) return rc;
+  const int64_t per_group = static_cast<int64_t>(group_size) * storage_bits(bits) / 8;
+  int64_t packed_total = 0, norms_total = 0;
+  for (int i = 0; i < n_tensors; ++i) {
+    if (rows[i] < 0 || cols[i] < 0) return fail(CQ_ERR_ARG, "tensor %d has a negative size", i);
+    packed_total += rows[i] * ceil_div(cols[i], group_size) * per_group;
+  }
+  int64_t p = 0;
+  for (int i = 0; i < n_tensors; ++i) {
+    const int64_t ng = rows[i] * ceil_div(cols[i], group_size);
+    if (packed_offsets) packed_offsets[i] = p;
+    if (norm_offsets) norm_offsets[i] = packed_total + norms_total;
+    p += ng * per_group;
+    norms_total += 2 * ng;
+  }
+  if (total_bytes) *total_bytes = packed_total + norms_total;
+  return CQ_OK;
 }
 
 int cq_fake_quant(const void* w, int w_dtype, int64_t rows, int64_t cols, int bits,

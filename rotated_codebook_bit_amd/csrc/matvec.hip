@@ -274,10 +274,17 @@ __global__ void __launch_bounds__(kBlock) zero_kernel(float* __restrict__ y, int
   if (i < count) y[i] = 0.0f;
 }
 
+// Rows per block for NB batch rows: RB * NB <= 32 keeps the accumulators in
+// registers; batch 1 uses 16 (a smaller reduction buffer and more resident
+// blocks measured faster than 32).
+constexpr int rows_per_block(int nb) {
+  return nb <= 1 ? 16 : 32 / (nb <= 2 ? 2 : nb <= 4 ? 4 : 8);
+}
+
 template <int SB, int NB>
 hipError_t launch_nb(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks,
                      const LevelTable& lv, const float* xr, int64_t b0, hipStream_t s) {
-  constexpr int RB = 32 / (NB <= 1 ? 1 : NB <= 2 ? 2 : NB <= 4 ? 4 : 8);
+  constexpr int RB = rows_per_block(NB);
   // One block per row block: the blocks are short, and letting the hardware
   // refill free slots measured faster than a resident grid that loops.
   hipLaunchKernelGGL((matvec_kernel<SB, NB, RB>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
@@ -302,7 +309,7 @@ hipError_t launch_sb(const MatvecDesc* table, const int64_t* bstart, int n, int6
 
 }  // namespace km
 
-int matvec_rows_per_block(int nb) { return 32 / (nb <= 1 ? 1 : nb <= 2 ? 2 : nb <= 4 ? 4 : 8); }
+int matvec_rows_per_block(int nb) { return km::rows_per_block(nb); }
 
 hipError_t launch_rotate(const MatvecDesc* table, const int64_t* gstart, int n, int64_t total_groups,
                          float* xr, hipStream_t stream) {

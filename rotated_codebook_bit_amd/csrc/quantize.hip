@@ -283,10 +283,48 @@ __device__ __forceinline__ void store_batch(uint8_t* __restrict__ packed, uint16
 // and computes.  The compiler waits for the direct-to-LDS loads (with a full
 // vmcnt(0)) right before the next LDS reads; deferring the stores by one
 // iteration means that wait finds only long-finished stores in flight.
-template <int L, bool BF16>
+//
+// One launch covers either one tensor (MANY = false: job.w, job.packed,
+// job.norms, job.n_groups) or a table of tensors whose column counts are
+// multiples of 128 (MANY = true: job.t, with the batches of each tensor
+// numbered consecutively; a tensor's last batch may be partial).
+struct QuantJob {
+  const uint8_t* w;
+  uint8_t* packed;
+  uint16_t* norms;
+  int64_t n_groups;
+  TensorTable<QuantDesc> t;
+  int64_t n_batches;
+};
+
+// Input and outputs of one 64-group batch: local batch bt of a tensor with
+// n_groups groups.
+struct QBatch {
+  const uint8_t* w;
+  uint8_t* packed;
+  uint16_t* norms;
+  int64_t bt;
+  int64_t n_groups;
+};
+
+// Batch b of the launch.  d carries the tensor index of the wave's previous
+// batch (batches only increase, so the search starts there).
+template <bool MANY>
+__device__ __forceinline__ QBatch resolve(const QuantJob& j, int64_t b, int& d) {
+  if constexpr (!MANY) {
+    return QBatch{j.w, j.packed, j.norms, b, j.n_groups};
+  } else {
+    d = find_unit(j.t.start, d, j.t.n, b);
+    // Field by field: each is then a scalar load (an aggregate copy is not).
+    const QuantDesc* q = j.t.desc + d;
+    return QBatch{load_const(&q->w), load_const(&q->packed), load_const(&q->norms),
+                  b - load_const(j.t.start + d), load_const(&q->rows) * (load_const(&q->cols) / kGroup)};
+  }
+}
+
+template <int L, bool BF16, bool MANY>
 __global__ void __launch_bounds__(kBlock, 2)
-quantize_contig(const uint8_t* __restrict__ w, int64_t n_groups, QuantParams p,
-                uint8_t* __restrict__ packed, uint16_t* __restrict__ norms) {
+quantize_contig(QuantJob job, QuantParams p) {
   constexpr int GB = BF16 ? 256 : 512;  // input bytes per group
   constexpr int CPG = GB / 16;          // 16-byte chunks per group
   constexpr int WAVE_BYTES = kWave * GB;
@@ -296,10 +334,11 @@ quantize_contig(const uint8_t* __restrict__ w, int64_t n_groups, QuantParams p,
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   uint8_t* const buf = lds + wave * WAVE_BYTES;
-  const int64_t n_batches = (n_groups + kWave - 1) / kWave;
+  const int64_t n_batches = job.n_batches;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
   int64_t batch = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
   if (batch >= n_batches) return;
+  int d = 0;
 
   // Load instruction i, lane l fills LDS slot 64 i + l (16 bytes each): group
   // gs = GPI*i + q with q = l / CPG, physical chunk cl = l % CPG, which holds
@@ -326,8 +365,9 @@ quantize_contig(const uint8_t* __restrict__ w, int64_t n_groups, QuantParams p,
 
   uint32_t words[Shape<L>::words];
   uint16_t n16 = 0;
-  int64_t prev = -1;  // batch whose results are waiting in words / n16
-  issue_batch<GB, NI, R>(w, batch, n_groups, buf, lane_part);
+  bool have_prev = false;  // results of batch `prev` are waiting in words / n16
+  QBatch cur = resolve<MANY>(job, batch, d), prev = cur;
+  issue_batch<GB, NI, R>(cur.w, cur.bt, cur.n_groups, buf, lane_part);
   for (;;) {
     uint32_t raw[GB / 4];
 #pragma unroll
@@ -342,9 +382,13 @@ quantize_contig(const uint8_t* __restrict__ w, int64_t n_groups, QuantParams p,
     // Keep the deferred stores (and the next DMA) after the LDS reads, i.e.
     // after the loop-head wait, instead of letting them float above it.
     asm volatile("" ::: "memory");
-    if (prev >= 0) store_batch<L>(packed, norms, prev, n_groups, lane, words, n16);
+    if (have_prev) store_batch<L>(prev.packed, prev.norms, prev.bt, prev.n_groups, lane, words, n16);
     const int64_t next = batch + stride;
-    if (next < n_batches) issue_batch<GB, NI, R>(w, next, n_groups, buf, lane_part);
+    QBatch nxt = cur;
+    if (next < n_batches) {
+      nxt = resolve<MANY>(job, next, d);
+      issue_batch<GB, NI, R>(nxt.w, nxt.bt, nxt.n_groups, buf, lane_part);
+    }
 
     float y[kGroup];
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
@@ -372,22 +416,39 @@ quantize_contig(const uint8_t* __restrict__ w, int64_t n_groups, QuantParams p,
       }
     }
     n16 = finish_group<L>(y, (s0 + s1) + (s2 + s3), p, words);
-    prev = batch;
+    prev = cur;
+    have_prev = true;
+    cur = nxt;
     batch = next;
     if (batch >= n_batches) break;
   }
-  store_batch<L>(packed, norms, prev, n_groups, lane, words, n16);
+  store_batch<L>(prev.packed, prev.norms, prev.bt, prev.n_groups, lane, words, n16);
 }
 
 // General path: rows whose length is not a multiple of 128; the last group
 // of each row is zero-padded.  Each lane gathers its own group.
-template <int L, bool BF16>
+// With MANY, thread g of the launch takes group g of the concatenation of the
+// table's tensors (t.start holds group prefixes) and the plain arguments are
+// ignored.
+template <int L, bool BF16, bool MANY>
 __global__ void __launch_bounds__(kBlock)
 quantize_ragged(const uint8_t* __restrict__ w, int64_t rows, int64_t cols, QuantParams p,
-                uint8_t* __restrict__ packed, uint16_t* __restrict__ norms) {
+                uint8_t* __restrict__ packed, uint16_t* __restrict__ norms,
+                TensorTable<QuantDesc> t, int64_t total) {
+  int64_t g = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  if constexpr (MANY) {
+    if (g >= total) return;
+    const int d = find_unit(t.start, 0, t.n, g);
+    const QuantDesc q = t.desc[d];
+    w = q.w;
+    packed = q.packed;
+    norms = q.norms;
+    rows = q.rows;
+    cols = q.cols;
+    g -= t.start[d];
+  }
   const int64_t ngr = (cols + kGroup - 1) / kGroup;
   const int64_t n_groups = rows * ngr;
-  const int64_t g = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
   if (g >= n_groups) return;
   const int64_t row = g / ngr, gi = g - row * ngr;
   const int64_t col0 = gi * kGroup;
@@ -724,15 +785,41 @@ hipError_t launch_l(const void* w, int64_t rows, int64_t cols, const QuantParams
     // built for); each wave loops over batches so the next batch's DMA
     // overlaps the current arithmetic.
     const int blocks = persistent_blocks((n_batches + kWaves - 1) / kWaves, kBlocksPerCu);
-    hipLaunchKernelGGL((quantize_contig<L, BF16>), dim3(blocks), dim3(kBlock), 0, s, wb, n_groups,
-                       p, packed, norms);
+    const QuantJob job{wb, packed, norms, n_groups, TensorTable<QuantDesc>{nullptr, nullptr, 0}, n_batches};
+    hipLaunchKernelGGL((quantize_contig<L, BF16, false>), dim3(blocks), dim3(kBlock), 0, s, job, p);
   } else {
     const int64_t n_groups = rows * ((cols + kGroup - 1) / kGroup);
     const int blocks = static_cast<int>((n_groups + kBlock - 1) / kBlock);
-    hipLaunchKernelGGL((quantize_ragged<L, BF16>), dim3(blocks), dim3(kBlock), 0, s, wb, rows,
-                       cols, p, packed, norms);
+    hipLaunchKernelGGL((quantize_ragged<L, BF16, false>), dim3(blocks), dim3(kBlock), 0, s, wb, rows,
+                       cols, p, packed, norms, TensorTable<QuantDesc>{nullptr, nullptr, 0}, int64_t{0});
   }
   return hipGetLastError();
+}
+
+template <int L, bool BF16>
+hipError_t launch_many_l(const QuantParams& p, TensorTable<QuantDesc> contig, int64_t contig_batches,
+                         TensorTable<QuantDesc> ragged, int64_t ragged_groups, hipStream_t s) {
+  if (contig_batches > 0) {
+    const int blocks = persistent_blocks((contig_batches + kWaves - 1) / kWaves, kBlocksPerCu);
+    const QuantJob job{nullptr, nullptr, nullptr, 0, contig, contig_batches};
+    hipLaunchKernelGGL((quantize_contig<L, BF16, true>), dim3(blocks), dim3(kBlock), 0, s, job, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (ragged_groups > 0) {
+    const int blocks = static_cast<int>((ragged_groups + kBlock - 1) / kBlock);
+    hipLaunchKernelGGL((quantize_ragged<L, BF16, true>), dim3(blocks), dim3(kBlock), 0, s, nullptr,
+                       int64_t{0}, int64_t{0}, p, nullptr, nullptr, ragged, ragged_groups);
+  }
+  return hipGetLastError();
+}
+
+template <int L>
+hipError_t launch_many_dtype(bool bf16, const QuantParams& p, TensorTable<QuantDesc> contig,
+                             int64_t contig_batches, TensorTable<QuantDesc> ragged,
+                             int64_t ragged_groups, hipStream_t s) {
+  return bf16 ? launch_many_l<L, true>(p, contig, contig_batches, ragged, ragged_groups, s)
+              : launch_many_l<L, false>(p, contig, contig_batches, ragged, ragged_groups, s);
 }
 
 template <int L>
@@ -764,6 +851,18 @@ hipError_t launch_quantize(const void* w, bool bf16, int64_t rows, int64_t cols,
     case 4: return kq::launch_dtype<4>(w, bf16, rows, cols, p, packed, norms, stream);
     case 8: return kq::launch_dtype<8>(w, bf16, rows, cols, p, packed, norms, stream);
     case 16: return kq::launch_dtype<16>(w, bf16, rows, cols, p, packed, norms, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_quantize_many(bool bf16, const QuantParams& p, TensorTable<QuantDesc> contig,
+                                int64_t contig_batches, TensorTable<QuantDesc> ragged,
+                                int64_t ragged_groups, hipStream_t stream) {
+  switch (p.n_levels) {
+    case 3: return kq::launch_many_dtype<3>(bf16, p, contig, contig_batches, ragged, ragged_groups, stream);
+    case 4: return kq::launch_many_dtype<4>(bf16, p, contig, contig_batches, ragged, ragged_groups, stream);
+    case 8: return kq::launch_many_dtype<8>(bf16, p, contig, contig_batches, ragged, ragged_groups, stream);
+    case 16: return kq::launch_many_dtype<16>(bf16, p, contig, contig_batches, ragged, ragged_groups, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -4,6 +4,7 @@ every argument-validation error is returned before any HIP call (so fake
 device pointers are safe here)."""
 
 import ctypes
+import json
 import os
 import re
 
@@ -233,3 +234,85 @@ def test_fake_quant_validation():
     assert fq(out=ctypes.c_void_p(0x100000 + 1024)) == E_ARG        # partial overlap
     assert fq(out=FAKE, dt=1, odt=0) == E_ARG                          # in place, dtypes differ
     assert fq(rows=0, w=None, out=None) == OK
+
+
+# -- multi-tensor calls and the serialized layout -------------------------------------
+
+def test_blob_layout_equals_oracle():
+    shapes = [s for _, s in W.needle2_shapes()] + [(2, 3, 130), (1, 1), (0, 128)]
+    for bits in (O.TERNARY, 1, 2, 3, 4):
+        for g in (8, 64, 128, 256):
+            po, no, total = cq.blob_layout(shapes, bits, g)
+            want = O.blob_offsets(shapes, bits, g)
+            assert (po, no, total) == (list(want[0]), list(want[1]), want[2])
+            assert total == cq.model_bytes(shapes, bits, g)
+    ex = json.load(open(os.path.join(ROOT, "tests", "golden", "hand_examples.json")))["blob_two_groups"]
+    assert cq.blob_layout([(1, 128), (1, 128)], 2) == (ex["packed_offsets"], ex["norm_offsets"], ex["total"])
+    assert cq.blob_layout([], 2) == ([], [], 0)
+
+
+def test_blob_layout_validation():
+    L = cq.lib()
+    r = (ctypes.c_int64 * 2)(3, -1)
+    c = (ctypes.c_int64 * 2)(128, 128)
+    t = ctypes.c_int64()
+    assert L.cq_blob_layout(2, r, c, 2, 128, None, None, ctypes.byref(t)) == E_ARG
+    assert L.cq_blob_layout(1, None, c, 2, 128, None, None, ctypes.byref(t)) == E_NULL
+    assert L.cq_blob_layout(1, r, c, 2, 4, None, None, ctypes.byref(t)) == E_ARG     # G < 8
+    assert L.cq_blob_layout(1, r, c, 5, 128, None, None, ctypes.byref(t)) == E_ARG
+    assert L.cq_blob_layout(1, r, c, 2, 128, None, None, None) == OK
+    u = ctypes.c_uint64()
+    assert L.cq_model_bytes(1, r, c, 2, 4, ctypes.byref(u)) == E_ARG
+
+
+def _qdesc(w=0x100000, rows=4, cols=256, packed=0x900000, norms=0x1100000):
+    return cq.QuantDesc(w, rows, cols, packed, norms)
+
+
+def test_quantize_many_validation():
+    L = cq.lib()
+    lv, lp = _levels(4)
+
+    def qm(descs, n=None, dt=1, bits=2, g=128, nl=4):
+        arr = (cq.QuantDesc * max(len(descs), 1))(*descs)
+        return L.cq_quantize_many(len(descs) if n is None else n, arr if descs else None, dt, bits, g,
+                                  lp if nl == 4 else _levels(nl)[1], nl, None)
+
+    good = _qdesc()
+    assert qm([], n=0) == OK
+    assert qm([good], n=-1) == E_ARG
+    assert L.cq_quantize_many(1, None, 1, 2, 128, lp, 4, None) == E_NULL
+    assert qm([good], dt=2) == E_ARG
+    assert qm([good], g=64) == E_UNSUP
+    assert qm([good], nl=8) == E_ARG
+    assert qm([good, _qdesc(rows=-1)]) == E_ARG
+    assert qm([good, _qdesc(w=0)]) == E_NULL
+    assert qm([good, _qdesc(w=0x100008)]) == E_ALIGN
+    assert qm([good, _qdesc(norms=0x1100001)]) == E_ALIGN
+    # 4 x 256 bf16 = 2 KiB input, 8 groups: 256 B packed, 16 B norms
+    assert qm([good, _qdesc(w=0x200000, packed=0x900000 + 128, norms=0x1200000)]) == E_ARG  # outputs overlap
+    assert qm([good, _qdesc(w=0x200000, packed=0x100000 + 512, norms=0x1200000)]) == E_ARG  # into an input
+    assert qm([_qdesc(rows=0, w=0, packed=0, norms=0), _qdesc(cols=0, w=0, packed=0, norms=0)]) == OK
+    assert L.cq_last_error() is not None
+
+
+def test_dequantize_many_validation():
+    L = cq.lib()
+    lv, lp = _levels(4)
+    D = cq.DequantDesc
+
+    def dm(descs, n=None, dt=0, bits=2, g=128):
+        arr = (D * max(len(descs), 1))(*descs)
+        return L.cq_dequantize_many(len(descs) if n is None else n, arr if descs else None, bits, g, lp, 4,
+                                    dt, None)
+
+    good = D(0x100000, 0x900000, 4, 256, 0x1100000)
+    assert dm([], n=0) == OK
+    assert dm([good], dt=5) == E_ARG
+    assert dm([good], g=256) == E_UNSUP
+    assert dm([good, D(0, 0x900000, 4, 256, 0x1200000)]) == E_NULL
+    assert dm([good, D(0x100000, 0x900000, 4, 256, 0x1200004)]) == E_ALIGN
+    # 4 x 256 f32 = 4 KiB outputs
+    assert dm([good, D(0x100000, 0x900000, 4, 256, 0x1100000 + 4000)]) == E_ARG        # outputs overlap
+    assert dm([good, D(0x100000, 0x900000, 4, 256, 0x100000 + 16)]) == E_ARG            # out over packed
+    assert dm([D(0, 0, 0, 256, 0)]) == OK
