@@ -248,6 +248,31 @@ typedef struct {
 int cq_dequant_matvec_many(int n, const cq_matvec_desc* descs, int bits, int group_size,
                            const float* levels, int n_levels, int64_t batch, void* stream);
 
+/* Batched product y = x . W_hat^T on the matrix cores, for the same inputs,
+ * layouts, validation and workspace rules as cq_dequant_matvec (x float32
+ * [batch][k], y float32 [batch][n_out], k a multiple of G), meant for larger
+ * batches such as a prefill pass (the decode-time matvec is the batch-1 case;
+ * "Performance Differences Between 2-Bit and 4-Bit Quantization in Needle",
+ * section Practical Code Comparison, runs the quantized weights in an
+ * ordinary forward product).  The activations are rotated once per group and
+ * split into two bf16 halves (hi = bf16(v), lo = bf16(v - hi)); the levels
+ * likewise; each product is taken as hi*hi + hi*lo + lo*hi by bf16 MFMAs with
+ * float32 accumulation, then scaled by norm / G per (row, group).  Each
+ * product is then within about 3 * 2^-16 of its float32 value, so
+ * |y - exact| <= about 5e-5 * ||x_b|| * ||W_hat_n||.  Deterministic (fixed
+ * order).  Workspace: about 4 * batch * k bytes (batch rounded up to 64) per
+ * matrix, stream-ordered (hipMallocAsync / hipFreeAsync on `stream`). */
+int cq_dequant_gemm(const uint8_t* packed, const uint16_t* norms, int64_t n_out,
+                    int64_t k, int bits, int group_size, const float* levels,
+                    int n_levels, const float* x, int64_t batch, float* y,
+                    void* stream);
+
+/* cq_dequant_gemm for n matrices sharing bits, levels and batch (descs: host
+ * array, as for cq_dequant_matvec_many): one rotation launch and one product
+ * launch for the whole set.  No y may overlap another buffer of the call. */
+int cq_dequant_gemm_many(int n, const cq_matvec_desc* descs, int bits, int group_size,
+                         const float* levels, int n_levels, int64_t batch, void* stream);
+
 /* Static description of a status code. */
 const char* cq_status_str(int status);
 

@@ -17,7 +17,8 @@ import numpy as np
 __all__ = [
     "TERNARY", "GROUP", "CQError", "lib", "storage_bits", "n_levels", "layout",
     "model_bytes", "codebook", "quantize", "dequantize", "dequant_matvec", "dequant_matvec_many",
-    "fake_quant", "blob_layout", "quantize_many", "dequantize_many",
+    "fake_quant", "blob_layout", "quantize_many", "dequantize_many", "dequant_gemm",
+    "dequant_gemm_many",
 ]
 
 TERNARY = 158
@@ -78,6 +79,10 @@ def lib() -> ctypes.CDLL:
                                        ctypes.POINTER(ctypes.c_float), i32, vp]
         L.cq_dequantize_many.argtypes = [i32, ctypes.POINTER(DequantDesc), i32, i32,
                                          ctypes.POINTER(ctypes.c_float), i32, i32, vp]
+        L.cq_dequant_gemm.argtypes = [vp, vp, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_float),
+                                      i32, vp, i64, vp, vp]
+        L.cq_dequant_gemm_many.argtypes = [i32, ctypes.POINTER(MatvecDesc), i32, i32,
+                                           ctypes.POINTER(ctypes.c_float), i32, i64, vp]
         L.cq_fake_quant.argtypes = [vp, i32, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_float), i32,
                                     vp, i32, vp]
         L.cq_dequant_matvec.argtypes = [vp, vp, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_float),
@@ -86,7 +91,8 @@ def lib() -> ctypes.CDLL:
                                              ctypes.POINTER(ctypes.c_float), i32, i64, vp]
         for name in ("cq_layout", "cq_model_bytes", "cq_codebook", "cq_quantize", "cq_dequantize",
                      "cq_fake_quant", "cq_dequant_matvec", "cq_dequant_matvec_many", "cq_blob_layout",
-                     "cq_quantize_many", "cq_dequantize_many"):
+                     "cq_quantize_many", "cq_dequantize_many", "cq_dequant_gemm",
+                     "cq_dequant_gemm_many"):
             getattr(L, name).restype = i32
         L.cq_status_str.argtypes = [i32]
         L.cq_status_str.restype = ctypes.c_char_p
@@ -353,3 +359,37 @@ def dequantize_many(items, bits: int, levels, out_dtype=None, outs=None, group_s
     _check("cq_dequantize_many", lib().cq_dequantize_many(len(items), arr, bits, group_size, lvp,
                                                           lv.size, dt, _stream_ptr(stream)))
     return outs
+
+
+def dequant_gemm(packed, norms, n_out: int, k: int, bits: int, levels, x, group_size: int = GROUP,
+                 y=None, stream=None):
+    """y = x . W_hat^T on the matrix cores (split-bf16 MFMA, see
+    cq_dequant_gemm); x float32 [batch, k].  Returns float32 [batch, n_out]."""
+    import torch
+    if x.dtype != torch.float32 or not x.is_contiguous():
+        raise TypeError("x must be a contiguous float32 tensor")
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError(f"x must be [batch, {k}], got {tuple(x.shape)}")
+    batch = x.shape[0]
+    if y is None:
+        y = torch.empty((batch, n_out), dtype=torch.float32, device=x.device)
+    lv, lvp = _levels_arg(levels)
+    _check("cq_dequant_gemm", lib().cq_dequant_gemm(_ptr(packed), _ptr(norms), n_out, k, bits, group_size,
+                                                    lvp, lv.size, _ptr(x), batch, _ptr(y),
+                                                    _stream_ptr(stream)))
+    return y
+
+
+def dequant_gemm_many(items, bits: int, levels, batch: int, group_size: int = GROUP, stream=None):
+    """dequant_gemm for every (packed, norms, n_out, k, x, y) in items as one
+    call (y float32 [batch, n_out] written in place).  Returns the y list."""
+    n = len(items)
+    arr = (MatvecDesc * max(n, 1))()
+    for i, (packed, norms, n_out, k, x, y) in enumerate(items):
+        arr[i] = MatvecDesc(packed.data_ptr() if packed.numel() else 0,
+                            norms.data_ptr() if norms.numel() else 0, n_out, k,
+                            x.data_ptr() if x.numel() else 0, y.data_ptr() if y.numel() else 0)
+    lv, lvp = _levels_arg(levels)
+    _check("cq_dequant_gemm_many", lib().cq_dequant_gemm_many(n, arr, bits, group_size, lvp, lv.size, batch,
+                                                              _stream_ptr(stream)))
+    return [it[5] for it in items]

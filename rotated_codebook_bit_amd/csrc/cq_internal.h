@@ -170,4 +170,36 @@ hipError_t launch_matvec(const MatvecDesc* table, const int64_t* bstart, int n, 
 
 hipError_t launch_zero(float* y, int64_t count, hipStream_t stream);
 
+// ---- Dequantize-GEMM on the matrix cores --------------------------------------
+
+// One matrix of a GEMM call (device-side descriptor).
+struct GemmDesc {
+  const uint8_t* packed;  // [n_out][k / 128][128 * sbits / 8]
+  const uint16_t* norms;  // [n_out][k / 128]
+  const float* x;         // [batch][k]
+  float* y;               // [batch][n_out]
+  int64_t n_out;
+  int64_t k;
+  int64_t mpad;           // batch rounded up to the block's row count
+  int64_t xs_off;         // bf16 offset of this matrix's split rotated x in the workspace
+};
+
+// Levels split into bf16 halves (bits in the low 16 bits): level = hi + lo
+// up to 2^-16 relative.
+struct SplitLevels {
+  uint32_t hi[kMaxLevels];
+  uint32_t lo[kMaxLevels];
+};
+
+int gemm_block_rows();  // batch rows per GEMM block
+int gemm_block_cols();  // outputs per GEMM block
+
+// Workspace units: matrix d has (k / 128) * mpad rotate units, each writing
+// 256 bf16 values.
+hipError_t launch_split_rotate(const GemmDesc* table, const int64_t* ustart, int n, int64_t units,
+                               int64_t batch, uint16_t* ws, hipStream_t stream);
+
+hipError_t launch_gemm(const GemmDesc* table, const int64_t* bstart, int n, int64_t blocks, int sbits,
+                       const SplitLevels& sl, const uint16_t* ws, int64_t batch, hipStream_t stream);
+
 }  // namespace cq

@@ -437,6 +437,105 @@ int cq_dequantize_many(int n, const cq_dequant_desc* descs, int bits, int group_
   return rc ? rc : rc2;
 }
 
+// float32 -> bfloat16 bits, round to nearest even (finite inputs).
+uint32_t bf16_rne_host(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+int cq_dequant_gemm_many(int n, const cq_matvec_desc* descs, int bits, int group_size,
+                         const float* levels, int n_levels, int64_t batch, void* stream) {
+  g_last_error[0] = 0;
+  int L, rc;
+  if ((rc = check_bits(bits, false, &L))) return rc;
+  if (n < 0) return fail(CQ_ERR_ARG, "n < 0");
+  if (batch < 1) return fail(CQ_ERR_ARG, "batch must be >= 1");
+  if ((rc = check_group(group_size, true))) return rc;
+  if ((rc = check_levels(levels, n_levels, L))) return rc;
+  if (n == 0) return CQ_OK;
+  if (!descs) return fail(CQ_ERR_NULL, "descs is NULL");
+  const int sb = storage_bits(bits);
+  std::vector<Span> outs, ins;
+  for (int i = 0; i < n; ++i) {
+    const cq_matvec_desc& d = descs[i];
+    if (d.n_out < 0 || d.k < 0) return fail(CQ_ERR_ARG, "matrix %d: negative size", i);
+    if (d.k % group_size)
+      return fail(CQ_ERR_UNSUPPORTED, "matrix %d: k=%lld is not a multiple of %d", i, (long long)d.k,
+                  group_size);
+    if (d.n_out == 0) continue;
+    if (!d.y) return fail(CQ_ERR_NULL, "matrix %d: y is NULL", i);
+    if (!aligned(d.y, 16)) return fail(CQ_ERR_ALIGN, "matrix %d: y needs 16-byte alignment", i);
+    outs.push_back(span(d.y, static_cast<size_t>(batch * d.n_out) * 4, i));
+    if (d.k == 0) continue;
+    if (!d.packed || !d.norms || !d.x) return fail(CQ_ERR_NULL, "matrix %d: packed/norms/x is NULL", i);
+    if (!aligned(d.x, 16) || !aligned(d.packed, 16) || !aligned(d.norms, 2))
+      return fail(CQ_ERR_ALIGN, "matrix %d: x, packed need 16-byte, norms 2-byte alignment", i);
+    const int64_t ng = d.n_out * (d.k / group_size);
+    ins.push_back(span(d.packed, static_cast<size_t>(ng) * group_size * sb / 8, i));
+    ins.push_back(span(d.norms, static_cast<size_t>(ng) * 2, i));
+    ins.push_back(span(d.x, static_cast<size_t>(batch * d.k) * 4, i));
+  }
+  const int bad = first_conflict(outs, ins);
+  if (bad >= 0) return fail(CQ_ERR_ARG, "matrix %d: y overlaps another buffer of the call", bad);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  cq::SplitLevels sl{};
+  for (int i = 0; i < L; ++i) {
+    const uint32_t hi = bf16_rne_host(levels[i]);
+    float hv;
+    const uint32_t hb = hi << 16;
+    std::memcpy(&hv, &hb, 4);
+    sl.hi[i] = hi;
+    sl.lo[i] = bf16_rne_host(levels[i] - hv);
+  }
+  const int64_t bm = cq::gemm_block_rows(), bn = cq::gemm_block_cols();
+  const int64_t mpad = ceil_div(batch, bm) * bm;
+  std::vector<cq::GemmDesc> act;
+  std::vector<int64_t> ustart{0}, bstart{0};
+  int64_t xs = 0;  // bf16 values
+  for (int i = 0; i < n; ++i) {
+    const cq_matvec_desc& d = descs[i];
+    if (d.n_out == 0) continue;
+    if (d.k == 0) {
+      if ((rc = hip_status(cq::launch_zero(d.y, batch * d.n_out, s), "zero launch"))) return rc;
+      continue;
+    }
+    act.push_back(cq::GemmDesc{d.packed, d.norms, d.x, d.y, d.n_out, d.k, mpad, xs});
+    xs += (d.k / group_size) * mpad * 2 * group_size;
+    ustart.push_back(ustart.back() + (d.k / group_size) * mpad);
+    bstart.push_back(bstart.back() + (mpad / bm) * ceil_div(d.n_out, bn));
+  }
+  if (act.empty()) return CQ_OK;
+  const int na = static_cast<int>(act.size());
+  auto up = [](size_t v) { return (v + 255) & ~size_t(255); };
+  const size_t tb = up(na * sizeof(cq::GemmDesc)), sb_ = up((na + 1) * 8);
+  const size_t ws_bytes = tb + 2 * sb_ + static_cast<size_t>(xs) * 2;
+  uint8_t* ws = nullptr;
+  if ((rc = hip_status(hipMallocAsync(reinterpret_cast<void**>(&ws), ws_bytes, s), "workspace alloc")))
+    return rc;
+  auto* table = reinterpret_cast<cq::GemmDesc*>(ws);
+  auto* u_dev = reinterpret_cast<int64_t*>(ws + tb);
+  auto* b_dev = reinterpret_cast<int64_t*>(ws + tb + sb_);
+  auto* xs_dev = reinterpret_cast<uint16_t*>(ws + tb + 2 * sb_);
+  rc = hip_status(cq::upload(act.data(), na * sizeof(cq::GemmDesc), table, s), "table upload");
+  if (!rc) rc = hip_status(cq::upload(ustart.data(), (na + 1) * 8, u_dev, s), "table upload");
+  if (!rc) rc = hip_status(cq::upload(bstart.data(), (na + 1) * 8, b_dev, s), "table upload");
+  if (!rc)
+    rc = hip_status(cq::launch_split_rotate(table, u_dev, na, ustart[na], batch, xs_dev, s), "rotate launch");
+  if (!rc)
+    rc = hip_status(cq::launch_gemm(table, b_dev, na, bstart[na], sb, sl, xs_dev, batch, s), "gemm launch");
+  const int rc2 = hip_status(hipFreeAsync(ws, s), "workspace free");
+  return rc ? rc : rc2;
+}
+
+int cq_dequant_gemm(const uint8_t* packed, const uint16_t* norms, int64_t n_out, int64_t k, int bits,
+                    int group_size, const float* levels, int n_levels, const float* x, int64_t batch,
+                    float* y, void* stream) {
+  const cq_matvec_desc d{packed, norms, n_out, k, x, y};
+  return cq_dequant_gemm_many(1, &d, bits, group_size, levels, n_levels, batch, stream);
+}
+
 int cq_blob_layout(int n_tensors, const int64_t* rows, const int64_t* cols, int bits, int group_size,
                    int64_t* packed_offsets, int64_t* norm_offsets, int64_t* total_bytes) {
   g_last_error[0] = 0;

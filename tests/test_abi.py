@@ -316,3 +316,35 @@ def test_dequantize_many_validation():
     assert dm([good, D(0x100000, 0x900000, 4, 256, 0x1100000 + 4000)]) == E_ARG        # outputs overlap
     assert dm([good, D(0x100000, 0x900000, 4, 256, 0x100000 + 16)]) == E_ARG            # out over packed
     assert dm([D(0, 0, 0, 256, 0)]) == OK
+
+
+def test_gemm_validation():
+    L = cq.lib()
+    lv, lp = _levels(4)
+    D = cq.MatvecDesc
+
+    def gm(packed=FAKE, norms=FAKE2, n_out=8, k=256, bits=2, x=ctypes.c_void_p(0x2100000), batch=16,
+           y=ctypes.c_void_p(0x3100000), g=128, nl=4):
+        return L.cq_dequant_gemm(packed, norms, n_out, k, bits, g, lp, nl, x, batch, y, None)
+
+    assert gm(k=200) == E_UNSUP
+    assert gm(g=64) == E_UNSUP
+    assert gm(batch=0) == E_ARG
+    assert gm(bits=158, nl=4) == E_ARG
+    assert gm(x=None) == E_NULL
+    assert gm(y=None) == E_NULL
+    assert gm(x=ctypes.c_void_p(0x2100004)) == E_ALIGN
+    assert gm(y=ctypes.c_void_p(0x2100000)) == E_ARG               # y overlaps x
+    assert gm(y=ctypes.c_void_p(0x100000 + 32)) == E_ARG            # y overlaps packed
+    assert gm(n_out=0, packed=None, norms=None, x=None, y=None) == OK
+
+    def many(descs, batch=16):
+        arr = (D * max(len(descs), 1))(*descs)
+        return L.cq_dequant_gemm_many(len(descs), arr if descs else None, 2, 128, lp, 4, batch, None)
+
+    good = D(0x100000, 0x900000, 8, 256, 0x2100000, 0x3100000)
+    assert many([]) == OK
+    assert many([good], batch=-1) == E_ARG
+    # the second matrix's y lands on the first one's y
+    assert many([good, D(0x100000, 0x900000, 8, 256, 0x2100000, 0x3100000 + 64)]) == E_ARG
+    assert many([good, D(0x100000, 0x900000, 8, 256, 0, 0x4100000)]) == E_NULL
