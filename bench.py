@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "CQ2 quantize+dequantize Gparams/s and % of HBM peak GB/s (1×MI355X)"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16 matrix peak
 BITS = 2
 G = 128
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama7b.json")
@@ -235,6 +236,31 @@ def main():
         "GB_per_s": round(gbs(fq_bytes, tfq), 1), "bytes": fq_bytes,
         "frac_hbm_peak": round(gbs(fq_bytes, tfq) / HBM_PEAK_GBS, 4),
         "note": "not part of the step; bf16 in, bf16 out, one launch"}
+    # Prefill-style batched product through all 225 matrices on the matrix
+    # cores (split-bf16 MFMA, three MFMAs per product), batch 256.
+    GB_ = 256
+    gx = {c: torch.randn((GB_, c), generator=xg, device="cuda", dtype=torch.float32)
+          for c in sorted({c for _, c in shapes})}
+    gy = [torch.empty((GB_, r), dtype=torch.float32, device="cuda") for r, _ in shapes]
+    gitems = [(p_, nv, r, c, gx[c], gy[i]) for i, (p_, nv, r, c) in enumerate(views)]
+    cq.dequant_gemm_many(gitems, BITS, levels, GB_)
+    torch.cuda.synchronize()
+    ge = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ge[0].record(stream)
+    for _ in range(3):
+        cq.dequant_gemm_many(gitems, BITS, levels, GB_)
+    ge[1].record(stream)
+    torch.cuda.synchronize()
+    tg = ge[0].elapsed_time(ge[1]) / 3
+    alg_tf = 2 * GB_ * params / (tg * 1e-3) / 1e12
+    phases["dequant_gemm_b256_extra"] = {
+        "ms": round(tg, 4), "alg_TFLOP_per_s": round(alg_tf, 1),
+        "mfma_bf16_TFLOP_per_s_executed": round(3 * alg_tf, 1),
+        "frac_bf16_mfma_peak_executed": round(3 * alg_tf / MFMA_BF16_PEAK_TFS, 4),
+        "note": "batch-256 product through all 225 matrices (one cq_dequant_gemm_many call: rotation + "
+                "MFMA launch); fp32-grade split-bf16 arithmetic, 3 MFMAs per product; not part of the step"}
+    del gx, gy, gitems
+
     # Quantize as 225 back-to-back per-tensor calls on one stream (launch
     # gaps and small-tensor tails), against the one flat launch above.
     def per_tensor():
