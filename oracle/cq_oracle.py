@@ -43,6 +43,7 @@ import numpy as np
 # Ternary case: the pages give the 3-level codebook explicitly instead of
 # training it (*Codebook training*, §Ternary Special Case Handling).
 TERNARY = 158  # bit-width code for the "1.58-bit" three-level codebook
+TERNARY_TRITS = 159  # the same codebook stored five trits per byte
 TERNARY_LEVELS = (-1.2240064, 0.0, 1.2240064)
 
 GROUP = 128  # default group size (*CQ2 overview*, §Group-wise Weight Partitioning)
@@ -56,7 +57,7 @@ LLOYD_ITERS = 200  # (*Codebook training*, §Iterative Refinement of Quantizatio
 
 def n_levels(bits: int) -> int:
     """Number of codebook levels: 3 for the ternary code, else 2**bits."""
-    if bits == TERNARY:
+    if bits in (TERNARY, TERNARY_TRITS):
         return 3
     if bits not in (1, 2, 3, 4):
         raise ValueError(f"unsupported bit-width {bits}")
@@ -65,8 +66,20 @@ def n_levels(bits: int) -> int:
 
 def storage_bits(bits: int) -> int:
     """Bits stored per index.  The three ternary codes use a 2-bit field
-    (reading: the pages describe no trit packing)."""
+    (reading: the pages describe no trit packing).  Trit storage has no bit
+    fields (see :func:`pack_trits`)."""
+    if bits == TERNARY_TRITS:
+        raise ValueError("trit storage has no fixed-width fields")
     return 2 if bits == TERNARY else n_levels(bits).bit_length() - 1
+
+
+def group_bytes(bits: int, g: int = GROUP) -> int:
+    """Bytes of packed indices per group: g*sbits/8, or ceil(g/5) for trit
+    storage (26 at g = 128, the 1.6-bit form of the "1.58-bit" ternary
+    code; *Codebook training* §Ternary Special Case Handling)."""
+    if bits == TERNARY_TRITS:
+        return -(-g // 5)
+    return g * storage_bits(bits) // 8
 
 
 def lloyd_max(samples: np.ndarray, levels: int, iters: int = LLOYD_ITERS) -> np.ndarray:
@@ -111,7 +124,7 @@ def codebook(bits: int, samples: np.ndarray | None = None,
     :func:`lloyd_max` on ``samples`` (the caller draws them: the pages use
     400,000 standard-normal draws from a seeded generator).
     """
-    if bits == TERNARY:
+    if bits in (TERNARY, TERNARY_TRITS):
         return np.array(TERNARY_LEVELS, dtype=np.float64)
     if samples is None:
         raise ValueError("Lloyd-Max codebooks need the Gaussian samples")
@@ -193,7 +206,7 @@ class Quantized:
 
     @property
     def packed(self) -> np.ndarray:
-        return pack(self.idx, storage_bits(self.bits))
+        return pack_indices(self.idx, self.bits)
 
 
 def fp16_bits(x: np.ndarray) -> np.ndarray:
@@ -256,7 +269,7 @@ def dequantize(packed: np.ndarray, norm16: np.ndarray, rows: int, cols: int,
     columns are dropped (*CQ2 overview* §The CQ2-bit Implementation Pipeline,
     step 6)."""
     ng = -(-cols // g)
-    idx = unpack(packed, storage_bits(bits), g).reshape(rows, ng, g)
+    idx = unpack_indices(packed, bits, g).reshape(rows, ng, g)
     xh = dequantize_groups(idx, np.asarray(norm16).reshape(rows, ng), levels, g)
     return xh.reshape(rows, ng * g)[:, :cols]
 
@@ -292,6 +305,48 @@ def unpack(packed: np.ndarray, sbits: int, g: int = GROUP) -> np.ndarray:
     return idx.reshape(packed.shape[:-1] + (g,)) if packed.ndim > 1 else idx.reshape(g)
 
 
+def pack_trits(idx: np.ndarray) -> np.ndarray:
+    """Five ternary indices per byte, base 3, least significant digit first:
+    within each group, index j is digit j % 5 of byte j // 5; the last byte
+    holds the g mod 5 remaining indices (upper digits zero).  Reading: the
+    pages name the 1.58-bit ternary code but no trit layout.  [..., g] ->
+    [..., ceil(g/5)]."""
+    idx = np.asarray(idx, dtype=np.int64)
+    if idx.size and (idx.min() < 0 or idx.max() > 2):
+        raise ValueError("ternary indices are 0, 1 or 2")
+    g = idx.shape[-1]
+    nb = -(-g // 5)
+    padded = np.zeros(idx.shape[:-1] + (nb * 5,), dtype=np.int64)
+    padded[..., :g] = idx
+    digits = padded.reshape(idx.shape[:-1] + (nb, 5))
+    weights = 3 ** np.arange(5)
+    return np.sum(digits * weights, axis=-1).astype(np.uint8)
+
+
+def unpack_trits(packed: np.ndarray, g: int = GROUP) -> np.ndarray:
+    """Inverse of :func:`pack_trits`: bytes [..., ceil(g/5)] -> indices [..., g]."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    nb = -(-g // 5)
+    flat = packed.reshape(-1, nb).astype(np.int64)
+    digits = (flat[..., None] // (3 ** np.arange(5))) % 3
+    idx = digits.reshape(flat.shape[0], nb * 5)[:, :g]
+    return idx.reshape(packed.shape[:-1] + (g,)) if packed.ndim > 1 else idx.reshape(g)
+
+
+def pack_indices(idx: np.ndarray, bits: int) -> np.ndarray:
+    """Packed storage of indices for a bit-width code (bit fields, or trits)."""
+    if bits == TERNARY_TRITS:
+        return pack_trits(idx)
+    return pack(idx, storage_bits(bits))
+
+
+def unpack_indices(packed: np.ndarray, bits: int, g: int = GROUP) -> np.ndarray:
+    """Inverse of :func:`pack_indices`."""
+    if bits == TERNARY_TRITS:
+        return unpack_trits(packed, g)
+    return unpack(packed, storage_bits(bits), g)
+
+
 # ---------------------------------------------------------------------------
 # Dequantize-matvec
 # ---------------------------------------------------------------------------
@@ -316,7 +371,7 @@ def matvec_rotated(packed: np.ndarray, norm16: np.ndarray, n_out: int, k: int,
         raise ValueError("k must be a multiple of the group size")
     ng = k // g
     levels32 = runtime_levels(levels)
-    idx = unpack(packed, storage_bits(bits), g).reshape(n_out, ng, g)
+    idx = unpack_indices(packed, bits, g).reshape(n_out, ng, g)
     n = np.asarray(norm16, dtype=np.uint16).reshape(n_out, ng).view(np.float16)
     q = levels32[idx] * (n.astype(np.float64)[..., None] / math.sqrt(g))
     xr = np.asarray(x, dtype=np.float64).reshape(-1, ng, g) @ hadamard(g)
@@ -332,14 +387,14 @@ def model_bytes(shapes, bits: int, g: int = GROUP) -> int:
     indices plus one binary16 norm, nothing else (*Footprint* §Per-Group
     Storage Breakdown).  A tensor of shape (..., D) has prod(leading) *
     ceil(D/g) groups; padded groups count in full."""
-    sb = storage_bits(bits)
+    per_group = group_bytes(bits, g) + 2
     total = 0
     for shape in shapes:
         shape = tuple(int(s) for s in shape)
         d = shape[-1]
         r = int(np.prod(shape[:-1], dtype=np.int64)) if len(shape) > 1 else 1
         groups = r * (-(-d // g))
-        total += groups * (g * sb // 8 + 2)
+        total += groups * per_group
     return total
 
 
@@ -359,13 +414,13 @@ def blob_offsets(shapes, bits: int, g: int = GROUP):
     """(packed_offsets, norm_offsets, total) of :func:`serialize`'s output for
     tensors of the given shapes: byte offsets of each tensor's indices and
     norms, and the total size (which equals :func:`model_bytes`)."""
-    sb = storage_bits(bits)
+    gb = group_bytes(bits, g)
     packed, norms = [], []
     for shape in shapes:
         shape = tuple(int(s) for s in shape)
         r = int(np.prod(shape[:-1], dtype=np.int64)) if len(shape) > 1 else 1
         groups = r * (-(-shape[-1] // g))
-        packed.append(groups * g * sb // 8)
+        packed.append(groups * gb)
         norms.append(groups * 2)
     p_off = [sum(packed[:i]) for i in range(len(packed))]
     n_off = [sum(packed) + sum(norms[:i]) for i in range(len(norms))]

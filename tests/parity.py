@@ -97,8 +97,8 @@ def check_norms(norm16_gpu: np.ndarray, q: O.Quantized) -> Report:
 
 def check_quantize(packed_gpu: np.ndarray, norms_gpu: np.ndarray, q: O.Quantized,
                    enforce_count: bool = True) -> Report:
-    sb = O.storage_bits(q.bits)
-    idx = O.unpack(np.asarray(packed_gpu).reshape(-1, q.g * sb // 8), sb, q.g)
+    gb = O.group_bytes(q.bits, q.g)
+    idx = O.unpack_indices(np.asarray(packed_gpu).reshape(-1, gb), q.bits, q.g)
     rep = check_indices(idx, q, enforce_count)
     rep.update(check_norms(norms_gpu, q))
     return rep

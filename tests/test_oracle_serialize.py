@@ -51,3 +51,42 @@ def test_blob_sections_round_trip(oracle_levels):
         assert np.array_equal(blob[po:po + pk.size], pk)
         nm = blob[no:no + 2 * q.norm16.size].view("<u2")
         assert np.array_equal(nm, q.norm16.ravel())
+
+
+# -- trit storage (five ternary indices per byte) --------------------------------
+
+def test_trit_bytes_by_hand():
+    # digits least significant first: 0 + 1*3 + 2*9 + 0*27 + 1*81 = 102
+    assert O.pack_trits(np.array([0, 1, 2, 0, 1])).tolist() == [102]
+    assert O.pack_trits(np.array([2, 2, 2, 2, 2])).tolist() == [242]     # 3^5 - 1
+    assert O.pack_trits(np.array([1, 0, 0, 0, 0, 2])).tolist() == [1, 2]  # a sixth index starts byte 2
+    assert O.pack_trits(np.array([0, 0, 0, 0, 1, 1, 1])).tolist() == [81, 4]
+    assert O.unpack_trits(np.array([102, 0], dtype=np.uint8), 7).tolist() == [0, 1, 2, 0, 1, 0, 0]
+
+
+def test_trit_group_sizes():
+    assert O.group_bytes(O.TERNARY_TRITS, 128) == 26          # 125 indices in 25 bytes + 3
+    assert O.group_bytes(O.TERNARY_TRITS, 64) == 13
+    assert O.group_bytes(O.TERNARY, 128) == 32
+    # 26 + 2 bytes per 128 weights = 1.75 bits per weight, against 2.125 with 2-bit fields
+    assert O.model_bytes([(1, 128)], O.TERNARY_TRITS) * 8 / 128 == 1.75
+    shapes = [s for _, s in W.needle2_shapes()]
+    groups = sum(-(-s[-1] // 128) * int(np.prod(s[:-1])) for s in shapes)
+    assert O.model_bytes(shapes, O.TERNARY_TRITS) == groups * 28
+    assert O.blob_offsets(shapes, O.TERNARY_TRITS)[2] == groups * 28
+
+
+def test_trit_round_trip_and_consistency(oracle_levels):
+    rng = np.random.default_rng(9)
+    idx = rng.integers(0, 3, (50, 128))
+    assert np.array_equal(O.unpack_trits(O.pack_trits(idx)), idx)
+    # the same decisions as the 2-bit-field ternary storage
+    w = rng.standard_normal((6, 300))
+    lv = oracle_levels[O.TERNARY]
+    q2, q3 = O.quantize(w, O.TERNARY, lv), O.quantize(w, O.TERNARY_TRITS, lv)
+    assert np.array_equal(q2.idx, q3.idx)
+    assert q3.packed.shape[-1] == 26
+    assert np.array_equal(O.unpack_trits(q3.packed), O.unpack(q2.packed, 2))
+    d2 = O.dequantize(q2.packed, q2.norm16, 6, 300, O.TERNARY, lv)
+    d3 = O.dequantize(q3.packed, q3.norm16, 6, 300, O.TERNARY_TRITS, lv)
+    assert np.array_equal(d2, d3)
