@@ -26,12 +26,16 @@
  *   - A tensor of any rank is passed as rows x cols: rows is the product of
  *     the leading dimensions, cols the last (grouping) dimension.  Rows are
  *     contiguous, row-major.
- *   - bits is one of CQ_TERNARY, 2, 3, 4 (1 is accepted by the host-only
- *     calls).  Storage bits per index (sbits): 2 for CQ_TERNARY, else bits.
- *   - Packed layout: packed[rows][ceil(cols/G)][G*sbits/8] bytes; inside a
- *     group, index j occupies bits [sbits*j, sbits*j + sbits) of a
- *     little-endian bit stream (least significant bit first).  Groups are in
- *     row-major order.
+ *   - bits is one of CQ_TERNARY, CQ_TERNARY_TRITS, 2, 3, 4 (1 is accepted by
+ *     the host-only calls).  Storage bits per index (sbits): 2 for CQ_TERNARY,
+ *     else bits.
+ *   - Packed layout: packed[rows][ceil(cols/G)][B] bytes with B = G*sbits/8
+ *     bytes per group; inside a group, index j occupies bits
+ *     [sbits*j, sbits*j + sbits) of a little-endian bit stream (least
+ *     significant bit first).  CQ_TERNARY_TRITS instead stores B = ceil(G/5)
+ *     bytes per group (26 at G = 128): index j is base-3 digit j % 5 of byte
+ *     j / 5, least significant digit first, unused digits of the last byte
+ *     zero.  Groups are in row-major order.
  *   - Norm layout: norms[rows][ceil(cols/G)], IEEE binary16 bit patterns,
  *     round to nearest even from the float32 norm; norms above 65504 store
  *     +Inf.
@@ -46,7 +50,8 @@
  *     faults surface at the caller's next synchronisation.  Buffers must stay
  *     alive until the stream has passed the call.
  *   - rows*cols == 0 (or n_out*k == 0) is a successful no-op.
- *   - Alignment: w, out, packed, x, y must be 16-byte aligned; norms 2-byte.
+ *   - Alignment: w, out, packed, x, y must be 16-byte aligned; norms 2-byte;
+ *     packed in trit storage (CQ_TERNARY_TRITS) 2-byte.
  *   - Inputs and outputs must not overlap.  Non-finite inputs give
  *     unspecified but deterministic results.
  *   - Return value: CQ_OK (0) or a negative cq_status.  cq_last_error()
@@ -78,6 +83,12 @@ typedef enum { CQ_F32 = 0, CQ_BF16 = 1 } cq_dtype;
  * ("How Quantization Codebooks Are Trained in Cactus Quants", section Ternary
  * Special Case Handling). */
 #define CQ_TERNARY 158
+/* The same three-level code stored five indices per byte: 26 bytes per
+ * 128-group, 1.625 bits per weight before the norm (the 2-bit field form
+ * takes 32 bytes).  Accepted by the host calls, cq_quantize(_many),
+ * cq_dequantize(_many) and cq_fake_quant; the product calls decode the
+ * field form (convert with cq_repack). */
+#define CQ_TERNARY_TRITS 159
 #define CQ_GROUP 128
 #define CQ_MAX_LEVELS 16
 
@@ -272,6 +283,16 @@ int cq_dequant_gemm(const uint8_t* packed, const uint16_t* norms, int64_t n_out,
  * launch for the whole set.  No y may overlap another buffer of the call. */
 int cq_dequant_gemm_many(int n, const cq_matvec_desc* descs, int bits, int group_size,
                          const float* levels, int n_levels, int64_t batch, void* stream);
+
+/* Converts n_groups groups of three-level indices between the 2-bit field
+ * form (CQ_TERNARY, 32 bytes per group, 16-byte aligned) and trit storage
+ * (CQ_TERNARY_TRITS, 26 bytes per group, 2-byte aligned), in either
+ * direction (src_bits -> dst_bits; any other pair is CQ_ERR_ARG).
+ * group_size must be 128.  Lossless for indices 0..2; a field holding 3 or a
+ * trit byte above 242 (neither is ever written by cq_quantize) converts to
+ * unspecified in-range values.  src and dst must not overlap. */
+int cq_repack(const uint8_t* src, int src_bits, uint8_t* dst, int dst_bits, int64_t n_groups,
+              int group_size, void* stream);
 
 /* Static description of a status code. */
 const char* cq_status_str(int status);

@@ -15,13 +15,14 @@ import os
 import numpy as np
 
 __all__ = [
-    "TERNARY", "GROUP", "CQError", "lib", "storage_bits", "n_levels", "layout",
+    "TERNARY", "TERNARY_TRITS", "GROUP", "group_bytes", "repack", "CQError", "lib", "storage_bits", "n_levels", "layout",
     "model_bytes", "codebook", "quantize", "dequantize", "dequant_matvec", "dequant_matvec_many",
     "fake_quant", "blob_layout", "quantize_many", "dequantize_many", "dequant_gemm",
     "dequant_gemm_many",
 ]
 
 TERNARY = 158
+TERNARY_TRITS = 159  # the ternary code stored five indices per byte
 GROUP = 128
 F32, BF16 = 0, 1
 
@@ -83,6 +84,7 @@ def lib() -> ctypes.CDLL:
                                       i32, vp, i64, vp, vp]
         L.cq_dequant_gemm_many.argtypes = [i32, ctypes.POINTER(MatvecDesc), i32, i32,
                                            ctypes.POINTER(ctypes.c_float), i32, i64, vp]
+        L.cq_repack.argtypes = [vp, i32, vp, i32, i64, i32, vp]
         L.cq_fake_quant.argtypes = [vp, i32, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_float), i32,
                                     vp, i32, vp]
         L.cq_dequant_matvec.argtypes = [vp, vp, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_float),
@@ -92,7 +94,7 @@ def lib() -> ctypes.CDLL:
         for name in ("cq_layout", "cq_model_bytes", "cq_codebook", "cq_quantize", "cq_dequantize",
                      "cq_fake_quant", "cq_dequant_matvec", "cq_dequant_matvec_many", "cq_blob_layout",
                      "cq_quantize_many", "cq_dequantize_many", "cq_dequant_gemm",
-                     "cq_dequant_gemm_many"):
+                     "cq_dequant_gemm_many", "cq_repack"):
             getattr(L, name).restype = i32
         L.cq_status_str.argtypes = [i32]
         L.cq_status_str.restype = ctypes.c_char_p
@@ -112,11 +114,18 @@ def _check(func: str, status: int) -> None:
 
 
 def storage_bits(bits: int) -> int:
-    return 2 if bits == TERNARY else int(bits)
+    return 2 if bits in (TERNARY, TERNARY_TRITS) else int(bits)
+
+
+def group_bytes(bits: int, group_size: int = GROUP) -> int:
+    """Packed bytes per group (ceil(G/5) for trit storage)."""
+    if bits == TERNARY_TRITS:
+        return -(-group_size // 5)
+    return group_size * storage_bits(bits) // 8
 
 
 def n_levels(bits: int) -> int:
-    return 3 if bits == TERNARY else 1 << int(bits)
+    return 3 if bits in (TERNARY, TERNARY_TRITS) else 1 << int(bits)
 
 
 def _levels_arg(levels) -> tuple[np.ndarray, ctypes.POINTER(ctypes.c_float)]:
@@ -196,7 +205,7 @@ def quantize(w, bits: int, levels, group_size: int = GROUP, packed=None, norms=N
         raise ValueError("w must be contiguous")
     rows, cols = _rows_cols(w.shape)
     ng = -(-cols // group_size) if cols else 0
-    pb = group_size * storage_bits(bits) // 8
+    pb = group_bytes(bits, group_size)
     if packed is None:
         packed = torch.empty((rows, ng, pb), dtype=torch.uint8, device=w.device)
     if norms is None:
@@ -317,7 +326,7 @@ def quantize_many(ws, bits: int, levels, blob=None, group_size: int = GROUP, str
         blob = torch.empty(total, dtype=torch.uint8, device=ws[0].device)
     if blob.dtype != torch.uint8 or blob.numel() != total or not blob.is_contiguous():
         raise ValueError(f"blob must be a contiguous uint8 tensor of {total} bytes")
-    pb = group_size * storage_bits(bits) // 8
+    pb = group_bytes(bits, group_size)
     base = blob.data_ptr() if total else 0
     out_views = []
     arr = (QuantDesc * len(ws))()
@@ -393,3 +402,20 @@ def dequant_gemm_many(items, bits: int, levels, batch: int, group_size: int = GR
     _check("cq_dequant_gemm_many", lib().cq_dequant_gemm_many(n, arr, bits, group_size, lvp, lv.size, batch,
                                                               _stream_ptr(stream)))
     return [it[5] for it in items]
+
+
+def repack(src, src_bits: int, dst_bits: int, dst=None, group_size: int = GROUP, stream=None):
+    """Convert packed ternary indices between 2-bit fields (TERNARY) and trit
+    storage (TERNARY_TRITS).  src: uint8 CUDA tensor whose last dimension is
+    one group's bytes ([..., 32] or [..., 26]).  Returns dst ([..., 26] or
+    [..., 32])."""
+    import torch
+    sb, db = group_bytes(src_bits, group_size), group_bytes(dst_bits, group_size)
+    if src.dtype != torch.uint8 or src.shape[-1] != sb or not src.is_contiguous():
+        raise ValueError(f"src must be a contiguous uint8 tensor [..., {sb}]")
+    n_groups = src.numel() // sb
+    if dst is None:
+        dst = torch.empty(tuple(src.shape[:-1]) + (db,), dtype=torch.uint8, device=src.device)
+    _check("cq_repack", lib().cq_repack(_ptr(src), src_bits, _ptr(dst), dst_bits, n_groups, group_size,
+                                        _stream_ptr(stream)))
+    return dst

@@ -41,6 +41,71 @@ __device__ __forceinline__ float level_at(const LevelTable& lv, int i) {
   return v;
 }
 
+// ---- Ternary trit storage ------------------------------------------------------
+//
+// A 128-group of ternary indices (0, 1, 2) is stored in 26 bytes: index j is
+// base-3 digit j % 5 of byte j / 5, least significant digit first (the last
+// byte holds indices 125..127).  In registers the same group is either eight
+// dwords of 2-bit fields (index j at bits 2 (j % 16) of word j / 16, the
+// layout of the 2-bit kernels) or 13 dwords holding two trit bytes each in
+// their low 16 bits.
+constexpr int kTritBytes = 26;
+constexpr int kTritStorage = 5;  // storage code of the dequantize launchers for trits
+
+// 2-bit fields -> trit bytes (13 values of two bytes; Horner from the top
+// digit, all positions compile-time).
+__device__ __forceinline__ void fields_to_trits(const uint32_t (&w)[8], uint32_t (&t)[13]) {
+#pragma unroll
+  for (int k = 0; k < 13; ++k) {
+    uint32_t pair = 0;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int b = 2 * k + half;
+      uint32_t v = 0;
+#pragma unroll
+      for (int i = 4; i >= 0; --i) {
+        const int j = 5 * b + i;
+        if (j < kGroup) v = v * 3u + ((w[j / 16] >> (2 * (j % 16))) & 3u);
+      }
+      pair |= v << (8 * half);
+    }
+    t[k] = pair;
+  }
+}
+
+// Entry b of the 256-entry trit table: the five base-3 digits of b as 2-bit
+// fields (digit i at bits 2i).  Bytes above 242 never come from a
+// quantizer; they map to some in-range fields.
+__device__ __forceinline__ uint32_t trit_table_entry(uint32_t b) {
+  uint32_t f = 0;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    f |= (b % 3u) << (2 * i);
+    b /= 3u;
+  }
+  return f;
+}
+
+// Trit bytes -> 2-bit fields through the LDS table `tab`.  Byte b's fields
+// land at bit 10 b of the group's 256-bit field stream.
+__device__ __forceinline__ void trits_to_fields(const uint32_t (&t)[13], const uint16_t* tab,
+                                                uint32_t (&w)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = 0u;
+#pragma unroll
+  for (int b = 0; b < kTritBytes; ++b) {
+    const uint32_t f = tab[(t[b / 2] >> (8 * (b % 2))) & 0xFFu];
+    const int pos = 10 * b, wi = pos / 32, sh = pos % 32;
+    w[wi] |= f << sh;
+    if (sh > 22 && wi + 1 < 8) w[wi + 1] |= f >> (32 - sh);
+  }
+}
+
+// Ternary 2-bit fields <-> trit storage for n_groups groups (to_trits: src
+// holds fields).
+hipError_t launch_repack(const uint8_t* src, bool to_trits, uint8_t* dst, int64_t n_groups,
+                         hipStream_t stream);
+
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
@@ -53,7 +118,8 @@ inline int persistent_blocks(int64_t work_blocks, int per_cu) {
 }
 
 // Launchers (return hipError_t of the launch).  All sizes already validated.
-hipError_t launch_quantize(const void* w, bool bf16, int64_t rows, int64_t cols,
+// trits: store the three-level code five indices per byte (26 B per group).
+hipError_t launch_quantize(const void* w, bool bf16, bool trits, int64_t rows, int64_t cols,
                            const QuantParams& p, uint8_t* packed, uint16_t* norms,
                            hipStream_t stream);
 
@@ -121,7 +187,7 @@ __device__ __forceinline__ int find_unit(const int64_t* __restrict__ start, int 
 // buffer may be reused as soon as the call returns.
 hipError_t upload(const void* src, size_t bytes, void* dst, hipStream_t stream);
 
-hipError_t launch_quantize_many(bool bf16, const QuantParams& p, TensorTable<QuantDesc> contig,
+hipError_t launch_quantize_many(bool bf16, bool trits, const QuantParams& p, TensorTable<QuantDesc> contig,
                                 int64_t contig_batches, TensorTable<QuantDesc> ragged,
                                 int64_t ragged_groups, hipStream_t stream);
 

@@ -214,6 +214,24 @@ __device__ __forceinline__ void fetch_batch(const uint8_t* __restrict__ packed,
 #endif
 }
 
+// Trit storage (three-level code, 26 bytes per group at 2-byte alignment):
+// 13 16-bit loads per lane, one trit byte pair in each dword's low half.
+__device__ __forceinline__ void fetch_batch_trits(const uint8_t* __restrict__ packed,
+                                                  const uint16_t* __restrict__ norms, int64_t bt,
+                                                  int nv, int lane, uint32_t (&t)[13], uint16_t& n16) {
+#if defined(__HIP_DEVICE_COMPILE__)  // buffer builtins exist only for the GPU target
+  const auto src = make_rsrc(packed + bt * kWave * kTritBytes, nv * kTritBytes);
+#pragma unroll
+  for (int k = 0; k < 13; ++k) t[k] = __builtin_amdgcn_raw_buffer_load_b16(src, lane * kTritBytes + 2 * k, 0, 0);
+  const auto nsrc = make_rsrc(norms + bt * kWave, nv * 2);
+  n16 = __builtin_amdgcn_raw_buffer_load_b16(nsrc, lane * 2, 0, 0);
+#endif
+}
+
+__device__ __forceinline__ void fill_trit_table(uint16_t* ttab, int t) {
+  if (t < 256) ttab[t] = static_cast<uint16_t>(trit_table_entry(static_cast<uint32_t>(t)));
+}
+
 __device__ __forceinline__ void store16(const uint4& v, __amdgpu_buffer_rsrc_t dst, uint32_t voff,
                                         uint32_t soff) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -266,7 +284,9 @@ __device__ __forceinline__ DBatch resolve(const DequantJob& j, int64_t b, int& d
   }
 }
 
-template <int SB, bool BF16OUT, bool MANY>
+// TRITS (with SB = 2): the packed input is trit storage, converted to 2-bit
+// fields in registers.
+template <int SB, bool BF16OUT, bool MANY, bool TRITS = false>
 __global__ void __launch_bounds__(kBlock, 2)
 dequantize_contig(DequantJob job, LevelTable lv) {
   constexpr int OB = BF16OUT ? 2 : 4;        // output bytes per element
@@ -279,6 +299,8 @@ dequantize_contig(DequantJob job, LevelTable lv) {
   constexpr int NI = WAVE_BYTES / 1024;      // store instructions per phase
   __shared__ __attribute__((aligned(16))) float tab[TableSize<SB>::floats];
   __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * WAVE_BYTES];
+  __shared__ uint16_t ttab[TRITS ? 256 : 1];
+  if constexpr (TRITS) fill_trit_table(ttab, threadIdx.x);
   fill_table<SB>(tab, lv, threadIdx.x);
   __syncthreads();
 
@@ -297,21 +319,33 @@ dequantize_contig(DequantJob job, LevelTable lv) {
   const int gq = lane / CPP, cc = lane % CPP;
   const uint32_t st_lane = static_cast<uint32_t>(gq * GOB + 16 * cc);
 
-  uint32_t nwords[4 * SB];
+  constexpr int FW = TRITS ? 13 : 4 * SB;  // fetched dwords per lane
+  uint32_t nwords[FW];
   uint16_t nn16 = 0;
+  auto fetch = [&](const DBatch& b_) __attribute__((always_inline)) {
+    if constexpr (TRITS)
+      fetch_batch_trits(b_.packed, b_.norms, b_.bt, b_.nvalid(), lane, nwords, nn16);
+    else
+      fetch_batch<SB>(b_.packed, b_.norms, b_.bt, b_.nvalid(), lane, nwords, nn16);
+  };
   DBatch cur = resolve<MANY>(job, batch, d);
-  fetch_batch<SB>(cur.packed, cur.norms, cur.bt, cur.nvalid(), lane, nwords, nn16);
+  fetch(cur);
   for (;;) {
     uint32_t words[4 * SB];
+    if constexpr (TRITS) {
+      static_assert(SB == 2, "trit storage decodes to 2-bit fields");
+      trits_to_fields(nwords, ttab, words);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4 * SB; ++i) words[i] = nwords[i];
+      for (int i = 0; i < 4 * SB; ++i) words[i] = nwords[i];
+    }
     const uint16_t n16 = nn16;
     const int64_t next = batch + stride;
     const int nv = cur.nvalid();
     DBatch nxt = cur;
     if (next < n_batches) {
       nxt = resolve<MANY>(job, next, d);
-      fetch_batch<SB>(nxt.packed, nxt.norms, nxt.bt, nxt.nvalid(), lane, nwords, nn16);
+      fetch(nxt);
     }
 
     float y[kGroup];
@@ -357,12 +391,14 @@ dequantize_contig(DequantJob job, LevelTable lv) {
 // With MANY, thread g of the launch takes group g of the concatenation of the
 // table's tensors (t.start holds group prefixes); the plain arguments are
 // ignored.
-template <int SB, bool BF16OUT, bool MANY>
+template <int SB, bool BF16OUT, bool MANY, bool TRITS = false>
 __global__ void __launch_bounds__(kBlock)
 dequantize_ragged(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
                   int64_t rows, int64_t cols, LevelTable lv, uint8_t* __restrict__ out,
                   TensorTable<DequantDesc> t, int64_t total) {
   __shared__ __attribute__((aligned(16))) float tab[TableSize<SB>::floats];
+  __shared__ uint16_t ttab[TRITS ? 256 : 1];
+  if constexpr (TRITS) fill_trit_table(ttab, threadIdx.x);
   fill_table<SB>(tab, lv, threadIdx.x);
   __syncthreads();
   int64_t g = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
@@ -382,7 +418,15 @@ dequantize_ragged(const uint8_t* __restrict__ packed, const uint16_t* __restrict
   const int64_t row = g / ngr, col0 = (g - row * ngr) * kGroup;
   const int64_t valid = cols - col0 < kGroup ? cols - col0 : kGroup;
   uint32_t words[4 * SB];
-  load_indices<SB>(packed, g, words);
+  if constexpr (TRITS) {
+    uint32_t tr[13];
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(packed + g * kTritBytes);
+#pragma unroll
+    for (int k = 0; k < 13; ++k) tr[k] = src[k];
+    trits_to_fields(tr, ttab, words);
+  } else {
+    load_indices<SB>(packed, g, words);
+  }
   float y[kGroup];
   reconstruct_fast<SB>(words, norms[g], tab, y);
   const int64_t base = row * cols + col0;
@@ -397,7 +441,7 @@ dequantize_ragged(const uint8_t* __restrict__ packed, const uint16_t* __restrict
   }
 }
 
-template <int SB, bool BF16OUT>
+template <int SB, bool BF16OUT, bool TRITS>
 hipError_t launch_sb(const uint8_t* packed, const uint16_t* norms, int64_t rows, int64_t cols,
                      const LevelTable& lv, void* out, hipStream_t s) {
   uint8_t* ob = static_cast<uint8_t*>(out);
@@ -407,51 +451,55 @@ hipError_t launch_sb(const uint8_t* packed, const uint16_t* norms, int64_t rows,
     const int blocks = persistent_blocks((n_batches + kWaves - 1) / kWaves, kBlocksPerCu);
     const DequantJob job{packed, norms, ob, n_groups, TensorTable<DequantDesc>{nullptr, nullptr, 0},
                          n_batches};
-    hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT, false>), dim3(blocks), dim3(kBlock), 0, s, job, lv);
+    hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT, false, TRITS>), dim3(blocks), dim3(kBlock), 0, s, job,
+                       lv);
   } else {
     const int64_t n_groups = rows * ((cols + kGroup - 1) / kGroup);
     const int blocks = static_cast<int>((n_groups + kBlock - 1) / kBlock);
-    hipLaunchKernelGGL((dequantize_ragged<SB, BF16OUT, false>), dim3(blocks), dim3(kBlock), 0, s, packed,
-                       norms, rows, cols, lv, ob, TensorTable<DequantDesc>{nullptr, nullptr, 0}, int64_t{0});
+    hipLaunchKernelGGL((dequantize_ragged<SB, BF16OUT, false, TRITS>), dim3(blocks), dim3(kBlock), 0, s,
+                       packed, norms, rows, cols, lv, ob, TensorTable<DequantDesc>{nullptr, nullptr, 0},
+                       int64_t{0});
   }
   return hipGetLastError();
 }
 
-template <int SB, bool BF16OUT>
+template <int SB, bool BF16OUT, bool TRITS>
 hipError_t launch_many_sb(const LevelTable& lv, TensorTable<DequantDesc> contig, int64_t contig_batches,
                           TensorTable<DequantDesc> ragged, int64_t ragged_groups, hipStream_t s) {
   if (contig_batches > 0) {
     const int blocks = persistent_blocks((contig_batches + kWaves - 1) / kWaves, kBlocksPerCu);
     const DequantJob job{nullptr, nullptr, nullptr, 0, contig, contig_batches};
-    hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT, true>), dim3(blocks), dim3(kBlock), 0, s, job, lv);
+    hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT, true, TRITS>), dim3(blocks), dim3(kBlock), 0, s, job,
+                       lv);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (ragged_groups > 0) {
     const int blocks = static_cast<int>((ragged_groups + kBlock - 1) / kBlock);
-    hipLaunchKernelGGL((dequantize_ragged<SB, BF16OUT, true>), dim3(blocks), dim3(kBlock), 0, s, nullptr,
-                       nullptr, int64_t{0}, int64_t{0}, lv, nullptr, ragged, ragged_groups);
+    hipLaunchKernelGGL((dequantize_ragged<SB, BF16OUT, true, TRITS>), dim3(blocks), dim3(kBlock), 0, s,
+                       nullptr, nullptr, int64_t{0}, int64_t{0}, lv, nullptr, ragged, ragged_groups);
   }
   return hipGetLastError();
 }
 
-template <int SB>
+template <int SB, bool TRITS = false>
 hipError_t launch_many_out(const LevelTable& lv, bool bf16_out, TensorTable<DequantDesc> contig,
                            int64_t contig_batches, TensorTable<DequantDesc> ragged, int64_t ragged_groups,
                            hipStream_t s) {
-  return bf16_out ? launch_many_sb<SB, true>(lv, contig, contig_batches, ragged, ragged_groups, s)
-                  : launch_many_sb<SB, false>(lv, contig, contig_batches, ragged, ragged_groups, s);
+  return bf16_out ? launch_many_sb<SB, true, TRITS>(lv, contig, contig_batches, ragged, ragged_groups, s)
+                  : launch_many_sb<SB, false, TRITS>(lv, contig, contig_batches, ragged, ragged_groups, s);
 }
 
-template <int SB>
+template <int SB, bool TRITS = false>
 hipError_t launch_out(const uint8_t* packed, const uint16_t* norms, int64_t rows, int64_t cols,
                       const LevelTable& lv, void* out, bool bf16_out, hipStream_t s) {
-  return bf16_out ? launch_sb<SB, true>(packed, norms, rows, cols, lv, out, s)
-                  : launch_sb<SB, false>(packed, norms, rows, cols, lv, out, s);
+  return bf16_out ? launch_sb<SB, true, TRITS>(packed, norms, rows, cols, lv, out, s)
+                  : launch_sb<SB, false, TRITS>(packed, norms, rows, cols, lv, out, s);
 }
 
 }  // namespace kd
 
+// sbits: 2, 3 or 4; kTritStorage: five ternary indices per byte.
 hipError_t launch_dequantize(const uint8_t* packed, const uint16_t* norms, int64_t rows,
                              int64_t cols, int sbits, const LevelTable& lv, void* out,
                              bool bf16_out, hipStream_t stream) {
@@ -459,6 +507,7 @@ hipError_t launch_dequantize(const uint8_t* packed, const uint16_t* norms, int64
     case 2: return kd::launch_out<2>(packed, norms, rows, cols, lv, out, bf16_out, stream);
     case 3: return kd::launch_out<3>(packed, norms, rows, cols, lv, out, bf16_out, stream);
     case 4: return kd::launch_out<4>(packed, norms, rows, cols, lv, out, bf16_out, stream);
+    case kTritStorage: return kd::launch_out<2, true>(packed, norms, rows, cols, lv, out, bf16_out, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -471,6 +520,8 @@ hipError_t launch_dequantize_many(int sbits, const LevelTable& lv, bool bf16_out
     case 2: return kd::launch_many_out<2>(lv, bf16_out, contig, contig_batches, ragged, ragged_groups, stream);
     case 3: return kd::launch_many_out<3>(lv, bf16_out, contig, contig_batches, ragged, ragged_groups, stream);
     case 4: return kd::launch_many_out<4>(lv, bf16_out, contig, contig_batches, ragged, ragged_groups, stream);
+    case kTritStorage:
+      return kd::launch_many_out<2, true>(lv, bf16_out, contig, contig_batches, ragged, ragged_groups, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -39,13 +39,15 @@ bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
 // Levels of a bit-width; -1 if unsupported.
 int levels_for_bits(int bits, bool host_only) {
-  if (bits == CQ_TERNARY) return 3;
+  if (bits == CQ_TERNARY || bits == CQ_TERNARY_TRITS) return 3;
   if (bits == 2 || bits == 3 || bits == 4) return 1 << bits;
   if (bits == 1 && host_only) return 2;
   return -1;
 }
 
-int storage_bits(int bits) { return bits == CQ_TERNARY ? 2 : bits; }
+// Bits of one index in the bit-field layouts (the ternary code uses 2-bit
+// fields; its trit storage has no fields, see group_bytes).
+int storage_bits(int bits) { return (bits == CQ_TERNARY || bits == CQ_TERNARY_TRITS) ? 2 : bits; }
 
 int check_bits(int bits, bool host_only, int* n_levels) {
   int l = levels_for_bits(bits, host_only);
@@ -85,6 +87,26 @@ int check_levels(const float* levels, int n_levels, int expect) {
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Packed bytes per group: G * sbits / 8, or ceil(G / 5) for trit storage.
+int64_t group_bytes(int bits, int group_size) {
+  if (bits == CQ_TERNARY_TRITS) return ceil_div(group_size, 5);
+  return static_cast<int64_t>(group_size) * storage_bits(bits) / 8;
+}
+
+// Storage code of the dequantize launchers: field width, or trits.
+int storage_code(int bits) { return bits == CQ_TERNARY_TRITS ? cq::kTritStorage : storage_bits(bits); }
+
+// Alignment the kernels need for packed indices: 16 bytes for bit fields
+// (128-bit accesses), 2 bytes for trit storage (16-bit accesses; a group is
+// 26 bytes, so tensors inside a serialized blob sit at even offsets).
+size_t packed_align(int bits) { return bits == CQ_TERNARY_TRITS ? 2 : 16; }
+
+int reject_trits(int bits) {
+  if (bits == CQ_TERNARY_TRITS)
+    return fail(CQ_ERR_UNSUPPORTED, "trit storage: convert it with cq_repack to CQ_TERNARY first");
+  return CQ_OK;
+}
 
 // Byte range [lo, hi) of one buffer of a multi-tensor call.
 struct Span {
@@ -250,7 +272,7 @@ int cq_layout(int64_t rows, int64_t cols, int bits, int group_size, int64_t* n_g
   if (rows < 0 || cols < 0) return fail(CQ_ERR_ARG, "negative size");
   int64_t g = rows * ceil_div(cols, group_size);
   if (n_groups) *n_groups = g;
-  if (packed_bytes) *packed_bytes = g * (group_size * storage_bits(bits) / 8);
+  if (packed_bytes) *packed_bytes = g * group_bytes(bits, group_size);
   return CQ_OK;
 }
 
@@ -263,7 +285,7 @@ int cq_model_bytes(int n_tensors, const int64_t* rows, const int64_t* cols, int 
   if (n_tensors > 0 && (!rows || !cols)) return fail(CQ_ERR_NULL, "rows/cols is NULL");
   if ((rc = check_bits(bits, true, nullptr))) return rc;
   if ((rc = check_group(group_size, false))) return rc;
-  const uint64_t per_group = static_cast<uint64_t>(group_size) * storage_bits(bits) / 8 + 2;
+  const uint64_t per_group = static_cast<uint64_t>(group_bytes(bits, group_size)) + 2;
   uint64_t total = 0;
   for (int i = 0; i < n_tensors; ++i) {
     if (rows[i] < 0 || cols[i] < 0) return fail(CQ_ERR_ARG, "tensor %d has a negative size", i);
@@ -280,7 +302,7 @@ int cq_codebook(int bits, const double* samples, int64_t n_samples, int iters, f
   int L, rc;
   if (!levels_out || !n_levels) return fail(CQ_ERR_NULL, "levels_out/n_levels is NULL");
   if ((rc = check_bits(bits, true, &L))) return rc;
-  if (bits == CQ_TERNARY) {
+  if (bits == CQ_TERNARY || bits == CQ_TERNARY_TRITS) {
     static const float kTernary[3] = {-1.2240064f, 0.0f, 1.2240064f};
     std::memcpy(levels_out, kTernary, sizeof(kTernary));
     *n_levels = 3;
@@ -335,17 +357,18 @@ int cq_quantize(const void* w, int w_dtype, int64_t rows, int64_t cols, int bits
   if ((rc = check_levels(levels, n_levels, L))) return rc;
   if (rows == 0 || cols == 0) return CQ_OK;
   if (!w || !packed || !norms) return fail(CQ_ERR_NULL, "w/packed/norms is NULL");
-  if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(norms, 2))
-    return fail(CQ_ERR_ALIGN, "w and packed need 16-byte, norms 2-byte alignment");
+  if (!aligned(w, 16) || !aligned(packed, packed_align(bits)) || !aligned(norms, 2))
+    return fail(CQ_ERR_ALIGN, "w needs 16-byte, packed 16-byte (trits: 2-byte), norms 2-byte alignment");
   const int64_t ng = rows * ceil_div(cols, group_size);
   const size_t in_bytes = static_cast<size_t>(rows * cols) * (w_dtype == CQ_F32 ? 4 : 2);
-  const size_t pk_bytes = static_cast<size_t>(ng) * group_size * storage_bits(bits) / 8;
+  const size_t pk_bytes = static_cast<size_t>(ng * group_bytes(bits, group_size));
   const size_t nm_bytes = static_cast<size_t>(ng) * 2;
   if (overlap(w, in_bytes, packed, pk_bytes) || overlap(w, in_bytes, norms, nm_bytes) ||
       overlap(packed, pk_bytes, norms, nm_bytes))
     return fail(CQ_ERR_ARG, "input and output buffers overlap");
   const cq::QuantParams p = make_quant_params(levels, L);
-  return hip_status(cq::launch_quantize(w, w_dtype == CQ_BF16, rows, cols, p, packed, norms,
+  return hip_status(cq::launch_quantize(w, w_dtype == CQ_BF16, bits == CQ_TERNARY_TRITS, rows, cols, p,
+                                        packed, norms,
                                         static_cast<hipStream_t>(stream)),
                     "quantize launch");
 }
@@ -362,7 +385,7 @@ int cq_quantize_many(int n, const cq_quant_desc* descs, int w_dtype, int bits, i
   if (n == 0) return CQ_OK;
   if (!descs) return fail(CQ_ERR_NULL, "descs is NULL");
   const size_t esz = w_dtype == CQ_F32 ? 4 : 2;
-  const int sb = storage_bits(bits);
+  const int64_t gb = group_bytes(bits, group_size);
   ManyTables<cq::QuantDesc> t;
   std::vector<Span> outs, ins;
   for (int i = 0; i < n; ++i) {
@@ -370,11 +393,11 @@ int cq_quantize_many(int n, const cq_quant_desc* descs, int w_dtype, int bits, i
     if (d.rows < 0 || d.cols < 0) return fail(CQ_ERR_ARG, "tensor %d: negative size", i);
     if (d.rows == 0 || d.cols == 0) continue;
     if (!d.w || !d.packed || !d.norms) return fail(CQ_ERR_NULL, "tensor %d: w/packed/norms is NULL", i);
-    if (!aligned(d.w, 16) || !aligned(d.packed, 16) || !aligned(d.norms, 2))
-      return fail(CQ_ERR_ALIGN, "tensor %d: w and packed need 16-byte, norms 2-byte alignment", i);
+    if (!aligned(d.w, 16) || !aligned(d.packed, packed_align(bits)) || !aligned(d.norms, 2))
+      return fail(CQ_ERR_ALIGN, "tensor %d: w needs 16-byte, packed 16-byte (trits: 2-byte), norms 2-byte alignment", i);
     const int64_t ng = d.rows * ceil_div(d.cols, group_size);
     ins.push_back(span(d.w, static_cast<size_t>(d.rows * d.cols) * esz, i));
-    outs.push_back(span(d.packed, static_cast<size_t>(ng) * group_size * sb / 8, i));
+    outs.push_back(span(d.packed, static_cast<size_t>(ng * gb), i));
     outs.push_back(span(d.norms, static_cast<size_t>(ng) * 2, i));
     t.add(cq::QuantDesc{static_cast<const uint8_t*>(d.w), d.packed, d.norms, d.rows, d.cols}, ng,
           d.cols % group_size == 0);
@@ -386,7 +409,7 @@ int cq_quantize_many(int n, const cq_quant_desc* descs, int w_dtype, int bits, i
   const cq::QuantParams p = make_quant_params(levels, L);
   rc = t.upload(s);
   if (!rc)
-    rc = hip_status(cq::launch_quantize_many(w_dtype == CQ_BF16, p, t.tc, t.bstart.back(), t.tr,
+    rc = hip_status(cq::launch_quantize_many(w_dtype == CQ_BF16, bits == CQ_TERNARY_TRITS, p, t.tc, t.bstart.back(), t.tr,
                                              t.gstart.back(), s),
                     "quantize launch");
   const int rc2 = t.release(s);
@@ -406,7 +429,7 @@ int cq_dequantize_many(int n, const cq_dequant_desc* descs, int bits, int group_
   if (n == 0) return CQ_OK;
   if (!descs) return fail(CQ_ERR_NULL, "descs is NULL");
   const size_t esz = out_dtype == CQ_F32 ? 4 : 2;
-  const int sb = storage_bits(bits);
+  const int64_t gb = group_bytes(bits, group_size);
   ManyTables<cq::DequantDesc> t;
   std::vector<Span> outs, ins;
   for (int i = 0; i < n; ++i) {
@@ -414,10 +437,10 @@ int cq_dequantize_many(int n, const cq_dequant_desc* descs, int bits, int group_
     if (d.rows < 0 || d.cols < 0) return fail(CQ_ERR_ARG, "tensor %d: negative size", i);
     if (d.rows == 0 || d.cols == 0) continue;
     if (!d.packed || !d.norms || !d.out) return fail(CQ_ERR_NULL, "tensor %d: packed/norms/out is NULL", i);
-    if (!aligned(d.out, 16) || !aligned(d.packed, 16) || !aligned(d.norms, 2))
-      return fail(CQ_ERR_ALIGN, "tensor %d: out and packed need 16-byte, norms 2-byte alignment", i);
+    if (!aligned(d.out, 16) || !aligned(d.packed, packed_align(bits)) || !aligned(d.norms, 2))
+      return fail(CQ_ERR_ALIGN, "tensor %d: out needs 16-byte, packed 16-byte (trits: 2-byte), norms 2-byte alignment", i);
     const int64_t ng = d.rows * ceil_div(d.cols, group_size);
-    ins.push_back(span(d.packed, static_cast<size_t>(ng) * group_size * sb / 8, i));
+    ins.push_back(span(d.packed, static_cast<size_t>(ng * gb), i));
     ins.push_back(span(d.norms, static_cast<size_t>(ng) * 2, i));
     outs.push_back(span(d.out, static_cast<size_t>(d.rows * d.cols) * esz, i));
     t.add(cq::DequantDesc{d.packed, d.norms, static_cast<uint8_t*>(d.out), d.rows, d.cols}, ng,
@@ -430,7 +453,7 @@ int cq_dequantize_many(int n, const cq_dequant_desc* descs, int bits, int group_
   const cq::LevelTable lv = make_table(levels, L);
   rc = t.upload(s);
   if (!rc)
-    rc = hip_status(cq::launch_dequantize_many(sb, lv, out_dtype == CQ_BF16, t.tc, t.bstart.back(), t.tr,
+    rc = hip_status(cq::launch_dequantize_many(storage_code(bits), lv, out_dtype == CQ_BF16, t.tc, t.bstart.back(), t.tr,
                                                t.gstart.back(), s),
                     "dequantize launch");
   const int rc2 = t.release(s);
@@ -449,6 +472,7 @@ int cq_dequant_gemm_many(int n, const cq_matvec_desc* descs, int bits, int group
   g_last_error[0] = 0;
   int L, rc;
   if ((rc = check_bits(bits, false, &L))) return rc;
+  if ((rc = reject_trits(bits))) return rc;
   if (n < 0) return fail(CQ_ERR_ARG, "n < 0");
   if (batch < 1) return fail(CQ_ERR_ARG, "batch must be >= 1");
   if ((rc = check_group(group_size, true))) return rc;
@@ -536,6 +560,30 @@ int cq_dequant_gemm(const uint8_t* packed, const uint16_t* norms, int64_t n_out,
   return cq_dequant_gemm_many(1, &d, bits, group_size, levels, n_levels, batch, stream);
 }
 
+int cq_repack(const uint8_t* src, int src_bits, uint8_t* dst, int dst_bits, int64_t n_groups,
+              int group_size, void* stream) {
+  g_last_error[0] = 0;
+  int rc;
+  const bool to_trits = src_bits == CQ_TERNARY && dst_bits == CQ_TERNARY_TRITS;
+  const bool to_fields = src_bits == CQ_TERNARY_TRITS && dst_bits == CQ_TERNARY;
+  if (!to_trits && !to_fields)
+    return fail(CQ_ERR_ARG, "cq_repack converts between CQ_TERNARY and CQ_TERNARY_TRITS (got %d -> %d)",
+                src_bits, dst_bits);
+  if (n_groups < 0) return fail(CQ_ERR_ARG, "n_groups < 0");
+  if ((rc = check_group(group_size, true))) return rc;
+  if (n_groups == 0) return CQ_OK;
+  if (!src || !dst) return fail(CQ_ERR_NULL, "src/dst is NULL");
+  const uint8_t* fields = to_trits ? src : dst;
+  const uint8_t* trits = to_trits ? dst : src;
+  if (!aligned(fields, 16) || !aligned(trits, 2))
+    return fail(CQ_ERR_ALIGN, "2-bit fields need 16-byte, trit storage 2-byte alignment");
+  if (overlap(src, static_cast<size_t>(n_groups * group_bytes(src_bits, group_size)), dst,
+              static_cast<size_t>(n_groups * group_bytes(dst_bits, group_size))))
+    return fail(CQ_ERR_ARG, "src and dst overlap");
+  return hip_status(cq::launch_repack(src, to_trits, dst, n_groups, static_cast<hipStream_t>(stream)),
+                    "repack launch");
+}
+
 int cq_blob_layout(int n_tensors, const int64_t* rows, const int64_t* cols, int bits, int group_size,
                    int64_t* packed_offsets, int64_t* norm_offsets, int64_t* total_bytes) {
   g_last_error[0] = 0;
@@ -544,7 +592,7 @@ int cq_blob_layout(int n_tensors, const int64_t* rows, const int64_t* cols, int 
   if (n_tensors > 0 && (!rows || !cols)) return fail(CQ_ERR_NULL, "rows/cols is NULL");
   if ((rc = check_bits(bits, true, nullptr))) return rc;
   if ((rc = check_group(group_size, false))) return rc;
-  const int64_t per_group = static_cast<int64_t>(group_size) * storage_bits(bits) / 8;
+  const int64_t per_group = group_bytes(bits, group_size);
   int64_t packed_total = 0, norms_total = 0;
   for (int i = 0; i < n_tensors; ++i) {
     if (rows[i] < 0 || cols[i] < 0) return fail(CQ_ERR_ARG, "tensor %d has a negative size", i);
@@ -603,15 +651,15 @@ int cq_dequantize(const uint8_t* packed, const uint16_t* norms, int64_t rows, in
   if ((rc = check_levels(levels, n_levels, L))) return rc;
   if (rows == 0 || cols == 0) return CQ_OK;
   if (!packed || !norms || !out) return fail(CQ_ERR_NULL, "packed/norms/out is NULL");
-  if (!aligned(out, 16) || !aligned(packed, 16) || !aligned(norms, 2))
-    return fail(CQ_ERR_ALIGN, "out and packed need 16-byte, norms 2-byte alignment");
+  if (!aligned(out, 16) || !aligned(packed, packed_align(bits)) || !aligned(norms, 2))
+    return fail(CQ_ERR_ALIGN, "out needs 16-byte, packed 16-byte (trits: 2-byte), norms 2-byte alignment");
   const int64_t ng = rows * ceil_div(cols, group_size);
   const size_t out_bytes = static_cast<size_t>(rows * cols) * (out_dtype == CQ_F32 ? 4 : 2);
-  const size_t pk_bytes = static_cast<size_t>(ng) * group_size * storage_bits(bits) / 8;
+  const size_t pk_bytes = static_cast<size_t>(ng * group_bytes(bits, group_size));
   if (overlap(out, out_bytes, packed, pk_bytes) || overlap(out, out_bytes, norms, ng * 2))
     return fail(CQ_ERR_ARG, "input and output buffers overlap");
   const cq::LevelTable lv = make_table(levels, L);
-  return hip_status(cq::launch_dequantize(packed, norms, rows, cols, storage_bits(bits), lv, out,
+  return hip_status(cq::launch_dequantize(packed, norms, rows, cols, storage_code(bits), lv, out,
                                           out_dtype == CQ_BF16, static_cast<hipStream_t>(stream)),
                     "dequantize launch");
 }
@@ -628,6 +676,7 @@ int cq_dequant_matvec_many(int n, const cq_matvec_desc* descs, int bits, int gro
   g_last_error[0] = 0;
   int L, rc;
   if ((rc = check_bits(bits, false, &L))) return rc;
+  if ((rc = reject_trits(bits))) return rc;
   if (n < 0) return fail(CQ_ERR_ARG, "n < 0");
   if (batch < 1) return fail(CQ_ERR_ARG, "batch must be >= 1");
   if ((rc = check_group(group_size, true))) return rc;

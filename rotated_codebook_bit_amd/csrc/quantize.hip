@@ -198,8 +198,19 @@ __device__ __forceinline__ uint16_t finish_group(float (&y)[kGroup], float S, co
 template <int L>
 __device__ __forceinline__ void store_group(uint8_t* __restrict__ packed, uint16_t* __restrict__ norms,
                                             int64_t g, const uint32_t (&words)[Shape<L>::words],
-                                            uint16_t n16) {
+                                            uint16_t n16, bool trits = false) {
   constexpr int W = Shape<L>::words;
+  if constexpr (L == 3) {
+    if (trits) {
+      uint32_t t[13];
+      fields_to_trits(words, t);
+      uint16_t* dst = reinterpret_cast<uint16_t*>(packed + g * kTritBytes);
+#pragma unroll
+      for (int k = 0; k < 13; ++k) dst[k] = static_cast<uint16_t>(t[k]);
+      norms[g] = n16;
+      return;
+    }
+  }
   uint4* dst = reinterpret_cast<uint4*>(packed + g * (W * 4));
 #pragma unroll
   for (int i = 0; i < W / 4; ++i)
@@ -257,13 +268,25 @@ __device__ __forceinline__ void issue_batch(const uint8_t* __restrict__ w, int64
 }
 
 // Packed words and norm of every lane's group of batch bt.
-template <int L>
+template <int L, bool TRITS = false>
 __device__ __forceinline__ void store_batch(uint8_t* __restrict__ packed, uint16_t* __restrict__ norms,
                                             int64_t bt, int64_t n_groups, int lane,
                                             const uint32_t (&words)[Shape<L>::words], uint16_t n16) {
   constexpr int PB = Shape<L>::words * 4;
 #if defined(__HIP_DEVICE_COMPILE__)  // GPU-only builtins, as in issue_batch
   const int nv = valid_in_batch(bt, n_groups);
+  if constexpr (TRITS) {
+    // 26 bytes per group at 2-byte alignment: 13 16-bit stores per lane.
+    uint32_t t[13];
+    fields_to_trits(words, t);
+    const auto tdst = make_rsrc(packed + bt * kWave * kTritBytes, nv * kTritBytes);
+#pragma unroll
+    for (int k = 0; k < 13; ++k)
+      __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(t[k]), tdst, lane * kTritBytes + 2 * k, 0, 0);
+    const auto tndst = make_rsrc(norms + bt * kWave, nv * 2);
+    __builtin_amdgcn_raw_buffer_store_b16(n16, tndst, lane * 2, 0, 0);
+    return;
+  }
   const auto dst = make_rsrc(packed + bt * kWave * PB, nv * PB);
 #pragma unroll
   for (int i = 0; i < PB / 16; ++i) {
@@ -322,7 +345,7 @@ __device__ __forceinline__ QBatch resolve(const QuantJob& j, int64_t b, int& d) 
   }
 }
 
-template <int L, bool BF16, bool MANY>
+template <int L, bool BF16, bool MANY, bool TRITS = false>
 __global__ void __launch_bounds__(kBlock, 2)
 quantize_contig(QuantJob job, QuantParams p) {
   constexpr int GB = BF16 ? 256 : 512;  // input bytes per group
@@ -382,7 +405,7 @@ quantize_contig(QuantJob job, QuantParams p) {
     // Keep the deferred stores (and the next DMA) after the LDS reads, i.e.
     // after the loop-head wait, instead of letting them float above it.
     asm volatile("" ::: "memory");
-    if (have_prev) store_batch<L>(prev.packed, prev.norms, prev.bt, prev.n_groups, lane, words, n16);
+    if (have_prev) store_batch<L, TRITS>(prev.packed, prev.norms, prev.bt, prev.n_groups, lane, words, n16);
     const int64_t next = batch + stride;
     QBatch nxt = cur;
     if (next < n_batches) {
@@ -422,7 +445,7 @@ quantize_contig(QuantJob job, QuantParams p) {
     batch = next;
     if (batch >= n_batches) break;
   }
-  store_batch<L>(prev.packed, prev.norms, prev.bt, prev.n_groups, lane, words, n16);
+  store_batch<L, TRITS>(prev.packed, prev.norms, prev.bt, prev.n_groups, lane, words, n16);
 }
 
 // General path: rows whose length is not a multiple of 128; the last group
@@ -430,7 +453,7 @@ quantize_contig(QuantJob job, QuantParams p) {
 // With MANY, thread g of the launch takes group g of the concatenation of the
 // table's tensors (t.start holds group prefixes) and the plain arguments are
 // ignored.
-template <int L, bool BF16, bool MANY>
+template <int L, bool BF16, bool MANY, bool TRITS = false>
 __global__ void __launch_bounds__(kBlock)
 quantize_ragged(const uint8_t* __restrict__ w, int64_t rows, int64_t cols, QuantParams p,
                 uint8_t* __restrict__ packed, uint16_t* __restrict__ norms,
@@ -479,7 +502,7 @@ quantize_ragged(const uint8_t* __restrict__ w, int64_t rows, int64_t cols, Quant
   }
   uint32_t words[Shape<L>::words];
   const uint16_t n16 = finish_group<L>(y, s0 + s1, p, words);
-  store_group<L>(packed, norms, g, words, n16);
+  store_group<L>(packed, norms, g, words, n16, TRITS);
 }
 
 // ---------------------------------------------------------------------------
@@ -774,7 +797,7 @@ hipError_t launch_fq_types(const void* w, bool bf16_in, int64_t rows, int64_t co
                   : launch_fq<L, false, false>(w, rows, cols, p, lv, out, s);
 }
 
-template <int L, bool BF16>
+template <int L, bool BF16, bool TRITS>
 hipError_t launch_l(const void* w, int64_t rows, int64_t cols, const QuantParams& p,
                     uint8_t* packed, uint16_t* norms, hipStream_t s) {
   const uint8_t* wb = static_cast<const uint8_t*>(w);
@@ -786,47 +809,60 @@ hipError_t launch_l(const void* w, int64_t rows, int64_t cols, const QuantParams
     // overlaps the current arithmetic.
     const int blocks = persistent_blocks((n_batches + kWaves - 1) / kWaves, kBlocksPerCu);
     const QuantJob job{wb, packed, norms, n_groups, TensorTable<QuantDesc>{nullptr, nullptr, 0}, n_batches};
-    hipLaunchKernelGGL((quantize_contig<L, BF16, false>), dim3(blocks), dim3(kBlock), 0, s, job, p);
+    hipLaunchKernelGGL((quantize_contig<L, BF16, false, TRITS>), dim3(blocks), dim3(kBlock), 0, s, job, p);
   } else {
     const int64_t n_groups = rows * ((cols + kGroup - 1) / kGroup);
     const int blocks = static_cast<int>((n_groups + kBlock - 1) / kBlock);
-    hipLaunchKernelGGL((quantize_ragged<L, BF16, false>), dim3(blocks), dim3(kBlock), 0, s, wb, rows,
+    hipLaunchKernelGGL((quantize_ragged<L, BF16, false, TRITS>), dim3(blocks), dim3(kBlock), 0, s, wb, rows,
                        cols, p, packed, norms, TensorTable<QuantDesc>{nullptr, nullptr, 0}, int64_t{0});
   }
   return hipGetLastError();
 }
 
-template <int L, bool BF16>
+template <int L, bool BF16, bool TRITS>
 hipError_t launch_many_l(const QuantParams& p, TensorTable<QuantDesc> contig, int64_t contig_batches,
                          TensorTable<QuantDesc> ragged, int64_t ragged_groups, hipStream_t s) {
   if (contig_batches > 0) {
     const int blocks = persistent_blocks((contig_batches + kWaves - 1) / kWaves, kBlocksPerCu);
     const QuantJob job{nullptr, nullptr, nullptr, 0, contig, contig_batches};
-    hipLaunchKernelGGL((quantize_contig<L, BF16, true>), dim3(blocks), dim3(kBlock), 0, s, job, p);
+    hipLaunchKernelGGL((quantize_contig<L, BF16, true, TRITS>), dim3(blocks), dim3(kBlock), 0, s, job, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (ragged_groups > 0) {
     const int blocks = static_cast<int>((ragged_groups + kBlock - 1) / kBlock);
-    hipLaunchKernelGGL((quantize_ragged<L, BF16, true>), dim3(blocks), dim3(kBlock), 0, s, nullptr,
+    hipLaunchKernelGGL((quantize_ragged<L, BF16, true, TRITS>), dim3(blocks), dim3(kBlock), 0, s, nullptr,
                        int64_t{0}, int64_t{0}, p, nullptr, nullptr, ragged, ragged_groups);
   }
   return hipGetLastError();
 }
 
+// Trit storage exists for the three-level code only.
 template <int L>
-hipError_t launch_many_dtype(bool bf16, const QuantParams& p, TensorTable<QuantDesc> contig,
+hipError_t launch_many_dtype(bool bf16, bool trits, const QuantParams& p, TensorTable<QuantDesc> contig,
                              int64_t contig_batches, TensorTable<QuantDesc> ragged,
                              int64_t ragged_groups, hipStream_t s) {
-  return bf16 ? launch_many_l<L, true>(p, contig, contig_batches, ragged, ragged_groups, s)
-              : launch_many_l<L, false>(p, contig, contig_batches, ragged, ragged_groups, s);
+  if constexpr (L == 3) {
+    if (trits)
+      return bf16 ? launch_many_l<L, true, true>(p, contig, contig_batches, ragged, ragged_groups, s)
+                  : launch_many_l<L, false, true>(p, contig, contig_batches, ragged, ragged_groups, s);
+  }
+  if (trits) return hipErrorInvalidValue;
+  return bf16 ? launch_many_l<L, true, false>(p, contig, contig_batches, ragged, ragged_groups, s)
+              : launch_many_l<L, false, false>(p, contig, contig_batches, ragged, ragged_groups, s);
 }
 
 template <int L>
-hipError_t launch_dtype(const void* w, bool bf16, int64_t rows, int64_t cols, const QuantParams& p,
-                        uint8_t* packed, uint16_t* norms, hipStream_t s) {
-  return bf16 ? launch_l<L, true>(w, rows, cols, p, packed, norms, s)
-              : launch_l<L, false>(w, rows, cols, p, packed, norms, s);
+hipError_t launch_dtype(const void* w, bool bf16, bool trits, int64_t rows, int64_t cols,
+                        const QuantParams& p, uint8_t* packed, uint16_t* norms, hipStream_t s) {
+  if constexpr (L == 3) {
+    if (trits)
+      return bf16 ? launch_l<L, true, true>(w, rows, cols, p, packed, norms, s)
+                  : launch_l<L, false, true>(w, rows, cols, p, packed, norms, s);
+  }
+  if (trits) return hipErrorInvalidValue;
+  return bf16 ? launch_l<L, true, false>(w, rows, cols, p, packed, norms, s)
+              : launch_l<L, false, false>(w, rows, cols, p, packed, norms, s);
 }
 
 }  // namespace kq
@@ -843,26 +879,26 @@ hipError_t launch_fake_quant(const void* w, bool bf16_in, int64_t rows, int64_t 
   }
 }
 
-hipError_t launch_quantize(const void* w, bool bf16, int64_t rows, int64_t cols,
+hipError_t launch_quantize(const void* w, bool bf16, bool trits, int64_t rows, int64_t cols,
                            const QuantParams& p, uint8_t* packed, uint16_t* norms,
                            hipStream_t stream) {
   switch (p.n_levels) {
-    case 3: return kq::launch_dtype<3>(w, bf16, rows, cols, p, packed, norms, stream);
-    case 4: return kq::launch_dtype<4>(w, bf16, rows, cols, p, packed, norms, stream);
-    case 8: return kq::launch_dtype<8>(w, bf16, rows, cols, p, packed, norms, stream);
-    case 16: return kq::launch_dtype<16>(w, bf16, rows, cols, p, packed, norms, stream);
+    case 3: return kq::launch_dtype<3>(w, bf16, trits, rows, cols, p, packed, norms, stream);
+    case 4: return kq::launch_dtype<4>(w, bf16, trits, rows, cols, p, packed, norms, stream);
+    case 8: return kq::launch_dtype<8>(w, bf16, trits, rows, cols, p, packed, norms, stream);
+    case 16: return kq::launch_dtype<16>(w, bf16, trits, rows, cols, p, packed, norms, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_quantize_many(bool bf16, const QuantParams& p, TensorTable<QuantDesc> contig,
+hipError_t launch_quantize_many(bool bf16, bool trits, const QuantParams& p, TensorTable<QuantDesc> contig,
                                 int64_t contig_batches, TensorTable<QuantDesc> ragged,
                                 int64_t ragged_groups, hipStream_t stream) {
   switch (p.n_levels) {
-    case 3: return kq::launch_many_dtype<3>(bf16, p, contig, contig_batches, ragged, ragged_groups, stream);
-    case 4: return kq::launch_many_dtype<4>(bf16, p, contig, contig_batches, ragged, ragged_groups, stream);
-    case 8: return kq::launch_many_dtype<8>(bf16, p, contig, contig_batches, ragged, ragged_groups, stream);
-    case 16: return kq::launch_many_dtype<16>(bf16, p, contig, contig_batches, ragged, ragged_groups, stream);
+    case 3: return kq::launch_many_dtype<3>(bf16, trits, p, contig, contig_batches, ragged, ragged_groups, stream);
+    case 4: return kq::launch_many_dtype<4>(bf16, trits, p, contig, contig_batches, ragged, ragged_groups, stream);
+    case 8: return kq::launch_many_dtype<8>(bf16, trits, p, contig, contig_batches, ragged, ragged_groups, stream);
+    case 16: return kq::launch_many_dtype<16>(bf16, trits, p, contig, contig_batches, ragged, ragged_groups, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,0 +1,59 @@
+// Conversion between the two storage forms of the three-level ("1.58-bit")
+// code ("How Quantization Codebooks Are Trained in Cactus Quants", section
+// Ternary Special Case Handling): 2-bit fields (32 bytes per 128-group, the
+// layout the product kernels decode) and trits (five indices per byte, 26
+// bytes per group).  One thread per group.
+
+#include "cq_internal.h"
+
+namespace cq {
+namespace {
+
+constexpr int kBlock = 256;
+
+__global__ void __launch_bounds__(kBlock)
+fields_to_trits_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t n_groups) {
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  if (g >= n_groups) return;
+  const uint4* s = reinterpret_cast<const uint4*>(src + g * 32);
+  const uint4 a = s[0], b = s[1];
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t t[13];
+  fields_to_trits(w, t);
+  uint16_t* d = reinterpret_cast<uint16_t*>(dst + g * kTritBytes);
+#pragma unroll
+  for (int k = 0; k < 13; ++k) d[k] = static_cast<uint16_t>(t[k]);
+}
+
+__global__ void __launch_bounds__(kBlock)
+trits_to_fields_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t n_groups) {
+  __shared__ uint16_t tab[256];
+  tab[threadIdx.x] = static_cast<uint16_t>(trit_table_entry(threadIdx.x));
+  __syncthreads();
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  if (g >= n_groups) return;
+  const uint16_t* s = reinterpret_cast<const uint16_t*>(src + g * kTritBytes);
+  uint32_t t[13];
+#pragma unroll
+  for (int k = 0; k < 13; ++k) t[k] = s[k];
+  uint32_t w[8];
+  trits_to_fields(t, tab, w);
+  uint4* d = reinterpret_cast<uint4*>(dst + g * 32);
+  d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
+}  // namespace
+
+hipError_t launch_repack(const uint8_t* src, bool to_trits, uint8_t* dst, int64_t n_groups,
+                         hipStream_t stream) {
+  if (n_groups <= 0) return hipSuccess;
+  const unsigned blocks = static_cast<unsigned>((n_groups + kBlock - 1) / kBlock);
+  if (to_trits)
+    hipLaunchKernelGGL(fields_to_trits_kernel, dim3(blocks), dim3(kBlock), 0, stream, src, dst, n_groups);
+  else
+    hipLaunchKernelGGL(trits_to_fields_kernel, dim3(blocks), dim3(kBlock), 0, stream, src, dst, n_groups);
+  return hipGetLastError();
+}
+
+}  // namespace cq

@@ -348,3 +348,45 @@ def test_gemm_validation():
     # the second matrix's y lands on the first one's y
     assert many([good, D(0x100000, 0x900000, 8, 256, 0x2100000, 0x3100000 + 64)]) == E_ARG
     assert many([good, D(0x100000, 0x900000, 8, 256, 0, 0x4100000)]) == E_NULL
+
+
+# -- trit storage ------------------------------------------------------------------------
+
+def test_trit_sizes_equal_oracle():
+    T = O.TERNARY_TRITS
+    assert cq.TERNARY_TRITS == T == 159
+    assert cq.layout(300, 1000, T) == (2400, 2400 * 26)
+    shapes = [s for _, s in W.needle2_shapes()] + [(2, 3, 130)]
+    for g in (8, 64, 128, 256):
+        assert cq.model_bytes(shapes, T, g) == O.model_bytes(shapes, T, g)
+        po, no, total = cq.blob_layout(shapes, T, g)
+        want = O.blob_offsets(shapes, T, g)
+        assert (po, no, total) == (list(want[0]), list(want[1]), want[2])
+    np.testing.assert_array_equal(cq.codebook(T), np.float32(O.TERNARY_LEVELS))
+
+
+def test_trit_validation():
+    L = cq.lib()
+    lv, lp = _levels(3)
+    T = O.TERNARY_TRITS
+    # the product calls decode 2-bit fields only
+    assert L.cq_dequant_matvec(FAKE, FAKE2, 8, 256, T, 128, lp, 3, ctypes.c_void_p(0x2100000), 1,
+                               ctypes.c_void_p(0x3100000), None) == E_UNSUP
+    assert L.cq_dequant_gemm(FAKE, FAKE2, 8, 256, T, 128, lp, 3, ctypes.c_void_p(0x2100000), 16,
+                             ctypes.c_void_p(0x3100000), None) == E_UNSUP
+    assert "cq_repack" in L.cq_last_error().decode()
+    # quantize with trit storage validates like any width
+    assert L.cq_quantize(FAKE, 0, 4, 256, T, 128, lp, 4, FAKE2, FAKE3, None) == E_ARG   # 3 levels needed
+    assert L.cq_quantize(FAKE, 0, 4, 256, T, 128, lp, 3, ctypes.c_void_p(0x100000 + 16), FAKE3,
+                         None) == E_ARG                                                   # packed overlaps w
+    # repack
+    R = L.cq_repack
+    assert R(FAKE, 2, FAKE2, T, 10, 128, None) == E_ARG          # only ternary <-> trits
+    assert R(FAKE, T, FAKE2, T, 10, 128, None) == E_ARG
+    assert R(FAKE, O.TERNARY, FAKE2, T, -1, 128, None) == E_ARG
+    assert R(FAKE, O.TERNARY, FAKE2, T, 10, 64, None) == E_UNSUP
+    assert R(None, O.TERNARY, FAKE2, T, 10, 128, None) == E_NULL
+    assert R(ctypes.c_void_p(0x100008), O.TERNARY, FAKE2, T, 10, 128, None) == E_ALIGN   # fields 16-B
+    assert R(FAKE, O.TERNARY, ctypes.c_void_p(0x900001), T, 10, 128, None) == E_ALIGN   # trits 2-B
+    assert R(FAKE, O.TERNARY, ctypes.c_void_p(0x100000 + 300), T, 10, 128, None) == E_ARG  # overlap
+    assert R(None, O.TERNARY, None, T, 0, 128, None) == OK
