@@ -42,8 +42,10 @@
  *   - levels (host, nullable where stated): n_levels float32 codebook levels
  *     in N(0,1) units (before the 1/sqrt(G) scaling), strictly ascending.
  *     n_levels must be 3 for CQ_TERNARY and 2^bits otherwise.
- *   - group_size must be 128 for device calls; host-only calls take any power
- *     of two from 8 to 4096 (so a group's packed indices fill whole bytes).
+ *   - group_size: cq_quantize, cq_dequantize and cq_fake_quant take 32, 64,
+ *     128 or 256 ("Cactus Quants CQ2-bit Quantization", FAQ on group size);
+ *     the other device calls take 128; host-only calls take any power of
+ *     two from 8 to 4096 (so a group's packed indices fill whole bytes).
  *   - Device calls validate every argument first, then enqueue their kernels
  *     on `stream` (a hipStream_t; NULL = the null stream) and return without
  *     waiting.  On a validation error nothing is enqueued.  Asynchronous

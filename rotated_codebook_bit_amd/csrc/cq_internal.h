@@ -132,6 +132,17 @@ hipError_t launch_dequantize(const uint8_t* packed, const uint16_t* norms,
                              const LevelTable& lv, void* out, bool bf16_out,
                              hipStream_t stream);
 
+// Group sizes 32, 64 and 256 (single-tensor codec calls; one or four lanes
+// per group).
+hipError_t launch_quantize_g(int group_size, const void* w, bool bf16, int64_t rows, int64_t cols,
+                             const QuantParams& p, uint8_t* packed, uint16_t* norms, hipStream_t stream);
+hipError_t launch_dequantize_g(int group_size, const uint8_t* packed, const uint16_t* norms, int64_t rows,
+                               int64_t cols, int sbits, const LevelTable& lv, void* out, bool bf16_out,
+                               hipStream_t stream);
+hipError_t launch_fake_quant_g(int group_size, const void* w, bool bf16, int64_t rows, int64_t cols,
+                               const QuantParams& p, const LevelTable& lv, void* out, bool bf16_out,
+                               hipStream_t stream);
+
 // ---- Multi-tensor codec calls ----------------------------------------------
 
 // One tensor of a multi-tensor quantize / dequantize call (device-side

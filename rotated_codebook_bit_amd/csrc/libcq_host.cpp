@@ -59,7 +59,7 @@ int check_bits(int bits, bool host_only, int* n_levels) {
 int check_group(int group_size, bool device) {
   if (device) {
     if (group_size != cq::kGroup)
-      return fail(CQ_ERR_UNSUPPORTED, "group_size=%d: device kernels support 128", group_size);
+      return fail(CQ_ERR_UNSUPPORTED, "group_size=%d: device kernels support 128 here", group_size);
   } else if (!is_pow2(group_size) || group_size < 8 || group_size > 4096) {
     // From 8 up, a group's packed indices fill whole bytes at every width.
     return fail(CQ_ERR_ARG, "group_size=%d must be a power of two in [8, 4096]", group_size);
@@ -87,6 +87,16 @@ int check_levels(const float* levels, int n_levels, int expect) {
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The single-tensor codec calls (quantize, dequantize, fake quantization)
+// also run group sizes 32, 64 and 256; trit storage is laid out for 128.
+int check_codec_group(int group_size, int bits) {
+  if (group_size != 32 && group_size != 64 && group_size != cq::kGroup && group_size != 256)
+    return fail(CQ_ERR_UNSUPPORTED, "group_size=%d: these kernels support 32, 64, 128 and 256", group_size);
+  if (bits == CQ_TERNARY_TRITS && group_size != cq::kGroup)
+    return fail(CQ_ERR_UNSUPPORTED, "trit storage is implemented for group_size 128");
+  return CQ_OK;
+}
 
 // Packed bytes per group: G * sbits / 8, or ceil(G / 5) for trit storage.
 int64_t group_bytes(int bits, int group_size) {
@@ -353,7 +363,7 @@ int cq_quantize(const void* w, int w_dtype, int64_t rows, int64_t cols, int bits
   if ((rc = check_bits(bits, false, &L))) return rc;
   if (w_dtype != CQ_F32 && w_dtype != CQ_BF16) return fail(CQ_ERR_ARG, "unknown w_dtype %d", w_dtype);
   if (rows < 0 || cols < 0) return fail(CQ_ERR_ARG, "negative size");
-  if ((rc = check_group(group_size, true))) return rc;
+  if ((rc = check_codec_group(group_size, bits))) return rc;
   if ((rc = check_levels(levels, n_levels, L))) return rc;
   if (rows == 0 || cols == 0) return CQ_OK;
   if (!w || !packed || !norms) return fail(CQ_ERR_NULL, "w/packed/norms is NULL");
@@ -367,6 +377,10 @@ int cq_quantize(const void* w, int w_dtype, int64_t rows, int64_t cols, int bits
       overlap(packed, pk_bytes, norms, nm_bytes))
     return fail(CQ_ERR_ARG, "input and output buffers overlap");
   const cq::QuantParams p = make_quant_params(levels, L);
+  if (group_size != cq::kGroup)
+    return hip_status(cq::launch_quantize_g(group_size, w, w_dtype == CQ_BF16, rows, cols, p, packed, norms,
+                                            static_cast<hipStream_t>(stream)),
+                      "quantize launch");
   return hip_status(cq::launch_quantize(w, w_dtype == CQ_BF16, bits == CQ_TERNARY_TRITS, rows, cols, p,
                                         packed, norms,
                                         static_cast<hipStream_t>(stream)),
@@ -620,7 +634,7 @@ int cq_fake_quant(const void* w, int w_dtype, int64_t rows, int64_t cols, int bi
   if (out_dtype != CQ_F32 && out_dtype != CQ_BF16)
     return fail(CQ_ERR_ARG, "unknown out_dtype %d", out_dtype);
   if (rows < 0 || cols < 0) return fail(CQ_ERR_ARG, "negative size");
-  if ((rc = check_group(group_size, true))) return rc;
+  if ((rc = check_codec_group(group_size, bits))) return rc;
   if ((rc = check_levels(levels, n_levels, L))) return rc;
   if (rows == 0 || cols == 0) return CQ_OK;
   if (!w || !out) return fail(CQ_ERR_NULL, "w/out is NULL");
@@ -633,6 +647,10 @@ int cq_fake_quant(const void* w, int w_dtype, int64_t rows, int64_t cols, int bi
     return fail(CQ_ERR_ARG, "w and out overlap (only out == w with equal dtypes is allowed)");
   const cq::QuantParams p = make_quant_params(levels, L);
   const cq::LevelTable lv = make_table(levels, L);
+  if (group_size != cq::kGroup)
+    return hip_status(cq::launch_fake_quant_g(group_size, w, w_dtype == CQ_BF16, rows, cols, p, lv, out,
+                                              out_dtype == CQ_BF16, static_cast<hipStream_t>(stream)),
+                      "fake-quant launch");
   return hip_status(cq::launch_fake_quant(w, w_dtype == CQ_BF16, rows, cols, p, lv, out,
                                           out_dtype == CQ_BF16, static_cast<hipStream_t>(stream)),
                     "fake-quant launch");
@@ -647,7 +665,7 @@ int cq_dequantize(const uint8_t* packed, const uint16_t* norms, int64_t rows, in
   if (out_dtype != CQ_F32 && out_dtype != CQ_BF16)
     return fail(CQ_ERR_ARG, "unknown out_dtype %d", out_dtype);
   if (rows < 0 || cols < 0) return fail(CQ_ERR_ARG, "negative size");
-  if ((rc = check_group(group_size, true))) return rc;
+  if ((rc = check_codec_group(group_size, bits))) return rc;
   if ((rc = check_levels(levels, n_levels, L))) return rc;
   if (rows == 0 || cols == 0) return CQ_OK;
   if (!packed || !norms || !out) return fail(CQ_ERR_NULL, "packed/norms/out is NULL");
@@ -659,6 +677,10 @@ int cq_dequantize(const uint8_t* packed, const uint16_t* norms, int64_t rows, in
   if (overlap(out, out_bytes, packed, pk_bytes) || overlap(out, out_bytes, norms, ng * 2))
     return fail(CQ_ERR_ARG, "input and output buffers overlap");
   const cq::LevelTable lv = make_table(levels, L);
+  if (group_size != cq::kGroup)
+    return hip_status(cq::launch_dequantize_g(group_size, packed, norms, rows, cols, storage_bits(bits), lv,
+                                              out, out_dtype == CQ_BF16, static_cast<hipStream_t>(stream)),
+                      "dequantize launch");
   return hip_status(cq::launch_dequantize(packed, norms, rows, cols, storage_code(bits), lv, out,
                                           out_dtype == CQ_BF16, static_cast<hipStream_t>(stream)),
                     "dequantize launch");

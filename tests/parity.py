@@ -130,14 +130,13 @@ def check_matvec(y_gpu: np.ndarray, y_ref: np.ndarray, x: np.ndarray, w_hat: np.
 
 
 def check_fake_quant(out_gpu: np.ndarray, w64: np.ndarray, bits: int, levels: np.ndarray,
-                     out_bf16: bool = False, enforce_count: bool = True) -> Report:
+                     out_bf16: bool = False, enforce_count: bool = True, g: int = O.GROUP) -> Report:
     """out_gpu: the GPU reconstruction of w64 (any shape, w64's size)."""
-    g = O.GROUP
     w2 = np.asarray(w64, dtype=np.float64).reshape(-1, np.shape(w64)[-1])
     rows, cols = w2.shape
     ng = -(-cols // g)
-    ref = O.fake_quant(w2, bits, levels)
-    q = O.quantize(w2, bits, levels)
+    ref = O.fake_quant(w2, bits, levels, g)
+    q = O.quantize(w2, bits, levels, g)
     lv32 = O.runtime_levels(levels)
     out = np.asarray(out_gpu, dtype=np.float64).reshape(rows, cols)
     n = q.norm

@@ -111,7 +111,7 @@ def test_quantize_validation():
     assert quant(bits=1) == E_ARG               # host-only width
     assert quant(dt=7) == E_ARG
     assert quant(rows=-1) == E_ARG
-    assert quant(g=64) == E_UNSUP
+    assert quant(g=512) == E_UNSUP
     assert quant(nl=3) == E_ARG                 # 2 bits needs 4 levels
     bad = np.array([0.0, 0.0, 1.0, 2.0], dtype=np.float32)
     assert quant(levels=(bad, bad.ctypes.data_as(F))) == E_ARG
@@ -138,7 +138,7 @@ def test_dequantize_validation():
 
     assert deq(dt=2) == E_ARG
     assert deq(bits=7) == E_ARG
-    assert deq(g=256) == E_UNSUP
+    assert deq(g=512) == E_UNSUP
     assert deq(nl=4) == E_ARG
     assert deq(out=None) == E_NULL
     assert deq(out=ctypes.c_void_p(0x1100008)) == E_ALIGN
@@ -225,7 +225,7 @@ def test_fake_quant_validation():
     assert fq(dt=3) == E_ARG
     assert fq(odt=-1) == E_ARG
     assert fq(bits=1) == E_ARG
-    assert fq(g=32) == E_UNSUP
+    assert fq(g=16) == E_UNSUP
     assert fq(nl=8) == E_ARG
     assert fq(rows=-2) == E_ARG
     assert fq(w=None) == E_NULL
@@ -390,3 +390,20 @@ def test_trit_validation():
     assert R(FAKE, O.TERNARY, ctypes.c_void_p(0x900001), T, 10, 128, None) == E_ALIGN   # trits 2-B
     assert R(FAKE, O.TERNARY, ctypes.c_void_p(0x100000 + 300), T, 10, 128, None) == E_ARG  # overlap
     assert R(None, O.TERNARY, None, T, 0, 128, None) == OK
+
+
+def test_group_size_support():
+    L = cq.lib()
+    lv, lp = _levels(4)
+    lv3, lp3 = _levels(3)
+    # codec calls: 32, 64, 128, 256; others unsupported; trit storage at 128 only
+    assert quant(g=16) == E_UNSUP
+    assert quant(g=1024) == E_UNSUP
+    assert L.cq_quantize(FAKE, 0, 4, 256, O.TERNARY_TRITS, 64, lp3, 3, FAKE2, FAKE3, None) == E_UNSUP
+    # product, multi-tensor and repack calls: 128 only
+    assert L.cq_dequant_matvec(FAKE, FAKE2, 8, 256, 2, 64, lp, 4, ctypes.c_void_p(0x2100000), 1,
+                               ctypes.c_void_p(0x3100000), None) == E_UNSUP
+    assert L.cq_repack(FAKE, O.TERNARY, FAKE2, O.TERNARY_TRITS, 4, 256, None) == E_UNSUP
+    # sizes for other group sizes
+    assert cq.layout(3, 200, 2, 64) == (12, 12 * 16)
+    assert cq.layout(3, 200, 4, 256) == (3, 3 * 128)

@@ -1,0 +1,108 @@
+"""GPU parity for group sizes other than 128 (32, 64, 256) through the C ABI:
+quantize, dequantize and fake quantization against the oracle run with the
+same group size.  Each case prints its name before it touches the GPU."""
+
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+from oracle import cq_oracle as O
+from rotated_codebook_bit_amd import workloads as W
+from parity import check_count, check_dequant, check_fake_quant, check_quantize
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import rotated_codebook_bit_amd as cq  # noqa: E402
+
+DEV = "cuda"
+ALL_BITS = [O.TERNARY, 2, 3, 4]
+
+# In-band index mismatches are correct results (either neighbour is); their
+# count is capped at 1e-6 of the elements over the module's whole workload,
+# checked by the last test.
+TALLY = {"mismatches": 0, "elements": 0}
+
+
+def tally(rep):
+    TALLY["mismatches"] += rep["index_mismatches"]
+    TALLY["elements"] += rep["elements"]
+
+
+def say(msg):
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def levels(lloyd_samples):
+    return {b: cq.codebook(b, lloyd_samples) for b in ALL_BITS}
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def f16_bits(t):
+    return host(t.contiguous().view(torch.int16)).view(np.uint16)
+
+
+def make(shape, seed, dtype):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal(shape) * 0.02).astype(np.float32)
+    if dtype == "bf16":
+        b = W.f32_to_bf16_bits(w)
+        return (W.bf16_bits_to_f32(b).astype(np.float64),
+                torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to(DEV).view(torch.bfloat16))
+    return w.astype(np.float64), torch.from_numpy(w).to(DEV)
+
+
+@pytest.mark.parametrize("g", [32, 64, 256])
+@pytest.mark.parametrize("bits", ALL_BITS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(300, 1000), (64, 512), (3, 1, 37)])
+def test_group_size_codec(g, bits, dtype, shape, levels):
+    lv = levels[bits]
+    w64, w_dev = make(shape, zlib.crc32(repr(("g", g, bits, dtype, shape)).encode()), dtype)
+    rows, cols = int(np.prod(shape[:-1])), shape[-1]
+    say(f"G={g} quantize bits={bits} {dtype}{shape}")
+    q = O.quantize(w64, bits, lv, g)
+    packed, norms = cq.quantize(w_dev, bits, lv, group_size=g)
+    tally(check_quantize(host(packed), f16_bits(norms), q, enforce_count=False))
+    say(f"G={g} dequantize bits={bits}")
+    ref = O.dequantize(q.packed, q.norm16, rows, cols, bits, lv, g)
+    out = cq.dequantize(torch.from_numpy(q.packed.reshape(rows, -1)).to(DEV),
+                        torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16),
+                        rows, cols, bits, lv, group_size=g)
+    check_dequant(host(out), ref, q.norm16, rows, cols, g)
+    say(f"G={g} fake quant bits={bits}")
+    fq = cq.fake_quant(w_dev, bits, lv, out_dtype=torch.float32, group_size=g)
+    rep = check_fake_quant(host(fq).astype(np.float64), w64, bits, lv, enforce_count=False, g=g)
+    TALLY["mismatches"] += rep.get("index_mismatches", 0)
+    TALLY["elements"] += rep.get("indices_read_back", 0)
+
+
+@pytest.mark.parametrize("g", [32, 64, 256])
+def test_group_size_special_groups(g, levels):
+    """Zero groups, constant groups and norms that overflow binary16."""
+    rng = np.random.default_rng(g)
+    w = np.concatenate([np.zeros((1, 2 * g)), np.full((1, 2 * g), 0.25), rng.standard_normal((1, 2 * g)),
+                        np.full((1, 2 * g), 1e5)], axis=0).astype(np.float32)
+    for bits in ALL_BITS:
+        say(f"G={g} special groups bits={bits}")
+        q = O.quantize(w.astype(np.float64), bits, levels[bits], g)
+        packed, norms = cq.quantize(torch.from_numpy(w).to(DEV), bits, levels[bits], group_size=g)
+        tally(check_quantize(host(packed), f16_bits(norms), q, enforce_count=False))
+        n = f16_bits(norms)
+        assert (n[0] == 0).all() and (n[-1] == 0x7C00).all()
+
+
+def test_zz_mismatch_total():
+    say(f"group sizes: {TALLY['mismatches']} in-band mismatches in {TALLY['elements']} elements")
+    check_count(TALLY["mismatches"], TALLY["elements"])
