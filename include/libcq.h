@@ -43,7 +43,8 @@
  *     in N(0,1) units (before the 1/sqrt(G) scaling), strictly ascending.
  *     n_levels must be 3 for CQ_TERNARY and 2^bits otherwise.
  *   - group_size: cq_quantize, cq_dequantize and cq_fake_quant take 32, 64,
- *     128 or 256 ("Cactus Quants CQ2-bit Quantization", FAQ on group size);
+ *     128 or 256 ("Cactus Quants CQ2-bit Quantization: Extreme Compression
+ *     for Edge LLMs", FAQ on group size);
  *     the other device calls take 128; host-only calls take any power of
  *     two from 8 to 4096 (so a group's packed indices fill whole bytes).
  *   - Device calls validate every argument first, then enqueue their kernels

@@ -59,7 +59,7 @@ int check_bits(int bits, bool host_only, int* n_levels) {
 int check_group(int group_size, bool device) {
   if (device) {
     if (group_size != cq::kGroup)
-      return fail(CQ_ERR_UNSUPPORTED, "group_size=%d: device kernels support 128 here", group_size);
+      return fail(CQ_ERR_UNSUPPORTED, "group_size=%d: this call supports 128", group_size);
   } else if (!is_pow2(group_size) || group_size < 8 || group_size > 4096) {
     // From 8 up, a group's packed indices fill whole bytes at every width.
     return fail(CQ_ERR_ARG, "group_size=%d must be a power of two in [8, 4096]", group_size);
