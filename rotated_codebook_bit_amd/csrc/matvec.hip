@@ -113,28 +113,45 @@ __device__ __forceinline__ uint64_t load_codes16(const uint8_t* __restrict__ row
 // Level table in LDS.  2 bits: entry b (a code byte) holds the 4 levels its
 // four 2-bit codes select; 4 bits: entry b holds the 2 levels of its two
 // nibbles; 3 bits: plain 8-entry table.
-template <int SB>
+//
+// The lookups are data-dependent, so lanes reading the LDS in the same cycle
+// collide on banks.  With K > 1 the table is stored in K interleaved copies
+// (entry e of copy c at slot e * K + c) and lane l reads copy l % K, so the
+// bank a lane touches depends on its copy rather than on its code.  Filling
+// K copies costs every block K times the table writes and K times the LDS:
+// measured on the 225-matrix pass, 8 copies pay from batch chunks of 4 rows
+// (batch 8: 7.0 -> 6.15 ms) and cost at 1 to 3 rows.
+template <int SB, int K>
 struct Levels {
-  static constexpr int floats = SB == 2 ? 1024 : (SB == 4 ? 512 : kMaxLevels);
+  static constexpr int entry = SB == 2 ? 4 : (SB == 4 ? 2 : 1);  // floats per entry
+  static constexpr int entries = SB == 3 ? kMaxLevels : 256;
+  static constexpr int floats = entries * entry * K;
   static __device__ __forceinline__ float lev(const LevelTable& lv, int i) { return level_at(lv, i); }
   static __device__ __forceinline__ void fill(float* tab, const LevelTable& lv, int t) {
+    if (t >= entries) return;
+    float e[entry];
     if constexpr (SB == 2) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) tab[4 * t + e] = lev(lv, (t >> (2 * e)) & 3);
+      for (int q = 0; q < 4; ++q) e[q] = lev(lv, (t >> (2 * q)) & 3);
     } else if constexpr (SB == 4) {
-      tab[2 * t] = lev(lv, t & 15);
-      tab[2 * t + 1] = lev(lv, t >> 4);
+      e[0] = lev(lv, t & 15);
+      e[1] = lev(lv, t >> 4);
     } else {
-      if (t < kMaxLevels) tab[t] = lev(lv, t);
+      e[0] = lev(lv, t);
     }
+#pragma unroll
+    for (int c = 0; c < K; ++c)
+#pragma unroll
+      for (int q = 0; q < entry; ++q) tab[(t * K + c) * entry + q] = e[q];
   }
-  // Levels of the 16 codes into v[16].
-  static __device__ __forceinline__ void decode(uint64_t codes, const float* tab, float (&v)[16]) {
+  // Levels of the 16 codes into v[16]; copy = lane % K.
+  static __device__ __forceinline__ void decode(uint64_t codes, const float* tab, int copy, float (&v)[16]) {
+    const float* t = tab + copy * entry;
     if constexpr (SB == 2) {
       const uint32_t c = static_cast<uint32_t>(codes);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 f = *reinterpret_cast<const float4*>(tab + 4 * ((c >> (8 * q)) & 0xFFu));
+        const float4 f = *reinterpret_cast<const float4*>(t + 4 * K * ((c >> (8 * q)) & 0xFFu));
         v[4 * q] = f.x;
         v[4 * q + 1] = f.y;
         v[4 * q + 2] = f.z;
@@ -143,16 +160,19 @@ struct Levels {
     } else if constexpr (SB == 4) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const float2 f = *reinterpret_cast<const float2*>(tab + 2 * ((codes >> (8 * q)) & 0xFFu));
+        const float2 f = *reinterpret_cast<const float2*>(t + 2 * K * ((codes >> (8 * q)) & 0xFFu));
         v[2 * q] = f.x;
         v[2 * q + 1] = f.y;
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) v[e] = tab[(codes >> (3 * e)) & 7u];
+      for (int e = 0; e < 16; ++e) v[e] = t[K * ((codes >> (3 * e)) & 7u)];
     }
   }
 };
+
+// Table copies for a batch chunk of NB rows.
+constexpr int table_copies(int nb) { return nb >= 4 ? 8 : 1; }
 
 // RB rows x NB batch rows per block; RB * NB <= 32 keeps the accumulators
 // and the activations of a chunk (16 * NB) in registers.
@@ -160,9 +180,10 @@ template <int SB, int NB, int RB>
 __global__ void __launch_bounds__(kBlock)
 matvec_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restrict__ bstart, int n,
               LevelTable lv, const float* __restrict__ xr, int64_t b0) {
-  __shared__ __attribute__((aligned(16))) float tab[Levels<SB>::floats];
+  using Lv = Levels<SB, table_copies(NB)>;
+  __shared__ __attribute__((aligned(16))) float tab[Lv::floats];
   __shared__ float red[RB * NB][kBlock + 1];
-  Levels<SB>::fill(tab, lv, threadIdx.x);
+  Lv::fill(tab, lv, threadIdx.x);
   __syncthreads();
   const int t = threadIdx.x;
   const int64_t total = bstart[n];
@@ -214,7 +235,7 @@ matvec_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restrict__ 
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
           float v[16];
-          Levels<SB>::decode(codes[r], tab, v);
+          Lv::decode(codes[r], tab, t % table_copies(NB), v);
           float part[NB];
 #pragma unroll
           for (int b = 0; b < NB; ++b) part[b] = 0.0f;
