@@ -314,8 +314,8 @@ def main():
     copy_gbs = 2 * src.numel() * 4 / (tcopy * 1e-3) / 1e9
     del src, dst
     dom = "dequantize_f32" if tdq >= tq else "quantize"
-    dom_kernel = {"dequantize_f32": "dequantize_contig<2, false, false>",
-                  "quantize": "quantize_contig<4, true, false>"}
+    dom_kernel = {"dequantize_f32": "dequantize_contig<2, false, false, false>",
+                  "quantize": "quantize_contig<4, true, false, false>"}
     ach = gbs(phases[dom]["bytes"], phases[dom]["ms"])
     traffic = None
     if os.path.exists(TRAFFIC_FILE):

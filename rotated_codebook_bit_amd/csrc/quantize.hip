@@ -617,7 +617,10 @@ fakequant_contig(const uint8_t* __restrict__ w, int64_t n_groups, QuantParams p,
   constexpr int NI = WAVE_BYTES / 1024;
   constexpr int OB = BF16OUT ? 2 : 4;     // output bytes per element
   constexpr int GOB = kGroup * OB;        // output bytes per group
-  constexpr int PB = 32;                  // bytes per group per phase
+  // Bytes per group per phase: 64 (half a 128-byte line per piece) where
+  // the LDS allows it, else 32 (8 and 16 levels with bf16 input keep their
+  // 64-byte level table and stay within two blocks per CU).
+  constexpr int PB = (L <= 4 || !BF16IN) ? 64 : 32;
   constexpr int PE = PB / OB;             // elements per group per phase
   constexpr int CPP = PB / 16;            // 16-byte chunks per group per phase
   constexpr int GPB = 256 / PB;           // groups per 256-byte LDS row
@@ -626,8 +629,12 @@ fakequant_contig(const uint8_t* __restrict__ w, int64_t n_groups, QuantParams p,
   constexpr int NIO = OWB / 1024;         // store instructions per phase
   __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * WAVE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t olds[kWaves * OWB];
-  __shared__ float lut[kMaxLevels];
-  if (threadIdx.x < kMaxLevels) lut[threadIdx.x] = level_at(lv, threadIdx.x);
+  float* lut = nullptr;  // level table for the 8- and 16-level searches only
+  if constexpr (L >= 8) {
+    __shared__ float lut_s[kMaxLevels];
+    if (threadIdx.x < kMaxLevels) lut_s[threadIdx.x] = level_at(lv, threadIdx.x);
+    lut = lut_s;
+  }
   __syncthreads();
 
   const int lane = threadIdx.x & (kWave - 1);
