@@ -171,7 +171,7 @@ def model_bytes(shapes, bits: int, group_size: int = GROUP) -> int:
 def codebook(bits: int, samples=None, iters: int = 200) -> np.ndarray:
     """float32 codebook levels in N(0,1) units.  ``samples`` (float64) are the
     Lloyd-Max training draws; None uses the standard 400,000 seed-0 draws."""
-    if samples is None and bits != TERNARY:
+    if samples is None and bits not in (TERNARY, TERNARY_TRITS):
         from .workloads import lloyd_samples
         samples = lloyd_samples()
     s = np.ascontiguousarray(np.zeros(0) if samples is None else samples, dtype=np.float64)
