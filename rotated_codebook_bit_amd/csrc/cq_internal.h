@@ -268,7 +268,7 @@ struct SplitLevels {
   uint32_t lo[kMaxLevels];
 };
 
-int gemm_block_rows();  // batch rows per GEMM block
+int gemm_block_rows(int64_t batch);  // batch rows per GEMM block (32 or 64)
 int gemm_block_cols();  // outputs per GEMM block
 
 // Workspace units: matrix d has (k / 128) * mpad rotate units, each writing

@@ -24,7 +24,8 @@
 //     out [group][row][hi 128 | lo 128] so that the 64-row tile of a group is
 //     32 KiB of contiguous memory; rows past the batch are zeros.
 //   gemm_kernel: a block computes a 64 (batch) x 256 (outputs) tile of one
-//     matrix; wave w owns outputs [64w, 64w + 64) as 2 x 2 tiles of 32 x 32.
+//     matrix; wave w owns outputs [64w, 64w + 64) as 2 x 2 tiles of 32 x 32
+//     (batches of at most 32: 32 x 256 tiles, 1 x 2 per wave).
 //     Per 128-value group:
 //       - the group's activation tile moves HBM -> LDS by direct-to-LDS DMA
 //         (double-buffered: the next group's DMA runs under this group's
@@ -47,11 +48,12 @@ namespace kg {
 
 constexpr int kWaves = 4;
 constexpr int kBlock = kWaves * kWave;
-constexpr int BM = 64;            // batch rows per block
 constexpr int BN = 256;           // outputs per block
-constexpr int TM = 2, TN = 2;     // 32 x 32 tiles per wave
+constexpr int TN = 2;             // 32 x 32 tiles per wave along the outputs
 constexpr int kRowBytes = 512;    // one workspace row of a group: 128 hi + 128 lo bf16
-constexpr int kTileBytes = BM * kRowBytes;  // 32 KiB
+// Rows per block: TM x 32 with TM = 2 (64 rows), or TM = 1 (32 rows) for
+// batches of at most 32, which halves the work spent on padding rows.
+constexpr int block_rows(int64_t batch) { return batch <= 32 ? 32 : 64; }
 constexpr int kXcds = 8;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -235,10 +237,13 @@ __device__ __forceinline__ float half_to_float(uint16_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, h));
 }
 
-template <int SB>
+template <int SB, int TM>
 __global__ void __launch_bounds__(kBlock, 2)
 gemm_kernel(const GemmDesc* __restrict__ table, const int64_t* __restrict__ bstart, int n,
             SplitLevels sl, const uint8_t* __restrict__ ws, int64_t batch) {
+  constexpr int BM = 32 * TM;                 // batch rows per block
+  constexpr int kTileBytes = BM * kRowBytes;  // 16 or 32 KiB per group
+  constexpr int kDmaPerWave = BM / 8;         // 1 KiB DMA instructions per wave per tile
   // Two tile buffers as separate objects, each access naming one of them, so
   // the compiler can tell the next tile's DMA from this tile's reads and does
   // not wait for the former before the latter.
@@ -290,7 +295,7 @@ gemm_kernel(const GemmDesc* __restrict__ table, const int64_t* __restrict__ bsta
 #if defined(__HIP_DEVICE_COMPILE__)
     const auto src = make_rsrc(xs + g * mpad * kRowBytes, kTileBytes);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kDmaPerWave; ++i) {
       const int slot0 = 64 * (4 * i + wave);
       const int slot = slot0 + lane;
       const int r = slot >> 5, p = slot & 31;
@@ -395,14 +400,18 @@ template <int SB>
 hipError_t launch_sb(const GemmDesc* table, const int64_t* bstart, int n, int64_t blocks,
                      const SplitLevels& sl, const uint8_t* ws, int64_t batch, hipStream_t s) {
   const int64_t grid = ((blocks + kXcds - 1) / kXcds) * kXcds;
-  hipLaunchKernelGGL((gemm_kernel<SB>), dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, s, table,
-                     bstart, n, sl, ws, batch);
+  if (block_rows(batch) == 32)
+    hipLaunchKernelGGL((gemm_kernel<SB, 1>), dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, s, table,
+                       bstart, n, sl, ws, batch);
+  else
+    hipLaunchKernelGGL((gemm_kernel<SB, 2>), dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, s, table,
+                       bstart, n, sl, ws, batch);
   return hipGetLastError();
 }
 
 }  // namespace kg
 
-int gemm_block_rows() { return kg::BM; }
+int gemm_block_rows(int64_t batch) { return kg::block_rows(batch); }
 int gemm_block_cols() { return kg::BN; }
 
 hipError_t launch_split_rotate(const GemmDesc* table, const int64_t* ustart, int n, int64_t units,

@@ -527,7 +527,7 @@ int cq_dequant_gemm_many(int n, const cq_matvec_desc* descs, int bits, int group
     sl.hi[i] = hi;
     sl.lo[i] = bf16_rne_host(levels[i] - hv);
   }
-  const int64_t bm = cq::gemm_block_rows(), bn = cq::gemm_block_cols();
+  const int64_t bm = cq::gemm_block_rows(batch), bn = cq::gemm_block_cols();
   const int64_t mpad = ceil_div(batch, bm) * bm;
   std::vector<cq::GemmDesc> act;
   std::vector<int64_t> ustart{0}, bstart{0};
