@@ -135,3 +135,22 @@ def test_gemm_deterministic_and_close_to_matvec(weight, levels):
     assert np.array_equal(a, b)
     m = host(cq.dequant_matvec(p, n, 11008, 4096, 2, levels[2], xd))
     check_matvec(a, m.astype(np.float64), x, w_hat, tol=GEMM_TOL + MV_TOL)
+
+
+@pytest.mark.parametrize("batch", [32, 64, 3])
+@pytest.mark.parametrize("n_out,k", [(512, 16384), (256, 128)])
+def test_gemm_and_matvec_edges(batch, n_out, k, levels):
+    """Tile boundaries (batch 32 / 64, outputs a multiple of 256), a long row
+    (k = 16384: 128 groups, 4 matvec passes) and a single-group row, through
+    both product calls."""
+    lv = levels[2]
+    rng = np.random.default_rng(zlib.crc32(repr(("edge", batch, n_out, k)).encode()))
+    q = O.quantize(rng.standard_normal((n_out, k)) * 0.02, 2, lv)
+    w_hat = O.dequantize(q.packed, q.norm16, n_out, k, 2, lv)
+    x = rng.standard_normal((batch, k)).astype(np.float32)
+    y_ref = x.astype(np.float64) @ w_hat.T
+    p, n = dev_q(q, n_out)
+    xd = torch.from_numpy(x).to(DEV)
+    say(f"edges gemm+matvec {n_out}x{k} batch={batch}")
+    check_matvec(host(cq.dequant_gemm(p, n, n_out, k, 2, lv, xd)), y_ref, x, w_hat, tol=GEMM_TOL)
+    check_matvec(host(cq.dequant_matvec(p, n, n_out, k, 2, lv, xd)), y_ref, x, w_hat, tol=MV_TOL)
