@@ -3,8 +3,8 @@
  * MI355X (gfx950).  C ABI.
  *
  * The method (sources are web pages, cited by title and section):
- *   - weights are cut into groups of G = 128 consecutive values along the
- *     last axis, the last group of a row zero-padded
+ *   - weights are cut into groups of G consecutive values along the last axis
+ *     (G = 128 unless stated), the last group of a row zero-padded
  *     ("Cactus Quants CQ2-bit Quantization: Extreme Compression for Edge
  *     LLMs", section Group-wise Weight Partitioning);
  *   - each group is rotated by the orthonormal Walsh-Hadamard matrix
@@ -41,7 +41,8 @@
  *     +Inf.
  *   - levels (host, nullable where stated): n_levels float32 codebook levels
  *     in N(0,1) units (before the 1/sqrt(G) scaling), strictly ascending.
- *     n_levels must be 3 for CQ_TERNARY and 2^bits otherwise.
+ *     n_levels must be 3 for CQ_TERNARY and CQ_TERNARY_TRITS, 2^bits
+ *     otherwise.
  *   - group_size: cq_quantize, cq_dequantize and cq_fake_quant take 32, 64,
  *     128 or 256 ("Cactus Quants CQ2-bit Quantization: Extreme Compression
  *     for Edge LLMs", FAQ on group size);
@@ -52,11 +53,12 @@
  *     waiting.  On a validation error nothing is enqueued.  Asynchronous
  *     faults surface at the caller's next synchronisation.  Buffers must stay
  *     alive until the stream has passed the call.
- *   - rows*cols == 0 (or n_out*k == 0) is a successful no-op.
+ *   - rows*cols == 0 (or n_out == 0) is a successful no-op; a product with
+ *     k == 0 writes zeros to y (an empty sum).
  *   - Alignment: w, out, packed, x, y must be 16-byte aligned; norms 2-byte;
  *     packed in trit storage (CQ_TERNARY_TRITS) 2-byte.
- *   - Inputs and outputs must not overlap.  Non-finite inputs give
- *     unspecified but deterministic results.
+ *   - Inputs and outputs must not overlap (cq_fake_quant allows out == w).
+ *     Non-finite inputs give unspecified but deterministic results.
  *   - Return value: CQ_OK (0) or a negative cq_status.  cq_last_error()
  *     returns a thread-local message for the last failing call.
  *   - Ownership: the caller owns every buffer.  The library keeps no pointer
@@ -97,13 +99,15 @@ typedef enum { CQ_F32 = 0, CQ_BF16 = 1 } cq_dtype;
 
 /* Sizes of the quantized form of one rows x cols tensor.
  * n_groups = rows * ceil(cols / group_size);
- * packed_bytes = n_groups * group_size * sbits / 8.  Host only, pure.
+ * packed_bytes = n_groups * B (B the bytes per group of the packed layout
+ * above: group_size * sbits / 8, or ceil(group_size / 5) for trit storage).
+ * Host only, pure.
  * Either output pointer may be NULL. */
 int cq_layout(int64_t rows, int64_t cols, int bits, int group_size,
               int64_t* n_groups, int64_t* packed_bytes);
 
-/* Storage size of a set of tensors: for every group, group_size*sbits/8 bytes
- * of indices plus 2 bytes of binary16 norm, and nothing else
+/* Storage size of a set of tensors: for every group, B bytes of indices (as
+ * in cq_layout) plus 2 bytes of binary16 norm, and nothing else
  * ("How CQ2-bit Quantization Contributes to Needle 2's Small Footprint",
  * section Per-Group Storage Breakdown).  rows/cols are host arrays of
  * n_tensors entries.  Padded groups count in full.  Host only, pure. */
@@ -112,7 +116,8 @@ int cq_model_bytes(int n_tensors, const int64_t* rows, const int64_t* cols,
 
 /* Codebook levels in N(0,1) units, written as float32 to levels_out (host,
  * room for CQ_MAX_LEVELS), count to *n_levels (host).
- * CQ_TERNARY returns the fixed levels -1.2240064, 0, 1.2240064
+ * CQ_TERNARY and CQ_TERNARY_TRITS return the fixed levels -1.2240064, 0,
+ * 1.2240064
  * ("How Quantization Codebooks Are Trained in Cactus Quants", section Ternary
  * Special Case Handling) and ignores samples.  Other widths run 1-D Lloyd-Max
  * (k-means) with 2^bits levels on the n_samples host samples (double), as the
@@ -155,9 +160,9 @@ int cq_dequantize(const uint8_t* packed, const uint16_t* norms, int64_t rows,
  * tensor i's packed indices to packed_offsets[i] and of its norms to
  * norm_offsets[i] (host arrays of n_tensors entries, each may be NULL) and
  * the blob size to *total_bytes (may be NULL), which equals cq_model_bytes.
- * With group_size 128 every offset is a multiple of 16 (packed) or 2
- * (norms), so a 16-byte aligned blob can take cq_quantize_many's outputs
- * directly.  Host only, pure. */
+ * With group_size 128 every offset is a multiple of 16 (packed bit fields;
+ * 2 for trit storage) or 2 (norms), so a 16-byte aligned blob can take
+ * cq_quantize_many's outputs directly.  Host only, pure. */
 int cq_blob_layout(int n_tensors, const int64_t* rows, const int64_t* cols, int bits,
                    int group_size, int64_t* packed_offsets, int64_t* norm_offsets,
                    int64_t* total_bytes);
@@ -167,7 +172,7 @@ typedef struct {
   const void* w;     /* rows x cols, the call's w_dtype */
   int64_t rows;
   int64_t cols;
-  uint8_t* packed;   /* [rows][ceil(cols/G)][G*sbits/8] */
+  uint8_t* packed;   /* [rows][ceil(cols/G)][B], B as in cq_layout */
   uint16_t* norms;   /* [rows][ceil(cols/G)] */
 } cq_quant_desc;
 
@@ -274,8 +279,9 @@ int cq_dequant_matvec_many(int n, const cq_matvec_desc* descs, int bits, int gro
  * float32 accumulation, then scaled by norm / G per (row, group).  Each
  * product is then within about 3 * 2^-16 of its float32 value, so
  * |y - exact| <= about 5e-5 * ||x_b|| * ||W_hat_n||.  Deterministic (fixed
- * order).  Workspace: about 4 * batch * k bytes (batch rounded up to 64) per
- * matrix, stream-ordered (hipMallocAsync / hipFreeAsync on `stream`). */
+ * order).  Workspace: 4 * batch * k bytes per matrix, with batch rounded up
+ * to 32 (batches of at most 32) or 64, stream-ordered (hipMallocAsync /
+ * hipFreeAsync on `stream`). */
 int cq_dequant_gemm(const uint8_t* packed, const uint16_t* norms, int64_t n_out,
                     int64_t k, int bits, int group_size, const float* levels,
                     int n_levels, const float* x, int64_t batch, float* y,
