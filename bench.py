@@ -112,12 +112,22 @@ def cpu_baseline() -> dict:
         dt += time.perf_counter() - t0
         params += w.size
         del w, q, w_hat
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(params / dt / 1e9, 6), "unit": "Gparams/s", "cores": int(blas_threads),
             "kind": "oracle",
             "sample": f"one 7B-shaped transformer layer + the embedding ({params:,} bf16-valued "
                       f"params, 8 tensors) "
                       f"through quantize, dequantize and a batch-1 matvec, float64 NumPy, "
-                      f"{dt:.1f} s timed; host cpu_count={os.cpu_count()}"}
+                      f"{dt:.1f} s timed; host {model}, cpu_count={os.cpu_count()}, "
+                      f"BLAS threads={blas_threads}"}
 
 
 def main():
