@@ -42,6 +42,17 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama7b.json")
 KERNEL_SOURCES = ["rotated_codebook_bit_amd/csrc/quantize.hip",
                   "rotated_codebook_bit_amd/csrc/dequantize.hip",
                   "rotated_codebook_bit_amd/csrc/matvec.hip"]
+# The source file of each measured phase's kernel: a traffic entry is valid
+# while that file is unchanged.
+PHASE_SOURCE = {"quantize": "rotated_codebook_bit_amd/csrc/quantize.hip",
+                "dequantize_f32": "rotated_codebook_bit_amd/csrc/dequantize.hip",
+                "matvec_pass_b1": "rotated_codebook_bit_amd/csrc/matvec.hip",
+                "fake_quant_bf16_extra": "rotated_codebook_bit_amd/csrc/quantize.hip"}
+
+
+def file_digest(rel: str) -> str:
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def sources_digest() -> str:
@@ -331,8 +342,9 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         try:
             t = json.load(open(TRAFFIC_FILE))
-            if t.get("sources_digest") == sources_digest() and dom in t.get("kernels", {}):
-                traffic = t["kernels"][dom]["hbm_bytes_per_launch"]
+            entry = t.get("kernels", {}).get(dom, {})
+            if entry.get("source_digest") == file_digest(PHASE_SOURCE[dom]):
+                traffic = entry["hbm_bytes_per_launch"]
         except Exception:
             traffic = None
     roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
