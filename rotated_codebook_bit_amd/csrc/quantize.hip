@@ -345,8 +345,12 @@ __device__ __forceinline__ QBatch resolve(const QuantJob& j, int64_t b, int& d) 
   }
 }
 
+// Resident blocks per CU: two for bf16 input (64 KiB of LDS each), one for
+// float32 input (128 KiB).
+constexpr int blocks_per_cu(bool bf16_in) { return bf16_in ? kBlocksPerCu : 1; }
+
 template <int L, bool BF16, bool MANY, bool TRITS = false>
-__global__ void __launch_bounds__(kBlock, 2)
+__global__ void __launch_bounds__(kBlock, blocks_per_cu(BF16))
 quantize_contig(QuantJob job, QuantParams p) {
   constexpr int GB = BF16 ? 256 : 512;  // input bytes per group
   constexpr int CPG = GB / 16;          // 16-byte chunks per group
@@ -608,7 +612,7 @@ __device__ __forceinline__ float stage1_group(const uint32_t (&raw)[BF16 ? 64 : 
 // buffer in phases of 32 bytes per group so that consecutive lanes store
 // consecutive bytes.
 template <int L, bool BF16IN, bool BF16OUT>
-__global__ void __launch_bounds__(kBlock, 2)
+__global__ void __launch_bounds__(kBlock, blocks_per_cu(BF16IN))
 fakequant_contig(const uint8_t* __restrict__ w, int64_t n_groups, QuantParams p, LevelTable lv,
                  uint8_t* __restrict__ out) {
   constexpr int GB = BF16IN ? 256 : 512;  // input bytes per group
@@ -781,7 +785,7 @@ hipError_t launch_fq(const void* w, int64_t rows, int64_t cols, const QuantParam
   if (cols % kGroup == 0) {
     const int64_t n_groups = rows * (cols / kGroup);
     const int64_t n_batches = (n_groups + kWave - 1) / kWave;
-    const int blocks = persistent_blocks((n_batches + kWaves - 1) / kWaves, BF16IN ? kBlocksPerCu : 1);
+    const int blocks = persistent_blocks((n_batches + kWaves - 1) / kWaves, blocks_per_cu(BF16IN));
     hipLaunchKernelGGL((fakequant_contig<L, BF16IN, BF16OUT>), dim3(blocks), dim3(kBlock), 0, s, wb,
                        n_groups, p, lv, ob);
   } else {
@@ -814,7 +818,7 @@ hipError_t launch_l(const void* w, int64_t rows, int64_t cols, const QuantParams
     // One resident grid (two blocks per CU, the occupancy the kernel is
     // built for); each wave loops over batches so the next batch's DMA
     // overlaps the current arithmetic.
-    const int blocks = persistent_blocks((n_batches + kWaves - 1) / kWaves, kBlocksPerCu);
+    const int blocks = persistent_blocks((n_batches + kWaves - 1) / kWaves, blocks_per_cu(BF16));
     const QuantJob job{wb, packed, norms, n_groups, TensorTable<QuantDesc>{nullptr, nullptr, 0}, n_batches};
     hipLaunchKernelGGL((quantize_contig<L, BF16, false, TRITS>), dim3(blocks), dim3(kBlock), 0, s, job, p);
   } else {
@@ -830,7 +834,7 @@ template <int L, bool BF16, bool TRITS>
 hipError_t launch_many_l(const QuantParams& p, TensorTable<QuantDesc> contig, int64_t contig_batches,
                          TensorTable<QuantDesc> ragged, int64_t ragged_groups, hipStream_t s) {
   if (contig_batches > 0) {
-    const int blocks = persistent_blocks((contig_batches + kWaves - 1) / kWaves, kBlocksPerCu);
+    const int blocks = persistent_blocks((contig_batches + kWaves - 1) / kWaves, blocks_per_cu(BF16));
     const QuantJob job{nullptr, nullptr, nullptr, 0, contig, contig_batches};
     hipLaunchKernelGGL((quantize_contig<L, BF16, true, TRITS>), dim3(blocks), dim3(kBlock), 0, s, job, p);
     const hipError_t e = hipGetLastError();
