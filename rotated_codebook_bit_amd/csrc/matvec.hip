@@ -26,6 +26,11 @@
 // (4-bit) levels per LDS read from a byte table, and accumulates NB partial
 // sums per row.  The block reduces its RB x NB partials through LDS in a
 // fixed order, so results are deterministic.
+//
+// One batch row with 2-bit codes (a decode step) takes matvec_pair_kernel
+// instead: per column pair it tabulates the 16 partial products a 4-bit
+// code pair can select, so the inner loop is one conflict-free LDS read and
+// one add per two weights (see the comment above that kernel).
 
 #include "cq_internal.h"
 
@@ -276,6 +281,177 @@ matvec_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restrict__ 
   }
 }
 
+// ---- One batch row, 2-bit codes: pair tables -----------------------------
+//
+// With one activation row, the partial product of two adjacent columns
+// depends only on their 4-bit code pair:
+//     P_j[v] = c[v & 3] * xr[2j] + c[v >> 2] * xr[2j + 1],   v = 0 .. 15.
+// A block builds the 16 sums of every column pair of a 1024-column tile once
+// and all its rows read them: one LDS read and one add per two weights,
+// instead of a level read and a multiply-add per weight.
+//
+// Lane l of every wave owns columns 16l .. 16l + 15 of the tile (pairs
+// q = 0 .. 7).  Entry (q, v, l) sits at float (16q + v) * 64 + l, so in any
+// read instruction lane l touches bank l (mod the bank count) whatever its
+// codes: the lookups are free of bank conflicts.  The byte address is
+// 4096 q + 256 v + 4 l; q is a compile-time offset, and 256 v + 4 l is one
+// byte permute of the code word (its nibbles first spread one per byte) and
+// the lane's byte.
+//
+// A block is kPairWaves waves over kPairRows consecutive rows of one matrix
+// (16 per wave); each wave keeps its 16 rows' sums in registers across the
+// tiles and reduces them over its lanes at the end.  Summation order is
+// fixed, so results are deterministic.
+constexpr int kPairWaves = 8;
+constexpr int kPairRowsPerWave = 16;
+constexpr int kPairRows = kPairWaves * kPairRowsPerWave;
+constexpr int log2i(int v) { return v <= 1 ? 0 : 1 + log2i(v / 2); }
+constexpr int kPairTile = kWave * kChunk;  // 1024 columns per tile
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pair_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+template <int W, int RPW>
+__global__ void __launch_bounds__(W * kWave)
+matvec_pair_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restrict__ bstart, int n,
+                   LevelTable lv, const float* __restrict__ xr, int64_t b0) {
+  __shared__ __attribute__((aligned(16))) float tab[8 * 16 * kWave];
+  const int lane = threadIdx.x % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t blk = blockIdx.x;  // one block per row block
+  const int d = find_unit(bstart, 0, n, blk);
+  const MatvecDesc* md = table + d;
+  const int64_t n_out = load_const(&md->n_out), k = load_const(&md->k);
+  const int64_t row0 = (blk - load_const(bstart + d)) * (W * RPW) + w * RPW;
+  const int64_t row_bytes = k / 4, ngr = k / kGroup;
+  const float* x_rot = xr + load_const(&md->xr_offset) + b0 * k;
+  // The wave's rows as buffer resources: rows past the end of the matrix lie
+  // outside them and read as zero (their sums are never stored).  The host
+  // sends a matrix here only when k <= 2^28, so 16 rows of codes (4 k bytes)
+  // and every offset below stay under 2^31.
+  const int64_t rows_in = n_out - row0 < RPW ? (n_out - row0 > 0 ? n_out - row0 : 0) : RPW;
+  const auto codes_src = pair_rsrc(load_const(&md->packed) + (rows_in ? row0 * row_bytes : 0), rows_in * row_bytes);
+  const auto norms_src = pair_rsrc(load_const(&md->norms) + (rows_in ? row0 * ngr : 0), rows_in * ngr * 2);
+  const float c0l = lv.c[0], c1l = lv.c[1], c2l = lv.c[2], c3l = lv.c[3];
+  const uint32_t lane_bytes = 4u * static_cast<uint32_t>(lane);
+
+  float acc[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
+
+  // Tile inputs: the activations of the PPT pairs this thread tabulates
+  // (pairs PPT w .. PPT w + PPT - 1 of lane `lane`'s chunk), and for each of
+  // the wave's rows the codes of this lane's 16 columns and the norm of
+  // their group.  The whole buffer offset goes in the range-checked vector
+  // operand; a lane without columns in the tile offsets by 2^30, past every
+  // resource (at most 4 k <= 2^30 bytes), and reads zero.
+  constexpr int PPT = W >= 8 ? 1 : 8 / W;
+  const bool builds = PPT * w < 8;  // with more than 8 waves, waves 8.. only read
+  struct Tile {
+    float2 x[PPT];
+    uint32_t codes[RPW];
+    _Float16 norm[RPW];
+  };
+  // Row r of the wave reads at scalar offset r * row_bytes; rows past the
+  // end of the matrix re-read its last row (their sums are never stored), so
+  // every in-range access lies inside the matrix.
+  int soff_c[RPW], soff_n[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int rr = r < rows_in ? r : (rows_in > 0 ? static_cast<int>(rows_in) - 1 : 0);
+    soff_c[r] = __builtin_amdgcn_readfirstlane(static_cast<int>(rr * row_bytes));
+    soff_n[r] = __builtin_amdgcn_readfirstlane(static_cast<int>(2 * rr * ngr));
+  }
+  auto load = [&](int64_t p0, Tile& t) {
+    const int64_t c0 = p0 + kChunk * lane;
+    const bool active = c0 < k;  // k % 128 == 0: whole chunks only
+#pragma unroll
+    for (int h = 0; h < PPT; ++h)
+      t.x[h] = active && builds ? *reinterpret_cast<const float2*>(x_rot + c0 + 2 * (PPT * w + h))
+                                : make_float2(0.0f, 0.0f);
+    const int coff = active ? static_cast<int>(c0 / 4) : (1 << 30);
+    const int noff = active ? static_cast<int>(2 * (c0 / kGroup)) : (1 << 30);
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      t.codes[r] = __builtin_amdgcn_raw_buffer_load_b32(codes_src, coff, soff_c[r], 0);
+      t.norm[r] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(norms_src, noff, soff_n[r], 0));
+    }
+  };
+  auto step = [&](int64_t p0, const Tile& t) {
+    const bool active = p0 + kChunk * lane < k;
+    __syncthreads();  // the previous tile's reads are done
+    if (active && builds) {
+#pragma unroll
+      for (int h = 0; h < PPT; ++h) {
+        const float x0 = t.x[h].x, x1 = t.x[h].y;
+        const float pa[4] = {c0l * x0, c1l * x0, c2l * x0, c3l * x0};
+        const float cb[4] = {c0l, c1l, c2l, c3l};
+        float* dst = tab + (16 * (PPT * w + h)) * kWave + lane;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) dst[(a + 4 * bb) * kWave] = __builtin_fmaf(cb[bb], x1, pa[a]);
+      }
+    }
+    __syncthreads();
+    if (active) {
+      const char* tb = reinterpret_cast<const char*>(tab);
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        // Pair q's nibble is byte q/2 of `ev` (q even) or of `od` (q odd).
+        const uint32_t ev = t.codes[r] & 0x0F0F0F0Fu, od = (t.codes[r] >> 4) & 0x0F0F0F0Fu;
+        float s = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          // Byte 0 of the address is the lane's (4 l), byte 1 is byte q/2
+          // of the spread nibbles (v), bytes 2 and 3 are zero (selector 12).
+          const uint32_t e = (q & 1) ? od : ev;
+          const uint32_t addr = __builtin_amdgcn_perm(e, lane_bytes, 0x0C0C0000u | ((4u + (q >> 1)) << 8));
+          const float v = *reinterpret_cast<const float*>(tb + addr + 4096 * q);
+          s = q ? s + v : v;
+        }
+        // norm * s here, and the exact power-of-two 1/128 once at the end.
+        acc[r] = __builtin_fmaf(static_cast<float>(t.norm[r]), s, acc[r]);
+      }
+    }
+  };
+
+  for (int64_t p0 = 0; p0 < k; p0 += kPairTile) {
+    Tile cur;
+    load(p0, cur);
+    step(p0, cur);
+  }
+
+  // Reduce the RPW row sums over the 64 lanes: each exchange halves the
+  // values a lane holds (the lane with the offset's bit set keeps the upper
+  // half), then the remaining offsets sum within groups of 64 / RPW lanes.
+  // With RPW = 16, lane l ends with row 8*b5 + 4*b4 + 2*b3 + b2 of its wave
+  // (b_i = bit i of l).  Both halves are summed and one is kept, so every
+  // select has constant operands (the two partners add the same two values,
+  // in either order).
+  constexpr int kSteps = log2i(RPW);
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int o = 32 >> i, V = RPW >> i;
+    const bool hi = lane & o;
+#pragma unroll
+    for (int j = 0; j < V / 2; ++j) {
+      const float lo_sum = acc[j] + __shfl_xor(acc[j], o, kWave);
+      const float hi_sum = acc[j + V / 2] + __shfl_xor(acc[j + V / 2], o, kWave);
+      acc[j] = hi ? hi_sum : lo_sum;
+    }
+  }
+  float s = acc[0];
+#pragma unroll
+  for (int o = 32 >> kSteps; o >= 1; o >>= 1) s += __shfl_xor(s, o, kWave);
+  s *= 1.0f / kGroup;
+  int r = 0;
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) r += ((lane >> (5 - i)) & 1) * (RPW >> (i + 1));
+  if ((lane & (64 / RPW - 1)) == 0 && row0 + r < n_out) load_const(&md->y)[b0 * n_out + row0 + r] = s;
+}
+
 // Writes a chunk of descriptors (received as kernel arguments) to the table.
 __global__ void table_init_kernel(DescChunk c, MatvecDesc* __restrict__ table,
                                   int64_t* __restrict__ gstart, int64_t* __restrict__ bstart0,
@@ -301,6 +477,11 @@ __global__ void __launch_bounds__(kBlock) zero_kernel(float* __restrict__ y, int
 constexpr int rows_per_block(int nb) {
   return nb <= 1 ? 16 : 32 / (nb <= 2 ? 2 : nb <= 4 ? 4 : 8);
 }
+
+// 2-bit codes with one batch row take the pair-table kernel when a wave's 16
+// rows of codes (4 k bytes) fit its 32-bit buffer range.
+constexpr int64_t kPairMaxK = int64_t(1) << 28;
+constexpr bool use_pairs(int sb, int nb, int64_t max_k) { return sb == 2 && nb == 1 && max_k <= kPairMaxK; }
 
 template <int SB, int NB>
 hipError_t launch_nb(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks,
@@ -330,7 +511,9 @@ hipError_t launch_sb(const MatvecDesc* table, const int64_t* bstart, int n, int6
 
 }  // namespace km
 
-int matvec_rows_per_block(int nb) { return km::rows_per_block(nb); }
+int matvec_rows_per_block(int sbits, int nb, int64_t max_k) {
+  return km::use_pairs(sbits, nb, max_k) ? km::kPairRows : km::rows_per_block(nb);
+}
 
 hipError_t launch_rotate(const MatvecDesc* table, const int64_t* gstart, int n, int64_t total_groups,
                          float* xr, hipStream_t stream) {
@@ -343,8 +526,13 @@ hipError_t launch_rotate(const MatvecDesc* table, const int64_t* gstart, int n, 
 
 hipError_t launch_matvec(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks,
                          int sbits, const LevelTable& lv, const float* xr, int64_t b0, int nb,
-                         hipStream_t stream) {
+                         int64_t max_k, hipStream_t stream) {
   if (blocks <= 0) return hipSuccess;
+  if (km::use_pairs(sbits, nb, max_k)) {
+    hipLaunchKernelGGL((km::matvec_pair_kernel<km::kPairWaves, km::kPairRowsPerWave>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(km::kPairWaves * kWave), 0, stream, table, bstart, n, lv, xr, b0);
+    return hipGetLastError();
+  }
   switch (sbits) {
     case 2: return km::launch_sb<2>(table, bstart, n, blocks, lv, xr, b0, nb, stream);
     case 3: return km::launch_sb<3>(table, bstart, n, blocks, lv, xr, b0, nb, stream);

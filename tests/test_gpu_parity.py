@@ -271,17 +271,18 @@ def test_matvec(batch, matvec_weight, levels):
     say(f"matvec batch={batch}: {check_matvec(y, y_ref, x, w_hat).line()}")
 
 
+@pytest.mark.parametrize("batch", [2, 1])
 @pytest.mark.parametrize("bits", [O.TERNARY, 3, 4])
 @pytest.mark.parametrize("n_out,k", [(37, 11008), (300, 384)])
-def test_matvec_bits_shapes(bits, n_out, k, levels):
+def test_matvec_bits_shapes(bits, n_out, k, batch, levels):
     lv = levels[bits]
     rng = np.random.default_rng(n_out + k + bits)
     w = rng.standard_normal((n_out, k)) * 0.02
     q = O.quantize(w, bits, lv)
-    x = rng.standard_normal((2, k)).astype(np.float32)
+    x = rng.standard_normal((batch, k)).astype(np.float32)
     w_hat = O.dequantize(q.packed, q.norm16, n_out, k, bits, lv)
     y_ref = x.astype(np.float64) @ w_hat.T
-    say(f"matvec bits={bits} {n_out}x{k}")
+    say(f"matvec bits={bits} {n_out}x{k} batch={batch}")
     y = host(cq.dequant_matvec(torch.from_numpy(q.packed.reshape(n_out, -1)).to(DEV),
                                torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16),
                                n_out, k, bits, lv, to_dev_f32(x)))
@@ -322,13 +323,14 @@ def test_matvec_many(batch, levels):
             check_matvec(y, x.astype(np.float64) @ w_hat.T, x, w_hat)
 
 
-def test_matvec_deterministic(matvec_weight, levels):
+@pytest.mark.parametrize("batch", [8, 1])
+def test_matvec_deterministic(batch, matvec_weight, levels):
     lv = levels[2]
     _, q = matvec_weight
     p_dev = torch.from_numpy(q.packed.reshape(11008, -1)).to(DEV)
     n_dev = torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16)
-    x = to_dev_f32(W.matvec_x(8))
-    say("matvec determinism")
+    x = to_dev_f32(W.matvec_x(batch))
+    say(f"matvec determinism batch={batch}")
     a = host(cq.dequant_matvec(p_dev, n_dev, 11008, 4096, 2, lv, x))
     b = host(cq.dequant_matvec(p_dev, n_dev, 11008, 4096, 2, lv, x))
     assert np.array_equal(a, b)
