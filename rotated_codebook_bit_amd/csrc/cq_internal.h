@@ -117,6 +117,13 @@ inline int persistent_blocks(int64_t work_blocks, int per_cu) {
   return static_cast<int>(b > 0 ? b : 1);
 }
 
+// Blocks of `waves` waves for a grid-stride kernel over n_batches batches in
+// which each wave takes about `per_wave` batches.
+inline int spread_blocks(int64_t n_batches, int waves, int per_wave) {
+  const int64_t b = (n_batches + static_cast<int64_t>(waves) * per_wave - 1) / (static_cast<int64_t>(waves) * per_wave);
+  return static_cast<int>(b > 0 ? b : 1);
+}
+
 // Launchers (return hipError_t of the launch).  All sizes already validated.
 // trits: store the three-level code five indices per byte (26 B per group).
 hipError_t launch_quantize(const void* w, bool bf16, bool trits, int64_t rows, int64_t cols,

@@ -26,8 +26,8 @@ namespace kd {
 
 constexpr int kWaves = 4;
 constexpr int kBlock = kWaves * kWave;
-// One resident block per CU measured faster than two for this store-heavy
-// kernel (fewer concurrent write streams).
+// Resident blocks per CU for the bf16-output grid: one measured faster than
+// two for this store-heavy kernel.
 constexpr int kBlocksPerCu = 1;
 
 __device__ __forceinline__ void butterfly(float (&y)[kGroup]) {
@@ -441,6 +441,16 @@ dequantize_ragged(const uint8_t* __restrict__ packed, const uint16_t* __restrict
   }
 }
 
+// Grid size.  Float32 output: one batch per wave, a grid that covers the
+// tensor (5-6% faster on the 7B-shaped model than a resident grid).  Bf16
+// output: a resident grid of kBlocksPerCu blocks per CU looping over the
+// batches (the covering grid measured 8% slower there).
+template <bool BF16OUT>
+int dequant_blocks(int64_t n_batches) {
+  return BF16OUT ? persistent_blocks((n_batches + kWaves - 1) / kWaves, kBlocksPerCu)
+                 : spread_blocks(n_batches, kWaves, 1);
+}
+
 template <int SB, bool BF16OUT, bool TRITS>
 hipError_t launch_sb(const uint8_t* packed, const uint16_t* norms, int64_t rows, int64_t cols,
                      const LevelTable& lv, void* out, hipStream_t s) {
@@ -448,7 +458,7 @@ hipError_t launch_sb(const uint8_t* packed, const uint16_t* norms, int64_t rows,
   if (cols % kGroup == 0) {
     const int64_t n_groups = rows * (cols / kGroup);
     const int64_t n_batches = (n_groups + kWave - 1) / kWave;
-    const int blocks = persistent_blocks((n_batches + kWaves - 1) / kWaves, kBlocksPerCu);
+    const int blocks = dequant_blocks<BF16OUT>(n_batches);
     const DequantJob job{packed, norms, ob, n_groups, TensorTable<DequantDesc>{nullptr, nullptr, 0},
                          n_batches};
     hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT, false, TRITS>), dim3(blocks), dim3(kBlock), 0, s, job,
@@ -467,7 +477,7 @@ template <int SB, bool BF16OUT, bool TRITS>
 hipError_t launch_many_sb(const LevelTable& lv, TensorTable<DequantDesc> contig, int64_t contig_batches,
                           TensorTable<DequantDesc> ragged, int64_t ragged_groups, hipStream_t s) {
   if (contig_batches > 0) {
-    const int blocks = persistent_blocks((contig_batches + kWaves - 1) / kWaves, kBlocksPerCu);
+    const int blocks = dequant_blocks<BF16OUT>(contig_batches);
     const DequantJob job{nullptr, nullptr, nullptr, 0, contig, contig_batches};
     hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT, true, TRITS>), dim3(blocks), dim3(kBlock), 0, s, job,
                        lv);
