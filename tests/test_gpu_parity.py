@@ -203,7 +203,10 @@ def test_sweep_4096(bits, levels):
 
 # -- 7B-shaped model, one flat launch, sampled checks --------------------------------
 
-def test_llama7b_flat_sampled(levels):
+@pytest.fixture(scope="module")
+def llama7b(levels):
+    """The whole 7B-shaped model quantized by one flat launch and dequantized
+    to float32 by one flat launch (the launches the benchmark times)."""
     lv = levels[2]
     say("llama7b: generate 6.6G bf16 params on the device")
     buf, offsets = W.llama7b_device(DEV)
@@ -211,31 +214,58 @@ def test_llama7b_flat_sampled(levels):
     w2 = buf.view(n_groups, 128)
     say(f"llama7b: quantize {n_groups} groups in one launch")
     packed, norms = cq.quantize(w2, 2, lv)
-    torch.cuda.synchronize()
-    rng = np.random.default_rng(7)
-    sample = np.unique(np.concatenate([
-        rng.choice(n_groups, 30_000, replace=False),
-        np.arange(n_groups - 300, n_groups),                  # the final, partial batches
-        np.arange(int(offsets[4]) // 128, int(offsets[5]) // 128),  # one full 4096x11008 tensor
-    ]))
-    idx_dev = torch.from_numpy(sample).to(DEV)
-    x = W.bf16_bits_to_f32(host(w2.index_select(0, idx_dev).view(torch.int16)).view(np.uint16))
-    say(f"llama7b: oracle on {sample.size} sampled groups")
-    q = O.quantize(x.astype(np.float64), 2, lv)
-    p = host(packed.view(n_groups, 32).index_select(0, idx_dev))
-    n = host(norms.view(n_groups).view(torch.int16).index_select(0, idx_dev)).view(np.uint16)
-    rep = check_quantize(p.reshape(-1, 1, 32), n.reshape(-1, 1), q)
-    say(f"llama7b quantize: {rep.line()}")
-    say("llama7b: dequantize whole model to fp32")
+    say("llama7b: dequantize the whole model to fp32 in one launch")
     out = cq.dequantize(packed.view(n_groups, 32), norms.view(n_groups, 1), n_groups, 128, 2, lv)
-    got = host(out.index_select(0, idx_dev))
-    del out
-    ref = O.dequantize(q.packed, q.norm16, sample.size, 128, 2, lv)
-    same = np.all(O.unpack(p, 2) == q.idx[:, 0], axis=1) & (n == q.norm16[:, 0])
-    rms = q.norm16[:, 0].view(np.float16).astype(np.float64) / math.sqrt(128)
-    err = np.abs(got.astype(np.float64) - ref)
-    assert np.all(err[same] <= 1e-5 * rms[same, None])
-    say(f"llama7b round trip: groups compared {int(same.sum())} of {sample.size}")
+    torch.cuda.synchronize()
+    yield {"w2": w2, "offsets": offsets, "n_groups": n_groups, "packed": packed.view(n_groups, 32),
+           "norms": norms.view(n_groups), "out": out}
+    del buf, w2, packed, norms, out
+    torch.cuda.empty_cache()
+
+
+def check_llama7b_groups(m, sample, lv, label):
+    """Quantize parity and round trip on the given group indices, oracle side
+    in chunks so host memory stays modest."""
+    mism = elems = compared = 0
+    for c0 in range(0, sample.size, 262_144):
+        part = sample[c0:c0 + 262_144]
+        idx_dev = torch.from_numpy(part).to(DEV)
+        x = W.bf16_bits_to_f32(host(m["w2"].index_select(0, idx_dev).view(torch.int16)).view(np.uint16))
+        q = O.quantize(x.astype(np.float64), 2, lv)
+        p = host(m["packed"].index_select(0, idx_dev))
+        n = host(m["norms"].view(torch.int16).index_select(0, idx_dev)).view(np.uint16)
+        rep = check_quantize(p.reshape(-1, 1, 32), n.reshape(-1, 1), q, enforce_count=False)
+        mism += rep["index_mismatches"]
+        elems += rep["elements"]
+        got = host(m["out"].index_select(0, idx_dev)).astype(np.float64)
+        ref = O.dequantize(q.packed, q.norm16, part.size, 128, 2, lv)
+        same = np.all(O.unpack(p, 2) == q.idx[:, 0], axis=1) & (n == q.norm16[:, 0])
+        rms = q.norm16[:, 0].view(np.float16).astype(np.float64) / math.sqrt(128)
+        assert np.all(np.abs(got - ref)[same] <= 1e-5 * rms[same, None])
+        compared += int(same.sum())
+        say(f"{label}: {c0 + part.size} of {sample.size} groups checked")
+    check_count(mism, elems)
+    say(f"{label}: {mism} in-band index mismatches in {elems} elements; round trip on {compared} groups")
+
+
+def test_llama7b_random_groups(llama7b, levels):
+    """A fixed random 1% of all groups, plus the final (partial) batches."""
+    n_groups = llama7b["n_groups"]
+    rng = np.random.default_rng(7)
+    sample = np.unique(np.concatenate([rng.choice(n_groups, n_groups // 100, replace=False),
+                                       np.arange(n_groups - 300, n_groups)]))
+    check_llama7b_groups(llama7b, sample, levels[2], "llama7b 1% sample")
+
+
+@pytest.mark.parametrize("tensor", [0, 4, 6, 224], ids=["4096x4096", "4096x11008", "11008x4096", "32000x4096"])
+def test_llama7b_full_tensor(tensor, llama7b, levels):
+    """Every group of the first tensor of each shape (the embedding is the
+    last tensor)."""
+    off = llama7b["offsets"]
+    sample = np.arange(int(off[tensor]) // 128, int(off[tensor + 1]) // 128)
+    shape = W.llama7b_shapes()[tensor]
+    assert sample.size == shape[0] * shape[1] // 128
+    check_llama7b_groups(llama7b, sample, levels[2], f"llama7b tensor {tensor} {shape}")
 
 
 # -- dequant-matvec 11008x4096 ------------------------------------------------------
