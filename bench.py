@@ -17,6 +17,21 @@ through the same three steps).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        python bench.py --copy-only   (plain device copy, for counter scaling)
+       python bench.py --configs     (the small configurations: one JSON report line)
+
+--configs times, per configuration, single calls with HIP events (3 warm-up
+calls, median of 15), warm (inputs cache-resident after the previous call)
+and cold (a 1 GiB device write before each timed call evicts L2 and the
+256 MB last-level cache):
+  C1  fp32 256x512, 2 bits: quantize and dequantize latency;
+  C2  the 45.8M-parameter Needle-2-sized set (fp32, 92 tensors, one 300x1000
+      tensor padded): one cq_quantize_many / cq_dequantize_many call, and the
+      same quantize as 92 per-tensor calls;
+  C3  bf16 4096x4096 heavy-tailed matrix, ternary / 2 / 3 / 4 bits: quantize,
+      dequantize and the relative reconstruction error;
+  C5  the 11008x4096 matrix at batch 1 and 8: dequant-matvec (and the GEMM at
+      batch 8) against the binding roof max(HBM time, fp32 VALU time);
+and the CPU oracle on C1, C2, C3 (each width) and C5, in full.
 """
 
 from __future__ import annotations
@@ -74,6 +89,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-only", action="store_true", help="only run a plain 4 GiB device copy")
+    ap.add_argument("--configs", action="store_true", help="report the small configurations instead")
     return ap.parse_args()
 
 
@@ -92,6 +108,161 @@ def copy_only(torch):
     ms = e0.elapsed_time(e1)
     print(json.dumps({"copy_bytes_each_way": 4 * n, "ms": ms,
                       "GBps_read_plus_write": 2 * 4 * n / ms / 1e6}), flush=True)
+
+
+# fp32 FMA rate without packed instructions (which this build does not use):
+# 256 CUs x 64 lanes x 2 flops x 2.4 GHz.
+VALU_F32_PEAK_TFS = 78.6
+
+
+def call_times(torch, fn, scrub=None, n=15, warm=3) -> float:
+    """Median milliseconds of n single calls timed with HIP events on the
+    current stream, after `warm` untimed calls.  With `scrub`, the tensor is
+    overwritten before each timed call (outside the events)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warm):
+        fn()
+    times = []
+    for _ in range(n):
+        if scrub is not None:
+            scrub.fill_(1.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return float(np.median(times))
+
+
+def warm_cold(torch, fn, scrub, nbytes=None) -> dict:
+    w, c = call_times(torch, fn), call_times(torch, fn, scrub)
+    r = {"warm_us": round(1e3 * w, 2), "cold_us": round(1e3 * c, 2)}
+    if nbytes:
+        r["warm_GBps"] = round(nbytes / w / 1e6, 1)
+        r["cold_GBps"] = round(nbytes / c / 1e6, 1)
+    return r
+
+
+def configs_report(torch) -> dict:
+    import rotated_codebook_bit_amd as cq
+    from rotated_codebook_bit_amd import workloads as W
+    dev = "cuda"
+    scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    rep = {"report": "configs", "timing": "HIP events around single calls; median of 15 after 3 warm-up "
+                                          "calls; cold = a 1 GiB device write before each timed call"}
+
+    # C1: latency of the smallest case.
+    lv2 = cq.codebook(2)
+    w = torch.from_numpy(W.small()).to(dev)
+    pk, nm = cq.quantize(w, 2, lv2)
+    out = torch.empty_like(w)
+    nb = w.numel() * 4 + pk.numel() + nm.numel() * 2
+    rep["C1"] = {"shape": [256, 512], "dtype": "f32", "bits": 2, "algorithmic_bytes": nb,
+                 "quantize": warm_cold(torch, lambda: cq.quantize(w, 2, lv2, packed=pk, norms=nm), scrub, nb),
+                 "dequantize": warm_cold(torch, lambda: cq.dequantize(pk, nm, 256, 512, 2, lv2, out=out), scrub, nb)}
+
+    # C2: the Needle-2-sized parameter set.
+    tensors = [torch.from_numpy(a).to(dev) for _, a in W.needle2()]
+    params = sum(t.numel() for t in tensors)
+    blob, views = cq.quantize_many(tensors, 2, lv2)
+    nbq = params * 4 + blob.numel()
+    items = [(p.reshape(t.shape[0], -1), n, t.shape[0], t.shape[1]) for t, (p, n) in zip(tensors, views)]
+    outs = [torch.empty_like(t) for t in tensors]
+    singles = [cq.quantize(t, 2, lv2) for t in tensors]
+
+    def per_tensor():
+        for t, (p, n) in zip(tensors, singles):
+            cq.quantize(t, 2, lv2, packed=p, norms=n)
+
+    rep["C2"] = {"tensors": len(tensors), "params": params, "model_bytes": blob.numel(),
+                 "quantize_many_1_call": warm_cold(torch, lambda: cq.quantize_many(tensors, 2, lv2, blob=blob,
+                                                                                    views=False), scrub, nbq),
+                 "dequantize_many_1_call": warm_cold(torch, lambda: cq.dequantize_many(items, 2, lv2, outs=outs),
+                                                     scrub, nbq),
+                 "quantize_per_tensor_calls": warm_cold(torch, per_tensor, scrub, nbq)}
+    del tensors, blob, views, items, outs, singles
+
+    # C3: every width on the heavy-tailed 4096x4096 bf16 matrix.
+    b = W.sweep_bits()
+    wb = torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)
+    w64 = wb.double()
+    rep["C3"] = {}
+    for bits, name in ((cq.TERNARY, "ternary"), (2, "2"), (3, "3"), (4, "4")):
+        lv = cq.codebook(bits)
+        pk, nm = cq.quantize(wb, bits, lv)
+        o = cq.dequantize(pk, nm, 4096, 4096, bits, lv)
+        nbq = wb.numel() * 2 + pk.numel() + nm.numel() * 2
+        nbd = pk.numel() + nm.numel() * 2 + o.numel() * 4
+        err = float(torch.linalg.vector_norm(w64 - o.double()) / torch.linalg.vector_norm(w64))
+        rep["C3"][name] = {"relative_error": round(err, 4),
+                           "quantize": warm_cold(torch, lambda: cq.quantize(wb, bits, lv, packed=pk, norms=nm),
+                                                 scrub, nbq),
+                           "dequantize": warm_cold(torch, lambda: cq.dequantize(pk, nm, 4096, 4096, bits, lv,
+                                                                                out=o), scrub, nbd)}
+    del wb, w64
+
+    # C5: the 11008x4096 product at batch 1 and 8.
+    wm = torch.from_numpy(W.matvec_weight_bits().view(np.int16)).to(dev).view(torch.bfloat16)
+    pk, nm = cq.quantize(wm, 2, lv2)
+    rep["C5"] = {}
+    for batch in (1, 8):
+        x = torch.from_numpy(W.matvec_x(batch)).to(dev)
+        y = torch.empty((batch, 11008), dtype=torch.float32, device=dev)
+        nbm = pk.numel() + nm.numel() * 2 + x.numel() * 4 + y.numel() * 4
+        flops = 2 * batch * 11008 * 4096
+        t_hbm = nbm / (HBM_PEAK_GBS * 1e9) * 1e6
+        t_valu = flops / (VALU_F32_PEAK_TFS * 1e12) * 1e6
+        roof = max(t_hbm, t_valu)
+        r = {"algorithmic_bytes": nbm, "flops": flops, "t_hbm_us": round(t_hbm, 3),
+             "t_valu_us": round(t_valu, 3), "binding": "hbm" if t_hbm >= t_valu else "valu"}
+        mv = warm_cold(torch, lambda: cq.dequant_matvec(pk, nm, 11008, 4096, 2, lv2, x, y=y), scrub)
+        mv["frac_of_roof_warm"] = round(roof / mv["warm_us"], 3)
+        mv["frac_of_roof_cold"] = round(roof / mv["cold_us"], 3)
+        r["matvec"] = mv
+        if batch >= 8:
+            gm = warm_cold(torch, lambda: cq.dequant_gemm(pk, nm, 11008, 4096, 2, lv2, x, y=y), scrub)
+            gm["frac_of_roof_warm"] = round(roof / gm["warm_us"], 3)
+            r["gemm"] = gm
+        rep["C5"][f"batch{batch}"] = r
+    rep["notes"] = ("C1, C3 and C5 take a few microseconds of kernel time, so launch latency and the "
+                    "per-call descriptor and rotation launches dominate their call times")
+    return rep
+
+
+def cpu_baseline_configs() -> dict:
+    """The oracle on C1, C2, C3 (each width) and C5 in full: quantize +
+    dequantize (C5: dequantize + the float64 product), params/s."""
+    from oracle import cq_oracle as O
+    from rotated_codebook_bit_amd import workloads as W
+    import rotated_codebook_bit_amd as cq
+    res = {}
+
+    def run(name, ws, bits, extra=None):
+        lv = cq.codebook(bits)
+        t0 = time.perf_counter()
+        n = 0
+        for w in ws:
+            q = O.quantize(w, bits, lv)
+            wh = O.dequantize(q.packed, q.norm16, w.shape[0], w.shape[1], bits, lv)
+            if extra is not None:
+                extra(wh)
+            n += w.size
+        dt = time.perf_counter() - t0
+        res[name] = {"s": round(dt, 3), "Mparams_per_s": round(n / dt / 1e6, 3)}
+
+    run("C1", [W.small().astype(np.float64)], 2)
+    run("C2", [a.astype(np.float64) for _, a in W.needle2()], 2)
+    w3 = W.bf16_bits_to_f32(W.sweep_bits()).astype(np.float64)
+    for bits, name in ((cq.TERNARY, "ternary"), (2, "2"), (3, "3"), (4, "4")):
+        run(f"C3_{name}", [w3], bits)
+    wm = W.bf16_bits_to_f32(W.matvec_weight_bits()).astype(np.float64)
+    for batch in (1, 8):
+        x = W.matvec_x(batch).astype(np.float64)
+        run(f"C5_batch{batch}", [wm], 2, extra=lambda wh: x @ wh.T)
+    res["note"] = "float64 NumPy oracle; C5 includes quantizing W (its input is the float matrix)"
+    res["cpu_count"] = os.cpu_count()
+    return res
 
 
 def cpu_baseline() -> dict:
@@ -153,6 +324,13 @@ def main():
         sys.exit(2)
     if args.copy_only:
         copy_only(torch)
+        return
+    if args.configs:
+        rep = configs_report(torch)
+        if not args.no_cpu:
+            log("CPU oracle on the small configurations")
+            rep["cpu_oracle"] = cpu_baseline_configs()
+        print(json.dumps(rep), flush=True)
         return
 
     import rotated_codebook_bit_amd as cq

@@ -118,9 +118,16 @@ inline int persistent_blocks(int64_t work_blocks, int per_cu) {
 }
 
 // Blocks of `waves` waves for a grid-stride kernel over n_batches batches in
-// which each wave takes about `per_wave` batches.
-inline int spread_blocks(int64_t n_batches, int waves, int per_wave) {
-  const int64_t b = (n_batches + static_cast<int64_t>(waves) * per_wave - 1) / (static_cast<int64_t>(waves) * per_wave);
+// which each wave takes about `per_wave` batches, but never fewer than one
+// batch per wave gives up to per_cu resident blocks per CU, so a mid-size
+// tensor still reaches every CU.
+inline int spread_blocks(int64_t n_batches, int waves, int per_wave, int per_cu) {
+  const int64_t w = waves;
+  const int64_t spread = (n_batches + w * per_wave - 1) / (w * per_wave);
+  const int64_t one = (n_batches + w - 1) / w;
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * per_cu;
+  const int64_t fill = one < cap ? one : cap;
+  const int64_t b = spread > fill ? spread : fill;
   return static_cast<int>(b > 0 ? b : 1);
 }
 

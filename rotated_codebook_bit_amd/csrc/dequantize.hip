@@ -448,7 +448,7 @@ dequantize_ragged(const uint8_t* __restrict__ packed, const uint16_t* __restrict
 template <bool BF16OUT>
 int dequant_blocks(int64_t n_batches) {
   return BF16OUT ? persistent_blocks((n_batches + kWaves - 1) / kWaves, kBlocksPerCu)
-                 : spread_blocks(n_batches, kWaves, 1);
+                 : spread_blocks(n_batches, kWaves, 1, kBlocksPerCu);
 }
 
 template <int SB, bool BF16OUT, bool TRITS>

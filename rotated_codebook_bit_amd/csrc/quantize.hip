@@ -352,7 +352,8 @@ constexpr int blocks_per_cu(bool bf16_in) { return bf16_in ? kBlocksPerCu : 1; }
 // Batches per wave of the grid.  A grid of about four batches per wave
 // (each wave strides by the grid) measured 4-7% faster on the 7B-shaped
 // model than a resident grid of blocks_per_cu blocks per CU that loops over
-// all batches, for quantize (bf16 and float32 input) and fake quant.
+// all batches, for quantize (bf16 and float32 input) and fake quant.  Smaller
+// tensors get at least the resident grid's block count (spread_blocks).
 constexpr int kBatchesPerWave = 4;
 
 template <int L, bool BF16, bool MANY, bool TRITS = false>
@@ -791,7 +792,7 @@ hipError_t launch_fq(const void* w, int64_t rows, int64_t cols, const QuantParam
   if (cols % kGroup == 0) {
     const int64_t n_groups = rows * (cols / kGroup);
     const int64_t n_batches = (n_groups + kWave - 1) / kWave;
-    const int blocks = spread_blocks(n_batches, kWaves, kBatchesPerWave);
+    const int blocks = spread_blocks(n_batches, kWaves, kBatchesPerWave, blocks_per_cu(BF16IN));
     hipLaunchKernelGGL((fakequant_contig<L, BF16IN, BF16OUT>), dim3(blocks), dim3(kBlock), 0, s, wb,
                        n_groups, p, lv, ob);
   } else {
@@ -823,7 +824,7 @@ hipError_t launch_l(const void* w, int64_t rows, int64_t cols, const QuantParams
     const int64_t n_batches = (n_groups + kWave - 1) / kWave;
     // Each wave loops over a few batches, so the next batch's DMA overlaps
     // the current arithmetic.
-    const int blocks = spread_blocks(n_batches, kWaves, kBatchesPerWave);
+    const int blocks = spread_blocks(n_batches, kWaves, kBatchesPerWave, blocks_per_cu(BF16));
     const QuantJob job{wb, packed, norms, n_groups, TensorTable<QuantDesc>{nullptr, nullptr, 0}, n_batches};
     hipLaunchKernelGGL((quantize_contig<L, BF16, false, TRITS>), dim3(blocks), dim3(kBlock), 0, s, job, p);
   } else {
@@ -839,7 +840,7 @@ template <int L, bool BF16, bool TRITS>
 hipError_t launch_many_l(const QuantParams& p, TensorTable<QuantDesc> contig, int64_t contig_batches,
                          TensorTable<QuantDesc> ragged, int64_t ragged_groups, hipStream_t s) {
   if (contig_batches > 0) {
-    const int blocks = spread_blocks(contig_batches, kWaves, kBatchesPerWave);
+    const int blocks = spread_blocks(contig_batches, kWaves, kBatchesPerWave, blocks_per_cu(BF16));
     const QuantJob job{nullptr, nullptr, nullptr, 0, contig, contig_batches};
     hipLaunchKernelGGL((quantize_contig<L, BF16, true, TRITS>), dim3(blocks), dim3(kBlock), 0, s, job, p);
     const hipError_t e = hipGetLastError();

@@ -353,6 +353,29 @@ def test_matvec_many(batch, levels):
             check_matvec(y, x.astype(np.float64) @ w_hat.T, x, w_hat)
 
 
+def test_matvec_many_large_call(levels):
+    """Batch 1 over 40 matrices of 2048 rows: enough row blocks for the
+    pair-table kernel's 128-row blocks (a single matrix takes 16-row ones),
+    with two k values and a ragged last row block."""
+    lv = levels[2]
+    rng = np.random.default_rng(55)
+    items, refs = [], []
+    for i in range(40):
+        n_out, k = (2048, 256) if i % 2 else (2047, 384)
+        q = O.quantize(rng.standard_normal((n_out, k)) * 0.02, 2, lv)
+        x = rng.standard_normal((1, k)).astype(np.float32)
+        w_hat = O.dequantize(q.packed, q.norm16, n_out, k, 2, lv)
+        y = torch.full((1, n_out), float("nan"), dtype=torch.float32, device=DEV)
+        items.append((torch.from_numpy(q.packed.reshape(n_out, -1)).to(DEV),
+                      torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16), n_out, k,
+                      to_dev_f32(x), y))
+        refs.append((x, w_hat))
+    say("matvec_many batch=1, 40 matrices")
+    cq.dequant_matvec_many(items, 2, lv, 1)
+    for (x, w_hat), it in zip(refs, items):
+        check_matvec(host(it[5]), x.astype(np.float64) @ w_hat.T, x, w_hat)
+
+
 @pytest.mark.parametrize("batch", [8, 1])
 def test_matvec_deterministic(batch, matvec_weight, levels):
     lv = levels[2]
