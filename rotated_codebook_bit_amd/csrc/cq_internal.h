@@ -249,16 +249,22 @@ struct DescChunk {
 hipError_t launch_table_init(const DescChunk& c, MatvecDesc* table, int64_t* gstart,
                              int64_t* bstart0, int64_t* bstart1, hipStream_t stream);
 
-// Rows per product-kernel block for a batch chunk of nb rows of sbits-bit
-// codes, the longest matrix row having max_k columns.
-int matvec_rows_per_block(int sbits, int nb, int64_t max_k);
+// Product kernel for a batch chunk of nb rows of sbits-bit codes over the n
+// matrices of descs (host array): its rows per block (the block prefix is
+// built from it) and, for the pair-table kernel, its rows per wave (0: the
+// byte-table kernel).  launch_matvec runs the kernel the plan names.
+struct MatvecPlan {
+  int rows_per_block;
+  int pair_rows_per_wave;
+};
+MatvecPlan matvec_plan(int sbits, int nb, const MatvecDesc* descs, int n);
 
 hipError_t launch_rotate(const MatvecDesc* table, const int64_t* gstart, int n, int64_t total_groups,
                          float* xr, hipStream_t stream);
 
 hipError_t launch_matvec(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks,
                          int sbits, const LevelTable& lv, const float* xr, int64_t b0, int nb,
-                         int64_t max_k, hipStream_t stream);
+                         const MatvecPlan& plan, hipStream_t stream);
 
 hipError_t launch_zero(float* y, int64_t count, hipStream_t stream);
 

@@ -745,10 +745,9 @@ int cq_dequant_matvec_many(int n, const cq_matvec_desc* descs, int bits, int gro
   // Batch rows go through the product kernel in chunks of at most 8.
   const int nb_full = static_cast<int>(batch < 8 ? batch : 8);
   const int nb_last = static_cast<int>(batch - 8 * ((batch - 1) / 8));
-  int64_t max_k = 0;
-  for (const cq::MatvecDesc& d : act) max_k = d.k > max_k ? d.k : max_k;
-  const int rb0 = cq::matvec_rows_per_block(sb, nb_full, max_k);
-  const int rb1 = cq::matvec_rows_per_block(sb, nb_last, max_k);
+  const cq::MatvecPlan plan0 = cq::matvec_plan(sb, nb_full, act.data(), na);
+  const cq::MatvecPlan plan1 = cq::matvec_plan(sb, nb_last, act.data(), na);
+  const int rb0 = plan0.rows_per_block, rb1 = plan1.rows_per_block;
   std::vector<int64_t> gstart(na + 1), bstart0(na + 1), bstart1(na + 1);
   int64_t xr_floats = 0;
   for (int i = 0; i < na; ++i) {
@@ -788,7 +787,7 @@ int cq_dequant_matvec_many(int n, const cq_matvec_desc* descs, int bits, int gro
     const int nb = static_cast<int>(batch - b0 < 8 ? batch - b0 : 8);
     const bool full = nb == nb_full;
     rc = hip_status(cq::launch_matvec(table, full ? b0_dev : b1_dev, na, full ? bstart0[na] : bstart1[na],
-                                      sb, lv, xr, b0, nb, max_k, s),
+                                      sb, lv, xr, b0, nb, full ? plan0 : plan1, s),
                     "matvec launch");
   }
   const int rc2 = hip_status(hipFreeAsync(ws, s), "workspace free");

@@ -61,41 +61,29 @@ __device__ __forceinline__ int find_desc(const int64_t* __restrict__ start, int 
 }
 
 // xr[m][b][g][:] = H x[m][b][g][:] for every 128-value group of every
-// matrix's activations; one thread per group.
+// matrix's activations; one wave per group.  Lane l holds values 2l and
+// 2l + 1: butterfly stage 1 runs inside the lane, stages 2..7 between lane l
+// and lane l ^ h (the lane with the bit clear keeps the sum), the same
+// operations in the same order as the sequential butterfly.
 __global__ void __launch_bounds__(kBlock)
 rotate_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restrict__ gstart, int n,
               float* __restrict__ xr) {
-  const int64_t g = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  const int lane = threadIdx.x % kWave;
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * kWaves + threadIdx.x / kWave;
   if (g >= gstart[n]) return;
   const int d = find_desc(gstart, n, g);
   const MatvecDesc& m = table[d];
   const int64_t local = g - gstart[d];  // group within the matrix's batch*k/128
-  const float* src = m.x + local * kGroup;
-  float* dst = xr + m.xr_offset + local * kGroup;
-  float y[kGroup];
+  const float2 v = reinterpret_cast<const float2*>(m.x + local * kGroup)[lane];
+  float y0 = v.x + v.y, y1 = v.x - v.y;
 #pragma unroll
-  for (int i = 0; i < kGroup / 4; ++i) {
-    const float4 v = reinterpret_cast<const float4*>(src)[i];
-    y[4 * i] = v.x;
-    y[4 * i + 1] = v.y;
-    y[4 * i + 2] = v.z;
-    y[4 * i + 3] = v.w;
+  for (int h = 1; h < kWave; h <<= 1) {
+    const float o0 = __shfl_xor(y0, h, kWave), o1 = __shfl_xor(y1, h, kWave);
+    const bool hi = lane & h;
+    y0 = hi ? o0 - y0 : y0 + o0;
+    y1 = hi ? o1 - y1 : y1 + o1;
   }
-#pragma unroll
-  for (int h = 1; h < kGroup; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < kGroup; i += 2 * h) {
-#pragma unroll
-      for (int j = i; j < i + h; ++j) {
-        const float a = y[j], b = y[j + h];
-        y[j] = a + b;
-        y[j + h] = a - b;
-      }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kGroup / 4; ++i)
-    reinterpret_cast<float4*>(dst)[i] = make_float4(y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]);
+  reinterpret_cast<float2*>(xr + m.xr_offset + local * kGroup)[lane] = make_float2(y0, y1);
 }
 
 // Packed codes of the 16 columns starting at column c0 (c0 % 16 == 0) of a
@@ -298,13 +286,15 @@ matvec_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restrict__ 
 // byte permute of the code word (its nibbles first spread one per byte) and
 // the lane's byte.
 //
-// A block is kPairWaves waves over kPairRows consecutive rows of one matrix
-// (16 per wave); each wave keeps its 16 rows' sums in registers across the
-// tiles and reduces them over its lanes at the end.  Summation order is
-// fixed, so results are deterministic.
+// A block is kPairWaves waves over consecutive rows of one matrix (16 per
+// wave, or kPairRowsPerWaveFew for calls with few rows); each wave keeps its
+// rows' sums in registers across the tiles and reduces them over its lanes
+// at the end.  Summation order is fixed, so results are deterministic.
 constexpr int kPairWaves = 8;
 constexpr int kPairRowsPerWave = 16;
-constexpr int kPairRows = kPairWaves * kPairRowsPerWave;
+// Rows per wave for calls whose 128-row blocks would not give every CU two:
+// more, shorter blocks.
+constexpr int kPairRowsPerWaveFew = 4;
 constexpr int log2i(int v) { return v <= 1 ? 0 : 1 + log2i(v / 2); }
 constexpr int kPairTile = kWave * kChunk;  // 1024 columns per tile
 
@@ -511,14 +501,22 @@ hipError_t launch_sb(const MatvecDesc* table, const int64_t* bstart, int n, int6
 
 }  // namespace km
 
-int matvec_rows_per_block(int sbits, int nb, int64_t max_k) {
-  return km::use_pairs(sbits, nb, max_k) ? km::kPairRows : km::rows_per_block(nb);
+MatvecPlan matvec_plan(int sbits, int nb, const MatvecDesc* descs, int n) {
+  int64_t max_k = 0;
+  for (int i = 0; i < n; ++i) max_k = descs[i].k > max_k ? descs[i].k : max_k;
+  if (!km::use_pairs(sbits, nb, max_k)) return MatvecPlan{km::rows_per_block(nb), 0};
+  constexpr int many = km::kPairWaves * km::kPairRowsPerWave;
+  int64_t blocks = 0;
+  for (int i = 0; i < n; ++i) blocks += (descs[i].n_out + many - 1) / many;
+  const int rpw = blocks >= 2 * static_cast<int64_t>(device_cu_count()) ? km::kPairRowsPerWave
+                                                                         : km::kPairRowsPerWaveFew;
+  return MatvecPlan{km::kPairWaves * rpw, rpw};
 }
 
 hipError_t launch_rotate(const MatvecDesc* table, const int64_t* gstart, int n, int64_t total_groups,
                          float* xr, hipStream_t stream) {
   if (total_groups <= 0) return hipSuccess;
-  const int64_t blocks = (total_groups + km::kBlock - 1) / km::kBlock;
+  const int64_t blocks = (total_groups + km::kWaves - 1) / km::kWaves;  // a wave per group
   hipLaunchKernelGGL(km::rotate_kernel, dim3(static_cast<unsigned>(blocks)), dim3(km::kBlock), 0,
                      stream, table, gstart, n, xr);
   return hipGetLastError();
@@ -526,13 +524,21 @@ hipError_t launch_rotate(const MatvecDesc* table, const int64_t* gstart, int n, 
 
 hipError_t launch_matvec(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks,
                          int sbits, const LevelTable& lv, const float* xr, int64_t b0, int nb,
-                         int64_t max_k, hipStream_t stream) {
+                         const MatvecPlan& plan, hipStream_t stream) {
   if (blocks <= 0) return hipSuccess;
-  if (km::use_pairs(sbits, nb, max_k)) {
-    hipLaunchKernelGGL((km::matvec_pair_kernel<km::kPairWaves, km::kPairRowsPerWave>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(km::kPairWaves * kWave), 0, stream, table, bstart, n, lv, xr, b0);
+  if (plan.pair_rows_per_wave == km::kPairRowsPerWave) {
+    hipLaunchKernelGGL((km::matvec_pair_kernel<km::kPairWaves, km::kPairRowsPerWave>),
+                       dim3(static_cast<unsigned>(blocks)), dim3(km::kPairWaves * kWave), 0, stream, table, bstart,
+                       n, lv, xr, b0);
     return hipGetLastError();
   }
+  if (plan.pair_rows_per_wave == km::kPairRowsPerWaveFew) {
+    hipLaunchKernelGGL((km::matvec_pair_kernel<km::kPairWaves, km::kPairRowsPerWaveFew>),
+                       dim3(static_cast<unsigned>(blocks)), dim3(km::kPairWaves * kWave), 0, stream, table, bstart,
+                       n, lv, xr, b0);
+    return hipGetLastError();
+  }
+  if (plan.pair_rows_per_wave != 0 || plan.rows_per_block != km::rows_per_block(nb)) return hipErrorInvalidValue;
   switch (sbits) {
     case 2: return km::launch_sb<2>(table, bstart, n, blocks, lv, xr, b0, nb, stream);
     case 3: return km::launch_sb<3>(table, bstart, n, blocks, lv, xr, b0, nb, stream);
