@@ -197,8 +197,10 @@ def test_sweep_4096(bits, levels):
     w64 = W.bf16_bits_to_f32(b).astype(np.float64)
     rep = run_case("sweep4096", w64, to_dev_bf16(b), bits, levels[bits])
     rot = O.relative_mse(w64, O.fake_quant(w64, bits, levels[bits]))
-    say(f"sweep4096 bits={bits} rel_mse={rot:.4f} rel_err={math.sqrt(rot):.4f}")
+    plain = O.relative_mse(w64, O.fake_quant(w64, bits, levels[bits], rotate=False))
+    say(f"sweep4096 bits={bits} rel_err={math.sqrt(rot):.4f} (without the rotation {math.sqrt(plain):.4f})")
     assert rep["elements"] == 4096 * 4096
+    assert rot < plain  # the outliers are what the rotation spreads
 
 
 # -- 7B-shaped model, one flat launch, sampled checks --------------------------------
