@@ -259,6 +259,11 @@ struct MatvecPlan {
 };
 MatvecPlan matvec_plan(int sbits, int nb, const MatvecDesc* descs, int n);
 
+// Activation rotations run one wave per 128-group when a call has fewer
+// than this many groups (a thread per group would leave most CUs idle), else
+// one thread per group (cheaper per group: no cross-lane traffic).
+constexpr int64_t kFewUnits = 32768;
+
 hipError_t launch_rotate(const MatvecDesc* table, const int64_t* gstart, int n, int64_t total_groups,
                          float* xr, hipStream_t stream);
 
@@ -280,6 +285,9 @@ struct GemmDesc {
   int64_t k;
   int64_t mpad;           // batch rounded up to the block's row count
   int64_t xs_off;         // bf16 offset of this matrix's split rotated x in the workspace
+  float* part;            // [ksplit][batch][n_out] partial sums in the workspace, or null: write y
+  int64_t ksplit;         // ranges of 128-groups along k, one block each per output tile
+  int64_t gps;            // groups per range (the last may be shorter)
 };
 
 // Levels split into bf16 halves (bits in the low 16 bits): level = hi + lo
@@ -296,6 +304,11 @@ int gemm_block_cols();  // outputs per GEMM block
 // 256 bf16 values.
 hipError_t launch_split_rotate(const GemmDesc* table, const int64_t* ustart, int n, int64_t units,
                                int64_t batch, uint16_t* ws, hipStream_t stream);
+
+// y = sum over the k ranges of each matrix's partial sums, in range order;
+// ostart: prefix of batch * n_out over the table's matrices.
+hipError_t launch_gemm_reduce(const GemmDesc* table, const int64_t* ostart, int n, int64_t outputs,
+                              int64_t batch, hipStream_t stream);
 
 hipError_t launch_gemm(const GemmDesc* table, const int64_t* bstart, int n, int64_t blocks, int sbits,
                        const SplitLevels& sl, const uint16_t* ws, int64_t batch, hipStream_t stream);

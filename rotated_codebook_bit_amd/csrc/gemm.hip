@@ -19,7 +19,8 @@
 // error, and a whole output at most about 5e-5 * ||x_b|| * ||W_hat_n||.
 //
 // Kernels.
-//   split_rotate_kernel: one thread per (matrix, group, padded batch row):
+//   split_rotate_kernel: one thread per (matrix, group, padded batch row)
+//     (split_rotate_wave_kernel: one wave, for calls with few of them):
 //     writes H x_g as 128 hi and 128 lo bf16 values to the workspace, laid
 //     out [group][row][hi 128 | lo 128] so that the 64-row tile of a group is
 //     32 KiB of contiguous memory; rows past the batch are zeros.
@@ -40,6 +41,10 @@
 //     Blocks are numbered so that consecutive blocks of a matrix share their
 //     weight tile, and the numbering is laid out so that such runs of blocks
 //     execute on the same XCD and share its L2.
+//   When a call has too few output tiles to give every CU two blocks (one
+//   matrix at a small batch, say), each tile's 128-groups are split into
+//   ranges, one block each, that write partial sums to the workspace, and
+//   gemm_reduce_kernel adds them in range order (deterministic results).
 
 #include "cq_internal.h"
 
@@ -140,6 +145,37 @@ split_rotate_kernel(const GemmDesc* __restrict__ table, const int64_t* __restric
   for (int i = 0; i < 16; ++i) d4[i] = make_uint4(hi[4 * i], hi[4 * i + 1], hi[4 * i + 2], hi[4 * i + 3]);
 #pragma unroll
   for (int i = 0; i < 16; ++i) d4[16 + i] = make_uint4(lo[4 * i], lo[4 * i + 1], lo[4 * i + 2], lo[4 * i + 3]);
+}
+
+// The same, one wave per (group, padded row), for calls with few units.  Lane l holds values 2l and 2l + 1:
+// butterfly stage 1 inside the lane, stages 2..7 between lane l and lane
+// l ^ h (the lane with the bit clear keeps the sum), the same operations in
+// the same order as the sequential butterfly.  Rows past the batch are zero.
+__global__ void __launch_bounds__(kBlock)
+split_rotate_wave_kernel(const GemmDesc* __restrict__ table, const int64_t* __restrict__ ustart, int n,
+                    int64_t batch, uint16_t* __restrict__ ws) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t u = static_cast<int64_t>(blockIdx.x) * kWaves + threadIdx.x / kWave;
+  if (u >= ustart[n]) return;  // whole waves
+  const int d = find_lane(ustart, n, u);
+  const GemmDesc& m = table[d];
+  const int64_t local = u - ustart[d];
+  const int64_t g = local / m.mpad, row = local - g * m.mpad;
+  float2 v = make_float2(0.0f, 0.0f);
+  if (row < batch) v = reinterpret_cast<const float2*>(m.x + row * m.k + g * kGroup)[lane];
+  float y0 = v.x + v.y, y1 = v.x - v.y;
+#pragma unroll
+  for (int h = 1; h < kWave; h <<= 1) {
+    const float o0 = __shfl_xor(y0, h, kWave), o1 = __shfl_xor(y1, h, kWave);
+    const bool up = lane & h;
+    y0 = up ? o0 - y0 : y0 + o0;
+    y1 = up ? o1 - y1 : y1 + o1;
+  }
+  const uint32_t h0 = bf16_rne_bits(y0), h1 = bf16_rne_bits(y1);
+  const uint32_t l0 = bf16_rne_bits(y0 - bf16_value(h0)), l1 = bf16_rne_bits(y1 - bf16_value(h1));
+  uint32_t* dst = reinterpret_cast<uint32_t*>(ws + m.xs_off + local * 256);
+  dst[lane] = h0 | (h1 << 16);
+  dst[64 + lane] = l0 | (l1 << 16);
 }
 
 // Byte tables in LDS.  SB = 2: entry b (a code byte, four codes) holds the
@@ -266,9 +302,15 @@ gemm_kernel(const GemmDesc* __restrict__ table, const int64_t* __restrict__ bsta
   const int64_t n_out = load_const(&md->n_out), k = load_const(&md->k);
   const int64_t mpad = load_const(&md->mpad), xs_off = load_const(&md->xs_off);
   const int64_t mtiles = mpad / BM;
+  const int64_t ksplit = load_const(&md->ksplit), gps = load_const(&md->gps);
+  float* const part = load_const(&md->part);
   const int64_t local = lb - load_const(bstart + d);
-  const int64_t nt = local / mtiles, mt = local - nt * mtiles;  // consecutive blocks share nt
+  const int64_t ks = local % ksplit, tile = local / ksplit;
+  const int64_t nt = tile / mtiles, mt = tile - nt * mtiles;  // consecutive blocks share nt
   const int64_t ngr = k / kGroup;
+  // This block's range of groups (never empty: the host sizes the ranges).
+  const int64_t g_begin = ks * gps;
+  const int64_t g_end = g_begin + gps < ngr ? g_begin + gps : ngr;
   const int64_t row_bytes = k * SB / 8;
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -312,10 +354,10 @@ gemm_kernel(const GemmDesc* __restrict__ table, const int64_t* __restrict__ bsta
   uint32_t ncur[TN], nnxt[TN];
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
-    load_codes<SB>(crow[t], cur[t]);
-    ncur[t] = nrow[t][0];
+    load_codes<SB>(crow[t] + g_begin * 16 * SB, cur[t]);
+    ncur[t] = nrow[t][g_begin];
   }
-  issue_tile(0, xt0);
+  issue_tile(g_begin, xt0);
   wait_vm0();       // own DMA and loads
   __syncthreads();                              // every wave's DMA; the table
 
@@ -327,7 +369,7 @@ gemm_kernel(const GemmDesc* __restrict__ table, const int64_t* __restrict__ bsta
 
   // One group: DMA of the next group's tile into `next`, MFMAs on `tile`.
   auto group = [&](int64_t g, const uint8_t* tile, uint8_t* next) __attribute__((always_inline)) {
-    if (g + 1 < ngr) {
+    if (g + 1 < g_end) {
       issue_tile(g + 1, next);
 #pragma unroll
       for (int t = 0; t < TN; ++t) {
@@ -367,7 +409,7 @@ gemm_kernel(const GemmDesc* __restrict__ table, const int64_t* __restrict__ bsta
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[i][t][j] = __builtin_fmaf(sc, tmp[i][t][j], acc[i][t][j]);
     }
-    if (g + 1 < ngr) {
+    if (g + 1 < g_end) {
 #pragma unroll
       for (int t = 0; t < TN; ++t) {
         cur[t] = nxt[t];
@@ -377,12 +419,14 @@ gemm_kernel(const GemmDesc* __restrict__ table, const int64_t* __restrict__ bsta
     wait_vm0();       // next tile and codes
     __syncthreads();  // next tile complete in every wave; this tile no longer read
   };
-  for (int64_t g = 0; g < ngr; g += 2) {
+  for (int64_t g = g_begin; g < g_end; g += 2) {
     group(g, xt0, xt1);
-    if (g + 1 < ngr) group(g + 1, xt1, xt0);
+    if (g + 1 < g_end) group(g + 1, xt1, xt0);
   }
 
   // D layout of a 32x32 tile: lane holds column c32, rows 8 (j / 4) + 4 h + j % 4.
+  // A split matrix writes its range's partial sums; the reduction adds them.
+  float* const out = part ? part + ks * batch * n_out : y;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -391,9 +435,26 @@ gemm_kernel(const GemmDesc* __restrict__ table, const int64_t* __restrict__ bsta
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int64_t m = mt * BM + 32 * i + 8 * (j / 4) + 4 * h + (j % 4);
-        if (m < batch) y[m * n_out + col[t]] = acc[i][t][j];
+        if (m < batch) out[m * n_out + col[t]] = acc[i][t][j];
       }
     }
+}
+
+// y[m][c] = sum over ranges r = 0 .. ksplit - 1 of part[r][m][c], in order;
+// one thread per output of the matrices that were split.
+__global__ void __launch_bounds__(kBlock)
+gemm_reduce_kernel(const GemmDesc* __restrict__ table, const int64_t* __restrict__ ostart, int n,
+                   int64_t batch) {
+  const int64_t o = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  if (o >= ostart[n]) return;
+  const int d = find_lane(ostart, n, o);
+  const GemmDesc& m = table[d];
+  if (!m.part) return;
+  const int64_t local = o - ostart[d];  // m * n_out + c
+  const int64_t step = batch * m.n_out;
+  float s = m.part[local];
+  for (int64_t r = 1; r < m.ksplit; ++r) s += m.part[r * step + local];
+  m.y[local] = s;
 }
 
 template <int SB>
@@ -417,9 +478,24 @@ int gemm_block_cols() { return kg::BN; }
 hipError_t launch_split_rotate(const GemmDesc* table, const int64_t* ustart, int n, int64_t units,
                                int64_t batch, uint16_t* ws, hipStream_t stream) {
   if (units <= 0) return hipSuccess;
-  const int64_t blocks = (units + kg::kBlock - 1) / kg::kBlock;
-  hipLaunchKernelGGL(kg::split_rotate_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kg::kBlock), 0,
-                     stream, table, ustart, n, batch, ws);
+  if (units < kFewUnits) {  // a wave per unit
+    const int64_t blocks = (units + kg::kWaves - 1) / kg::kWaves;
+    hipLaunchKernelGGL(kg::split_rotate_wave_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kg::kBlock), 0,
+                       stream, table, ustart, n, batch, ws);
+  } else {  // a thread per unit
+    const int64_t blocks = (units + kg::kBlock - 1) / kg::kBlock;
+    hipLaunchKernelGGL(kg::split_rotate_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kg::kBlock), 0,
+                       stream, table, ustart, n, batch, ws);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_reduce(const GemmDesc* table, const int64_t* ostart, int n, int64_t outputs,
+                              int64_t batch, hipStream_t stream) {
+  if (outputs <= 0) return hipSuccess;
+  const int64_t blocks = (outputs + kg::kBlock - 1) / kg::kBlock;
+  hipLaunchKernelGGL(kg::gemm_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kg::kBlock), 0, stream,
+                     table, ostart, n, batch);
   return hipGetLastError();
 }
 

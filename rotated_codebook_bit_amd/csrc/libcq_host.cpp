@@ -530,8 +530,6 @@ int cq_dequant_gemm_many(int n, const cq_matvec_desc* descs, int bits, int group
   const int64_t bm = cq::gemm_block_rows(batch), bn = cq::gemm_block_cols();
   const int64_t mpad = ceil_div(batch, bm) * bm;
   std::vector<cq::GemmDesc> act;
-  std::vector<int64_t> ustart{0}, bstart{0};
-  int64_t xs = 0;  // bf16 values
   for (int i = 0; i < n; ++i) {
     const cq_matvec_desc& d = descs[i];
     if (d.n_out == 0) continue;
@@ -539,30 +537,56 @@ int cq_dequant_gemm_many(int n, const cq_matvec_desc* descs, int bits, int group
       if ((rc = hip_status(cq::launch_zero(d.y, batch * d.n_out, s), "zero launch"))) return rc;
       continue;
     }
-    act.push_back(cq::GemmDesc{d.packed, d.norms, d.x, d.y, d.n_out, d.k, mpad, xs});
-    xs += (d.k / group_size) * mpad * 2 * group_size;
-    ustart.push_back(ustart.back() + (d.k / group_size) * mpad);
-    bstart.push_back(bstart.back() + (mpad / bm) * ceil_div(d.n_out, bn));
+    act.push_back(cq::GemmDesc{d.packed, d.norms, d.x, d.y, d.n_out, d.k, mpad, 0, nullptr, 1, 0});
   }
   if (act.empty()) return CQ_OK;
   const int na = static_cast<int>(act.size());
+  // When the call's output tiles would not give every CU two blocks, each
+  // tile's 128-groups are split into `split` ranges (one block each) whose
+  // partial sums a reduction launch adds in range order.
+  int64_t tiles = 0;
+  for (const cq::GemmDesc& g : act) tiles += (mpad / bm) * ceil_div(g.n_out, bn);
+  const int64_t target = 2 * static_cast<int64_t>(cq::device_cu_count());
+  const int64_t split = tiles >= target ? 1 : ceil_div(target, tiles);
+  std::vector<int64_t> ustart{0}, bstart{0}, ostart{0}, part_off;
+  int64_t xs = 0, parts = 0;  // bf16 values; partial-sum floats
+  for (cq::GemmDesc& g : act) {
+    const int64_t ngr = g.k / group_size;
+    g.xs_off = xs;
+    g.gps = ceil_div(ngr, split);
+    g.ksplit = ceil_div(ngr, g.gps);  // every range non-empty
+    xs += ngr * mpad * 2 * group_size;
+    ustart.push_back(ustart.back() + ngr * mpad);
+    bstart.push_back(bstart.back() + (mpad / bm) * ceil_div(g.n_out, bn) * g.ksplit);
+    ostart.push_back(ostart.back() + batch * g.n_out);
+    part_off.push_back(parts);
+    if (split > 1) parts += g.ksplit * batch * g.n_out;
+  }
   auto up = [](size_t v) { return (v + 255) & ~size_t(255); };
   const size_t tb = up(na * sizeof(cq::GemmDesc)), sb_ = up((na + 1) * 8);
-  const size_t ws_bytes = tb + 2 * sb_ + static_cast<size_t>(xs) * 2;
+  const size_t xb = up(static_cast<size_t>(xs) * 2);
+  const size_t ws_bytes = tb + 3 * sb_ + xb + static_cast<size_t>(parts) * 4;
   uint8_t* ws = nullptr;
   if ((rc = hip_status(hipMallocAsync(reinterpret_cast<void**>(&ws), ws_bytes, s), "workspace alloc")))
     return rc;
   auto* table = reinterpret_cast<cq::GemmDesc*>(ws);
   auto* u_dev = reinterpret_cast<int64_t*>(ws + tb);
   auto* b_dev = reinterpret_cast<int64_t*>(ws + tb + sb_);
-  auto* xs_dev = reinterpret_cast<uint16_t*>(ws + tb + 2 * sb_);
+  auto* o_dev = reinterpret_cast<int64_t*>(ws + tb + 2 * sb_);
+  auto* xs_dev = reinterpret_cast<uint16_t*>(ws + tb + 3 * sb_);
+  auto* part_dev = reinterpret_cast<float*>(ws + tb + 3 * sb_ + xb);
+  if (split > 1)
+    for (int i = 0; i < na; ++i) act[i].part = part_dev + part_off[i];
   rc = hip_status(cq::upload(act.data(), na * sizeof(cq::GemmDesc), table, s), "table upload");
   if (!rc) rc = hip_status(cq::upload(ustart.data(), (na + 1) * 8, u_dev, s), "table upload");
   if (!rc) rc = hip_status(cq::upload(bstart.data(), (na + 1) * 8, b_dev, s), "table upload");
+  if (!rc && split > 1) rc = hip_status(cq::upload(ostart.data(), (na + 1) * 8, o_dev, s), "table upload");
   if (!rc)
     rc = hip_status(cq::launch_split_rotate(table, u_dev, na, ustart[na], batch, xs_dev, s), "rotate launch");
   if (!rc)
     rc = hip_status(cq::launch_gemm(table, b_dev, na, bstart[na], sb, sl, xs_dev, batch, s), "gemm launch");
+  if (!rc && split > 1)
+    rc = hip_status(cq::launch_gemm_reduce(table, o_dev, na, ostart[na], batch, s), "reduce launch");
   const int rc2 = hip_status(hipFreeAsync(ws, s), "workspace free");
   return rc ? rc : rc2;
 }

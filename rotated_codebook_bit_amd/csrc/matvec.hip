@@ -61,12 +61,50 @@ __device__ __forceinline__ int find_desc(const int64_t* __restrict__ start, int 
 }
 
 // xr[m][b][g][:] = H x[m][b][g][:] for every 128-value group of every
-// matrix's activations; one wave per group.  Lane l holds values 2l and
+// matrix's activations; one thread per group.
+__global__ void __launch_bounds__(kBlock)
+rotate_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restrict__ gstart, int n,
+              float* __restrict__ xr) {
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  if (g >= gstart[n]) return;
+  const int d = find_desc(gstart, n, g);
+  const MatvecDesc& m = table[d];
+  const int64_t local = g - gstart[d];  // group within the matrix's batch*k/128
+  const float* src = m.x + local * kGroup;
+  float* dst = xr + m.xr_offset + local * kGroup;
+  float y[kGroup];
+#pragma unroll
+  for (int i = 0; i < kGroup / 4; ++i) {
+    const float4 v = reinterpret_cast<const float4*>(src)[i];
+    y[4 * i] = v.x;
+    y[4 * i + 1] = v.y;
+    y[4 * i + 2] = v.z;
+    y[4 * i + 3] = v.w;
+  }
+#pragma unroll
+  for (int h = 1; h < kGroup; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < kGroup; i += 2 * h) {
+#pragma unroll
+      for (int j = i; j < i + h; ++j) {
+        const float a = y[j], b = y[j + h];
+        y[j] = a + b;
+        y[j + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kGroup / 4; ++i)
+    reinterpret_cast<float4*>(dst)[i] = make_float4(y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]);
+}
+
+// The same, one wave per group, for calls with few groups (the thread
+// version then leaves most of the chip idle).  Lane l holds values 2l and
 // 2l + 1: butterfly stage 1 runs inside the lane, stages 2..7 between lane l
 // and lane l ^ h (the lane with the bit clear keeps the sum), the same
 // operations in the same order as the sequential butterfly.
 __global__ void __launch_bounds__(kBlock)
-rotate_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restrict__ gstart, int n,
+rotate_wave_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restrict__ gstart, int n,
               float* __restrict__ xr) {
   const int lane = threadIdx.x % kWave;
   const int64_t g = static_cast<int64_t>(blockIdx.x) * kWaves + threadIdx.x / kWave;
@@ -516,9 +554,15 @@ MatvecPlan matvec_plan(int sbits, int nb, const MatvecDesc* descs, int n) {
 hipError_t launch_rotate(const MatvecDesc* table, const int64_t* gstart, int n, int64_t total_groups,
                          float* xr, hipStream_t stream) {
   if (total_groups <= 0) return hipSuccess;
-  const int64_t blocks = (total_groups + km::kWaves - 1) / km::kWaves;  // a wave per group
-  hipLaunchKernelGGL(km::rotate_kernel, dim3(static_cast<unsigned>(blocks)), dim3(km::kBlock), 0,
-                     stream, table, gstart, n, xr);
+  if (total_groups < kFewUnits) {  // a wave per group
+    const int64_t blocks = (total_groups + km::kWaves - 1) / km::kWaves;
+    hipLaunchKernelGGL(km::rotate_wave_kernel, dim3(static_cast<unsigned>(blocks)), dim3(km::kBlock), 0,
+                       stream, table, gstart, n, xr);
+  } else {  // a thread per group
+    const int64_t blocks = (total_groups + km::kBlock - 1) / km::kBlock;
+    hipLaunchKernelGGL(km::rotate_kernel, dim3(static_cast<unsigned>(blocks)), dim3(km::kBlock), 0,
+                       stream, table, gstart, n, xr);
+  }
   return hipGetLastError();
 }
 

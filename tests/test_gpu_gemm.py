@@ -154,3 +154,20 @@ def test_gemm_and_matvec_edges(batch, n_out, k, levels):
     say(f"edges gemm+matvec {n_out}x{k} batch={batch}")
     check_matvec(host(cq.dequant_gemm(p, n, n_out, k, 2, lv, xd)), y_ref, x, w_hat, tol=GEMM_TOL)
     check_matvec(host(cq.dequant_matvec(p, n, n_out, k, 2, lv, xd)), y_ref, x, w_hat, tol=MV_TOL)
+
+
+def test_gemm_and_matvec_many_groups(levels):
+    """k = 16384 at batch 256: 32,768 (group, row) units, where both products
+    rotate the activations with one thread per unit instead of one wave."""
+    lv = levels[2]
+    rng = np.random.default_rng(61)
+    n_out, k, batch = 64, 16384, 256
+    q = O.quantize(rng.standard_normal((n_out, k)) * 0.02, 2, lv)
+    w_hat = O.dequantize(q.packed, q.norm16, n_out, k, 2, lv)
+    x = rng.standard_normal((batch, k)).astype(np.float32)
+    y_ref = x.astype(np.float64) @ w_hat.T
+    p, n = dev_q(q, n_out)
+    xd = torch.from_numpy(x).to(DEV)
+    say(f"gemm+matvec {n_out}x{k} batch={batch} (thread-per-unit rotation)")
+    check_matvec(host(cq.dequant_gemm(p, n, n_out, k, 2, lv, xd)), y_ref, x, w_hat, tol=GEMM_TOL)
+    check_matvec(host(cq.dequant_matvec(p, n, n_out, k, 2, lv, xd)), y_ref, x, w_hat, tol=MV_TOL)
