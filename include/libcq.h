@@ -43,11 +43,12 @@
  *     in N(0,1) units (before the 1/sqrt(G) scaling), strictly ascending.
  *     n_levels must be 3 for CQ_TERNARY and CQ_TERNARY_TRITS, 2^bits
  *     otherwise.
- *   - group_size: cq_quantize, cq_dequantize and cq_fake_quant take 32, 64,
- *     128 or 256 ("Cactus Quants CQ2-bit Quantization: Extreme Compression
- *     for Edge LLMs", FAQ on group size);
- *     the other device calls take 128; host-only calls take any power of
- *     two from 8 to 4096 (so a group's packed indices fill whole bytes).
+ *   - group_size: cq_quantize, cq_dequantize, cq_fake_quant,
+ *     cq_quantize_many and cq_dequantize_many take 32, 64, 128 or 256
+ *     ("Cactus Quants CQ2-bit Quantization: Extreme Compression for Edge
+ *     LLMs", FAQ on group size); trit storage and the other device calls
+ *     take 128; host-only calls take any power of two from 8 to 4096 (so a
+ *     group's packed indices fill whole bytes).
  *   - Device calls validate every argument first, then enqueue their kernels
  *     on `stream` (a hipStream_t; NULL = the null stream) and return without
  *     waiting.  On a validation error nothing is enqueued.  Asynchronous
@@ -56,7 +57,8 @@
  *   - rows*cols == 0 (or n_out == 0) is a successful no-op; a product with
  *     k == 0 writes zeros to y (an empty sum).
  *   - Alignment: w, out, packed, x, y must be 16-byte aligned; norms 2-byte;
- *     packed in trit storage (CQ_TERNARY_TRITS) 2-byte.
+ *     packed at group sizes other than 128 4-byte, in trit storage
+ *     (CQ_TERNARY_TRITS) 2-byte.
  *   - Inputs and outputs must not overlap (cq_fake_quant allows out == w).
  *     Non-finite inputs give unspecified but deterministic results.
  *   - Return value: CQ_OK (0) or a negative cq_status.  cq_last_error()
@@ -160,8 +162,9 @@ int cq_dequantize(const uint8_t* packed, const uint16_t* norms, int64_t rows,
  * tensor i's packed indices to packed_offsets[i] and of its norms to
  * norm_offsets[i] (host arrays of n_tensors entries, each may be NULL) and
  * the blob size to *total_bytes (may be NULL), which equals cq_model_bytes.
- * With group_size 128 every offset is a multiple of 16 (packed bit fields;
- * 2 for trit storage) or 2 (norms), so a 16-byte aligned blob can take
+ * Every packed offset meets the call's packed alignment (a multiple of 16
+ * at group size 128, of 4 at the others, of 2 in trit storage) and every
+ * norm offset is even, so a 16-byte aligned blob can take
  * cq_quantize_many's outputs directly.  Host only, pure. */
 int cq_blob_layout(int n_tensors, const int64_t* rows, const int64_t* cols, int bits,
                    int group_size, int64_t* packed_offsets, int64_t* norm_offsets,
@@ -177,18 +180,19 @@ typedef struct {
 } cq_quant_desc;
 
 /* cq_quantize over n tensors (descs: host array) sharing w_dtype, bits and
- * levels, e.g. every weight of a model, in one call: one launch for all the
- * tensors whose cols is a multiple of G plus one for the others, instead of
- * one launch per tensor (a parameter tree quantized as in "Cactus Quants
- * CQ2-bit Quantization: Extreme Compression for Edge LLMs", section The
- * CQ2-bit Implementation Pipeline).  Results are identical to cq_quantize on
- * each tensor.  Pointing packed/norms at the offsets of cq_blob_layout writes
+ * levels, e.g. every weight of a model, in one call (a parameter tree
+ * quantized as in "Cactus Quants CQ2-bit Quantization: Extreme Compression
+ * for Edge LLMs", section The CQ2-bit Implementation Pipeline).  At group
+ * size 128: one launch for all the tensors whose cols is a multiple of G
+ * plus one for the others, instead of one launch per tensor; at 32, 64 and
+ * 256, cq_quantize's kernels once per tensor.  Results are identical to
+ * cq_quantize on each tensor.  Pointing packed/norms at the offsets of cq_blob_layout writes
  * the serialized blob in place.  Every descriptor is validated as
  * cq_quantize validates its arguments (the first failing tensor is reported;
  * nothing is enqueued then); no output may overlap another output or any
- * input of the call (CQ_ERR_ARG).  Empty tensors are skipped.  Takes
- * 48 bytes per tensor of stream-ordered device memory for the descriptor
- * table (hipMallocAsync / hipFreeAsync on `stream`). */
+ * input of the call (CQ_ERR_ARG).  Empty tensors are skipped.  At group
+ * size 128 takes 48 bytes per tensor of stream-ordered device memory for
+ * the descriptor table (hipMallocAsync / hipFreeAsync on `stream`). */
 int cq_quantize_many(int n, const cq_quant_desc* descs, int w_dtype, int bits, int group_size,
                      const float* levels, int n_levels, void* stream);
 

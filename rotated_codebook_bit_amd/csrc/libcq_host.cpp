@@ -107,10 +107,15 @@ int64_t group_bytes(int bits, int group_size) {
 // Storage code of the dequantize launchers: field width, or trits.
 int storage_code(int bits) { return bits == CQ_TERNARY_TRITS ? cq::kTritStorage : storage_bits(bits); }
 
-// Alignment the kernels need for packed indices: 16 bytes for bit fields
-// (128-bit accesses), 2 bytes for trit storage (16-bit accesses; a group is
-// 26 bytes, so tensors inside a serialized blob sit at even offsets).
-size_t packed_align(int bits) { return bits == CQ_TERNARY_TRITS ? 2 : 16; }
+// Alignment the kernels need for packed indices: 16 bytes for bit fields at
+// G = 128 (128-bit accesses), 4 bytes at the other group sizes (32-bit
+// accesses; their groups are multiples of 4 bytes, so every offset inside a
+// serialized blob qualifies), 2 bytes for trit storage (16-bit accesses; a
+// group is 26 bytes, so tensors inside a blob sit at even offsets).
+size_t packed_align(int bits, int group_size) {
+  if (bits == CQ_TERNARY_TRITS) return 2;
+  return group_size == cq::kGroup ? 16 : 4;
+}
 
 int reject_trits(int bits) {
   if (bits == CQ_TERNARY_TRITS)
@@ -367,8 +372,8 @@ int cq_quantize(const void* w, int w_dtype, int64_t rows, int64_t cols, int bits
   if ((rc = check_levels(levels, n_levels, L))) return rc;
   if (rows == 0 || cols == 0) return CQ_OK;
   if (!w || !packed || !norms) return fail(CQ_ERR_NULL, "w/packed/norms is NULL");
-  if (!aligned(w, 16) || !aligned(packed, packed_align(bits)) || !aligned(norms, 2))
-    return fail(CQ_ERR_ALIGN, "w needs 16-byte, packed 16-byte (trits: 2-byte), norms 2-byte alignment");
+  if (!aligned(w, 16) || !aligned(packed, packed_align(bits, group_size)) || !aligned(norms, 2))
+    return fail(CQ_ERR_ALIGN, "w needs 16-byte, packed 16-byte (G != 128: 4-byte; trits: 2-byte), norms 2-byte alignment");
   const int64_t ng = rows * ceil_div(cols, group_size);
   const size_t in_bytes = static_cast<size_t>(rows * cols) * (w_dtype == CQ_F32 ? 4 : 2);
   const size_t pk_bytes = static_cast<size_t>(ng * group_bytes(bits, group_size));
@@ -394,7 +399,7 @@ int cq_quantize_many(int n, const cq_quant_desc* descs, int w_dtype, int bits, i
   if ((rc = check_bits(bits, false, &L))) return rc;
   if (w_dtype != CQ_F32 && w_dtype != CQ_BF16) return fail(CQ_ERR_ARG, "unknown w_dtype %d", w_dtype);
   if (n < 0) return fail(CQ_ERR_ARG, "n < 0");
-  if ((rc = check_group(group_size, true))) return rc;
+  if ((rc = check_codec_group(group_size, bits))) return rc;
   if ((rc = check_levels(levels, n_levels, L))) return rc;
   if (n == 0) return CQ_OK;
   if (!descs) return fail(CQ_ERR_NULL, "descs is NULL");
@@ -407,8 +412,8 @@ int cq_quantize_many(int n, const cq_quant_desc* descs, int w_dtype, int bits, i
     if (d.rows < 0 || d.cols < 0) return fail(CQ_ERR_ARG, "tensor %d: negative size", i);
     if (d.rows == 0 || d.cols == 0) continue;
     if (!d.w || !d.packed || !d.norms) return fail(CQ_ERR_NULL, "tensor %d: w/packed/norms is NULL", i);
-    if (!aligned(d.w, 16) || !aligned(d.packed, packed_align(bits)) || !aligned(d.norms, 2))
-      return fail(CQ_ERR_ALIGN, "tensor %d: w needs 16-byte, packed 16-byte (trits: 2-byte), norms 2-byte alignment", i);
+    if (!aligned(d.w, 16) || !aligned(d.packed, packed_align(bits, group_size)) || !aligned(d.norms, 2))
+      return fail(CQ_ERR_ALIGN, "tensor %d: w needs 16-byte, packed 16-byte (G != 128: 4-byte; trits: 2-byte), norms 2-byte alignment", i);
     const int64_t ng = d.rows * ceil_div(d.cols, group_size);
     ins.push_back(span(d.w, static_cast<size_t>(d.rows * d.cols) * esz, i));
     outs.push_back(span(d.packed, static_cast<size_t>(ng * gb), i));
@@ -421,6 +426,17 @@ int cq_quantize_many(int n, const cq_quant_desc* descs, int w_dtype, int bits, i
   if (t.empty()) return CQ_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const cq::QuantParams p = make_quant_params(levels, L);
+  if (group_size != cq::kGroup) {
+    // Other group sizes: the single-tensor kernels, one launch per tensor.
+    for (int i = 0; i < n && !rc; ++i) {
+      const cq_quant_desc& d = descs[i];
+      if (d.rows == 0 || d.cols == 0) continue;
+      rc = hip_status(cq::launch_quantize_g(group_size, d.w, w_dtype == CQ_BF16, d.rows, d.cols, p, d.packed,
+                                            d.norms, s),
+                      "quantize launch");
+    }
+    return rc;
+  }
   rc = t.upload(s);
   if (!rc)
     rc = hip_status(cq::launch_quantize_many(w_dtype == CQ_BF16, bits == CQ_TERNARY_TRITS, p, t.tc, t.bstart.back(), t.tr,
@@ -438,7 +454,7 @@ int cq_dequantize_many(int n, const cq_dequant_desc* descs, int bits, int group_
   if (out_dtype != CQ_F32 && out_dtype != CQ_BF16)
     return fail(CQ_ERR_ARG, "unknown out_dtype %d", out_dtype);
   if (n < 0) return fail(CQ_ERR_ARG, "n < 0");
-  if ((rc = check_group(group_size, true))) return rc;
+  if ((rc = check_codec_group(group_size, bits))) return rc;
   if ((rc = check_levels(levels, n_levels, L))) return rc;
   if (n == 0) return CQ_OK;
   if (!descs) return fail(CQ_ERR_NULL, "descs is NULL");
@@ -451,8 +467,8 @@ int cq_dequantize_many(int n, const cq_dequant_desc* descs, int bits, int group_
     if (d.rows < 0 || d.cols < 0) return fail(CQ_ERR_ARG, "tensor %d: negative size", i);
     if (d.rows == 0 || d.cols == 0) continue;
     if (!d.packed || !d.norms || !d.out) return fail(CQ_ERR_NULL, "tensor %d: packed/norms/out is NULL", i);
-    if (!aligned(d.out, 16) || !aligned(d.packed, packed_align(bits)) || !aligned(d.norms, 2))
-      return fail(CQ_ERR_ALIGN, "tensor %d: out needs 16-byte, packed 16-byte (trits: 2-byte), norms 2-byte alignment", i);
+    if (!aligned(d.out, 16) || !aligned(d.packed, packed_align(bits, group_size)) || !aligned(d.norms, 2))
+      return fail(CQ_ERR_ALIGN, "tensor %d: out needs 16-byte, packed 16-byte (G != 128: 4-byte; trits: 2-byte), norms 2-byte alignment", i);
     const int64_t ng = d.rows * ceil_div(d.cols, group_size);
     ins.push_back(span(d.packed, static_cast<size_t>(ng * gb), i));
     ins.push_back(span(d.norms, static_cast<size_t>(ng) * 2, i));
@@ -465,6 +481,17 @@ int cq_dequantize_many(int n, const cq_dequant_desc* descs, int bits, int group_
   if (t.empty()) return CQ_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const cq::LevelTable lv = make_table(levels, L);
+  if (group_size != cq::kGroup) {
+    // Other group sizes: the single-tensor kernels, one launch per tensor.
+    for (int i = 0; i < n && !rc; ++i) {
+      const cq_dequant_desc& d = descs[i];
+      if (d.rows == 0 || d.cols == 0) continue;
+      rc = hip_status(cq::launch_dequantize_g(group_size, d.packed, d.norms, d.rows, d.cols, storage_bits(bits),
+                                              lv, d.out, out_dtype == CQ_BF16, s),
+                      "dequantize launch");
+    }
+    return rc;
+  }
   rc = t.upload(s);
   if (!rc)
     rc = hip_status(cq::launch_dequantize_many(storage_code(bits), lv, out_dtype == CQ_BF16, t.tc, t.bstart.back(), t.tr,
@@ -693,8 +720,8 @@ int cq_dequantize(const uint8_t* packed, const uint16_t* norms, int64_t rows, in
   if ((rc = check_levels(levels, n_levels, L))) return rc;
   if (rows == 0 || cols == 0) return CQ_OK;
   if (!packed || !norms || !out) return fail(CQ_ERR_NULL, "packed/norms/out is NULL");
-  if (!aligned(out, 16) || !aligned(packed, packed_align(bits)) || !aligned(norms, 2))
-    return fail(CQ_ERR_ALIGN, "out needs 16-byte, packed 16-byte (trits: 2-byte), norms 2-byte alignment");
+  if (!aligned(out, 16) || !aligned(packed, packed_align(bits, group_size)) || !aligned(norms, 2))
+    return fail(CQ_ERR_ALIGN, "out needs 16-byte, packed 16-byte (G != 128: 4-byte; trits: 2-byte), norms 2-byte alignment");
   const int64_t ng = rows * ceil_div(cols, group_size);
   const size_t out_bytes = static_cast<size_t>(rows * cols) * (out_dtype == CQ_F32 ? 4 : 2);
   const size_t pk_bytes = static_cast<size_t>(ng * group_bytes(bits, group_size));

@@ -283,7 +283,10 @@ def test_quantize_many_validation():
     assert qm([good], n=-1) == E_ARG
     assert L.cq_quantize_many(1, None, 1, 2, 128, lp, 4, None) == E_NULL
     assert qm([good], dt=2) == E_ARG
-    assert qm([good], g=64) == E_UNSUP
+    assert qm([good], g=512) == E_UNSUP
+    assert qm([good], g=16) == E_UNSUP
+    assert qm([good], bits=O.TERNARY_TRITS, nl=3, g=64) == E_UNSUP  # trits are laid out for 128
+    assert qm([good, _qdesc(rows=-1)], g=64) == E_ARG                  # G = 64 validates as 128 does
     assert qm([good], nl=8) == E_ARG
     assert qm([good, _qdesc(rows=-1)]) == E_ARG
     assert qm([good, _qdesc(w=0)]) == E_NULL
@@ -309,7 +312,8 @@ def test_dequantize_many_validation():
     good = D(0x100000, 0x900000, 4, 256, 0x1100000)
     assert dm([], n=0) == OK
     assert dm([good], dt=5) == E_ARG
-    assert dm([good], g=256) == E_UNSUP
+    assert dm([good], g=512) == E_UNSUP
+    assert dm([good, D(0, 0x900000, 4, 256, 0x1200000)], g=256) == E_NULL
     assert dm([good, D(0, 0x900000, 4, 256, 0x1200000)]) == E_NULL
     assert dm([good, D(0x100000, 0x900000, 4, 256, 0x1200004)]) == E_ALIGN
     # 4 x 256 f32 = 4 KiB outputs

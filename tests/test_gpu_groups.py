@@ -103,6 +103,40 @@ def test_group_size_special_groups(g, levels):
         assert (n[0] == 0).all() and (n[-1] == 0x7C00).all()
 
 
+@pytest.mark.parametrize("g", [32, 64, 256])
+@pytest.mark.parametrize("bits", [2, 3])
+def test_group_size_many_calls(g, bits, levels):
+    """cq_quantize_many / cq_dequantize_many at other group sizes: the blob at
+    the oracle's serialized offsets (some only 4- or 8-byte aligned),
+    identical to the single-tensor calls, and parity on one tensor."""
+    lv = levels[bits]
+    rng = np.random.default_rng(70 + g + bits)
+    shapes = [(5, 300), (64, 512), (1, 1), (0, 256), (2, 3, 2 * g), (3, 1000)]
+    ws = [torch.from_numpy((rng.standard_normal(s) * 0.02).astype(np.float32)).to(DEV) for s in shapes]
+    say(f"G={g} bits={bits} quantize_many")
+    blob, views = cq.quantize_many(ws, bits, lv, group_size=g)
+    po, no, total = O.blob_offsets(shapes, bits, g)
+    assert blob.numel() == total == O.model_bytes(shapes, bits, g)
+    assert list(cq.blob_layout(shapes, bits, g)[:2]) == [list(po), list(no)]
+    items = []
+    for s, w, (pk, nm) in zip(shapes, ws, views):
+        rows, cols = int(np.prod(s[:-1])), s[-1]
+        if rows * cols == 0:
+            continue
+        p1, n1 = cq.quantize(w, bits, lv, group_size=g)
+        assert torch.equal(p1.reshape(-1), pk.reshape(-1)), s
+        assert torch.equal(n1.view(torch.int16).reshape(-1), nm.view(torch.int16).reshape(-1)), s
+        items.append((pk.reshape(rows, -1), nm, rows, cols))
+    w64 = ws[1].double().cpu().numpy()
+    tally(check_quantize(host(views[1][0]), f16_bits(views[1][1]), O.quantize(w64, bits, lv, g),
+                         enforce_count=False))
+    say(f"G={g} bits={bits} dequantize_many")
+    outs = cq.dequantize_many(items, bits, lv, group_size=g)
+    for (pk, nm, rows, cols), out in zip(items, outs):
+        o1 = cq.dequantize(pk, nm, rows, cols, bits, lv, group_size=g)
+        assert torch.equal(o1, out)
+
+
 def test_zz_mismatch_total():
     say(f"group sizes: {TALLY['mismatches']} in-band mismatches in {TALLY['elements']} elements")
     check_count(TALLY["mismatches"], TALLY["elements"])
