@@ -44,11 +44,12 @@
  *     n_levels must be 3 for CQ_TERNARY and CQ_TERNARY_TRITS, 2^bits
  *     otherwise.
  *   - group_size: cq_quantize, cq_dequantize, cq_fake_quant,
- *     cq_quantize_many and cq_dequantize_many take 32, 64, 128 or 256
- *     ("Cactus Quants CQ2-bit Quantization: Extreme Compression for Edge
- *     LLMs", FAQ on group size); trit storage and the other device calls
- *     take 128; host-only calls take any power of two from 8 to 4096 (so a
- *     group's packed indices fill whole bytes).
+ *     cq_quantize_many, cq_dequantize_many, cq_dequant_matvec and
+ *     cq_dequant_matvec_many take 32, 64, 128 or 256 ("Cactus Quants
+ *     CQ2-bit Quantization: Extreme Compression for Edge LLMs", FAQ on group
+ *     size); trit storage, the GEMM calls and cq_repack take 128; host-only
+ *     calls take any power of two from 8 to 4096 (so a group's packed
+ *     indices fill whole bytes).
  *   - Device calls validate every argument first, then enqueue their kernels
  *     on `stream` (a hipStream_t; NULL = the null stream) and return without
  *     waiting.  On a validation error nothing is enqueued.  Asynchronous

@@ -265,11 +265,11 @@ MatvecPlan matvec_plan(int sbits, int nb, const MatvecDesc* descs, int n);
 constexpr int64_t kFewUnits = 32768;
 
 hipError_t launch_rotate(const MatvecDesc* table, const int64_t* gstart, int n, int64_t total_groups,
-                         float* xr, hipStream_t stream);
+                         int group_size, float* xr, hipStream_t stream);
 
 hipError_t launch_matvec(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks,
                          int sbits, const LevelTable& lv, const float* xr, int64_t b0, int nb,
-                         const MatvecPlan& plan, hipStream_t stream);
+                         const MatvecPlan& plan, int group_size, hipStream_t stream);
 
 hipError_t launch_zero(float* y, int64_t count, hipStream_t stream);
 

@@ -752,7 +752,7 @@ int cq_dequant_matvec_many(int n, const cq_matvec_desc* descs, int bits, int gro
   if ((rc = reject_trits(bits))) return rc;
   if (n < 0) return fail(CQ_ERR_ARG, "n < 0");
   if (batch < 1) return fail(CQ_ERR_ARG, "batch must be >= 1");
-  if ((rc = check_group(group_size, true))) return rc;
+  if ((rc = check_codec_group(group_size, bits))) return rc;
   if ((rc = check_levels(levels, n_levels, L))) return rc;
   if (n == 0) return CQ_OK;
   if (!descs) return fail(CQ_ERR_NULL, "descs is NULL");
@@ -833,12 +833,12 @@ int cq_dequant_matvec_many(int n, const cq_matvec_desc* descs, int bits, int gro
     }
     rc = hip_status(cq::launch_table_init(c, table, g_dev, b0_dev, b1_dev, s), "table launch");
   }
-  if (!rc) rc = hip_status(cq::launch_rotate(table, g_dev, na, gstart[na], xr, s), "rotate launch");
+  if (!rc) rc = hip_status(cq::launch_rotate(table, g_dev, na, gstart[na], group_size, xr, s), "rotate launch");
   for (int64_t b0 = 0; b0 < batch && !rc; b0 += 8) {
     const int nb = static_cast<int>(batch - b0 < 8 ? batch - b0 : 8);
     const bool full = nb == nb_full;
     rc = hip_status(cq::launch_matvec(table, full ? b0_dev : b1_dev, na, full ? bstart0[na] : bstart1[na],
-                                      sb, lv, xr, b0, nb, full ? plan0 : plan1, s),
+                                      sb, lv, xr, b0, nb, full ? plan0 : plan1, group_size, s),
                     "matvec launch");
   }
   const int rc2 = hip_status(hipFreeAsync(ws, s), "workspace free");

@@ -60,8 +60,9 @@ __device__ __forceinline__ int find_desc(const int64_t* __restrict__ start, int 
   return lo;
 }
 
-// xr[m][b][g][:] = H x[m][b][g][:] for every 128-value group of every
+// xr[m][b][g][:] = H x[m][b][g][:] for every G-value group of every
 // matrix's activations; one thread per group.
+template <int G>
 __global__ void __launch_bounds__(kBlock)
 rotate_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restrict__ gstart, int n,
               float* __restrict__ xr) {
@@ -69,12 +70,12 @@ rotate_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restrict__ 
   if (g >= gstart[n]) return;
   const int d = find_desc(gstart, n, g);
   const MatvecDesc& m = table[d];
-  const int64_t local = g - gstart[d];  // group within the matrix's batch*k/128
-  const float* src = m.x + local * kGroup;
-  float* dst = xr + m.xr_offset + local * kGroup;
-  float y[kGroup];
+  const int64_t local = g - gstart[d];  // group within the matrix's batch*k/G
+  const float* src = m.x + local * G;
+  float* dst = xr + m.xr_offset + local * G;
+  float y[G];
 #pragma unroll
-  for (int i = 0; i < kGroup / 4; ++i) {
+  for (int i = 0; i < G / 4; ++i) {
     const float4 v = reinterpret_cast<const float4*>(src)[i];
     y[4 * i] = v.x;
     y[4 * i + 1] = v.y;
@@ -82,9 +83,9 @@ rotate_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restrict__ 
     y[4 * i + 3] = v.w;
   }
 #pragma unroll
-  for (int h = 1; h < kGroup; h <<= 1) {
+  for (int h = 1; h < G; h <<= 1) {
 #pragma unroll
-    for (int i = 0; i < kGroup; i += 2 * h) {
+    for (int i = 0; i < G; i += 2 * h) {
 #pragma unroll
       for (int j = i; j < i + h; ++j) {
         const float a = y[j], b = y[j + h];
@@ -94,12 +95,12 @@ rotate_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restrict__ 
     }
   }
 #pragma unroll
-  for (int i = 0; i < kGroup / 4; ++i)
+  for (int i = 0; i < G / 4; ++i)
     reinterpret_cast<float4*>(dst)[i] = make_float4(y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]);
 }
 
-// The same, one wave per group, for calls with few groups (the thread
-// version then leaves most of the chip idle).  Lane l holds values 2l and
+// The same for G = 128, one wave per group, for calls with few groups (the
+// thread version then leaves most of the chip idle).  Lane l holds values 2l and
 // 2l + 1: butterfly stage 1 runs inside the lane, stages 2..7 between lane l
 // and lane l ^ h (the lane with the bit clear keeps the sum), the same
 // operations in the same order as the sequential butterfly.
@@ -210,7 +211,7 @@ constexpr int table_copies(int nb) { return nb >= 4 ? 8 : 1; }
 template <int SB, int NB, int RB>
 __global__ void __launch_bounds__(kBlock)
 matvec_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restrict__ bstart, int n,
-              LevelTable lv, const float* __restrict__ xr, int64_t b0) {
+              LevelTable lv, const float* __restrict__ xr, int64_t b0, int log2g) {
   using Lv = Levels<SB, table_copies(NB)>;
   __shared__ __attribute__((aligned(16))) float tab[Lv::floats];
   __shared__ float red[RB * NB][kBlock + 1];
@@ -227,7 +228,8 @@ matvec_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restrict__ 
     const int64_t n_out = m.n_out, k = m.k;
     const int64_t row0 = (blk - bstart[d]) * RB;
     const int64_t row_bytes = k * SB / 8;
-    const int64_t ngr = k / kGroup;
+    const int64_t ngr = k >> log2g;
+    const float inv_g = 1.0f / static_cast<float>(1 << log2g);  // exact: a power of two
     const float* x_rot = xr + m.xr_offset;
 
     float acc[RB][NB];
@@ -261,7 +263,7 @@ matvec_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restrict__ 
         for (int r = 0; r < RB; ++r) {
           const int64_t row = row0 + r < n_out ? row0 + r : n_out - 1;
           codes[r] = load_codes16<SB>(m.packed + row * row_bytes, c0);
-          scale[r] = half_to_float(m.norms[row * ngr + c0 / kGroup]) * (1.0f / kGroup);
+          scale[r] = half_to_float(m.norms[row * ngr + (c0 >> log2g)]) * inv_g;
         }
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
@@ -343,7 +345,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t pair_rsrc(const void* base, in
 template <int W, int RPW>
 __global__ void __launch_bounds__(W * kWave)
 matvec_pair_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restrict__ bstart, int n,
-                   LevelTable lv, const float* __restrict__ xr, int64_t b0) {
+                   LevelTable lv, const float* __restrict__ xr, int64_t b0, int log2g) {
   __shared__ __attribute__((aligned(16))) float tab[8 * 16 * kWave];
   const int lane = threadIdx.x % kWave;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -352,7 +354,7 @@ matvec_pair_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restri
   const MatvecDesc* md = table + d;
   const int64_t n_out = load_const(&md->n_out), k = load_const(&md->k);
   const int64_t row0 = (blk - load_const(bstart + d)) * (W * RPW) + w * RPW;
-  const int64_t row_bytes = k / 4, ngr = k / kGroup;
+  const int64_t row_bytes = k / 4, ngr = k >> log2g;
   const float* x_rot = xr + load_const(&md->xr_offset) + b0 * k;
   // The wave's rows as buffer resources: rows past the end of the matrix lie
   // outside them and read as zero (their sums are never stored).  The host
@@ -399,7 +401,7 @@ matvec_pair_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restri
       t.x[h] = active && builds ? *reinterpret_cast<const float2*>(x_rot + c0 + 2 * (PPT * w + h))
                                 : make_float2(0.0f, 0.0f);
     const int coff = active ? static_cast<int>(c0 / 4) : (1 << 30);
-    const int noff = active ? static_cast<int>(2 * (c0 / kGroup)) : (1 << 30);
+    const int noff = active ? static_cast<int>(2 * (c0 >> log2g)) : (1 << 30);
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       t.codes[r] = __builtin_amdgcn_raw_buffer_load_b32(codes_src, coff, soff_c[r], 0);
@@ -473,7 +475,7 @@ matvec_pair_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restri
   float s = acc[0];
 #pragma unroll
   for (int o = 32 >> kSteps; o >= 1; o >>= 1) s += __shfl_xor(s, o, kWave);
-  s *= 1.0f / kGroup;
+  s *= 1.0f / static_cast<float>(1 << log2g);  // exact: a power of two
   int r = 0;
 #pragma unroll
   for (int i = 0; i < kSteps; ++i) r += ((lane >> (5 - i)) & 1) * (RPW >> (i + 1));
@@ -513,29 +515,39 @@ constexpr bool use_pairs(int sb, int nb, int64_t max_k) { return sb == 2 && nb =
 
 template <int SB, int NB>
 hipError_t launch_nb(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks,
-                     const LevelTable& lv, const float* xr, int64_t b0, hipStream_t s) {
+                     const LevelTable& lv, const float* xr, int64_t b0, int log2g, hipStream_t s) {
   constexpr int RB = rows_per_block(NB);
   // One block per row block: the blocks are short, and letting the hardware
   // refill free slots measured faster than a resident grid that loops.
   hipLaunchKernelGGL((matvec_kernel<SB, NB, RB>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
-                     s, table, bstart, n, lv, xr, b0);
+                     s, table, bstart, n, lv, xr, b0, log2g);
   return hipGetLastError();
 }
 
 template <int SB>
 hipError_t launch_sb(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks,
-                     const LevelTable& lv, const float* xr, int64_t b0, int nb, hipStream_t s) {
+                     const LevelTable& lv, const float* xr, int64_t b0, int nb, int log2g, hipStream_t s) {
   switch (nb) {
-    case 1: return launch_nb<SB, 1>(table, bstart, n, blocks, lv, xr, b0, s);
-    case 2: return launch_nb<SB, 2>(table, bstart, n, blocks, lv, xr, b0, s);
-    case 3: return launch_nb<SB, 3>(table, bstart, n, blocks, lv, xr, b0, s);
-    case 4: return launch_nb<SB, 4>(table, bstart, n, blocks, lv, xr, b0, s);
-    case 5: return launch_nb<SB, 5>(table, bstart, n, blocks, lv, xr, b0, s);
-    case 6: return launch_nb<SB, 6>(table, bstart, n, blocks, lv, xr, b0, s);
-    case 7: return launch_nb<SB, 7>(table, bstart, n, blocks, lv, xr, b0, s);
-    default: return launch_nb<SB, 8>(table, bstart, n, blocks, lv, xr, b0, s);
+    case 1: return launch_nb<SB, 1>(table, bstart, n, blocks, lv, xr, b0, log2g, s);
+    case 2: return launch_nb<SB, 2>(table, bstart, n, blocks, lv, xr, b0, log2g, s);
+    case 3: return launch_nb<SB, 3>(table, bstart, n, blocks, lv, xr, b0, log2g, s);
+    case 4: return launch_nb<SB, 4>(table, bstart, n, blocks, lv, xr, b0, log2g, s);
+    case 5: return launch_nb<SB, 5>(table, bstart, n, blocks, lv, xr, b0, log2g, s);
+    case 6: return launch_nb<SB, 6>(table, bstart, n, blocks, lv, xr, b0, log2g, s);
+    case 7: return launch_nb<SB, 7>(table, bstart, n, blocks, lv, xr, b0, log2g, s);
+    default: return launch_nb<SB, 8>(table, bstart, n, blocks, lv, xr, b0, log2g, s);
   }
 }
+
+template <int G>
+void launch_rotate_threads(const MatvecDesc* table, const int64_t* gstart, int n, int64_t total_groups,
+                           float* xr, hipStream_t stream) {
+  const int64_t blocks = (total_groups + kBlock - 1) / kBlock;
+  hipLaunchKernelGGL(rotate_kernel<G>, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, stream, table,
+                     gstart, n, xr);
+}
+
+constexpr int log2_group(int g) { return g == 32 ? 5 : g == 64 ? 6 : g == 256 ? 8 : 7; }
 
 }  // namespace km
 
@@ -552,41 +564,47 @@ MatvecPlan matvec_plan(int sbits, int nb, const MatvecDesc* descs, int n) {
 }
 
 hipError_t launch_rotate(const MatvecDesc* table, const int64_t* gstart, int n, int64_t total_groups,
-                         float* xr, hipStream_t stream) {
+                         int group_size, float* xr, hipStream_t stream) {
   if (total_groups <= 0) return hipSuccess;
-  if (total_groups < kFewUnits) {  // a wave per group
+  if (group_size == kGroup && total_groups < kFewUnits) {  // a wave per group
     const int64_t blocks = (total_groups + km::kWaves - 1) / km::kWaves;
     hipLaunchKernelGGL(km::rotate_wave_kernel, dim3(static_cast<unsigned>(blocks)), dim3(km::kBlock), 0,
                        stream, table, gstart, n, xr);
-  } else {  // a thread per group
-    const int64_t blocks = (total_groups + km::kBlock - 1) / km::kBlock;
-    hipLaunchKernelGGL(km::rotate_kernel, dim3(static_cast<unsigned>(blocks)), dim3(km::kBlock), 0,
-                       stream, table, gstart, n, xr);
+    return hipGetLastError();
+  }
+  switch (group_size) {  // a thread per group
+    case 32: km::launch_rotate_threads<32>(table, gstart, n, total_groups, xr, stream); break;
+    case 64: km::launch_rotate_threads<64>(table, gstart, n, total_groups, xr, stream); break;
+    case 128: km::launch_rotate_threads<128>(table, gstart, n, total_groups, xr, stream); break;
+    case 256: km::launch_rotate_threads<256>(table, gstart, n, total_groups, xr, stream); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_matvec(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks,
                          int sbits, const LevelTable& lv, const float* xr, int64_t b0, int nb,
-                         const MatvecPlan& plan, hipStream_t stream) {
+                         const MatvecPlan& plan, int group_size, hipStream_t stream) {
   if (blocks <= 0) return hipSuccess;
+  const int log2g = km::log2_group(group_size);
+  if ((1 << log2g) != group_size) return hipErrorInvalidValue;
   if (plan.pair_rows_per_wave == km::kPairRowsPerWave) {
     hipLaunchKernelGGL((km::matvec_pair_kernel<km::kPairWaves, km::kPairRowsPerWave>),
                        dim3(static_cast<unsigned>(blocks)), dim3(km::kPairWaves * kWave), 0, stream, table, bstart,
-                       n, lv, xr, b0);
+                       n, lv, xr, b0, log2g);
     return hipGetLastError();
   }
   if (plan.pair_rows_per_wave == km::kPairRowsPerWaveFew) {
     hipLaunchKernelGGL((km::matvec_pair_kernel<km::kPairWaves, km::kPairRowsPerWaveFew>),
                        dim3(static_cast<unsigned>(blocks)), dim3(km::kPairWaves * kWave), 0, stream, table, bstart,
-                       n, lv, xr, b0);
+                       n, lv, xr, b0, log2g);
     return hipGetLastError();
   }
   if (plan.pair_rows_per_wave != 0 || plan.rows_per_block != km::rows_per_block(nb)) return hipErrorInvalidValue;
   switch (sbits) {
-    case 2: return km::launch_sb<2>(table, bstart, n, blocks, lv, xr, b0, nb, stream);
-    case 3: return km::launch_sb<3>(table, bstart, n, blocks, lv, xr, b0, nb, stream);
-    case 4: return km::launch_sb<4>(table, bstart, n, blocks, lv, xr, b0, nb, stream);
+    case 2: return km::launch_sb<2>(table, bstart, n, blocks, lv, xr, b0, nb, log2g, stream);
+    case 3: return km::launch_sb<3>(table, bstart, n, blocks, lv, xr, b0, nb, log2g, stream);
+    case 4: return km::launch_sb<4>(table, bstart, n, blocks, lv, xr, b0, nb, log2g, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -155,6 +155,9 @@ def test_matvec_validation():
         return L.cq_dequant_matvec(packed, norms, n_out, k, bits, g, lp, nl, x, batch, y, None)
 
     assert mv(k=200) == E_UNSUP
+    assert mv(g=512) == E_UNSUP
+    assert mv(g=64, k=96) == E_UNSUP                                 # k % G != 0
+    assert mv(g=32, batch=0) == E_ARG                                # G = 32 validates as 128 does
     assert mv(batch=0) == E_ARG
     assert mv(bits=158, nl=4) == E_ARG
     assert mv(x=None) == E_NULL
@@ -404,9 +407,11 @@ def test_group_size_support():
     assert quant(g=16) == E_UNSUP
     assert quant(g=1024) == E_UNSUP
     assert L.cq_quantize(FAKE, 0, 4, 256, O.TERNARY_TRITS, 64, lp3, 3, FAKE2, FAKE3, None) == E_UNSUP
-    # product, multi-tensor and repack calls: 128 only
-    assert L.cq_dequant_matvec(FAKE, FAKE2, 8, 256, 2, 64, lp, 4, ctypes.c_void_p(0x2100000), 1,
+    # the matvec takes the codec sizes too; the GEMM and repack take 128 only
+    assert L.cq_dequant_matvec(FAKE, FAKE2, 8, 256, 2, 512, lp, 4, ctypes.c_void_p(0x2100000), 1,
                                ctypes.c_void_p(0x3100000), None) == E_UNSUP
+    assert L.cq_dequant_gemm(FAKE, FAKE2, 8, 256, 2, 64, lp, 4, ctypes.c_void_p(0x2100000), 16,
+                             ctypes.c_void_p(0x3100000), None) == E_UNSUP
     assert L.cq_repack(FAKE, O.TERNARY, FAKE2, O.TERNARY_TRITS, 4, 256, None) == E_UNSUP
     # sizes for other group sizes
     assert cq.layout(3, 200, 2, 64) == (12, 12 * 16)

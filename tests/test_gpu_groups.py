@@ -140,3 +140,24 @@ def test_group_size_many_calls(g, bits, levels):
 def test_zz_mismatch_total():
     say(f"group sizes: {TALLY['mismatches']} in-band mismatches in {TALLY['elements']} elements")
     check_count(TALLY["mismatches"], TALLY["elements"])
+
+
+@pytest.mark.parametrize("g", [32, 64, 256])
+@pytest.mark.parametrize("bits", ALL_BITS)
+@pytest.mark.parametrize("batch", [1, 3])
+def test_group_size_matvec(g, bits, batch, levels):
+    """cq_dequant_matvec at other group sizes against the oracle's x @ W_hat^T
+    (batch 1 of 2-bit fields takes the pair-table kernel, the rest the
+    byte-table kernel), including k not a multiple of the 1024-column tile."""
+    from parity import check_matvec
+    lv = levels[bits]
+    rng = np.random.default_rng(zlib.crc32(repr(("mv", g, bits, batch)).encode()))
+    n_out, k = 300, 1536 if g != 256 else 1280
+    q = O.quantize(rng.standard_normal((n_out, k)) * 0.02, bits, lv, g)
+    w_hat = O.dequantize(q.packed, q.norm16, n_out, k, bits, lv, g)
+    x = rng.standard_normal((batch, k)).astype(np.float32)
+    say(f"G={g} matvec bits={bits} batch={batch}")
+    y = cq.dequant_matvec(torch.from_numpy(q.packed.reshape(n_out, -1)).to(DEV),
+                          torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16),
+                          n_out, k, bits, lv, torch.from_numpy(x).to(DEV), group_size=g)
+    check_matvec(host(y), x.astype(np.float64) @ w_hat.T, x, w_hat)
