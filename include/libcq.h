@@ -43,13 +43,12 @@
  *     in N(0,1) units (before the 1/sqrt(G) scaling), strictly ascending.
  *     n_levels must be 3 for CQ_TERNARY and CQ_TERNARY_TRITS, 2^bits
  *     otherwise.
- *   - group_size: cq_quantize, cq_dequantize, cq_fake_quant,
- *     cq_quantize_many, cq_dequantize_many, cq_dequant_matvec and
- *     cq_dequant_matvec_many take 32, 64, 128 or 256 ("Cactus Quants
+ *   - group_size: the device calls take 32, 64, 128 or 256 ("Cactus Quants
  *     CQ2-bit Quantization: Extreme Compression for Edge LLMs", FAQ on group
- *     size); trit storage, the GEMM calls and cq_repack take 128; host-only
- *     calls take any power of two from 8 to 4096 (so a group's packed
- *     indices fill whole bytes).
+ *     size), except trit storage and cq_repack (128 only); the GEMM calls
+ *     also need k to be a multiple of 128 (of 256 at group size 256).
+ *     Host-only calls take any power of two from 8 to 4096 (so a group's
+ *     packed indices fill whole bytes).
  *   - Device calls validate every argument first, then enqueue their kernels
  *     on `stream` (a hipStream_t; NULL = the null stream) and return without
  *     waiting.  On a validation error nothing is enqueued.  Asynchronous

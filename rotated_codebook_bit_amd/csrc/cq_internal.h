@@ -297,13 +297,13 @@ struct SplitLevels {
   uint32_t lo[kMaxLevels];
 };
 
-int gemm_block_rows(int64_t batch);  // batch rows per GEMM block (32 or 64)
+int gemm_block_rows(int64_t batch, int group_size);  // batch rows per GEMM block (32 or 64)
 int gemm_block_cols();  // outputs per GEMM block
 
 // Workspace units: matrix d has (k / 128) * mpad rotate units, each writing
 // 256 bf16 values.
 hipError_t launch_split_rotate(const GemmDesc* table, const int64_t* ustart, int n, int64_t units,
-                               int64_t batch, uint16_t* ws, hipStream_t stream);
+                               int64_t batch, int group_size, uint16_t* ws, hipStream_t stream);
 
 // y = sum over the k ranges of each matrix's partial sums, in range order;
 // ostart: prefix of batch * n_out over the table's matrices.
@@ -311,6 +311,7 @@ hipError_t launch_gemm_reduce(const GemmDesc* table, const int64_t* ostart, int 
                               int64_t batch, hipStream_t stream);
 
 hipError_t launch_gemm(const GemmDesc* table, const int64_t* bstart, int n, int64_t blocks, int sbits,
-                       const SplitLevels& sl, const uint16_t* ws, int64_t batch, hipStream_t stream);
+                       const SplitLevels& sl, const uint16_t* ws, int64_t batch, int group_size,
+                       hipStream_t stream);
 
 }  // namespace cq

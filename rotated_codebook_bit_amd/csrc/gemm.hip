@@ -20,8 +20,8 @@
 //
 // Kernels.
 //   split_rotate_kernel: one thread per (matrix, group, padded batch row)
-//     (split_rotate_wave_kernel: one wave, for calls with few of them):
-//     writes H x_g as 128 hi and 128 lo bf16 values to the workspace, laid
+//     (split_rotate_wave_kernel: one wave, for calls with few of them at
+//     G = 128): writes H x_g as hi and lo bf16 values to the workspace, laid
 //     out [group][row][hi 128 | lo 128] so that the 64-row tile of a group is
 //     32 KiB of contiguous memory; rows past the batch are zeros.
 //   gemm_kernel: a block computes a 64 (batch) x 256 (outputs) tile of one
@@ -57,8 +57,9 @@ constexpr int BN = 256;           // outputs per block
 constexpr int TN = 2;             // 32 x 32 tiles per wave along the outputs
 constexpr int kRowBytes = 512;    // one workspace row of a group: 128 hi + 128 lo bf16
 // Rows per block: TM x 32 with TM = 2 (64 rows), or TM = 1 (32 rows) for
-// batches of at most 32, which halves the work spent on padding rows.
-constexpr int block_rows(int64_t batch) { return batch <= 32 ? 32 : 64; }
+// batches of at most 32, which halves the work spent on padding rows, and
+// at group size 32, whose 64-row kernel would not fit its registers.
+constexpr int block_rows(int64_t batch, int group_size) { return batch <= 32 || group_size < 64 ? 32 : 64; }
 constexpr int kXcds = 8;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -94,7 +95,12 @@ __device__ __forceinline__ int find_lane(const int64_t* __restrict__ start, int 
   return lo;
 }
 
-// ws[xs_off + (g * mpad + m) * 256 + (0..127 | 128..255)] = hi | lo of H x[m][g].
+// Rotated, split activations in 128-column tiles:
+//   ws[xs_off + (t * mpad + m) * 256 + (0..127 | 128..255)] = hi | lo of
+//   columns 128 t .. 128 t + 127 of (H x_g for each G-group g) in row m.
+// One thread per (G-group, padded row); a 256-group fills two tiles, a
+// smaller one part of a tile.
+template <int G>
 __global__ void __launch_bounds__(kBlock)
 split_rotate_kernel(const GemmDesc* __restrict__ table, const int64_t* __restrict__ ustart, int n,
                     int64_t batch, uint16_t* __restrict__ ws) {
@@ -104,12 +110,11 @@ split_rotate_kernel(const GemmDesc* __restrict__ table, const int64_t* __restric
   const GemmDesc& m = table[d];
   const int64_t local = u - ustart[d];
   const int64_t g = local / m.mpad, row = local - g * m.mpad;
-  uint16_t* dst = ws + m.xs_off + local * 256;
-  float y[kGroup];
+  float y[G];
   if (row < batch) {
-    const float4* src = reinterpret_cast<const float4*>(m.x + row * m.k + g * kGroup);
+    const float4* src = reinterpret_cast<const float4*>(m.x + row * m.k + g * G);
 #pragma unroll
-    for (int i = 0; i < kGroup / 4; ++i) {
+    for (int i = 0; i < G / 4; ++i) {
       const float4 v = src[i];
       y[4 * i] = v.x;
       y[4 * i + 1] = v.y;
@@ -118,12 +123,12 @@ split_rotate_kernel(const GemmDesc* __restrict__ table, const int64_t* __restric
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < kGroup; ++i) y[i] = 0.0f;
+    for (int i = 0; i < G; ++i) y[i] = 0.0f;
   }
 #pragma unroll
-  for (int h = 1; h < kGroup; h <<= 1) {
+  for (int h = 1; h < G; h <<= 1) {
 #pragma unroll
-    for (int i = 0; i < kGroup; i += 2 * h) {
+    for (int i = 0; i < G; i += 2 * h) {
 #pragma unroll
       for (int j = i; j < i + h; ++j) {
         const float a = y[j], b = y[j + h];
@@ -132,19 +137,29 @@ split_rotate_kernel(const GemmDesc* __restrict__ table, const int64_t* __restric
       }
     }
   }
-  uint32_t hi[kGroup / 2], lo[kGroup / 2];
+  uint32_t hi[G / 2], lo[G / 2];
 #pragma unroll
-  for (int i = 0; i < kGroup; i += 2) {
+  for (int i = 0; i < G; i += 2) {
     const uint32_t h0 = bf16_rne_bits(y[i]), h1 = bf16_rne_bits(y[i + 1]);
     const uint32_t l0 = bf16_rne_bits(y[i] - bf16_value(h0)), l1 = bf16_rne_bits(y[i + 1] - bf16_value(h1));
     hi[i / 2] = h0 | (h1 << 16);
     lo[i / 2] = l0 | (l1 << 16);
   }
-  uint4* d4 = reinterpret_cast<uint4*>(dst);
+  constexpr int W = G < kGroup ? G : kGroup;  // values per tile piece
+  const int64_t c0 = g * G;                   // first column of the group
 #pragma unroll
-  for (int i = 0; i < 16; ++i) d4[i] = make_uint4(hi[4 * i], hi[4 * i + 1], hi[4 * i + 2], hi[4 * i + 3]);
+  for (int piece = 0; piece < G / W; ++piece) {
+    const int64_t c = c0 + piece * W;
+    uint16_t* dst = ws + m.xs_off + ((c / kGroup) * m.mpad + row) * 256 + c % kGroup;
+    uint4* dh = reinterpret_cast<uint4*>(dst);
+    uint4* dl = reinterpret_cast<uint4*>(dst + kGroup);
+    const int o = piece * (W / 2);  // first packed word of the piece
 #pragma unroll
-  for (int i = 0; i < 16; ++i) d4[16 + i] = make_uint4(lo[4 * i], lo[4 * i + 1], lo[4 * i + 2], lo[4 * i + 3]);
+    for (int i = 0; i < W / 8; ++i) {
+      dh[i] = make_uint4(hi[o + 4 * i], hi[o + 4 * i + 1], hi[o + 4 * i + 2], hi[o + 4 * i + 3]);
+      dl[i] = make_uint4(lo[o + 4 * i], lo[o + 4 * i + 1], lo[o + 4 * i + 2], lo[o + 4 * i + 3]);
+    }
+  }
 }
 
 // The same, one wave per (group, padded row), for calls with few units.  Lane l holds values 2l and 2l + 1:
@@ -273,8 +288,12 @@ __device__ __forceinline__ float half_to_float(uint16_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, h));
 }
 
-template <int SB, int TM>
-__global__ void __launch_bounds__(kBlock, 2)
+// G: the quantization group size.  The K loop runs over 128-column tiles
+// either way; a tile holds 128 / G groups (G <= 128), each scaled by its own
+// norm after its G / 16 MFMA steps, or half of a 256-group (scaled by that
+// group's norm, the scale distributing over the two halves).
+template <int SB, int TM, int G>
+__global__ void __launch_bounds__(kBlock, G < kGroup ? 1 : 2)  // G < 128: more live norms and sums
 gemm_kernel(const GemmDesc* __restrict__ table, const int64_t* __restrict__ bstart, int n,
             SplitLevels sl, const uint8_t* __restrict__ ws, int64_t batch) {
   constexpr int BM = 32 * TM;                 // batch rows per block
@@ -307,8 +326,11 @@ gemm_kernel(const GemmDesc* __restrict__ table, const int64_t* __restrict__ bsta
   const int64_t local = lb - load_const(bstart + d);
   const int64_t ks = local % ksplit, tile = local / ksplit;
   const int64_t nt = tile / mtiles, mt = tile - nt * mtiles;  // consecutive blocks share nt
-  const int64_t ngr = k / kGroup;
-  // This block's range of groups (never empty: the host sizes the ranges).
+  const int64_t ngr = k / kGroup;  // 128-column tiles
+  constexpr int NPT = G <= kGroup ? kGroup / G : 1;  // norms per tile
+  constexpr int SPG = G <= kGroup ? G / 16 : 8;      // MFMA steps per scaled piece
+  const int64_t nrow_len = k / G;                    // norms per output row
+  // This block's range of tiles (never empty: the host sizes the ranges).
   const int64_t g_begin = ks * gps;
   const int64_t g_end = g_begin + gps < ngr ? g_begin + gps : ngr;
   const int64_t row_bytes = k * SB / 8;
@@ -326,7 +348,7 @@ gemm_kernel(const GemmDesc* __restrict__ table, const int64_t* __restrict__ bsta
     col[t] = nt * BN + 64 * wave + 32 * t + c32;
     const int64_t cl = col[t] < n_out ? col[t] : n_out - 1;
     crow[t] = packed + cl * row_bytes;
-    nrow[t] = norms + cl * ngr;
+    nrow[t] = norms + cl * nrow_len;
   }
 
   // DMA of group g's activation tile into buffer b.  Instruction i of wave w
@@ -351,11 +373,16 @@ gemm_kernel(const GemmDesc* __restrict__ table, const int64_t* __restrict__ bsta
   // Norm bits held in 32-bit registers: packing two 16-bit loads into one
   // register would make the compiler wait for them (and, in order, for the
   // DMA issued before them) right away.
-  uint32_t ncur[TN], nnxt[TN];
+  uint32_t ncur[TN][NPT], nnxt[TN][NPT];
+  // Norm j of tile g for output column t.
+  auto norm_at = [&](int t, int64_t g, int j) __attribute__((always_inline)) -> uint32_t {
+    return G <= kGroup ? nrow[t][g * NPT + j] : nrow[t][g / 2];
+  };
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
     load_codes<SB>(crow[t] + g_begin * 16 * SB, cur[t]);
-    ncur[t] = nrow[t][g_begin];
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) ncur[t][j] = norm_at(t, g_begin, j);
   }
   issue_tile(g_begin, xt0);
   wait_vm0();       // own DMA and loads
@@ -374,7 +401,8 @@ gemm_kernel(const GemmDesc* __restrict__ table, const int64_t* __restrict__ bsta
 #pragma unroll
       for (int t = 0; t < TN; ++t) {
         load_codes<SB>(crow[t] + (g + 1) * 16 * SB, nxt[t]);
-        nnxt[t] = nrow[t][g + 1];
+#pragma unroll
+        for (int j = 0; j < NPT; ++j) nnxt[t][j] = norm_at(t, g + 1, j);
       }
     }
     f32x16 tmp[TM][TN];
@@ -394,26 +422,29 @@ gemm_kernel(const GemmDesc* __restrict__ table, const int64_t* __restrict__ bsta
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int t = 0; t < TN; ++t) {
-          f32x16 c = s == 0 ? f32x16{} : tmp[i][t];
+          f32x16 c = s % SPG == 0 ? f32x16{} : tmp[i][t];
           c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh[t], c, 0, 0, 0);
           c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bl[t], c, 0, 0, 0);
           c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh[t], c, 0, 0, 0);
           tmp[i][t] = c;
         }
-    }
+      if (s % SPG == SPG - 1) {  // a piece of one group is complete: scale and add
 #pragma unroll
-    for (int t = 0; t < TN; ++t) {
-      const float sc = half_to_float(static_cast<uint16_t>(ncur[t])) * (1.0f / kGroup);
+        for (int t = 0; t < TN; ++t) {
+          const float sc = half_to_float(static_cast<uint16_t>(ncur[t][s / SPG])) * (1.0f / G);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+          for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) acc[i][t][j] = __builtin_fmaf(sc, tmp[i][t][j], acc[i][t][j]);
+            for (int j = 0; j < 16; ++j) acc[i][t][j] = __builtin_fmaf(sc, tmp[i][t][j], acc[i][t][j]);
+        }
+      }
     }
     if (g + 1 < g_end) {
 #pragma unroll
       for (int t = 0; t < TN; ++t) {
         cur[t] = nxt[t];
-        ncur[t] = nnxt[t];
+#pragma unroll
+        for (int j = 0; j < NPT; ++j) ncur[t][j] = nnxt[t][j];
       }
     }
     wait_vm0();       // next tile and codes
@@ -457,35 +488,62 @@ gemm_reduce_kernel(const GemmDesc* __restrict__ table, const int64_t* __restrict
   m.y[local] = s;
 }
 
+template <int SB, int G>
+hipError_t launch_sbg(const GemmDesc* table, const int64_t* bstart, int n, int64_t blocks,
+                      const SplitLevels& sl, const uint8_t* ws, int64_t batch, hipStream_t s) {
+  const int64_t grid = ((blocks + kXcds - 1) / kXcds) * kXcds;
+  if constexpr (G >= 64) {
+    if (block_rows(batch, G) == 64) {
+      hipLaunchKernelGGL((gemm_kernel<SB, 2, G>), dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, s, table,
+                         bstart, n, sl, ws, batch);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_kernel<SB, 1, G>), dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, s, table,
+                     bstart, n, sl, ws, batch);
+  return hipGetLastError();
+}
+
 template <int SB>
 hipError_t launch_sb(const GemmDesc* table, const int64_t* bstart, int n, int64_t blocks,
-                     const SplitLevels& sl, const uint8_t* ws, int64_t batch, hipStream_t s) {
-  const int64_t grid = ((blocks + kXcds - 1) / kXcds) * kXcds;
-  if (block_rows(batch) == 32)
-    hipLaunchKernelGGL((gemm_kernel<SB, 1>), dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, s, table,
-                       bstart, n, sl, ws, batch);
-  else
-    hipLaunchKernelGGL((gemm_kernel<SB, 2>), dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, s, table,
-                       bstart, n, sl, ws, batch);
-  return hipGetLastError();
+                     const SplitLevels& sl, const uint8_t* ws, int64_t batch, int group_size, hipStream_t s) {
+  switch (group_size) {
+    case 32: return launch_sbg<SB, 32>(table, bstart, n, blocks, sl, ws, batch, s);
+    case 64: return launch_sbg<SB, 64>(table, bstart, n, blocks, sl, ws, batch, s);
+    case 128: return launch_sbg<SB, 128>(table, bstart, n, blocks, sl, ws, batch, s);
+    case 256: return launch_sbg<SB, 256>(table, bstart, n, blocks, sl, ws, batch, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int G>
+void launch_split_rotate_threads(const GemmDesc* table, const int64_t* ustart, int n, int64_t units,
+                                 int64_t batch, uint16_t* ws, hipStream_t stream) {
+  const int64_t blocks = (units + kBlock - 1) / kBlock;
+  hipLaunchKernelGGL(split_rotate_kernel<G>, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, stream, table,
+                     ustart, n, batch, ws);
 }
 
 }  // namespace kg
 
-int gemm_block_rows(int64_t batch) { return kg::block_rows(batch); }
+int gemm_block_rows(int64_t batch, int group_size) { return kg::block_rows(batch, group_size); }
 int gemm_block_cols() { return kg::BN; }
 
 hipError_t launch_split_rotate(const GemmDesc* table, const int64_t* ustart, int n, int64_t units,
-                               int64_t batch, uint16_t* ws, hipStream_t stream) {
+                               int64_t batch, int group_size, uint16_t* ws, hipStream_t stream) {
   if (units <= 0) return hipSuccess;
-  if (units < kFewUnits) {  // a wave per unit
+  if (group_size == kGroup && units < kFewUnits) {  // a wave per unit
     const int64_t blocks = (units + kg::kWaves - 1) / kg::kWaves;
     hipLaunchKernelGGL(kg::split_rotate_wave_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kg::kBlock), 0,
                        stream, table, ustart, n, batch, ws);
-  } else {  // a thread per unit
-    const int64_t blocks = (units + kg::kBlock - 1) / kg::kBlock;
-    hipLaunchKernelGGL(kg::split_rotate_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kg::kBlock), 0,
-                       stream, table, ustart, n, batch, ws);
+    return hipGetLastError();
+  }
+  switch (group_size) {  // a thread per unit
+    case 32: kg::launch_split_rotate_threads<32>(table, ustart, n, units, batch, ws, stream); break;
+    case 64: kg::launch_split_rotate_threads<64>(table, ustart, n, units, batch, ws, stream); break;
+    case 128: kg::launch_split_rotate_threads<128>(table, ustart, n, units, batch, ws, stream); break;
+    case 256: kg::launch_split_rotate_threads<256>(table, ustart, n, units, batch, ws, stream); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -500,13 +558,14 @@ hipError_t launch_gemm_reduce(const GemmDesc* table, const int64_t* ostart, int 
 }
 
 hipError_t launch_gemm(const GemmDesc* table, const int64_t* bstart, int n, int64_t blocks, int sbits,
-                       const SplitLevels& sl, const uint16_t* ws, int64_t batch, hipStream_t stream) {
+                       const SplitLevels& sl, const uint16_t* ws, int64_t batch, int group_size,
+                       hipStream_t stream) {
   if (blocks <= 0) return hipSuccess;
   const uint8_t* w8 = reinterpret_cast<const uint8_t*>(ws);
   switch (sbits) {
-    case 2: return kg::launch_sb<2>(table, bstart, n, blocks, sl, w8, batch, stream);
-    case 3: return kg::launch_sb<3>(table, bstart, n, blocks, sl, w8, batch, stream);
-    case 4: return kg::launch_sb<4>(table, bstart, n, blocks, sl, w8, batch, stream);
+    case 2: return kg::launch_sb<2>(table, bstart, n, blocks, sl, w8, batch, group_size, stream);
+    case 3: return kg::launch_sb<3>(table, bstart, n, blocks, sl, w8, batch, group_size, stream);
+    case 4: return kg::launch_sb<4>(table, bstart, n, blocks, sl, w8, batch, group_size, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -516,7 +516,7 @@ int cq_dequant_gemm_many(int n, const cq_matvec_desc* descs, int bits, int group
   if ((rc = reject_trits(bits))) return rc;
   if (n < 0) return fail(CQ_ERR_ARG, "n < 0");
   if (batch < 1) return fail(CQ_ERR_ARG, "batch must be >= 1");
-  if ((rc = check_group(group_size, true))) return rc;
+  if ((rc = check_codec_group(group_size, bits))) return rc;
   if ((rc = check_levels(levels, n_levels, L))) return rc;
   if (n == 0) return CQ_OK;
   if (!descs) return fail(CQ_ERR_NULL, "descs is NULL");
@@ -525,9 +525,11 @@ int cq_dequant_gemm_many(int n, const cq_matvec_desc* descs, int bits, int group
   for (int i = 0; i < n; ++i) {
     const cq_matvec_desc& d = descs[i];
     if (d.n_out < 0 || d.k < 0) return fail(CQ_ERR_ARG, "matrix %d: negative size", i);
-    if (d.k % group_size)
-      return fail(CQ_ERR_UNSUPPORTED, "matrix %d: k=%lld is not a multiple of %d", i, (long long)d.k,
-                  group_size);
+    // The GEMM runs 128-column tiles whatever the group size.
+    const int64_t kmul = group_size > cq::kGroup ? group_size : cq::kGroup;
+    if (d.k % kmul)
+      return fail(CQ_ERR_UNSUPPORTED, "matrix %d: k=%lld is not a multiple of %lld", i, (long long)d.k,
+                  (long long)kmul);
     if (d.n_out == 0) continue;
     if (!d.y) return fail(CQ_ERR_NULL, "matrix %d: y is NULL", i);
     if (!aligned(d.y, 16)) return fail(CQ_ERR_ALIGN, "matrix %d: y needs 16-byte alignment", i);
@@ -554,7 +556,7 @@ int cq_dequant_gemm_many(int n, const cq_matvec_desc* descs, int bits, int group
     sl.hi[i] = hi;
     sl.lo[i] = bf16_rne_host(levels[i] - hv);
   }
-  const int64_t bm = cq::gemm_block_rows(batch), bn = cq::gemm_block_cols();
+  const int64_t bm = cq::gemm_block_rows(batch, group_size), bn = cq::gemm_block_cols();
   const int64_t mpad = ceil_div(batch, bm) * bm;
   std::vector<cq::GemmDesc> act;
   for (int i = 0; i < n; ++i) {
@@ -578,12 +580,12 @@ int cq_dequant_gemm_many(int n, const cq_matvec_desc* descs, int bits, int group
   std::vector<int64_t> ustart{0}, bstart{0}, ostart{0}, part_off;
   int64_t xs = 0, parts = 0;  // bf16 values; partial-sum floats
   for (cq::GemmDesc& g : act) {
-    const int64_t ngr = g.k / group_size;
+    const int64_t ngr = g.k / cq::kGroup;  // 128-column tiles
     g.xs_off = xs;
     g.gps = ceil_div(ngr, split);
     g.ksplit = ceil_div(ngr, g.gps);  // every range non-empty
-    xs += ngr * mpad * 2 * group_size;
-    ustart.push_back(ustart.back() + ngr * mpad);
+    xs += ngr * mpad * 2 * cq::kGroup;
+    ustart.push_back(ustart.back() + (g.k / group_size) * mpad);  // rotation units: (group, row)
     bstart.push_back(bstart.back() + (mpad / bm) * ceil_div(g.n_out, bn) * g.ksplit);
     ostart.push_back(ostart.back() + batch * g.n_out);
     part_off.push_back(parts);
@@ -609,9 +611,11 @@ int cq_dequant_gemm_many(int n, const cq_matvec_desc* descs, int bits, int group
   if (!rc) rc = hip_status(cq::upload(bstart.data(), (na + 1) * 8, b_dev, s), "table upload");
   if (!rc && split > 1) rc = hip_status(cq::upload(ostart.data(), (na + 1) * 8, o_dev, s), "table upload");
   if (!rc)
-    rc = hip_status(cq::launch_split_rotate(table, u_dev, na, ustart[na], batch, xs_dev, s), "rotate launch");
+    rc = hip_status(cq::launch_split_rotate(table, u_dev, na, ustart[na], batch, group_size, xs_dev, s),
+                    "rotate launch");
   if (!rc)
-    rc = hip_status(cq::launch_gemm(table, b_dev, na, bstart[na], sb, sl, xs_dev, batch, s), "gemm launch");
+    rc = hip_status(cq::launch_gemm(table, b_dev, na, bstart[na], sb, sl, xs_dev, batch, group_size, s),
+                    "gemm launch");
   if (!rc && split > 1)
     rc = hip_status(cq::launch_gemm_reduce(table, o_dev, na, ostart[na], batch, s), "reduce launch");
   const int rc2 = hip_status(hipFreeAsync(ws, s), "workspace free");

@@ -335,7 +335,8 @@ def test_gemm_validation():
         return L.cq_dequant_gemm(packed, norms, n_out, k, bits, g, lp, nl, x, batch, y, None)
 
     assert gm(k=200) == E_UNSUP
-    assert gm(g=64) == E_UNSUP
+    assert gm(g=512) == E_UNSUP
+    assert gm(g=64, k=192) == E_UNSUP                                 # tiles of 128 columns
     assert gm(batch=0) == E_ARG
     assert gm(bits=158, nl=4) == E_ARG
     assert gm(x=None) == E_NULL
@@ -407,10 +408,15 @@ def test_group_size_support():
     assert quant(g=16) == E_UNSUP
     assert quant(g=1024) == E_UNSUP
     assert L.cq_quantize(FAKE, 0, 4, 256, O.TERNARY_TRITS, 64, lp3, 3, FAKE2, FAKE3, None) == E_UNSUP
-    # the matvec takes the codec sizes too; the GEMM and repack take 128 only
+    # the products take the codec sizes too; repack takes 128 only
     assert L.cq_dequant_matvec(FAKE, FAKE2, 8, 256, 2, 512, lp, 4, ctypes.c_void_p(0x2100000), 1,
                                ctypes.c_void_p(0x3100000), None) == E_UNSUP
-    assert L.cq_dequant_gemm(FAKE, FAKE2, 8, 256, 2, 64, lp, 4, ctypes.c_void_p(0x2100000), 16,
+    assert L.cq_dequant_gemm(FAKE, FAKE2, 8, 256, 2, 512, lp, 4, ctypes.c_void_p(0x2100000), 16,
+                             ctypes.c_void_p(0x3100000), None) == E_UNSUP
+    # the GEMM runs 128-column tiles at every group size
+    assert L.cq_dequant_gemm(FAKE, FAKE2, 8, 192, 2, 64, lp, 4, ctypes.c_void_p(0x2100000), 16,
+                             ctypes.c_void_p(0x3100000), None) == E_UNSUP
+    assert L.cq_dequant_gemm(FAKE, FAKE2, 8, 384, 2, 256, lp, 4, ctypes.c_void_p(0x2100000), 16,
                              ctypes.c_void_p(0x3100000), None) == E_UNSUP
     assert L.cq_repack(FAKE, O.TERNARY, FAKE2, O.TERNARY_TRITS, 4, 256, None) == E_UNSUP
     # sizes for other group sizes

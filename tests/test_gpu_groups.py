@@ -161,3 +161,48 @@ def test_group_size_matvec(g, bits, batch, levels):
                           torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16),
                           n_out, k, bits, lv, torch.from_numpy(x).to(DEV), group_size=g)
     check_matvec(host(y), x.astype(np.float64) @ w_hat.T, x, w_hat)
+
+
+@pytest.mark.parametrize("g", [32, 64, 256])
+@pytest.mark.parametrize("bits", ALL_BITS)
+@pytest.mark.parametrize("batch", [16, 70])
+def test_group_size_gemm(g, bits, batch, levels):
+    """cq_dequant_gemm at other group sizes against the oracle (GEMM bound):
+    several scaled groups per 128-column tile (32, 64) or one group over two
+    tiles (256); batch 70 takes 64-row tiles where the group size allows."""
+    from parity import GEMM_TOL, check_matvec
+    lv = levels[bits]
+    rng = np.random.default_rng(zlib.crc32(repr(("gemm", g, bits, batch)).encode()))
+    n_out, k = 300, 1536
+    q = O.quantize(rng.standard_normal((n_out, k)) * 0.02, bits, lv, g)
+    w_hat = O.dequantize(q.packed, q.norm16, n_out, k, bits, lv, g)
+    x = rng.standard_normal((batch, k)).astype(np.float32)
+    say(f"G={g} gemm bits={bits} batch={batch}")
+    y = cq.dequant_gemm(torch.from_numpy(q.packed.reshape(n_out, -1)).to(DEV),
+                        torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16),
+                        n_out, k, bits, lv, torch.from_numpy(x).to(DEV), group_size=g)
+    check_matvec(host(y), x.astype(np.float64) @ w_hat.T, x, w_hat, tol=GEMM_TOL)
+
+
+@pytest.mark.parametrize("g", [32, 64, 256])
+def test_group_size_gemm_many_groups(g, levels):
+    """The thread-per-unit activation rotation (at least 32,768 (group, row)
+    units) and many matrices in one call at another group size."""
+    from parity import GEMM_TOL, check_matvec
+    lv = levels[2]
+    rng = np.random.default_rng(90 + g)
+    batch = 256
+    items, refs = [], []
+    for n_out, k in [(64, 8192), (200, 1024), (33, 2048)]:
+        q = O.quantize(rng.standard_normal((n_out, k)) * 0.02, 2, lv, g)
+        w_hat = O.dequantize(q.packed, q.norm16, n_out, k, 2, lv, g)
+        x = rng.standard_normal((batch, k)).astype(np.float32)
+        y = torch.full((batch, n_out), float("nan"), dtype=torch.float32, device=DEV)
+        items.append((torch.from_numpy(q.packed.reshape(n_out, -1)).to(DEV),
+                      torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16), n_out, k,
+                      torch.from_numpy(x).to(DEV), y))
+        refs.append((x, w_hat))
+    say(f"G={g} gemm_many batch={batch}")
+    cq.dequant_gemm_many(items, 2, lv, batch, group_size=g)
+    for (x, w_hat), it in zip(refs, items):
+        check_matvec(host(it[5]), x.astype(np.float64) @ w_hat.T, x, w_hat, tol=GEMM_TOL)
