@@ -158,14 +158,17 @@ int cq_dequantize(const uint8_t* packed, const uint16_t* norms, int64_t rows,
  * in the order of "How CQ2-bit Quantization Contributes to Needle 2's Small
  * Footprint", section Binary Serialization: the packed indices of every
  * tensor, tensor after tensor, then the binary16 norms of every tensor in the
- * same order, with no header and no padding.  Writes the byte offset of
- * tensor i's packed indices to packed_offsets[i] and of its norms to
- * norm_offsets[i] (host arrays of n_tensors entries, each may be NULL) and
- * the blob size to *total_bytes (may be NULL), which equals cq_model_bytes.
- * Every packed offset meets the call's packed alignment (a multiple of 16
- * at group size 128, of 4 at the others, of 2 in trit storage) and every
- * norm offset is even, so a 16-byte aligned blob can take
- * cq_quantize_many's outputs directly.  Host only, pure. */
+ * same order, with no header.  When the indices take an odd number of bytes
+ * (trit storage at group sizes whose groups are 7 or 13 bytes) one pad byte
+ * follows them, which cq_quantize_many does not write.  Writes the byte
+ * offset of tensor i's packed indices to packed_offsets[i] and of its norms
+ * to norm_offsets[i] (host arrays of n_tensors entries, each may be NULL)
+ * and the blob size to *total_bytes (may be NULL), which equals
+ * cq_model_bytes plus that pad byte.  Every packed offset meets the call's
+ * packed alignment (a multiple of 16 at group size 128, of 4 at the others,
+ * of 2 in trit storage at 128, any otherwise) and every norm offset is even,
+ * so a 16-byte aligned blob can take cq_quantize_many's outputs directly.
+ * Host only, pure. */
 int cq_blob_layout(int n_tensors, const int64_t* rows, const int64_t* cols, int bits,
                    int group_size, int64_t* packed_offsets, int64_t* norm_offsets,
                    int64_t* total_bytes);

@@ -402,9 +402,14 @@ def serialize(quantized) -> np.ndarray:
     """Serialized weights of a sequence of quantized tensors, in the order of
     *Footprint* §Binary Serialization: the packed indices of every tensor,
     tensor after tensor, followed by every tensor's binary16 norms
-    (little-endian), in the same tensor order.  No header and no padding
-    (reading: the norms of all tensors follow all the indices)."""
+    (little-endian), in the same tensor order.  No header (reading: the
+    norms of all tensors follow all the indices).  Trit storage can leave the
+    indices an odd number of bytes (7- or 13-byte groups at g = 32, 64); then
+    one zero byte follows them, so the binary16 norms start at an even
+    offset (reading: the pages give no trit layout at these group sizes)."""
     parts = [np.asarray(q.packed, dtype=np.uint8).ravel() for q in quantized]
+    if sum(p.size for p in parts) % 2:
+        parts.append(np.zeros(1, dtype=np.uint8))
     parts += [np.asarray(q.norm16, dtype=np.uint16).astype("<u2").view(np.uint8).ravel()
               for q in quantized]
     return np.concatenate(parts) if parts else np.zeros(0, dtype=np.uint8)
@@ -413,7 +418,8 @@ def serialize(quantized) -> np.ndarray:
 def blob_offsets(shapes, bits: int, g: int = GROUP):
     """(packed_offsets, norm_offsets, total) of :func:`serialize`'s output for
     tensors of the given shapes: byte offsets of each tensor's indices and
-    norms, and the total size (which equals :func:`model_bytes`)."""
+    norms, and the total size (which equals :func:`model_bytes`, plus the pad
+    byte after an odd-length index section)."""
     gb = group_bytes(bits, g)
     packed, norms = [], []
     for shape in shapes:
@@ -423,8 +429,9 @@ def blob_offsets(shapes, bits: int, g: int = GROUP):
         packed.append(groups * gb)
         norms.append(groups * 2)
     p_off = [sum(packed[:i]) for i in range(len(packed))]
-    n_off = [sum(packed) + sum(norms[:i]) for i in range(len(norms))]
-    return p_off, n_off, sum(packed) + sum(norms)
+    n0 = sum(packed) + sum(packed) % 2
+    n_off = [n0 + sum(norms[:i]) for i in range(len(norms))]
+    return p_off, n_off, n0 + sum(norms)
 
 
 def relative_mse(w: np.ndarray, w_hat: np.ndarray) -> float:

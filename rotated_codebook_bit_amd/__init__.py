@@ -324,6 +324,12 @@ def quantize_many(ws, bits: int, levels, blob=None, group_size: int = GROUP, str
     po, no, total = blob_layout([tuple(w.shape) for w in ws], bits, group_size)
     if blob is None:
         blob = torch.empty(total, dtype=torch.uint8, device=ws[0].device)
+        # An odd-length index section is followed by a pad byte the library
+        # does not write: zero it, so the blob is fully defined.
+        packed_end = group_bytes(bits, group_size) * sum(
+            r * -(-c // group_size) for r, c in (_rows_cols(tuple(w.shape)) for w in ws))
+        if packed_end % 2:
+            blob[packed_end:packed_end + 1].zero_()
     if blob.dtype != torch.uint8 or blob.numel() != total or not blob.is_contiguous():
         raise ValueError(f"blob must be a contiguous uint8 tensor of {total} bytes")
     pb = group_bytes(bits, group_size)

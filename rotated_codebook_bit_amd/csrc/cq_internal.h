@@ -101,9 +101,9 @@ __device__ __forceinline__ void trits_to_fields(const uint32_t (&t)[13], const u
   }
 }
 
-// Ternary 2-bit fields <-> trit storage for n_groups groups (to_trits: src
-// holds fields).
-hipError_t launch_repack(const uint8_t* src, bool to_trits, uint8_t* dst, int64_t n_groups,
+// Ternary 2-bit fields <-> trit storage for n_groups groups of group_size
+// (32, 64, 128, 256) indices (to_trits: src holds fields).
+hipError_t launch_repack(const uint8_t* src, bool to_trits, uint8_t* dst, int64_t n_groups, int group_size,
                          hipStream_t stream);
 
 // Compute units of the current device (cached per device).

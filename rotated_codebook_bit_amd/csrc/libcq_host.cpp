@@ -88,13 +88,12 @@ int check_levels(const float* levels, int n_levels, int expect) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// The single-tensor codec calls (quantize, dequantize, fake quantization)
-// also run group sizes 32, 64 and 256; trit storage is laid out for 128.
+// The codec calls (quantize, dequantize, fake quantization, their
+// multi-tensor forms, repacking) run group sizes 32, 64, 128 and 256.
 int check_codec_group(int group_size, int bits) {
+  (void)bits;
   if (group_size != 32 && group_size != 64 && group_size != cq::kGroup && group_size != 256)
     return fail(CQ_ERR_UNSUPPORTED, "group_size=%d: these kernels support 32, 64, 128 and 256", group_size);
-  if (bits == CQ_TERNARY_TRITS && group_size != cq::kGroup)
-    return fail(CQ_ERR_UNSUPPORTED, "trit storage is implemented for group_size 128");
   return CQ_OK;
 }
 
@@ -113,7 +112,7 @@ int storage_code(int bits) { return bits == CQ_TERNARY_TRITS ? cq::kTritStorage 
 // serialized blob qualifies), 2 bytes for trit storage (16-bit accesses; a
 // group is 26 bytes, so tensors inside a blob sit at even offsets).
 size_t packed_align(int bits, int group_size) {
-  if (bits == CQ_TERNARY_TRITS) return 2;
+  if (bits == CQ_TERNARY_TRITS) return group_size == cq::kGroup ? 2 : 1;
   return group_size == cq::kGroup ? 16 : 4;
 }
 
@@ -228,6 +227,38 @@ cq::QuantParams make_quant_params(const float* levels, int n_levels) {
   }
   return p;
 }
+
+// Trit storage at group sizes other than 128: the 2-bit field kernels with a
+// stream-ordered workspace of fields (G / 4 bytes per group), converted by
+// cq_repack's kernels.
+int quantize_trits_g(const void* w, bool bf16, int64_t rows, int64_t cols, int group_size,
+                     const cq::QuantParams& p, uint8_t* packed, uint16_t* norms, hipStream_t s) {
+  const int64_t ng = rows * ceil_div(cols, group_size);
+  uint8_t* ws = nullptr;
+  int rc = hip_status(hipMallocAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(ng) * (group_size / 4), s),
+                      "workspace alloc");
+  if (rc) return rc;
+  rc = hip_status(cq::launch_quantize_g(group_size, w, bf16, rows, cols, p, ws, norms, s), "quantize launch");
+  if (!rc) rc = hip_status(cq::launch_repack(ws, true, packed, ng, group_size, s), "repack launch");
+  const int rc2 = hip_status(hipFreeAsync(ws, s), "workspace free");
+  return rc ? rc : rc2;
+}
+
+int dequantize_trits_g(const uint8_t* packed, const uint16_t* norms, int64_t rows, int64_t cols, int group_size,
+                       const cq::LevelTable& lv, void* out, bool bf16_out, hipStream_t s) {
+  const int64_t ng = rows * ceil_div(cols, group_size);
+  uint8_t* ws = nullptr;
+  int rc = hip_status(hipMallocAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(ng) * (group_size / 4), s),
+                      "workspace alloc");
+  if (rc) return rc;
+  rc = hip_status(cq::launch_repack(packed, false, ws, ng, group_size, s), "repack launch");
+  if (!rc)
+    rc = hip_status(cq::launch_dequantize_g(group_size, ws, norms, rows, cols, 2, lv, out, bf16_out, s),
+                    "dequantize launch");
+  const int rc2 = hip_status(hipFreeAsync(ws, s), "workspace free");
+  return rc ? rc : rc2;
+}
+
 
 cq::LevelTable make_table(const float* levels, int n_levels) {
   cq::LevelTable t{};
@@ -373,7 +404,7 @@ int cq_quantize(const void* w, int w_dtype, int64_t rows, int64_t cols, int bits
   if (rows == 0 || cols == 0) return CQ_OK;
   if (!w || !packed || !norms) return fail(CQ_ERR_NULL, "w/packed/norms is NULL");
   if (!aligned(w, 16) || !aligned(packed, packed_align(bits, group_size)) || !aligned(norms, 2))
-    return fail(CQ_ERR_ALIGN, "w needs 16-byte, packed 16-byte (G != 128: 4-byte; trits: 2-byte), norms 2-byte alignment");
+    return fail(CQ_ERR_ALIGN, "w needs 16-byte, packed 16-byte (G != 128: 4-byte; trits: 2-byte, any at G != 128), norms 2-byte alignment");
   const int64_t ng = rows * ceil_div(cols, group_size);
   const size_t in_bytes = static_cast<size_t>(rows * cols) * (w_dtype == CQ_F32 ? 4 : 2);
   const size_t pk_bytes = static_cast<size_t>(ng * group_bytes(bits, group_size));
@@ -382,6 +413,9 @@ int cq_quantize(const void* w, int w_dtype, int64_t rows, int64_t cols, int bits
       overlap(packed, pk_bytes, norms, nm_bytes))
     return fail(CQ_ERR_ARG, "input and output buffers overlap");
   const cq::QuantParams p = make_quant_params(levels, L);
+  if (group_size != cq::kGroup && bits == CQ_TERNARY_TRITS)
+    return quantize_trits_g(w, w_dtype == CQ_BF16, rows, cols, group_size, p, packed, norms,
+                            static_cast<hipStream_t>(stream));
   if (group_size != cq::kGroup)
     return hip_status(cq::launch_quantize_g(group_size, w, w_dtype == CQ_BF16, rows, cols, p, packed, norms,
                                             static_cast<hipStream_t>(stream)),
@@ -413,7 +447,7 @@ int cq_quantize_many(int n, const cq_quant_desc* descs, int w_dtype, int bits, i
     if (d.rows == 0 || d.cols == 0) continue;
     if (!d.w || !d.packed || !d.norms) return fail(CQ_ERR_NULL, "tensor %d: w/packed/norms is NULL", i);
     if (!aligned(d.w, 16) || !aligned(d.packed, packed_align(bits, group_size)) || !aligned(d.norms, 2))
-      return fail(CQ_ERR_ALIGN, "tensor %d: w needs 16-byte, packed 16-byte (G != 128: 4-byte; trits: 2-byte), norms 2-byte alignment", i);
+      return fail(CQ_ERR_ALIGN, "tensor %d: w needs 16-byte, packed 16-byte (G != 128: 4-byte; trits: 2-byte, any at G != 128), norms 2-byte alignment", i);
     const int64_t ng = d.rows * ceil_div(d.cols, group_size);
     ins.push_back(span(d.w, static_cast<size_t>(d.rows * d.cols) * esz, i));
     outs.push_back(span(d.packed, static_cast<size_t>(ng * gb), i));
@@ -431,9 +465,11 @@ int cq_quantize_many(int n, const cq_quant_desc* descs, int w_dtype, int bits, i
     for (int i = 0; i < n && !rc; ++i) {
       const cq_quant_desc& d = descs[i];
       if (d.rows == 0 || d.cols == 0) continue;
-      rc = hip_status(cq::launch_quantize_g(group_size, d.w, w_dtype == CQ_BF16, d.rows, d.cols, p, d.packed,
-                                            d.norms, s),
-                      "quantize launch");
+      rc = bits == CQ_TERNARY_TRITS
+               ? quantize_trits_g(d.w, w_dtype == CQ_BF16, d.rows, d.cols, group_size, p, d.packed, d.norms, s)
+               : hip_status(cq::launch_quantize_g(group_size, d.w, w_dtype == CQ_BF16, d.rows, d.cols, p,
+                                                  d.packed, d.norms, s),
+                            "quantize launch");
     }
     return rc;
   }
@@ -468,7 +504,7 @@ int cq_dequantize_many(int n, const cq_dequant_desc* descs, int bits, int group_
     if (d.rows == 0 || d.cols == 0) continue;
     if (!d.packed || !d.norms || !d.out) return fail(CQ_ERR_NULL, "tensor %d: packed/norms/out is NULL", i);
     if (!aligned(d.out, 16) || !aligned(d.packed, packed_align(bits, group_size)) || !aligned(d.norms, 2))
-      return fail(CQ_ERR_ALIGN, "tensor %d: out needs 16-byte, packed 16-byte (G != 128: 4-byte; trits: 2-byte), norms 2-byte alignment", i);
+      return fail(CQ_ERR_ALIGN, "tensor %d: out needs 16-byte, packed 16-byte (G != 128: 4-byte; trits: 2-byte, any at G != 128), norms 2-byte alignment", i);
     const int64_t ng = d.rows * ceil_div(d.cols, group_size);
     ins.push_back(span(d.packed, static_cast<size_t>(ng * gb), i));
     ins.push_back(span(d.norms, static_cast<size_t>(ng) * 2, i));
@@ -486,9 +522,11 @@ int cq_dequantize_many(int n, const cq_dequant_desc* descs, int bits, int group_
     for (int i = 0; i < n && !rc; ++i) {
       const cq_dequant_desc& d = descs[i];
       if (d.rows == 0 || d.cols == 0) continue;
-      rc = hip_status(cq::launch_dequantize_g(group_size, d.packed, d.norms, d.rows, d.cols, storage_bits(bits),
-                                              lv, d.out, out_dtype == CQ_BF16, s),
-                      "dequantize launch");
+      rc = bits == CQ_TERNARY_TRITS
+               ? dequantize_trits_g(d.packed, d.norms, d.rows, d.cols, group_size, lv, d.out, out_dtype == CQ_BF16, s)
+               : hip_status(cq::launch_dequantize_g(group_size, d.packed, d.norms, d.rows, d.cols,
+                                                    storage_bits(bits), lv, d.out, out_dtype == CQ_BF16, s),
+                            "dequantize launch");
     }
     return rc;
   }
@@ -639,17 +677,18 @@ int cq_repack(const uint8_t* src, int src_bits, uint8_t* dst, int dst_bits, int6
     return fail(CQ_ERR_ARG, "cq_repack converts between CQ_TERNARY and CQ_TERNARY_TRITS (got %d -> %d)",
                 src_bits, dst_bits);
   if (n_groups < 0) return fail(CQ_ERR_ARG, "n_groups < 0");
-  if ((rc = check_group(group_size, true))) return rc;
+  if ((rc = check_codec_group(group_size, CQ_TERNARY_TRITS))) return rc;
   if (n_groups == 0) return CQ_OK;
   if (!src || !dst) return fail(CQ_ERR_NULL, "src/dst is NULL");
   const uint8_t* fields = to_trits ? src : dst;
   const uint8_t* trits = to_trits ? dst : src;
-  if (!aligned(fields, 16) || !aligned(trits, 2))
-    return fail(CQ_ERR_ALIGN, "2-bit fields need 16-byte, trit storage 2-byte alignment");
+  if (!aligned(fields, packed_align(CQ_TERNARY, group_size)) ||
+      !aligned(trits, packed_align(CQ_TERNARY_TRITS, group_size)))
+    return fail(CQ_ERR_ALIGN, "2-bit fields need 16-byte (G != 128: 4-byte), trit storage 2-byte (G != 128: any) alignment");
   if (overlap(src, static_cast<size_t>(n_groups * group_bytes(src_bits, group_size)), dst,
               static_cast<size_t>(n_groups * group_bytes(dst_bits, group_size))))
     return fail(CQ_ERR_ARG, "src and dst overlap");
-  return hip_status(cq::launch_repack(src, to_trits, dst, n_groups, static_cast<hipStream_t>(stream)),
+  return hip_status(cq::launch_repack(src, to_trits, dst, n_groups, group_size, static_cast<hipStream_t>(stream)),
                     "repack launch");
 }
 
@@ -667,15 +706,18 @@ int cq_blob_layout(int n_tensors, const int64_t* rows, const int64_t* cols, int 
     if (rows[i] < 0 || cols[i] < 0) return fail(CQ_ERR_ARG, "tensor %d has a negative size", i);
     packed_total += rows[i] * ceil_div(cols[i], group_size) * per_group;
   }
+  // An odd index section (trit storage with 7- or 13-byte groups) is followed
+  // by one pad byte, so the binary16 norms start at an even offset.
+  const int64_t norms_start = packed_total + packed_total % 2;
   int64_t p = 0;
   for (int i = 0; i < n_tensors; ++i) {
     const int64_t ng = rows[i] * ceil_div(cols[i], group_size);
     if (packed_offsets) packed_offsets[i] = p;
-    if (norm_offsets) norm_offsets[i] = packed_total + norms_total;
+    if (norm_offsets) norm_offsets[i] = norms_start + norms_total;
     p += ng * per_group;
     norms_total += 2 * ng;
   }
-  if (total_bytes) *total_bytes = packed_total + norms_total;
+  if (total_bytes) *total_bytes = norms_start + norms_total;
   return CQ_OK;
 }
 
@@ -725,13 +767,16 @@ int cq_dequantize(const uint8_t* packed, const uint16_t* norms, int64_t rows, in
   if (rows == 0 || cols == 0) return CQ_OK;
   if (!packed || !norms || !out) return fail(CQ_ERR_NULL, "packed/norms/out is NULL");
   if (!aligned(out, 16) || !aligned(packed, packed_align(bits, group_size)) || !aligned(norms, 2))
-    return fail(CQ_ERR_ALIGN, "out needs 16-byte, packed 16-byte (G != 128: 4-byte; trits: 2-byte), norms 2-byte alignment");
+    return fail(CQ_ERR_ALIGN, "out needs 16-byte, packed 16-byte (G != 128: 4-byte; trits: 2-byte, any at G != 128), norms 2-byte alignment");
   const int64_t ng = rows * ceil_div(cols, group_size);
   const size_t out_bytes = static_cast<size_t>(rows * cols) * (out_dtype == CQ_F32 ? 4 : 2);
   const size_t pk_bytes = static_cast<size_t>(ng * group_bytes(bits, group_size));
   if (overlap(out, out_bytes, packed, pk_bytes) || overlap(out, out_bytes, norms, ng * 2))
     return fail(CQ_ERR_ARG, "input and output buffers overlap");
   const cq::LevelTable lv = make_table(levels, L);
+  if (group_size != cq::kGroup && bits == CQ_TERNARY_TRITS)
+    return dequantize_trits_g(packed, norms, rows, cols, group_size, lv, out, out_dtype == CQ_BF16,
+                              static_cast<hipStream_t>(stream));
   if (group_size != cq::kGroup)
     return hip_status(cq::launch_dequantize_g(group_size, packed, norms, rows, cols, storage_bits(bits), lv,
                                               out, out_dtype == CQ_BF16, static_cast<hipStream_t>(stream)),

@@ -243,12 +243,16 @@ def test_fake_quant_validation():
 
 def test_blob_layout_equals_oracle():
     shapes = [s for _, s in W.needle2_shapes()] + [(2, 3, 130), (1, 1), (0, 128)]
-    for bits in (O.TERNARY, 1, 2, 3, 4):
-        for g in (8, 64, 128, 256):
+    for bits in (O.TERNARY, O.TERNARY_TRITS, 1, 2, 3, 4):
+        for g in (8, 32, 64, 128, 256):
             po, no, total = cq.blob_layout(shapes, bits, g)
             want = O.blob_offsets(shapes, bits, g)
             assert (po, no, total) == (list(want[0]), list(want[1]), want[2])
-            assert total == cq.model_bytes(shapes, bits, g)
+            # model bytes, plus one pad byte after an odd-length index section
+            groups = sum(int(np.prod(s[:-1])) * -(-s[-1] // g) for s in shapes)
+            index_bytes = groups * O.group_bytes(bits, g)
+            assert total == cq.model_bytes(shapes, bits, g) + index_bytes % 2
+            assert no[0] == index_bytes + index_bytes % 2
     ex = json.load(open(os.path.join(ROOT, "tests", "golden", "hand_examples.json")))["blob_two_groups"]
     assert cq.blob_layout([(1, 128), (1, 128)], 2) == (ex["packed_offsets"], ex["norm_offsets"], ex["total"])
     assert cq.blob_layout([], 2) == ([], [], 0)
@@ -288,7 +292,7 @@ def test_quantize_many_validation():
     assert qm([good], dt=2) == E_ARG
     assert qm([good], g=512) == E_UNSUP
     assert qm([good], g=16) == E_UNSUP
-    assert qm([good], bits=O.TERNARY_TRITS, nl=3, g=64) == E_UNSUP  # trits are laid out for 128
+    assert qm([good], bits=O.TERNARY_TRITS, nl=3, g=512) == E_UNSUP
     assert qm([good, _qdesc(rows=-1)], g=64) == E_ARG                  # G = 64 validates as 128 does
     assert qm([good], nl=8) == E_ARG
     assert qm([good, _qdesc(rows=-1)]) == E_ARG
@@ -392,7 +396,8 @@ def test_trit_validation():
     assert R(FAKE, 2, FAKE2, T, 10, 128, None) == E_ARG          # only ternary <-> trits
     assert R(FAKE, T, FAKE2, T, 10, 128, None) == E_ARG
     assert R(FAKE, O.TERNARY, FAKE2, T, -1, 128, None) == E_ARG
-    assert R(FAKE, O.TERNARY, FAKE2, T, 10, 64, None) == E_UNSUP
+    assert R(FAKE, O.TERNARY, FAKE2, T, 10, 512, None) == E_UNSUP
+    assert R(ctypes.c_void_p(0x100002), O.TERNARY, FAKE2, T, 10, 64, None) == E_ALIGN   # fields 4-B at 64
     assert R(None, O.TERNARY, FAKE2, T, 10, 128, None) == E_NULL
     assert R(ctypes.c_void_p(0x100008), O.TERNARY, FAKE2, T, 10, 128, None) == E_ALIGN   # fields 16-B
     assert R(FAKE, O.TERNARY, ctypes.c_void_p(0x900001), T, 10, 128, None) == E_ALIGN   # trits 2-B
@@ -407,7 +412,7 @@ def test_group_size_support():
     # codec calls: 32, 64, 128, 256; others unsupported; trit storage at 128 only
     assert quant(g=16) == E_UNSUP
     assert quant(g=1024) == E_UNSUP
-    assert L.cq_quantize(FAKE, 0, 4, 256, O.TERNARY_TRITS, 64, lp3, 3, FAKE2, FAKE3, None) == E_UNSUP
+    assert L.cq_quantize(FAKE, 0, 4, 256, O.TERNARY_TRITS, 16, lp3, 3, FAKE2, FAKE3, None) == E_UNSUP
     # the products take the codec sizes too; repack takes 128 only
     assert L.cq_dequant_matvec(FAKE, FAKE2, 8, 256, 2, 512, lp, 4, ctypes.c_void_p(0x2100000), 1,
                                ctypes.c_void_p(0x3100000), None) == E_UNSUP
@@ -418,7 +423,7 @@ def test_group_size_support():
                              ctypes.c_void_p(0x3100000), None) == E_UNSUP
     assert L.cq_dequant_gemm(FAKE, FAKE2, 8, 384, 2, 256, lp, 4, ctypes.c_void_p(0x2100000), 16,
                              ctypes.c_void_p(0x3100000), None) == E_UNSUP
-    assert L.cq_repack(FAKE, O.TERNARY, FAKE2, O.TERNARY_TRITS, 4, 256, None) == E_UNSUP
+    assert L.cq_repack(FAKE, O.TERNARY, FAKE2, O.TERNARY_TRITS, 4, 512, None) == E_UNSUP
     # sizes for other group sizes
     assert cq.layout(3, 200, 2, 64) == (12, 12 * 16)
     assert cq.layout(3, 200, 4, 256) == (3, 3 * 128)

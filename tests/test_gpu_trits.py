@@ -133,3 +133,50 @@ def test_trit_needle2_footprint(lv):
         mism += rep["index_mismatches"]
         elems += rep["elements"]
     check_count(mism, elems)
+
+
+@pytest.mark.parametrize("g", [32, 64, 256])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(100, 384), (7, 1000)])
+def test_trit_group_sizes(g, dtype, shape, lv):
+    """Trit storage at group sizes other than 128 (ceil(G/5) bytes per group):
+    quantize and dequantize against the oracle, and equality with 2-bit
+    ternary quantize followed by cq_repack (both directions)."""
+    w64, w_dev = make(shape, zlib.crc32(repr(("trit-g", g, dtype, shape)).encode()), dtype)
+    rows, cols = shape
+    say(f"trit G={g} quantize {dtype}{shape}")
+    q = O.quantize(w64, T, lv, g)
+    packed, norms = cq.quantize(w_dev, T, lv, group_size=g)
+    assert packed.shape[-1] == -(-g // 5)
+    check_quantize(host(packed), f16_bits(norms), q)
+    p2, n2 = cq.quantize(w_dev, O.TERNARY, lv, group_size=g)
+    assert torch.equal(cq.repack(p2, O.TERNARY, T, group_size=g), packed)
+    assert torch.equal(cq.repack(packed, T, O.TERNARY, group_size=g), p2)
+    say(f"trit G={g} dequantize {shape}")
+    ref = O.dequantize(q.packed, q.norm16, rows, cols, T, lv, g)
+    out = cq.dequantize(torch.from_numpy(q.packed.reshape(rows, -1)).to(DEV),
+                        torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16),
+                        rows, cols, T, lv, group_size=g)
+    check_dequant(host(out), ref, q.norm16, rows, cols, g)
+
+
+def test_trit_many_calls_group_64(lv):
+    """The multi-tensor calls with trit storage at G = 64: 13-byte groups, so
+    tensors sit at odd blob offsets."""
+    rng = np.random.default_rng(19)
+    shapes = [(3, 64), (5, 300), (1, 1), (64, 512)]
+    ws = [torch.from_numpy((rng.standard_normal(s) * 0.02).astype(np.float32)).to(DEV) for s in shapes]
+    say("trit G=64 quantize_many")
+    blob, views = cq.quantize_many(ws, T, lv, group_size=64)
+    po, no, total = O.blob_offsets(shapes, T, 64)
+    assert blob.numel() == total and any(o % 2 for o in po)
+    items = []
+    for s, w, (pk, nm) in zip(shapes, ws, views):
+        p1, n1 = cq.quantize(w, T, lv, group_size=64)
+        assert torch.equal(p1.reshape(-1), pk.reshape(-1)) and torch.equal(n1.view(torch.int16).reshape(-1),
+                                                                             nm.view(torch.int16).reshape(-1)), s
+        items.append((pk.reshape(s[0], -1), nm, s[0], s[1]))
+    say("trit G=64 dequantize_many")
+    outs = cq.dequantize_many(items, T, lv, group_size=64)
+    for (pk, nm, rows, cols), out in zip(items, outs):
+        assert torch.equal(cq.dequantize(pk, nm, rows, cols, T, lv, group_size=64), out)

@@ -76,6 +76,20 @@ def test_trit_group_sizes():
     assert O.blob_offsets(shapes, O.TERNARY_TRITS)[2] == groups * 28
 
 
+def test_blob_pad_after_odd_trit_section(oracle_levels):
+    """Trit storage at g = 64 (13-byte groups): a zero 1 x 64 tensor gives
+    index 1 everywhere (the ternary thresholds straddle 0), so 12 bytes of
+    1+3+9+27+81 = 121 and a 13th of 1+3+9+27 = 40; one zero pad byte follows
+    the odd index section and the norm (0) starts at offset 14."""
+    q = O.quantize(np.zeros((1, 64)), O.TERNARY_TRITS, oracle_levels[O.TERNARY], 64)
+    blob = O.serialize([q])
+    assert blob.tolist() == [121] * 12 + [40] + [0] + [0, 0]
+    assert O.blob_offsets([(1, 64)], O.TERNARY_TRITS, 64) == ([0], [14], 16)
+    # an even index section gets no pad
+    assert O.blob_offsets([(2, 64)], O.TERNARY_TRITS, 64) == ([0], [26], 30)
+    assert O.model_bytes([(1, 64)], O.TERNARY_TRITS, 64) == 15  # the pad is not storage
+
+
 def test_trit_round_trip_and_consistency(oracle_levels):
     rng = np.random.default_rng(9)
     idx = rng.integers(0, 3, (50, 128))
