@@ -45,8 +45,8 @@
  *     otherwise.
  *   - group_size: the device calls take 32, 64, 128 or 256 ("Cactus Quants
  *     CQ2-bit Quantization: Extreme Compression for Edge LLMs", FAQ on group
- *     size), except trit storage and cq_repack (128 only); the GEMM calls
- *     also need k to be a multiple of 128 (of 256 at group size 256).
+ *     size); the GEMM calls also need k to be a multiple of 128 (of 256 at
+ *     group size 256).
  *     Host-only calls take any power of two from 8 to 4096 (so a group's
  *     packed indices fill whole bytes).
  *   - Device calls validate every argument first, then enqueue their kernels
@@ -57,8 +57,8 @@
  *   - rows*cols == 0 (or n_out == 0) is a successful no-op; a product with
  *     k == 0 writes zeros to y (an empty sum).
  *   - Alignment: w, out, packed, x, y must be 16-byte aligned; norms 2-byte;
- *     packed at group sizes other than 128 4-byte, in trit storage
- *     (CQ_TERNARY_TRITS) 2-byte.
+ *     packed at group sizes other than 128 4-byte; packed in trit storage
+ *     (CQ_TERNARY_TRITS) 2-byte at group size 128, any at the others.
  *   - Inputs and outputs must not overlap (cq_fake_quant allows out == w).
  *     Non-finite inputs give unspecified but deterministic results.
  *   - Return value: CQ_OK (0) or a negative cq_status.  cq_last_error()
@@ -90,11 +90,11 @@ typedef enum { CQ_F32 = 0, CQ_BF16 = 1 } cq_dtype;
  * ("How Quantization Codebooks Are Trained in Cactus Quants", section Ternary
  * Special Case Handling). */
 #define CQ_TERNARY 158
-/* The same three-level code stored five indices per byte: 26 bytes per
- * 128-group, 1.625 bits per weight before the norm (the 2-bit field form
- * takes 32 bytes).  Accepted by the host calls, cq_quantize(_many),
- * cq_dequantize(_many) and cq_fake_quant; the product calls decode the
- * field form (convert with cq_repack). */
+/* The same three-level code stored five indices per byte: ceil(G/5) bytes
+ * per group, 26 per 128-group, 1.625 bits per weight before the norm (the
+ * 2-bit field form takes 32 bytes).  Accepted by the host calls,
+ * cq_quantize(_many), cq_dequantize(_many) and cq_fake_quant at every group
+ * size; the product calls decode the field form (convert with cq_repack). */
 #define CQ_TERNARY_TRITS 159
 #define CQ_GROUP 128
 #define CQ_MAX_LEVELS 16
@@ -301,12 +301,14 @@ int cq_dequant_gemm_many(int n, const cq_matvec_desc* descs, int bits, int group
                          const float* levels, int n_levels, int64_t batch, void* stream);
 
 /* Converts n_groups groups of three-level indices between the 2-bit field
- * form (CQ_TERNARY, 32 bytes per group, 16-byte aligned) and trit storage
- * (CQ_TERNARY_TRITS, 26 bytes per group, 2-byte aligned), in either
- * direction (src_bits -> dst_bits; any other pair is CQ_ERR_ARG).
- * group_size must be 128.  Lossless for indices 0..2; a field holding 3 or a
- * trit byte above 242 (neither is ever written by cq_quantize) converts to
- * unspecified in-range values.  src and dst must not overlap. */
+ * form (CQ_TERNARY, G/4 bytes per group: 32 at G = 128, 16-byte aligned;
+ * 4-byte aligned at other G) and trit storage (CQ_TERNARY_TRITS, ceil(G/5)
+ * bytes per group: 26 at G = 128, 2-byte aligned; any alignment at other
+ * G), in either direction (src_bits -> dst_bits; any other pair is
+ * CQ_ERR_ARG), for group_size 32, 64, 128 or 256.  Lossless for indices
+ * 0..2; a field holding 3 or a trit byte above 242 (neither is ever written
+ * by cq_quantize) converts to unspecified in-range values.  src and dst must
+ * not overlap. */
 int cq_repack(const uint8_t* src, int src_bits, uint8_t* dst, int dst_bits, int64_t n_groups,
               int group_size, void* stream);
 
