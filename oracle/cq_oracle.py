@@ -2,7 +2,8 @@
 
 TEST INFRASTRUCTURE ONLY.  This module is the plain, slow reference the HIP
 library is checked against.  Only ``tests/``, ``__graft_entry__.smoke()`` and
-the ``cpu_baseline`` leg of ``bench.py`` may import it; the product path
+the CPU baseline legs of ``bench.py`` (``cpu_baseline``,
+``cpu_baseline_configs``) may import it; the product path
 (``rotated_codebook_bit_amd``) never does, and this module imports nothing from
 the product path.  It shares no code, table or constant generator with the
 HIP library.
