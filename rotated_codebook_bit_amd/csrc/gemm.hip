@@ -215,10 +215,11 @@ __device__ __forceinline__ void fill_table(uint32_t* tab, const SplitLevels& s, 
   if (t >= Table<SB>::entries) return;
   if constexpr (SB == 2) {
     const int c0 = t & 3, c1 = (t >> 2) & 3, c2 = (t >> 4) & 3, c3 = t >> 6;
-    tab[4 * t] = split_at(s, c0, false) | (split_at(s, c1, false) << 16);
-    tab[4 * t + 1] = split_at(s, c2, false) | (split_at(s, c3, false) << 16);
-    tab[4 * t + 2] = split_at(s, c0, true) | (split_at(s, c1, true) << 16);
-    tab[4 * t + 3] = split_at(s, c2, true) | (split_at(s, c3, true) << 16);
+    // hi pairs in the first 512 words, lo pairs in the next 512
+    tab[2 * t] = split_at(s, c0, false) | (split_at(s, c1, false) << 16);
+    tab[2 * t + 1] = split_at(s, c2, false) | (split_at(s, c3, false) << 16);
+    tab[512 + 2 * t] = split_at(s, c0, true) | (split_at(s, c1, true) << 16);
+    tab[512 + 2 * t + 1] = split_at(s, c2, true) | (split_at(s, c3, true) << 16);
   } else {
     const int c0 = SB == 4 ? (t & 15) : (t & 7), c1 = SB == 4 ? (t >> 4) : (t >> 3);
     tab[2 * t] = split_at(s, c0, false) | (split_at(s, c1, false) << 16);
@@ -252,11 +253,14 @@ __device__ __forceinline__ void decode(const Codes<SB>& c, int s, int h, const u
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   u32x4 H, L;
   if constexpr (SB == 2) {
+    // Two 8-byte reads per operand, straight into its register quadruple.
     const uint32_t pair = (c.w[s] >> (16 * h)) & 0xFFFFu;
-    const uint4 e0 = reinterpret_cast<const uint4*>(tab)[pair & 0xFFu];
-    const uint4 e1 = reinterpret_cast<const uint4*>(tab)[pair >> 8];
-    H = u32x4{e0.x, e0.y, e1.x, e1.y};
-    L = u32x4{e0.z, e0.w, e1.z, e1.w};
+    const uint2 h0 = reinterpret_cast<const uint2*>(tab)[pair & 0xFFu];
+    const uint2 h1 = reinterpret_cast<const uint2*>(tab)[pair >> 8];
+    const uint2 l0 = reinterpret_cast<const uint2*>(tab + 512)[pair & 0xFFu];
+    const uint2 l1 = reinterpret_cast<const uint2*>(tab + 512)[pair >> 8];
+    H = u32x4{h0.x, h0.y, h1.x, h1.y};
+    L = u32x4{l0.x, l0.y, l1.x, l1.y};
   } else if constexpr (SB == 4) {
     const uint32_t q = h ? c.w[2 * s + 1] : c.w[2 * s];
     const uint2 e0 = reinterpret_cast<const uint2*>(tab)[q & 0xFFu];
