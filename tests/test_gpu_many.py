@@ -102,6 +102,32 @@ def test_dequantize_many_needle2(levels):
 
 
 @pytest.mark.parametrize("bits", ALL_BITS)
+def test_quantize_many_batch_tails(bits, levels):
+    """Tensors whose full 64-group batches are not a multiple of 32 (the
+    quantize kernel takes full batches 32 at a time and the rest one by one),
+    with partial last batches, in one bf16 call: per-tensor oracle parity and
+    bit-identity with the single-tensor call."""
+    lv = levels[bits]
+    shapes = [(6637, 128), (2213, 384), (4096, 512), (700, 1024), (64 * 33 + 1, 128)]
+    rng = np.random.default_rng(zlib.crc32(repr(("tails", bits)).encode()))
+    hb = [W.f32_to_bf16_bits((rng.standard_normal(sh) * 0.02).astype(np.float32)) for sh in shapes]
+    ws = [torch.from_numpy(b.view(np.int16)).to(DEV).view(torch.bfloat16) for b in hb]
+    say(f"quantize_many tails bits={bits}: {shapes}")
+    blob, views = cq.quantize_many(ws, bits, lv)
+    mism = elems = 0
+    for sh, b, w, (pk, nm) in zip(shapes, hb, ws, views):
+        q = O.quantize(W.bf16_bits_to_f32(b).astype(np.float64), bits, lv)
+        packed, norms = host(pk), f16_bits(nm)
+        rep = check_quantize(packed, norms, q, enforce_count=False)
+        mism += rep["index_mismatches"]
+        elems += rep["elements"]
+        p1, n1 = cq.quantize(w, bits, lv)
+        assert np.array_equal(host(p1), packed) and np.array_equal(f16_bits(n1), norms), sh
+    say(f"quantize_many tails bits={bits}: {mism} in-band mismatches in {elems} elements")
+    check_count(mism, elems)
+
+
+@pytest.mark.parametrize("bits", ALL_BITS)
 def test_many_small_mixed(bits, levels):
     """Many small tensors of mixed shapes (multiples of 128 and ragged,
     empty, 3-D) in one call, bf16: bit-identical to the single-tensor calls,

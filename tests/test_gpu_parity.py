@@ -101,7 +101,9 @@ def test_small_matrix_2bit(levels):
 
 @pytest.mark.parametrize("bits", ALL_BITS)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("shape", [(1000, 384), (77, 1000), (3, 1, 130), (1, 128), (1, 1)])
+# (6637, 128): 103 full 64-group batches and a 45-group tail, i.e. three
+# 32-batch super-batches, seven more full batches and a partial one.
+@pytest.mark.parametrize("shape", [(1000, 384), (6637, 128), (77, 1000), (3, 1, 130), (1, 128), (1, 1)])
 def test_bits_dtypes_shapes(bits, dtype, shape, levels):
     rng = np.random.default_rng(zlib.crc32(repr((bits, dtype, shape)).encode()))
     w = (rng.standard_normal(shape) * 0.02).astype(np.float32)
