@@ -234,8 +234,9 @@ struct MatvecDesc {
 
 // Descriptors are written to device memory by a small kernel that receives
 // them as kernel arguments, kDescPerInit at a time (no host-to-device copy,
-// so the call stays asynchronous).
-constexpr int kDescPerInit = 24;
+// so the call stays asynchronous).  A chunk is 80 kDescPerInit + 40 bytes:
+// 48 keeps it under 4 KiB of kernel arguments (5 launches for 225 matrices).
+constexpr int kDescPerInit = 48;
 struct DescChunk {
   MatvecDesc d[kDescPerInit];
   int64_t gstart[kDescPerInit + 1];   // rotate-kernel group prefix
@@ -245,6 +246,7 @@ struct DescChunk {
   int first;                          // index of d[0] in the table
   int last_chunk;                     // 1: also write the sentinel entries [count]
 };
+static_assert(sizeof(DescChunk) <= 4096, "kernel arguments stay within 4 KiB");
 
 hipError_t launch_table_init(const DescChunk& c, MatvecDesc* table, int64_t* gstart,
                              int64_t* bstart0, int64_t* bstart1, hipStream_t stream);

@@ -8,12 +8,13 @@
 namespace cq {
 namespace {
 
-constexpr int kUploadWords = 768;  // 3 KiB per launch (the argument block holds 4 KiB)
+constexpr int kUploadWords = 1016;  // 4,064 bytes per launch (the argument block holds 4 KiB)
 
 struct UploadChunk {
   uint32_t w[kUploadWords];
   uint32_t n_words;
 };
+static_assert(sizeof(UploadChunk) <= 4096, "kernel arguments stay within 4 KiB");
 
 __global__ void __launch_bounds__(256) upload_kernel(UploadChunk c, uint32_t* __restrict__ dst) {
   for (uint32_t i = threadIdx.x; i < c.n_words; i += blockDim.x) dst[i] = c.w[i];
