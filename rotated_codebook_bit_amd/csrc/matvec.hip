@@ -407,9 +407,12 @@ matvec_pair_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restri
                                 : make_float2(0.0f, 0.0f);
     const int coff = active ? static_cast<int>(c0 / 4) : (1 << 30);
     const int noff = active ? static_cast<int>(2 * (c0 >> log2g)) : (1 << 30);
+    // The codes are read once: loaded non-temporal (aux bit nt), they leave
+    // the L2 to the activations every row block re-reads (4.6% faster on the
+    // 225-matrix pass; nt on the norms as well was 3% slower).
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
-      t.codes[r] = __builtin_amdgcn_raw_buffer_load_b32(codes_src, coff, soff_c[r], 0);
+      t.codes[r] = __builtin_amdgcn_raw_buffer_load_b32(codes_src, coff, soff_c[r], 2);
       t.norm[r] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(norms_src, noff, soff_n[r], 0));
     }
   };
