@@ -206,12 +206,16 @@ struct Levels {
 // Table copies for a batch chunk of NB rows.
 constexpr int table_copies(int nb) { return nb >= 4 ? 8 : 1; }
 
-// RB rows x NB batch rows per block; RB * NB <= 32 keeps the accumulators
-// and the activations of a chunk (16 * NB) in registers.
+// rg groups of RB rows x NB batch rows per block; RB * NB <= 32 keeps the
+// accumulators and the activations of a chunk (16 * NB) in registers.  The
+// groups of a block run one after the other, each with its own block
+// reduction.  When the matrix fits one pass (k <= kPass) the thread's
+// activations are loaded once for all rg groups: at batch 8 they are 8 bytes
+// of L2 traffic per weight, which a 4-row block re-read for every 4 rows.
 template <int SB, int NB, int RB>
 __global__ void __launch_bounds__(kBlock)
 matvec_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restrict__ bstart, int n,
-              LevelTable lv, const float* __restrict__ xr, int64_t b0, int log2g) {
+              LevelTable lv, const float* __restrict__ xr, int64_t b0, int log2g, int rg) {
   using Lv = Levels<SB, table_copies(NB)>;
   __shared__ __attribute__((aligned(16))) float tab[Lv::floats];
   __shared__ float red[RB * NB][kBlock + 1];
@@ -226,86 +230,97 @@ matvec_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restrict__ 
     const int d = find_desc(bstart, n, blk);
     const MatvecDesc& m = table[d];
     const int64_t n_out = m.n_out, k = m.k;
-    const int64_t row0 = (blk - bstart[d]) * RB;
+    const int64_t row_base = (blk - bstart[d]) * RB * rg;
     const int64_t row_bytes = k * SB / 8;
     const int64_t ngr = k >> log2g;
     const float inv_g = 1.0f / static_cast<float>(1 << log2g);  // exact: a power of two
     const float* x_rot = xr + m.xr_offset;
+    const bool one_pass = k <= kPass;
 
-    float acc[RB][NB];
+    float xv[NB][16];
+    auto load_x = [&](int64_t c0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < RB; ++r)
+      for (int b = 0; b < NB; ++b) {
+        const float4* src = reinterpret_cast<const float4*>(x_rot + (b0 + b) * k + c0);
 #pragma unroll
-      for (int b = 0; b < NB; ++b) acc[r][b] = 0.0f;
-
-    for (int64_t p0 = 0; p0 < k; p0 += kPass) {
-      const int64_t c0 = p0 + kChunk * t;
-      if (c0 < k) {
-        float xv[NB][16];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const float4* src = reinterpret_cast<const float4*>(x_rot + (b0 + b) * k + c0);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float4 v = src[i];
-            xv[b][4 * i] = v.x;
-            xv[b][4 * i + 1] = v.y;
-            xv[b][4 * i + 2] = v.z;
-            xv[b][4 * i + 3] = v.w;
-          }
-        }
-        // All rows' codes and norms are loaded before any is used, so a
-        // thread keeps RB loads in flight.  Rows past the end re-read the
-        // last row; their sums are never stored.
-        uint64_t codes[RB];
-        float scale[RB];
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-          const int64_t row = row0 + r < n_out ? row0 + r : n_out - 1;
-          codes[r] = load_codes16<SB>(m.packed + row * row_bytes, c0);
-          scale[r] = half_to_float(m.norms[row * ngr + (c0 >> log2g)]) * inv_g;
-        }
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-          float v[16];
-          Lv::decode(codes[r], tab, t % table_copies(NB), v);
-          float part[NB];
-#pragma unroll
-          for (int b = 0; b < NB; ++b) part[b] = 0.0f;
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-#pragma unroll
-            for (int b = 0; b < NB; ++b) part[b] = __builtin_fmaf(v[e], xv[b][e], part[b]);
-#pragma unroll
-          for (int b = 0; b < NB; ++b) acc[r][b] = __builtin_fmaf(scale[r], part[b], acc[r][b]);
+        for (int i = 0; i < 4; ++i) {
+          const float4 v = src[i];
+          xv[b][4 * i] = v.x;
+          xv[b][4 * i + 1] = v.y;
+          xv[b][4 * i + 2] = v.z;
+          xv[b][4 * i + 3] = v.w;
         }
       }
-    }
+    };
+    if (one_pass && kChunk * t < k) load_x(kChunk * t);
 
-    // Block reduction in a fixed order: thread t's partials go to column t
-    // of `red`; thread t then sums value t / 8 over columns 32*(t%8) ..
-    // 32*(t%8)+31 and the 8 threads of a value combine by shuffles.
+    for (int g = 0; g < rg; ++g) {
+      const int64_t row0 = row_base + static_cast<int64_t>(g) * RB;
+      if (row0 >= n_out) break;  // the same for every thread of the block
+
+      float acc[RB][NB];
 #pragma unroll
-    for (int r = 0; r < RB; ++r)
+      for (int r = 0; r < RB; ++r)
 #pragma unroll
-      for (int b = 0; b < NB; ++b) red[r * NB + b][t] = acc[r][b];
-    __syncthreads();
-    constexpr int V = RB * NB;  // values to reduce (<= 32)
-    const int vi = t / 8, part = t % 8;
-    float s = 0.0f;
-    if (vi < V) {
+        for (int b = 0; b < NB; ++b) acc[r][b] = 0.0f;
+
+      for (int64_t p0 = 0; p0 < k; p0 += kPass) {
+        const int64_t c0 = p0 + kChunk * t;
+        if (c0 < k) {
+          if (!one_pass) load_x(c0);
+          // All rows' codes and norms are loaded before any is used, so a
+          // thread keeps RB loads in flight.  Rows past the end re-read the
+          // last row; their sums are never stored.
+          uint64_t codes[RB];
+          float scale[RB];
+#pragma unroll
+          for (int r = 0; r < RB; ++r) {
+            const int64_t row = row0 + r < n_out ? row0 + r : n_out - 1;
+            codes[r] = load_codes16<SB>(m.packed + row * row_bytes, c0);
+            scale[r] = half_to_float(m.norms[row * ngr + (c0 >> log2g)]) * inv_g;
+          }
+#pragma unroll
+          for (int r = 0; r < RB; ++r) {
+            float v[16];
+            Lv::decode(codes[r], tab, t % table_copies(NB), v);
+            float part[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) part[b] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+#pragma unroll
+              for (int b = 0; b < NB; ++b) part[b] = __builtin_fmaf(v[e], xv[b][e], part[b]);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[r][b] = __builtin_fmaf(scale[r], part[b], acc[r][b]);
+          }
+        }
+      }
+
+      // Block reduction in a fixed order: thread t's partials go to column t
+      // of `red`; thread t then sums value t / 8 over columns 32*(t%8) ..
+      // 32*(t%8)+31 and the 8 threads of a value combine by shuffles.
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) red[r * NB + b][t] = acc[r][b];
+      __syncthreads();
+      constexpr int V = RB * NB;  // values to reduce (<= 32)
+      const int vi = t / 8, part = t % 8;
+      float s = 0.0f;
+      if (vi < V) {
 #pragma unroll 8
-      for (int i = 0; i < 32; ++i) s += red[vi][32 * part + i];
+        for (int i = 0; i < 32; ++i) s += red[vi][32 * part + i];
+      }
+      s += __shfl_xor(s, 1, kWave);
+      s += __shfl_xor(s, 2, kWave);
+      s += __shfl_xor(s, 4, kWave);
+      if (vi < V && part == 0) {
+        const int r = vi / NB, b = vi % NB;
+        const int64_t row = row0 + r;
+        if (row < n_out) m.y[(b0 + b) * n_out + row] = s;
+      }
+      __syncthreads();  // `red` is rewritten by the next row group
     }
-    s += __shfl_xor(s, 1, kWave);
-    s += __shfl_xor(s, 2, kWave);
-    s += __shfl_xor(s, 4, kWave);
-    if (vi < V && part == 0) {
-      const int r = vi / NB, b = vi % NB;
-      const int64_t row = row0 + r;
-      if (row < n_out) m.y[(b0 + b) * n_out + row] = s;
-    }
-    __syncthreads();  // `red` is rewritten by the next row block
   }
 }
 
@@ -516,6 +531,9 @@ constexpr int rows_per_block(int nb) {
   return nb <= 1 ? 16 : 32 / (nb <= 2 ? 2 : nb <= 4 ? 4 : 8);
 }
 
+// Most row groups per block of the byte-table kernel.
+constexpr int kMaxRowGroups = 8;
+
 // 2-bit codes with one batch row take the pair-table kernel when a wave's 16
 // rows of codes (4 k bytes) fit its 32-bit buffer range.
 constexpr int64_t kPairMaxK = int64_t(1) << 28;
@@ -523,27 +541,28 @@ constexpr bool use_pairs(int sb, int nb, int64_t max_k) { return sb == 2 && nb =
 
 template <int SB, int NB>
 hipError_t launch_nb(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks,
-                     const LevelTable& lv, const float* xr, int64_t b0, int log2g, hipStream_t s) {
+                     const LevelTable& lv, const float* xr, int64_t b0, int log2g, int rg, hipStream_t s) {
   constexpr int RB = rows_per_block(NB);
   // One block per row block: the blocks are short, and letting the hardware
   // refill free slots measured faster than a resident grid that loops.
   hipLaunchKernelGGL((matvec_kernel<SB, NB, RB>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
-                     s, table, bstart, n, lv, xr, b0, log2g);
+                     s, table, bstart, n, lv, xr, b0, log2g, rg);
   return hipGetLastError();
 }
 
 template <int SB>
 hipError_t launch_sb(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks,
-                     const LevelTable& lv, const float* xr, int64_t b0, int nb, int log2g, hipStream_t s) {
+                     const LevelTable& lv, const float* xr, int64_t b0, int nb, int log2g, int rg,
+                     hipStream_t s) {
   switch (nb) {
-    case 1: return launch_nb<SB, 1>(table, bstart, n, blocks, lv, xr, b0, log2g, s);
-    case 2: return launch_nb<SB, 2>(table, bstart, n, blocks, lv, xr, b0, log2g, s);
-    case 3: return launch_nb<SB, 3>(table, bstart, n, blocks, lv, xr, b0, log2g, s);
-    case 4: return launch_nb<SB, 4>(table, bstart, n, blocks, lv, xr, b0, log2g, s);
-    case 5: return launch_nb<SB, 5>(table, bstart, n, blocks, lv, xr, b0, log2g, s);
-    case 6: return launch_nb<SB, 6>(table, bstart, n, blocks, lv, xr, b0, log2g, s);
-    case 7: return launch_nb<SB, 7>(table, bstart, n, blocks, lv, xr, b0, log2g, s);
-    default: return launch_nb<SB, 8>(table, bstart, n, blocks, lv, xr, b0, log2g, s);
+    case 1: return launch_nb<SB, 1>(table, bstart, n, blocks, lv, xr, b0, log2g, rg, s);
+    case 2: return launch_nb<SB, 2>(table, bstart, n, blocks, lv, xr, b0, log2g, rg, s);
+    case 3: return launch_nb<SB, 3>(table, bstart, n, blocks, lv, xr, b0, log2g, rg, s);
+    case 4: return launch_nb<SB, 4>(table, bstart, n, blocks, lv, xr, b0, log2g, rg, s);
+    case 5: return launch_nb<SB, 5>(table, bstart, n, blocks, lv, xr, b0, log2g, rg, s);
+    case 6: return launch_nb<SB, 6>(table, bstart, n, blocks, lv, xr, b0, log2g, rg, s);
+    case 7: return launch_nb<SB, 7>(table, bstart, n, blocks, lv, xr, b0, log2g, rg, s);
+    default: return launch_nb<SB, 8>(table, bstart, n, blocks, lv, xr, b0, log2g, rg, s);
   }
 }
 
@@ -562,7 +581,17 @@ constexpr int log2_group(int g) { return g == 32 ? 5 : g == 64 ? 6 : g == 256 ? 
 MatvecPlan matvec_plan(int sbits, int nb, const MatvecDesc* descs, int n) {
   int64_t max_k = 0;
   for (int i = 0; i < n; ++i) max_k = descs[i].k > max_k ? descs[i].k : max_k;
-  if (!km::use_pairs(sbits, nb, max_k)) return MatvecPlan{km::rows_per_block(nb), 0};
+  if (!km::use_pairs(sbits, nb, max_k)) {
+    // Byte-table kernel: the most row groups per block (8, 4, 2) that still
+    // give every CU two blocks.
+    const int rb = km::rows_per_block(nb);
+    for (int rg = km::kMaxRowGroups; rg > 1; rg /= 2) {
+      int64_t blocks = 0;
+      for (int i = 0; i < n; ++i) blocks += (descs[i].n_out + rb * rg - 1) / (rb * rg);
+      if (blocks >= 2 * static_cast<int64_t>(device_cu_count())) return MatvecPlan{rb * rg, 0};
+    }
+    return MatvecPlan{rb, 0};
+  }
   constexpr int many = km::kPairWaves * km::kPairRowsPerWave;
   int64_t blocks = 0;
   for (int i = 0; i < n; ++i) blocks += (descs[i].n_out + many - 1) / many;
@@ -608,11 +637,14 @@ hipError_t launch_matvec(const MatvecDesc* table, const int64_t* bstart, int n, 
                        n, lv, xr, b0, log2g);
     return hipGetLastError();
   }
-  if (plan.pair_rows_per_wave != 0 || plan.rows_per_block != km::rows_per_block(nb)) return hipErrorInvalidValue;
+  const int rb = km::rows_per_block(nb);
+  const int rg = plan.rows_per_block / rb;
+  if (plan.pair_rows_per_wave != 0 || plan.rows_per_block % rb || rg < 1 || rg > km::kMaxRowGroups)
+    return hipErrorInvalidValue;
   switch (sbits) {
-    case 2: return km::launch_sb<2>(table, bstart, n, blocks, lv, xr, b0, nb, log2g, stream);
-    case 3: return km::launch_sb<3>(table, bstart, n, blocks, lv, xr, b0, nb, log2g, stream);
-    case 4: return km::launch_sb<4>(table, bstart, n, blocks, lv, xr, b0, nb, log2g, stream);
+    case 2: return km::launch_sb<2>(table, bstart, n, blocks, lv, xr, b0, nb, log2g, rg, stream);
+    case 3: return km::launch_sb<3>(table, bstart, n, blocks, lv, xr, b0, nb, log2g, rg, stream);
+    case 4: return km::launch_sb<4>(table, bstart, n, blocks, lv, xr, b0, nb, log2g, rg, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -357,6 +357,32 @@ def test_matvec_many(batch, levels):
             check_matvec(y, x.astype(np.float64) @ w_hat.T, x, w_hat)
 
 
+@pytest.mark.parametrize("bits,batch", [(2, 8), (2, 3), (3, 5), (4, 8), (O.TERNARY, 2), (4, 12)])
+def test_matvec_row_groups(bits, batch, levels):
+    """Calls with enough rows that the byte-table kernel gives each block
+    several groups of rows: a 16401-row single-pass matrix (its last block
+    holds a one-row group), a matrix whose k spans three passes, and a small
+    one; the batches give blocks of 8, 4 and 2 groups of 4, 8 and 16 rows."""
+    lv = levels[bits]
+    shapes = [(16401, 256), (100, 8320), (37, 384)]
+    rng = np.random.default_rng(zlib.crc32(repr(("row_groups", bits, batch)).encode()))
+    items, refs = [], []
+    for n_out, k in shapes:
+        w = rng.standard_normal((n_out, k)) * 0.02
+        q = O.quantize(w, bits, lv)
+        x = rng.standard_normal((batch, k)).astype(np.float32)
+        w_hat = O.dequantize(q.packed, q.norm16, n_out, k, bits, lv)
+        p_dev = torch.from_numpy(q.packed.reshape(n_out, -1)).to(DEV)
+        n_dev = torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16)
+        y = torch.full((batch, n_out), float("nan"), dtype=torch.float32, device=DEV)
+        items.append((p_dev, n_dev, n_out, k, to_dev_f32(x), y))
+        refs.append((x, w_hat))
+    say(f"matvec row groups bits={bits} batch={batch}")
+    cq.dequant_matvec_many(items, bits, lv, batch)
+    for (x, w_hat), it in zip(refs, items):
+        check_matvec(host(it[5]), x.astype(np.float64) @ w_hat.T, x, w_hat)
+
+
 def test_matvec_many_large_call(levels):
     """Batch 1 over 40 matrices of 2048 rows: enough row blocks for the
     pair-table kernel's 128-row blocks (a single matrix takes 16-row ones),
