@@ -29,6 +29,11 @@ constexpr int kBlock = kWaves * kWave;
 // Resident blocks per CU for the bf16-output grid: one measured faster than
 // two for this store-heavy kernel.
 constexpr int kBlocksPerCu = 1;
+// Waves per block of dequantize_contig: eight for float32 output (1.6%
+// faster on the 7B-shaped model than four; at 201 VGPRs a CU holds eight
+// waves either way), four for bf16 output, whose resident grid ran 28% slower
+// with eight.
+constexpr int contig_waves(bool bf16_out) { return bf16_out ? kWaves : 2 * kWaves; }
 
 __device__ __forceinline__ void butterfly(float (&y)[kGroup]) {
 #pragma unroll
@@ -295,8 +300,9 @@ __device__ __forceinline__ DBatch resolve(const DequantJob& j, int64_t b, int& d
 // TRITS (with SB = 2): the packed input is trit storage, converted to 2-bit
 // fields in registers.
 template <int SB, bool BF16OUT, bool MANY, bool TRITS = false>
-__global__ void __launch_bounds__(kBlock, 2)
+__global__ void __launch_bounds__(contig_waves(BF16OUT) * kWave, 2)
 dequantize_contig(DequantJob job, LevelTable lv) {
+  constexpr int W = contig_waves(BF16OUT);
   constexpr int OB = BF16OUT ? 2 : 4;        // output bytes per element
   constexpr int GOB = kGroup * OB;           // output bytes per group
   constexpr int PB = 32 * OB;                // bytes per group per phase
@@ -306,7 +312,7 @@ dequantize_contig(DequantJob job, LevelTable lv) {
   constexpr int WAVE_BYTES = kWave * PB;
   constexpr int NI = WAVE_BYTES / 1024;      // store instructions per phase
   __shared__ __attribute__((aligned(16))) float tab[TableSize<SB>::floats];
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * WAVE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[W * WAVE_BYTES];
   __shared__ uint16_t ttab[TRITS ? 256 : 1];
   if constexpr (TRITS) fill_trit_table(ttab, threadIdx.x);
   fill_table<SB>(tab, lv, threadIdx.x);
@@ -316,8 +322,8 @@ dequantize_contig(DequantJob job, LevelTable lv) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   uint8_t* const buf = lds + wave * WAVE_BYTES;
   const int64_t n_batches = job.n_batches;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
-  int64_t batch = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * W;
+  int64_t batch = static_cast<int64_t>(blockIdx.x) * W + wave;
   if (batch >= n_batches) return;
   int d = 0;
 
@@ -455,8 +461,9 @@ dequantize_ragged(const uint8_t* __restrict__ packed, const uint16_t* __restrict
 // batches (the covering grid measured 8% slower there).
 template <bool BF16OUT>
 int dequant_blocks(int64_t n_batches) {
-  return BF16OUT ? persistent_blocks((n_batches + kWaves - 1) / kWaves, kBlocksPerCu)
-                 : spread_blocks(n_batches, kWaves, 1, kBlocksPerCu);
+  constexpr int W = contig_waves(BF16OUT);
+  return BF16OUT ? persistent_blocks((n_batches + W - 1) / W, kBlocksPerCu)
+                 : spread_blocks(n_batches, W, 1, kBlocksPerCu);
 }
 
 template <int SB, bool BF16OUT, bool TRITS>
@@ -469,8 +476,8 @@ hipError_t launch_sb(const uint8_t* packed, const uint16_t* norms, int64_t rows,
     const int blocks = dequant_blocks<BF16OUT>(n_batches);
     const DequantJob job{packed, norms, ob, n_groups, TensorTable<DequantDesc>{nullptr, nullptr, 0},
                          n_batches};
-    hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT, false, TRITS>), dim3(blocks), dim3(kBlock), 0, s, job,
-                       lv);
+    hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT, false, TRITS>), dim3(blocks),
+                       dim3(contig_waves(BF16OUT) * kWave), 0, s, job, lv);
   } else {
     const int64_t n_groups = rows * ((cols + kGroup - 1) / kGroup);
     const int blocks = static_cast<int>((n_groups + kBlock - 1) / kBlock);
@@ -487,8 +494,8 @@ hipError_t launch_many_sb(const LevelTable& lv, TensorTable<DequantDesc> contig,
   if (contig_batches > 0) {
     const int blocks = dequant_blocks<BF16OUT>(contig_batches);
     const DequantJob job{nullptr, nullptr, nullptr, 0, contig, contig_batches};
-    hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT, true, TRITS>), dim3(blocks), dim3(kBlock), 0, s, job,
-                       lv);
+    hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT, true, TRITS>), dim3(blocks),
+                       dim3(contig_waves(BF16OUT) * kWave), 0, s, job, lv);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
