@@ -413,6 +413,15 @@ __device__ __forceinline__ QBatch resolve(const QuantJob& j, int64_t b, int& d) 
 // float32 input (128 KiB).
 constexpr int blocks_per_cu(bool bf16_in) { return bf16_in ? kBlocksPerCu : 1; }
 
+// Waves per block of the contiguous kernels (7B-shaped model, ms at 4 / 2 /
+// 1 waves per block): quantize from bf16 2.69 / 2.76 / 2.82, from float32
+// 5.15 / 4.98 / 5.35; fake quant bf16 -> bf16 5.21 / 5.10 / 4.93.
+constexpr int quant_waves(bool bf16_in) { return bf16_in ? kWaves : kWaves / 2; }
+constexpr int fake_waves() { return 1; }
+// The smallest grid a mid-size tensor gets, in blocks of w waves: as many
+// waves per CU as blocks_per_cu blocks of kWaves waves.
+constexpr int floor_blocks_per_cu(bool bf16_in, int w) { return blocks_per_cu(bf16_in) * kWaves / w; }
+
 // Batches per wave of the grid.  A grid of about four batches per wave
 // (each wave strides by the grid) measured 4-7% faster on the 7B-shaped
 // model than a resident grid of blocks_per_cu blocks per CU that loops over
@@ -421,20 +430,21 @@ constexpr int blocks_per_cu(bool bf16_in) { return bf16_in ? kBlocksPerCu : 1; }
 constexpr int kBatchesPerWave = 4;
 
 template <int L, bool BF16, bool MANY, bool TRITS = false>
-__global__ void __launch_bounds__(kBlock, blocks_per_cu(BF16))
+__global__ void __launch_bounds__(quant_waves(BF16) * kWave, blocks_per_cu(BF16))
 quantize_contig(QuantJob job, QuantParams p) {
+  constexpr int W = quant_waves(BF16);
   constexpr int GB = BF16 ? 256 : 512;  // input bytes per group
   constexpr int CPG = GB / 16;          // 16-byte chunks per group
   constexpr int WAVE_BYTES = kWave * GB;
   constexpr int NI = WAVE_BYTES / 1024;  // 1 KiB load instructions per batch
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * WAVE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[W * WAVE_BYTES];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   uint8_t* const buf = lds + wave * WAVE_BYTES;
   const int64_t n_batches = job.n_batches;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
-  int64_t batch = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * W;
+  int64_t batch = static_cast<int64_t>(blockIdx.x) * W + wave;
   if (batch >= n_batches) return;
   int d = 0;
 
@@ -684,9 +694,10 @@ __device__ __forceinline__ float stage1_group(const uint32_t (&raw)[BF16 ? 64 : 
 // buffer in phases of 32 bytes per group so that consecutive lanes store
 // consecutive bytes.
 template <int L, bool BF16IN, bool BF16OUT>
-__global__ void __launch_bounds__(kBlock, blocks_per_cu(BF16IN))
+__global__ void __launch_bounds__(fake_waves() * kWave, blocks_per_cu(BF16IN))
 fakequant_contig(const uint8_t* __restrict__ w, int64_t n_groups, QuantParams p, LevelTable lv,
                  uint8_t* __restrict__ out) {
+  constexpr int W = fake_waves();
   constexpr int GB = BF16IN ? 256 : 512;  // input bytes per group
   constexpr int CPG = GB / 16;
   constexpr int WAVE_BYTES = kWave * GB;
@@ -703,8 +714,8 @@ fakequant_contig(const uint8_t* __restrict__ w, int64_t n_groups, QuantParams p,
   constexpr int GPO = kWave / CPP;        // groups per store instruction
   constexpr int OWB = kWave * PB;         // output staging bytes per wave
   constexpr int NIO = OWB / 1024;         // store instructions per phase
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * WAVE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t olds[kWaves * OWB];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[W * WAVE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t olds[W * OWB];
   float* lut = nullptr;  // level table for the 8- and 16-level searches only
   if constexpr (L >= 8) {
     __shared__ float lut_s[kMaxLevels];
@@ -718,8 +729,8 @@ fakequant_contig(const uint8_t* __restrict__ w, int64_t n_groups, QuantParams p,
   uint8_t* const buf = lds + wave * WAVE_BYTES;
   uint8_t* const obuf = olds + wave * OWB;
   const int64_t n_batches = (n_groups + kWave - 1) / kWave;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
-  int64_t batch = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * W;
+  int64_t batch = static_cast<int64_t>(blockIdx.x) * W + wave;
   if (batch >= n_batches) return;
 
   constexpr int GPI = kWave / CPG;
@@ -857,8 +868,9 @@ hipError_t launch_fq(const void* w, int64_t rows, int64_t cols, const QuantParam
   if (cols % kGroup == 0) {
     const int64_t n_groups = rows * (cols / kGroup);
     const int64_t n_batches = (n_groups + kWave - 1) / kWave;
-    const int blocks = spread_blocks(n_batches, kWaves, kBatchesPerWave, blocks_per_cu(BF16IN));
-    hipLaunchKernelGGL((fakequant_contig<L, BF16IN, BF16OUT>), dim3(blocks), dim3(kBlock), 0, s, wb,
+    constexpr int W = fake_waves();
+    const int blocks = spread_blocks(n_batches, W, kBatchesPerWave, floor_blocks_per_cu(BF16IN, W));
+    hipLaunchKernelGGL((fakequant_contig<L, BF16IN, BF16OUT>), dim3(blocks), dim3(W * kWave), 0, s, wb,
                        n_groups, p, lv, ob);
   } else {
     const int64_t n_groups = rows * ((cols + kGroup - 1) / kGroup);
@@ -889,9 +901,10 @@ hipError_t launch_l(const void* w, int64_t rows, int64_t cols, const QuantParams
     const int64_t n_batches = (n_groups + kWave - 1) / kWave;
     // Each wave loops over a few batches, so the next batch's DMA overlaps
     // the current arithmetic.
-    const int blocks = spread_blocks(n_batches, kWaves, kBatchesPerWave, blocks_per_cu(BF16));
+    constexpr int W = quant_waves(BF16);
+    const int blocks = spread_blocks(n_batches, W, kBatchesPerWave, floor_blocks_per_cu(BF16, W));
     const QuantJob job{wb, packed, norms, n_groups, TensorTable<QuantDesc>{nullptr, nullptr, 0}, n_batches};
-    hipLaunchKernelGGL((quantize_contig<L, BF16, false, TRITS>), dim3(blocks), dim3(kBlock), 0, s, job, p);
+    hipLaunchKernelGGL((quantize_contig<L, BF16, false, TRITS>), dim3(blocks), dim3(W * kWave), 0, s, job, p);
   } else {
     const int64_t n_groups = rows * ((cols + kGroup - 1) / kGroup);
     const int blocks = static_cast<int>((n_groups + kBlock - 1) / kBlock);
@@ -905,9 +918,10 @@ template <int L, bool BF16, bool TRITS>
 hipError_t launch_many_l(const QuantParams& p, TensorTable<QuantDesc> contig, int64_t contig_batches,
                          TensorTable<QuantDesc> ragged, int64_t ragged_groups, hipStream_t s) {
   if (contig_batches > 0) {
-    const int blocks = spread_blocks(contig_batches, kWaves, kBatchesPerWave, blocks_per_cu(BF16));
+    constexpr int W = quant_waves(BF16);
+    const int blocks = spread_blocks(contig_batches, W, kBatchesPerWave, floor_blocks_per_cu(BF16, W));
     const QuantJob job{nullptr, nullptr, nullptr, 0, contig, contig_batches};
-    hipLaunchKernelGGL((quantize_contig<L, BF16, true, TRITS>), dim3(blocks), dim3(kBlock), 0, s, job, p);
+    hipLaunchKernelGGL((quantize_contig<L, BF16, true, TRITS>), dim3(blocks), dim3(W * kWave), 0, s, job, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
