@@ -185,9 +185,29 @@ def codebook(bits: int, samples=None, iters: int = 200) -> np.ndarray:
 # -- device calls ---------------------------------------------------------------
 
 def _rows_cols(shape) -> tuple[int, int]:
-    cols = int(shape[-1])
-    rows = int(np.prod(shape[:-1], dtype=np.int64)) if len(shape) > 1 else 1
-    return rows, cols
+    rows = 1
+    for d in shape[:-1]:
+        rows *= int(d)
+    return rows, int(shape[-1])
+
+
+def _desc_array(cls, columns):
+    """A ctypes array of the descriptor struct `cls`, field i taken from the
+    sequence columns[i].  It is filled through a NumPy record array of the
+    same layout (every field is 8 bytes), one vectorised assignment per field
+    instead of one ctypes construction per element."""
+    n = len(columns[0])
+    dt = np.dtype([(name, "<u8" if typ is ctypes.c_void_p else "<i8") for name, typ in cls._fields_])
+    assert dt.itemsize == ctypes.sizeof(cls)
+    rec = np.zeros(max(n, 1), dt)
+    if n:
+        for (name, _), col in zip(cls._fields_, columns):
+            rec[name] = col
+    return (cls * max(n, 1)).from_buffer(rec)
+
+
+def _ptr_or_0(t) -> int:
+    return t.data_ptr() if t.numel() else 0
 
 
 def quantize(w, bits: int, levels, group_size: int = GROUP, packed=None, norms=None, stream=None):
@@ -275,16 +295,19 @@ def dequant_matvec(packed, norms, n_out: int, k: int, bits: int, levels, x, grou
     return y
 
 
+def _matvec_descs(items):
+    return _desc_array(MatvecDesc, (
+        [_ptr_or_0(it[0]) for it in items], [_ptr_or_0(it[1]) for it in items],
+        [it[2] for it in items], [it[3] for it in items],
+        [_ptr_or_0(it[4]) for it in items], [_ptr_or_0(it[5]) for it in items]))
+
+
 def dequant_matvec_many(items, bits: int, levels, batch: int, group_size: int = GROUP, stream=None):
     """Run y = x . W_hat^T for every (packed, norms, n_out, k, x, y) in items
     as one call (the y tensors, float32 [batch, n_out], are written in place).
     Returns the list of y tensors."""
     n = len(items)
-    arr = (MatvecDesc * max(n, 1))()
-    for i, (packed, norms, n_out, k, x, y) in enumerate(items):
-        arr[i] = MatvecDesc(packed.data_ptr() if packed.numel() else 0,
-                            norms.data_ptr() if norms.numel() else 0, n_out, k,
-                            x.data_ptr() if x.numel() else 0, y.data_ptr() if y.numel() else 0)
+    arr = _matvec_descs(items)
     lv, lvp = _levels_arg(levels)
     _check("cq_dequant_matvec_many", lib().cq_dequant_matvec_many(n, arr, bits, group_size, lvp, lv.size,
                                                                   batch, _stream_ptr(stream)))
@@ -296,14 +319,16 @@ def blob_layout(shapes, bits: int, group_size: int = GROUP):
     tensors with the given shapes: (packed_offsets, norm_offsets, total)."""
     dims = [_rows_cols(tuple(sh)) for sh in shapes]
     n = len(dims)
-    rows = (ctypes.c_int64 * max(n, 1))(*[r for r, _ in dims])
-    cols = (ctypes.c_int64 * max(n, 1))(*[c for _, c in dims])
-    po = (ctypes.c_int64 * max(n, 1))()
-    no = (ctypes.c_int64 * max(n, 1))()
+    rc = np.zeros((2, max(n, 1)), np.int64)
+    if n:
+        rc[:, :n] = np.array(dims, np.int64).T
+    out = np.zeros((2, max(n, 1)), np.int64)
+    p64 = ctypes.POINTER(ctypes.c_int64)
     total = ctypes.c_int64()
-    _check("cq_blob_layout", lib().cq_blob_layout(n, rows, cols, bits, group_size, po, no,
-                                                  ctypes.byref(total)))
-    return list(po)[:n], list(no)[:n], total.value
+    _check("cq_blob_layout", lib().cq_blob_layout(n, rc[0].ctypes.data_as(p64), rc[1].ctypes.data_as(p64), bits,
+                                                  group_size, out[0].ctypes.data_as(p64),
+                                                  out[1].ctypes.data_as(p64), ctypes.byref(total)))
+    return out[0, :n].tolist(), out[1, :n].tolist(), total.value
 
 
 def quantize_many(ws, bits: int, levels, blob=None, group_size: int = GROUP, stream=None,
@@ -334,15 +359,15 @@ def quantize_many(ws, bits: int, levels, blob=None, group_size: int = GROUP, str
         raise ValueError(f"blob must be a contiguous uint8 tensor of {total} bytes")
     pb = group_bytes(bits, group_size)
     base = blob.data_ptr() if total else 0
+    dims = [_rows_cols(tuple(w.shape)) for w in ws]
+    live = [r * c != 0 for r, c in dims]
+    arr = _desc_array(QuantDesc, (
+        [w.data_ptr() if a else 0 for w, a in zip(ws, live)], [r for r, _ in dims], [c for _, c in dims],
+        [base + o if a else 0 for o, a in zip(po, live)], [base + o if a else 0 for o, a in zip(no, live)]))
     out_views = []
-    arr = (QuantDesc * len(ws))()
-    for i, w in enumerate(ws):
-        rows, cols = _rows_cols(tuple(w.shape))
-        ng = -(-cols // group_size) if cols else 0
-        empty = rows * cols == 0
-        arr[i] = QuantDesc(0 if empty else w.data_ptr(), rows, cols, 0 if empty else base + po[i],
-                           0 if empty else base + no[i])
-        if views:
+    if views:
+        for i, (rows, cols) in enumerate(dims):
+            ng = -(-cols // group_size) if cols else 0
             pk = blob[po[i]:po[i] + rows * ng * pb].view(rows, ng, pb)
             nm = blob[no[i]:no[i] + 2 * rows * ng].view(torch.float16).view(rows, ng)
             out_views.append((pk, nm))
@@ -363,13 +388,12 @@ def dequantize_many(items, bits: int, levels, out_dtype=None, outs=None, group_s
     if outs is None:
         dev = items[0][0].device if items else "cpu"
         outs = [torch.empty((r, c), dtype=out_dtype, device=dev) for _, _, r, c in items]
-    arr = (DequantDesc * max(len(items), 1))()
-    for i, ((packed, norms, rows, cols), out) in enumerate(zip(items, outs)):
+    for i, ((_, _, rows, cols), out) in enumerate(zip(items, outs)):
         if out.dtype != out_dtype or out.numel() != rows * cols or not out.is_contiguous():
             raise ValueError(f"outs[{i}] must be a contiguous {out_dtype} tensor of {rows}x{cols}")
-        arr[i] = DequantDesc(packed.data_ptr() if packed.numel() else 0,
-                             norms.data_ptr() if norms.numel() else 0, rows, cols,
-                             out.data_ptr() if out.numel() else 0)
+    arr = _desc_array(DequantDesc, (
+        [_ptr_or_0(it[0]) for it in items], [_ptr_or_0(it[1]) for it in items], [it[2] for it in items],
+        [it[3] for it in items], [_ptr_or_0(o) for o in outs]))
     lv, lvp = _levels_arg(levels)
     _check("cq_dequantize_many", lib().cq_dequantize_many(len(items), arr, bits, group_size, lvp,
                                                           lv.size, dt, _stream_ptr(stream)))
@@ -399,11 +423,7 @@ def dequant_gemm_many(items, bits: int, levels, batch: int, group_size: int = GR
     """dequant_gemm for every (packed, norms, n_out, k, x, y) in items as one
     call (y float32 [batch, n_out] written in place).  Returns the y list."""
     n = len(items)
-    arr = (MatvecDesc * max(n, 1))()
-    for i, (packed, norms, n_out, k, x, y) in enumerate(items):
-        arr[i] = MatvecDesc(packed.data_ptr() if packed.numel() else 0,
-                            norms.data_ptr() if norms.numel() else 0, n_out, k,
-                            x.data_ptr() if x.numel() else 0, y.data_ptr() if y.numel() else 0)
+    arr = _matvec_descs(items)
     lv, lvp = _levels_arg(levels)
     _check("cq_dequant_gemm_many", lib().cq_dequant_gemm_many(n, arr, bits, group_size, lvp, lv.size, batch,
                                                               _stream_ptr(stream)))
