@@ -109,14 +109,6 @@ hipError_t launch_repack(const uint8_t* src, bool to_trits, uint8_t* dst, int64_
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
-// Blocks for a persistent grid-stride kernel: `per_cu` resident blocks on
-// every compute unit, but no more than there is work for.
-inline int persistent_blocks(int64_t work_blocks, int per_cu) {
-  const int64_t cap = static_cast<int64_t>(device_cu_count()) * per_cu;
-  const int64_t b = work_blocks < cap ? work_blocks : cap;
-  return static_cast<int>(b > 0 ? b : 1);
-}
-
 // Blocks of `waves` waves for a grid-stride kernel over n_batches batches in
 // which each wave takes about `per_wave` batches, but never fewer than one
 // batch per wave gives up to per_cu resident blocks per CU, so a mid-size

@@ -26,14 +26,13 @@ namespace kd {
 
 constexpr int kWaves = 4;
 constexpr int kBlock = kWaves * kWave;
-// Resident blocks per CU for the bf16-output grid: one measured faster than
-// two for this store-heavy kernel.
+// Floor of the covering grid for mid-size tensors: one block per CU.
 constexpr int kBlocksPerCu = 1;
-// Waves per block of dequantize_contig: eight for float32 output (1.6%
-// faster on the 7B-shaped model than four; at 201 VGPRs a CU holds eight
-// waves either way), four for bf16 output, whose resident grid ran 28% slower
-// with eight.
-constexpr int contig_waves(bool bf16_out) { return bf16_out ? kWaves : 2 * kWaves; }
+// Waves per block of dequantize_contig: eight.  On the 7B-shaped model that
+// was 1.6% faster than four for float32 output (at about 200 VGPRs a CU holds
+// eight waves either way) and, with the covering grid, 6.6% faster than the
+// resident grid of 4-wave blocks that bf16 output used before.
+constexpr int contig_waves(bool) { return 2 * kWaves; }
 
 __device__ __forceinline__ void butterfly(float (&y)[kGroup]) {
 #pragma unroll
@@ -455,15 +454,13 @@ dequantize_ragged(const uint8_t* __restrict__ packed, const uint16_t* __restrict
   }
 }
 
-// Grid size.  Float32 output: one batch per wave, a grid that covers the
-// tensor (5-6% faster on the 7B-shaped model than a resident grid).  Bf16
-// output: a resident grid of kBlocksPerCu blocks per CU looping over the
-// batches (the covering grid measured 8% slower there).
+// Grid size: one batch per wave, a grid that covers the tensor (5-6% faster
+// on the 7B-shaped model than a resident grid for float32 output; 2 and 4
+// batches per wave were 4% and 8% slower).
 template <bool BF16OUT>
 int dequant_blocks(int64_t n_batches) {
   constexpr int W = contig_waves(BF16OUT);
-  return BF16OUT ? persistent_blocks((n_batches + W - 1) / W, kBlocksPerCu)
-                 : spread_blocks(n_batches, W, 1, kBlocksPerCu);
+  return spread_blocks(n_batches, W, 1, kBlocksPerCu);
 }
 
 template <int SB, bool BF16OUT, bool TRITS>
