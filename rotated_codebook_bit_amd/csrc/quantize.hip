@@ -422,12 +422,15 @@ constexpr int fake_waves() { return 1; }
 // waves per CU as blocks_per_cu blocks of kWaves waves.
 constexpr int floor_blocks_per_cu(bool bf16_in, int w) { return blocks_per_cu(bf16_in) * kWaves / w; }
 
-// Batches per wave of the grid.  A grid of about four batches per wave
-// (each wave strides by the grid) measured 4-7% faster on the 7B-shaped
-// model than a resident grid of blocks_per_cu blocks per CU that loops over
-// all batches, for quantize (bf16 and float32 input) and fake quant.  Smaller
-// tensors get at least the resident grid's block count (spread_blocks).
-constexpr int kBatchesPerWave = 4;
+// Batches per wave of the grid (each wave strides by the grid).  A grid of a
+// few batches per wave measured 4-7% faster on the 7B-shaped model than a
+// resident grid of blocks_per_cu blocks per CU that loops over all batches.
+// With the block sizes above (ms at 1 / 2 / 4 / 8 batches per wave):
+// quantize from bf16 2.76 / 2.72 / 2.70 / 2.74, from float32 4.78 / 4.84 /
+// 4.96 / 5.23; fake quant bf16 -> bf16 4.88 / 4.75 / 4.93 / 5.06.  Smaller
+// tensors get at least the resident grid's waves (spread_blocks).
+constexpr int quant_batches_per_wave(bool bf16_in) { return bf16_in ? 4 : 1; }
+constexpr int fake_batches_per_wave() { return 2; }
 
 template <int L, bool BF16, bool MANY, bool TRITS = false>
 __global__ void __launch_bounds__(quant_waves(BF16) * kWave, blocks_per_cu(BF16))
@@ -869,7 +872,7 @@ hipError_t launch_fq(const void* w, int64_t rows, int64_t cols, const QuantParam
     const int64_t n_groups = rows * (cols / kGroup);
     const int64_t n_batches = (n_groups + kWave - 1) / kWave;
     constexpr int W = fake_waves();
-    const int blocks = spread_blocks(n_batches, W, kBatchesPerWave, floor_blocks_per_cu(BF16IN, W));
+    const int blocks = spread_blocks(n_batches, W, fake_batches_per_wave(), floor_blocks_per_cu(BF16IN, W));
     hipLaunchKernelGGL((fakequant_contig<L, BF16IN, BF16OUT>), dim3(blocks), dim3(W * kWave), 0, s, wb,
                        n_groups, p, lv, ob);
   } else {
@@ -902,7 +905,7 @@ hipError_t launch_l(const void* w, int64_t rows, int64_t cols, const QuantParams
     // Each wave loops over a few batches, so the next batch's DMA overlaps
     // the current arithmetic.
     constexpr int W = quant_waves(BF16);
-    const int blocks = spread_blocks(n_batches, W, kBatchesPerWave, floor_blocks_per_cu(BF16, W));
+    const int blocks = spread_blocks(n_batches, W, quant_batches_per_wave(BF16), floor_blocks_per_cu(BF16, W));
     const QuantJob job{wb, packed, norms, n_groups, TensorTable<QuantDesc>{nullptr, nullptr, 0}, n_batches};
     hipLaunchKernelGGL((quantize_contig<L, BF16, false, TRITS>), dim3(blocks), dim3(W * kWave), 0, s, job, p);
   } else {
@@ -919,7 +922,8 @@ hipError_t launch_many_l(const QuantParams& p, TensorTable<QuantDesc> contig, in
                          TensorTable<QuantDesc> ragged, int64_t ragged_groups, hipStream_t s) {
   if (contig_batches > 0) {
     constexpr int W = quant_waves(BF16);
-    const int blocks = spread_blocks(contig_batches, W, kBatchesPerWave, floor_blocks_per_cu(BF16, W));
+    const int blocks =
+        spread_blocks(contig_batches, W, quant_batches_per_wave(BF16), floor_blocks_per_cu(BF16, W));
     const QuantJob job{nullptr, nullptr, nullptr, 0, contig, contig_batches};
     hipLaunchKernelGGL((quantize_contig<L, BF16, true, TRITS>), dim3(blocks), dim3(W * kWave), 0, s, job, p);
     const hipError_t e = hipGetLastError();
