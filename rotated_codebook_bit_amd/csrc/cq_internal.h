@@ -109,6 +109,22 @@ hipError_t launch_repack(const uint8_t* src, bool to_trits, uint8_t* dst, int64_
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
+// Chunks a wave has just stored to LDS (a ds_write_b128 each) keep their
+// registers until the LDS has taken them.  Measured on gfx950: with the bf16
+// output of dequantize at 3 bits, the compiler reused the first data
+// register of each ds_write_b128 in the very next instruction, and the store
+// now and then took the new value (zeros in the first dword of some 16-byte
+// chunks, different ones from run to run).  Waiting for the wave's LDS
+// operations (lgkmcnt(0)), with the registers named as inputs of asm
+// statements placed after the wait, rules that out: the registers cannot be
+// reused before the wait, and after it the writes are done.
+template <int N>
+__device__ __forceinline__ void hold_until_lds_written(const uint4 (&v)[N]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(v[i].x), "v"(v[i].y), "v"(v[i].z), "v"(v[i].w));
+}
+
 // Blocks of `waves` waves for a grid-stride kernel over n_batches batches in
 // which each wave takes about `per_wave` batches, but never fewer than one
 // batch per wave gives up to per_cu resident blocks per CU, so a mid-size

@@ -365,25 +365,30 @@ dequantize_contig(DequantJob job, LevelTable lv) {
     reconstruct_fast<SB>(words, n16, tab, y);
 
     const auto dst = make_rsrc(cur.out + cur.bt * kWave * GOB, nv * GOB);
+    // bf16 output: all 128 values are rounded and packed before the first
+    // phase, so the phases only move finished registers.
+    uint32_t pk[BF16OUT ? kGroup / 2 : 1];
+    if constexpr (BF16OUT) {
+#pragma unroll
+      for (int i = 0; i < kGroup / 2; ++i) pk[i] = f32_to_bf16_rne(y[2 * i]) | (f32_to_bf16_rne(y[2 * i + 1]) << 16);
+    }
 #pragma unroll
     for (int ph = 0; ph < 4; ++ph) {
       // Scatter this lane's 32 values of the phase into the swizzled buffer.
+      uint4 ch[CPP];
 #pragma unroll
       for (int c = 0; c < CPP; ++c) {
-        uint4 v;
         if constexpr (BF16OUT) {
-          const int e = 32 * ph + 8 * c;
-          v.x = f32_to_bf16_rne(y[e]) | (f32_to_bf16_rne(y[e + 1]) << 16);
-          v.y = f32_to_bf16_rne(y[e + 2]) | (f32_to_bf16_rne(y[e + 3]) << 16);
-          v.z = f32_to_bf16_rne(y[e + 4]) | (f32_to_bf16_rne(y[e + 5]) << 16);
-          v.w = f32_to_bf16_rne(y[e + 6]) | (f32_to_bf16_rne(y[e + 7]) << 16);
+          const int q = 16 * ph + 4 * c;
+          ch[c] = make_uint4(pk[q], pk[q + 1], pk[q + 2], pk[q + 3]);
         } else {
           const int e = 32 * ph + 4 * c;
-          v = make_uint4(__builtin_bit_cast(uint32_t, y[e]), __builtin_bit_cast(uint32_t, y[e + 1]),
-                         __builtin_bit_cast(uint32_t, y[e + 2]), __builtin_bit_cast(uint32_t, y[e + 3]));
+          ch[c] = make_uint4(__builtin_bit_cast(uint32_t, y[e]), __builtin_bit_cast(uint32_t, y[e + 1]),
+                             __builtin_bit_cast(uint32_t, y[e + 2]), __builtin_bit_cast(uint32_t, y[e + 3]));
         }
-        *reinterpret_cast<uint4*>(buf + lane * PB + 16 * (c ^ swz_w)) = v;
       }
+#pragma unroll
+      for (int c = 0; c < CPP; ++c) *reinterpret_cast<uint4*>(buf + lane * PB + 16 * (c ^ swz_w)) = ch[c];
       // Gather 16-byte chunks so consecutive lanes write consecutive bytes.
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
@@ -392,6 +397,9 @@ dequantize_contig(DequantJob job, LevelTable lv) {
         const uint4 v = *reinterpret_cast<const uint4*>(buf + gs * PB + 16 * (cc ^ sw));
         store16<BF16OUT ? 0 : kStoreF32>(v, dst, st_lane + ph * PB, static_cast<uint32_t>(GPI * i * GOB));
       }
+      // After the gather reads (which complete after the writes), so the wait
+      // adds nothing to the phase.
+      hold_until_lds_written(ch);
     }
     cur = nxt;
     batch = next;

@@ -17,15 +17,15 @@
 // Both kernels read a table of matrix descriptors in device memory, so any
 // number of matrices (a whole model's decode step) runs as two launches.
 //
-// Product kernel mapping: a block (4 waves) owns RB consecutive rows of one
-// matrix.  Thread t owns 16-column chunks t, t + 256, ... of the row (one
-// 4096-column pass per 256 chunks) and keeps the rotated activations of its
-// chunk in registers for the whole pass; for every row it loads the 4 (2-bit)
-// / 6 (3-bit) / 8 (4-bit) bytes of codes of its chunk (a wave instruction
-// reads 256-512 contiguous bytes of the row), decodes four (2-bit) or two
-// (4-bit) levels per LDS read from a byte table, and accumulates NB partial
-// sums per row.  The block reduces its RB x NB partials through LDS in a
-// fixed order, so results are deterministic.
+// Product kernel mapping: a block (4 waves) owns up to 8 groups of RB
+// consecutive rows of one matrix.  Thread t owns 16-column chunks t, t + 256,
+// ... of a row (one 4096-column pass per 256 chunks) and keeps the rotated
+// activations of its chunk in registers for the pass; for every row it loads
+// the 4 (2-bit) / 6 (3-bit) / 8 (4-bit) bytes of codes of its chunk (a wave
+// instruction reads 256-512 contiguous bytes of the row), decodes four
+// (2-bit) or two (4-bit) levels per LDS read from a byte table, and
+// accumulates NB partial sums per row.  The block reduces each group's RB x
+// NB partials through LDS in a fixed order, so results are deterministic.
 //
 // One batch row with 2-bit codes (a decode step) takes matvec_pair_kernel
 // instead: per column pair it tabulates the 16 partial products a 4-bit

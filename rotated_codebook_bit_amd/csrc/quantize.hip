@@ -779,22 +779,23 @@ fakequant_contig(const uint8_t* __restrict__ w, int64_t n_groups, QuantParams p,
     const auto dst = make_rsrc(out + batch * kWave * GOB, valid_in_batch(batch, n_groups) * GOB);
 #pragma unroll
     for (int ph = 0; ph < kGroup / PE; ++ph) {
+      uint4 ch[CPP];
 #pragma unroll
       for (int c = 0; c < CPP; ++c) {
-        uint4 v;
         if constexpr (BF16OUT) {
           const int e = PE * ph + 8 * c;
-          v.x = f32_to_bf16_rne(y[e]) | (f32_to_bf16_rne(y[e + 1]) << 16);
-          v.y = f32_to_bf16_rne(y[e + 2]) | (f32_to_bf16_rne(y[e + 3]) << 16);
-          v.z = f32_to_bf16_rne(y[e + 4]) | (f32_to_bf16_rne(y[e + 5]) << 16);
-          v.w = f32_to_bf16_rne(y[e + 6]) | (f32_to_bf16_rne(y[e + 7]) << 16);
+          ch[c].x = f32_to_bf16_rne(y[e]) | (f32_to_bf16_rne(y[e + 1]) << 16);
+          ch[c].y = f32_to_bf16_rne(y[e + 2]) | (f32_to_bf16_rne(y[e + 3]) << 16);
+          ch[c].z = f32_to_bf16_rne(y[e + 4]) | (f32_to_bf16_rne(y[e + 5]) << 16);
+          ch[c].w = f32_to_bf16_rne(y[e + 6]) | (f32_to_bf16_rne(y[e + 7]) << 16);
         } else {
           const int e = PE * ph + 4 * c;
-          v = make_uint4(__builtin_bit_cast(uint32_t, y[e]), __builtin_bit_cast(uint32_t, y[e + 1]),
-                         __builtin_bit_cast(uint32_t, y[e + 2]), __builtin_bit_cast(uint32_t, y[e + 3]));
+          ch[c] = make_uint4(__builtin_bit_cast(uint32_t, y[e]), __builtin_bit_cast(uint32_t, y[e + 1]),
+                             __builtin_bit_cast(uint32_t, y[e + 2]), __builtin_bit_cast(uint32_t, y[e + 3]));
         }
-        *reinterpret_cast<uint4*>(obuf + lane * PB + 16 * (c ^ swz_w)) = v;
       }
+#pragma unroll
+      for (int c = 0; c < CPP; ++c) *reinterpret_cast<uint4*>(obuf + lane * PB + 16 * (c ^ swz_w)) = ch[c];
 #pragma unroll
       for (int i = 0; i < NIO; ++i) {
         const int gs = GPO * i + gq;
@@ -802,6 +803,9 @@ fakequant_contig(const uint8_t* __restrict__ w, int64_t n_groups, QuantParams p,
         const uint4 v = *reinterpret_cast<const uint4*>(obuf + gs * PB + 16 * (cc ^ sw));
         store16(v, dst, st_lane + ph * PB, static_cast<uint32_t>(GPO * i * GOB));
       }
+      // After the gather reads (which complete after the writes), so the wait
+      // adds nothing to the phase.
+      hold_until_lds_written(ch);
     }
     batch = next;
     if (batch >= n_batches) break;
