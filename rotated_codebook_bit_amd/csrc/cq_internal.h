@@ -125,6 +125,18 @@ __device__ __forceinline__ void hold_until_lds_written(const uint4 (&v)[N]) {
   for (int i = 0; i < N; ++i) asm volatile("" ::"v"(v[i].x), "v"(v[i].y), "v"(v[i].z), "v"(v[i].w));
 }
 
+// The same for 32-bit values (table fills): wait for the wave's LDS writes,
+// then name the stored values, so their registers outlive the writes.
+__device__ __forceinline__ void wait_lds_writes() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+template <typename T>
+__device__ __forceinline__ void hold_value(const T& v) {
+  asm volatile("" ::"v"(v));
+}
+template <typename... T>
+__device__ __forceinline__ void hold_values(const T&... v) {
+  (hold_value(v), ...);
+}
+
 // Blocks of `waves` waves for a grid-stride kernel over n_batches batches in
 // which each wave takes about `per_wave` batches, but never fewer than one
 // batch per wave gives up to per_cu resident blocks per CU, so a mid-size

@@ -129,13 +129,19 @@ struct ByteTable {
     }
     if constexpr (E == 4) {
       const float a0 = q[0] + q[1], a1 = q[0] - q[1], a2 = q[2] + q[3], a3 = q[2] - q[3];
-      tab[4 * t] = a0 + a2;
-      tab[4 * t + 1] = a1 + a3;
-      tab[4 * t + 2] = a0 - a2;
-      tab[4 * t + 3] = a1 - a3;
+      const float v0 = a0 + a2, v1 = a1 + a3, v2 = a0 - a2, v3 = a1 - a3;
+      tab[4 * t] = v0;
+      tab[4 * t + 1] = v1;
+      tab[4 * t + 2] = v2;
+      tab[4 * t + 3] = v3;
+      wait_lds_writes();
+      hold_values(v0, v1, v2, v3);
     } else {
-      tab[2 * t] = q[0] + q[1];
-      tab[2 * t + 1] = q[0] - q[1];
+      const float v0 = q[0] + q[1], v1 = q[0] - q[1];
+      tab[2 * t] = v0;
+      tab[2 * t + 1] = v1;
+      wait_lds_writes();
+      hold_values(v0, v1);
     }
   }
   // Byte k (0..G*SB/8-1) of the group's packed bits.
@@ -170,7 +176,12 @@ struct TableSize {
 template <int SB>
 __device__ __forceinline__ void fill_table(float* tab, const LevelTable& lv, int t) {
   if constexpr (SB == 3) {
-    if (t < kMaxLevels) tab[t] = level_at(lv, t);
+    if (t < kMaxLevels) {
+      const float v = level_at(lv, t);
+      tab[t] = v;
+      wait_lds_writes();
+      hold_values(v);
+    }
   } else {
     ByteTable<SB>::fill(tab, lv, t);
   }
@@ -233,7 +244,12 @@ __device__ __forceinline__ void fetch_batch_trits(const uint8_t* __restrict__ pa
 }
 
 __device__ __forceinline__ void fill_trit_table(uint16_t* ttab, int t) {
-  if (t < 256) ttab[t] = static_cast<uint16_t>(trit_table_entry(static_cast<uint32_t>(t)));
+  if (t < 256) {
+    const uint32_t v = trit_table_entry(static_cast<uint32_t>(t));
+    ttab[t] = static_cast<uint16_t>(v);
+    wait_lds_writes();
+    hold_values(v);
+  }
 }
 
 // Cache policy of the output stores (the buffer instruction's aux bits:

@@ -216,14 +216,24 @@ __device__ __forceinline__ void fill_table(uint32_t* tab, const SplitLevels& s, 
   if constexpr (SB == 2) {
     const int c0 = t & 3, c1 = (t >> 2) & 3, c2 = (t >> 4) & 3, c3 = t >> 6;
     // hi pairs in the first 512 words, lo pairs in the next 512
-    tab[2 * t] = split_at(s, c0, false) | (split_at(s, c1, false) << 16);
-    tab[2 * t + 1] = split_at(s, c2, false) | (split_at(s, c3, false) << 16);
-    tab[512 + 2 * t] = split_at(s, c0, true) | (split_at(s, c1, true) << 16);
-    tab[512 + 2 * t + 1] = split_at(s, c2, true) | (split_at(s, c3, true) << 16);
+    const uint32_t h0 = split_at(s, c0, false) | (split_at(s, c1, false) << 16);
+    const uint32_t h1 = split_at(s, c2, false) | (split_at(s, c3, false) << 16);
+    const uint32_t l0 = split_at(s, c0, true) | (split_at(s, c1, true) << 16);
+    const uint32_t l1 = split_at(s, c2, true) | (split_at(s, c3, true) << 16);
+    tab[2 * t] = h0;
+    tab[2 * t + 1] = h1;
+    tab[512 + 2 * t] = l0;
+    tab[512 + 2 * t + 1] = l1;
+    wait_lds_writes();  // the values keep their registers until stored
+    hold_values(h0, h1, l0, l1);
   } else {
     const int c0 = SB == 4 ? (t & 15) : (t & 7), c1 = SB == 4 ? (t >> 4) : (t >> 3);
-    tab[2 * t] = split_at(s, c0, false) | (split_at(s, c1, false) << 16);
-    tab[2 * t + 1] = split_at(s, c0, true) | (split_at(s, c1, true) << 16);
+    const uint32_t h = split_at(s, c0, false) | (split_at(s, c1, false) << 16);
+    const uint32_t l = split_at(s, c0, true) | (split_at(s, c1, true) << 16);
+    tab[2 * t] = h;
+    tab[2 * t + 1] = l;
+    wait_lds_writes();
+    hold_values(h, l);
   }
 }
 

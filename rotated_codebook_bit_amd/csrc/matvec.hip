@@ -175,6 +175,9 @@ struct Levels {
     for (int c = 0; c < K; ++c)
 #pragma unroll
       for (int q = 0; q < entry; ++q) tab[(t * K + c) * entry + q] = e[q];
+    wait_lds_writes();  // the values keep their registers until stored
+#pragma unroll
+    for (int q = 0; q < entry; ++q) hold_values(e[q]);
   }
   // Levels of the 16 codes into v[16]; copy = lane % K.
   static __device__ __forceinline__ void decode(uint64_t codes, const float* tab, int copy, float (&v)[16]) {
@@ -441,10 +444,19 @@ matvec_pair_kernel(const MatvecDesc* __restrict__ table, const int64_t* __restri
         const float pa[4] = {c0l * x0, c1l * x0, c2l * x0, c3l * x0};
         const float cb[4] = {c0l, c1l, c2l, c3l};
         float* dst = tab + (16 * (PPT * w + h)) * kWave + lane;
+        // Four entries at a time keep their registers until the LDS has
+        // them (a wait per four; held in larger sets they spill at this
+        // kernel's 64 VGPRs).
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb)
+        for (int bb = 0; bb < 4; ++bb) {
+          float e[4];
 #pragma unroll
-          for (int a = 0; a < 4; ++a) dst[(a + 4 * bb) * kWave] = __builtin_fmaf(cb[bb], x1, pa[a]);
+          for (int a = 0; a < 4; ++a) e[a] = __builtin_fmaf(cb[bb], x1, pa[a]);
+#pragma unroll
+          for (int a = 0; a < 4; ++a) dst[(a + 4 * bb) * kWave] = e[a];
+          wait_lds_writes();
+          hold_values(e[0], e[1], e[2], e[3]);
+        }
       }
     }
     __syncthreads();

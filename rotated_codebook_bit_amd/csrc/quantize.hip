@@ -722,7 +722,12 @@ fakequant_contig(const uint8_t* __restrict__ w, int64_t n_groups, QuantParams p,
   float* lut = nullptr;  // level table for the 8- and 16-level searches only
   if constexpr (L >= 8) {
     __shared__ float lut_s[kMaxLevels];
-    if (threadIdx.x < kMaxLevels) lut_s[threadIdx.x] = level_at(lv, threadIdx.x);
+    if (threadIdx.x < kMaxLevels) {
+      const float v = level_at(lv, threadIdx.x);
+      lut_s[threadIdx.x] = v;
+      wait_lds_writes();  // the value keeps its register until stored
+      hold_values(v);
+    }
     lut = lut_s;
   }
   __syncthreads();
@@ -819,7 +824,12 @@ __global__ void __launch_bounds__(kBlock)
 fakequant_ragged(const uint8_t* __restrict__ w, int64_t rows, int64_t cols, QuantParams p,
                  LevelTable lv, uint8_t* __restrict__ out) {
   __shared__ float lut[kMaxLevels];
-  if (threadIdx.x < kMaxLevels) lut[threadIdx.x] = level_at(lv, threadIdx.x);
+  if (threadIdx.x < kMaxLevels) {
+    const float v = level_at(lv, threadIdx.x);
+    lut[threadIdx.x] = v;
+    wait_lds_writes();  // the value keeps its register until stored
+    hold_values(v);
+  }
   __syncthreads();
   const int64_t ngr = (cols + kGroup - 1) / kGroup;
   const int64_t g = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;

@@ -28,7 +28,12 @@ fields_to_trits_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ ds
 __global__ void __launch_bounds__(kBlock)
 trits_to_fields_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t n_groups) {
   __shared__ uint16_t tab[256];
-  tab[threadIdx.x] = static_cast<uint16_t>(trit_table_entry(threadIdx.x));
+  {
+    const uint32_t v = trit_table_entry(threadIdx.x);
+    tab[threadIdx.x] = static_cast<uint16_t>(v);
+    wait_lds_writes();  // the value keeps its register until stored
+    hold_values(v);
+  }
   __syncthreads();
   const int64_t g = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
   if (g >= n_groups) return;
@@ -74,7 +79,12 @@ __global__ void __launch_bounds__(kBlock)
 trits_to_fields_g(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t n_groups) {
   constexpr int TB = (G + 4) / 5;
   __shared__ uint16_t tab[256];
-  tab[threadIdx.x] = static_cast<uint16_t>(trit_table_entry(threadIdx.x));
+  {
+    const uint32_t v = trit_table_entry(threadIdx.x);
+    tab[threadIdx.x] = static_cast<uint16_t>(v);
+    wait_lds_writes();  // the value keeps its register until stored
+    hold_values(v);
+  }
   __syncthreads();
   const int64_t g = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
   if (g >= n_groups) return;
