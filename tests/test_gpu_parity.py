@@ -169,15 +169,15 @@ def test_bf16_output(levels):
     assert np.all(np.abs(got - ref) <= 2 * np.abs(ref) * 2.0 ** -8 + 1e-5 * rms)
 
 
-@pytest.mark.parametrize("bits", ALL_BITS)
+@pytest.mark.parametrize("bits", ALL_BITS + [cq.TERNARY_TRITS])
 def test_bf16_output_is_rounded_f32_output(bits, levels):
     """At a size that fills many blocks per CU (11008x4096 bf16), the bf16
     outputs of dequantize and fake quant are the round-to-nearest-even of
     the float32 outputs, bit for bit: both paths compute the same float32
     values and differ only in the store.  (The float32 outputs are checked
     against the oracle by the other tests.)"""
-    lv = levels[bits]
-    g = torch.Generator(device=DEV).manual_seed(1000 + (bits if bits != O.TERNARY else 1))
+    lv = levels[O.TERNARY if bits == cq.TERNARY_TRITS else bits]
+    g = torch.Generator(device=DEV).manual_seed(1000 + bits)
     w = (torch.randn((11008, 4096), device=DEV, generator=g) * 0.02).to(torch.bfloat16)
     say(f"bf16 vs f32 output 11008x4096 bits={bits}")
     pk, nm = cq.quantize(w, bits, lv)
@@ -193,9 +193,10 @@ def test_bf16_output_is_rounded_f32_output(bits, levels):
     d32 = cq.dequantize(pk, nm, 11008, 4096, bits, lv)
     d16 = cq.dequantize(pk, nm, 11008, 4096, bits, lv, out_dtype=torch.bfloat16)
     same(d16, d32, "dequantize")
-    f32 = cq.fake_quant(w, bits, lv, out_dtype=torch.float32)
-    f16 = cq.fake_quant(w, bits, lv, out_dtype=torch.bfloat16)
-    same(f16, f32, "fake quant")
+    if bits != cq.TERNARY_TRITS:  # fake quant takes the level count, not the storage
+        f32 = cq.fake_quant(w, bits, lv, out_dtype=torch.float32)
+        f16 = cq.fake_quant(w, bits, lv, out_dtype=torch.bfloat16)
+        same(f16, f32, "fake quant")
 
 
 # -- the 45.5M-parameter set --------------------------------------------------------
