@@ -253,13 +253,15 @@ __device__ __forceinline__ int valid_in_batch(int64_t bt, int64_t n_groups) {
 
 // Where a batch's 64 groups lie: 16 slots of 4 consecutive groups, slot j
 // at slot index first + j * step of the tensor.  Plain batches are
-// contiguous (first = 16 bt, step = 1).  For 2- and 4-bit fields the full
-// batches of a tensor are also taken kInterleave at a time: batch r of such a
-// super-batch owns slots r, r + kInterleave, ..., so that at any moment the
-// neighbouring waves of the grid read neighbouring kilobytes.  On the
-// 7B-shaped bf16 model this cut quantize from 2.95-3.0 ms to 2.65 ms against
-// 16 contiguous kilobytes per wave; 16 and 64 measured 2.7-2.8 ms, widths
-// that are not powers of two (24, 48) 2.9 ms.  A slot's packed output is whole
+// contiguous (first = 16 bt, step = 1).  With bf16 input and 2- or 4-bit
+// fields the full batches of a tensor are also taken S = kInterleaveBf16 at
+// a time: batch r of such a super-batch owns slots r, r + S, ..., so that at
+// any moment the neighbouring waves of the grid read neighbouring kilobytes.
+// On the 7B-shaped bf16 model this cut quantize from 2.95-3.0 ms to 2.65 ms
+// against 16 contiguous kilobytes per wave; S = 16 and 64 measured 2.7-2.8
+// ms, widths that are not powers of two (24, 48) 2.9 ms.  Float32 input
+// (2 KiB slots) was slower at every width (S = 8 / 16 / 32: 5.39 / 5.24 /
+// 5.48 ms against 5.19) and keeps contiguous batches.  A slot's packed output is whole
 // 128-byte lines at these widths (4 x 32 or 4 x 64 bytes), so no line is
 // shared between waves; 3-bit fields (48 bytes a group) and trits keep the
 // contiguous placement.  Norms are 8 bytes a slot, so a norm line is written
