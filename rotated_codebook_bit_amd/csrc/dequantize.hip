@@ -329,16 +329,20 @@ dequantize_contig(DequantJob job, LevelTable lv) {
   __shared__ __attribute__((aligned(16))) float tab[TableSize<SB>::floats];
   __shared__ __attribute__((aligned(16))) uint8_t lds[W * WAVE_BYTES];
   __shared__ uint16_t ttab[TRITS ? 256 : 1];
-  if constexpr (TRITS) fill_trit_table(ttab, threadIdx.x);
-  fill_table<SB>(tab, lv, threadIdx.x);
+  // Blocks have 1 to W waves (dequant_grid); the tables need 256 entries.
+  for (int t = threadIdx.x; t < 256; t += blockDim.x) {
+    if constexpr (TRITS) fill_trit_table(ttab, t);
+    fill_table<SB>(tab, lv, t);
+  }
   __syncthreads();
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int waves = __builtin_amdgcn_readfirstlane(blockDim.x / kWave);
   uint8_t* const buf = lds + wave * WAVE_BYTES;
   const int64_t n_batches = job.n_batches;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * W;
-  int64_t batch = static_cast<int64_t>(blockIdx.x) * W + wave;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * waves;
+  int64_t batch = static_cast<int64_t>(blockIdx.x) * waves + wave;
   if (batch >= n_batches) return;
   int d = 0;
 
@@ -478,13 +482,23 @@ dequantize_ragged(const uint8_t* __restrict__ packed, const uint16_t* __restrict
   }
 }
 
-// Grid size: one batch per wave, a grid that covers the tensor (5-6% faster
-// on the 7B-shaped model than a resident grid for float32 output; 2 and 4
-// batches per wave were 4% and 8% slower).
+// Grid: one batch per wave, a grid that covers the tensor (5-6% faster on
+// the 7B-shaped model than a resident grid for float32 output; 2 and 4
+// batches per wave were 4% and 8% slower), in blocks of W waves.  A call
+// with fewer than W batches per CU takes smaller blocks, so its batches
+// spread over more CUs (256x512, 16 batches: 16 one-wave blocks instead of
+// two of eight).
+struct ContigGrid {
+  int blocks;
+  int waves;
+};
 template <bool BF16OUT>
-int dequant_blocks(int64_t n_batches) {
+ContigGrid dequant_grid(int64_t n_batches) {
   constexpr int W = contig_waves(BF16OUT);
-  return spread_blocks(n_batches, W, 1, kBlocksPerCu);
+  const int64_t cus = device_cu_count();
+  if (n_batches >= W * cus) return ContigGrid{spread_blocks(n_batches, W, 1, kBlocksPerCu), W};
+  const int w = n_batches > cus ? static_cast<int>((n_batches + cus - 1) / cus) : 1;  // 1 .. W
+  return ContigGrid{static_cast<int>((n_batches + w - 1) / w), w};
 }
 
 template <int SB, bool BF16OUT, bool TRITS>
@@ -494,11 +508,11 @@ hipError_t launch_sb(const uint8_t* packed, const uint16_t* norms, int64_t rows,
   if (cols % kGroup == 0) {
     const int64_t n_groups = rows * (cols / kGroup);
     const int64_t n_batches = (n_groups + kWave - 1) / kWave;
-    const int blocks = dequant_blocks<BF16OUT>(n_batches);
+    const ContigGrid g = dequant_grid<BF16OUT>(n_batches);
     const DequantJob job{packed, norms, ob, n_groups, TensorTable<DequantDesc>{nullptr, nullptr, 0},
                          n_batches};
-    hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT, false, TRITS>), dim3(blocks),
-                       dim3(contig_waves(BF16OUT) * kWave), 0, s, job, lv);
+    hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT, false, TRITS>), dim3(g.blocks), dim3(g.waves * kWave), 0, s,
+                       job, lv);
   } else {
     const int64_t n_groups = rows * ((cols + kGroup - 1) / kGroup);
     const int blocks = static_cast<int>((n_groups + kBlock - 1) / kBlock);
@@ -513,10 +527,10 @@ template <int SB, bool BF16OUT, bool TRITS>
 hipError_t launch_many_sb(const LevelTable& lv, TensorTable<DequantDesc> contig, int64_t contig_batches,
                           TensorTable<DequantDesc> ragged, int64_t ragged_groups, hipStream_t s) {
   if (contig_batches > 0) {
-    const int blocks = dequant_blocks<BF16OUT>(contig_batches);
+    const ContigGrid g = dequant_grid<BF16OUT>(contig_batches);
     const DequantJob job{nullptr, nullptr, nullptr, 0, contig, contig_batches};
-    hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT, true, TRITS>), dim3(blocks),
-                       dim3(contig_waves(BF16OUT) * kWave), 0, s, job, lv);
+    hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT, true, TRITS>), dim3(g.blocks), dim3(g.waves * kWave), 0, s,
+                       job, lv);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
