@@ -151,6 +151,22 @@ inline int spread_blocks(int64_t n_batches, int waves, int per_wave, int per_cu)
   return static_cast<int>(b > 0 ? b : 1);
 }
 
+// Grid of a contiguous kernel: blocks and waves per block (the kernel reads
+// its waves per block from blockDim).  With at least W batches per CU the
+// blocks have W waves (spread_blocks); a smaller call gets blocks of
+// ceil(batches / CUs) waves, one batch per wave, so that it spreads over as
+// many CUs as it has batches.
+struct ContigGrid {
+  int blocks;
+  int waves;
+};
+inline ContigGrid contig_grid(int64_t n_batches, int W, int per_wave, int per_cu) {
+  const int64_t cus = device_cu_count();
+  if (n_batches >= W * cus) return ContigGrid{spread_blocks(n_batches, W, per_wave, per_cu), W};
+  const int w = n_batches > cus ? static_cast<int>((n_batches + cus - 1) / cus) : 1;  // 1 .. W
+  return ContigGrid{static_cast<int>(n_batches > 0 ? (n_batches + w - 1) / w : 1), w};
+}
+
 // Launchers (return hipError_t of the launch).  All sizes already validated.
 // trits: store the three-level code five indices per byte (26 B per group).
 hipError_t launch_quantize(const void* w, bool bf16, bool trits, int64_t rows, int64_t cols,

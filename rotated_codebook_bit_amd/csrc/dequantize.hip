@@ -488,17 +488,9 @@ dequantize_ragged(const uint8_t* __restrict__ packed, const uint16_t* __restrict
 // with fewer than W batches per CU takes smaller blocks, so its batches
 // spread over more CUs (256x512, 16 batches: 16 one-wave blocks instead of
 // two of eight).
-struct ContigGrid {
-  int blocks;
-  int waves;
-};
 template <bool BF16OUT>
 ContigGrid dequant_grid(int64_t n_batches) {
-  constexpr int W = contig_waves(BF16OUT);
-  const int64_t cus = device_cu_count();
-  if (n_batches >= W * cus) return ContigGrid{spread_blocks(n_batches, W, 1, kBlocksPerCu), W};
-  const int w = n_batches > cus ? static_cast<int>((n_batches + cus - 1) / cus) : 1;  // 1 .. W
-  return ContigGrid{static_cast<int>((n_batches + w - 1) / w), w};
+  return contig_grid(n_batches, contig_waves(BF16OUT), 1, kBlocksPerCu);
 }
 
 template <int SB, bool BF16OUT, bool TRITS>

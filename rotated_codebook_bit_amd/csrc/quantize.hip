@@ -446,10 +446,12 @@ quantize_contig(QuantJob job, QuantParams p) {
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  // Blocks have 1 to W waves (quant_grid).
+  const int waves = __builtin_amdgcn_readfirstlane(blockDim.x / kWave);
   uint8_t* const buf = lds + wave * WAVE_BYTES;
   const int64_t n_batches = job.n_batches;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * W;
-  int64_t batch = static_cast<int64_t>(blockIdx.x) * W + wave;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * waves;
+  int64_t batch = static_cast<int64_t>(blockIdx.x) * waves + wave;
   if (batch >= n_batches) return;
   int d = 0;
 
@@ -911,6 +913,15 @@ hipError_t launch_fq_types(const void* w, bool bf16_in, int64_t rows, int64_t co
                   : launch_fq<L, false, false>(w, rows, cols, p, lv, out, s);
 }
 
+// Grid of the contiguous quantize kernel: a few batches per wave in blocks of
+// quant_waves waves; a call with fewer than that many batches per CU takes
+// smaller blocks, one batch per wave, so its batches spread over more CUs.
+template <bool BF16>
+ContigGrid quant_grid(int64_t n_batches) {
+  constexpr int W = quant_waves(BF16);
+  return contig_grid(n_batches, W, quant_batches_per_wave(BF16), floor_blocks_per_cu(BF16, W));
+}
+
 template <int L, bool BF16, bool TRITS>
 hipError_t launch_l(const void* w, int64_t rows, int64_t cols, const QuantParams& p,
                     uint8_t* packed, uint16_t* norms, hipStream_t s) {
@@ -920,10 +931,10 @@ hipError_t launch_l(const void* w, int64_t rows, int64_t cols, const QuantParams
     const int64_t n_batches = (n_groups + kWave - 1) / kWave;
     // Each wave loops over a few batches, so the next batch's DMA overlaps
     // the current arithmetic.
-    constexpr int W = quant_waves(BF16);
-    const int blocks = spread_blocks(n_batches, W, quant_batches_per_wave(BF16), floor_blocks_per_cu(BF16, W));
+    const ContigGrid g = quant_grid<BF16>(n_batches);
     const QuantJob job{wb, packed, norms, n_groups, TensorTable<QuantDesc>{nullptr, nullptr, 0}, n_batches};
-    hipLaunchKernelGGL((quantize_contig<L, BF16, false, TRITS>), dim3(blocks), dim3(W * kWave), 0, s, job, p);
+    hipLaunchKernelGGL((quantize_contig<L, BF16, false, TRITS>), dim3(g.blocks), dim3(g.waves * kWave), 0, s, job,
+                       p);
   } else {
     const int64_t n_groups = rows * ((cols + kGroup - 1) / kGroup);
     const int blocks = static_cast<int>((n_groups + kBlock - 1) / kBlock);
@@ -937,11 +948,10 @@ template <int L, bool BF16, bool TRITS>
 hipError_t launch_many_l(const QuantParams& p, TensorTable<QuantDesc> contig, int64_t contig_batches,
                          TensorTable<QuantDesc> ragged, int64_t ragged_groups, hipStream_t s) {
   if (contig_batches > 0) {
-    constexpr int W = quant_waves(BF16);
-    const int blocks =
-        spread_blocks(contig_batches, W, quant_batches_per_wave(BF16), floor_blocks_per_cu(BF16, W));
+    const ContigGrid g = quant_grid<BF16>(contig_batches);
     const QuantJob job{nullptr, nullptr, nullptr, 0, contig, contig_batches};
-    hipLaunchKernelGGL((quantize_contig<L, BF16, true, TRITS>), dim3(blocks), dim3(W * kWave), 0, s, job, p);
+    hipLaunchKernelGGL((quantize_contig<L, BF16, true, TRITS>), dim3(g.blocks), dim3(g.waves * kWave), 0, s, job,
+                       p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

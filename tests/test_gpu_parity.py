@@ -199,6 +199,25 @@ def test_bf16_output_is_rounded_f32_output(bits, levels):
         same(f16, f32, "fake quant")
 
 
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+# Between one and a few batches per CU: the contiguous kernels then launch
+# blocks of fewer waves.  201 x 16256: 25,527 groups, 399 batches (two waves
+# per block for quantize, both input types, and dequantize); 353 x 16256:
+# 44,831 groups, 701 batches (three for quantize from bf16 and dequantize),
+# each with a partial last batch.
+@pytest.mark.parametrize("shape", [(201, 16256), (353, 16256)])
+def test_small_call_grids(bits, dtype, shape, levels):
+    rng = np.random.default_rng(zlib.crc32(repr(("grid", bits, dtype, shape)).encode()))
+    w = (rng.standard_normal(shape) * 0.02).astype(np.float32)
+    if dtype == "bf16":
+        b = W.f32_to_bf16_bits(w)
+        run_case(f"grid {dtype}{shape}", W.bf16_bits_to_f32(b).astype(np.float64), to_dev_bf16(b), bits,
+                 levels[bits])
+    else:
+        run_case(f"grid {dtype}{shape}", w.astype(np.float64), to_dev_f32(w), bits, levels[bits])
+
 # -- the 45.5M-parameter set --------------------------------------------------------
 
 def test_needle2_set(levels):
