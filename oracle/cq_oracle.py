@@ -27,8 +27,8 @@ describe, with dense matrices where the pages use dense matrices.  Sources
   Initialization, §Iterative Refinement of Quantization Levels,
   §Ternary Special Case Handling, §Production Codebook Generation and Caching.
 
-Readings where the pages are silent or ambiguous are listed in DESIGN.md;
-the ones that shape this file are repeated next to the code they affect.
+Where the pages are silent or ambiguous, the reading taken is stated next to
+the code it affects.
 
 Parity pins: every public function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, textbook values, brute force or hand-worked examples.

@@ -125,8 +125,8 @@ def test_two_bit_levels_match_textbook(oracle_levels):
 
 
 def test_seed0_levels_regression(oracle_levels):
-    # Seed-0 Lloyd-Max levels computed separately for the design survey of this
-    # library (an independent script); six printed decimals.
+    # Seed-0 Lloyd-Max levels computed separately, before this oracle was
+    # written (an independent script); six printed decimals.
     want = {
         1: [-0.792722, 0.800951],
         2: [-1.506671, -0.451441, 0.452947, 1.509933],
