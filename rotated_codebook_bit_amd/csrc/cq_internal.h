@@ -296,6 +296,9 @@ struct MatvecPlan {
   int pair_rows_per_wave;
 };
 MatvecPlan matvec_plan(int sbits, int nb, const MatvecDesc* descs, int n);
+// Batch rows per product-kernel launch for a call of `batch` rows over the n
+// matrices of descs: 1 where the pair-table kernel takes each row, else 8.
+int matvec_chunk(int sbits, int64_t batch, const MatvecDesc* descs, int n);
 
 // Activation rotations run one wave per 128-group when a call has fewer
 // than this many groups (a thread per group would leave most CUs idle), else

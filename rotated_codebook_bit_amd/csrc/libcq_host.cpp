@@ -842,9 +842,10 @@ int cq_dequant_matvec_many(int n, const cq_matvec_desc* descs, int bits, int gro
   }
   if (act.empty()) return CQ_OK;
   const int na = static_cast<int>(act.size());
-  // Batch rows go through the product kernel in chunks of at most 8.
-  const int nb_full = static_cast<int>(batch < 8 ? batch : 8);
-  const int nb_last = static_cast<int>(batch - 8 * ((batch - 1) / 8));
+  // Batch rows go through the product kernel in chunks of `chunk` rows.
+  const int chunk = cq::matvec_chunk(sb, batch, act.data(), na);
+  const int nb_full = static_cast<int>(batch < chunk ? batch : chunk);
+  const int nb_last = static_cast<int>(batch - chunk * ((batch - 1) / chunk));
   const cq::MatvecPlan plan0 = cq::matvec_plan(sb, nb_full, act.data(), na);
   const cq::MatvecPlan plan1 = cq::matvec_plan(sb, nb_last, act.data(), na);
   const int rb0 = plan0.rows_per_block, rb1 = plan1.rows_per_block;
@@ -883,8 +884,8 @@ int cq_dequant_matvec_many(int n, const cq_matvec_desc* descs, int bits, int gro
     rc = hip_status(cq::launch_table_init(c, table, g_dev, b0_dev, b1_dev, s), "table launch");
   }
   if (!rc) rc = hip_status(cq::launch_rotate(table, g_dev, na, gstart[na], group_size, xr, s), "rotate launch");
-  for (int64_t b0 = 0; b0 < batch && !rc; b0 += 8) {
-    const int nb = static_cast<int>(batch - b0 < 8 ? batch - b0 : 8);
+  for (int64_t b0 = 0; b0 < batch && !rc; b0 += chunk) {
+    const int nb = static_cast<int>(batch - b0 < chunk ? batch - b0 : chunk);
     const bool full = nb == nb_full;
     rc = hip_status(cq::launch_matvec(table, full ? b0_dev : b1_dev, na, full ? bstart0[na] : bstart1[na],
                                       sb, lv, xr, b0, nb, full ? plan0 : plan1, group_size, s),

@@ -27,10 +27,10 @@
 // accumulates NB partial sums per row.  The block reduces each group's RB x
 // NB partials through LDS in a fixed order, so results are deterministic.
 //
-// One batch row with 2-bit codes (a decode step) takes matvec_pair_kernel
-// instead: per column pair it tabulates the 16 partial products a 4-bit
-// code pair can select, so the inner loop is one conflict-free LDS read and
-// one add per two weights (see the comment above that kernel).
+// One batch row with 2-bit codes (a decode step), and large calls of up to 8
+// rows, take matvec_pair_kernel instead, one launch per batch row: per column pair it tabulates the 16 partial products
+// a 4-bit code pair can select, so the inner loop is one conflict-free LDS
+// read and one add per two weights (see the comment above that kernel).
 
 #include "cq_internal.h"
 
@@ -557,6 +557,20 @@ constexpr int kMaxRowGroups = 8;
 // rows of codes (4 k bytes) fit its 32-bit buffer range.
 constexpr int64_t kPairMaxK = int64_t(1) << 28;
 constexpr bool use_pairs(int sb, int nb, int64_t max_k) { return sb == 2 && nb == 1 && max_k <= kPairMaxK; }
+// Large calls of 2 to kPairMaxBatch batch rows with 2-bit codes run the
+// pair-table kernel once per row, reading the codes once per row; other
+// calls take the byte-table kernel eight rows at a time.  Call times on
+// subsets of the 7B-shaped model's matrices, per-row pairs / byte table (us):
+// 11 MB of codes: batch 2 43-46 / 42, batch 8 78-83 / 50; 51 MB: batch 2
+// 55-56 / 72, batch 4 99-105 / 102, batch 8 185-235 / 142; 202 MB: batch 2
+// 158-160 / 196, batch 4 306-308 / 267, batch 8 594-603 / 499; 1.65 GB:
+// batch 2 823-907 / 1090, batch 4 1577-1594 / 1922, batch 8 3069-3084 / 3686.
+// A pair launch costs about bytes / 4.3 TB/s + 28 us there, the byte table
+// about 1.16 (batch 4) to 2.23 (batch 8) us per MB, which puts the switch
+// for batches 3-8 at 480-610 MB; batch 2 switches between 11 and 51 MB.
+constexpr int64_t kPairMaxBatch = 8;
+constexpr int64_t kPairMinBytesBatch2 = int64_t(32) << 20;
+constexpr int64_t kPairMinBytes = int64_t(512) << 20;
 
 template <int SB, int NB>
 hipError_t launch_nb(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks,
@@ -596,6 +610,16 @@ void launch_rotate_threads(const MatvecDesc* table, const int64_t* gstart, int n
 constexpr int log2_group(int g) { return g == 32 ? 5 : g == 64 ? 6 : g == 256 ? 8 : 7; }
 
 }  // namespace km
+
+int matvec_chunk(int sbits, int64_t batch, const MatvecDesc* descs, int n) {
+  int64_t max_k = 0;
+  for (int i = 0; i < n; ++i) max_k = descs[i].k > max_k ? descs[i].k : max_k;
+  if (sbits != 2 || max_k > km::kPairMaxK || batch > km::kPairMaxBatch) return 8;
+  int64_t bytes = 0;  // 2-bit codes: k / 4 bytes per row
+  for (int i = 0; i < n; ++i) bytes += descs[i].n_out * (descs[i].k / 4);
+  if (batch == 1 || bytes >= km::kPairMinBytes) return 1;
+  return batch == 2 && bytes >= km::kPairMinBytesBatch2 ? 1 : 8;
+}
 
 MatvecPlan matvec_plan(int sbits, int nb, const MatvecDesc* descs, int n) {
   int64_t max_k = 0;

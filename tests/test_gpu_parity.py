@@ -406,12 +406,15 @@ def test_matvec_many(batch, levels):
             check_matvec(y, x.astype(np.float64) @ w_hat.T, x, w_hat)
 
 
-@pytest.mark.parametrize("bits,batch", [(2, 8), (2, 3), (3, 5), (4, 8), (O.TERNARY, 2), (4, 12)])
+@pytest.mark.parametrize("bits,batch", [(2, 10), (2, 8), (2, 3), (3, 5), (4, 8), (O.TERNARY, 2), (4, 12)])
 def test_matvec_row_groups(bits, batch, levels):
     """Calls with enough rows that the byte-table kernel gives each block
     several groups of rows: a 16401-row single-pass matrix (its last block
     holds a one-row group), a matrix whose k spans three passes, and a small
-    one; the batches give blocks of 8, 4 and 2 groups of 4, 8 and 16 rows."""
+    one; the batches give blocks of 8, 4 and 2 groups of 4, 8 and 16 rows.
+    2-bit codes take the byte-table kernel here (a call this small runs the
+    pair kernel per row only at batch 1); batch 10 is a chunk of 8 rows and
+    one of 2."""
     lv = levels[bits]
     shapes = [(16401, 256), (100, 8320), (37, 384)]
     rng = np.random.default_rng(zlib.crc32(repr(("row_groups", bits, batch)).encode()))
@@ -453,6 +456,36 @@ def test_matvec_many_large_call(levels):
     cq.dequant_matvec_many(items, 2, lv, 1)
     for (x, w_hat), it in zip(refs, items):
         check_matvec(host(it[5]), x.astype(np.float64) @ w_hat.T, x, w_hat)
+
+
+@pytest.mark.parametrize("batch,rows,n_mat", [(2, 4096, 4), (3, 16384, 8)])
+def test_matvec_pair_rows_large_call(batch, rows, n_mat, levels):
+    """Large 2-bit calls of several batch rows run the pair-table kernel once
+    per row: 64 MiB of codes at batch 2, 512 MiB at batch 3.  Random codes and
+    norms (uniform codes, norms 0.5-2); 48 sampled rows per matrix, the first
+    and last among them, are checked against the oracle."""
+    lv = levels[2]
+    k = 16384
+    gen = torch.Generator(device=DEV).manual_seed(1000 * batch + n_mat)
+    rng = np.random.default_rng(batch)
+    items = []
+    for _ in range(n_mat):
+        p = torch.randint(0, 256, (rows, k // O.GROUP, 32), dtype=torch.uint8, device=DEV, generator=gen)
+        nv = (torch.rand((rows, k // O.GROUP), device=DEV, generator=gen) * 1.5 + 0.5).half()
+        x = rng.standard_normal((batch, k)).astype(np.float32)
+        y = torch.full((batch, rows), float("nan"), dtype=torch.float32, device=DEV)
+        items.append((p, nv, rows, k, to_dev_f32(x), y))
+    say(f"matvec pair rows batch={batch}, {n_mat} matrices of {rows}x{k}")
+    cq.dequant_matvec_many(items, 2, lv, batch)
+    torch.cuda.synchronize()
+    for p, nv, n_out, _, xd, y in items:
+        sel = np.unique(np.concatenate([[0, n_out - 1], rng.choice(n_out, 46, replace=False)]))
+        pk = host(p[torch.from_numpy(sel).to(DEV)])  # [rows, groups, 32]
+        n16 = host(nv[torch.from_numpy(sel).to(DEV)].view(torch.int16)).view(np.uint16)
+        w_hat = O.dequantize(pk, n16, len(sel), k, 2, lv)
+        x = host(xd)
+        check_matvec(host(y)[:, sel], x.astype(np.float64) @ w_hat.T, x, w_hat)
+        del p
 
 
 @pytest.mark.parametrize("batch", [8, 1])
