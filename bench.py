@@ -152,8 +152,9 @@ def configs_report(torch) -> dict:
     rep = {"report": "configs", "timing": "HIP events around single calls; median of 15 after 3 warm-up "
                                           "calls; cold = a 1 GiB device write before each timed call"}
 
-    # C1: latency of the smallest case.
-    lv2 = cq.codebook(2)
+    # C1: latency of the smallest case.  Every GPU call here passes NULL
+    # levels: the library's built-in codebook.
+    lv2 = None
     w = torch.from_numpy(W.small()).to(dev)
     pk, nm = cq.quantize(w, 2, lv2)
     out = torch.empty_like(w)
@@ -189,7 +190,7 @@ def configs_report(torch) -> dict:
     w64 = wb.double()
     rep["C3"] = {}
     for bits, name in ((cq.TERNARY, "ternary"), (2, "2"), (3, "3"), (4, "4")):
-        lv = cq.codebook(bits)
+        lv = None
         pk, nm = cq.quantize(wb, bits, lv)
         o = cq.dequantize(pk, nm, 4096, 4096, bits, lv)
         nbq = wb.numel() * 2 + pk.numel() + nm.numel() * 2
@@ -238,8 +239,10 @@ def cpu_baseline_configs() -> dict:
     import rotated_codebook_bit_amd as cq
     res = {}
 
+    samples = W.lloyd_samples()
+
     def run(name, ws, bits, extra=None):
-        lv = cq.codebook(bits)
+        lv = O.runtime_levels(O.codebook(bits, samples)).astype(np.float32)
         t0 = time.perf_counter()
         n = 0
         for w in ws:
@@ -277,8 +280,7 @@ def cpu_baseline() -> dict:
         blas_threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
         blas_threads = os.cpu_count() or 1
-    import rotated_codebook_bit_amd as cq
-    levels = cq.codebook(BITS)
+    levels = O.runtime_levels(O.codebook(BITS, W.lloyd_samples())).astype(np.float32)
     rng = np.random.default_rng(0)
     shapes = W.llama7b_shapes()
     layer = shapes[:7] + shapes[-1:]
@@ -336,7 +338,7 @@ def main():
     import rotated_codebook_bit_amd as cq
     from rotated_codebook_bit_amd import workloads as W
 
-    levels = cq.codebook(BITS)
+    levels = None  # the library's built-in codebook
     shapes = W.llama7b_shapes()
     log("generating the 7B-shaped bf16 model on the device")
     buf, offsets = W.llama7b_device("cuda")

@@ -39,10 +39,11 @@
  *   - Norm layout: norms[rows][ceil(cols/G)], IEEE binary16 bit patterns,
  *     round to nearest even from the float32 norm; norms above 65504 store
  *     +Inf.
- *   - levels (host, nullable where stated): n_levels float32 codebook levels
- *     in N(0,1) units (before the 1/sqrt(G) scaling), strictly ascending.
- *     n_levels must be 3 for CQ_TERNARY and CQ_TERNARY_TRITS, 2^bits
- *     otherwise.
+ *   - levels (host, nullable): n_levels float32 codebook levels in N(0,1)
+ *     units (before the 1/sqrt(G) scaling), strictly ascending.  n_levels
+ *     must be 3 for CQ_TERNARY and CQ_TERNARY_TRITS, 2^bits otherwise.
+ *     NULL selects the built-in table of the width (the levels cq_codebook
+ *     returns); n_levels is then ignored.
  *   - group_size: the device calls take 32, 64, 128 or 256 ("Cactus Quants
  *     CQ2-bit Quantization: Extreme Compression for Edge LLMs", FAQ on group
  *     size); the GEMM calls also need k to be a multiple of 128 (of 256 at
@@ -99,7 +100,12 @@ typedef enum { CQ_F32 = 0, CQ_BF16 = 1 } cq_dtype;
 #define CQ_GROUP 128
 #define CQ_MAX_LEVELS 16
 
-/* Sizes of the quantized form of one rows x cols tensor.
+/* Sizes of the quantized form of one rows x cols tensor: the last axis is
+ * zero-padded to a multiple of the group size and cut into groups ("Cactus
+ * Quants CQ2-bit Quantization: Extreme Compression for Edge LLMs", section
+ * Group-wise Weight Partitioning), each stored as packed indices ("How
+ * CQ2-bit Quantization Contributes to Needle 2's Small Footprint", section
+ * Per-Group Storage Breakdown).
  * n_groups = rows * ceil(cols / group_size);
  * packed_bytes = n_groups * B (B the bytes per group of the packed layout
  * above: group_size * sbits / 8, or ceil(group_size / 5) for trit storage).
@@ -116,40 +122,69 @@ int cq_layout(int64_t rows, int64_t cols, int bits, int group_size,
 int cq_model_bytes(int n_tensors, const int64_t* rows, const int64_t* cols,
                    int bits, int group_size, uint64_t* bytes_out);
 
-/* Codebook levels in N(0,1) units, written as float32 to levels_out (host,
- * room for CQ_MAX_LEVELS), count to *n_levels (host).
- * CQ_TERNARY and CQ_TERNARY_TRITS return the fixed levels -1.2240064, 0,
- * 1.2240064
- * ("How Quantization Codebooks Are Trained in Cactus Quants", section Ternary
- * Special Case Handling) and ignores samples.  Other widths run 1-D Lloyd-Max
- * (k-means) with 2^bits levels on the n_samples host samples (double), as the
- * same page describes in sections Gaussian Sampling and Initialization and
- * Iterative Refinement of Quantization Levels: sort, quantile initialisation
- * at sorted position floor((k + 1/2) n / L), then `iters` rounds of midpoint
- * boundaries, assignment (a sample equal to a boundary goes to the lower
- * cell) and cell means; an empty cell keeps its level; result sorted.  The
- * pages draw 400,000 standard-normal samples and run 200 iterations.
- * Host only; the samples array is not modified. */
-int cq_codebook(int bits, const double* samples, int64_t n_samples, int iters,
-                float* levels_out, int* n_levels);
+/* The built-in codebook of a width: float32 levels in N(0,1) units written
+ * to levels_out (host, room for CQ_MAX_LEVELS), their count to *n_levels
+ * (host).  These are the levels every call uses when its `levels` argument
+ * is NULL.
+ * CQ_TERNARY and CQ_TERNARY_TRITS: the fixed levels -1.2240064, 0, 1.2240064
+ * ("How Quantization Codebooks Are Trained in Cactus Quants: Lloyd-Max on
+ * Gaussian Data", section Ternary Special Case Handling).  Widths 1-4: the
+ * same page's recipe (sections Gaussian Sampling and Initialization,
+ * Iterative Refinement of Quantization Levels, Production Codebook
+ * Generation and Caching): 1-D Lloyd-Max with 2^bits levels, 200 rounds,
+ * on 400,000 standard-normal samples.  The pages draw the samples from a
+ * seeded NumPy generator; this library draws them from its own documented
+ * deterministic generator: SplitMix64 words from state 0, each turned into
+ * a uniform u = ((w >> 11) + 1) * 2^-53 in (0, 1], consecutive pairs
+ * (u1, u2) turned into sqrt(-2 ln u1) cos(2 pi u2) and
+ * sqrt(-2 ln u1) sin(2 pi u2) (Box-Muller), each normal taken with its
+ * negation (100,000 pairs, a sample set symmetric about 0).  Computed on
+ * first use, cached,
+ * immutable.  The levels are within sampling noise of the Gaussian Lloyd-Max
+ * optimum (2 bits: about +-0.4528, +-1.510), not bit-identical to the
+ * pages' own draws.  Host only. */
+int cq_codebook(int bits, float* levels_out, int* n_levels);
+
+/* Lloyd-Max on caller-supplied samples: the training recipe of
+ * cq_codebook run on the n_samples host doubles `samples` for `iters`
+ * rounds: sort, quantile initialisation at sorted position
+ * floor((k + 1/2) n / L), then per round midpoint boundaries, assignment
+ * (a sample equal to a boundary goes to the lower cell) and cell means; an
+ * empty cell keeps its level; result sorted ("How Quantization Codebooks
+ * Are Trained in Cactus Quants", sections Gaussian Sampling and
+ * Initialization and Iterative Refinement of Quantization Levels).  The
+ * ternary widths return the fixed table and ignore the samples.  Host only;
+ * samples is not modified. */
+int cq_codebook_train(int bits, const double* samples, int64_t n_samples, int iters,
+                      float* levels_out, int* n_levels);
 
 /* Quantize w (rows x cols, dtype w_dtype = CQ_F32 or CQ_BF16) into packed
- * indices and binary16 norms (layouts above).  levels (host, required):
- * n_levels float32 levels.  Each group's index j is the number of decision
- * thresholds (midpoints of neighbouring levels) strictly below
- * sqrt(G) * y_j / ||y|| (y the rotated group); an all-zero group uses 0 for
- * that value.  The decision is taken in float32; values within about 1e-6
- * of a threshold may land on either side. */
+ * indices and binary16 norms (layouts above), the steps of "Cactus Quants
+ * CQ2-bit Quantization: Extreme Compression for Edge LLMs", section The
+ * CQ2-bit Implementation Pipeline: pad and group, rotate each group by the
+ * orthonormal Walsh-Hadamard matrix, normalise by the group's L2 norm,
+ * snap to the nearest level, store indices and the binary16 norm ("How
+ * CQ2-bit Quantization Contributes to Needle 2's Small Footprint", section
+ * Per-Group Storage Breakdown).  levels (host, nullable: built-in table).
+ * Each group's index j is the number of decision thresholds (midpoints of
+ * neighbouring levels, "How Quantization Codebooks Are Trained in Cactus
+ * Quants", section Iterative Refinement of Quantization Levels) strictly
+ * below sqrt(G) * y_j / ||y|| (y the rotated group); an all-zero group uses
+ * 0 for that value.  The decision is taken in float32; values within about
+ * 1e-6 of a threshold may land on either side. */
 int cq_quantize(const void* w, int w_dtype, int64_t rows, int64_t cols,
                 int bits, int group_size, const float* levels, int n_levels,
                 uint8_t* packed, uint16_t* norms, void* stream);
 
 /* Dequantize packed indices + binary16 norms to out (rows x cols, dtype
- * out_dtype = CQ_F32 or CQ_BF16, pad columns not written):
+ * out_dtype = CQ_F32 or CQ_BF16, pad columns not written): look the levels
+ * up, rescale by the stored norm and rotate back ("Cactus Quants CQ2-bit
+ * Quantization: Extreme Compression for Edge LLMs", section The CQ2-bit
+ * Implementation Pipeline), i.e.
  * x_hat = (norm / G) * H * levels[idx] with H the +-1 Sylvester-Hadamard
  * matrix, which equals (norm/sqrt(G)) * levels[idx] times the orthonormal
  * Hadamard matrix.  Computed in float32 (bf16 output rounds to nearest
- * even).  levels (host, required). */
+ * even).  levels (host, nullable: built-in table). */
 int cq_dequantize(const uint8_t* packed, const uint16_t* norms, int64_t rows,
                   int64_t cols, int bits, int group_size, const float* levels,
                   int n_levels, void* out, int out_dtype, void* stream);
@@ -229,7 +264,7 @@ int cq_dequantize_many(int n, const cq_dequant_desc* descs, int bits, int group_
  * output rounds to nearest even), both 16-byte aligned.  out == w with
  * w_dtype == out_dtype (in place) is allowed: every group is read in full
  * before it is written.  Any other overlap is CQ_ERR_ARG.  levels (host,
- * required). */
+ * nullable: built-in table). */
 int cq_fake_quant(const void* w, int w_dtype, int64_t rows, int64_t cols, int bits,
                   int group_size, const float* levels, int n_levels, void* out, int out_dtype,
                   void* stream);

@@ -31,8 +31,10 @@ Where the pages are silent or ambiguous, the reading taken is stated next to
 the code it affects.
 
 Parity pins: every public function here is pinned by ``tests/test_oracle_*.py``
-against closed forms, textbook values, brute force or hand-worked examples.
-No function is "parity unpinned".
+against closed forms, textbook values, brute force or hand-worked examples;
+the tolerance helpers ``threshold_distance`` and ``admissible_indices`` by
+hand-worked values on a codebook whose thresholds are exact
+(``tests/test_oracle_band.py``).
 """
 
 from __future__ import annotations
@@ -467,7 +469,21 @@ def fake_quant(w: np.ndarray, bits: int, levels: np.ndarray, g: int = GROUP,
 
 def threshold_distance(z: np.ndarray, levels: np.ndarray) -> np.ndarray:
     """Distance (z units) from each normalised value to its nearest decision
-    threshold; used to decide which index differences are admissible."""
+    threshold (the midpoints of *Codebook training* §Iterative Refinement),
+    element by element, same shape as z."""
     t = thresholds(runtime_levels(levels))
     z = np.asarray(z, dtype=np.float64)
     return np.min(np.abs(z[..., None] - t), axis=-1)
+
+
+def admissible_indices(z: np.ndarray, levels: np.ndarray, band: float):
+    """Indices a quantizer may return for the normalised value z when its own
+    value of z can be off by up to ``band`` (z units): every index the
+    nearest-level rule gives to some z' in [z - band, z + band].  The rule is
+    monotone in z', so these are the integers from the index of z - band to
+    the index of z + band.  Returns (lo, hi), each shaped like z."""
+    t = thresholds(runtime_levels(levels))
+    z = np.asarray(z, dtype=np.float64)
+    lo = np.searchsorted(t, z - band, side="left").astype(np.int64)
+    hi = np.searchsorted(t, z + band, side="left").astype(np.int64)
+    return lo, hi

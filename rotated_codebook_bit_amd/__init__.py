@@ -16,7 +16,7 @@ import numpy as np
 
 __all__ = [
     "TERNARY", "TERNARY_TRITS", "GROUP", "group_bytes", "repack", "CQError", "lib", "storage_bits", "n_levels", "layout",
-    "model_bytes", "codebook", "quantize", "dequantize", "dequant_matvec", "dequant_matvec_many",
+    "model_bytes", "codebook", "codebook_train", "quantize", "dequantize", "dequant_matvec", "dequant_matvec_many",
     "fake_quant", "blob_layout", "quantize_many", "dequantize_many", "dequant_gemm",
     "dequant_gemm_many",
 ]
@@ -68,8 +68,9 @@ def lib() -> ctypes.CDLL:
         L.cq_layout.argtypes = [i64, i64, i32, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)]
         L.cq_model_bytes.argtypes = [i32, ctypes.POINTER(i64), ctypes.POINTER(i64), i32, i32,
                                      ctypes.POINTER(ctypes.c_uint64)]
-        L.cq_codebook.argtypes = [i32, ctypes.POINTER(ctypes.c_double), i64, i32,
-                                  ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
+        L.cq_codebook.argtypes = [i32, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
+        L.cq_codebook_train.argtypes = [i32, ctypes.POINTER(ctypes.c_double), i64, i32,
+                                        ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
         L.cq_quantize.argtypes = [vp, i32, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_float), i32,
                                   vp, vp, vp]
         L.cq_dequantize.argtypes = [vp, vp, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_float), i32,
@@ -91,7 +92,7 @@ def lib() -> ctypes.CDLL:
                                         i32, vp, i64, vp, vp]
         L.cq_dequant_matvec_many.argtypes = [i32, ctypes.POINTER(MatvecDesc), i32, i32,
                                              ctypes.POINTER(ctypes.c_float), i32, i64, vp]
-        for name in ("cq_layout", "cq_model_bytes", "cq_codebook", "cq_quantize", "cq_dequantize",
+        for name in ("cq_layout", "cq_model_bytes", "cq_codebook", "cq_codebook_train", "cq_quantize", "cq_dequantize",
                      "cq_fake_quant", "cq_dequant_matvec", "cq_dequant_matvec_many", "cq_blob_layout",
                      "cq_quantize_many", "cq_dequantize_many", "cq_dequant_gemm",
                      "cq_dequant_gemm_many", "cq_repack"):
@@ -128,9 +129,17 @@ def n_levels(bits: int) -> int:
     return 3 if bits in (TERNARY, TERNARY_TRITS) else 1 << int(bits)
 
 
-def _levels_arg(levels) -> tuple[np.ndarray, ctypes.POINTER(ctypes.c_float)]:
+def _levels_arg(levels) -> tuple[np.ndarray | None, ctypes.POINTER(ctypes.c_float)]:
+    """(kept-alive array, pointer) for a levels argument; None passes NULL,
+    which selects the library's built-in table."""
+    if levels is None:
+        return None, ctypes.POINTER(ctypes.c_float)()
     arr = np.ascontiguousarray(np.asarray(levels, dtype=np.float32))
     return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+def _nlev(arr) -> int:
+    return 0 if arr is None else int(arr.size)
 
 
 def _stream_ptr(stream=None):
@@ -168,17 +177,23 @@ def model_bytes(shapes, bits: int, group_size: int = GROUP) -> int:
     return out.value
 
 
-def codebook(bits: int, samples=None, iters: int = 200) -> np.ndarray:
-    """float32 codebook levels in N(0,1) units.  ``samples`` (float64) are the
-    Lloyd-Max training draws; None uses the standard 400,000 seed-0 draws."""
-    if samples is None and bits not in (TERNARY, TERNARY_TRITS):
-        from .workloads import lloyd_samples
-        samples = lloyd_samples()
+def codebook(bits: int) -> np.ndarray:
+    """The built-in float32 codebook of a width (N(0,1) units): the table
+    every call uses when its levels argument is None."""
+    out = (ctypes.c_float * 16)()
+    n = ctypes.c_int()
+    _check("cq_codebook", lib().cq_codebook(bits, out, ctypes.byref(n)))
+    return np.array(out[:n.value], dtype=np.float32)
+
+
+def codebook_train(bits: int, samples, iters: int = 200) -> np.ndarray:
+    """float32 Lloyd-Max codebook (N(0,1) units) trained by the library on the
+    given float64 samples."""
     s = np.ascontiguousarray(np.zeros(0) if samples is None else samples, dtype=np.float64)
     out = (ctypes.c_float * 16)()
     n = ctypes.c_int()
-    _check("cq_codebook", lib().cq_codebook(bits, s.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
-                                            s.size, iters, out, ctypes.byref(n)))
+    _check("cq_codebook_train", lib().cq_codebook_train(
+        bits, s.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), s.size, iters, out, ctypes.byref(n)))
     return np.array(out[:n.value], dtype=np.float32)
 
 
@@ -231,7 +246,7 @@ def quantize(w, bits: int, levels, group_size: int = GROUP, packed=None, norms=N
     if norms is None:
         norms = torch.empty((rows, ng), dtype=torch.float16, device=w.device)
     lv, lvp = _levels_arg(levels)
-    _check("cq_quantize", lib().cq_quantize(_ptr(w), dt, rows, cols, bits, group_size, lvp, lv.size,
+    _check("cq_quantize", lib().cq_quantize(_ptr(w), dt, rows, cols, bits, group_size, lvp, _nlev(lv),
                                             _ptr(packed), _ptr(norms), _stream_ptr(stream)))
     return packed, norms
 
@@ -247,7 +262,7 @@ def dequantize(packed, norms, rows: int, cols: int, bits: int, levels, out_dtype
         out = torch.empty((rows, cols), dtype=out_dtype, device=packed.device)
     lv, lvp = _levels_arg(levels)
     _check("cq_dequantize", lib().cq_dequantize(_ptr(packed), _ptr(norms), rows, cols, bits,
-                                                group_size, lvp, lv.size, _ptr(out), dt,
+                                                group_size, lvp, _nlev(lv), _ptr(out), dt,
                                                 _stream_ptr(stream)))
     return out
 
@@ -270,7 +285,7 @@ def fake_quant(w, bits: int, levels, out_dtype=None, group_size: int = GROUP, ou
     rows, cols = _rows_cols(w.shape)
     lv, lvp = _levels_arg(levels)
     _check("cq_fake_quant", lib().cq_fake_quant(_ptr(w), dts[w.dtype], rows, cols, bits, group_size,
-                                                lvp, lv.size, _ptr(out), dts[out.dtype],
+                                                lvp, _nlev(lv), _ptr(out), dts[out.dtype],
                                                 _stream_ptr(stream)))
     return out
 
@@ -290,7 +305,7 @@ def dequant_matvec(packed, norms, n_out: int, k: int, bits: int, levels, x, grou
         y = torch.empty((batch, n_out), dtype=torch.float32, device=x.device)
     lv, lvp = _levels_arg(levels)
     _check("cq_dequant_matvec", lib().cq_dequant_matvec(_ptr(packed), _ptr(norms), n_out, k, bits,
-                                                        group_size, lvp, lv.size, _ptr(x2), batch,
+                                                        group_size, lvp, _nlev(lv), _ptr(x2), batch,
                                                         _ptr(y), _stream_ptr(stream)))
     return y
 
@@ -309,7 +324,7 @@ def dequant_matvec_many(items, bits: int, levels, batch: int, group_size: int = 
     n = len(items)
     arr = _matvec_descs(items)
     lv, lvp = _levels_arg(levels)
-    _check("cq_dequant_matvec_many", lib().cq_dequant_matvec_many(n, arr, bits, group_size, lvp, lv.size,
+    _check("cq_dequant_matvec_many", lib().cq_dequant_matvec_many(n, arr, bits, group_size, lvp, _nlev(lv),
                                                                   batch, _stream_ptr(stream)))
     return [it[5] for it in items]
 
@@ -372,7 +387,7 @@ def quantize_many(ws, bits: int, levels, blob=None, group_size: int = GROUP, str
             nm = blob[no[i]:no[i] + 2 * rows * ng].view(torch.float16).view(rows, ng)
             out_views.append((pk, nm))
     lv, lvp = _levels_arg(levels)
-    _check("cq_quantize_many", lib().cq_quantize_many(len(ws), arr, dt, bits, group_size, lvp, lv.size,
+    _check("cq_quantize_many", lib().cq_quantize_many(len(ws), arr, dt, bits, group_size, lvp, _nlev(lv),
                                                       _stream_ptr(stream)))
     return blob, out_views
 
@@ -396,7 +411,7 @@ def dequantize_many(items, bits: int, levels, out_dtype=None, outs=None, group_s
         [it[3] for it in items], [_ptr_or_0(o) for o in outs]))
     lv, lvp = _levels_arg(levels)
     _check("cq_dequantize_many", lib().cq_dequantize_many(len(items), arr, bits, group_size, lvp,
-                                                          lv.size, dt, _stream_ptr(stream)))
+                                                          _nlev(lv), dt, _stream_ptr(stream)))
     return outs
 
 
@@ -414,7 +429,7 @@ def dequant_gemm(packed, norms, n_out: int, k: int, bits: int, levels, x, group_
         y = torch.empty((batch, n_out), dtype=torch.float32, device=x.device)
     lv, lvp = _levels_arg(levels)
     _check("cq_dequant_gemm", lib().cq_dequant_gemm(_ptr(packed), _ptr(norms), n_out, k, bits, group_size,
-                                                    lvp, lv.size, _ptr(x), batch, _ptr(y),
+                                                    lvp, _nlev(lv), _ptr(x), batch, _ptr(y),
                                                     _stream_ptr(stream)))
     return y
 
@@ -425,7 +440,7 @@ def dequant_gemm_many(items, bits: int, levels, batch: int, group_size: int = GR
     n = len(items)
     arr = _matvec_descs(items)
     lv, lvp = _levels_arg(levels)
-    _check("cq_dequant_gemm_many", lib().cq_dequant_gemm_many(n, arr, bits, group_size, lvp, lv.size, batch,
+    _check("cq_dequant_gemm_many", lib().cq_dequant_gemm_many(n, arr, bits, group_size, lvp, _nlev(lv), batch,
                                                               _stream_ptr(stream)))
     return [it[5] for it in items]
 

@@ -74,8 +74,15 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return na && nb && x < y + nb && y < x + na;
 }
 
-int check_levels(const float* levels, int n_levels, int expect) {
-  if (!levels) return fail(CQ_ERR_NULL, "levels is NULL");
+const float* builtin_levels(int bits);
+
+// Validates a caller's codebook; NULL selects the built-in table of the
+// width (n_levels is then ignored) and `levels` is pointed at it.
+int check_levels(const float*& levels, int n_levels, int expect, int bits) {
+  if (!levels) {
+    levels = builtin_levels(bits);
+    return CQ_OK;
+  }
   if (n_levels != expect)
     return fail(CQ_ERR_ARG, "n_levels=%d, this bit-width needs %d", n_levels, expect);
   for (int i = 0; i < n_levels; ++i) {
@@ -150,6 +157,107 @@ int first_conflict(std::vector<Span> outs, const std::vector<Span>& ins) {
 }
 
 int hip_status(hipError_t e, const char* what);
+
+// 1-D Lloyd-Max (k-means) with L levels on sorted samples x, as "How
+// Quantization Codebooks Are Trained in Cactus Quants: Lloyd-Max on Gaussian
+// Data" describes it (sections Gaussian Sampling and Initialization and
+// Iterative Refinement of Quantization Levels): level k starts at the sorted
+// sample floor((k + 1/2) n / L); each round puts the boundaries at the
+// midpoints of neighbouring levels, gives every sample to the cell whose
+// lower boundary it strictly exceeds (a sample equal to a boundary stays in
+// the lower cell) and moves each level to the mean of its cell; an empty
+// cell keeps its level.  Cells are contiguous runs of the sorted array, so a
+// round needs only the L-1 split positions.  Writes the sorted levels as
+// float32.
+void lloyd_max_sorted(const std::vector<double>& x, int L, int iters, float* levels_out) {
+  const int64_t n = static_cast<int64_t>(x.size());
+  std::vector<double> c(L);
+  for (int k = 0; k < L; ++k) c[k] = x[((2 * static_cast<int64_t>(k) + 1) * n) / (2 * L)];
+  std::vector<int64_t> start(L + 1);
+  for (int it = 0; it < iters; ++it) {
+    start[0] = 0;
+    start[L] = n;
+    for (int k = 1; k < L; ++k) {
+      const double edge = 0.5 * (c[k - 1] + c[k]);
+      // First sample strictly above the boundary.
+      start[k] = std::upper_bound(x.begin(), x.end(), edge) - x.begin();
+    }
+    for (int k = 0; k < L; ++k) {
+      const int64_t lo = start[k], hi = start[k + 1];
+      if (hi <= lo) continue;  // empty cell keeps its level
+      long double sum = 0.0L;
+      for (int64_t i = lo; i < hi; ++i) sum += x[i];
+      c[k] = static_cast<double>(sum / static_cast<long double>(hi - lo));
+    }
+  }
+  std::sort(c.begin(), c.end());
+  for (int k = 0; k < L; ++k) levels_out[k] = static_cast<float>(c[k]);
+}
+
+// ---- Built-in codebook ---------------------------------------------------------
+//
+// The training recipe of the codebook page (400,000 standard-normal samples,
+// quantile initialisation, 200 Lloyd-Max rounds), run once per width on
+// samples from this library's own deterministic generator:
+//   - uniform 64-bit words from SplitMix64 (G. Steele, D. Lea, C. Flood,
+//     "Fast Splittable Pseudorandom Number Generators", OOPSLA 2014) with
+//     state 0: the state advances by 0x9E3779B97F4A7C15 and each output is
+//     the state mixed by z ^= z >> 30, z *= 0xBF58476D1CE4E5B9,
+//     z ^= z >> 27, z *= 0x94D049BB133111EB, z ^= z >> 31;
+//   - a uniform double u = ((w >> 11) + 1) * 2^-53 in (0, 1] per word;
+//   - normals by the Box-Muller transform of consecutive (u1, u2):
+//     sqrt(-2 ln u1) * cos(2 pi u2), then sqrt(-2 ln u1) * sin(2 pi u2);
+//   - each normal is used together with its negation (antithetic pairs), so
+//     the 400,000 samples are 100,000 Box-Muller pairs and the sample set
+//     is symmetric about 0.  Without it a finite sample's Lloyd-Max fixed
+//     point shifts with the sample's own asymmetry: the first 400,000
+//     normals of this generator put the 2-bit levels 7e-3 off the Gaussian
+//     optimum, their symmetrised half within 1.5e-3.
+// The ternary width has the fixed table of the page's section Ternary Special
+// Case Handling.  The tables are built on first use and never change.
+constexpr int64_t kBuiltinSamples = 400000;  // a multiple of 4
+constexpr int kBuiltinIters = 200;
+const float kTernaryLevels[3] = {-1.2240064f, 0.0f, 1.2240064f};
+
+uint64_t splitmix64(uint64_t& state) {
+  state += 0x9E3779B97F4A7C15ull;
+  uint64_t z = state;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+std::vector<double> builtin_samples() {
+  std::vector<double> x(kBuiltinSamples);
+  uint64_t state = 0;
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int64_t i = 0; i < kBuiltinSamples; i += 4) {
+    const double u1 = static_cast<double>((splitmix64(state) >> 11) + 1) * 0x1.0p-53;
+    const double u2 = static_cast<double>((splitmix64(state) >> 11) + 1) * 0x1.0p-53;
+    const double r = std::sqrt(-2.0 * std::log(u1));
+    const double z0 = r * std::cos(two_pi * u2), z1 = r * std::sin(two_pi * u2);
+    x[i] = z0;
+    x[i + 1] = -z0;
+    x[i + 2] = z1;
+    x[i + 3] = -z1;
+  }
+  std::sort(x.begin(), x.end());
+  return x;
+}
+
+struct BuiltinTables {
+  float lv[5][cq::kMaxLevels];  // index = bits (1..4)
+  BuiltinTables() {
+    const std::vector<double> x = builtin_samples();
+    for (int bits = 1; bits <= 4; ++bits) lloyd_max_sorted(x, 1 << bits, kBuiltinIters, lv[bits]);
+  }
+};
+
+const float* builtin_levels(int bits) {
+  if (bits == CQ_TERNARY || bits == CQ_TERNARY_TRITS) return kTernaryLevels;
+  static const BuiltinTables tables;  // built once, thread-safe (C++11 static init)
+  return tables.lv[bits];
+}
 
 // Device table of one multi-tensor call: descriptors of the fast-path
 // (cols % 128 == 0) and ragged tensors, with their work-unit prefixes, in one
@@ -342,15 +450,24 @@ int cq_model_bytes(int n_tensors, const int64_t* rows, const int64_t* cols, int 
   return CQ_OK;
 }
 
-int cq_codebook(int bits, const double* samples, int64_t n_samples, int iters, float* levels_out,
-                int* n_levels) {
+int cq_codebook(int bits, float* levels_out, int* n_levels) {
+  g_last_error[0] = 0;
+  int L, rc;
+  if (!levels_out || !n_levels) return fail(CQ_ERR_NULL, "levels_out/n_levels is NULL");
+  if ((rc = check_bits(bits, true, &L))) return rc;
+  std::memcpy(levels_out, builtin_levels(bits), static_cast<size_t>(L) * sizeof(float));
+  *n_levels = L;
+  return CQ_OK;
+}
+
+int cq_codebook_train(int bits, const double* samples, int64_t n_samples, int iters, float* levels_out,
+                      int* n_levels) {
   g_last_error[0] = 0;
   int L, rc;
   if (!levels_out || !n_levels) return fail(CQ_ERR_NULL, "levels_out/n_levels is NULL");
   if ((rc = check_bits(bits, true, &L))) return rc;
   if (bits == CQ_TERNARY || bits == CQ_TERNARY_TRITS) {
-    static const float kTernary[3] = {-1.2240064f, 0.0f, 1.2240064f};
-    std::memcpy(levels_out, kTernary, sizeof(kTernary));
+    std::memcpy(levels_out, kTernaryLevels, sizeof(kTernaryLevels));
     *n_levels = 3;
     return CQ_OK;
   }
@@ -359,34 +476,9 @@ int cq_codebook(int bits, const double* samples, int64_t n_samples, int iters, f
   if (iters < 0) return fail(CQ_ERR_ARG, "iters < 0");
   for (int64_t i = 0; i < n_samples; ++i)
     if (!std::isfinite(samples[i])) return fail(CQ_ERR_ARG, "sample %lld is not finite", (long long)i);
-
-  // 1-D k-means on the sorted samples.  Cells are contiguous runs of the
-  // sorted array, so each round needs only the L-1 split positions.
   std::vector<double> x(samples, samples + n_samples);
   std::sort(x.begin(), x.end());
-  const int64_t n = n_samples;
-  std::vector<double> c(L);
-  for (int k = 0; k < L; ++k) c[k] = x[((2 * static_cast<int64_t>(k) + 1) * n) / (2 * L)];
-  std::vector<int64_t> start(L + 1);
-  for (int it = 0; it < iters; ++it) {
-    start[0] = 0;
-    start[L] = n;
-    for (int k = 1; k < L; ++k) {
-      const double edge = 0.5 * (c[k - 1] + c[k]);
-      // First sample strictly above the boundary: a sample equal to the
-      // boundary stays in the lower cell.
-      start[k] = std::upper_bound(x.begin(), x.end(), edge) - x.begin();
-    }
-    for (int k = 0; k < L; ++k) {
-      const int64_t lo = start[k], hi = start[k + 1];
-      if (hi <= lo) continue;  // empty cell keeps its level
-      long double s = 0.0L;
-      for (int64_t i = lo; i < hi; ++i) s += x[i];
-      c[k] = static_cast<double>(s / static_cast<long double>(hi - lo));
-    }
-  }
-  std::sort(c.begin(), c.end());
-  for (int k = 0; k < L; ++k) levels_out[k] = static_cast<float>(c[k]);
+  lloyd_max_sorted(x, L, iters, levels_out);
   *n_levels = L;
   return CQ_OK;
 }
@@ -400,7 +492,7 @@ int cq_quantize(const void* w, int w_dtype, int64_t rows, int64_t cols, int bits
   if (w_dtype != CQ_F32 && w_dtype != CQ_BF16) return fail(CQ_ERR_ARG, "unknown w_dtype %d", w_dtype);
   if (rows < 0 || cols < 0) return fail(CQ_ERR_ARG, "negative size");
   if ((rc = check_codec_group(group_size, bits))) return rc;
-  if ((rc = check_levels(levels, n_levels, L))) return rc;
+  if ((rc = check_levels(levels, n_levels, L, bits))) return rc;
   if (rows == 0 || cols == 0) return CQ_OK;
   if (!w || !packed || !norms) return fail(CQ_ERR_NULL, "w/packed/norms is NULL");
   if (!aligned(w, 16) || !aligned(packed, packed_align(bits, group_size)) || !aligned(norms, 2))
@@ -434,7 +526,7 @@ int cq_quantize_many(int n, const cq_quant_desc* descs, int w_dtype, int bits, i
   if (w_dtype != CQ_F32 && w_dtype != CQ_BF16) return fail(CQ_ERR_ARG, "unknown w_dtype %d", w_dtype);
   if (n < 0) return fail(CQ_ERR_ARG, "n < 0");
   if ((rc = check_codec_group(group_size, bits))) return rc;
-  if ((rc = check_levels(levels, n_levels, L))) return rc;
+  if ((rc = check_levels(levels, n_levels, L, bits))) return rc;
   if (n == 0) return CQ_OK;
   if (!descs) return fail(CQ_ERR_NULL, "descs is NULL");
   const size_t esz = w_dtype == CQ_F32 ? 4 : 2;
@@ -491,7 +583,7 @@ int cq_dequantize_many(int n, const cq_dequant_desc* descs, int bits, int group_
     return fail(CQ_ERR_ARG, "unknown out_dtype %d", out_dtype);
   if (n < 0) return fail(CQ_ERR_ARG, "n < 0");
   if ((rc = check_codec_group(group_size, bits))) return rc;
-  if ((rc = check_levels(levels, n_levels, L))) return rc;
+  if ((rc = check_levels(levels, n_levels, L, bits))) return rc;
   if (n == 0) return CQ_OK;
   if (!descs) return fail(CQ_ERR_NULL, "descs is NULL");
   const size_t esz = out_dtype == CQ_F32 ? 4 : 2;
@@ -555,7 +647,7 @@ int cq_dequant_gemm_many(int n, const cq_matvec_desc* descs, int bits, int group
   if (n < 0) return fail(CQ_ERR_ARG, "n < 0");
   if (batch < 1) return fail(CQ_ERR_ARG, "batch must be >= 1");
   if ((rc = check_codec_group(group_size, bits))) return rc;
-  if ((rc = check_levels(levels, n_levels, L))) return rc;
+  if ((rc = check_levels(levels, n_levels, L, bits))) return rc;
   if (n == 0) return CQ_OK;
   if (!descs) return fail(CQ_ERR_NULL, "descs is NULL");
   const int sb = storage_bits(bits);
@@ -732,7 +824,7 @@ int cq_fake_quant(const void* w, int w_dtype, int64_t rows, int64_t cols, int bi
     return fail(CQ_ERR_ARG, "unknown out_dtype %d", out_dtype);
   if (rows < 0 || cols < 0) return fail(CQ_ERR_ARG, "negative size");
   if ((rc = check_codec_group(group_size, bits))) return rc;
-  if ((rc = check_levels(levels, n_levels, L))) return rc;
+  if ((rc = check_levels(levels, n_levels, L, bits))) return rc;
   if (rows == 0 || cols == 0) return CQ_OK;
   if (!w || !out) return fail(CQ_ERR_NULL, "w/out is NULL");
   if (!aligned(w, 16) || !aligned(out, 16))
@@ -763,7 +855,7 @@ int cq_dequantize(const uint8_t* packed, const uint16_t* norms, int64_t rows, in
     return fail(CQ_ERR_ARG, "unknown out_dtype %d", out_dtype);
   if (rows < 0 || cols < 0) return fail(CQ_ERR_ARG, "negative size");
   if ((rc = check_codec_group(group_size, bits))) return rc;
-  if ((rc = check_levels(levels, n_levels, L))) return rc;
+  if ((rc = check_levels(levels, n_levels, L, bits))) return rc;
   if (rows == 0 || cols == 0) return CQ_OK;
   if (!packed || !norms || !out) return fail(CQ_ERR_NULL, "packed/norms/out is NULL");
   if (!aligned(out, 16) || !aligned(packed, packed_align(bits, group_size)) || !aligned(norms, 2))
@@ -802,7 +894,7 @@ int cq_dequant_matvec_many(int n, const cq_matvec_desc* descs, int bits, int gro
   if (n < 0) return fail(CQ_ERR_ARG, "n < 0");
   if (batch < 1) return fail(CQ_ERR_ARG, "batch must be >= 1");
   if ((rc = check_codec_group(group_size, bits))) return rc;
-  if ((rc = check_levels(levels, n_levels, L))) return rc;
+  if ((rc = check_levels(levels, n_levels, L, bits))) return rc;
   if (n == 0) return CQ_OK;
   if (!descs) return fail(CQ_ERR_NULL, "descs is NULL");
   const int sb = storage_bits(bits);

@@ -23,10 +23,12 @@ int main(void) {
          (long long)po[2], (long long)no[0], (long long)no[1], (long long)no[2], (long long)total);
   float lv[CQ_MAX_LEVELS];
   int n = 0;
-  rc = cq_codebook(CQ_TERNARY, NULL, 0, 0, lv, &n);
+  rc = cq_codebook(CQ_TERNARY, lv, &n);
   printf("ternary %d %d %.7f %.7f %.7f\n", rc, n, lv[0], lv[1], lv[2]);
+  rc = cq_codebook(2, lv, &n);
+  printf("builtin2 %d %d %.7f %.7f %.7f %.7f\n", rc, n, lv[0], lv[1], lv[2], lv[3]);
   const double samples[4] = {-2.0, -1.0, 1.0, 3.0};
-  rc = cq_codebook(1, samples, 4, 10, lv, &n);
+  rc = cq_codebook_train(1, samples, 4, 10, lv, &n);
   printf("lloyd1 %d %d %.7f %.7f\n", rc, n, lv[0], lv[1]);
   /* validation errors come back before any device work */
   rc = cq_quantize(NULL, CQ_F32, 4, 256, 5, 128, lv, 4, NULL, NULL, NULL);

@@ -1,6 +1,7 @@
 import os
 import sys
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -23,3 +24,11 @@ def oracle_levels(lloyd_samples):
     """Oracle codebooks (N(0,1) units, float64) for every supported width."""
     from oracle import cq_oracle as O
     return {b: O.codebook(b, lloyd_samples) for b in (1, 2, 3, 4, O.TERNARY)}
+
+
+@pytest.fixture(scope="session")
+def levels32(oracle_levels):
+    """The oracle's codebooks as the float32 tables every parity run hands to
+    both sides (GPU and oracle get bit-identical levels)."""
+    from oracle import cq_oracle as O
+    return {b: O.runtime_levels(v).astype(np.float32) for b, v in oracle_levels.items()}

@@ -47,20 +47,55 @@ def test_status_strings():
 # -- host-only calls vs the oracle ------------------------------------------------
 
 @pytest.mark.parametrize("bits", [O.TERNARY, 1, 2, 3, 4])
-def test_codebook_equals_oracle_float32(bits, lloyd_samples, oracle_levels):
-    got = cq.codebook(bits, lloyd_samples)
+def test_codebook_train_equals_oracle_float32(bits, lloyd_samples, oracle_levels):
+    got = cq.codebook_train(bits, lloyd_samples)
     want = O.runtime_levels(oracle_levels[bits]).astype(np.float32)
     np.testing.assert_array_equal(got, want)
 
 
-def test_codebook_iterations_and_tiny_example(lloyd_samples):
+def test_codebook_train_iterations_and_tiny_example(lloyd_samples):
     import json
     ex = json.load(open(os.path.join(ROOT, "tests", "golden", "hand_examples.json")))["lloyd_tiny"]
     # 1 level-bit = 2 levels, the tiny hand example
-    got = cq.codebook(1, np.array(ex["samples"]), iters=10)
+    got = cq.codebook_train(1, np.array(ex["samples"]), iters=10)
     np.testing.assert_allclose(got, np.float32(ex["result"]), rtol=0, atol=0)
-    got0 = cq.codebook(1, np.array(ex["samples"]), iters=0)
+    got0 = cq.codebook_train(1, np.array(ex["samples"]), iters=0)
     np.testing.assert_array_equal(got0, np.float32(ex["init"]))
+
+
+# -- the built-in codebook (levels == NULL) ----------------------------------------
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_builtin_codebook_near_gaussian_optimum(bits):
+    """libcq's own Lloyd-Max run on its own N(0,1) generator: the exact
+    Gaussian mean-square error of its levels lies within 0.2% above the
+    continuous optimum (unique for a log-concave density, so never below)."""
+    from test_oracle_codebook import exact_lloyd, gaussian_mse
+    lv = cq.codebook(bits)
+    n = 1 << bits
+    assert lv.dtype == np.float32 and lv.shape == (n,) and np.all(np.diff(lv) > 0)
+    d_star = gaussian_mse(exact_lloyd(n))
+    d = gaussian_mse(lv.astype(np.float64))
+    assert d_star <= d <= 1.002 * d_star
+
+
+def test_builtin_codebook_two_bit_levels_and_ternary():
+    table = json.load(open(os.path.join(ROOT, "tests", "golden", "max1960_gaussian.json")))
+    pos = table["quantizers"]["4"]["levels"]
+    np.testing.assert_allclose(cq.codebook(2), [-pos[1], -pos[0], pos[0], pos[1]], atol=5e-3)
+    np.testing.assert_array_equal(cq.codebook(O.TERNARY_TRITS), np.float32(O.TERNARY_LEVELS))
+    np.testing.assert_array_equal(cq.codebook(O.TERNARY), np.float32(O.TERNARY_LEVELS))
+
+
+def test_builtin_codebook_is_cached_and_independent_of_the_pages_draws(lloyd_samples):
+    a = [cq.codebook(b) for b in (1, 2, 3, 4)]
+    b = [cq.codebook(b) for b in (1, 2, 3, 4)]
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    # Its own generator, not the pages' seeded draws: close, not equal.
+    trained = cq.codebook_train(2, lloyd_samples)
+    assert not np.array_equal(a[1], trained)
+    np.testing.assert_allclose(a[1], trained, atol=1e-2)
 
 
 def test_layout_and_model_bytes():
@@ -117,7 +152,11 @@ def test_quantize_validation():
     assert quant(levels=(bad, bad.ctypes.data_as(F))) == E_ARG
     nan = np.array([0.0, np.nan, 1.0, 2.0], dtype=np.float32)
     assert quant(levels=(nan, nan.ctypes.data_as(F))) == E_ARG
-    assert quant(levels=(np.zeros(4, np.float32), None)) == E_NULL
+    # NULL levels select the built-in table and pass validation whatever
+    # n_levels says: the call gets as far as the next check (alignment).
+    assert quant(levels=(np.zeros(4, np.float32), None), w=ctypes.c_void_p(0x100004)) == E_ALIGN
+    assert quant(levels=(np.zeros(4, np.float32), None), nl=0, w=ctypes.c_void_p(0x100004)) == E_ALIGN
+    assert quant(levels=(np.zeros(4, np.float32), None), nl=0, rows=0) == OK
     assert quant(w=None) == E_NULL
     assert quant(packed=None) == E_NULL
     assert quant(w=ctypes.c_void_p(0x100004)) == E_ALIGN
@@ -171,12 +210,16 @@ def test_host_call_validation():
     L = cq.lib()
     out = (ctypes.c_float * 16)()
     n = ctypes.c_int()
-    assert L.cq_codebook(2, None, 10, 200, out, ctypes.byref(n)) == E_NULL
+    assert L.cq_codebook_train(2, None, 10, 200, out, ctypes.byref(n)) == E_NULL
     s = np.zeros(3)
-    assert L.cq_codebook(2, s.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), 3, 200, out,
-                         ctypes.byref(n)) == E_ARG        # fewer samples than levels
-    assert L.cq_codebook(9, None, 0, 200, out, ctypes.byref(n)) == E_ARG
-    assert L.cq_codebook(158, None, 0, 0, out, ctypes.byref(n)) == OK and n.value == 3
+    assert L.cq_codebook_train(2, s.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), 3, 200, out,
+                               ctypes.byref(n)) == E_ARG        # fewer samples than levels
+    assert L.cq_codebook_train(9, None, 0, 200, out, ctypes.byref(n)) == E_ARG
+    assert L.cq_codebook_train(158, None, 0, 0, out, ctypes.byref(n)) == OK and n.value == 3
+    assert L.cq_codebook(9, out, ctypes.byref(n)) == E_ARG
+    assert L.cq_codebook(2, None, ctypes.byref(n)) == E_NULL
+    assert L.cq_codebook(2, out, None) == E_NULL
+    assert L.cq_codebook(4, out, ctypes.byref(n)) == OK and n.value == 16
     ng = ctypes.c_int64()
     assert L.cq_layout(1, 1, 2, 96, ctypes.byref(ng), None) == E_ARG
     assert L.cq_layout(-1, 1, 2, 128, ctypes.byref(ng), None) == E_ARG

@@ -40,6 +40,8 @@ def test_c_host_calls(output):
     assert output["blob"] == ["0"] + [str(v) for v in po + no + [total]]
     assert output["ternary"][:2] == ["0", "3"]
     assert [float(v) for v in output["ternary"][2:]] == pytest.approx([-1.2240064, 0.0, 1.2240064], abs=1e-7)
+    assert output["builtin2"][:2] == ["0", "4"]
+    assert [float(v) for v in output["builtin2"][2:]] == pytest.approx(list(cq.codebook(2)), abs=1e-7)
     want = O.lloyd_max(__import__("numpy").array([-2.0, -1.0, 1.0, 3.0]), 2, 10)
     assert output["lloyd1"][:2] == ["0", "2"]
     assert [float(v) for v in output["lloyd1"][2:]] == pytest.approx(list(want), abs=1e-6)

@@ -34,8 +34,9 @@ def say(msg):
 
 
 @pytest.fixture(scope="module")
-def levels(lloyd_samples):
-    return {b: cq.codebook(b, lloyd_samples) for b in ALL_BITS}
+def levels(levels32):
+    # The oracle's float32 codebooks, handed to both sides.
+    return {b: levels32[b] for b in ALL_BITS}
 
 
 def host(t):

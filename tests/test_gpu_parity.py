@@ -35,10 +35,9 @@ def say(msg):
 
 
 @pytest.fixture(scope="module")
-def levels(lloyd_samples):
-    # Both sides use the same float32 levels: libcq's own Lloyd-Max run (the
-    # ABI tests pin it to the oracle's bit for bit).
-    return {b: cq.codebook(b, lloyd_samples) for b in ALL_BITS}
+def levels(levels32):
+    # The oracle's float32 codebooks, handed to both sides.
+    return {b: levels32[b] for b in ALL_BITS}
 
 
 def to_dev_f32(a):
@@ -593,3 +592,38 @@ def test_fake_quant_llama7b_layer_sampled(levels):
     rep = check_fake_quant(_out_host(out[ridx]), w_s, 2, lv, out_bf16=True, enforce_count=False)
     check_count(rep["index_mismatches"], rep["indices_read_back"])
     say(f"fake_quant llama7b sampled: {rep.line()}")
+
+
+# -- levels == NULL: the built-in codebook ---------------------------------------------
+
+@pytest.mark.parametrize("bits", [O.TERNARY, 2, 4])
+def test_builtin_codebook_when_levels_null(bits):
+    """levels=None selects libcq's built-in table: every call gives the same
+    bits as with that table passed explicitly, and the oracle, given the same
+    table, agrees with the NULL-levels results."""
+    lv_b = cq.codebook(bits)
+    rows, cols = 300, 1024
+    rng = np.random.default_rng(bits)
+    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    say(f"NULL levels bits={bits}: quantize / dequantize / matvec / fake quant")
+    p0, n0 = gpu_quantize(to_dev_f32(w), bits, None)
+    p1, n1 = gpu_quantize(to_dev_f32(w), bits, lv_b)
+    assert np.array_equal(p0, p1) and np.array_equal(n0, n1)
+    q = O.quantize(w.astype(np.float64), bits, lv_b)
+    check_quantize(p0, n0, q)
+    p_dev = torch.from_numpy(q.packed.reshape(rows, -1)).to(DEV)
+    n_dev = torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16)
+    d0 = host(cq.dequantize(p_dev, n_dev, rows, cols, bits, None))
+    d1 = host(cq.dequantize(p_dev, n_dev, rows, cols, bits, lv_b))
+    assert np.array_equal(d0, d1)
+    ref = O.dequantize(q.packed, q.norm16, rows, cols, bits, lv_b)
+    check_dequant(d0, ref, q.norm16, rows, cols)
+    x = W.matvec_x(2, k=cols)
+    xd = torch.from_numpy(x).to(DEV)
+    y0 = host(cq.dequant_matvec(p_dev, n_dev, rows, cols, bits, None, xd))
+    y1 = host(cq.dequant_matvec(p_dev, n_dev, rows, cols, bits, lv_b, xd))
+    assert np.array_equal(y0, y1)
+    check_matvec(y0, x.astype(np.float64) @ ref.T, x, ref)
+    f0 = host(cq.fake_quant(to_dev_f32(w), bits, None))
+    f1 = host(cq.fake_quant(to_dev_f32(w), bits, lv_b))
+    assert np.array_equal(f0, f1)

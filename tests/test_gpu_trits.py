@@ -32,7 +32,8 @@ def say(msg):
 
 @pytest.fixture(scope="module")
 def lv():
-    return cq.codebook(T)
+    # The oracle's ternary levels as float32 (the fixed three-level codebook).
+    return O.runtime_levels(O.codebook(T)).astype(np.float32)
 
 
 def host(t):
