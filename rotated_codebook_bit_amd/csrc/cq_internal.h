@@ -314,6 +314,33 @@ hipError_t launch_matvec(const MatvecDesc* table, const int64_t* bstart, int n, 
 
 hipError_t launch_zero(float* y, int64_t count, hipStream_t stream);
 
+// ---- Single-matrix dequant-matvec: one launch, no workspace ---------------------
+
+// The matrix and activations of one product, passed by value as a kernel
+// argument.
+struct MatvecArgs {
+  const uint8_t* packed;  // [n_out][k / G][G * sbits / 8]
+  const uint16_t* norms;  // [n_out][k / G]
+  const float* x;         // [batch][k]
+  float* y;               // [batch][n_out]
+  int64_t n_out;
+  int64_t k;
+  int64_t batch;
+};
+
+// Which kernel runs a single-matrix product: the pair-table kernel with
+// pair_rows_per_wave rows per wave (2, 4 or 8; 2-bit fields only, one batch
+// row per grid row), or (0) the per-lane-table kernel aiming at
+// blocks_per_cu blocks per compute unit.
+struct MatvecOnePlan {
+  int pair_rows_per_wave;
+  int blocks_per_cu;
+};
+
+MatvecOnePlan matvec_one_plan(int sbits, int64_t n_out, int64_t k, int64_t batch);
+hipError_t launch_matvec_one(const MatvecArgs& a, int sbits, const LevelTable& lv, int group_size,
+                             const MatvecOnePlan& plan, hipStream_t stream);
+
 // ---- Dequantize-GEMM on the matrix cores --------------------------------------
 
 // One matrix of a GEMM call (device-side descriptor).

@@ -631,8 +631,31 @@ int cq_dequantize_many(int n, const cq_dequant_desc* descs, int bits, int group_
   return rc ? rc : rc2;
 }
 
+// Validates one matrix of a product call (sizes, pointers, alignment,
+// overlap of y with the inputs).
+static int check_matvec_desc(const cq_matvec_desc& d, int i, int64_t batch, int sb, int group_size) {
+  if (d.n_out < 0 || d.k < 0) return fail(CQ_ERR_ARG, "matrix %d: negative size", i);
+  if (d.k % group_size)
+    return fail(CQ_ERR_UNSUPPORTED, "matrix %d: k=%lld is not a multiple of %d", i, (long long)d.k,
+                group_size);
+  if (d.n_out == 0) return CQ_OK;
+  if (!d.y) return fail(CQ_ERR_NULL, "matrix %d: y is NULL", i);
+  if (!aligned(d.y, 16)) return fail(CQ_ERR_ALIGN, "matrix %d: y needs 16-byte alignment", i);
+  if (d.k == 0) return CQ_OK;
+  if (!d.packed || !d.norms || !d.x) return fail(CQ_ERR_NULL, "matrix %d: packed/norms/x is NULL", i);
+  if (!aligned(d.x, 16) || !aligned(d.packed, 16) || !aligned(d.norms, 2))
+    return fail(CQ_ERR_ALIGN, "matrix %d: x, packed need 16-byte, norms 2-byte alignment", i);
+  const int64_t ng = d.n_out * (d.k / group_size);
+  const size_t y_bytes = static_cast<size_t>(batch * d.n_out) * 4;
+  const size_t pk_bytes = static_cast<size_t>(ng) * group_size * sb / 8;
+  if (overlap(d.y, y_bytes, d.packed, pk_bytes) || overlap(d.y, y_bytes, d.norms, ng * 2) ||
+      overlap(d.y, y_bytes, d.x, static_cast<size_t>(batch * d.k) * 4))
+    return fail(CQ_ERR_ARG, "matrix %d: input and output buffers overlap", i);
+  return CQ_OK;
+}
+
 // float32 -> bfloat16 bits, round to nearest even (finite inputs).
-uint32_t bf16_rne_host(float f) {
+static uint32_t bf16_rne_host(float f) {
   uint32_t u;
   std::memcpy(&u, &f, 4);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
@@ -881,8 +904,25 @@ int cq_dequantize(const uint8_t* packed, const uint16_t* norms, int64_t rows, in
 int cq_dequant_matvec(const uint8_t* packed, const uint16_t* norms, int64_t n_out, int64_t k,
                       int bits, int group_size, const float* levels, int n_levels, const float* x,
                       int64_t batch, float* y, void* stream) {
+  g_last_error[0] = 0;
+  int L, rc;
+  if ((rc = check_bits(bits, false, &L))) return rc;
+  if ((rc = reject_trits(bits))) return rc;
+  if (batch < 1) return fail(CQ_ERR_ARG, "batch must be >= 1");
+  if ((rc = check_codec_group(group_size, bits))) return rc;
+  if ((rc = check_levels(levels, n_levels, L, bits))) return rc;
   const cq_matvec_desc d{packed, norms, n_out, k, x, y};
-  return cq_dequant_matvec_many(1, &d, bits, group_size, levels, n_levels, batch, stream);
+  if ((rc = check_matvec_desc(d, 0, batch, storage_bits(bits), group_size))) return rc;
+  if (n_out == 0) return CQ_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (k == 0) return hip_status(cq::launch_zero(y, batch * n_out, s), "zero launch");
+  // One launch: the descriptor is a kernel argument and every block rotates
+  // the activations it consumes.
+  const int sb = storage_bits(bits);
+  const cq::MatvecArgs a{packed, norms, x, y, n_out, k, batch};
+  return hip_status(cq::launch_matvec_one(a, sb, make_table(levels, L), group_size,
+                                          cq::matvec_one_plan(sb, n_out, k, batch), s),
+                    "matvec launch");
 }
 
 int cq_dequant_matvec_many(int n, const cq_matvec_desc* descs, int bits, int group_size,
@@ -898,26 +938,8 @@ int cq_dequant_matvec_many(int n, const cq_matvec_desc* descs, int bits, int gro
   if (n == 0) return CQ_OK;
   if (!descs) return fail(CQ_ERR_NULL, "descs is NULL");
   const int sb = storage_bits(bits);
-  for (int i = 0; i < n; ++i) {
-    const cq_matvec_desc& d = descs[i];
-    if (d.n_out < 0 || d.k < 0) return fail(CQ_ERR_ARG, "matrix %d: negative size", i);
-    if (d.k % group_size)
-      return fail(CQ_ERR_UNSUPPORTED, "matrix %d: k=%lld is not a multiple of %d", i, (long long)d.k,
-                  group_size);
-    if (d.n_out == 0) continue;
-    if (!d.y) return fail(CQ_ERR_NULL, "matrix %d: y is NULL", i);
-    if (!aligned(d.y, 16)) return fail(CQ_ERR_ALIGN, "matrix %d: y needs 16-byte alignment", i);
-    if (d.k == 0) continue;
-    if (!d.packed || !d.norms || !d.x) return fail(CQ_ERR_NULL, "matrix %d: packed/norms/x is NULL", i);
-    if (!aligned(d.x, 16) || !aligned(d.packed, 16) || !aligned(d.norms, 2))
-      return fail(CQ_ERR_ALIGN, "matrix %d: x, packed need 16-byte, norms 2-byte alignment", i);
-    const int64_t ng = d.n_out * (d.k / group_size);
-    const size_t y_bytes = static_cast<size_t>(batch * d.n_out) * 4;
-    const size_t pk_bytes = static_cast<size_t>(ng) * group_size * sb / 8;
-    if (overlap(d.y, y_bytes, d.packed, pk_bytes) || overlap(d.y, y_bytes, d.norms, ng * 2) ||
-        overlap(d.y, y_bytes, d.x, static_cast<size_t>(batch * d.k) * 4))
-      return fail(CQ_ERR_ARG, "matrix %d: input and output buffers overlap", i);
-  }
+  for (int i = 0; i < n; ++i)
+    if ((rc = check_matvec_desc(descs[i], i, batch, sb, group_size))) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const cq::LevelTable lv = make_table(levels, L);
 

@@ -18,7 +18,7 @@ import tempfile
 
 LLVM = "/opt/rocm/llvm/bin"
 BUILD = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "rotated_codebook_bit_amd", "_build")
-KERNEL_OBJECTS = ("quantize", "dequantize", "matvec", "gemm", "groups", "repack", "upload")
+KERNEL_OBJECTS = ("quantize", "dequantize", "matvec", "matvec_rot", "gemm", "groups", "repack", "upload")
 
 
 def _vregs(op: str) -> set:

@@ -149,7 +149,8 @@ def test_zz_mismatch_total():
 def test_group_size_matvec(g, bits, batch, levels):
     """cq_dequant_matvec at other group sizes against the oracle's x @ W_hat^T
     (batch 1 of 2-bit fields takes the pair-table kernel, the rest the
-    byte-table kernel), including k not a multiple of the 1024-column tile."""
+    per-lane-table kernel; both rotate the activations over G / 2 or G / 16
+    lanes), including k not a multiple of the 1024-column tile."""
     from parity import check_matvec
     lv = levels[bits]
     rng = np.random.default_rng(zlib.crc32(repr(("mv", g, bits, batch)).encode()))

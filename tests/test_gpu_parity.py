@@ -487,6 +487,39 @@ def test_matvec_pair_rows_large_call(batch, rows, n_mat, levels):
         del p
 
 
+@pytest.mark.parametrize("bits,n_out,k,batch", [
+    (2, 1, 128, 1),          # one row, one group
+    (2, 7, 2176, 1),         # a partial 1024-column tile
+    (2, 300, 17408, 1),      # 17 tiles: two windows of rotated activations
+    (2, 2049, 384, 1),       # a partial block of rows; 2-row waves
+    (2, 20000, 256, 1),      # 4-row waves
+    (2, 32800, 128, 1),      # 8-row waves
+    (2, 33, 8320, 3),        # three 4096-column passes, rotated per unit
+    (2, 130, 4096, 17),      # batch chunks of 8, 8 and a partial one of 1
+    (4, 129, 640, 9),
+    (3, 65, 4096, 6),
+    (O.TERNARY, 500, 1024, 4),
+])
+def test_matvec_single_call(bits, n_out, k, batch, levels):
+    """cq_dequant_matvec runs as one launch that rotates the activations in
+    each block: partial tiles and passes, several windows of rotated
+    activations, every rows-per-wave choice of the batch-1 pair-table kernel,
+    batches split into chunks of eight rows with a partial last chunk."""
+    lv = levels[bits]
+    rng = np.random.default_rng(zlib.crc32(repr(("single", bits, n_out, k, batch)).encode()))
+    w = rng.standard_normal((n_out, k)) * 0.02
+    q = O.quantize(w, bits, lv)
+    x = rng.standard_normal((batch, k)).astype(np.float32)
+    w_hat = O.dequantize(q.packed, q.norm16, n_out, k, bits, lv)
+    y_ref = x.astype(np.float64) @ w_hat.T
+    say(f"single-call matvec bits={bits} {n_out}x{k} batch={batch}")
+    y = torch.full((batch, n_out), float("nan"), dtype=torch.float32, device=DEV)
+    cq.dequant_matvec(torch.from_numpy(q.packed.reshape(n_out, -1)).to(DEV),
+                      torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16),
+                      n_out, k, bits, lv, to_dev_f32(x), y=y)
+    say(f"single-call matvec: {check_matvec(host(y), y_ref, x, w_hat).line()}")
+
+
 @pytest.mark.parametrize("batch", [8, 1])
 def test_matvec_deterministic(batch, matvec_weight, levels):
     lv = levels[2]
