@@ -277,8 +277,13 @@ int cq_fake_quant(const void* w, int w_dtype, int64_t rows, int64_t cols, int bi
  * orthonormal Hadamard matrix is symmetric and its own inverse,
  * x_g . W_hat_g = (norm / G) * <H x_g, levels[idx]> with H the +-1
  * Sylvester-Hadamard matrix.  float32 accumulation in a fixed order
- * (deterministic).  Same as cq_dequant_matvec_many with one matrix, whose
- * notes on workspace memory apply. */
+ * (deterministic).  One kernel launch (for batches up to 524,280 rows),
+ * and no memory beyond the call's buffers: each thread block rotates the
+ * activations it uses ("How Needle 2 Model Compresses to a Single Binary",
+ * section Stage 3: the weights are decoded on the fly inside the product).
+ * k <= 2^28 (CQ_ERR_UNSUPPORTED otherwise).  Results equal those of
+ * cq_dequant_matvec_many on the same matrix to the product tolerance (the
+ * two may sum in different orders). */
 int cq_dequant_matvec(const uint8_t* packed, const uint16_t* norms, int64_t n_out,
                       int64_t k, int bits, int group_size, const float* levels,
                       int n_levels, const float* x, int64_t batch, float* y,

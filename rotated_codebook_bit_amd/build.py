@@ -35,10 +35,16 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# Per-file flags.  matvec_rot.hip: without SLP vectorization, so that the
+# binary16 norms of its load rings are not packed two to a register (the
+# packing waits for the loads as soon as they are issued).
+EXTRA = {"matvec_rot.hip": ["-fno-slp-vectorize"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     path = os.path.join(CSRC, src)
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", *COMMON]
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", *COMMON, *EXTRA.get(src, [])]
     if src.endswith(".hip"):
         cmd += ["-x", "hip", *DEVICE]
     else:

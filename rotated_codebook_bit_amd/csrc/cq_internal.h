@@ -329,11 +329,11 @@ struct MatvecArgs {
 };
 
 // Which kernel runs a single-matrix product: the pair-table kernel with
-// pair_rows_per_wave rows per wave (2, 4 or 8; 2-bit fields only, one batch
+// pair_rows_per_block rows per block (1 .. 64; 2-bit fields only, one batch
 // row per grid row), or (0) the per-lane-table kernel aiming at
 // blocks_per_cu blocks per compute unit.
 struct MatvecOnePlan {
-  int pair_rows_per_wave;
+  int pair_rows_per_block;
   int blocks_per_cu;
 };
 

@@ -913,6 +913,8 @@ int cq_dequant_matvec(const uint8_t* packed, const uint16_t* norms, int64_t n_ou
   if ((rc = check_levels(levels, n_levels, L, bits))) return rc;
   const cq_matvec_desc d{packed, norms, n_out, k, x, y};
   if ((rc = check_matvec_desc(d, 0, batch, storage_bits(bits), group_size))) return rc;
+  if (k > (int64_t(1) << 28))
+    return fail(CQ_ERR_UNSUPPORTED, "k=%lld: the single-matrix product takes k <= 2^28", (long long)k);
   if (n_out == 0) return CQ_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (k == 0) return hip_status(cq::launch_zero(y, batch * n_out, s), "zero launch");

@@ -51,196 +51,235 @@ __device__ __forceinline__ float xstage(float v, int s, float sgn) {
   return __builtin_fmaf(sgn, v, o);
 }
 
+// The same stage for a lane stride s of 1, 2, 4 or 8, inside the 16-lane
+// rows of DPP: the lane with bit s clear takes v + (lane l + s's value), the
+// other (lane l - s's value) - v.  No LDS traffic, only VALU operations.
+template <int S>
+__device__ __forceinline__ float dpp_stage(float v, bool upper) {
+  // row_shl:S (0x100 + S): lane l reads lane l + S of its row; row_shr:S
+  // (0x110 + S): lane l reads lane l - S.  Lanes whose source falls outside
+  // the row keep 0 and never use the value.
+  const float from_above = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, v), 0x100 + S, 0xF, 0xF, false));
+  const float from_below = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, v), 0x110 + S, 0xF, 0xF, false));
+  return upper ? from_below - v : v + from_above;
+}
+
 // ---- pair tables, one batch row per grid row ------------------------------------
 
 constexpr int kPairWaves = 8;
 constexpr int kPairBlock = kPairWaves * kWave;
-// Rotated x of a tile in LDS: column c at float c + 2 (c / 16), so that the
-// table build's reads (lane l reads columns 16 l + 2 w, +1) fall on distinct
-// banks and the rotation's writes (lane l of wave w writes 128 w + 2 l, +1)
-// stay conflict free.
-constexpr int kTilePadded = kTile + kTile / 8;
-__device__ __forceinline__ int xpad(int c) { return c + 2 * (c >> 4); }
-// Tiles of rotated x held in LDS at once (72 KiB at most); longer rows are
-// processed in windows of this many tiles.
-constexpr int kMaxWindowTiles = 16;
+// A pass is 4096 columns: lane l of every wave owns columns 64 l .. 64 l + 63
+// of it, so a row's codes for the lane are one 16-byte load and its norm
+// (group size >= 64) one 2-byte load.
+constexpr int kPassCols = kWave * 64;
+// Rotated x of a pass in LDS: column c at float c + 4 (c / 64), so that the
+// table build's 16-byte reads (lane l at column 64 l + 8 w) and the
+// rotation's 16-byte writes (thread t at column 8 t) spread over the banks.
+constexpr int kXsFloats = kPassCols + kPassCols / 16;
+__device__ __forceinline__ int xpad(int c) { return c + 4 * (c >> 6); }
+// Pair tables of a pass: entry (pair q of lane l's 64 columns, code pair v)
+// at float (16 q + v) * 64 + l, 128 KiB.  In every lookup instruction lane l
+// touches bank l whatever its code: no bank conflicts by construction.
+constexpr int kTableFloats = 32 * 16 * kWave;
 
-template <int RPW, int PF>
-__global__ void __launch_bounds__(kPairBlock, 2)
-matvec_pair_rot_kernel(MatvecArgs a, LevelTable lv, int log2g, int window_tiles) {
-  extern __shared__ __attribute__((aligned(16))) float xs[];  // window_tiles * kTilePadded
-  __shared__ __attribute__((aligned(16))) float tab[8 * 16 * kWave];
+// A block owns rows_per_block consecutive rows of the matrix (about an equal
+// share for every compute unit); wave w takes rows w, w + 8, w + 16, ... of
+// them, at most MAXR.  Per 4096-column pass: the pass's activations and the
+// codes and norms of all the wave's rows are loaded at once; the block
+// rotates the activations into LDS and builds the pass's pair tables; then
+// every wave runs through its rows without further barriers.
+template <int MAXR, bool TWO_NORMS>
+__global__ void __launch_bounds__(kPairBlock, 1)
+matvec_pair_rot_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_block) {
+  __shared__ __attribute__((aligned(16))) float tab[kTableFloats];
+  __shared__ __attribute__((aligned(16))) float xs[kXsFloats];
   const int lane = threadIdx.x % kWave;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t k = a.k, n_out = a.n_out;
   const int64_t brow = blockIdx.y;  // batch row
-  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * (kPairWaves * RPW) + w * RPW;
+  const int64_t row_base = static_cast<int64_t>(blockIdx.x) * rows_per_block;
+  const int64_t block_rows = n_out - row_base < rows_per_block ? n_out - row_base : rows_per_block;
+  // This wave's rows: row_base + w + 8 i for i < nrows.
+  const int nrows = block_rows > w ? static_cast<int>((block_rows - w + kPairWaves - 1) / kPairWaves) : 0;
   const int64_t row_bytes = k / 4, ngr = k >> log2g;
-  const int64_t n_tiles = (k + kTile - 1) / kTile;
   const int G = 1 << log2g;
   const float* __restrict__ xrow = a.x + brow * k;
 
-  // The wave's rows as buffer resources: rows past the end of the matrix lie
-  // outside them and read as zero (their sums are never stored).  The host
-  // sends a matrix here only when k <= 2^28, so RPW <= 16 rows of codes and
-  // every offset below stay under 2^31.
-  const int64_t rows_in = n_out - row0 < RPW ? (n_out - row0 > 0 ? n_out - row0 : 0) : RPW;
-  const auto codes_src = rsrc(a.packed + (rows_in ? row0 * row_bytes : 0), rows_in * row_bytes);
-  const auto norms_src = rsrc(a.norms + (rows_in ? row0 * ngr : 0), rows_in * ngr * 2);
-  int soff_c[RPW], soff_n[RPW];
+  // The wave's rows as one buffer resource from its first row; row i at the
+  // scalar offset 8 i rows.  Rows past the wave's last re-read its last one
+  // (their sums are never stored); a lane without columns in a pass offsets
+  // by 2^30, past the resource, and reads zeros.  The host sends a matrix
+  // here only when k <= 2^26 and k % 64 == 0, so a block's 64 rows of codes
+  // (16 k bytes) stay under 2^30 and every offset under 2^31.
+  const int64_t first = row_base + w;
+  const int64_t span = nrows ? (static_cast<int64_t>(nrows - 1) * kPairWaves + 1) : 0;
+  const auto codes_src = rsrc(a.packed + (nrows ? first * row_bytes : 0), span * row_bytes);
+  const auto norms_src = rsrc(a.norms + (nrows ? first * ngr : 0), span * ngr * 2);
+  int soff_c[MAXR], soff_n[MAXR];
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const int rr = r < rows_in ? r : (rows_in > 0 ? static_cast<int>(rows_in) - 1 : 0);
-    soff_c[r] = __builtin_amdgcn_readfirstlane(static_cast<int>(rr * row_bytes));
-    soff_n[r] = __builtin_amdgcn_readfirstlane(static_cast<int>(2 * rr * ngr));
+  for (int i = 0; i < MAXR; ++i) {
+    const int ii = i < nrows ? i : (nrows > 0 ? nrows - 1 : 0);
+    soff_c[i] = __builtin_amdgcn_readfirstlane(static_cast<int>(ii * kPairWaves * row_bytes));
+    soff_n[i] = __builtin_amdgcn_readfirstlane(static_cast<int>(2 * ii * kPairWaves * ngr));
   }
   const float c0l = lv.c[0], c1l = lv.c[1], c2l = lv.c[2], c3l = lv.c[3];
-  const uint32_t lane_bytes = 4u * static_cast<uint32_t>(lane);
+  // Table byte address of (pair q, code pair v) for this lane: one byte
+  // permute of the spread nibbles and one of these (byte 0 the lane's 4 l;
+  // byte 2 selects the upper 64 KiB for pairs 16 .. 31).
+  const uint32_t lane_lo = 4u * static_cast<uint32_t>(lane);
+  const uint32_t lane_hi = lane_lo | 0x10000u;
+  // TWO_NORMS: group size 32, two groups (two norms) per lane.
 
-  // Codes of tile t for the wave's rows, PF tiles in flight.  A lane without
-  // columns in the tile offsets by 2^30, past every resource, and reads zero.
-  uint32_t codes[PF][RPW];
-  _Float16 norm[PF][RPW];
-  auto issue = [&](int64_t t, uint32_t (&c)[RPW], _Float16 (&nv)[RPW]) {
-    const int64_t c0 = t * kTile + kChunk * lane;
-    const bool active = t < n_tiles && c0 < k;  // k % G == 0: whole chunks only
+  float acc[MAXR];
+#pragma unroll
+  for (int i = 0; i < MAXR; ++i) acc[i] = 0.0f;
+  const float sgn16 = (lane >> 4) & 1 ? -1.0f : 1.0f;
+
+  for (int64_t p0 = 0; p0 < k; p0 += kPassCols) {
+    // 1. Loads, all in flight together: the pass's activations (thread t
+    //    takes columns 8 t .. 8 t + 7, at addresses clamped into the row),
+    //    then each row's 16 bytes of codes and its norm(s) for this lane.
+    const int64_t my_c = p0 + 8 * static_cast<int64_t>(threadIdx.x);
+    const bool my_live = my_c < k;  // whole 8-value runs: k % 64 == 0
+    float xv[8];
+    {
+      const int64_t c = my_live ? my_c : 0;
+      const float4 p = *reinterpret_cast<const float4*>(xrow + c);
+      const float4 q = *reinterpret_cast<const float4*>(xrow + c + 4);
+      xv[0] = p.x; xv[1] = p.y; xv[2] = p.z; xv[3] = p.w;
+      xv[4] = q.x; xv[5] = q.y; xv[6] = q.z; xv[7] = q.w;
+    }
+    const int64_t c0 = p0 + 64 * lane;
+    const bool active = c0 < k;
     const int coff = active ? static_cast<int>(c0 / 4) : (1 << 30);
     const int noff = active ? static_cast<int>(2 * (c0 >> log2g)) : (1 << 30);
+    uint32_t codes[MAXR][4];
+    uint32_t nrm[MAXR];  // binary16 norm(s): low half, and the high half for group size 32
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      c[r] = __builtin_amdgcn_raw_buffer_load_b32(codes_src, coff, soff_c[r], 2);  // nt: read once
-      nv[r] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(norms_src, noff, soff_n[r], 0));
+    for (int r = 0; r < MAXR; ++r) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(codes_src, coff, soff_c[r], 2);  // nt: read once
+      codes[r][0] = v[0]; codes[r][1] = v[1]; codes[r][2] = v[2]; codes[r][3] = v[3];
+      if constexpr (TWO_NORMS)
+        nrm[r] = __builtin_amdgcn_raw_buffer_load_b32(norms_src, noff, soff_n[r], 0);
+      else
+        nrm[r] = __builtin_amdgcn_raw_buffer_load_b16(norms_src, noff, soff_n[r], 0);
     }
-  };
+    __syncthreads();  // the previous pass's tables and activations are no longer read
+    // 2. Rotate: butterfly stages 1, 2, 4 inside the thread, lane strides
+    //    1, 2, 4, 8 (element strides 8 .. 64) inside DPP rows, lane stride
+    //    16 (element stride 128, group size 256) across rows; store to LDS.
 #pragma unroll
-  for (int j = 0; j < PF; ++j) issue(j, codes[j], norm[j]);
-
-  float acc[RPW];
+    for (int e = 0; e < 8; ++e) xv[e] = my_live ? xv[e] : 0.0f;
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
-
-  // Butterfly signs of the cross-lane stages (lane stride s = 1 .. 32).
-  float sgn[6];
+    for (int h = 1; h < 8; h <<= 1)
 #pragma unroll
-  for (int i = 0; i < 6; ++i) sgn[i] = (lane >> i) & 1 ? -1.0f : 1.0f;
-  const int in_wave = G < 2 * kWave ? G : 2 * kWave;  // butterfly width inside a wave
-
-  for (int64_t w0 = 0; w0 < n_tiles; w0 += window_tiles) {
-    const int nt = static_cast<int>(n_tiles - w0 < window_tiles ? n_tiles - w0 : window_tiles);
-    __syncthreads();  // the previous window's rotated x is no longer read
-    // Load the window's activations (two per thread per tile), all loads
-    // first, then rotate and store each tile.
-    float2 raw[kMaxWindowTiles];
+      for (int i = 0; i < 8; i += 2 * h)
 #pragma unroll
-    for (int i = 0; i < kMaxWindowTiles; ++i) {
-      const int64_t c = (w0 + i) * kTile + 2 * threadIdx.x;
-      raw[i] = i < nt && c < k ? *reinterpret_cast<const float2*>(xrow + c) : make_float2(0.0f, 0.0f);
-    }
-#pragma unroll
-    for (int i = 0; i < kMaxWindowTiles; ++i) {
-      if (i < nt) {
-        float y0 = raw[i].x + raw[i].y, y1 = raw[i].x - raw[i].y;
-#pragma unroll
-        for (int st = 0; st < 6; ++st) {
-          if ((2 << st) < in_wave) {
-            y0 = xstage(y0, 1 << st, sgn[st]);
-            y1 = xstage(y1, 1 << st, sgn[st]);
-          }
+        for (int j = i; j < i + h; ++j) {
+          const float u = xv[j], v = xv[j + h];
+          xv[j] = u + v;
+          xv[j + h] = u - v;
         }
-        *reinterpret_cast<float2*>(xs + i * kTilePadded + xpad(2 * threadIdx.x)) = make_float2(y0, y1);
-        wait_lds_writes();  // the stored values keep their registers until the LDS has them
-        hold_values(y0, y1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xv[e] = dpp_stage<1>(xv[e], lane & 1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xv[e] = dpp_stage<2>(xv[e], lane & 2);
+    if (G > 32) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xv[e] = dpp_stage<4>(xv[e], lane & 4);
+    }
+    if (G > 64) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xv[e] = dpp_stage<8>(xv[e], lane & 8);
+    }
+    if (G > 128) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xv[e] = xstage(xv[e], 16, sgn16);
+    }
+    {
+      float* dst = xs + xpad(8 * threadIdx.x);
+      *reinterpret_cast<float4*>(dst) = make_float4(xv[0], xv[1], xv[2], xv[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(xv[4], xv[5], xv[6], xv[7]);
+      wait_lds_writes();  // the stored values keep their registers until the LDS has them
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hold_values(xv[e]);
+    }
+    __syncthreads();
+    // 3. Pair tables: thread (w, lane) builds pairs 4 w .. 4 w + 3 of the
+    //    lane's 64 columns (columns 64 lane + 8 w .. 64 lane + 8 w + 7).
+    if (active) {
+      const float* src = xs + xpad(64 * lane + 8 * w);
+      const float4 p = *reinterpret_cast<const float4*>(src);
+      const float4 q = *reinterpret_cast<const float4*>(src + 4);
+      const float xr[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+      const float cb[4] = {c0l, c1l, c2l, c3l};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float x0 = xr[2 * h], x1 = xr[2 * h + 1];
+        const float pa[4] = {c0l * x0, c1l * x0, c2l * x0, c3l * x0};
+        float e[16];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) e[qq + 4 * bb] = __builtin_fmaf(cb[bb], x1, pa[qq]);
+        float* dst = tab + (16 * (4 * w + h)) * kWave + lane;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dst[v * kWave] = e[v];
+        wait_lds_writes();
+#pragma unroll
+        for (int v = 0; v < 16; ++v) hold_values(e[v]);
       }
     }
-
-    for (int i0 = 0; i0 < nt; i0 += PF) {
+    __syncthreads();
+    // 4. Every row of the wave: 32 lookups and adds per lane, then the norm.
+    const char* tb = reinterpret_cast<const char*>(tab);
 #pragma unroll
-      for (int j = 0; j < PF; ++j) {
-        const int i = i0 + j;
-        if (i >= nt) break;  // the same for the whole block
-        const int64_t t = w0 + i;
-        const int64_t c0 = t * kTile + kChunk * lane;
-        const bool active = c0 < k;
-        __syncthreads();  // rotated x stored; the previous tile's table reads are done
-        if (active) {
-          // Pair w of this lane's chunk: columns 16 lane + 2 w, + 1 of the tile.
-          const float* xt = xs + i * kTilePadded;
-          const int c = kChunk * lane + 2 * w;
-          float x0, x1;
-          if (G > 2 * kWave) {
-            // The last butterfly stage (stride 128) joins two waves' halves.
-            const int lo = c & ~128;
-            const float2 p = *reinterpret_cast<const float2*>(xt + xpad(lo));
-            const float2 q = *reinterpret_cast<const float2*>(xt + xpad(lo + 128));
-            x0 = c & 128 ? p.x - q.x : p.x + q.x;
-            x1 = c & 128 ? p.y - q.y : p.y + q.y;
-          } else {
-            const float2 p = *reinterpret_cast<const float2*>(xt + xpad(c));
-            x0 = p.x;
-            x1 = p.y;
-          }
-          const float pa[4] = {c0l * x0, c1l * x0, c2l * x0, c3l * x0};
-          const float cb[4] = {c0l, c1l, c2l, c3l};
-          float e[16];
+    for (int r = 0; r < MAXR; ++r) {
+      if (r >= nrows) break;  // the same for the whole wave
+      float part[2] = {0.0f, 0.0f};  // columns 0-31 and 32-63 of the lane
 #pragma unroll
-          for (int bb = 0; bb < 4; ++bb)
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t cw = codes[r][d];
+        const uint32_t ev = cw & 0x0F0F0F0Fu, od = (cw >> 4) & 0x0F0F0F0Fu;
+        const uint32_t base = d < 2 ? lane_lo : lane_hi;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) e[q + 4 * bb] = __builtin_fmaf(cb[bb], x1, pa[q]);
-          float* dst = tab + (16 * w) * kWave + lane;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) dst[v * kWave] = e[v];
-          wait_lds_writes();
-#pragma unroll
-          for (int v = 0; v < 16; ++v) hold_values(e[v]);
+        for (int qq = 0; qq < 8; ++qq) {
+          // Pair q = 8 d + qq: its nibble is byte qq / 2 of ev (qq even) or od.
+          const uint32_t e = (qq & 1) ? od : ev;
+          // Selector: byte 0 = base byte 0 (4 l), byte 1 = byte qq / 2 of e,
+          // byte 2 = base byte 2 (the 64 KiB half), byte 3 = zero.
+          const uint32_t addr = __builtin_amdgcn_perm(e, base, 0x0C020000u | ((4u + (qq >> 1)) << 8));
+          const float v = *reinterpret_cast<const float*>(tb + addr + 4096 * ((8 * d + qq) & 15));
+          part[d >> 1] = (d & 1) || qq ? part[d >> 1] + v : v;
         }
-        __syncthreads();
-        if (active) {
-          const char* tb = reinterpret_cast<const char*>(tab);
-#pragma unroll
-          for (int r = 0; r < RPW; ++r) {
-            const uint32_t cw = codes[j][r];
-            const uint32_t ev = cw & 0x0F0F0F0Fu, od = (cw >> 4) & 0x0F0F0F0Fu;
-            float s = 0.0f;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              // Byte 0 of the address is the lane's (4 l), byte 1 the pair's
-              // code v (its nibble, spread one per byte), bytes 2-3 zero.
-              const uint32_t e = (q & 1) ? od : ev;
-              const uint32_t addr = __builtin_amdgcn_perm(e, lane_bytes, 0x0C0C0000u | ((4u + (q >> 1)) << 8));
-              const float v = *reinterpret_cast<const float*>(tb + addr + 4096 * q);
-              s = q ? s + v : v;
-            }
-            acc[r] = __builtin_fmaf(static_cast<float>(norm[j][r]), s, acc[r]);
-          }
-        }
-        issue(t + PF, codes[j], norm[j]);
+      }
+      // Lanes without columns in the pass read codes 0 and norms 0: they add 0.
+      const float n_lo = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(nrm[r])));
+      if constexpr (TWO_NORMS) {
+        const float n_hi = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(nrm[r] >> 16)));
+        acc[r] = __builtin_fmaf(n_hi, part[1], __builtin_fmaf(n_lo, part[0], acc[r]));
+      } else {
+        acc[r] = __builtin_fmaf(n_lo, part[0] + part[1], acc[r]);
       }
     }
   }
 
-  // Reduce the RPW row sums over the 64 lanes: each exchange halves the
-  // values a lane holds (the lane with the offset's bit set keeps the upper
-  // half), then the remaining offsets sum within groups of 64 / RPW lanes.
-  constexpr int kSteps = RPW >= 16 ? 4 : RPW >= 8 ? 3 : RPW >= 4 ? 2 : RPW >= 2 ? 1 : 0;
+  // acc[r] holds lane partial sums of row first + 8 r: sum over the 64 lanes
+  // (a fixed shuffle tree), then lane 0 stores.
 #pragma unroll
-  for (int i = 0; i < kSteps; ++i) {
-    const int o = 32 >> i, V = RPW >> i;
-    const bool hi = lane & o;
+  for (int r = 0; r < MAXR; ++r) {
+    float v = acc[r];
 #pragma unroll
-    for (int jj = 0; jj < V / 2; ++jj) {
-      const float lo_sum = acc[jj] + __shfl_xor(acc[jj], o, kWave);
-      const float hi_sum = acc[jj + V / 2] + __shfl_xor(acc[jj + V / 2], o, kWave);
-      acc[jj] = hi ? hi_sum : lo_sum;
-    }
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+    acc[r] = v;
   }
-  float s = acc[0];
+  if (lane == 0) {
 #pragma unroll
-  for (int o = 32 >> kSteps; o >= 1; o >>= 1) s += __shfl_xor(s, o, kWave);
-  s *= 1.0f / static_cast<float>(G);  // exact: a power of two
-  int r = 0;
-#pragma unroll
-  for (int i = 0; i < kSteps; ++i) r += ((lane >> (5 - i)) & 1) * (RPW >> (i + 1));
-  if ((lane & (64 / RPW - 1)) == 0 && row0 + r < n_out) a.y[brow * n_out + row0 + r] = s;
+    for (int r = 0; r < MAXR; ++r)
+      if (r < nrows) a.y[brow * n_out + first + static_cast<int64_t>(r) * kPairWaves] = acc[r] * (1.0f / static_cast<float>(G));
+  }
 }
 
 // ---- any width, NB batch rows -------------------------------------------------
@@ -335,7 +374,7 @@ __device__ __forceinline__ uint64_t codes16(const uint8_t* __restrict__ row_ptr,
 // pass the thread's activations are loaded and rotated once for all of the
 // block's rows; otherwise once per unit.
 template <int SB, int NB, int RB, int PF>
-__global__ void __launch_bounds__(kRotBlock)
+__global__ void __launch_bounds__(kRotBlock, 2)
 matvec_rot_kernel(MatvecArgs a, LevelTable lv, int log2g, int rg) {
   using LT = LaneTab<SB>;
   __shared__ __attribute__((aligned(16))) float tab[LT::floats];
@@ -362,23 +401,37 @@ matvec_rot_kernel(MatvecArgs a, LevelTable lv, int log2g, int rg) {
   for (int i = 0; i < 4; ++i) sgn[i] = (lane >> i) & 1 ? -1.0f : 1.0f;
 
   float xv[NB][kChunk];
-  // Rotated activations of this thread's 16 columns of pass p: the 16-point
-  // butterfly inside the thread, then log2(G / 16) stages across the lanes
-  // that share the group.
+  // Activations of this thread's 16 columns of pass p, loaded at addresses
+  // clamped into x (past k: the row's last chunk; past the batch: its last
+  // row), unconditionally, so that the wait before the rotation counts them
+  // exactly; out-of-range values become zeros at use.
   auto load_x = [&](int p) __attribute__((always_inline)) {
-    const int64_t c0 = static_cast<int64_t>(p) * kPass + kChunk * t;
+    int64_t c0 = static_cast<int64_t>(p) * kPass + kChunk * t;
+    c0 = c0 < k ? c0 : k - kChunk;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const bool live = c0 < k && b0 + b < a.batch;
-      const float4* src = reinterpret_cast<const float4*>(a.x + (b0 + b) * k + c0);
+      const int64_t bb = b0 + b < a.batch ? b0 + b : a.batch - 1;
+      const float4* src = reinterpret_cast<const float4*>(a.x + bb * k + c0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float4 v = live ? src[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        const float4 v = src[i];
         xv[b][4 * i] = v.x;
         xv[b][4 * i + 1] = v.y;
         xv[b][4 * i + 2] = v.z;
         xv[b][4 * i + 3] = v.w;
       }
+    }
+  };
+  // Rotated activations of pass p: zeros where out of range, then the
+  // 16-point butterfly inside the thread, then log2(G / 16) stages across
+  // the lanes that share the group.
+  auto rotate_x = [&](int p) __attribute__((always_inline)) {
+    const bool cols = static_cast<int64_t>(p) * kPass + kChunk * t < k;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const bool live = cols && b0 + b < a.batch;
+#pragma unroll
+      for (int e = 0; e < kChunk; ++e) xv[b][e] = live ? xv[b][e] : 0.0f;
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -400,32 +453,63 @@ matvec_rot_kernel(MatvecArgs a, LevelTable lv, int log2g, int rg) {
     }
   };
 
+  // Codes and binary16 norms of PF units in flight, loaded through buffer
+  // resources of the unit's rows: each row's offset is a scalar, the lane's
+  // column offset one register shared by all rows, and a thread without
+  // columns in the pass offsets by 2^30, past the resource, and reads zeros
+  // (norm 0, so its products vanish even where a stored norm is +Inf).  Rows
+  // past the end of the matrix re-read its last row (never stored); units
+  // past the block's last re-read that one (never used).  No loaded value is
+  // selected or converted before its unit comes up, so no load is waited
+  // for early.  The host sends a matrix here only when k <= 2^28, so a unit's
+  // RB rows of codes and every offset stay under 2^31.
   using CodeT = typename std::conditional<SB == 2, uint32_t, uint64_t>::type;
   CodeT codes[PF][RB];
-  float scale[PF][RB];
-  auto issue = [&](int u, CodeT (&c)[RB], float (&sc)[RB]) __attribute__((always_inline)) {
-    const int g = u / n_pass, p = u - g * n_pass;
+  _Float16 nbits[PF][RB];
+  auto issue = [&](int u, CodeT (&c)[RB], _Float16 (&nb)[RB]) __attribute__((always_inline)) {
+    const int uu = u < n_units ? u : n_units - 1;
+    const int g = uu / n_pass, p = uu - g * n_pass;
+    const int64_t grow0 = row_base + static_cast<int64_t>(g) * RB;
+    const int64_t rows_in = n_out - grow0 < RB ? n_out - grow0 : RB;  // >= 1
+    const auto csrc = rsrc(a.packed + grow0 * row_bytes, rows_in * row_bytes);
+    const auto nsrc = rsrc(a.norms + grow0 * ngr, rows_in * ngr * 2);
     const int64_t c0 = static_cast<int64_t>(p) * kPass + kChunk * t;
-    const bool live = u < n_units && c0 < k;
+    const bool in = c0 < k;
+    const int coff = in ? static_cast<int>(c0 * SB / 8) : (1 << 30);
+    const int noff = in ? static_cast<int>(2 * (c0 >> log2g)) : (1 << 30);
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
-      int64_t row = row_base + static_cast<int64_t>(g) * RB + r;
-      row = row < n_out ? row : n_out - 1;  // rows past the end re-read the last; never stored
-      c[r] = live ? static_cast<CodeT>(codes16<SB>(a.packed + row * row_bytes, c0)) : CodeT(0);
-      sc[r] = live ? static_cast<float>(__builtin_bit_cast(_Float16, a.norms[row * ngr + (c0 >> log2g)])) * inv_g
-                   : 0.0f;
+      const int rr = r < rows_in ? r : static_cast<int>(rows_in) - 1;
+      const int sc = __builtin_amdgcn_readfirstlane(static_cast<int>(rr * row_bytes));
+      const int sn = __builtin_amdgcn_readfirstlane(static_cast<int>(2 * rr * ngr));
+      if constexpr (SB == 2) {
+        c[r] = __builtin_amdgcn_raw_buffer_load_b32(csrc, coff, sc, 2);  // nt: read once
+      } else if constexpr (SB == 4) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(csrc, coff, sc, 2);
+        c[r] = static_cast<uint64_t>(v[0]) | (static_cast<uint64_t>(v[1]) << 32);
+      } else {
+        // 6 bytes at the 2-byte aligned offset 6 (c0 / 16).
+        const uint64_t h0 = __builtin_amdgcn_raw_buffer_load_b16(csrc, coff, sc, 2);
+        const uint64_t h1 = __builtin_amdgcn_raw_buffer_load_b16(csrc, coff + 2, sc, 2);
+        const uint64_t h2 = __builtin_amdgcn_raw_buffer_load_b16(csrc, coff + 4, sc, 2);
+        c[r] = h0 | (h1 << 16) | (h2 << 32);
+      }
+      nb[r] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(nsrc, noff, sn, 0));
     }
   };
+  if (one_pass) load_x(0);  // before the codes, so the rotation waits for these loads only
 #pragma unroll
-  for (int j = 0; j < PF; ++j) issue(j, codes[j], scale[j]);
-  if (one_pass) load_x(0);
+  for (int j = 0; j < PF; ++j) issue(j, codes[j], nbits[j]);
+  if (one_pass) rotate_x(0);
 
   float acc[RB][NB];
   for (int u0 = 0; u0 < n_units; u0 += PF) {
+    // Unrolled by PF with a guard (not an early exit), so that every index
+    // into the ring of codes is a compile-time constant.
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
       const int u = u0 + j;
-      if (u >= n_units) break;  // the same for the whole block
+      if (u < n_units) {  // the same for the whole block
       const int g = u / n_pass, p = u - g * n_pass;
       if (p == 0) {
 #pragma unroll
@@ -433,7 +517,10 @@ matvec_rot_kernel(MatvecArgs a, LevelTable lv, int log2g, int rg) {
 #pragma unroll
           for (int b = 0; b < NB; ++b) acc[r][b] = 0.0f;
       }
-      if (!one_pass) load_x(p);
+      if (!one_pass) {
+        load_x(p);
+        rotate_x(p);
+      }
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         float v[kChunk];
@@ -445,10 +532,14 @@ matvec_rot_kernel(MatvecArgs a, LevelTable lv, int log2g, int rg) {
         for (int e = 0; e < kChunk; ++e)
 #pragma unroll
           for (int b = 0; b < NB; ++b) part[b] = __builtin_fmaf(v[e], xv[b][e], part[b]);
+        const float sc = static_cast<float>(nbits[j][r]) * inv_g;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) acc[r][b] = __builtin_fmaf(scale[j][r], part[b], acc[r][b]);
+        for (int b = 0; b < NB; ++b) acc[r][b] = __builtin_fmaf(sc, part[b], acc[r][b]);
+        // One row at a time: without this the compiler hoists every row's
+        // table reads to the top and needs a register per level read.
+        __builtin_amdgcn_sched_barrier(0);
       }
-      issue(u + PF, codes[j], scale[j]);
+      if (u + PF < n_units) issue(u + PF, codes[j], nbits[j]);
       if (p == n_pass - 1) {
         // Block reduction in a fixed order: thread t's partials go to column
         // t of `red`; thread t then sums value t / 8 over columns
@@ -476,6 +567,7 @@ matvec_rot_kernel(MatvecArgs a, LevelTable lv, int log2g, int rg) {
         }
         __syncthreads();  // `red` is rewritten by the next row group
       }
+      }
     }
   }
 }
@@ -485,21 +577,23 @@ matvec_rot_kernel(MatvecArgs a, LevelTable lv, int log2g, int rg) {
 // Largest grid.y of one launch.
 constexpr int64_t kMaxGridY = 65535;
 
-template <int RPW, int PF>
-hipError_t launch_pair_rot(const MatvecArgs& a, const LevelTable& lv, int log2g, hipStream_t s) {
-  constexpr int rows = kPairWaves * RPW;
-  const int64_t blocks = (a.n_out + rows - 1) / rows;
-  const int64_t n_tiles = (a.k + kTile - 1) / kTile;
-  const int window = static_cast<int>(n_tiles < kMaxWindowTiles ? n_tiles : kMaxWindowTiles);
-  const size_t lds = static_cast<size_t>(window) * kTilePadded * sizeof(float);
+// Rows per wave of the pair-table kernel (the most a wave's registers hold).
+constexpr int kPairMaxRows = 8;
+
+hipError_t launch_pair_rot(const MatvecArgs& a, const LevelTable& lv, int log2g, int rows_per_block, hipStream_t s) {
+  const int64_t blocks = (a.n_out + rows_per_block - 1) / rows_per_block;
   // One batch row per grid row, at most kMaxGridY per launch.
   for (int64_t b0 = 0; b0 < a.batch; b0 += kMaxGridY) {
     MatvecArgs part = a;
     part.x = a.x + b0 * a.k;
     part.y = a.y + b0 * a.n_out;
     part.batch = a.batch - b0 < kMaxGridY ? a.batch - b0 : kMaxGridY;
-    hipLaunchKernelGGL((matvec_pair_rot_kernel<RPW, PF>), dim3(static_cast<unsigned>(blocks),
-                       static_cast<unsigned>(part.batch)), dim3(kPairBlock), lds, s, part, lv, log2g, window);
+    if (log2g == 5)
+      hipLaunchKernelGGL((matvec_pair_rot_kernel<kPairMaxRows, true>), dim3(static_cast<unsigned>(blocks),
+                         static_cast<unsigned>(part.batch)), dim3(kPairBlock), 0, s, part, lv, log2g, rows_per_block);
+    else
+      hipLaunchKernelGGL((matvec_pair_rot_kernel<kPairMaxRows, false>), dim3(static_cast<unsigned>(blocks),
+                         static_cast<unsigned>(part.batch)), dim3(kPairBlock), 0, s, part, lv, log2g, rows_per_block);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -512,7 +606,7 @@ hipError_t launch_rot_nb(const MatvecArgs& a, const LevelTable& lv, int log2g, i
   // Rows per group (RB * NB <= 32 partial sums in registers) and units of
   // codes in flight (at most 32 dwords of codes per thread).
   constexpr int RB = NB <= 4 ? 8 : 4;
-  constexpr int PF = SB == 2 ? 4 : NB <= 4 ? 2 : 3;
+  constexpr int PF = NB <= 4 ? (SB == 2 ? 4 : 2) : 2;
   // Row groups per block: the rotation of the block's activations is paid
   // once per block, so blocks are as large as filling the chip allows.
   const int64_t groups = (a.n_out + RB - 1) / RB;
@@ -555,14 +649,19 @@ constexpr int log2_group(int g) { return g == 32 ? 5 : g == 64 ? 6 : g == 256 ? 
 
 }  // namespace kr
 
+// Longest rows of the pair-table kernel (its row offsets are 32-bit).
+constexpr int64_t kPairMaxK = int64_t(1) << 26;
+
 MatvecOnePlan matvec_one_plan(int sbits, int64_t n_out, int64_t k, int64_t batch) {
-  // 2-bit fields at batch 1 take the pair-table kernel: the most rows per
-  // wave (8, 4, 2) that still gives every compute unit two blocks.
-  if (sbits == 2 && batch == 1 && k <= (int64_t(1) << 28)) {
-    const int64_t target = 2 * static_cast<int64_t>(device_cu_count());
-    for (int rpw = 8; rpw > 2; rpw /= 2)
-      if ((n_out + kr::kPairWaves * rpw - 1) / (kr::kPairWaves * rpw) >= target) return MatvecOnePlan{rpw, 0};
-    return MatvecOnePlan{2, 0};
+  // 2-bit fields at batch 1 take the pair-table kernel with about an equal
+  // share of the rows for every compute unit (one block each; at most 8 rows
+  // per wave, so a block takes at most 64).
+  if (sbits == 2 && batch == 1 && k <= kPairMaxK && k % 64 == 0) {
+    const int64_t cus = device_cu_count();
+    int64_t rpb = (n_out + cus - 1) / cus;
+    const int64_t cap = static_cast<int64_t>(kr::kPairWaves) * kr::kPairMaxRows;
+    rpb = rpb < 1 ? 1 : rpb > cap ? cap : rpb;
+    return MatvecOnePlan{static_cast<int>(rpb), 0};
   }
   return MatvecOnePlan{0, 1};
 }
@@ -572,14 +671,10 @@ hipError_t launch_matvec_one(const MatvecArgs& a, int sbits, const LevelTable& l
   if (a.n_out <= 0 || a.batch <= 0) return hipSuccess;
   const int log2g = kr::log2_group(group_size);
   if ((1 << log2g) != group_size) return hipErrorInvalidValue;
-  if (plan.pair_rows_per_wave) {
-    if (sbits != 2 || a.k > (int64_t(1) << 28)) return hipErrorInvalidValue;
-    switch (plan.pair_rows_per_wave) {
-      case 2: return kr::launch_pair_rot<2, 8>(a, lv, log2g, stream);
-      case 4: return kr::launch_pair_rot<4, 4>(a, lv, log2g, stream);
-      case 8: return kr::launch_pair_rot<8, 2>(a, lv, log2g, stream);
-      default: return hipErrorInvalidValue;
-    }
+  if (plan.pair_rows_per_block) {
+    if (sbits != 2 || a.k > kPairMaxK || a.k % 64 || plan.pair_rows_per_block > kr::kPairWaves * kr::kPairMaxRows)
+      return hipErrorInvalidValue;
+    return kr::launch_pair_rot(a, lv, log2g, plan.pair_rows_per_block, stream);
   }
   const int bpc = plan.blocks_per_cu > 0 ? plan.blocks_per_cu : 1;
   switch (sbits) {
