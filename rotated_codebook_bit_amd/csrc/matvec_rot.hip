@@ -237,7 +237,7 @@ matvec_pair_rot_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_bloc
     const char* tb = reinterpret_cast<const char*>(tab);
 #pragma unroll
     for (int r = 0; r < MAXR; ++r) {
-      if (r >= nrows) break;  // the same for the whole wave
+      if (r < nrows) {  // the same for the whole wave (a guard: an early exit stops the unrolling)
       float part[2] = {0.0f, 0.0f};  // columns 0-31 and 32-63 of the lane
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
@@ -262,6 +262,7 @@ matvec_pair_rot_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_bloc
         acc[r] = __builtin_fmaf(n_hi, part[1], __builtin_fmaf(n_lo, part[0], acc[r]));
       } else {
         acc[r] = __builtin_fmaf(n_lo, part[0] + part[1], acc[r]);
+      }
       }
     }
   }
@@ -293,17 +294,20 @@ constexpr int kPass = kRotBlock * kChunk;  // 4096 columns per pass
 // code and its own lane byte, and in every read instruction lane l touches
 // bank l whatever its code (no bank conflicts by construction).
 //   2-bit fields: the codes of two adjacent columns form a nibble v; table 0
-//     holds level[v & 3], table 1 (4 KiB further) level[v >> 2];
+//     holds level[v & 3], table 1 (4 KiB + 64 bytes further, so that a lane's
+//     two reads fall on different banks) level[v >> 2];
 //   4-bit fields: one code per nibble, one table;
 //   3-bit fields: one 8-entry table, the code extracted by a shift.
 template <int SB>
 struct LaneTab {
   static constexpr int entries = SB == 3 ? 8 : 16;
   static constexpr int tables = SB == 2 ? 2 : 1;
-  static constexpr int floats = tables * 16 * kWave;
+  static constexpr int kSecond = 16 * kWave + 16;  // float offset of table 1
+  static constexpr int floats = tables == 2 ? kSecond + 16 * kWave : 16 * kWave;
   static __device__ __forceinline__ void fill(float* tab, const LevelTable& lv, int t) {
     for (int i = t; i < floats; i += kRotBlock) {
-      const int tb = i / (16 * kWave), v = (i / kWave) % 16;
+      const int tb = tables == 2 && i >= kSecond ? 1 : 0;
+      const int v = ((tb ? i - kSecond : i) / kWave) % 16;
       float val = 0.0f;
       if (v < entries) {
         if constexpr (SB == 2)
@@ -327,7 +331,7 @@ struct LaneTab {
         const uint32_t e = (q & 1) ? od : ev;
         const uint32_t addr = __builtin_amdgcn_perm(e, lane_bytes, 0x0C0C0000u | ((4u + (q >> 1)) << 8));
         v[2 * q] = *reinterpret_cast<const float*>(tb + addr);
-        v[2 * q + 1] = *reinterpret_cast<const float*>(tb + addr + 16 * 4 * kWave);
+        v[2 * q + 1] = *reinterpret_cast<const float*>(tb + addr + 4 * kSecond);
       }
     } else if constexpr (SB == 4) {
 #pragma unroll
@@ -605,12 +609,15 @@ hipError_t launch_rot_nb(const MatvecArgs& a, const LevelTable& lv, int log2g, i
                          hipStream_t s) {
   // Rows per group (RB * NB <= 32 partial sums in registers) and units of
   // codes in flight (at most 32 dwords of codes per thread).
-  constexpr int RB = NB <= 4 ? 8 : 4;
-  constexpr int PF = NB <= 4 ? (SB == 2 ? 4 : 2) : 2;
+  constexpr int RB = NB <= 2 ? 8 : 4;
+  constexpr int PF = 2;
   // Row groups per block: the rotation of the block's activations is paid
-  // once per block, so blocks are as large as filling the chip allows.
+  // once per block, so blocks are as large as filling the chip allows
+  // (blocks_per_cu blocks per compute unit over all batch chunks).
   const int64_t groups = (a.n_out + RB - 1) / RB;
-  const int64_t target = static_cast<int64_t>(device_cu_count()) * blocks_per_cu;
+  const int64_t n_chunks = (a.batch + NB - 1) / NB;
+  int64_t target = static_cast<int64_t>(device_cu_count()) * blocks_per_cu / (n_chunks < blocks_per_cu ? n_chunks : blocks_per_cu);
+  target = target < 1 ? 1 : target;
   int64_t rg = (groups + target - 1) / target;
   rg = rg < 1 ? 1 : rg > 64 ? 64 : rg;
   const int64_t blocks = (groups + rg - 1) / rg;
@@ -633,15 +640,13 @@ hipError_t launch_rot_nb(const MatvecArgs& a, const LevelTable& lv, int log2g, i
 template <int SB>
 hipError_t launch_rot_sb(const MatvecArgs& a, const LevelTable& lv, int log2g, int blocks_per_cu,
                          hipStream_t s) {
-  switch (a.batch >= 8 ? 8 : a.batch) {
+  // Batch chunks of at most 4 rows (grid.y): a chunk's activations (16 x 4
+  // floats per thread) leave room for two waves per SIMD.
+  switch (a.batch >= 4 ? 4 : a.batch) {
     case 1: return launch_rot_nb<SB, 1>(a, lv, log2g, blocks_per_cu, s);
     case 2: return launch_rot_nb<SB, 2>(a, lv, log2g, blocks_per_cu, s);
     case 3: return launch_rot_nb<SB, 3>(a, lv, log2g, blocks_per_cu, s);
-    case 4: return launch_rot_nb<SB, 4>(a, lv, log2g, blocks_per_cu, s);
-    case 5: return launch_rot_nb<SB, 5>(a, lv, log2g, blocks_per_cu, s);
-    case 6: return launch_rot_nb<SB, 6>(a, lv, log2g, blocks_per_cu, s);
-    case 7: return launch_rot_nb<SB, 7>(a, lv, log2g, blocks_per_cu, s);
-    default: return launch_rot_nb<SB, 8>(a, lv, log2g, blocks_per_cu, s);
+    default: return launch_rot_nb<SB, 4>(a, lv, log2g, blocks_per_cu, s);
   }
 }
 
@@ -663,7 +668,7 @@ MatvecOnePlan matvec_one_plan(int sbits, int64_t n_out, int64_t k, int64_t batch
     rpb = rpb < 1 ? 1 : rpb > cap ? cap : rpb;
     return MatvecOnePlan{static_cast<int>(rpb), 0};
   }
-  return MatvecOnePlan{0, 1};
+  return MatvecOnePlan{0, 2};
 }
 
 hipError_t launch_matvec_one(const MatvecArgs& a, int sbits, const LevelTable& lv, int group_size,
