@@ -63,6 +63,35 @@ def violations(lines: list, window: int = 64) -> list:
     return out
 
 
+def store_reuse(lines: list, window: int = 64) -> list:
+    """(index, store, overwrite) for every buffer or global store whose data
+    registers are written again before the next vmcnt wait: the same
+    register-lifetime question as for DS writes, asked of VMEM stores.  The
+    data operand is the first operand of a buffer store and the second of a
+    global store.  (A report: the compiler emits this pattern at most VMEM
+    stores, and every stored byte of the codec kernels is checked against
+    the oracle at full size, so it is not a gate the way the DS-write scan
+    is.)"""
+    out = []
+    for i, ins in enumerate(lines):
+        if not ins.startswith(("buffer_store", "global_store")):
+            continue
+        ops = _operands(ins)
+        pos = 0 if ins.startswith("buffer_store") else 1
+        data = _vregs(ops[pos].split()[0]) if len(ops) > pos and ops[pos] else set()
+        if not data:
+            continue
+        for ins2 in lines[i + 1:i + 1 + window]:
+            if ins2.startswith("s_waitcnt") and "vmcnt" in ins2:
+                break
+            if ins2.startswith(("v_", "ds_read", "ds_load", "buffer_load", "global_load", "flat_load")):
+                o2 = _operands(ins2)
+                if o2 and (_vregs(o2[0]) & data):
+                    out.append((i, ins, ins2))
+                    break
+    return out
+
+
 def disassemble(obj: str) -> dict:
     """Kernel name -> list of instruction texts, from the gfx950 code object
     embedded in the host object `obj`."""

@@ -21,6 +21,21 @@ def test_scanner_finds_the_pattern():
     assert not S.violations(["ds_write_b32 v1, v2", "s_waitcnt lgkmcnt(0)", "v_add_u32 v2, v2, v3"])
 
 
+def test_store_scanner_finds_the_pattern():
+    # A 128-bit buffer store whose first data register is rewritten before a
+    # vmcnt wait: flagged; likewise the data pair of a global store.
+    bad = ["buffer_store_dwordx4 v[52:55], v83, s[12:15], 0 offen", "v_bfe_u32 v53, v126, 16, 1"]
+    assert [h[0] for h in S.store_reuse(bad)] == [0]
+    bad_g = ["global_store_dwordx4 v[2:3], v[4:7], off", "v_lshrrev_b32_e32 v7, 28, v13"]
+    assert [h[0] for h in S.store_reuse(bad_g)] == [0]
+    # The wait first, a rewrite of the address register only, or a load
+    # into another register: not flagged.
+    assert not S.store_reuse(["buffer_store_dwordx4 v[52:55], v83, s[12:15], 0 offen", "s_waitcnt vmcnt(0)",
+                              "v_mov_b32 v52, 0"])
+    assert not S.store_reuse(["global_store_dwordx4 v[2:3], v[4:7], off", "v_mov_b32 v2, 0"])
+    assert not S.store_reuse(["buffer_store_dword v9, v1, s[0:3], 0 offen", "ds_read_b32 v10, v2"])
+
+
 @pytest.mark.parametrize("name", S.KERNEL_OBJECTS)
 def test_no_lds_write_register_reuse(name):
     obj = os.path.join(S.BUILD, f"{name}.o")
