@@ -314,6 +314,22 @@ typedef struct {
 int cq_dequant_matvec_many(int n, const cq_matvec_desc* descs, int bits, int group_size,
                            const float* levels, int n_levels, int64_t batch, void* stream);
 
+/* cq_dequant_matvec_many for callers that cannot allocate device memory
+ * (code under stream capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments, validation, kernels and results (bit for
+ * bit), but the workspace lives in a fixed array of this library, 16 MiB
+ * per GPU (held from the library's load until the process ends), and the
+ * call allocates nothing.  The workspace a call needs is a descriptor table
+ * of about 56 bytes per matrix plus sum(batch * k) * 4 bytes of rotated
+ * activations (4.6 MB for the 225 matrices of a 7B-parameter model at
+ * batch 1); a call that needs more than 16 MiB returns CQ_ERR_UNSUPPORTED
+ * before anything is enqueued (use cq_dequant_matvec_many then).  Every
+ * call on a GPU uses that GPU's one workspace: calls that overlap on the
+ * same GPU (on different streams or host threads) race and must be
+ * serialized by the caller; calls in order on one stream are safe. */
+int cq_dequant_matvec_many_noalloc(int n, const cq_matvec_desc* descs, int bits, int group_size,
+                                   const float* levels, int n_levels, int64_t batch, void* stream);
+
 /* Batched product y = x . W_hat^T on the matrix cores, for the same inputs,
  * layouts, validation and workspace rules as cq_dequant_matvec (x float32
  * [batch][k], y float32 [batch][n_out], k a multiple of G), meant for larger

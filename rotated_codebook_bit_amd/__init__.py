@@ -17,6 +17,7 @@ import numpy as np
 __all__ = [
     "TERNARY", "TERNARY_TRITS", "GROUP", "group_bytes", "repack", "CQError", "lib", "storage_bits", "n_levels", "layout",
     "model_bytes", "codebook", "codebook_train", "quantize", "dequantize", "dequant_matvec", "dequant_matvec_many",
+    "dequant_matvec_many_noalloc",
     "fake_quant", "blob_layout", "quantize_many", "dequantize_many", "dequant_gemm",
     "dequant_gemm_many",
 ]
@@ -92,8 +93,10 @@ def lib() -> ctypes.CDLL:
                                         i32, vp, i64, vp, vp]
         L.cq_dequant_matvec_many.argtypes = [i32, ctypes.POINTER(MatvecDesc), i32, i32,
                                              ctypes.POINTER(ctypes.c_float), i32, i64, vp]
+        L.cq_dequant_matvec_many_noalloc.argtypes = L.cq_dequant_matvec_many.argtypes
         for name in ("cq_layout", "cq_model_bytes", "cq_codebook", "cq_codebook_train", "cq_quantize", "cq_dequantize",
-                     "cq_fake_quant", "cq_dequant_matvec", "cq_dequant_matvec_many", "cq_blob_layout",
+                     "cq_fake_quant", "cq_dequant_matvec", "cq_dequant_matvec_many",
+                     "cq_dequant_matvec_many_noalloc", "cq_blob_layout",
                      "cq_quantize_many", "cq_dequantize_many", "cq_dequant_gemm",
                      "cq_dequant_gemm_many", "cq_repack"):
             getattr(L, name).restype = i32
@@ -326,6 +329,19 @@ def dequant_matvec_many(items, bits: int, levels, batch: int, group_size: int = 
     lv, lvp = _levels_arg(levels)
     _check("cq_dequant_matvec_many", lib().cq_dequant_matvec_many(n, arr, bits, group_size, lvp, _nlev(lv),
                                                                   batch, _stream_ptr(stream)))
+    return [it[5] for it in items]
+
+
+def dequant_matvec_many_noalloc(items, bits: int, levels, batch: int, group_size: int = GROUP, stream=None):
+    """dequant_matvec_many with the library's fixed 16 MiB workspace instead of
+    memory allocated per call (cq_dequant_matvec_many_noalloc).  Calls that
+    overlap on one GPU race on that workspace."""
+    n = len(items)
+    arr = _matvec_descs(items)
+    lv, lvp = _levels_arg(levels)
+    _check("cq_dequant_matvec_many_noalloc",
+           lib().cq_dequant_matvec_many_noalloc(n, arr, bits, group_size, lvp, _nlev(lv), batch,
+                                                _stream_ptr(stream)))
     return [it[5] for it in items]
 
 

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libcq.so")
 BUILD = os.path.join(PKG, "_build")
 
-SOURCES = ["libcq_host.cpp", "quantize.hip", "dequantize.hip", "matvec.hip", "matvec_rot.hip", "upload.hip", "gemm.hip", "repack.hip", "groups.hip"]
+SOURCES = ["libcq_host.cpp", "quantize.hip", "dequantize.hip", "matvec.hip", "matvec_rot.hip", "upload.hip", "gemm.hip", "repack.hip", "groups.hip", "noalloc.hip"]
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", f"-I{os.path.join(ROOT, 'include')}"]

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/libcq.h"
+
 namespace cq {
 
 constexpr int kGroup = 128;       // elements per group
@@ -313,6 +315,15 @@ hipError_t launch_matvec(const MatvecDesc* table, const int64_t* bstart, int n, 
                          const MatvecPlan& plan, int group_size, hipStream_t stream);
 
 hipError_t launch_zero(float* y, int64_t count, hipStream_t stream);
+
+// The multi-matrix product (cq_dequant_matvec_many) with a stream-ordered
+// workspace (fixed_ws == nullptr) or a fixed one of fixed_cap bytes whose
+// device address fixed_ws returns, called only after validation and the
+// size check; defined in libcq_host.cpp.
+int matvec_many_impl(int n, const cq_matvec_desc* descs, int bits, int group_size, const float* levels,
+                     int n_levels, int64_t batch, void* stream, int (*fixed_ws)(uint8_t**), size_t fixed_cap);
+// Records a failure (status and message) for cq_last_error; returns status.
+int report(int status, const char* msg);
 
 // ---- Single-matrix dequant-matvec: one launch, no workspace ---------------------
 

@@ -929,6 +929,20 @@ int cq_dequant_matvec(const uint8_t* packed, const uint16_t* norms, int64_t n_ou
 
 int cq_dequant_matvec_many(int n, const cq_matvec_desc* descs, int bits, int group_size,
                            const float* levels, int n_levels, int64_t batch, void* stream) {
+  return cq::matvec_many_impl(n, descs, bits, group_size, levels, n_levels, batch, stream, nullptr, 0);
+}
+
+}  // extern "C"
+
+namespace cq {
+
+// The multi-matrix product with its workspace either stream-ordered
+// (fixed_ws == nullptr: hipMallocAsync / hipFreeAsync on the stream) or a
+// fixed one of fixed_cap bytes whose device address fixed_ws returns
+// (nothing allocated; a call that needs more is rejected before anything is
+// enqueued, and fixed_ws is called only once the call is known to run).
+int matvec_many_impl(int n, const cq_matvec_desc* descs, int bits, int group_size, const float* levels,
+                     int n_levels, int64_t batch, void* stream, int (*fixed_ws)(uint8_t**), size_t fixed_cap) {
   g_last_error[0] = 0;
   int L, rc;
   if ((rc = check_bits(bits, false, &L))) return rc;
@@ -947,17 +961,22 @@ int cq_dequant_matvec_many(int n, const cq_matvec_desc* descs, int bits, int gro
 
   // Matrices with k = 0 produce zeros; the rest go to the descriptor table.
   std::vector<cq::MatvecDesc> act;
+  std::vector<int> zero_k;
   for (int i = 0; i < n; ++i) {
     const cq_matvec_desc& d = descs[i];
     if (d.n_out == 0) continue;
     if (d.k == 0) {
-      if ((rc = hip_status(cq::launch_zero(d.y, batch * d.n_out, s), "zero launch"))) return rc;
+      zero_k.push_back(i);
       continue;
     }
     act.push_back(cq::MatvecDesc{d.packed, d.norms, d.x, d.y, d.n_out, d.k, 0});
   }
-  if (act.empty()) return CQ_OK;
   const int na = static_cast<int>(act.size());
+  if (na == 0) {
+    for (int i : zero_k)
+      if ((rc = hip_status(cq::launch_zero(descs[i].y, batch * descs[i].n_out, s), "zero launch"))) return rc;
+    return CQ_OK;
+  }
   // Batch rows go through the product kernel in chunks of `chunk` rows.
   const int chunk = cq::matvec_chunk(sb, batch, act.data(), na);
   const int nb_full = static_cast<int>(batch < chunk ? batch : chunk);
@@ -978,8 +997,16 @@ int cq_dequant_matvec_many(int n, const cq_matvec_desc* descs, int bits, int gro
   const size_t table_b = round_up(na * sizeof(cq::MatvecDesc));
   const size_t start_b = round_up((na + 1) * sizeof(int64_t));
   const size_t ws_bytes = table_b + 3 * start_b + static_cast<size_t>(xr_floats) * sizeof(float);
+  if (fixed_ws && ws_bytes > fixed_cap)
+    return fail(CQ_ERR_UNSUPPORTED,
+                "this call needs %zu bytes of workspace (the descriptor table and batch * sum(k) rotated "
+                "activations); the fixed workspace holds %zu",
+                ws_bytes, fixed_cap);
   uint8_t* ws = nullptr;
-  if ((rc = hip_status(hipMallocAsync(reinterpret_cast<void**>(&ws), ws_bytes, s), "workspace alloc")))
+  if (fixed_ws && (rc = fixed_ws(&ws))) return rc;
+  for (int i : zero_k)
+    if ((rc = hip_status(cq::launch_zero(descs[i].y, batch * descs[i].n_out, s), "zero launch"))) return rc;
+  if (!fixed_ws && (rc = hip_status(hipMallocAsync(reinterpret_cast<void**>(&ws), ws_bytes, s), "workspace alloc")))
     return rc;
   auto* table = reinterpret_cast<cq::MatvecDesc*>(ws);
   auto* g_dev = reinterpret_cast<int64_t*>(ws + table_b);
@@ -1007,8 +1034,11 @@ int cq_dequant_matvec_many(int n, const cq_matvec_desc* descs, int bits, int gro
                                       sb, lv, xr, b0, nb, full ? plan0 : plan1, group_size, s),
                     "matvec launch");
   }
-  const int rc2 = hip_status(hipFreeAsync(ws, s), "workspace free");
+  const int rc2 = fixed_ws ? CQ_OK : hip_status(hipFreeAsync(ws, s), "workspace free");
   return rc ? rc : rc2;
 }
 
-}  // extern "C"
+int report(int status, const char* msg) { return fail(status, "%s", msg); }
+
+}  // namespace cq
+

@@ -470,3 +470,20 @@ def test_group_size_support():
     # sizes for other group sizes
     assert cq.layout(3, 200, 2, 64) == (12, 12 * 16)
     assert cq.layout(3, 200, 4, 256) == (3, 3 * 128)
+
+
+def test_matvec_many_noalloc_rejects_beyond_its_workspace():
+    """The allocation-free product checks its workspace need (about 56 bytes
+    per matrix plus batch * sum(k) * 4 bytes) against its fixed 16 MiB before
+    any device work, so fake device pointers are safe here."""
+    L = cq.lib()
+    lv, lp = _levels(4)
+    # 8 rows x k = 2^20 at batch 8: 32 MiB of rotated activations.
+    k = 1 << 20
+    d = (cq.MatvecDesc * 1)(cq.MatvecDesc(0x1000000, 0x9000000, 8, k, 0x20000000, 0x60000000))
+    assert L.cq_dequant_matvec_many_noalloc(1, d, 2, 128, lp, 4, 8, None) == E_UNSUP
+    assert b"16777216" in L.cq_last_error()
+    # Argument errors come first, as for cq_dequant_matvec_many.
+    assert L.cq_dequant_matvec_many_noalloc(1, d, 2, 128, lp, 4, 0, None) == E_ARG
+    assert L.cq_dequant_matvec_many_noalloc(1, d, 5, 128, lp, 4, 1, None) == E_ARG
+    assert L.cq_dequant_matvec_many_noalloc(0, None, 2, 128, lp, 4, 1, None) == OK
