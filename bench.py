@@ -9,6 +9,13 @@ One step is one pass of the whole path over the 7B-shaped model (bf16,
      cq_dequant_matvec_many call over the 225 matrices: one rotation launch,
      one product launch).
 
+Extra phases after the step (in `phases`, not part of it): fused fake
+quantization, the batch-256 dequant-GEMM, quantize as 225 calls and as one
+multi-tensor call, the 11008x4096 product at batch 1 and 8 (one
+cq_dequant_matvec call each, warm and cold, fraction of the binding roof),
+and the 92-tensor Needle-2-sized set through cq_quantize_many and
+cq_dequantize_many (warm and cold).
+
 Prints one JSON line.  `value` is model parameters per second over the whole
 step (wall clock, inputs resident in HBM).  Per-kernel times come from HIP
 events recorded on the stream the kernels run on.  The CPU oracle is timed on
@@ -16,8 +23,9 @@ a bounded sample (one transformer layer and the embedding, 333M params,
 through the same three steps).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       python bench.py --copy-only   (plain device copy, for counter scaling)
+       python bench.py --copy-only   (plain 4 GiB device copy, for calibrating the byte counters)
        python bench.py --configs     (the small configurations: one JSON report line)
+       python bench.py --trace-summary DIR   (per-kernel, per-grid table of a rocprofv3 kernel trace)
 
 --configs times, per configuration, single calls with HIP events (3 warm-up
 calls, median of 15), warm (inputs cache-resident after the previous call)
@@ -90,6 +98,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-only", action="store_true", help="only run a plain 4 GiB device copy")
     ap.add_argument("--configs", action="store_true", help="report the small configurations instead")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="print a per-kernel, per-grid table of a rocprofv3 kernel trace directory and exit")
     return ap.parse_args()
 
 
@@ -231,6 +241,72 @@ def configs_report(torch) -> dict:
     return rep
 
 
+def c5_phases(torch, cq, W, scrub) -> dict:
+    """cq_dequant_matvec on the 11008x4096 2-bit matrix at batch 1 and 8:
+    median call time (HIP events around one call, launch included), warm and
+    cold, and its fraction of the binding roof."""
+    wm = torch.from_numpy(W.matvec_weight_bits().view(np.int16)).to("cuda").view(torch.bfloat16)
+    pk, nm = cq.quantize(wm, 2, None)
+    del wm
+    out = {}
+    for batch in (1, 8):
+        x = torch.from_numpy(W.matvec_x(batch)).to("cuda")
+        y = torch.empty((batch, 11008), dtype=torch.float32, device="cuda")
+        nbm = pk.numel() + nm.numel() * 2 + x.numel() * 4 + y.numel() * 4
+        flops = 2 * batch * 11008 * 4096
+        t_hbm = nbm / (HBM_PEAK_GBS * 1e9) * 1e6
+        t_valu = flops / (VALU_F32_PEAK_TFS * 1e12) * 1e6
+        roof = max(t_hbm, t_valu)
+        r = warm_cold(torch, lambda: cq.dequant_matvec(pk, nm, 11008, 4096, 2, None, x, y=y), scrub)
+        r.update({"algorithmic_bytes": nbm, "flops": flops, "roof_us": round(roof, 3),
+                  "binding": "hbm" if t_hbm >= t_valu else "valu (fp32, non-packed)",
+                  "frac_of_roof_warm": round(roof / r["warm_us"], 4),
+                  "frac_of_roof_cold": round(roof / r["cold_us"], 4)})
+        out[f"batch{batch}"] = r
+    out["note"] = ("call times include the launch; kernel times are in the rocprofv3 trace "
+                   "(profiles/kernel_trace_configs.md)")
+    return out
+
+
+def c2_phases(torch, cq, W, scrub) -> dict:
+    """The 92-tensor Needle-2-sized set (fp32) through one cq_quantize_many
+    call (writing the blob) and one cq_dequantize_many call: call times warm
+    and cold, GB/s of algorithmic bytes."""
+    tensors = [torch.from_numpy(a).to("cuda") for _, a in W.needle2()]
+    params = sum(t.numel() for t in tensors)
+    blob, views = cq.quantize_many(tensors, 2, None)
+    nb = params * 4 + blob.numel()
+    items = [(p.reshape(t.shape[0], -1), n, t.shape[0], t.shape[1]) for t, (p, n) in zip(tensors, views)]
+    outs = [torch.empty_like(t) for t in tensors]
+    r = {"tensors": len(tensors), "params": params, "model_bytes": blob.numel(), "algorithmic_bytes": nb,
+         "quantize_many": warm_cold(torch, lambda: cq.quantize_many(tensors, 2, None, blob=blob, views=False),
+                                    scrub, nb),
+         "dequantize_many": warm_cold(torch, lambda: cq.dequantize_many(items, 2, None, outs=outs), scrub, nb)}
+    del tensors, blob, views, items, outs
+    return r
+
+
+def trace_summary(path: str) -> None:
+    """Per (kernel, grid) dispatch counts and durations from the kernel-trace
+    CSV files of a rocprofv3 output directory (one markdown table)."""
+    import csv
+    import glob
+    import statistics
+    rows = {}
+    for f in glob.glob(os.path.join(path, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
+                key = (name, r.get("Grid_Size_X", r.get("Grid_Size", "")),
+                       r.get("Grid_Size_Y", "1"), r.get("Workgroup_Size_X", r.get("Workgroup_Size", "")))
+                rows.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print("| kernel | grid x | grid y | block | launches | median us | mean us | min us | total us |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for (name, gx, gy, wg), ds in sorted(rows.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| `{name}` | {gx} | {gy} | {wg} | {len(ds)} | {statistics.median(ds):.2f} | "
+              f"{statistics.mean(ds):.2f} | {min(ds):.2f} | {sum(ds):.1f} |")
+
+
 def cpu_baseline_configs() -> dict:
     """The oracle on C1, C2, C3 (each width) and C5 in full: quantize +
     dequantize (C5: dequantize + the float64 product), params/s."""
@@ -316,6 +392,9 @@ def cpu_baseline() -> dict:
 
 def main():
     args = parse()
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus "
               f"{args.gpus}).  Run with --gpus 1.", file=sys.stderr)
@@ -501,19 +580,19 @@ def main():
                 "serialized blob; not part of the step"}
     del blob
 
-    # Practical ceiling in the same process: a 4 GiB device-to-device copy.
-    src = torch.empty(1 << 30, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ce[0].record(stream)
-    for _ in range(5):
-        dst.copy_(src)
-    ce[1].record(stream)
-    torch.cuda.synchronize()
-    tcopy = ce[0].elapsed_time(ce[1]) / 5
-    copy_gbs = 2 * src.numel() * 4 / (tcopy * 1e-3) / 1e9
-    del src, dst
+    # The 11008x4096 product (one cq_dequant_matvec call: one launch, no
+    # workspace) at batch 1 and 8, warm and cold (a 1 GiB device write before
+    # each timed call), against its binding roof max(HBM time, fp32 VALU time).
+    del out
+    torch.cuda.empty_cache()
+    scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    phases["matvec_11008x4096_extra"] = c5_phases(torch, cq, W, scrub)
+    # The 45.8M-parameter Needle-2-sized set: 92 fp32 tensors (one 300x1000,
+    # padded) through one cq_quantize_many call writing the serialized blob
+    # and one cq_dequantize_many call back to fp32, warm and cold.
+    phases["needle2_92_tensors_extra"] = c2_phases(torch, cq, W, scrub)
+    del scrub
+
     dom = "dequantize_f32" if tdq >= tq else "quantize"
     dom_kernel = {"dequantize_f32": "dequantize_contig<2, false, false, false>",
                   "quantize": "quantize_contig<4, true, false, false>"}
@@ -529,9 +608,7 @@ def main():
             traffic = None
     roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": dom_kernel[dom], "bytes_per_launch": phases[dom]["bytes"],
-                "copy_4GiB_GB_per_s": round(copy_gbs, 1),
-                "frac_of_copy": round(ach / copy_gbs, 4)}
+                "kernel": dom_kernel[dom], "bytes_per_launch": phases[dom]["bytes"]}
     result = {
         "metric": METRIC,
         "value": round(params / (ms_step * 1e-3) / 1e9, 2),
@@ -554,7 +631,7 @@ def main():
         "roofline": roofline,
         "sources_digest": sources_digest(),
     }
-    del out, buf
+    del buf
     torch.cuda.empty_cache()
     if not args.no_cpu:
         log("timing the CPU oracle on a sample")
