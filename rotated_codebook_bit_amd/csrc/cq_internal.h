@@ -139,6 +139,197 @@ __device__ __forceinline__ void hold_values(const T&... v) {
   (hold_value(v), ...);
 }
 
+// ---- Ragged rows: one group over a quad of lanes ---------------------------------
+//
+// Where a row's length is not a multiple of 128, groups start anywhere and
+// the last group of each row is partial (zero-padded on input, its padding
+// dropped on output: "Cactus Quants CQ2-bit Quantization: Extreme
+// Compression for Edge LLMs", section Group-wise Weight Partitioning).  The
+// kernels for such tensors give a group to a quad of four consecutive
+// lanes: lane q of the quad holds elements 32q .. 32q+31.  Butterfly stages
+// with pair distances 1..16 then stay inside a lane's registers, and the
+// stages with distances 32 and 64 pair lane q with lanes q^1 and q^2 of the
+// same quad (DPP quad permutes, no LDS).  A wave covers 16 groups, so a
+// small tensor spreads over four times as many waves as with one lane per
+// group, each doing a quarter of the arithmetic.
+
+constexpr int kQuadElems = kGroup / 4;  // elements per lane
+constexpr int kQuadGroups = kWave / 4;  // groups per wave
+
+// Value of lane (lane ^ X) of the same quad, X = 1 or 2: DPP quad_perm
+// [1,0,3,2] (0xB1) or [2,3,0,1] (0x4E).  Every lane of the quad must be active.
+template <int X>
+__device__ __forceinline__ float quad_xor(float v) {
+  static_assert(X == 1 || X == 2, "quad lanes differ in bit 0 or bit 1");
+  constexpr int kCtrl = X == 1 ? 0xB1 : 0x4E;
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+
+// Word held by lane K of the quad (quad_perm [K,K,K,K]).
+template <int K>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x55 * K, 0xF, 0xF, false));
+}
+
+// Butterfly stages with pair distances H0, 2 H0, ..., 16 over a lane's 32
+// elements.
+template <int H0>
+__device__ __forceinline__ void quad_butterfly_in_lane(float (&y)[kQuadElems]) {
+#pragma unroll
+  for (int h = H0; h < kQuadElems; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < kQuadElems; i += 2 * h) {
+#pragma unroll
+      for (int j = i; j < i + h; ++j) {
+        const float a = y[j], b = y[j + h];
+        y[j] = a + b;
+        y[j + h] = a - b;
+      }
+    }
+  }
+}
+
+// Butterfly stage of pair distance 32 X across the quad.  The lane with bit
+// X of q clear holds a and takes a + b; its partner holds b and takes a - b
+// (fma(-1, b, a) is the rounded a - b), the same operations as in one lane.
+template <int X>
+__device__ __forceinline__ void quad_butterfly_across(float (&y)[kQuadElems], int q) {
+  const float sgn = (q & X) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int j = 0; j < kQuadElems; ++j) y[j] = __builtin_fmaf(sgn, y[j], quad_xor<X>(y[j]));
+}
+
+// Sum of v over the quad, the same value (bit for bit) in all four lanes:
+// (v0 + v1) + (v2 + v3) in every lane, as float addition commutes.
+__device__ __forceinline__ float quad_sum(float v) {
+  v += quad_xor<1>(v);
+  return v + quad_xor<2>(v);
+}
+
+// Group gl of a tensor with `cols` columns: index of its first element and
+// how many of its 128 elements exist (1..128).
+struct QuadPlace {
+  int64_t first;
+  int valid;
+};
+__device__ __forceinline__ QuadPlace quad_place(int64_t gl, int64_t cols) {
+  const int64_t ngr = (cols + kGroup - 1) / kGroup;
+  int64_t row, gi;
+  if (gl <= 0xFFFFFFFFll && ngr <= 0xFFFFFFFFll) {  // 32-bit division when it fits
+    const uint32_t r = static_cast<uint32_t>(gl) / static_cast<uint32_t>(ngr);
+    row = r;
+    gi = gl - static_cast<int64_t>(r) * ngr;
+  } else {
+    row = gl / ngr;
+    gi = gl - row * ngr;
+  }
+  const int64_t col0 = gi * kGroup, left = cols - col0;
+  return QuadPlace{row * cols + col0, left < kGroup ? static_cast<int>(left) : kGroup};
+}
+
+// Elements 32q .. 32q+31 of a group (first element `first`, `valid` of them
+// exist) as float32, the missing ones 0.  WIDE: 16-byte loads; the caller
+// guarantees a 16-byte aligned base and cols a multiple of 16 / element
+// bytes, so every 16-byte piece lies in one row and exists whole or not at
+// all.  Otherwise one load per element.  Addresses of missing pieces are
+// clamped to the group's first element, so all loads issue unconditionally;
+// the zero fill follows them.
+template <bool BF16, bool WIDE>
+__device__ __forceinline__ void quad_load(const uint8_t* __restrict__ w, int64_t first, int valid, int q,
+                                          float (&x)[kQuadElems]) {
+  constexpr int EB = BF16 ? 2 : 4;
+  const int vq = valid - kQuadElems * q;
+  const int64_t mine = first + kQuadElems * q;
+  if constexpr (WIDE) {
+    constexpr int VW = 16 / EB;  // elements per load
+    constexpr int NL = kQuadElems / VW;
+    uint4 raw[NL];
+#pragma unroll
+    for (int c = 0; c < NL; ++c) {
+      const int64_t e = VW * c < vq ? mine + VW * c : first;
+      raw[c] = *reinterpret_cast<const uint4*>(w + e * EB);
+    }
+#pragma unroll
+    for (int c = 0; c < NL; ++c) {
+      const uint32_t u[4] = {raw[c].x, raw[c].y, raw[c].z, raw[c].w};
+      const bool in = VW * c < vq;
+#pragma unroll
+      for (int k = 0; k < VW; ++k) {
+        uint32_t bits;
+        if constexpr (BF16)
+          bits = k & 1 ? u[k / 2] & 0xFFFF0000u : u[k / 2] << 16;
+        else
+          bits = u[k];
+        x[VW * c + k] = in ? __builtin_bit_cast(float, bits) : 0.0f;
+      }
+    }
+  } else {
+    uint32_t raw[kQuadElems];
+#pragma unroll
+    for (int m = 0; m < kQuadElems; ++m) {
+      const int64_t e = m < vq ? mine + m : first;
+      if constexpr (BF16)
+        raw[m] = static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(w)[e]) << 16;
+      else
+        raw[m] = reinterpret_cast<const uint32_t*>(w)[e];
+    }
+#pragma unroll
+    for (int m = 0; m < kQuadElems; ++m) x[m] = m < vq ? __builtin_bit_cast(float, raw[m]) : 0.0f;
+  }
+}
+
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Writes the existing ones of elements 32q .. 32q+31 of a group (see
+// quad_load for WIDE), float32 or bf16 (round to nearest even).
+template <bool BF16, bool WIDE>
+__device__ __forceinline__ void quad_store(uint8_t* __restrict__ out, int64_t first, int valid, int q,
+                                           const float (&y)[kQuadElems]) {
+  constexpr int EB = BF16 ? 2 : 4;
+  const int vq = valid - kQuadElems * q;
+  const int64_t mine = first + kQuadElems * q;
+  if constexpr (WIDE) {
+    constexpr int VW = 16 / EB;
+#pragma unroll
+    for (int c = 0; c < kQuadElems / VW; ++c) {
+      uint32_t u[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (BF16)
+          u[k] = bf16_bits_rne(y[VW * c + 2 * k]) | (bf16_bits_rne(y[VW * c + 2 * k + 1]) << 16);
+        else
+          u[k] = __builtin_bit_cast(uint32_t, y[VW * c + k]);
+      }
+      if (VW * c < vq) *reinterpret_cast<uint4*>(out + (mine + VW * c) * EB) = make_uint4(u[0], u[1], u[2], u[3]);
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < kQuadElems; ++m) {
+      if (m < vq) {
+        if constexpr (BF16)
+          reinterpret_cast<uint16_t*>(out)[mine + m] = static_cast<uint16_t>(bf16_bits_rne(y[m]));
+        else
+          reinterpret_cast<float*>(out)[mine + m] = y[m];
+      }
+    }
+  }
+}
+
+// Elements per 16-byte piece of the WIDE forms: 8 (bf16) or 4 (float32).
+constexpr int64_t wide_elems(bool bf16) { return bf16 ? 8 : 4; }
+
+// Blocks (one wave each) of a ragged kernel over n_groups groups: one 16-group
+// step per wave up to eight waves per CU, then a grid-stride loop.
+inline int quad_blocks(int64_t n_groups) {
+  const int64_t steps = (n_groups + kQuadGroups - 1) / kQuadGroups;
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
+  return static_cast<int>(steps < cap ? (steps > 0 ? steps : 1) : cap);
+}
+
 // Blocks of `waves` waves for a grid-stride kernel over n_batches batches in
 // which each wave takes about `per_wave` batches, but never fewer than one
 // batch per wave gives up to per_cu resident blocks per CU, so a mid-size
@@ -250,14 +441,16 @@ __device__ __forceinline__ int find_unit(const int64_t* __restrict__ start, int 
 // buffer may be reused as soon as the call returns.
 hipError_t upload(const void* src, size_t bytes, void* dst, hipStream_t stream);
 
+// ragged_cols_gcd: gcd of the ragged tensors' column counts (picks the
+// 16-byte load / store form where every width allows it).
 hipError_t launch_quantize_many(bool bf16, bool trits, const QuantParams& p, TensorTable<QuantDesc> contig,
                                 int64_t contig_batches, TensorTable<QuantDesc> ragged,
-                                int64_t ragged_groups, hipStream_t stream);
+                                int64_t ragged_groups, int64_t ragged_cols_gcd, hipStream_t stream);
 
 hipError_t launch_dequantize_many(int sbits, const LevelTable& lv, bool bf16_out,
                                   TensorTable<DequantDesc> contig, int64_t contig_batches,
                                   TensorTable<DequantDesc> ragged, int64_t ragged_groups,
-                                  hipStream_t stream);
+                                  int64_t ragged_cols_gcd, hipStream_t stream);
 
 // One matrix of a dequant-matvec call (device-side descriptor).
 struct MatvecDesc {

@@ -427,58 +427,113 @@ dequantize_contig(DequantJob job, LevelTable lv) {
   }
 }
 
-// General path: rows of any length; each lane writes its own group's valid
-// columns.
-// With MANY, thread g of the launch takes group g of the concatenation of the
-// table's tensors (t.start holds group prefixes); the plain arguments are
+// General path: rows whose length is not a multiple of 128, in quad form
+// (see quad_load / quad_butterfly_across): lane q of a quad reads the
+// quarter of its group's packed bytes that codes elements 32q .. 32q+31,
+// looks them up (the byte table also runs the first butterfly stages), runs
+// the remaining stages in its registers and across the quad, scales by
+// norm / 128 and writes its existing elements.  One-wave blocks take 16
+// groups per step of a grid-stride loop.  With MANY, unit u is group u of
+// the concatenation of the table's tensors and the plain arguments are
 // ignored.
-template <int SB, bool BF16OUT, bool MANY, bool TRITS = false>
-__global__ void __launch_bounds__(kBlock)
+template <int SB, bool BF16OUT, bool MANY, bool TRITS, bool WIDE>
+__global__ void __launch_bounds__(kWave)
 dequantize_ragged(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
                   int64_t rows, int64_t cols, LevelTable lv, uint8_t* __restrict__ out,
                   TensorTable<DequantDesc> t, int64_t total) {
   __shared__ __attribute__((aligned(16))) float tab[TableSize<SB>::floats];
   __shared__ uint16_t ttab[TRITS ? 256 : 1];
-  if constexpr (TRITS) fill_trit_table(ttab, threadIdx.x);
-  fill_table<SB>(tab, lv, threadIdx.x);
+#pragma unroll
+  for (int i = 0; i < 256; i += kWave) {
+    if constexpr (TRITS) fill_trit_table(ttab, i + threadIdx.x);
+    fill_table<SB>(tab, lv, i + threadIdx.x);
+  }
   __syncthreads();
-  int64_t g = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-  if constexpr (MANY) {
-    if (g >= total) return;
-    const int d = find_unit(t.start, 0, t.n, g);
-    const DequantDesc q = t.desc[d];
-    packed = q.packed;
-    norms = q.norms;
-    out = q.out;
-    rows = q.rows;
-    cols = q.cols;
-    g -= t.start[d];
-  }
-  const int64_t ngr = (cols + kGroup - 1) / kGroup;
-  if (g >= rows * ngr) return;
-  const int64_t row = g / ngr, col0 = (g - row * ngr) * kGroup;
-  const int64_t valid = cols - col0 < kGroup ? cols - col0 : kGroup;
-  uint32_t words[4 * SB];
-  if constexpr (TRITS) {
-    uint32_t tr[13];
-    const uint16_t* src = reinterpret_cast<const uint16_t*>(packed + g * kTritBytes);
-#pragma unroll
-    for (int k = 0; k < 13; ++k) tr[k] = src[k];
-    trits_to_fields(tr, ttab, words);
-  } else {
-    load_indices<SB>(packed, g, words);
-  }
-  float y[kGroup];
-  reconstruct_fast<SB>(words, norms[g], tab, y);
-  const int64_t base = row * cols + col0;
-#pragma unroll
-  for (int j = 0; j < kGroup; ++j) {
-    if (j < valid) {
-      if constexpr (BF16OUT)
-        reinterpret_cast<uint16_t*>(out)[base + j] = static_cast<uint16_t>(f32_to_bf16_rne(y[j]));
-      else
-        reinterpret_cast<float*>(out)[base + j] = y[j];
+  constexpr int PB = 16 * SB;  // packed bytes per group (2-bit fields for trits)
+  const int q = threadIdx.x & 3;
+  const int64_t n_units = MANY ? total : rows * ((cols + kGroup - 1) / kGroup);
+  const int64_t n_steps = (n_units + kQuadGroups - 1) / kQuadGroups;
+  for (int64_t s = blockIdx.x; s < n_steps; s += gridDim.x) {
+    int64_t u = s * kQuadGroups + (threadIdx.x >> 2);
+    const bool live = u < n_units;
+    if (!live) u = n_units - 1;  // the quad computes on a real group and stores nothing
+    const uint8_t* pk = packed;
+    const uint16_t* nm = norms;
+    uint8_t* o = out;
+    int64_t c = cols, gl = u;
+    if constexpr (MANY) {
+      const int d = find_unit(t.start, 0, t.n, u);
+      const DequantDesc* qd = t.desc + d;
+      pk = load_const(&qd->packed);
+      nm = load_const(&qd->norms);
+      o = load_const(&qd->out);
+      c = load_const(&qd->cols);
+      gl = u - load_const(t.start + d);
     }
+    const QuadPlace pl = quad_place(gl, c);
+    uint32_t words[SB];
+    if constexpr (TRITS) {
+      uint32_t tr[13], all[8];
+      const uint16_t* src = reinterpret_cast<const uint16_t*>(pk + gl * kTritBytes);
+#pragma unroll
+      for (int k = 0; k < 13; ++k) tr[k] = src[k];
+      trits_to_fields(tr, ttab, all);
+      words[0] = q == 0 ? all[0] : q == 1 ? all[2] : q == 2 ? all[4] : all[6];
+      words[1] = q == 0 ? all[1] : q == 1 ? all[3] : q == 2 ? all[5] : all[7];
+    } else {
+      const uint8_t* src = pk + gl * PB + q * (4 * SB);
+      if constexpr (SB == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(src);
+        words[0] = v.x;
+        words[1] = v.y;
+      } else if constexpr (SB == 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src);
+        words[0] = v.x;
+        words[1] = v.y;
+        words[2] = v.z;
+        words[3] = v.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < SB; ++i) words[i] = reinterpret_cast<const uint32_t*>(src)[i];
+      }
+    }
+    const uint16_t n16 = nm[gl];
+    float y[kQuadElems];
+    if constexpr (SB == 3) {
+      // Element m's field at bit 3m of the lane's 96 bits.
+#pragma unroll
+      for (int m = 0; m < kQuadElems; ++m) {
+        const int pos = 3 * m, wd = pos >> 5, off = pos & 31;
+        uint32_t v = words[wd] >> off;
+        if (off > 29) v |= words[wd + 1] << (32 - off);
+        y[m] = tab[v & 7u];
+      }
+      quad_butterfly_in_lane<1>(y);
+    } else {
+      constexpr int E = ByteTable<SB>::E;
+#pragma unroll
+      for (int k = 0; k < kQuadElems / E; ++k) {
+        const uint32_t b = (words[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+        if constexpr (E == 4) {
+          const float4 v = *reinterpret_cast<const float4*>(tab + 4 * b);
+          y[4 * k] = v.x;
+          y[4 * k + 1] = v.y;
+          y[4 * k + 2] = v.z;
+          y[4 * k + 3] = v.w;
+        } else {
+          const float2 v = *reinterpret_cast<const float2*>(tab + 2 * b);
+          y[2 * k] = v.x;
+          y[2 * k + 1] = v.y;
+        }
+      }
+      quad_butterfly_in_lane<E>(y);
+    }
+    quad_butterfly_across<1>(y, q);
+    quad_butterfly_across<2>(y, q);
+    const float sc = half_to_float(n16) * (1.0f / kGroup);
+#pragma unroll
+    for (int j = 0; j < kQuadElems; ++j) y[j] *= sc;
+    if (live) quad_store<BF16OUT, WIDE>(o, pl.first, pl.valid, q, y);
   }
 }
 
@@ -506,18 +561,22 @@ hipError_t launch_sb(const uint8_t* packed, const uint16_t* norms, int64_t rows,
     hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT, false, TRITS>), dim3(g.blocks), dim3(g.waves * kWave), 0, s,
                        job, lv);
   } else {
-    const int64_t n_groups = rows * ((cols + kGroup - 1) / kGroup);
-    const int blocks = static_cast<int>((n_groups + kBlock - 1) / kBlock);
-    hipLaunchKernelGGL((dequantize_ragged<SB, BF16OUT, false, TRITS>), dim3(blocks), dim3(kBlock), 0, s,
-                       packed, norms, rows, cols, lv, ob, TensorTable<DequantDesc>{nullptr, nullptr, 0},
-                       int64_t{0});
+    const int blocks = quad_blocks(rows * ((cols + kGroup - 1) / kGroup));
+    const TensorTable<DequantDesc> none{nullptr, nullptr, 0};
+    if (cols % wide_elems(BF16OUT) == 0)  // whole 16-byte pieces (the output is 16-byte aligned)
+      hipLaunchKernelGGL((dequantize_ragged<SB, BF16OUT, false, TRITS, true>), dim3(blocks), dim3(kWave), 0, s,
+                         packed, norms, rows, cols, lv, ob, none, int64_t{0});
+    else
+      hipLaunchKernelGGL((dequantize_ragged<SB, BF16OUT, false, TRITS, false>), dim3(blocks), dim3(kWave), 0, s,
+                         packed, norms, rows, cols, lv, ob, none, int64_t{0});
   }
   return hipGetLastError();
 }
 
 template <int SB, bool BF16OUT, bool TRITS>
 hipError_t launch_many_sb(const LevelTable& lv, TensorTable<DequantDesc> contig, int64_t contig_batches,
-                          TensorTable<DequantDesc> ragged, int64_t ragged_groups, hipStream_t s) {
+                          TensorTable<DequantDesc> ragged, int64_t ragged_groups, int64_t ragged_cols_gcd,
+                          hipStream_t s) {
   if (contig_batches > 0) {
     const ContigGrid g = dequant_grid<BF16OUT>(contig_batches);
     const DequantJob job{nullptr, nullptr, nullptr, 0, contig, contig_batches};
@@ -527,9 +586,13 @@ hipError_t launch_many_sb(const LevelTable& lv, TensorTable<DequantDesc> contig,
     if (e != hipSuccess) return e;
   }
   if (ragged_groups > 0) {
-    const int blocks = static_cast<int>((ragged_groups + kBlock - 1) / kBlock);
-    hipLaunchKernelGGL((dequantize_ragged<SB, BF16OUT, true, TRITS>), dim3(blocks), dim3(kBlock), 0, s,
-                       nullptr, nullptr, int64_t{0}, int64_t{0}, lv, nullptr, ragged, ragged_groups);
+    const int blocks = quad_blocks(ragged_groups);
+    if (ragged_cols_gcd % wide_elems(BF16OUT) == 0)  // every ragged width, so their gcd
+      hipLaunchKernelGGL((dequantize_ragged<SB, BF16OUT, true, TRITS, true>), dim3(blocks), dim3(kWave), 0, s,
+                         nullptr, nullptr, int64_t{0}, int64_t{0}, lv, nullptr, ragged, ragged_groups);
+    else
+      hipLaunchKernelGGL((dequantize_ragged<SB, BF16OUT, true, TRITS, false>), dim3(blocks), dim3(kWave), 0, s,
+                         nullptr, nullptr, int64_t{0}, int64_t{0}, lv, nullptr, ragged, ragged_groups);
   }
   return hipGetLastError();
 }
@@ -537,9 +600,10 @@ hipError_t launch_many_sb(const LevelTable& lv, TensorTable<DequantDesc> contig,
 template <int SB, bool TRITS = false>
 hipError_t launch_many_out(const LevelTable& lv, bool bf16_out, TensorTable<DequantDesc> contig,
                            int64_t contig_batches, TensorTable<DequantDesc> ragged, int64_t ragged_groups,
-                           hipStream_t s) {
-  return bf16_out ? launch_many_sb<SB, true, TRITS>(lv, contig, contig_batches, ragged, ragged_groups, s)
-                  : launch_many_sb<SB, false, TRITS>(lv, contig, contig_batches, ragged, ragged_groups, s);
+                           int64_t ragged_cols_gcd, hipStream_t s) {
+  return bf16_out
+             ? launch_many_sb<SB, true, TRITS>(lv, contig, contig_batches, ragged, ragged_groups, ragged_cols_gcd, s)
+             : launch_many_sb<SB, false, TRITS>(lv, contig, contig_batches, ragged, ragged_groups, ragged_cols_gcd, s);
 }
 
 template <int SB, bool TRITS = false>
@@ -567,13 +631,17 @@ hipError_t launch_dequantize(const uint8_t* packed, const uint16_t* norms, int64
 hipError_t launch_dequantize_many(int sbits, const LevelTable& lv, bool bf16_out,
                                   TensorTable<DequantDesc> contig, int64_t contig_batches,
                                   TensorTable<DequantDesc> ragged, int64_t ragged_groups,
-                                  hipStream_t stream) {
+                                  int64_t ragged_cols_gcd, hipStream_t stream) {
   switch (sbits) {
-    case 2: return kd::launch_many_out<2>(lv, bf16_out, contig, contig_batches, ragged, ragged_groups, stream);
-    case 3: return kd::launch_many_out<3>(lv, bf16_out, contig, contig_batches, ragged, ragged_groups, stream);
-    case 4: return kd::launch_many_out<4>(lv, bf16_out, contig, contig_batches, ragged, ragged_groups, stream);
+    case 2: return kd::launch_many_out<2>(lv, bf16_out, contig, contig_batches, ragged, ragged_groups, ragged_cols_gcd,
+                                         stream);
+    case 3: return kd::launch_many_out<3>(lv, bf16_out, contig, contig_batches, ragged, ragged_groups, ragged_cols_gcd,
+                                         stream);
+    case 4: return kd::launch_many_out<4>(lv, bf16_out, contig, contig_batches, ragged, ragged_groups, ragged_cols_gcd,
+                                         stream);
     case kTritStorage:
-      return kd::launch_many_out<2, true>(lv, bf16_out, contig, contig_batches, ragged, ragged_groups, stream);
+      return kd::launch_many_out<2, true>(lv, bf16_out, contig, contig_batches, ragged, ragged_groups, ragged_cols_gcd,
+                                         stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -18,6 +18,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <numeric>
 #include <vector>
 
 #include "../../include/libcq.h"
@@ -266,6 +267,7 @@ template <class D>
 struct ManyTables {
   std::vector<D> contig, ragged;
   std::vector<int64_t> bstart{0}, gstart{0};  // 64-group batches / groups
+  int64_t ragged_gcd = 0;                       // gcd of the ragged tensors' column counts
   uint8_t* ws = nullptr;
   cq::TensorTable<D> tc{}, tr{};
 
@@ -276,6 +278,7 @@ struct ManyTables {
     } else {
       ragged.push_back(d);
       gstart.push_back(gstart.back() + n_groups);
+      ragged_gcd = std::gcd(ragged_gcd, d.cols);
     }
   }
   bool empty() const { return contig.empty() && ragged.empty(); }
@@ -568,7 +571,7 @@ int cq_quantize_many(int n, const cq_quant_desc* descs, int w_dtype, int bits, i
   rc = t.upload(s);
   if (!rc)
     rc = hip_status(cq::launch_quantize_many(w_dtype == CQ_BF16, bits == CQ_TERNARY_TRITS, p, t.tc, t.bstart.back(), t.tr,
-                                             t.gstart.back(), s),
+                                             t.gstart.back(), t.ragged_gcd, s),
                     "quantize launch");
   const int rc2 = t.release(s);
   return rc ? rc : rc2;
@@ -625,7 +628,7 @@ int cq_dequantize_many(int n, const cq_dequant_desc* descs, int bits, int group_
   rc = t.upload(s);
   if (!rc)
     rc = hip_status(cq::launch_dequantize_many(storage_code(bits), lv, out_dtype == CQ_BF16, t.tc, t.bstart.back(), t.tr,
-                                               t.gstart.back(), s),
+                                               t.gstart.back(), t.ragged_gcd, s),
                     "dequantize launch");
   const int rc2 = t.release(s);
   return rc ? rc : rc2;

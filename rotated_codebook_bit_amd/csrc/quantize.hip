@@ -541,61 +541,171 @@ quantize_contig(QuantJob job, QuantParams p) {
   store_batch<L, BF16, TRITS>(prev.packed, prev.norms, prev.bt, prev.n_groups, lane, words, n16);
 }
 
-// General path: rows whose length is not a multiple of 128; the last group
-// of each row is zero-padded.  Each lane gathers its own group.
-// With MANY, thread g of the launch takes group g of the concatenation of the
-// table's tensors (t.start holds group prefixes) and the plain arguments are
-// ignored.
-template <int L, bool BF16, bool MANY, bool TRITS = false>
-__global__ void __launch_bounds__(kBlock)
-quantize_ragged(const uint8_t* __restrict__ w, int64_t rows, int64_t cols, QuantParams p,
-                uint8_t* __restrict__ packed, uint16_t* __restrict__ norms,
-                TensorTable<QuantDesc> t, int64_t total) {
-  int64_t g = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-  if constexpr (MANY) {
-    if (g >= total) return;
-    const int d = find_unit(t.start, 0, t.n, g);
-    const QuantDesc q = t.desc[d];
-    w = q.w;
-    packed = q.packed;
-    norms = q.norms;
-    rows = q.rows;
-    cols = q.cols;
-    g -= t.start[d];
-  }
-  const int64_t ngr = (cols + kGroup - 1) / kGroup;
-  const int64_t n_groups = rows * ngr;
-  if (g >= n_groups) return;
-  const int64_t row = g / ngr, gi = g - row * ngr;
-  const int64_t col0 = gi * kGroup;
-  const int64_t valid = cols - col0 < kGroup ? cols - col0 : kGroup;
-  const int64_t base = row * cols + col0;
-  float x[kGroup];
+// Decisions and packed fields of a lane's 32 elements (ragged kernels):
+// y holds the lane's butterfly outputs, ns the decision scale.  The lane's
+// elements 32q .. 32q+31 fill a contiguous quarter of the group's packed
+// bits, Shape<L>::sbits dwords, in the same LSB-first order as finish_group.
+template <int L>
+__device__ __forceinline__ void decide_quarter(const float (&y)[kQuadElems], float ns, const QuantParams& p,
+                                               uint32_t (&words)[Shape<L>::sbits]) {
+  if constexpr (L == 3 || L == 4) {
+    const float A = p.hmid * ns, D = p.delta * ns;
 #pragma unroll
-  for (int j = 0; j < kGroup; ++j) {
-    float v = 0.0f;
-    if (j < valid) {
-      if constexpr (BF16) {
-        const uint16_t b = reinterpret_cast<const uint16_t*>(w)[base + j];
-        v = __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);
-      } else {
-        v = reinterpret_cast<const float*>(w)[base + j];
+    for (int wd = 0; wd < 2; ++wd) {
+      uint32_t acc = 0;
+#pragma unroll
+      for (int pos = 15; pos >= 0; --pos) {
+        const float v = y[16 * wd + pos];
+        acc = shift_in(acc, v > A);
+        acc = shift_in(acc, __builtin_fabsf(v) > D);
       }
+      if constexpr (L == 4)
+        acc ^= ((acc >> 1) & 0x55555555u) ^ 0x55555555u;
+      else
+        acc ^= 0x55555555u;
+      words[wd] = acc;
     }
-    x[j] = v;
+  } else if constexpr (L == 8) {
+    float T[kMaxLevels - 1];
+#pragma unroll
+    for (int i = 0; i < 7; ++i) T[i] = p.thr[i] * ns;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) words[i] = 0;
+#pragma unroll
+    for (int j = 0; j < kQuadElems; ++j) {
+      const uint32_t idx = search8(y[j], T);
+      const int pos = 3 * j, wd = pos >> 5, off = pos & 31;
+      words[wd] |= idx << off;
+      if (off > 29) words[wd + 1] |= idx >> (32 - off);
+    }
+  } else {
+    float T[kMaxLevels - 1];
+#pragma unroll
+    for (int i = 0; i < 15; ++i) T[i] = p.thr[i] * ns;
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+      uint32_t acc = 0;
+#pragma unroll
+      for (int pos = 7; pos >= 0; --pos) {
+        bool b3, b2, b1, b0;
+        search16(y[8 * wd + pos], T, b3, b2, b1, b0);
+        acc = shift_in(acc, b3);
+        acc = shift_in(acc, b2);
+        acc = shift_in(acc, b1);
+        acc = shift_in(acc, b0);
+      }
+      words[wd] = acc;
+    }
   }
-  float y[kGroup];
+}
+
+// Front half of a ragged-path group in quad form: load the lane's 32
+// elements, stage 1 and the quad's sum of squares, the two-compare shift
+// (lane 0 holds the group's first pair), stages 2..7.  Returns the group
+// norm; *ns is the decision scale, as in forward_group.
+template <int L, bool BF16, bool WIDE>
+__device__ __forceinline__ float quad_forward(const uint8_t* __restrict__ w, const QuadPlace& pl, int q,
+                                              const QuantParams& p, float (&y)[kQuadElems], float* ns_out) {
+  float x[kQuadElems];
+  quad_load<BF16, WIDE>(w, pl.first, pl.valid, q, x);
   float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-  for (int i = 0; i < kGroup; i += 2) {
+  for (int i = 0; i < kQuadElems; i += 2) {
     y[i] = x[i] + x[i + 1];
     y[i + 1] = x[i] - x[i + 1];
     s0 = __builtin_fmaf(x[i], x[i], s0);
     s1 = __builtin_fmaf(x[i + 1], x[i + 1], s1);
   }
-  uint32_t words[Shape<L>::words];
-  const uint16_t n16 = finish_group<L>(y, s0 + s1, p, words);
-  store_group<L>(packed, norms, g, words, n16, TRITS);
+  const float S = quad_sum(s0 + s1);
+  const float n = __builtin_sqrtf(S);
+  const float ns = S > 0.0f ? n : 1.0f;
+  if constexpr (L == 3 || L == 4) {
+    const float sh = q == 0 ? p.mu * ns : 0.0f;
+    y[0] -= sh;
+    y[1] -= sh;
+  }
+  quad_butterfly_in_lane<2>(y);
+  quad_butterfly_across<1>(y, q);
+  quad_butterfly_across<2>(y, q);
+  *ns_out = ns;
+  return n;
+}
+
+// Unit u of a ragged launch: its group within its tensor and that tensor's
+// pointers and width.  With MANY, u indexes the concatenation of the
+// table's tensors (t.start holds group prefixes); without, the plain
+// arguments describe the one tensor.
+template <bool MANY>
+__device__ __forceinline__ void ragged_unit(const TensorTable<QuantDesc>& t, int64_t u, const uint8_t*& w,
+                                            uint8_t*& packed, uint16_t*& norms, int64_t& cols, int64_t& gl) {
+  gl = u;
+  if constexpr (MANY) {
+    const int d = find_unit(t.start, 0, t.n, u);
+    const QuantDesc* qd = t.desc + d;
+    w = load_const(&qd->w);
+    packed = load_const(&qd->packed);
+    norms = load_const(&qd->norms);
+    cols = load_const(&qd->cols);
+    gl = u - load_const(t.start + d);
+  }
+}
+
+// General path: rows whose length is not a multiple of 128; the last group
+// of each row is zero-padded.  A quad of lanes takes one group (quad form
+// of the transform, see quad_load and quad_butterfly_across); each lane
+// decides and packs its own 32 elements and stores its quarter of the
+// group's packed bytes, lane 0 the norm.  One-wave blocks take 16 groups per
+// step of a grid-stride loop (quad_blocks).
+template <int L, bool BF16, bool MANY, bool TRITS, bool WIDE>
+__global__ void __launch_bounds__(kWave)
+quantize_ragged(const uint8_t* __restrict__ w, int64_t rows, int64_t cols, QuantParams p,
+                uint8_t* __restrict__ packed, uint16_t* __restrict__ norms,
+                TensorTable<QuantDesc> t, int64_t total) {
+  constexpr int SW = Shape<L>::sbits;      // packed dwords per lane
+  constexpr int PB = Shape<L>::words * 4;  // packed bytes per group
+  const int q = threadIdx.x & 3;
+  const int64_t n_units = MANY ? total : rows * ((cols + kGroup - 1) / kGroup);
+  const int64_t n_steps = (n_units + kQuadGroups - 1) / kQuadGroups;
+  for (int64_t s = blockIdx.x; s < n_steps; s += gridDim.x) {
+    int64_t u = s * kQuadGroups + (threadIdx.x >> 2);
+    const bool live = u < n_units;
+    if (!live) u = n_units - 1;  // the quad computes on a real group and stores nothing
+    const uint8_t* src = w;
+    uint8_t* pk = packed;
+    uint16_t* nm = norms;
+    int64_t c = cols, gl;
+    ragged_unit<MANY>(t, u, src, pk, nm, c, gl);
+    const QuadPlace pl = quad_place(gl, c);
+    float y[kQuadElems], ns;
+    const float n = quad_forward<L, BF16, WIDE>(src, pl, q, p, y, &ns);
+    uint32_t words[SW];
+    decide_quarter<L>(y, ns, p, words);
+    const uint16_t n16 = __builtin_bit_cast(uint16_t, static_cast<_Float16>(n));
+    if constexpr (TRITS) {
+      // The quad's eight field dwords, then trit bytes; lane q writes the
+      // byte pairs k = q, q + 4, ... (13 pairs, 26 bytes, 2-byte aligned).
+      uint32_t all[8] = {quad_bcast<0>(words[0]), quad_bcast<0>(words[1]), quad_bcast<1>(words[0]),
+                         quad_bcast<1>(words[1]), quad_bcast<2>(words[0]), quad_bcast<2>(words[1]),
+                         quad_bcast<3>(words[0]), quad_bcast<3>(words[1])};
+      uint32_t tr[13];
+      fields_to_trits(all, tr);
+      uint16_t* dst = reinterpret_cast<uint16_t*>(pk + gl * kTritBytes);
+#pragma unroll
+      for (int k = 0; k < 13; ++k)
+        if (live && (k & 3) == q) dst[k] = static_cast<uint16_t>(tr[k]);
+    } else if (live) {
+      uint8_t* dst = pk + gl * PB + q * (4 * SW);
+      if constexpr (SW == 2) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(words[0], words[1]);
+      } else if constexpr (SW == 4) {
+        *reinterpret_cast<uint4*>(dst) = make_uint4(words[0], words[1], words[2], words[3]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < SW; ++i) reinterpret_cast<uint32_t*>(dst)[i] = words[i];
+      }
+    }
+    if (live && q == 0) nm[gl] = n16;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -821,10 +931,44 @@ fakequant_contig(const uint8_t* __restrict__ w, int64_t n_groups, QuantParams p,
   }
 }
 
-// General path: rows of any length; each lane gathers its own group and
-// writes its valid columns.
-template <int L, bool BF16IN, bool BF16OUT>
-__global__ void __launch_bounds__(kBlock)
+// Levels of a lane's 32 decisions, in place (ragged fake quant; the same
+// decisions as decide_quarter).
+template <int L>
+__device__ __forceinline__ void levels_quarter(float (&y)[kQuadElems], float ns, const QuantParams& p,
+                                               const LevelTable& lv, const float* lut) {
+  if constexpr (L == 3 || L == 4) {
+    const float A = p.hmid * ns, D = p.delta * ns;
+    const float lo = lv.c[0], mid = lv.c[1], hi = lv.c[L - 1], mid2 = lv.c[L == 4 ? 2 : 1];
+#pragma unroll
+    for (int j = 0; j < kQuadElems; ++j) {
+      const float v = y[j];
+      const bool h = v > A, q = __builtin_fabsf(v) > D;
+      y[j] = q ? (h ? hi : lo) : (h ? mid2 : mid);
+    }
+  } else if constexpr (L == 8) {
+    float T[kMaxLevels - 1];
+#pragma unroll
+    for (int i = 0; i < 7; ++i) T[i] = p.thr[i] * ns;
+#pragma unroll
+    for (int j = 0; j < kQuadElems; ++j) y[j] = lut[search8(y[j], T)];
+  } else {
+    float T[kMaxLevels - 1];
+#pragma unroll
+    for (int i = 0; i < 15; ++i) T[i] = p.thr[i] * ns;
+#pragma unroll
+    for (int j = 0; j < kQuadElems; ++j) {
+      bool b3, b2, b1, b0;
+      search16(y[j], T, b3, b2, b1, b0);
+      y[j] = lut[(bit(b3) << 3) | (bit(b2) << 2) | (bit(b1) << 1) | bit(b0)];
+    }
+  }
+}
+
+// General path: rows of any length, in quad form (see quantize_ragged): the
+// quad's forward transform, each lane's levels, the 7-stage transform back,
+// the unrounded norm / 128, and each lane writes its existing elements.
+template <int L, bool BF16IN, bool BF16OUT, bool WIDE>
+__global__ void __launch_bounds__(kWave)
 fakequant_ragged(const uint8_t* __restrict__ w, int64_t rows, int64_t cols, QuantParams p,
                  LevelTable lv, uint8_t* __restrict__ out) {
   __shared__ float lut[kMaxLevels];
@@ -835,49 +979,24 @@ fakequant_ragged(const uint8_t* __restrict__ w, int64_t rows, int64_t cols, Quan
     hold_values(v);
   }
   __syncthreads();
-  const int64_t ngr = (cols + kGroup - 1) / kGroup;
-  const int64_t g = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-  if (g >= rows * ngr) return;
-  const int64_t row = g / ngr, col0 = (g - row * ngr) * kGroup;
-  const int64_t valid = cols - col0 < kGroup ? cols - col0 : kGroup;
-  const int64_t base = row * cols + col0;
-  float x[kGroup];
+  const int q = threadIdx.x & 3;
+  const int64_t n_units = rows * ((cols + kGroup - 1) / kGroup);
+  const int64_t n_steps = (n_units + kQuadGroups - 1) / kQuadGroups;
+  for (int64_t s = blockIdx.x; s < n_steps; s += gridDim.x) {
+    int64_t u = s * kQuadGroups + (threadIdx.x >> 2);
+    const bool live = u < n_units;
+    if (!live) u = n_units - 1;
+    const QuadPlace pl = quad_place(u, cols);
+    float y[kQuadElems], ns;
+    const float n = quad_forward<L, BF16IN, WIDE>(w, pl, q, p, y, &ns);
+    levels_quarter<L>(y, ns, p, lv, lut);
+    quad_butterfly_in_lane<1>(y);
+    quad_butterfly_across<1>(y, q);
+    quad_butterfly_across<2>(y, q);
+    const float sc = n * (1.0f / kGroup);
 #pragma unroll
-  for (int j = 0; j < kGroup; ++j) {
-    float v = 0.0f;
-    if (j < valid) {
-      if constexpr (BF16IN) {
-        const uint16_t b = reinterpret_cast<const uint16_t*>(w)[base + j];
-        v = __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);
-      } else {
-        v = reinterpret_cast<const float*>(w)[base + j];
-      }
-    }
-    x[j] = v;
-  }
-  float y[kGroup];
-  float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-  for (int i = 0; i < kGroup; i += 2) {
-    y[i] = x[i] + x[i + 1];
-    y[i + 1] = x[i] - x[i + 1];
-    s0 = __builtin_fmaf(x[i], x[i], s0);
-    s1 = __builtin_fmaf(x[i + 1], x[i + 1], s1);
-  }
-  float ns;
-  const float n = forward_group<L>(y, s0 + s1, p, &ns);
-  levels_in_place<L>(y, ns, p, lv, lut);
-  butterfly_all(y);
-  const float sc = n * (1.0f / kGroup);
-#pragma unroll
-  for (int j = 0; j < kGroup; ++j) {
-    if (j < valid) {
-      const float v = y[j] * sc;
-      if constexpr (BF16OUT)
-        reinterpret_cast<uint16_t*>(out)[base + j] = static_cast<uint16_t>(f32_to_bf16_rne(v));
-      else
-        reinterpret_cast<float*>(out)[base + j] = v;
-    }
+    for (int j = 0; j < kQuadElems; ++j) y[j] *= sc;
+    if (live) quad_store<BF16OUT, WIDE>(out, pl.first, pl.valid, q, y);
   }
 }
 
@@ -894,10 +1013,15 @@ hipError_t launch_fq(const void* w, int64_t rows, int64_t cols, const QuantParam
     hipLaunchKernelGGL((fakequant_contig<L, BF16IN, BF16OUT>), dim3(blocks), dim3(W * kWave), 0, s, wb,
                        n_groups, p, lv, ob);
   } else {
-    const int64_t n_groups = rows * ((cols + kGroup - 1) / kGroup);
-    const int blocks = static_cast<int>((n_groups + kBlock - 1) / kBlock);
-    hipLaunchKernelGGL((fakequant_ragged<L, BF16IN, BF16OUT>), dim3(blocks), dim3(kBlock), 0, s, wb, rows,
-                       cols, p, lv, ob);
+    const int blocks = quad_blocks(rows * ((cols + kGroup - 1) / kGroup));
+    // 16-byte pieces need whole pieces on both sides (16-byte aligned base
+    // pointers are required by the caller).
+    if (cols % wide_elems(BF16IN) == 0 && cols % wide_elems(BF16OUT) == 0)
+      hipLaunchKernelGGL((fakequant_ragged<L, BF16IN, BF16OUT, true>), dim3(blocks), dim3(kWave), 0, s, wb, rows,
+                         cols, p, lv, ob);
+    else
+      hipLaunchKernelGGL((fakequant_ragged<L, BF16IN, BF16OUT, false>), dim3(blocks), dim3(kWave), 0, s, wb, rows,
+                         cols, p, lv, ob);
   }
   return hipGetLastError();
 }
@@ -936,17 +1060,22 @@ hipError_t launch_l(const void* w, int64_t rows, int64_t cols, const QuantParams
     hipLaunchKernelGGL((quantize_contig<L, BF16, false, TRITS>), dim3(g.blocks), dim3(g.waves * kWave), 0, s, job,
                        p);
   } else {
-    const int64_t n_groups = rows * ((cols + kGroup - 1) / kGroup);
-    const int blocks = static_cast<int>((n_groups + kBlock - 1) / kBlock);
-    hipLaunchKernelGGL((quantize_ragged<L, BF16, false, TRITS>), dim3(blocks), dim3(kBlock), 0, s, wb, rows,
-                       cols, p, packed, norms, TensorTable<QuantDesc>{nullptr, nullptr, 0}, int64_t{0});
+    const int blocks = quad_blocks(rows * ((cols + kGroup - 1) / kGroup));
+    const TensorTable<QuantDesc> none{nullptr, nullptr, 0};
+    if (cols % wide_elems(BF16) == 0)
+      hipLaunchKernelGGL((quantize_ragged<L, BF16, false, TRITS, true>), dim3(blocks), dim3(kWave), 0, s, wb,
+                         rows, cols, p, packed, norms, none, int64_t{0});
+    else
+      hipLaunchKernelGGL((quantize_ragged<L, BF16, false, TRITS, false>), dim3(blocks), dim3(kWave), 0, s, wb,
+                         rows, cols, p, packed, norms, none, int64_t{0});
   }
   return hipGetLastError();
 }
 
 template <int L, bool BF16, bool TRITS>
 hipError_t launch_many_l(const QuantParams& p, TensorTable<QuantDesc> contig, int64_t contig_batches,
-                         TensorTable<QuantDesc> ragged, int64_t ragged_groups, hipStream_t s) {
+                         TensorTable<QuantDesc> ragged, int64_t ragged_groups, int64_t ragged_cols_gcd,
+                         hipStream_t s) {
   if (contig_batches > 0) {
     const ContigGrid g = quant_grid<BF16>(contig_batches);
     const QuantJob job{nullptr, nullptr, nullptr, 0, contig, contig_batches};
@@ -956,9 +1085,15 @@ hipError_t launch_many_l(const QuantParams& p, TensorTable<QuantDesc> contig, in
     if (e != hipSuccess) return e;
   }
   if (ragged_groups > 0) {
-    const int blocks = static_cast<int>((ragged_groups + kBlock - 1) / kBlock);
-    hipLaunchKernelGGL((quantize_ragged<L, BF16, true, TRITS>), dim3(blocks), dim3(kBlock), 0, s, nullptr,
-                       int64_t{0}, int64_t{0}, p, nullptr, nullptr, ragged, ragged_groups);
+    // The 16-byte form needs every ragged tensor's width to be a multiple
+    // of the piece (their gcd is).
+    const int blocks = quad_blocks(ragged_groups);
+    if (ragged_cols_gcd % wide_elems(BF16) == 0)
+      hipLaunchKernelGGL((quantize_ragged<L, BF16, true, TRITS, true>), dim3(blocks), dim3(kWave), 0, s, nullptr,
+                         int64_t{0}, int64_t{0}, p, nullptr, nullptr, ragged, ragged_groups);
+    else
+      hipLaunchKernelGGL((quantize_ragged<L, BF16, true, TRITS, false>), dim3(blocks), dim3(kWave), 0, s,
+                         nullptr, int64_t{0}, int64_t{0}, p, nullptr, nullptr, ragged, ragged_groups);
   }
   return hipGetLastError();
 }
@@ -967,15 +1102,15 @@ hipError_t launch_many_l(const QuantParams& p, TensorTable<QuantDesc> contig, in
 template <int L>
 hipError_t launch_many_dtype(bool bf16, bool trits, const QuantParams& p, TensorTable<QuantDesc> contig,
                              int64_t contig_batches, TensorTable<QuantDesc> ragged,
-                             int64_t ragged_groups, hipStream_t s) {
+                             int64_t ragged_groups, int64_t ragged_cols_gcd, hipStream_t s) {
   if constexpr (L == 3) {
     if (trits)
-      return bf16 ? launch_many_l<L, true, true>(p, contig, contig_batches, ragged, ragged_groups, s)
-                  : launch_many_l<L, false, true>(p, contig, contig_batches, ragged, ragged_groups, s);
+      return bf16 ? launch_many_l<L, true, true>(p, contig, contig_batches, ragged, ragged_groups, ragged_cols_gcd, s)
+                  : launch_many_l<L, false, true>(p, contig, contig_batches, ragged, ragged_groups, ragged_cols_gcd, s);
   }
   if (trits) return hipErrorInvalidValue;
-  return bf16 ? launch_many_l<L, true, false>(p, contig, contig_batches, ragged, ragged_groups, s)
-              : launch_many_l<L, false, false>(p, contig, contig_batches, ragged, ragged_groups, s);
+  return bf16 ? launch_many_l<L, true, false>(p, contig, contig_batches, ragged, ragged_groups, ragged_cols_gcd, s)
+              : launch_many_l<L, false, false>(p, contig, contig_batches, ragged, ragged_groups, ragged_cols_gcd, s);
 }
 
 template <int L>
@@ -1019,12 +1154,12 @@ hipError_t launch_quantize(const void* w, bool bf16, bool trits, int64_t rows, i
 
 hipError_t launch_quantize_many(bool bf16, bool trits, const QuantParams& p, TensorTable<QuantDesc> contig,
                                 int64_t contig_batches, TensorTable<QuantDesc> ragged,
-                                int64_t ragged_groups, hipStream_t stream) {
+                                int64_t ragged_groups, int64_t ragged_cols_gcd, hipStream_t stream) {
   switch (p.n_levels) {
-    case 3: return kq::launch_many_dtype<3>(bf16, trits, p, contig, contig_batches, ragged, ragged_groups, stream);
-    case 4: return kq::launch_many_dtype<4>(bf16, trits, p, contig, contig_batches, ragged, ragged_groups, stream);
-    case 8: return kq::launch_many_dtype<8>(bf16, trits, p, contig, contig_batches, ragged, ragged_groups, stream);
-    case 16: return kq::launch_many_dtype<16>(bf16, trits, p, contig, contig_batches, ragged, ragged_groups, stream);
+    case 3: return kq::launch_many_dtype<3>(bf16, trits, p, contig, contig_batches, ragged, ragged_groups, ragged_cols_gcd, stream);
+    case 4: return kq::launch_many_dtype<4>(bf16, trits, p, contig, contig_batches, ragged, ragged_groups, ragged_cols_gcd, stream);
+    case 8: return kq::launch_many_dtype<8>(bf16, trits, p, contig, contig_batches, ragged, ragged_groups, ragged_cols_gcd, stream);
+    case 16: return kq::launch_many_dtype<16>(bf16, trits, p, contig, contig_batches, ragged, ragged_groups, ragged_cols_gcd, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -178,6 +178,55 @@ def test_many_small_mixed(bits, levels):
         assert torch.equal(o1, out), (rows, cols)
 
 
+# Ragged tensors of one call load and store in 16-byte pieces when every
+# ragged width is a multiple of the piece (8 bf16 or 4 float32 elements),
+# else element by element: sets whose widths have gcd 8, 4 and 2.
+RAGGED_SETS = [[(7, 1000), (3, 200), (11, 1016)], [(5, 1004), (3, 1000), (2, 12)], [(4, 130), (6, 1000), (1, 1)]]
+
+
+@pytest.mark.parametrize("bits", ALL_BITS)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("which", range(len(RAGGED_SETS)))
+def test_many_ragged_widths(bits, dtype, which, levels):
+    """Only ragged tensors in one call: bit-identical to the single-tensor
+    calls (each picks its own load form), and the oracle's rules."""
+    lv = levels[bits]
+    shapes = RAGGED_SETS[which]
+    rng = np.random.default_rng(zlib.crc32(repr(("ragged", bits, dtype, which)).encode()))
+    hosts = [(rng.standard_normal(s) * 0.02).astype(np.float32) for s in shapes]
+    if dtype == "bf16":
+        hb = [W.f32_to_bf16_bits(h) for h in hosts]
+        ws = [torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to(DEV).view(torch.bfloat16) for b in hb]
+        w64 = [W.bf16_bits_to_f32(b).astype(np.float64) for b in hb]
+    else:
+        ws = [torch.from_numpy(h).to(DEV) for h in hosts]
+        w64 = [h.astype(np.float64) for h in hosts]
+    say(f"quantize_many ragged {shapes} {dtype} bits={bits}")
+    blob, views = cq.quantize_many(ws, bits, lv)
+    items, refs = [], []
+    for s, w, x64, (pk, nm) in zip(shapes, ws, w64, views):
+        p1, n1 = cq.quantize(w, bits, lv)
+        assert np.array_equal(host(p1), host(pk)), s
+        assert np.array_equal(f16_bits(n1), f16_bits(nm)), s
+        q = O.quantize(x64, bits, lv)
+        check_quantize(host(pk), f16_bits(nm), q)
+        # Dequantize the oracle's packing, so the expected values are the
+        # oracle's alone.
+        items.append((torch.from_numpy(q.packed.reshape(s[0], -1)).to(DEV),
+                      torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16), s[0], s[1]))
+        refs.append((O.dequantize(q.packed, q.norm16, s[0], s[1], bits, lv), q.norm16))
+    say(f"dequantize_many ragged {shapes} bits={bits}")
+    for odt in (torch.float32, torch.bfloat16):
+        outs = cq.dequantize_many(items, bits, lv, out_dtype=odt)
+        for (pk, nm, rows, cols), out, (ref, n16) in zip(items, outs, refs):
+            o1 = cq.dequantize(pk, nm, rows, cols, bits, lv, out_dtype=odt)
+            if odt == torch.bfloat16:
+                assert torch.equal(o1.view(torch.int16), out.view(torch.int16)), (rows, cols, odt)
+            else:
+                assert torch.equal(o1, out), (rows, cols, odt)
+                check_dequant(host(out), ref, n16, rows, cols)
+
+
 def test_quantize_many_shared_input(levels):
     """Two descriptors may read the same input; their outputs are equal."""
     lv = levels[2]

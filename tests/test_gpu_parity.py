@@ -102,7 +102,10 @@ def test_small_matrix_2bit(levels):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 # (6637, 128): 103 full 64-group batches and a 45-group tail, i.e. three
 # 32-batch super-batches, seven more full batches and a partial one.
-@pytest.mark.parametrize("shape", [(1000, 384), (6637, 128), (77, 1000), (3, 1, 130), (1, 128), (1, 1)])
+# Ragged widths: 1000 (16-byte loads for both dtypes), 1004 (float32 only),
+# 130 (element loads).
+@pytest.mark.parametrize("shape", [(1000, 384), (6637, 128), (77, 1000), (9, 1004), (3, 1, 130), (1, 128),
+                                   (1, 1)])
 def test_bits_dtypes_shapes(bits, dtype, shape, levels):
     rng = np.random.default_rng(zlib.crc32(repr((bits, dtype, shape)).encode()))
     w = (rng.standard_normal(shape) * 0.02).astype(np.float32)
@@ -552,7 +555,7 @@ def _out_host(t):
 
 @pytest.mark.parametrize("bits", ALL_BITS)
 @pytest.mark.parametrize("dtypes", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"), ("f32", "bf16")])
-@pytest.mark.parametrize("shape", [(600, 512), (33, 1000), (2, 3, 130), (1, 1)])
+@pytest.mark.parametrize("shape", [(600, 512), (33, 1000), (5, 1004), (2, 3, 130), (1, 1)])
 def test_fake_quant(bits, dtypes, shape, levels):
     din, dout = dtypes
     w64, w_dev = _w(shape, zlib.crc32(repr(("fq", bits, dtypes, shape)).encode()), din)

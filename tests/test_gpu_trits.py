@@ -94,11 +94,14 @@ def test_trit_equals_field_form_and_repack(lv):
     check_quantize(host(p3), f16_bits(n3), q)
 
 
-def test_trit_many_calls(lv):
+# The ragged tensors of the first set load element by element (widths 300
+# and 1), those of the second in 16-byte pieces (widths 1000 and 200).
+@pytest.mark.parametrize("shapes", [[(64, 128), (5, 300), (1, 1), (300, 512), (0, 128), (2, 3, 256)],
+                                    [(7, 1000), (64, 128), (3, 200)]])
+def test_trit_many_calls(lv, shapes):
     """Mixed shapes through cq_quantize_many / cq_dequantize_many with trit
     storage: identical to the single-tensor calls, blob offsets as laid out."""
-    rng = np.random.default_rng(8)
-    shapes = [(64, 128), (5, 300), (1, 1), (300, 512), (0, 128), (2, 3, 256)]
+    rng = np.random.default_rng(8 + len(shapes))
     ws = [torch.from_numpy((rng.standard_normal(s) * 0.02).astype(np.float32)).to(DEV) for s in shapes]
     say("trit quantize_many")
     blob, views = cq.quantize_many(ws, T, lv)
