@@ -34,7 +34,9 @@ Parity pins: every public function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, textbook values, brute force or hand-worked examples;
 the tolerance helpers ``threshold_distance`` and ``admissible_indices`` by
 hand-worked values on a codebook whose thresholds are exact
-(``tests/test_oracle_band.py``).
+(``tests/test_oracle_band.py``); ``normalised_groups`` by the norm invariant,
+an independent in-lane transform and an exact-cancellation example
+(``tests/test_oracle_transform.py``, ``tests/test_oracle_quantize.py``).
 """
 
 from __future__ import annotations
@@ -170,6 +172,26 @@ def hadamard(g: int) -> np.ndarray:
     return sylvester(g) / math.sqrt(g)
 
 
+def normalised_groups(x: np.ndarray, g: int) -> tuple[np.ndarray, np.ndarray]:
+    """Group norms n and normalised rotated values z = sqrt(g) * y / n of the
+    rows of x, y = x H/sqrt(g) the orthonormal rotation (z = 0 for a zero
+    group).
+
+    Computed from the +-1 product hx = x H: y = hx / sqrt(g), so
+    sqrt(g) * y = hx, ||y||^2 = sum(hx^2) / g and z = hx / n.  The +-1 sums
+    of float32 or bf16 inputs are exact in float64, so a component that
+    cancels exactly is exactly 0 and a tie at a threshold of 0 is decided by
+    the tie rule (multiplying by the rounded entries 1/sqrt(g) first leaves
+    ~1e-17 there, i.e. rounding noise decides); the division by g = 2^k is
+    exact, so a norm that is a float64 number comes out exactly."""
+    hx = np.asarray(x, dtype=np.float64) @ sylvester(g)
+    n = np.sqrt(np.sum(hx * hx, axis=1) / g)
+    z = np.zeros_like(hx)
+    nz = n > 0
+    z[nz] = hx[nz] / n[nz, None]
+    return n, z
+
+
 # ---------------------------------------------------------------------------
 # Quantize / dequantize
 # ---------------------------------------------------------------------------
@@ -224,7 +246,8 @@ def quantize(w: np.ndarray, bits: int, levels: np.ndarray, g: int = GROUP) -> Qu
     Pipeline (steps 1-4) and *Footprint* §Per-Group Storage Breakdown.
 
     1. pad the last axis with zeros to a multiple of g, cut into groups;
-    2. rotate every group by the orthonormal Hadamard matrix (dense product);
+    2. rotate every group by the orthonormal Hadamard matrix (dense product;
+       :func:`normalised_groups` does steps 2 and 3);
     3. take the group's L2 norm n and normalise: z = sqrt(g) * y / n
        (equivalently unit-norm components against levels / sqrt(g),
        *Codebook training* §Production Codebook Generation and Caching);
@@ -241,11 +264,7 @@ def quantize(w: np.ndarray, bits: int, levels: np.ndarray, g: int = GROUP) -> Qu
         raise ValueError("codebook size does not match the bit-width")
     t = thresholds(levels32)
     x, r, d = to_groups(w, g)
-    y = x @ hadamard(g)
-    n = np.sqrt(np.sum(y * y, axis=1))
-    z = np.zeros_like(y)
-    nz = n > 0
-    z[nz] = math.sqrt(g) * y[nz] / n[nz, None]
+    n, z = normalised_groups(x, g)
     idx = np.searchsorted(t, z, side="left").astype(np.int64)
     ng = x.shape[0] // r if r else 0
     shape3 = (r, ng, g)
@@ -456,11 +475,13 @@ def fake_quant(w: np.ndarray, bits: int, levels: np.ndarray, g: int = GROUP,
     t = thresholds(levels32)
     x, r, d = to_groups(w, g)
     h = hadamard(g) if rotate else np.eye(g)
-    y = x @ h
-    n = np.sqrt(np.sum(y * y, axis=1))
-    z = np.zeros_like(y)
-    nz = n > 0
-    z[nz] = math.sqrt(g) * y[nz] / n[nz, None]
+    if rotate:
+        n, z = normalised_groups(x, g)
+    else:
+        n = np.sqrt(np.sum(x * x, axis=1))
+        z = np.zeros_like(x)
+        nz = n > 0
+        z[nz] = math.sqrt(g) * x[nz] / n[nz, None]
     idx = np.searchsorted(t, z, side="left")
     xh = (levels32[idx] * (n[:, None] / math.sqrt(g))) @ h.T
     ng = x.shape[0] // r

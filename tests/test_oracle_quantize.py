@@ -132,6 +132,30 @@ def test_zero_group(oracle_levels):
     assert not O.dequantize(q.packed, q.norm16, 2, 256, 2, levels).any()
 
 
+def test_exact_cancellation_takes_the_tie_rule():
+    """A group whose +-1 transform cancels exactly at some positions: with a
+    codebook symmetric about 0 (Max's 4-level table), those components sit
+    exactly on the middle threshold 0, so z must be exactly 0 there and the
+    index the lower level's (the tie rule), whatever the rounding of
+    1/sqrt(G).  The integer group [5, 5, 1, 9, 0, ...] cancels at 32 of its
+    128 positions (5 + 5 - 1 - 9 = 0 and sign patterns with the same sum)."""
+    table = json.load(open(os.path.join(GOLDEN, "max1960_gaussian.json")))
+    pos = table["quantizers"]["4"]["levels"]
+    levels = np.array([-pos[1], -pos[0], pos[0], pos[1]])
+    x = np.zeros((1, 128))
+    x[0, :4] = [5, 5, 1, 9]
+    hx = x[0] @ O.sylvester(128)  # small integers: exact
+    zero = hx == 0
+    assert zero.sum() == 32
+    q = O.quantize(x, 2, levels)
+    assert np.all(q.z[0, 0][zero] == 0.0)
+    np.testing.assert_array_equal(q.idx[0, 0][zero], 1)
+    # Away from the zeros every component is an integer multiple of
+    # 1/sqrt(128) of size >= 2, far from all thresholds: the plain rule.
+    t = O.thresholds(O.runtime_levels(levels))
+    np.testing.assert_array_equal(q.idx[0, 0][~zero], np.searchsorted(t, q.z[0, 0][~zero], side="left"))
+
+
 def test_leading_dims_flatten(oracle_levels):
     w = np.random.RandomState(11).randn(3, 4, 256)
     a = O.quantize(w, 2, oracle_levels[2])

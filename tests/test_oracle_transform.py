@@ -54,6 +54,29 @@ def test_rotation_preserves_norm():
     np.testing.assert_allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-14)
 
 
+@pytest.mark.parametrize("g", [32, 128, 256])
+def test_normalised_groups(g):
+    """n is the group's L2 norm (the rotation preserves it), z the rotated
+    group (by the independent in-lane transform above) scaled to norm
+    sqrt(g); a zero group gives n = 0 and z = 0; bf16-representable inputs
+    give exactly the integer-scaled sums the butterfly gives."""
+    x = np.random.RandomState(g).randn(40, g) * 0.02
+    x[3] = 0.0
+    n, z = O.normalised_groups(x, g)
+    np.testing.assert_allclose(n, np.linalg.norm(x, axis=1), rtol=1e-14)
+    live = n > 0
+    np.testing.assert_allclose(z[live], (fwht(x)[live] / math.sqrt(g)) * math.sqrt(g) / n[live, None],
+                               rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(np.linalg.norm(z[live], axis=1), math.sqrt(g), rtol=1e-14)
+    assert n[3] == 0 and not z[3].any()
+    # Small integers: the +-1 sums are exact, so z * n equals fwht exactly.
+    xi = np.random.RandomState(7).randint(-20, 21, size=(5, g)).astype(np.float64)
+    ni, zi = O.normalised_groups(xi, g)
+    exact = fwht(xi)
+    np.testing.assert_array_equal(zi == 0, exact == 0)
+    np.testing.assert_allclose(zi * ni[:, None], exact, rtol=1e-15)
+
+
 def test_non_power_of_two_rejected():
     with pytest.raises(ValueError):
         O.sylvester(96)
