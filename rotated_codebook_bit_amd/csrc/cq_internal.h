@@ -26,6 +26,11 @@ struct QuantParams {
   float delta;  // half distance between the outer pair
   float hmid;   // L = 4: middle threshold minus mu; L = 3: delta
   int n_levels;
+  // Symmetric decisions (quantize.hip, shift_in_pair): 1 when the middle
+  // threshold is the centre of the outer pair (three levels always; four
+  // levels when hmid == 0), with neg2_over_delta = -2 / delta.
+  int sym;
+  float neg2_over_delta;
 };
 
 struct LevelTable {

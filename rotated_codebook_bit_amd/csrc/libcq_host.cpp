@@ -170,10 +170,21 @@ int hip_status(hipError_t e, const char* what);
 // cell keeps its level.  Cells are contiguous runs of the sorted array, so a
 // round needs only the L-1 split positions.  Writes the sorted levels as
 // float32.
-void lloyd_max_sorted(const std::vector<double>& x, int L, int iters, float* levels_out) {
+//
+// mirrored: the samples are symmetric about 0 (x[n-1-i] = -x[i]).  The
+// upper half of the levels then starts at the mirror images of the lower
+// half's order statistics (x[n-1-i] rather than the sample at the upper
+// quantile's own index, which is one position off the mirror), so every
+// round keeps the partition symmetric; the result is symmetrised once more
+// to drop differences of summation order.  With the plain start the 2-bit
+// levels settle on an asymmetric fixed point (a few samples just above 0
+// stay in the lower cell; the inner levels then differ by 8.5e-5).
+void lloyd_max_sorted(const std::vector<double>& x, int L, int iters, float* levels_out, bool mirrored) {
   const int64_t n = static_cast<int64_t>(x.size());
   std::vector<double> c(L);
   for (int k = 0; k < L; ++k) c[k] = x[((2 * static_cast<int64_t>(k) + 1) * n) / (2 * L)];
+  if (mirrored)
+    for (int k = L / 2; k < L; ++k) c[k] = x[n - 1 - ((2 * static_cast<int64_t>(L - 1 - k) + 1) * n) / (2 * L)];
   std::vector<int64_t> start(L + 1);
   for (int it = 0; it < iters; ++it) {
     start[0] = 0;
@@ -192,6 +203,14 @@ void lloyd_max_sorted(const std::vector<double>& x, int L, int iters, float* lev
     }
   }
   std::sort(c.begin(), c.end());
+  if (mirrored) {
+    for (int k = 0; k < L / 2; ++k) {
+      const double h = 0.5 * (c[L - 1 - k] - c[k]);
+      c[k] = -h;
+      c[L - 1 - k] = h;
+    }
+    if (L % 2) c[L / 2] = 0.0;
+  }
   for (int k = 0; k < L; ++k) levels_out[k] = static_cast<float>(c[k]);
 }
 
@@ -250,7 +269,7 @@ struct BuiltinTables {
   float lv[5][cq::kMaxLevels];  // index = bits (1..4)
   BuiltinTables() {
     const std::vector<double> x = builtin_samples();
-    for (int bits = 1; bits <= 4; ++bits) lloyd_max_sorted(x, 1 << bits, kBuiltinIters, lv[bits]);
+    for (int bits = 1; bits <= 4; ++bits) lloyd_max_sorted(x, 1 << bits, kBuiltinIters, lv[bits], true);
   }
 };
 
@@ -335,6 +354,11 @@ cq::QuantParams make_quant_params(const float* levels, int n_levels) {
     p.mu = static_cast<float>(mu);
     p.delta = static_cast<float>(d);
     p.hmid = static_cast<float>(t[1] - mu);
+  }
+  if (n_levels == 3 || (n_levels == 4 && p.hmid == 0.0f)) {
+    const float k = static_cast<float>(-2.0 / static_cast<double>(p.delta));
+    p.neg2_over_delta = k;
+    p.sym = std::isfinite(k) ? 1 : 0;
   }
   return p;
 }
@@ -481,7 +505,7 @@ int cq_codebook_train(int bits, const double* samples, int64_t n_samples, int it
     if (!std::isfinite(samples[i])) return fail(CQ_ERR_ARG, "sample %lld is not finite", (long long)i);
   std::vector<double> x(samples, samples + n_samples);
   std::sort(x.begin(), x.end());
-  lloyd_max_sorted(x, L, iters, levels_out);
+  lloyd_max_sorted(x, L, iters, levels_out, false);
   *n_levels = L;
   return CQ_OK;
 }

@@ -93,6 +93,51 @@ __device__ __forceinline__ uint32_t shift_in(uint32_t acc, bool b) {
   return r;
 }
 
+// acc * 2 + [t > v] in two instructions with no mask register: t - v is
+// negative (sign bit set) exactly when v > t, for every non-NaN t and v
+// (a difference of two floats is zero only when they are equal, and
+// rounding or flushing keeps its sign), and v_alignbit_b32 shifts that sign
+// bit in: ({acc, d} >> 31) = (acc << 1) | (d >> 31).  Equal t and v give
+// +0, bit 0, as the compare would.  Used for the two-compare decisions,
+// where the mask form needs a wait state between each carry write and the
+// next compare.  t is a rounded float32 threshold: the subtraction must
+// not be contracted with the product that made t into one fma, which would
+// compare against the unrounded product.
+__device__ __forceinline__ uint32_t shift_in_gt(uint32_t acc, float v, float t) {
+#pragma clang fp contract(off)
+  const float d = t - v;
+  return __builtin_amdgcn_alignbit(acc, __builtin_bit_cast(uint32_t, d), 31);
+}
+
+// Symmetric two-bit decisions (three levels, or four whose middle threshold
+// is the centre of the outer pair: QuantParams::sym).  With the shifted
+// value v and D = delta * ns, one product x = fma(v, k, +0), k = -2 / D,
+// carries both decision bits in its top two bits:
+//   bit 31 (sign)  = [v > 0]: k < 0, and the +0 addend turns the -0 of a
+//                    zero product into +0, so v = +-0 gives 0;
+//   bit 30         = [|x| >= 2] (exponent field >= 128, also for inf), i.e.
+//                    |v| >= D up to the roundings of -2 / delta, of the
+//                    (correctly rounded) division by ns and of the product:
+//                    1.5 float32 ulps of the threshold, against 1 ulp for
+//                    the compare with D = delta * ns.
+// v_alignbit_b32 shifts both in at once: ({acc, x} >> 30) = acc << 2 | x >> 30.
+// A word of 16 such pairs (s, q) becomes the index fields with one or two
+// bitwise steps per word (finish_sym_word).
+__device__ __forceinline__ uint32_t shift_in_pair(uint32_t acc, float v, float k) {
+  const float x = __builtin_fmaf(v, k, 0.0f);
+  return __builtin_amdgcn_alignbit(acc, __builtin_bit_cast(uint32_t, x), 30);
+}
+
+// (s, q) pairs -> index fields.  Four levels: s is the high bit h, and the
+// low bit is NOT (q XOR h).  Three levels: h = s AND q, low bit NOT q.
+template <int L>
+__device__ __forceinline__ uint32_t finish_sym_word(uint32_t acc) {
+  if constexpr (L == 4)
+    return acc ^ (((acc >> 1) & 0x55555555u) ^ 0x55555555u);
+  else
+    return (acc & (acc << 1) & 0xAAAAAAAAu) | (~acc & 0x55555555u);
+}
+
 // Index by binary search over 7 thresholds (8 levels).
 __device__ __forceinline__ uint32_t search8(float v, const float (&T)[kMaxLevels - 1]) {
   const bool b2 = v > T[3];
@@ -143,6 +188,17 @@ __device__ __forceinline__ uint16_t finish_group(float (&y)[kGroup], float S, co
   float ns;
   const float n = forward_group<L>(y, S, p, &ns);
   if constexpr (L == 3 || L == 4) {
+    if (p.sym) {  // the same for the whole launch
+      const float k = p.neg2_over_delta / ns;
+#pragma unroll
+      for (int wd = 0; wd < 8; ++wd) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int pos = 15; pos >= 0; --pos) acc = shift_in_pair(acc, y[16 * wd + pos], k);
+        words[wd] = finish_sym_word<L>(acc);
+      }
+      return __builtin_bit_cast(uint16_t, static_cast<_Float16>(n));
+    }
     const float A = p.hmid * ns, D = p.delta * ns;
 #pragma unroll
     for (int wd = 0; wd < 8; ++wd) {
@@ -150,8 +206,8 @@ __device__ __forceinline__ uint16_t finish_group(float (&y)[kGroup], float S, co
 #pragma unroll
       for (int pos = 15; pos >= 0; --pos) {
         const float v = y[16 * wd + pos];
-        acc = shift_in(acc, v > A);
-        acc = shift_in(acc, __builtin_fabsf(v) > D);
+        acc = shift_in_gt(acc, v, A);
+        acc = shift_in_gt(acc, __builtin_fabsf(v), D);
       }
       if constexpr (L == 4)
         acc ^= ((acc >> 1) & 0x55555555u) ^ 0x55555555u;
@@ -427,12 +483,36 @@ constexpr int floor_blocks_per_cu(bool bf16_in, int w) { return blocks_per_cu(bf
 // Batches per wave of the grid (each wave strides by the grid).  A grid of a
 // few batches per wave measured 4-7% faster on the 7B-shaped model than a
 // resident grid of blocks_per_cu blocks per CU that loops over all batches.
-// With the block sizes above (ms at 1 / 2 / 4 / 8 batches per wave):
-// quantize from bf16 2.76 / 2.72 / 2.70 / 2.74, from float32 4.78 / 4.84 /
-// 4.96 / 5.23; fake quant bf16 -> bf16 4.88 / 4.75 / 4.93 / 5.06.  Smaller
-// tensors get at least the resident grid's waves (spread_blocks).
-constexpr int quant_batches_per_wave(bool bf16_in) { return bf16_in ? 4 : 1; }
+// With the block sizes above (ms at 1 / 2 / 4 / 8 batches per wave), without
+// the XCD block order (xcd_block): quantize from bf16 2.76 / 2.72 / 2.70 /
+// 2.74, from float32 4.78 / 4.84 / 4.96 / 5.23; fake quant bf16 -> bf16
+// 4.88 / 4.75 / 4.93 / 5.06.  With it, quantize from bf16 at 1 / 2 / 3 / 4 /
+// 8 batches per wave took 2.47 / 2.53 / 2.59 / 2.66 / 2.77 ms (one box, one
+// process; 2-wave blocks at one batch per wave 2.49), so bf16 takes a
+// covering grid.  Smaller tensors get at least the resident grid's waves
+// (spread_blocks).
+constexpr int quant_batches_per_wave(bool) { return 1; }
 constexpr int fake_batches_per_wave() { return 2; }
+
+// Blocks of a launch are handed to the 8 XCDs in turn (block b runs on XCD
+// b % 8, each XCD with its own L2).  xcd_block renumbers the blocks of the
+// complete rounds of 8 so that consecutive numbers run on one XCD: XCD x
+// takes numbers x * n8 .. x * n8 + n8 - 1 (n8 = blocks / 8, rounded down);
+// the last blocks keep their numbers.  With it the 8 blocks of a 32-batch
+// super-batch share an L2, and so do the 16 waves that write the pieces of
+// one 128-byte line of norms (8 bytes each, see store_batch): the pieces
+// merge in that L2 instead of reaching HBM as partial lines from up to four
+// L2s.  On the 7B-shaped bf16 model the norm stores alone had cost 4-5% of
+// quantize's time (2.71 -> 2.61 ms without them, a timing-only build); the
+// renumbering took it from 2.73 to 2.66 ms at four batches per wave, and to
+// 2.47 ms with one batch per wave (quant_batches_per_wave).  Storing each
+// slot's four norms as one 8-byte piece (lane 4j after two DPP exchanges)
+// measured 2.52 ms there, so the norms keep their 2-byte stores.
+__device__ __forceinline__ int xcd_block(int b, int n) {
+  const int full = n & ~7;
+  if (b >= full) return b;
+  return (b & 7) * (full >> 3) + (b >> 3);
+}
 
 template <int L, bool BF16, bool MANY, bool TRITS = false>
 __global__ void __launch_bounds__(quant_waves(BF16) * kWave, blocks_per_cu(BF16))
@@ -451,7 +531,7 @@ quantize_contig(QuantJob job, QuantParams p) {
   uint8_t* const buf = lds + wave * WAVE_BYTES;
   const int64_t n_batches = job.n_batches;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * waves;
-  int64_t batch = static_cast<int64_t>(blockIdx.x) * waves + wave;
+  int64_t batch = static_cast<int64_t>(xcd_block(blockIdx.x, gridDim.x)) * waves + wave;
   if (batch >= n_batches) return;
   int d = 0;
 
@@ -549,6 +629,17 @@ template <int L>
 __device__ __forceinline__ void decide_quarter(const float (&y)[kQuadElems], float ns, const QuantParams& p,
                                                uint32_t (&words)[Shape<L>::sbits]) {
   if constexpr (L == 3 || L == 4) {
+    if (p.sym) {
+      const float k = p.neg2_over_delta / ns;
+#pragma unroll
+      for (int wd = 0; wd < 2; ++wd) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int pos = 15; pos >= 0; --pos) acc = shift_in_pair(acc, y[16 * wd + pos], k);
+        words[wd] = finish_sym_word<L>(acc);
+      }
+      return;
+    }
     const float A = p.hmid * ns, D = p.delta * ns;
 #pragma unroll
     for (int wd = 0; wd < 2; ++wd) {
@@ -556,8 +647,8 @@ __device__ __forceinline__ void decide_quarter(const float (&y)[kQuadElems], flo
 #pragma unroll
       for (int pos = 15; pos >= 0; --pos) {
         const float v = y[16 * wd + pos];
-        acc = shift_in(acc, v > A);
-        acc = shift_in(acc, __builtin_fabsf(v) > D);
+        acc = shift_in_gt(acc, v, A);
+        acc = shift_in_gt(acc, __builtin_fabsf(v), D);
       }
       if constexpr (L == 4)
         acc ^= ((acc >> 1) & 0x55555555u) ^ 0x55555555u;

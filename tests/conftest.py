@@ -32,3 +32,16 @@ def levels32(oracle_levels):
     both sides (GPU and oracle get bit-identical levels)."""
     from oracle import cq_oracle as O
     return {b: O.runtime_levels(v).astype(np.float32) for b, v in oracle_levels.items()}
+
+
+@pytest.fixture(scope="session")
+def sym_levels32(levels32):
+    """The oracle's 2-bit float32 codebook made exactly antisymmetric
+    (l[3-k] = -l[k], each pair's magnitude the mean of the oracle's two):
+    its middle threshold is the centre of the outer pair, the case in which
+    libcq's quantize kernels take their one-product decisions."""
+    lv = levels32[2].astype(np.float64)
+    h = np.array([(lv[3] - lv[0]) / 2, (lv[2] - lv[1]) / 2]).astype(np.float32)
+    out = np.array([-h[0], -h[1], h[1], h[0]], dtype=np.float32)
+    assert np.all(out == -out[::-1]) and np.all(np.diff(out) > 0)
+    return out

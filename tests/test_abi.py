@@ -87,6 +87,25 @@ def test_builtin_codebook_two_bit_levels_and_ternary():
     np.testing.assert_array_equal(cq.codebook(O.TERNARY), np.float32(O.TERNARY_LEVELS))
 
 
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_builtin_codebook_is_antisymmetric(bits):
+    """The built-in generator's samples come in +- pairs, so the Lloyd-Max
+    fixed point it reaches is symmetric about 0: level L-1-k is exactly
+    -level k in float32 (then the middle threshold of the four-level code is
+    0, the centre of the outer pair)."""
+    lv = cq.codebook(bits)
+    np.testing.assert_array_equal(lv, -lv[::-1])
+
+
+def test_codebook_train_keeps_the_plain_recipe(lloyd_samples):
+    """Caller samples get the page's recipe as it stands (plain quantile
+    start, no symmetrisation; equal to the oracle's levels, see
+    test_codebook_train_equals_oracle_float32): the pages' draws are not
+    symmetric, nor are their levels."""
+    trained = cq.codebook_train(2, lloyd_samples)
+    assert not np.array_equal(trained, -trained[::-1])
+
+
 def test_builtin_codebook_is_cached_and_independent_of_the_pages_draws(lloyd_samples):
     a = [cq.codebook(b) for b in (1, 2, 3, 4)]
     b = [cq.codebook(b) for b in (1, 2, 3, 4)]

@@ -128,12 +128,16 @@ def test_quantize_many_batch_tails(bits, levels):
     check_count(mism, elems)
 
 
-@pytest.mark.parametrize("bits", ALL_BITS)
-def test_many_small_mixed(bits, levels):
+@pytest.mark.parametrize("bits", ALL_BITS + ["sym2"])
+def test_many_small_mixed(bits, levels, sym_levels32):
     """Many small tensors of mixed shapes (multiples of 128 and ragged,
     empty, 3-D) in one call, bf16: bit-identical to the single-tensor calls,
-    and the oracle's rules on every tensor."""
-    lv = levels[bits]
+    and the oracle's rules on every tensor.  "sym2": 2 bits with an
+    antisymmetric codebook."""
+    if bits == "sym2":
+        bits, lv = 2, sym_levels32
+    else:
+        lv = levels[bits]
     rng = np.random.default_rng(zlib.crc32(repr(("many", bits)).encode()))
     shapes = []
     for _ in range(150):
@@ -184,13 +188,17 @@ def test_many_small_mixed(bits, levels):
 RAGGED_SETS = [[(7, 1000), (3, 200), (11, 1016)], [(5, 1004), (3, 1000), (2, 12)], [(4, 130), (6, 1000), (1, 1)]]
 
 
-@pytest.mark.parametrize("bits", ALL_BITS)
+@pytest.mark.parametrize("bits", ALL_BITS + ["sym2"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("which", range(len(RAGGED_SETS)))
-def test_many_ragged_widths(bits, dtype, which, levels):
+def test_many_ragged_widths(bits, dtype, which, levels, sym_levels32):
     """Only ragged tensors in one call: bit-identical to the single-tensor
-    calls (each picks its own load form), and the oracle's rules."""
-    lv = levels[bits]
+    calls (each picks its own load form), and the oracle's rules.  "sym2":
+    2 bits with an antisymmetric codebook."""
+    if bits == "sym2":
+        bits, lv = 2, sym_levels32
+    else:
+        lv = levels[bits]
     shapes = RAGGED_SETS[which]
     rng = np.random.default_rng(zlib.crc32(repr(("ragged", bits, dtype, which)).encode()))
     hosts = [(rng.standard_normal(s) * 0.02).astype(np.float32) for s in shapes]

@@ -117,19 +117,40 @@ def test_bits_dtypes_shapes(bits, dtype, shape, levels):
         run_case(f"{dtype}{shape}", w.astype(np.float64), to_dev_f32(w), bits, levels[bits])
 
 
-def test_special_groups(levels):
+def test_special_groups(levels, sym_levels32):
     """Zero groups, constant groups, power-of-two scaled copies, huge values
-    whose norm overflows binary16 (stored as +Inf)."""
+    whose norm overflows binary16 (stored as +Inf); contiguous and ragged
+    (a 130-column copy, whose second groups are 2-element pads).  The 2-bit
+    case also runs with an antisymmetric codebook (one-product decisions),
+    where zero and constant groups give exact zeros at the middle threshold."""
     rng = np.random.default_rng(5)
     base = rng.standard_normal((1, 128))
     w = np.concatenate([np.zeros((1, 128)), np.full((1, 128), 0.25), base, base * 2.0 ** 10,
                         np.full((1, 128), -3.0), np.full((1, 128), 1e5)], axis=0).astype(np.float32)
-    for bits in ALL_BITS:
-        say(f"special groups bits={bits}")
-        q = O.quantize(w.astype(np.float64), bits, levels[bits])
-        packed, norms = gpu_quantize(to_dev_f32(w), bits, levels[bits])
-        check_quantize(packed, norms, q)
-        assert norms[-1, 0] == 0x7C00 and norms[0, 0] == 0
+    w_r = np.concatenate([w, w[:, :2]], axis=1)
+    cases = [(b, levels[b]) for b in ALL_BITS] + [(2, sym_levels32)]
+    for bits, lv in cases:
+        for arr in (w, w_r):
+            say(f"special groups bits={bits} shape={arr.shape} levels={lv}")
+            q = O.quantize(arr.astype(np.float64), bits, lv)
+            packed, norms = gpu_quantize(to_dev_f32(arr), bits, lv)
+            check_quantize(packed, norms, q)
+            assert norms[-1, 0] == 0x7C00 and norms[0, 0] == 0
+
+
+# The antisymmetric 2-bit codebook: contiguous rows (several batches and a
+# tail), ragged rows in both load forms, the 1x1 case.
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(1000, 384), (6637, 128), (77, 1000), (9, 1004), (3, 1, 130), (1, 1)])
+def test_symmetric_codebook(dtype, shape, sym_levels32):
+    rng = np.random.default_rng(zlib.crc32(repr(("sym", dtype, shape)).encode()))
+    w = (rng.standard_normal(shape) * 0.02).astype(np.float32)
+    if dtype == "bf16":
+        b = W.f32_to_bf16_bits(w)
+        run_case(f"sym {dtype}{shape}", W.bf16_bits_to_f32(b).astype(np.float64), to_dev_bf16(b), 2,
+                 sym_levels32)
+    else:
+        run_case(f"sym {dtype}{shape}", w.astype(np.float64), to_dev_f32(w), 2, sym_levels32)
 
 
 def test_empty_inputs(levels):
