@@ -26,6 +26,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        python bench.py --copy-only   (plain 4 GiB device copy, for calibrating the byte counters)
        python bench.py --configs     (the small configurations: one JSON report line)
        python bench.py --trace-summary DIR   (per-kernel, per-grid table of a rocprofv3 kernel trace)
+       python bench.py --traffic-summary DIR (profiles/traffic_llama7b.{json,md} from FETCH_SIZE /
+                                              WRITE_SIZE runs under DIR/{fetch,write,copy_fetch,copy_write})
 
 --configs times, per configuration, single calls with HIP events (3 warm-up
 calls, median of 15), warm (inputs cache-resident after the previous call)
@@ -98,6 +100,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-only", action="store_true", help="only run a plain 4 GiB device copy")
     ap.add_argument("--configs", action="store_true", help="report the small configurations instead")
+    ap.add_argument("--traffic-summary", metavar="DIR",
+                    help="write profiles/traffic_llama7b.{json,md} from rocprofv3 counter runs under DIR")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="print a per-kernel, per-grid table of a rocprofv3 kernel trace directory and exit")
     return ap.parse_args()
@@ -307,6 +311,92 @@ def trace_summary(path: str) -> None:
               f"{statistics.mean(ds):.2f} | {min(ds):.2f} | {sum(ds):.1f} |")
 
 
+# Kernels of the traffic profile: phase -> kernel name (the largest dispatch
+# of that name is the whole-model launch).
+TRAFFIC_KERNELS = {"quantize": "cq::kq::quantize_contig<4, true, false, false>",
+                   "dequantize_f32": "cq::kd::dequantize_contig<2, false, false, false>",
+                   "matvec_pass_b1": "cq::km::matvec_pair_kernel<",
+                   "fake_quant_bf16_extra": "cq::kq::fakequant_contig<4, true, true>"}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 4 << 30  # copy_only: 4 GiB read and 4 GiB written
+
+
+def traffic_summary(path: str) -> None:
+    """Writes profiles/traffic_llama7b.{json,md} from four rocprofv3 --pmc
+    runs under `path` (CSV output): fetch/ and write/ (FETCH_SIZE or
+    WRITE_SIZE of `bench.py --steps 1 --warmup 0 --no-cpu`), copy_fetch/ and
+    copy_write/ (the same counters of `bench.py --copy-only`).  Each counter
+    is scaled by what it reports for the copy, whose bytes are known."""
+    import csv
+    import glob
+    from rotated_codebook_bit_amd import workloads as W
+
+    def largest(sub, counter, name_prefix):
+        best = None
+        for f in glob.glob(os.path.join(path, sub, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
+                    if r["Counter_Name"] != counter or not (name.startswith(name_prefix)
+                                                           or name.startswith("void " + name_prefix)):
+                        continue
+                    key = (int(r["Grid_Size"]), float(r["Counter_Value"]))
+                    if best is None or key > best:
+                        best = key
+        if best is None:
+            raise SystemExit(f"no {counter} dispatch of {name_prefix} under {path}/{sub}")
+        return best[1] * 1024.0  # KiB -> bytes
+
+    fs = COPY_BYTES / largest("copy_fetch", "FETCH_SIZE", COPY_KERNEL)
+    ws = COPY_BYTES / largest("copy_write", "WRITE_SIZE", COPY_KERNEL)
+    shapes = W.llama7b_shapes()
+    params = sum(r * c for r, c in shapes)
+    ng = params // G
+    alg = {"quantize": params * 2 + ng * (G * BITS // 8) + ng * 2,
+           "dequantize_f32": ng * (G * BITS // 8) + ng * 2 + params * 4,
+           "matvec_pass_b1": ng * (G * BITS // 8 + 2) + sum(c * 4 + r * 4 for r, c in shapes),
+           "fake_quant_bf16_extra": params * 4}
+    kernels = {}
+    for phase, kname in TRAFFIC_KERNELS.items():
+        fb = round(largest("fetch", "FETCH_SIZE", kname) * fs)
+        wb = round(largest("write", "WRITE_SIZE", kname) * ws)
+        kernels[phase] = {"kernel": kname.replace("cq::", "").rstrip("<"), "fetch_bytes": fb, "write_bytes": wb,
+                          "hbm_bytes_per_launch": fb + wb, "algorithmic_bytes": alg[phase],
+                          "source": PHASE_SOURCE[phase], "source_digest": file_digest(PHASE_SOURCE[phase])}
+    cmd = "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc {c} --output-format csv -d $R/{d} -o run -- python3 $R/bench.py {a}"
+    out = {"what": ("HBM bytes per launch on the 7B-shaped model (bf16, 2-bit, G=128), from rocprofv3 FETCH_SIZE "
+                    "and WRITE_SIZE (KiB per dispatch, the largest dispatch of each kernel), each scaled by what the "
+                    f"same counter reports for a plain 4 GiB device copy ({COPY_KERNEL}): scale {fs:.3f} for "
+                    f"FETCH_SIZE, {ws:.3f} for WRITE_SIZE."),
+           "commands": [cmd.format(c="FETCH_SIZE", d=f"{path}/fetch", a="--steps 1 --warmup 0 --no-cpu"),
+                        cmd.format(c="WRITE_SIZE", d=f"{path}/write", a="--steps 1 --warmup 0 --no-cpu"),
+                        cmd.format(c="FETCH_SIZE", d=f"{path}/copy_fetch", a="--copy-only"),
+                        cmd.format(c="WRITE_SIZE", d=f"{path}/copy_write", a="--copy-only"),
+                        f"python3 bench.py --traffic-summary {path}"],
+           "kernels": kernels,
+           "note": ("each entry holds the digest of its kernel's source file as measured; bench.py reports an "
+                    "entry only while that file is unchanged")}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    lines = ["# HBM traffic per launch: 7B-shaped model (bf16, 2-bit, G=128)", "",
+             "Counters: rocprofv3 `FETCH_SIZE` and `WRITE_SIZE` (KiB per dispatch), one pass each, "
+             "`python3 bench.py --steps 1 --warmup 0 --no-cpu`; per kernel the largest dispatch (the whole-model "
+             "launch); the commands are in `traffic_llama7b.json`, which `python3 bench.py --traffic-summary DIR` "
+             "writes together with this file.",
+             f"Calibration: a plain 4 GiB device copy (`bench.py --copy-only`, kernel `{COPY_KERNEL}`); scale "
+             f"{fs:.3f} for `FETCH_SIZE`, {ws:.3f} for `WRITE_SIZE`.", "",
+             "| kernel | read (scaled) | written (scaled) | total | algorithmic | ratio |", "|---|---|---|---|---|---|"]
+    for phase, k in kernels.items():
+        lines.append(f"| {k['kernel']} | {k['fetch_bytes'] / 1e9:.3f} GB | {k['write_bytes'] / 1e9:.3f} GB | "
+                     f"{k['hbm_bytes_per_launch'] / 1e9:.3f} GB | {k['algorithmic_bytes'] / 1e9:.3f} GB | "
+                     f"{k['hbm_bytes_per_launch'] / k['algorithmic_bytes']:.4f} |")
+    lines += ["", "Each kernel's source digest at measurement is in `traffic_llama7b.json`."]
+    with open(TRAFFIC_FILE.replace(".json", ".md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(open(TRAFFIC_FILE.replace(".json", ".md")).read())
+
+
 def cpu_baseline_configs() -> dict:
     """The oracle on C1, C2, C3 (each width) and C5 in full: quantize +
     dequantize (C5: dequantize + the float64 product), params/s."""
@@ -394,6 +484,9 @@ def main():
     args = parse()
     if args.trace_summary:
         trace_summary(args.trace_summary)
+        return
+    if args.traffic_summary:
+        traffic_summary(args.traffic_summary)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus "

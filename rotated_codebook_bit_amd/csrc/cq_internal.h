@@ -144,6 +144,18 @@ __device__ __forceinline__ void hold_values(const T&... v) {
   (hold_value(v), ...);
 }
 
+// Blocks of a launch are handed to the 8 XCDs in turn (block b runs on XCD
+// b % 8, each XCD with its own L2).  xcd_block renumbers the blocks of the
+// complete rounds of 8 so that consecutive numbers run on one XCD: XCD x
+// takes numbers x * n8 .. x * n8 + n8 - 1 (n8 = blocks / 8, rounded down);
+// the last blocks keep their numbers.  A kernel that hands out work by this
+// number keeps neighbouring work units in one L2.
+__device__ __forceinline__ int xcd_block(int b, int n) {
+  const int full = n & ~7;
+  if (b >= full) return b;
+  return (b & 7) * (full >> 3) + (b >> 3);
+}
+
 // ---- Ragged rows: one group over a quad of lanes ---------------------------------
 //
 // Where a row's length is not a multiple of 128, groups start anywhere and

@@ -429,6 +429,17 @@ __device__ __forceinline__ void store_batch(uint8_t* __restrict__ packed, uint16
 // vmcnt(0)) right before the next LDS reads; deferring the stores by one
 // iteration means that wait finds only long-finished stores in flight.
 //
+// Work is handed out by xcd_block's number: the 8 blocks of a 32-batch
+// super-batch then share an L2, and so do the 16 waves that write the
+// pieces of one 128-byte line of norms (8 bytes each, see store_batch): the
+// pieces merge in that L2 instead of reaching HBM as partial lines from up
+// to four L2s.  On the 7B-shaped bf16 model the norm stores alone had cost
+// 4-5% of quantize's time (2.71 -> 2.61 ms without them, a timing-only
+// build); the renumbering took it from 2.73 to 2.66 ms at four batches per
+// wave, and to 2.47 ms with one batch per wave (quant_batches_per_wave).
+// Storing each slot's four norms as one 8-byte piece (lane 4j after two DPP
+// exchanges) measured 2.52 ms there, so the norms keep their 2-byte stores.
+//
 // One launch covers either one tensor (MANY = false: job.w, job.packed,
 // job.norms, job.n_groups) or a table of tensors whose column counts are
 // multiples of 128 (MANY = true: job.t, with the batches of each tensor
@@ -492,27 +503,14 @@ constexpr int floor_blocks_per_cu(bool bf16_in, int w) { return blocks_per_cu(bf
 // covering grid.  Smaller tensors get at least the resident grid's waves
 // (spread_blocks).
 constexpr int quant_batches_per_wave(bool) { return 1; }
+// The multi-tensor launch resolves each batch's tensor by a binary search
+// that starts from the wave's previous tensor, so a wave's later batches
+// find theirs in a step or two.  The 7B-shaped model as 225 tensors in one
+// call (ms per call at 1 / 2 / 4 batches per wave, one box): 2.66 / 2.53 /
+// 2.63-2.65.  The XCD block order did not move dequantize or fake quant
+// beyond the run-to-run spread (about 1%), so they keep plain numbering.
+constexpr int kManyBatchesPerWave = 2;
 constexpr int fake_batches_per_wave() { return 2; }
-
-// Blocks of a launch are handed to the 8 XCDs in turn (block b runs on XCD
-// b % 8, each XCD with its own L2).  xcd_block renumbers the blocks of the
-// complete rounds of 8 so that consecutive numbers run on one XCD: XCD x
-// takes numbers x * n8 .. x * n8 + n8 - 1 (n8 = blocks / 8, rounded down);
-// the last blocks keep their numbers.  With it the 8 blocks of a 32-batch
-// super-batch share an L2, and so do the 16 waves that write the pieces of
-// one 128-byte line of norms (8 bytes each, see store_batch): the pieces
-// merge in that L2 instead of reaching HBM as partial lines from up to four
-// L2s.  On the 7B-shaped bf16 model the norm stores alone had cost 4-5% of
-// quantize's time (2.71 -> 2.61 ms without them, a timing-only build); the
-// renumbering took it from 2.73 to 2.66 ms at four batches per wave, and to
-// 2.47 ms with one batch per wave (quant_batches_per_wave).  Storing each
-// slot's four norms as one 8-byte piece (lane 4j after two DPP exchanges)
-// measured 2.52 ms there, so the norms keep their 2-byte stores.
-__device__ __forceinline__ int xcd_block(int b, int n) {
-  const int full = n & ~7;
-  if (b >= full) return b;
-  return (b & 7) * (full >> 3) + (b >> 3);
-}
 
 template <int L, bool BF16, bool MANY, bool TRITS = false>
 __global__ void __launch_bounds__(quant_waves(BF16) * kWave, blocks_per_cu(BF16))
@@ -1132,9 +1130,9 @@ hipError_t launch_fq_types(const void* w, bool bf16_in, int64_t rows, int64_t co
 // quant_waves waves; a call with fewer than that many batches per CU takes
 // smaller blocks, one batch per wave, so its batches spread over more CUs.
 template <bool BF16>
-ContigGrid quant_grid(int64_t n_batches) {
+ContigGrid quant_grid(int64_t n_batches, int per_wave = quant_batches_per_wave(BF16)) {
   constexpr int W = quant_waves(BF16);
-  return contig_grid(n_batches, W, quant_batches_per_wave(BF16), floor_blocks_per_cu(BF16, W));
+  return contig_grid(n_batches, W, per_wave, floor_blocks_per_cu(BF16, W));
 }
 
 template <int L, bool BF16, bool TRITS>
@@ -1168,7 +1166,7 @@ hipError_t launch_many_l(const QuantParams& p, TensorTable<QuantDesc> contig, in
                          TensorTable<QuantDesc> ragged, int64_t ragged_groups, int64_t ragged_cols_gcd,
                          hipStream_t s) {
   if (contig_batches > 0) {
-    const ContigGrid g = quant_grid<BF16>(contig_batches);
+    const ContigGrid g = quant_grid<BF16>(contig_batches, kManyBatchesPerWave);
     const QuantJob job{nullptr, nullptr, nullptr, 0, contig, contig_batches};
     hipLaunchKernelGGL((quantize_contig<L, BF16, true, TRITS>), dim3(g.blocks), dim3(g.waves * kWave), 0, s, job,
                        p);
