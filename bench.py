@@ -26,6 +26,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        python bench.py --copy-only   (plain 4 GiB device copy, for calibrating the byte counters)
        python bench.py --configs     (the small configurations: one JSON report line)
        python bench.py --trace-summary DIR   (per-kernel, per-grid table of a rocprofv3 kernel trace)
+       python bench.py --counter-summary DIR (per-kernel table of a rocprofv3 --pmc run of COUNTERS)
        python bench.py --traffic-summary DIR (profiles/traffic_llama7b.{json,md} from FETCH_SIZE /
                                               WRITE_SIZE runs under DIR/{fetch,write,copy_fetch,copy_write})
 
@@ -100,6 +101,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-only", action="store_true", help="only run a plain 4 GiB device copy")
     ap.add_argument("--configs", action="store_true", help="report the small configurations instead")
+    ap.add_argument("--counter-summary", metavar="DIR",
+                    help="per-kernel SQ counter table of a rocprofv3 --pmc run (the counters of COUNTERS)")
     ap.add_argument("--traffic-summary", metavar="DIR",
                     help="write profiles/traffic_llama7b.{json,md} from rocprofv3 counter runs under DIR")
     ap.add_argument("--trace-summary", metavar="DIR",
@@ -397,6 +400,54 @@ def traffic_summary(path: str) -> None:
     print(open(TRAFFIC_FILE.replace(".json", ".md")).read())
 
 
+COUNTERS = ["GRBM_GUI_ACTIVE", "SQ_WAVES", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_BUSY_CU_CYCLES",
+            "SQ_INSTS_LDS", "SQ_ACTIVE_INST_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_VALU_MFMA_BUSY_CYCLES"]
+
+
+def counter_summary(path: str) -> None:
+    """Per (kernel, grid) medians of the SQ counters of one rocprofv3 --pmc
+    run under `path` (CSV output; the counters of COUNTERS), library kernels
+    only, as a markdown table.  Units as this GPU reports them:
+    GRBM_GUI_ACTIVE is GPU cycles summed over the 8 XCDs; SQ_BUSY_CU_CYCLES,
+    SQ_ACTIVE_INST_VALU and SQ_ACTIVE_INST_LDS are quad-cycles summed over the
+    SIMDs; SQ_LDS_BANK_CONFLICT and SQ_VALU_MFMA_BUSY_CYCLES are cycles summed
+    over the SIMDs.  Derived columns: clock = GRBM_GUI_ACTIVE / 8 / the
+    dispatch's duration (its timestamps in the same run); VALU busy =
+    SQ_ACTIVE_INST_VALU / SQ_BUSY_CU_CYCLES (above 1 where two waves issue a
+    VALU instruction each in one quad-cycle); LDS conflict =
+    SQ_LDS_BANK_CONFLICT / (4 SQ_ACTIVE_INST_LDS), the share of LDS-active
+    cycles lost to bank conflicts; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /
+    (4 SQ_BUSY_CU_CYCLES)."""
+    import csv
+    import glob
+    import statistics
+    vals = {}
+    for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
+                if "cq::" not in name:
+                    continue
+                key = (name.replace("void ", ""), r["Grid_Size"])
+                d = vals.setdefault(key, {}).setdefault(r["Dispatch_Id"], {})
+                d[r["Counter_Name"]] = float(r["Counter_Value"])
+                d["ns"] = float(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    print("| kernel | grid | dispatches | " + " | ".join(c for c in COUNTERS) +
+          " | us | clock GHz | VALU busy | LDS conflict | MFMA busy |")
+    print("|---|---|---|" + "---|" * (len(COUNTERS) + 5))
+    order = sorted(vals.items(), key=lambda kv: -statistics.median(
+        d.get("GRBM_GUI_ACTIVE", 0.0) for d in kv[1].values()))
+    for (name, grid), disp in order:
+        med = {c: statistics.median(d.get(c, 0.0) for d in disp.values()) for c in COUNTERS + ["ns"]}
+        busy = med["SQ_BUSY_CU_CYCLES"]
+        valu = med["SQ_ACTIVE_INST_VALU"] / busy if busy else 0.0
+        lds = med["SQ_LDS_BANK_CONFLICT"] / (4 * med["SQ_ACTIVE_INST_LDS"]) if med["SQ_ACTIVE_INST_LDS"] else 0.0
+        mfma = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (4 * busy) if busy else 0.0
+        clock = med["GRBM_GUI_ACTIVE"] / 8 / med["ns"] if med["ns"] else 0.0
+        print(f"| `{name}` | {grid} | {len(disp)} | " + " | ".join(f"{med[c]:.4g}" for c in COUNTERS) +
+              f" | {med['ns'] / 1e3:.1f} | {clock:.2f} | {valu:.3f} | {lds:.3f} | {mfma:.3f} |")
+
+
 def cpu_baseline_configs() -> dict:
     """The oracle on C1, C2, C3 (each width) and C5 in full: quantize +
     dequantize (C5: dequantize + the float64 product), params/s."""
@@ -487,6 +538,9 @@ def main():
         return
     if args.traffic_summary:
         traffic_summary(args.traffic_summary)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus "
