@@ -24,6 +24,7 @@ through the same three steps).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        python bench.py --copy-only   (plain 4 GiB device copy, for calibrating the byte counters)
+       python bench.py --hbm-probe   (torch's read / write / copy kernels on 4 GiB: what this HBM delivers)
        python bench.py --configs     (the small configurations: one JSON report line)
        python bench.py --trace-summary DIR   (per-kernel, per-grid table of a rocprofv3 kernel trace)
        python bench.py --counter-summary DIR (per-kernel table of a rocprofv3 --pmc run of COUNTERS)
@@ -100,6 +101,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-only", action="store_true", help="only run a plain 4 GiB device copy")
+    ap.add_argument("--hbm-probe", action="store_true",
+                    help="time torch's read, write and copy kernels on 4 GiB buffers (one JSON line)")
     ap.add_argument("--configs", action="store_true", help="report the small configurations instead")
     ap.add_argument("--counter-summary", metavar="DIR",
                     help="per-kernel SQ counter table of a rocprofv3 --pmc run (the counters of COUNTERS)")
@@ -125,6 +128,36 @@ def copy_only(torch):
     ms = e0.elapsed_time(e1)
     print(json.dumps({"copy_bytes_each_way": 4 * n, "ms": ms,
                       "GBps_read_plus_write": 2 * 4 * n / ms / 1e6}), flush=True)
+
+
+def hbm_probe(torch):
+    """What this HBM delivers to plain torch kernels on 4 GiB buffers: a read
+    (sum of a float32 vector), a write (fill_) and a copy, each the median of
+    10 timed calls after 3 untimed ones (HIP events on the current stream)."""
+    n = 1 << 30  # 4 GiB of float32
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    acc = torch.empty((), dtype=torch.float32, device="cuda")
+    ops = {"read": (lambda: torch.sum(a, dim=0, out=acc), 4 * n),
+           "write": (lambda: b.fill_(1.0), 4 * n),
+           "copy": (lambda: b.copy_(a), 8 * n)}
+    res = {}
+    for name, (fn, nbytes) in ops.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = float(np.median(ts))
+        res[name] = {"bytes": nbytes, "ms": round(ms, 4), "TBps": round(nbytes / ms / 1e9, 3),
+                     "frac_of_8TBps": round(nbytes / ms / 1e9 / 8.0, 4)}
+    print(json.dumps({"hbm_probe": res, "device": torch.cuda.get_device_name(0)}), flush=True)
 
 
 # fp32 FMA rate without packed instructions (which this build does not use):
@@ -550,6 +583,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.hbm_probe:
+        hbm_probe(torch)
+        return
     if args.copy_only:
         copy_only(torch)
         return
