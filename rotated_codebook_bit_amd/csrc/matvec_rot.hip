@@ -609,7 +609,7 @@ hipError_t launch_rot_nb(const MatvecArgs& a, const LevelTable& lv, int log2g, i
                          hipStream_t s) {
   // Rows per group (RB * NB <= 32 partial sums in registers) and units of
   // codes in flight (at most 32 dwords of codes per thread).
-  constexpr int RB = NB <= 2 ? 8 : 4;
+  constexpr int RB = NB <= 2 ? 8 : NB <= 4 ? 4 : 2;
   constexpr int PF = 2;
   // Row groups per block: the rotation of the block's activations is paid
   // once per block, so blocks are as large as filling the chip allows
@@ -640,8 +640,13 @@ hipError_t launch_rot_nb(const MatvecArgs& a, const LevelTable& lv, int log2g, i
 template <int SB>
 hipError_t launch_rot_sb(const MatvecArgs& a, const LevelTable& lv, int log2g, int blocks_per_cu,
                          hipStream_t s) {
-  // Batch chunks of at most 4 rows (grid.y): a chunk's activations (16 x 4
-  // floats per thread) leave room for two waves per SIMD.
+  // Batch chunks (grid.y) of 8 rows (16 x 8 activations per thread, 214
+  // VGPRs) or of at most 4.
+  // From 16 rows, chunks of 8: the codes are decoded and the activations
+  // rotated once per 8 rows (11008x4096 at batch 16: 63 us against 68 in
+  // chunks of 4).  At batch 8 one chunk halves the blocks of this
+  // latency-bound launch (40.5 us against 37.0), so it keeps two of 4.
+  if (a.batch >= 16) return launch_rot_nb<SB, 8>(a, lv, log2g, blocks_per_cu, s);
   switch (a.batch >= 4 ? 4 : a.batch) {
     case 1: return launch_rot_nb<SB, 1>(a, lv, log2g, blocks_per_cu, s);
     case 2: return launch_rot_nb<SB, 2>(a, lv, log2g, blocks_per_cu, s);

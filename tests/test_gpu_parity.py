@@ -429,6 +429,42 @@ def test_matvec_many(batch, levels):
             check_matvec(y, x.astype(np.float64) @ w_hat.T, x, w_hat)
 
 
+@pytest.mark.parametrize("batch", [1, 3])
+def test_matvec_many_repeated_calls(batch, levels):
+    """Calls over the same matrices and buffers reuse the device copy of the
+    descriptor table: a repeated call, also after the activations changed in
+    place, gives exactly what a call whose table differs (the matrices in
+    reverse order, which changes no matrix's arithmetic) gives, and both
+    follow the oracle."""
+    lv = levels[2]
+    shapes = [(100, 512), (37, 11008), (64, 128), (300, 384)]
+    rng = np.random.default_rng(70 + batch)
+    items, refs = [], []
+    for n_out, k in shapes:
+        w = rng.standard_normal((n_out, k)) * 0.02
+        q = O.quantize(w, 2, lv)
+        p_dev = torch.from_numpy(q.packed.reshape(n_out, -1)).to(DEV)
+        n_dev = torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16)
+        x = torch.zeros((batch, k), dtype=torch.float32, device=DEV)
+        y = torch.full((batch, n_out), float("nan"), dtype=torch.float32, device=DEV)
+        items.append((p_dev, n_dev, n_out, k, x, y))
+        refs.append(O.dequantize(q.packed, q.norm16, n_out, k, 2, lv))
+    rev = list(reversed(items))
+    for step in range(3):
+        xs = [rng.standard_normal((batch, k)).astype(np.float32) for _, k in shapes]
+        for it, xh in zip(items, xs):
+            it[4].copy_(torch.from_numpy(xh))
+        say(f"matvec_many repeated calls batch={batch} step={step}")
+        cq.dequant_matvec_many(items, 2, lv, batch)  # the same table as the previous step's last call
+        cq.dequant_matvec_many(items, 2, lv, batch)
+        first = [host(it[5]).copy() for it in items]
+        cq.dequant_matvec_many(rev, 2, lv, batch)  # another table: uploaded again
+        for it, y0, xh, w_hat in zip(items, first, xs, refs):
+            y1 = host(it[5])
+            assert np.array_equal(y0, y1)
+            check_matvec(y1, xh.astype(np.float64) @ w_hat.T, xh, w_hat)
+
+
 @pytest.mark.parametrize("bits,batch", [(2, 10), (2, 8), (2, 3), (3, 5), (4, 8), (O.TERNARY, 2), (4, 12)])
 def test_matvec_row_groups(bits, batch, levels):
     """Calls with enough rows that the byte-table kernel gives each block
@@ -520,8 +556,11 @@ def test_matvec_pair_rows_large_call(batch, rows, n_mat, levels):
     (2, 32800, 128, 1),      # 8-row waves
     (2, 33, 8320, 3),        # three 4096-column passes, rotated per unit
     (2, 130, 4096, 17),      # batch chunks of 8, 8 and a partial one of 1
+    (2, 300, 4096, 8),       # batch 8: two chunks of 4
     (4, 129, 640, 9),
     (3, 65, 4096, 6),
+    (3, 65, 4096, 16),       # 3-bit codes, two chunks of 8 batch rows
+    (4, 129, 640, 20),       # 4-bit codes, chunks of 8, 8 and a partial one of 4
     (O.TERNARY, 500, 1024, 4),
 ])
 def test_matvec_single_call(bits, n_out, k, batch, levels):
