@@ -551,11 +551,13 @@ struct MatvecArgs {
 
 // Which kernel runs a single-matrix product: the pair-table kernel with
 // pair_rows_per_block rows per block (1 .. 64; 2-bit fields only, one batch
-// row per grid row), or (0) the per-lane-table kernel aiming at
-// blocks_per_cu blocks per compute unit.
+// row per grid row), the matrix-core kernel with mfma_rows_per_block rows
+// per block (1 .. 48; chunks of 4 or 8 batch rows), or (both 0) the
+// per-lane-table kernel aiming at blocks_per_cu blocks per compute unit.
 struct MatvecOnePlan {
   int pair_rows_per_block;
   int blocks_per_cu;
+  int mfma_rows_per_block;
 };
 
 MatvecOnePlan matvec_one_plan(int sbits, int64_t n_out, int64_t k, int64_t batch);

@@ -12,7 +12,7 @@
 // it consumes itself (no rotated copy in device memory, no second launch),
 // and the matrix descriptor is a kernel argument.
 //
-// Two kernels:
+// Three kernels:
 //   - matvec_pair_rot_kernel: 2-bit fields, one batch row per grid row
 //     (blockIdx.y).  Per 1024-column tile the block builds, for every column
 //     pair, the 16 partial products a 4-bit code pair can select; every row
@@ -26,8 +26,15 @@
 //     thread, the remaining stages across lanes), decodes the codes through
 //     a per-lane copy of a small level table (so the data-dependent lookups
 //     never collide on LDS banks) and reduces each group of rows over the
-//     block in a fixed order.
-// Both are deterministic: every sum runs in a fixed order.
+//     block in a fixed order.  It serves rows whose length is not a multiple
+//     of 64 columns.
+//   - matvec_mfma_kernel: any field width, 2 or more batch rows in chunks of
+//     4 or 8.  The block rotates its chunk of activations into LDS; the
+//     products run on the matrix cores (v_mfma_f32_4x4x1_16b_f32: the batch
+//     rows of a chunk against one decoded weight per lane), so a weight costs
+//     one table read and a quarter of a byte permute however many batch rows
+//     share it.
+// All are deterministic: every sum runs in a fixed order.
 
 #include <type_traits>
 
@@ -86,10 +93,11 @@ constexpr int kTableFloats = 32 * 16 * kWave;
 
 // A block owns rows_per_block consecutive rows of the matrix (about an equal
 // share for every compute unit); wave w takes rows w, w + 8, w + 16, ... of
-// them, at most MAXR.  Per 4096-column pass: the pass's activations and the
-// codes and norms of all the wave's rows are loaded at once; the block
-// rotates the activations into LDS and builds the pass's pair tables; then
-// every wave runs through its rows without further barriers.
+// them, at most MAXR.  Per 4096-column pass: the block loads the pass's
+// activations and rotates them into LDS; the codes and norms of all the
+// wave's rows are then requested at once, and the block builds the pass's
+// pair tables while they arrive; then every wave runs through its rows
+// without further barriers.
 template <int MAXR, bool TWO_NORMS>
 __global__ void __launch_bounds__(kPairBlock, 1)
 matvec_pair_rot_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_block) {
@@ -138,9 +146,8 @@ matvec_pair_rot_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_bloc
   const float sgn16 = (lane >> 4) & 1 ? -1.0f : 1.0f;
 
   for (int64_t p0 = 0; p0 < k; p0 += kPassCols) {
-    // 1. Loads, all in flight together: the pass's activations (thread t
-    //    takes columns 8 t .. 8 t + 7, at addresses clamped into the row),
-    //    then each row's 16 bytes of codes and its norm(s) for this lane.
+    // 1. The pass's activations: thread t takes columns 8 t .. 8 t + 7, at
+    //    addresses clamped into the row.
     const int64_t my_c = p0 + 8 * static_cast<int64_t>(threadIdx.x);
     const bool my_live = my_c < k;  // whole 8-value runs: k % 64 == 0
     float xv[8];
@@ -157,15 +164,6 @@ matvec_pair_rot_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_bloc
     const int noff = active ? static_cast<int>(2 * (c0 >> log2g)) : (1 << 30);
     uint32_t codes[MAXR][4];
     uint32_t nrm[MAXR];  // binary16 norm(s): low half, and the high half for group size 32
-#pragma unroll
-    for (int r = 0; r < MAXR; ++r) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(codes_src, coff, soff_c[r], 2);  // nt: read once
-      codes[r][0] = v[0]; codes[r][1] = v[1]; codes[r][2] = v[2]; codes[r][3] = v[3];
-      if constexpr (TWO_NORMS)
-        nrm[r] = __builtin_amdgcn_raw_buffer_load_b32(norms_src, noff, soff_n[r], 0);
-      else
-        nrm[r] = __builtin_amdgcn_raw_buffer_load_b16(norms_src, noff, soff_n[r], 0);
-    }
     __syncthreads();  // the previous pass's tables and activations are no longer read
     // 2. Rotate: butterfly stages 1, 2, 4 inside the thread, lane strides
     //    1, 2, 4, 8 (element strides 8 .. 64) inside DPP rows, lane stride
@@ -207,6 +205,19 @@ matvec_pair_rot_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_bloc
       for (int e = 0; e < 8; ++e) hold_values(xv[e]);
     }
     __syncthreads();
+    // The codes and norms of the wave's rows are requested only now: issued
+    // together with the activations, the whole grid's code stream delayed
+    // the activations that every block waits for first (11008x4096: 8.04 ->
+    // 7.80 us; 4096x11008, three passes: 13.44 -> 12.20 us).
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(codes_src, coff, soff_c[r], 2);  // nt: read once
+      codes[r][0] = v[0]; codes[r][1] = v[1]; codes[r][2] = v[2]; codes[r][3] = v[3];
+      if constexpr (TWO_NORMS)
+        nrm[r] = __builtin_amdgcn_raw_buffer_load_b32(norms_src, noff, soff_n[r], 0);
+      else
+        nrm[r] = __builtin_amdgcn_raw_buffer_load_b16(norms_src, noff, soff_n[r], 0);
+    }
     // 3. Pair tables: thread (w, lane) builds pairs 4 w .. 4 w + 3 of the
     //    lane's 64 columns (columns 64 lane + 8 w .. 64 lane + 8 w + 7).
     if (active) {
@@ -576,6 +587,368 @@ matvec_rot_kernel(MatvecArgs a, LevelTable lv, int log2g, int rg) {
   }
 }
 
+// ---- matrix cores, up to 8 batch rows per block ---------------------------------
+
+typedef float mf_v4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMfWaves = 8;
+constexpr int kMfBlock = kMfWaves * kWave;     // 512 threads, one block per compute unit
+constexpr int kMfPass = 4096;                  // columns of rotated activations in LDS
+constexpr int kMfSlices = 4;                   // column slices of a pass
+constexpr int kMfSlice = kMfPass / kMfSlices;  // 1024 columns: 64 for each group of 4 lanes
+constexpr int kMfSubsets = kMfWaves / kMfSlices;  // row subsets: waves per slice
+constexpr int kMfMaxQuads = 6;                 // row quads per wave
+constexpr int kMfMaxRows = kMfSubsets * kMfMaxQuads * 4;  // 48 rows per block
+// Row quads per wave of a kernel instance: 3- and 4-bit codes of 8 batch
+// rows take 4 (32 rows per block), which keeps them within 256 registers.
+__host__ __device__ constexpr int mf_quads(int sb, int nh) { return nh == 2 && sb != 2 ? 4 : kMfMaxQuads; }
+
+// Activations of the pass in LDS: float4 f of batch row r at float4
+// r * kMfRowF4 + f + f / 16 (one float4 of padding per 16, rows 1090 float4
+// apart, 2 mod 8).  In every group of eight lanes the product's 16-byte
+// reads (lanes 4 b + q: row q (+4), float4 16 b + c) and the coalesced
+// writes (consecutive float4s) fall on eight different 16-byte bank slots,
+// as do the rotation's own-run reads and writes with 16 float4 per thread
+// (8 float4 per thread: two lanes per slot); and every address is a
+// per-lane base plus a constant offset.
+constexpr int kMfRowF4 = 1090;
+__device__ __forceinline__ int mf_pad(int f) { return f + (f >> 4); }
+
+// Sum of a value over the four lanes l, l +- 4, l +- 8 of a 16-lane DPP row
+// that share l % 4: two row rotations (DPP row_ror 4 and 8), no LDS.
+__device__ __forceinline__ float mf_row_sum4(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+  return v;
+}
+
+// Codes of the lane's 64 columns of a slice (SB bits each, 8 SB bytes).
+template <int SB>
+struct MfCodes {
+  uint32_t d[2 * SB];
+  // Codes of columns 16 c .. 16 c + 15 of the 64, column 16 c + e at bits [SB e, SB e + SB).
+  __device__ __forceinline__ uint64_t chunk(int c) const {
+    if constexpr (SB == 2) {
+      return d[c];
+    } else if constexpr (SB == 4) {
+      return static_cast<uint64_t>(d[2 * c]) | (static_cast<uint64_t>(d[2 * c + 1]) << 32);
+    } else {
+      const uint64_t w0 = static_cast<uint64_t>(d[0]) | (static_cast<uint64_t>(d[1]) << 32);
+      const uint64_t w1 = static_cast<uint64_t>(d[2]) | (static_cast<uint64_t>(d[3]) << 32);
+      const uint64_t w2 = static_cast<uint64_t>(d[4]) | (static_cast<uint64_t>(d[5]) << 32);
+      return c == 0 ? w0 : c == 1 ? (w0 >> 48) | (w1 << 16) : c == 2 ? (w1 >> 32) | (w2 << 32) : w2 >> 16;
+    }
+  }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t src, int voff) {
+    if constexpr (SB == 2) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(src, voff, 0, 2);  // nt: read once
+      d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
+    } else if constexpr (SB == 4) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(src, voff, 0, 2);
+      const auto u = __builtin_amdgcn_raw_buffer_load_b128(src, voff + 16, 0, 2);
+      d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
+      d[4] = u[0]; d[5] = u[1]; d[6] = u[2]; d[7] = u[3];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(src, voff + 8 * i, 0, 2);
+        d[2 * i] = v[0]; d[2 * i + 1] = v[1];
+      }
+    }
+  }
+};
+
+// One block per compute unit owns rows_per_block consecutive rows of the
+// matrix (at most 48) and a chunk of 4 NH batch rows (blockIdx.y).  Per
+// 4096-column pass the block rotates the pass's activations of its batch
+// rows into LDS (the threads of a batch row own V consecutive columns: the
+// butterfly inside the thread, the remaining stages across lanes by DPP).
+// Wave w takes column slice w % 4 of the pass and the row quads w / 4,
+// w / 4 + 2, ..., w / 4 + 10 of the block.
+//
+// The products run on v_mfma_f32_4x4x1_16b_f32: 16 blocks of a 4x4 outer
+// product per instruction.  Lane l = 4 b + q feeds block b the activation of
+// batch row q (+4 h) and the scaled level norm * levels[code] of weight row
+// q of the quad, both at column 64 b + 16 c + j of the slice in step
+// (c, j); the block's accumulator, held by lanes 4 b .. 4 b + 3, sums
+// x[batch i] * w[row q] over block b's columns.  The 16 blocks' sums are
+// added over the lanes at the end and the four slices in LDS, in a fixed
+// order.  Lane l's 64 columns are one 8 SB-byte load of codes per row and
+// lie in one or two groups, whose norms scale the decoded levels (one
+// multiply per weight, shared by all batch rows).
+template <int SB, int NH>
+__global__ void __launch_bounds__(kMfBlock, 1)
+matvec_mfma_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_block) {
+  constexpr int NB = 4 * NH;                  // batch rows per block
+  constexpr int TPR = kMfBlock / NB;          // rotation threads per batch row
+  constexpr int V = kMfPass / TPR;            // columns per rotation thread: 32 or 64
+  constexpr int MQ = mf_quads(SB, NH);        // row quads per wave
+  static_assert(MQ % 2 == 0, "quads run in pairs");
+  using LT = LaneTab<SB>;
+  // One LDS array: the level table first, at address 0, so that its reads
+  // take their offsets as immediates; then the activations.
+  constexpr int kTabF = (LT::floats + 3) / 4 * 4;
+  __shared__ __attribute__((aligned(16))) float lds[kTabF + NB * kMfRowF4 * 4];
+  float* const tab = lds;
+  float* const xs = lds + kTabF;
+  if (threadIdx.x < kRotBlock) LT::fill(tab, lv, threadIdx.x);
+
+  const int t = threadIdx.x, lane = t % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(t / kWave);
+  const int slice = w % kMfSlices, rsub = w / kMfSlices;
+  const int bq = lane >> 2, q = lane & 3;
+  const int64_t k = a.k, n_out = a.n_out;
+  const int64_t b0 = static_cast<int64_t>(blockIdx.y) * NB;
+  const int64_t row_base = static_cast<int64_t>(blockIdx.x) * rows_per_block;
+  const int block_rows = static_cast<int>(n_out - row_base < rows_per_block ? n_out - row_base : rows_per_block);
+  const int n_quads = (block_rows + 3) / 4;
+  const int nq = n_quads > rsub ? (n_quads - rsub + kMfSubsets - 1) / kMfSubsets : 0;  // this wave's quads
+  const int64_t row_bytes = k * SB / 8, ngr = k >> log2g;
+  const int G = 1 << log2g;
+  const char* tb = reinterpret_cast<const char*>(tab);
+  const uint32_t lane_bytes = 4u * static_cast<uint32_t>(lane);
+  // The block's rows as one buffer resource; lanes past the block's last row
+  // re-read it (never stored).  The host sends a matrix here only when
+  // k <= 2^26, so 48 rows of codes stay under 2^31 bytes.
+  const auto codes_src = rsrc(a.packed + row_base * row_bytes, block_rows * row_bytes);
+  const auto norms_src = rsrc(a.norms + row_base * ngr, block_rows * ngr * 2);
+  int roff_c[MQ], roff_n[MQ];
+#pragma unroll
+  for (int i = 0; i < MQ; ++i) {
+    int r = 4 * (rsub + kMfSubsets * i) + q;
+    r = r < block_rows ? r : block_rows - 1;
+    roff_c[i] = static_cast<int>(r * row_bytes);
+    roff_n[i] = static_cast<int>(r * ngr * 2);
+  }
+  // Rotation thread: batch row rr, columns V cb .. V cb + V - 1 of the pass.
+  const int rr = t / TPR, cb = t % TPR;
+  const bool row_live = b0 + rr < a.batch;
+  const float* __restrict__ xrow = a.x + (b0 + rr) * k;  // dereferenced only when row_live
+
+  mf_v4 acc[MQ][NH];
+#pragma unroll
+  for (int i = 0; i < MQ; ++i)
+#pragma unroll
+    for (int h = 0; h < NH; ++h) acc[i][h] = mf_v4{0.0f, 0.0f, 0.0f, 0.0f};
+  // Rows of one pass with groups of 64 or more columns: a lane's 64 columns
+  // share one norm, so the levels go in unscaled and each accumulator is
+  // scaled once at the end by its lane's norm (lane l's accumulator only
+  // sums products with lane l's weights).  Otherwise every level is scaled
+  // by its norm before its products.
+  const bool late = k <= kMfPass && G >= 64;
+  float lnorm[MQ];
+#pragma unroll
+  for (int i = 0; i < MQ; ++i) lnorm[i] = 0.0f;
+
+  for (int64_t p0 = 0; p0 < k; p0 += kMfPass) {
+    // 1. The pass's activations, coalesced: thread (rr, cb) loads float4s
+    //    cb + TPR s (s < V / 4) of batch row rr, zeros past k or past the
+    //    batch (such a float4 is read at the start of x instead).
+    uint4 raw[V / 4];
+#pragma unroll
+    for (int i = 0; i < V / 4; ++i) {
+      const int64_t c = p0 + 4 * static_cast<int64_t>(cb + TPR * i);
+      const bool live = row_live && c < k;  // k % 4 == 0
+      const uint4 v = *reinterpret_cast<const uint4*>(live ? xrow + c : a.x);
+      raw[i] = live ? v : make_uint4(0u, 0u, 0u, 0u);
+    }
+    // 2. Codes and norms of the wave's quads for its slice of the pass:
+    //    lane 4 b + q takes columns 64 b .. 64 b + 63 of the slice of row
+    //    4 quad + q.  Lanes whose columns lie past k get norm 0 (their
+    //    activations are 0 too), so nothing they read contributes.
+    const int64_t c0 = p0 + static_cast<int64_t>(slice) * kMfSlice + 64 * bq;
+    const bool slice_live = p0 + static_cast<int64_t>(slice) * kMfSlice < k;  // the same for the wave
+    MfCodes<SB> codes[MQ] = {};
+    uint32_t nrm[MQ][2] = {};
+    {
+      const int cvo = static_cast<int>(c0 * SB / 8);
+      const int g0 = static_cast<int>(c0 >> log2g);
+#pragma unroll
+      for (int i = 0; i < MQ; ++i) {
+        if (slice_live && i < nq) {
+          codes[i].load(codes_src, roff_c[i] + cvo);
+          nrm[i][0] = __builtin_amdgcn_raw_buffer_load_b16(norms_src, roff_n[i] + 2 * g0, 0, 0);
+          nrm[i][1] = G == 32 ? __builtin_amdgcn_raw_buffer_load_b16(norms_src, roff_n[i] + 2 * g0 + 2, 0, 0) : 0u;
+        }
+      }
+    }
+    __syncthreads();  // the previous pass's activations are no longer read
+    // 3. Through LDS to the rotation's layout: thread (rr, cb) reads back
+    //    columns V cb .. V cb + V - 1 (both steps conflict-free: mf_slot),
+    //    then rotates them and writes them to the very slots it read.
+    {
+      float* dst = xs + rr * kMfRowF4 * 4;
+#pragma unroll
+      for (int i = 0; i < V / 4; ++i) *reinterpret_cast<uint4*>(dst + 4 * mf_pad(cb + TPR * i)) = raw[i];
+      hold_until_lds_written(raw);
+    }
+    __syncthreads();
+    float xv[V];
+    {
+      const float* src = xs + rr * kMfRowF4 * 4;
+#pragma unroll
+      for (int i = 0; i < V / 4; ++i) {
+        const float4 v = *reinterpret_cast<const float4*>(src + 4 * mf_pad((V / 4) * cb + i));
+        xv[4 * i] = v.x; xv[4 * i + 1] = v.y; xv[4 * i + 2] = v.z; xv[4 * i + 3] = v.w;
+      }
+    }
+    //    Butterfly stages of element stride 1 .. min(V, G)/2 inside the
+    //    thread, then strides V .. G/2 across lanes (lane strides 1 .. 8).
+#pragma unroll
+    for (int hh = 1; hh < V; hh <<= 1) {
+      if (hh < G) {
+#pragma unroll
+        for (int i = 0; i < V; i += 2 * hh)
+#pragma unroll
+          for (int j = i; j < i + hh; ++j) {
+            const float u = xv[j], v = xv[j + hh];
+            xv[j] = u + v;
+            xv[j + hh] = u - v;
+          }
+      }
+    }
+    if (V < G) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) xv[e] = dpp_stage<1>(xv[e], lane & 1);
+    }
+    if (2 * V < G) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) xv[e] = dpp_stage<2>(xv[e], lane & 2);
+    }
+    if (4 * V < G) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) xv[e] = dpp_stage<4>(xv[e], lane & 4);
+    }
+    if (8 * V < G) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) xv[e] = dpp_stage<8>(xv[e], lane & 8);
+    }
+    {
+      float* dst = xs + rr * kMfRowF4 * 4;
+      uint4 ch[V / 4];
+#pragma unroll
+      for (int i = 0; i < V / 4; ++i) {
+        ch[i] = make_uint4(__builtin_bit_cast(uint32_t, xv[4 * i]), __builtin_bit_cast(uint32_t, xv[4 * i + 1]),
+                           __builtin_bit_cast(uint32_t, xv[4 * i + 2]), __builtin_bit_cast(uint32_t, xv[4 * i + 3]));
+        *reinterpret_cast<uint4*>(dst + 4 * mf_pad((V / 4) * cb + i)) = ch[i];
+      }
+      hold_until_lds_written(ch);  // the stored chunks keep their registers until the LDS has them
+    }
+    __syncthreads();
+    // 4. Products: per 16-column chunk c of the lane's 64 columns, the
+    //    chunk's activations (one 64-byte run per batch row half), then for
+    //    every quad the 16 scaled levels and 16 NH matrix-core steps.
+    if (slice_live) {
+      float nscale[MQ][2];
+#pragma unroll
+      for (int i = 0; i < MQ; ++i) {
+        const bool in0 = c0 < k, in1 = c0 + 32 < k;
+        const float n0 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(nrm[i][0])));
+        const float n1 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(nrm[i][1])));
+        nscale[i][0] = in0 ? n0 : 0.0f;
+        nscale[i][1] = G == 32 ? (in1 ? n1 : 0.0f) : nscale[i][0];
+        lnorm[i] = nscale[i][0];
+      }
+      // Float4 16 b + 4 c + u of the slice sits at mf_pad(...) = 17 (f0 / 16) + 4 c + u.
+      const float* xbase = xs + q * kMfRowF4 * 4 + 4 * mf_pad((slice * kMfSlice) / 4 + 16 * bq);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float xa[NH][16];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          const float* src = xbase + 4 * h * kMfRowF4 * 4;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float4 v = *reinterpret_cast<const float4*>(src + 4 * (4 * c + u));
+            xa[h][4 * u] = v.x; xa[h][4 * u + 1] = v.y; xa[h][4 * u + 2] = v.z; xa[h][4 * u + 3] = v.w;
+          }
+        }
+        // Quads in pairs: both quads' level reads are in flight together and
+        // the steps alternate over 2 NH accumulators.  A wave with an odd
+        // number of quads runs its last pair's second quad with norm 0 into
+        // rows past the block (never stored).
+#pragma unroll
+        for (int i = 0; i < MQ; i += 2) {
+          if (i < nq) {  // the same for the whole wave
+            float lev0[16], lev1[16];
+            LT::decode(codes[i].chunk(c), tb, lane_bytes, lev0);
+            LT::decode(codes[i + 1].chunk(c), tb, lane_bytes, lev1);
+            if (late) {
+#pragma unroll
+              for (int j = 0; j < 16; ++j)
+#pragma unroll
+                for (int h = 0; h < NH; ++h) {
+                  acc[i][h] = __builtin_amdgcn_mfma_f32_4x4x1f32(xa[h][j], lev0[j], acc[i][h], 0, 0, 0);
+                  acc[i + 1][h] = __builtin_amdgcn_mfma_f32_4x4x1f32(xa[h][j], lev1[j], acc[i + 1][h], 0, 0, 0);
+                }
+            } else {
+              const float s0 = nscale[i][c >> 1], s1 = nscale[i + 1][c >> 1];
+#pragma unroll
+              for (int j = 0; j < 16; ++j) {
+                const float w0 = lev0[j] * s0, w1 = lev1[j] * s1;
+#pragma unroll
+                for (int h = 0; h < NH; ++h) {
+                  acc[i][h] = __builtin_amdgcn_mfma_f32_4x4x1f32(xa[h][j], w0, acc[i][h], 0, 0, 0);
+                  acc[i + 1][h] = __builtin_amdgcn_mfma_f32_4x4x1f32(xa[h][j], w1, acc[i + 1][h], 0, 0, 0);
+                }
+              }
+            }
+          }
+          // One pair at a time: otherwise the compiler hoists every quad's
+          // table reads to the top and needs a register per level read.
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  }
+
+  // 5. Sums: the four lanes of a 16-lane row that hold one (row, batch)
+  //    value add up by DPP; lanes 16 j + q (j = 0-3) then leave their
+  //    row's sum in LDS as partial 4 slice + j of that output, and one
+  //    thread per output adds its 16 partials in order.  The activations'
+  //    LDS is free once every wave is past its last products.
+  __syncthreads();
+  float* dump = xs;  // [kMfMaxRows][16][NB]
+#pragma unroll
+  for (int i = 0; i < MQ; ++i)
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float v = late ? acc[i][h][m] * lnorm[i] : acc[i][h][m];
+        acc[i][h][m] = mf_row_sum4(v);
+      }
+  if ((lane & 12) == 0) {
+    const int part = 4 * slice + (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < MQ; ++i) {
+      const int r = 4 * (rsub + kMfSubsets * i) + q;  // < 48
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+        *reinterpret_cast<float4*>(dump + (r * 16 + part) * NB + 4 * h) =
+            make_float4(acc[i][h][0], acc[i][h][1], acc[i][h][2], acc[i][h][3]);
+    }
+    wait_lds_writes();  // the stored sums keep their registers until the LDS has them
+#pragma unroll
+    for (int i = 0; i < MQ; ++i)
+#pragma unroll
+      for (int h = 0; h < NH; ++h) hold_values(acc[i][h][0], acc[i][h][1], acc[i][h][2], acc[i][h][3]);
+  }
+  __syncthreads();
+  const float inv_g = 1.0f / static_cast<float>(G);  // exact: a power of two
+  for (int o = t; o < block_rows * NB; o += kMfBlock) {
+    const int r = o / NB, m = o % NB;
+    if (b0 + m < a.batch) {
+      const float* src = dump + r * 16 * NB + m;
+      float sum = src[0];
+#pragma unroll
+      for (int p = 1; p < 16; ++p) sum += src[p * NB];
+      a.y[(b0 + m) * n_out + row_base + r] = sum * inv_g;
+    }
+  }
+}
+
+
 // ---- launchers ------------------------------------------------------------------
 
 // Largest grid.y of one launch.
@@ -598,6 +971,32 @@ hipError_t launch_pair_rot(const MatvecArgs& a, const LevelTable& lv, int log2g,
     else
       hipLaunchKernelGGL((matvec_pair_rot_kernel<kPairMaxRows, false>), dim3(static_cast<unsigned>(blocks),
                          static_cast<unsigned>(part.batch)), dim3(kPairBlock), 0, s, part, lv, log2g, rows_per_block);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_mfma_rot(const MatvecArgs& a, const LevelTable& lv, int sbits, int log2g, int rows_per_block,
+                           hipStream_t s) {
+  const int64_t blocks = (a.n_out + rows_per_block - 1) / rows_per_block;
+  const int nh = a.batch > 4 ? 2 : 1;
+  const int64_t nb = 4 * nh;
+  // Batch chunks of 4 NH rows along grid.y, at most kMaxGridY per launch.
+  for (int64_t c0 = 0; c0 * nb < a.batch; c0 += kMaxGridY) {
+    MatvecArgs part = a;
+    part.x = a.x + c0 * nb * a.k;
+    part.y = a.y + c0 * nb * a.n_out;
+    part.batch = a.batch - c0 * nb;
+    const int64_t chunks = (part.batch + nb - 1) / nb;
+    const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(chunks < kMaxGridY ? chunks : kMaxGridY));
+#define CQ_MF(SB, NH) hipLaunchKernelGGL((matvec_mfma_kernel<SB, NH>), grid, dim3(kMfBlock), 0, s, part, lv, log2g, rows_per_block)
+    if (nh == 2) {
+      if (sbits == 2) CQ_MF(2, 2); else if (sbits == 3) CQ_MF(3, 2); else CQ_MF(4, 2);
+    } else {
+      if (sbits == 2) CQ_MF(2, 1); else if (sbits == 3) CQ_MF(3, 1); else CQ_MF(4, 1);
+    }
+#undef CQ_MF
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -671,9 +1070,19 @@ MatvecOnePlan matvec_one_plan(int sbits, int64_t n_out, int64_t k, int64_t batch
     int64_t rpb = (n_out + cus - 1) / cus;
     const int64_t cap = static_cast<int64_t>(kr::kPairWaves) * kr::kPairMaxRows;
     rpb = rpb < 1 ? 1 : rpb > cap ? cap : rpb;
-    return MatvecOnePlan{static_cast<int>(rpb), 0};
+    return MatvecOnePlan{static_cast<int>(rpb), 0, 0};
   }
-  return MatvecOnePlan{0, 2};
+  // Two or more batch rows take the matrix-core kernel: one block of up to
+  // 48 rows per compute unit.  Rows of a multiple of 64 columns keep every
+  // lane's 64-column run inside the row and its code loads aligned.
+  if (batch >= 2 && k <= kPairMaxK && k % 64 == 0) {
+    const int64_t cus = device_cu_count();
+    int64_t rpb = (n_out + cus - 1) / cus;
+    const int64_t cap = static_cast<int64_t>(kr::kMfSubsets) * 4 * kr::mf_quads(sbits, batch > 4 ? 2 : 1);
+    rpb = rpb < 1 ? 1 : rpb > cap ? cap : rpb;
+    return MatvecOnePlan{0, 0, static_cast<int>(rpb)};
+  }
+  return MatvecOnePlan{0, 2, 0};
 }
 
 hipError_t launch_matvec_one(const MatvecArgs& a, int sbits, const LevelTable& lv, int group_size,
@@ -681,6 +1090,12 @@ hipError_t launch_matvec_one(const MatvecArgs& a, int sbits, const LevelTable& l
   if (a.n_out <= 0 || a.batch <= 0) return hipSuccess;
   const int log2g = kr::log2_group(group_size);
   if ((1 << log2g) != group_size) return hipErrorInvalidValue;
+  if (plan.mfma_rows_per_block) {
+    if (a.k > kPairMaxK || a.k % 64 || sbits < 2 || sbits > 4 ||
+        plan.mfma_rows_per_block > kr::kMfSubsets * 4 * kr::mf_quads(sbits, a.batch > 4 ? 2 : 1))
+      return hipErrorInvalidValue;
+    return kr::launch_mfma_rot(a, lv, sbits, log2g, plan.mfma_rows_per_block, stream);
+  }
   if (plan.pair_rows_per_block) {
     if (sbits != 2 || a.k > kPairMaxK || a.k % 64 || plan.pair_rows_per_block > kr::kPairWaves * kr::kPairMaxRows)
       return hipErrorInvalidValue;

@@ -148,9 +148,10 @@ def test_zz_mismatch_total():
 @pytest.mark.parametrize("batch", [1, 3])
 def test_group_size_matvec(g, bits, batch, levels):
     """cq_dequant_matvec at other group sizes against the oracle's x @ W_hat^T
-    (batch 1 of 2-bit fields takes the pair-table kernel, the rest the
-    per-lane-table kernel; both rotate the activations over G / 2 or G / 16
-    lanes), including k not a multiple of the 1024-column tile."""
+    (batch 1 of 2-bit fields takes the pair-table kernel, batch 3 the
+    matrix-core kernel with 4 batch rows per block; both rotate the
+    activations partly across lanes), including k not a multiple of the
+    1024-column tile."""
     from parity import check_matvec
     lv = levels[bits]
     rng = np.random.default_rng(zlib.crc32(repr(("mv", g, bits, batch)).encode()))
@@ -159,6 +160,45 @@ def test_group_size_matvec(g, bits, batch, levels):
     w_hat = O.dequantize(q.packed, q.norm16, n_out, k, bits, lv, g)
     x = rng.standard_normal((batch, k)).astype(np.float32)
     say(f"G={g} matvec bits={bits} batch={batch}")
+    y = cq.dequant_matvec(torch.from_numpy(q.packed.reshape(n_out, -1)).to(DEV),
+                          torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16),
+                          n_out, k, bits, lv, torch.from_numpy(x).to(DEV), group_size=g)
+    check_matvec(host(y), x.astype(np.float64) @ w_hat.T, x, w_hat)
+
+
+@pytest.mark.parametrize("bits", ALL_BITS)
+@pytest.mark.parametrize("batch", [1, 3, 12])
+def test_group32_odd_width_matvec(bits, batch, levels):
+    """Rows of an odd number of 32-column groups (k = 32 mod 64) take the
+    per-lane-table kernel at every batch."""
+    from parity import check_matvec
+    lv = levels[bits]
+    rng = np.random.default_rng(zlib.crc32(repr(("mv32", bits, batch)).encode()))
+    n_out, k = 200, 1504
+    q = O.quantize(rng.standard_normal((n_out, k)) * 0.02, bits, lv, 32)
+    w_hat = O.dequantize(q.packed, q.norm16, n_out, k, bits, lv, 32)
+    x = rng.standard_normal((batch, k)).astype(np.float32)
+    say(f"G=32 odd-width matvec bits={bits} batch={batch}")
+    y = cq.dequant_matvec(torch.from_numpy(q.packed.reshape(n_out, -1)).to(DEV),
+                          torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16),
+                          n_out, k, bits, lv, torch.from_numpy(x).to(DEV), group_size=32)
+    check_matvec(host(y), x.astype(np.float64) @ w_hat.T, x, w_hat)
+
+
+@pytest.mark.parametrize("g", [32, 64, 256])
+@pytest.mark.parametrize("bits", ALL_BITS)
+def test_group_size_matvec_two_passes(g, bits, levels):
+    """The matrix-core kernel with 8 batch rows per block (batch 6: two rows
+    past the batch) on rows of two 4096-column passes, where every level is
+    scaled by its norm before its products."""
+    from parity import check_matvec
+    lv = levels[bits]
+    rng = np.random.default_rng(zlib.crc32(repr(("mv2", g, bits)).encode()))
+    n_out, k, batch = 100, 4352, 6
+    q = O.quantize(rng.standard_normal((n_out, k)) * 0.02, bits, lv, g)
+    w_hat = O.dequantize(q.packed, q.norm16, n_out, k, bits, lv, g)
+    x = rng.standard_normal((batch, k)).astype(np.float32)
+    say(f"G={g} two-pass matvec bits={bits} batch={batch}")
     y = cq.dequant_matvec(torch.from_numpy(q.packed.reshape(n_out, -1)).to(DEV),
                           torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16),
                           n_out, k, bits, lv, torch.from_numpy(x).to(DEV), group_size=g)

@@ -554,9 +554,10 @@ def test_matvec_pair_rows_large_call(batch, rows, n_mat, levels):
     (2, 2049, 384, 1),       # a partial block of rows; 2-row waves
     (2, 20000, 256, 1),      # 4-row waves
     (2, 32800, 128, 1),      # 8-row waves
-    (2, 33, 8320, 3),        # three 4096-column passes, rotated per unit
+    (2, 33, 8320, 3),        # three 4096-column passes: levels scaled per element
     (2, 130, 4096, 17),      # batch chunks of 8, 8 and a partial one of 1
-    (2, 300, 4096, 8),       # batch 8: two chunks of 4
+    (2, 300, 4096, 8),       # batch 8: one chunk of 8, norms applied after the products
+    (2, 2750, 4096, 5),      # 11 rows per block: odd quad counts, three rows past the batch
     (4, 129, 640, 9),
     (3, 65, 4096, 6),
     (3, 65, 4096, 16),       # 3-bit codes, two chunks of 8 batch rows
@@ -567,7 +568,8 @@ def test_matvec_single_call(bits, n_out, k, batch, levels):
     """cq_dequant_matvec runs as one launch that rotates the activations in
     each block: partial tiles and passes, several windows of rotated
     activations, every rows-per-wave choice of the batch-1 pair-table kernel,
-    batches split into chunks of eight rows with a partial last chunk."""
+    and for two or more batch rows the matrix-core kernel's chunks of 4 or 8
+    rows with a partial last chunk."""
     lv = levels[bits]
     rng = np.random.default_rng(zlib.crc32(repr(("single", bits, n_out, k, batch)).encode()))
     w = rng.standard_normal((n_out, k)) * 0.02
