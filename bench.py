@@ -25,6 +25,8 @@ through the same three steps).
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        python bench.py --copy-only   (plain 4 GiB device copy, for calibrating the byte counters)
        python bench.py --hbm-probe   (torch's read / write / copy kernels on 4 GiB: what this HBM delivers)
+       python bench.py --matvec-sweep   (cq_dequant_matvec_many at batch 2 / 4 / 8 over the 7B-shaped
+                                         model's matrices: all 225, the first layer, one 11008x4096)
        python bench.py --configs     (the small configurations: one JSON report line)
        python bench.py --trace-summary DIR   (per-kernel, per-grid table of a rocprofv3 kernel trace)
        python bench.py --counter-summary DIR (per-kernel table of a rocprofv3 --pmc run of COUNTERS)
@@ -104,6 +106,8 @@ def parse():
     ap.add_argument("--hbm-probe", action="store_true",
                     help="time torch's read, write and copy kernels on 4 GiB buffers (one JSON line)")
     ap.add_argument("--configs", action="store_true", help="report the small configurations instead")
+    ap.add_argument("--matvec-sweep", action="store_true",
+                    help="time cq_dequant_matvec_many at batch 2/4/8 on model subsets (one JSON line)")
     ap.add_argument("--counter-summary", metavar="DIR",
                     help="per-kernel SQ counter table of a rocprofv3 --pmc run (the counters of COUNTERS)")
     ap.add_argument("--traffic-summary", metavar="DIR",
@@ -111,6 +115,47 @@ def parse():
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="print a per-kernel, per-grid table of a rocprofv3 kernel trace directory and exit")
     return ap.parse_args()
+
+
+def matvec_sweep(torch):
+    """cq_dequant_matvec_many over the 7B-shaped model's 2-bit matrices at
+    batch 2, 4 and 8: all 225 matrices, the first layer (7) and one
+    11008x4096 matrix; median of 15 back-to-back calls (HIP events around
+    each call, the call's launches included)."""
+    import rotated_codebook_bit_amd as cq
+    from rotated_codebook_bit_amd import workloads as W
+    buf, offsets = W.llama7b_device("cuda")
+    shapes = W.llama7b_shapes()
+    ng = buf.numel() // 128
+    packed = torch.empty((ng, 32), dtype=torch.uint8, device="cuda")
+    norms = torch.empty((ng,), dtype=torch.float16, device="cuda")
+    cq.quantize(buf.view(ng, 128), 2, None, packed=packed.view(ng, 1, -1), norms=norms.view(ng, 1))
+    del buf
+    kmax = max(c for _, c in shapes)
+    res = {}
+    for batch in (2, 4, 8):
+        gen = torch.Generator(device="cuda").manual_seed(batch)
+        x = torch.randn((batch, kmax), generator=gen, device="cuda")
+        xs = {c: x[:, :c].contiguous() for _, c in shapes}
+        items = []
+        for i, (r, c) in enumerate(shapes):
+            g0, g1 = int(offsets[i]) // 128, int(offsets[i + 1]) // 128
+            items.append((packed[g0:g1], norms[g0:g1], r, c, xs[c], torch.empty((batch, r), device="cuda")))
+        one = [it for it in items if it[2] == 11008][:1]
+        for name, sel in (("all_225", items), ("first_layer", items[:7]), ("one_11008x4096", one)):
+            for _ in range(3):
+                cq.dequant_matvec_many(sel, 2, None, batch)
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(16)]
+            for i in range(15):
+                ev[i].record()
+                cq.dequant_matvec_many(sel, 2, None, batch)
+            ev[15].record()
+            torch.cuda.synchronize()
+            ts = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(15))
+            res[f"batch{batch}_{name}_us"] = round(ts[7], 1)
+        del items, xs, x
+    print(json.dumps({"matvec_sweep": res}), flush=True)
 
 
 def copy_only(torch):
@@ -589,6 +634,9 @@ def main():
         sys.exit(2)
     if args.hbm_probe:
         hbm_probe(torch)
+        return
+    if args.matvec_sweep:
+        matvec_sweep(torch)
         return
     if args.copy_only:
         copy_only(torch)

@@ -506,6 +506,7 @@ hipError_t launch_table_init(const DescChunk& c, MatvecDesc* table, int64_t* gst
 struct MatvecPlan {
   int rows_per_block;
   int pair_rows_per_wave;
+  int mfma;  // 1: the matrix-core kernel (2 to 8 batch rows per launch)
 };
 MatvecPlan matvec_plan(int sbits, int nb, const MatvecDesc* descs, int n);
 // Batch rows per product-kernel launch for a call of `batch` rows over the n
@@ -525,6 +526,16 @@ hipError_t launch_matvec(const MatvecDesc* table, const int64_t* bstart, int n, 
                          const MatvecPlan& plan, int group_size, hipStream_t stream);
 
 hipError_t launch_zero(float* y, int64_t count, hipStream_t stream);
+
+// The matrix-core product over many matrices (matvec_rot.hip): activations
+// rotated beforehand into xr, batch rows b0 .. b0 + nb - 1 (nb 1 .. 8), at
+// most mfma_rows_cap(sbits, nb) rows per block.  A matrix qualifies when
+// mfma_fits(k): k % 64 == 0 and k <= 2^26.
+int mfma_rows_cap(int sbits, int nb);
+bool mfma_fits(int64_t k);
+hipError_t launch_mfma_many(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks, int sbits,
+                            const LevelTable& lv, const float* xr, int64_t b0, int nb, int log2g,
+                            int rows_per_block, hipStream_t stream);
 
 // The multi-matrix product (cq_dequant_matvec_many) with a stream-ordered
 // workspace (fixed_ws == nullptr) or a fixed one of fixed_cap bytes whose

@@ -658,6 +658,31 @@ struct MfCodes {
   }
 };
 
+// The many-matrix form's arguments: the device descriptor table, its
+// row-block prefix (block b belongs to descriptor d with bstart[d] <= b <
+// bstart[d + 1]), the rotated activations and the batch rows b0 .. b0 + nb - 1
+// of this launch.
+struct MfMany {
+  const MatvecDesc* table;
+  const int64_t* bstart;
+  int n;
+  const float* xr;
+  int64_t b0;
+  int nb;
+};
+
+__device__ __forceinline__ int mf_find_desc(const int64_t* __restrict__ start, int n, int64_t v) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (start[mid] <= v)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
 // One block per compute unit owns rows_per_block consecutive rows of the
 // matrix (at most 48) and a chunk of 4 NH batch rows (blockIdx.y).  Per
 // 4096-column pass the block rotates the pass's activations of its batch
@@ -676,9 +701,9 @@ struct MfCodes {
 // order.  Lane l's 64 columns are one 8 SB-byte load of codes per row and
 // lie in one or two groups, whose norms scale the decoded levels (one
 // multiply per weight, shared by all batch rows).
-template <int SB, int NH>
+template <int SB, int NH, bool MANY>
 __global__ void __launch_bounds__(kMfBlock, 1)
-matvec_mfma_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_block) {
+matvec_mfma_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_block, MfMany many) {
   constexpr int NB = 4 * NH;                  // batch rows per block
   constexpr int TPR = kMfBlock / NB;          // rotation threads per batch row
   constexpr int V = kMfPass / TPR;            // columns per rotation thread: 32 or 64
@@ -697,9 +722,26 @@ matvec_mfma_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_block) {
   const int w = __builtin_amdgcn_readfirstlane(t / kWave);
   const int slice = w % kMfSlices, rsub = w / kMfSlices;
   const int bq = lane >> 2, q = lane & 3;
+  int64_t b0, row_base;
+  if constexpr (MANY) {
+    // The block's matrix from the descriptor table (scalar loads); its
+    // activations are the rotated copy, batch rows b0 .. b0 + nb - 1.
+    const int d = mf_find_desc(many.bstart, many.n, blockIdx.x);
+    const MatvecDesc* m = many.table + d;
+    a.packed = m->packed;
+    a.norms = m->norms;
+    a.x = many.xr + m->xr_offset;
+    a.y = m->y;
+    a.n_out = m->n_out;
+    a.k = m->k;
+    a.batch = many.b0 + many.nb;
+    b0 = many.b0;
+    row_base = (static_cast<int64_t>(blockIdx.x) - many.bstart[d]) * rows_per_block;
+  } else {
+    b0 = static_cast<int64_t>(blockIdx.y) * NB;
+    row_base = static_cast<int64_t>(blockIdx.x) * rows_per_block;
+  }
   const int64_t k = a.k, n_out = a.n_out;
-  const int64_t b0 = static_cast<int64_t>(blockIdx.y) * NB;
-  const int64_t row_base = static_cast<int64_t>(blockIdx.x) * rows_per_block;
   const int block_rows = static_cast<int>(n_out - row_base < rows_per_block ? n_out - row_base : rows_per_block);
   const int n_quads = (block_rows + 3) / 4;
   const int nq = n_quads > rsub ? (n_quads - rsub + kMfSubsets - 1) / kMfSubsets : 0;  // this wave's quads
@@ -774,8 +816,10 @@ matvec_mfma_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_block) {
     }
     __syncthreads();  // the previous pass's activations are no longer read
     // 3. Through LDS to the rotation's layout: thread (rr, cb) reads back
-    //    columns V cb .. V cb + V - 1 (both steps conflict-free: mf_slot),
-    //    then rotates them and writes them to the very slots it read.
+    //    columns V cb .. V cb + V - 1 (both steps conflict-free: mf_pad),
+    //    then rotates them and writes them to the very slots it read.  The
+    //    many-matrix form loads activations rotated beforehand: it stops
+    //    after the first write.
     {
       float* dst = xs + rr * kMfRowF4 * 4;
 #pragma unroll
@@ -783,6 +827,7 @@ matvec_mfma_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_block) {
       hold_until_lds_written(raw);
     }
     __syncthreads();
+    if constexpr (!MANY) {
     float xv[V];
     {
       const float* src = xs + rr * kMfRowF4 * 4;
@@ -835,6 +880,7 @@ matvec_mfma_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_block) {
       hold_until_lds_written(ch);  // the stored chunks keep their registers until the LDS has them
     }
     __syncthreads();
+    }
     // 4. Products: per 16-column chunk c of the lane's 64 columns, the
     //    chunk's activations (one 64-byte run per batch row half), then for
     //    every quad the 16 scaled levels and 16 NH matrix-core steps.
@@ -990,7 +1036,7 @@ hipError_t launch_mfma_rot(const MatvecArgs& a, const LevelTable& lv, int sbits,
     part.batch = a.batch - c0 * nb;
     const int64_t chunks = (part.batch + nb - 1) / nb;
     const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(chunks < kMaxGridY ? chunks : kMaxGridY));
-#define CQ_MF(SB, NH) hipLaunchKernelGGL((matvec_mfma_kernel<SB, NH>), grid, dim3(kMfBlock), 0, s, part, lv, log2g, rows_per_block)
+#define CQ_MF(SB, NH) hipLaunchKernelGGL((matvec_mfma_kernel<SB, NH, false>), grid, dim3(kMfBlock), 0, s, part, lv, log2g, rows_per_block, MfMany{})
     if (nh == 2) {
       if (sbits == 2) CQ_MF(2, 2); else if (sbits == 3) CQ_MF(3, 2); else CQ_MF(4, 2);
     } else {
@@ -1001,6 +1047,24 @@ hipError_t launch_mfma_rot(const MatvecArgs& a, const LevelTable& lv, int sbits,
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// The many-matrix form: one launch per batch chunk of nb <= 8 rows over
+// blocks row blocks (the prefix bstart built with rows_per_block).
+hipError_t launch_mfma_many_kr(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks, int sbits,
+                               const LevelTable& lv, const float* xr, int64_t b0, int nb, int log2g,
+                               int rows_per_block, hipStream_t s) {
+  const MfMany many{table, bstart, n, xr, b0, nb};
+  MatvecArgs a{};
+  const dim3 grid(static_cast<unsigned>(blocks));
+#define CQ_MFM(SB, NH) hipLaunchKernelGGL((matvec_mfma_kernel<SB, NH, true>), grid, dim3(kMfBlock), 0, s, a, lv, log2g, rows_per_block, many)
+  if (nb > 4) {
+    if (sbits == 2) CQ_MFM(2, 2); else if (sbits == 3) CQ_MFM(3, 2); else CQ_MFM(4, 2);
+  } else {
+    if (sbits == 2) CQ_MFM(2, 1); else if (sbits == 3) CQ_MFM(3, 1); else CQ_MFM(4, 1);
+  }
+#undef CQ_MFM
+  return hipGetLastError();
 }
 
 template <int SB, int NB>
@@ -1083,6 +1147,19 @@ MatvecOnePlan matvec_one_plan(int sbits, int64_t n_out, int64_t k, int64_t batch
     return MatvecOnePlan{0, 0, static_cast<int>(rpb)};
   }
   return MatvecOnePlan{0, 2, 0};
+}
+
+int mfma_rows_cap(int sbits, int nb) { return kr::kMfSubsets * 4 * kr::mf_quads(sbits, nb > 4 ? 2 : 1); }
+
+bool mfma_fits(int64_t k) { return k <= kPairMaxK && k % 64 == 0; }
+
+hipError_t launch_mfma_many(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks, int sbits,
+                            const LevelTable& lv, const float* xr, int64_t b0, int nb, int log2g,
+                            int rows_per_block, hipStream_t stream) {
+  if (blocks <= 0) return hipSuccess;
+  if (nb < 1 || nb > 8 || sbits < 2 || sbits > 4 || rows_per_block < 1 || rows_per_block > mfma_rows_cap(sbits, nb))
+    return hipErrorInvalidValue;
+  return kr::launch_mfma_many_kr(table, bstart, n, blocks, sbits, lv, xr, b0, nb, log2g, rows_per_block, stream);
 }
 
 hipError_t launch_matvec_one(const MatvecArgs& a, int sbits, const LevelTable& lv, int group_size,

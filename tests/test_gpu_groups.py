@@ -185,6 +185,31 @@ def test_group32_odd_width_matvec(bits, batch, levels):
     check_matvec(host(y), x.astype(np.float64) @ w_hat.T, x, w_hat)
 
 
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("batch", [3, 8, 10])
+def test_group32_odd_width_matvec_many(bits, batch, levels):
+    """cq_dequant_matvec_many over matrices of an odd number of 32-column
+    groups (k = 32 mod 64), which the matrix-core kernel does not take:
+    the byte-table kernel runs chunks of 3, 8, and 8 + 2 batch rows."""
+    from parity import check_matvec
+    lv = levels[bits]
+    rng = np.random.default_rng(zlib.crc32(repr(("mvm32", bits, batch)).encode()))
+    items, refs = [], []
+    for n_out, k in ((70, 1504), (33, 96), (260, 4128)):
+        q = O.quantize(rng.standard_normal((n_out, k)) * 0.02, bits, lv, 32)
+        w_hat = O.dequantize(q.packed, q.norm16, n_out, k, bits, lv, 32)
+        x = rng.standard_normal((batch, k)).astype(np.float32)
+        items.append((torch.from_numpy(q.packed.reshape(n_out, -1)).to(DEV),
+                      torch.from_numpy(q.norm16.view(np.int16)).to(DEV).view(torch.float16),
+                      n_out, k, torch.from_numpy(x).to(DEV),
+                      torch.full((batch, n_out), float("nan"), dtype=torch.float32, device=DEV)))
+        refs.append((x, w_hat))
+    say(f"G=32 odd-width matvec_many bits={bits} batch={batch}")
+    cq.dequant_matvec_many(items, bits, lv, batch, group_size=32)
+    for it, (x, w_hat) in zip(items, refs):
+        check_matvec(host(it[5]), x.astype(np.float64) @ w_hat.T, x, w_hat)
+
+
 @pytest.mark.parametrize("g", [32, 64, 256])
 @pytest.mark.parametrize("bits", ALL_BITS)
 def test_group_size_matvec_two_passes(g, bits, levels):

@@ -467,13 +467,12 @@ def test_matvec_many_repeated_calls(batch, levels):
 
 @pytest.mark.parametrize("bits,batch", [(2, 10), (2, 8), (2, 3), (3, 5), (4, 8), (O.TERNARY, 2), (4, 12)])
 def test_matvec_row_groups(bits, batch, levels):
-    """Calls with enough rows that the byte-table kernel gives each block
-    several groups of rows: a 16401-row single-pass matrix (its last block
+    """Calls with many rows: a 16401-row single-pass matrix (its last block
     holds a one-row group), a matrix whose k spans three passes, and a small
-    one; the batches give blocks of 8, 4 and 2 groups of 4, 8 and 16 rows.
-    2-bit codes take the byte-table kernel here (a call this small runs the
-    pair kernel per row only at batch 1); batch 10 is a chunk of 8 rows and
-    one of 2."""
+    one.  Chunks of 3 to 8 batch rows take the matrix-core kernel (48- or
+    32-row blocks); chunks of 2 the byte-table kernel, whose blocks then hold
+    several groups of 16 rows (the batch-2 and ternary cases, and the last
+    chunk of batch 10 = 8 + 2)."""
     lv = levels[bits]
     shapes = [(16401, 256), (100, 8320), (37, 384)]
     rng = np.random.default_rng(zlib.crc32(repr(("row_groups", bits, batch)).encode()))

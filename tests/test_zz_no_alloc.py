@@ -57,7 +57,7 @@ def _run(mats, bits, lv, batch, fn):
 @pytest.mark.parametrize("bits", [2, 4])
 def test_noalloc_equals_stream_ordered_workspace(bits, levels32):
     lv = levels32[bits]
-    # First call: mixed shapes, one k = 0 matrix, batch 3 (byte-table kernel).
+    # First call: mixed shapes, one k = 0 matrix, batch 3 (matrix-core kernel).
     big = [(1000, 4096), (37, 11008), (64, 128), (5, 0), (300, 384), (2048, 1024)]
     # Second call, smaller: fewer matrices, smaller k, batch 1 (pair kernel
     # for 2-bit fields) -- the workspace keeps the first call's contents.
