@@ -516,12 +516,14 @@ def test_matvec_many_large_call(levels):
         check_matvec(host(it[5]), x.astype(np.float64) @ w_hat.T, x, w_hat)
 
 
-@pytest.mark.parametrize("batch,rows,n_mat", [(2, 4096, 4), (3, 16384, 8)])
+@pytest.mark.parametrize("batch,rows,n_mat", [(2, 4096, 4), (3, 16384, 8), (8, 16384, 8)])
 def test_matvec_pair_rows_large_call(batch, rows, n_mat, levels):
-    """Large 2-bit calls of several batch rows run the pair-table kernel once
-    per row: 64 MiB of codes at batch 2, 512 MiB at batch 3.  Random codes and
-    norms (uniform codes, norms 0.5-2); 48 sampled rows per matrix, the first
-    and last among them, are checked against the oracle."""
+    """Large 2-bit calls of several batch rows: at batch 2 (64 MiB of codes)
+    and 3 (512 MiB) the pair-table kernel runs once per row; at batch 8
+    (512 MiB, rows of four 4096-column passes) the matrix-core kernel takes
+    the whole chunk.  Random codes and norms (uniform codes, norms 0.5-2); 48
+    sampled rows per matrix, the first and last among them, are checked
+    against the oracle."""
     lv = levels[2]
     k = 16384
     gen = torch.Generator(device=DEV).manual_seed(1000 * batch + n_mat)
