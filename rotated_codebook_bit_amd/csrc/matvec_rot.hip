@@ -683,24 +683,27 @@ __device__ __forceinline__ int mf_find_desc(const int64_t* __restrict__ start, i
   return lo;
 }
 
-// One block per compute unit owns rows_per_block consecutive rows of the
-// matrix (at most 48) and a chunk of 4 NH batch rows (blockIdx.y).  Per
-// 4096-column pass the block rotates the pass's activations of its batch
-// rows into LDS (the threads of a batch row own V consecutive columns: the
-// butterfly inside the thread, the remaining stages across lanes by DPP).
-// Wave w takes column slice w % 4 of the pass and the row quads w / 4,
-// w / 4 + 2, ..., w / 4 + 10 of the block.
+// One block per compute unit owns rows_per_block consecutive rows of a
+// matrix (at most 48; 32 for 3- and 4-bit codes at 8 batch rows) and a
+// chunk of 4 NH batch rows (blockIdx.y; the many-matrix form: one chunk per
+// launch, the block's matrix from the descriptor table).  Per 4096-column
+// pass the block brings the pass's activations of its batch rows into LDS
+// and, in the single-matrix form, rotates them there (the threads of a batch
+// row own V consecutive columns: the butterfly inside the thread, the
+// remaining stages across lanes by DPP).  Wave w takes column slice w % 4 of
+// the pass and the row quads w / 4, w / 4 + 2, ... of the block.
 //
 // The products run on v_mfma_f32_4x4x1_16b_f32: 16 blocks of a 4x4 outer
 // product per instruction.  Lane l = 4 b + q feeds block b the activation of
-// batch row q (+4 h) and the scaled level norm * levels[code] of weight row
-// q of the quad, both at column 64 b + 16 c + j of the slice in step
-// (c, j); the block's accumulator, held by lanes 4 b .. 4 b + 3, sums
-// x[batch i] * w[row q] over block b's columns.  The 16 blocks' sums are
-// added over the lanes at the end and the four slices in LDS, in a fixed
-// order.  Lane l's 64 columns are one 8 SB-byte load of codes per row and
-// lie in one or two groups, whose norms scale the decoded levels (one
-// multiply per weight, shared by all batch rows).
+// batch row q (+4 h) and the level of weight row q of the quad, both at
+// column 64 b + 16 c + j of the slice in step (c, j); the block's
+// accumulator, held by lanes 4 b .. 4 b + 3, sums x[batch i] * w[row q]
+// over block b's columns.  The 16 blocks' sums are added over the lanes at
+// the end and the slices and lane rows in LDS, in a fixed order.  Lane l's
+// 64 columns are one 8 SB-byte load of codes per row and lie in one or two
+// groups, whose norms scale either each decoded level (one multiply per
+// weight, shared by all batch rows) or, for rows of one pass with groups of
+// 64 or more columns, the lane's accumulator once at the end.
 template <int SB, int NH, bool MANY>
 __global__ void __launch_bounds__(kMfBlock, 1)
 matvec_mfma_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_block, MfMany many) {
