@@ -559,6 +559,8 @@ def test_matvec_pair_rows_large_call(batch, rows, n_mat, levels):
     (2, 130, 4096, 17),      # batch chunks of 8, 8 and a partial one of 1
     (2, 300, 4096, 8),       # batch 8: one chunk of 8, norms applied after the products
     (2, 2750, 4096, 5),      # 11 rows per block: odd quad counts, three rows past the batch
+    (2, 1, 128, 3),          # one row, one group: three of four slices and most lanes past k
+    (3, 5, 128, 8),          # five rows of one group at batch 8
     (4, 129, 640, 9),
     (3, 65, 4096, 6),
     (3, 65, 4096, 16),       # 3-bit codes, two chunks of 8 batch rows
