@@ -303,14 +303,19 @@ typedef struct {
 
 /* cq_dequant_matvec for n matrices (descs: host array) that share bits,
  * levels and batch: the whole set runs as one activation-rotation launch and
- * one product launch per 8 batch rows, e.g. every weight matrix of a model
- * for one decode step ("How Needle 2 Model Compresses to a Single Binary",
- * section Stage 3: the runtime decodes the packed tensors on the fly).
- * Each descriptor is validated as cq_dequant_matvec validates its arguments
- * (the first failing one is reported; nothing is enqueued then).  Takes
- * sum(batch*k)*4 bytes plus a small descriptor table of stream-ordered
- * device memory (hipMallocAsync / hipFreeAsync on `stream`).  Results are
- * deterministic (fixed reduction order). */
+ * one product launch per 8 batch rows (per batch row for large 2-bit calls
+ * of 1 to 4 rows), e.g. every weight matrix of a model for one decode step
+ * ("How Needle 2 Model Compresses to a Single Binary", section Stage 3: the
+ * runtime decodes the packed tensors on the fly).  Each descriptor is
+ * validated as cq_dequant_matvec validates its arguments (the first failing
+ * one is reported; nothing is enqueued then).  Takes sum(batch*k)*4 bytes
+ * of stream-ordered device memory for the rotated activations
+ * (hipMallocAsync / hipFreeAsync on `stream`).  The device copy of the
+ * descriptor table (about 80 bytes per matrix) is kept per (device, stream)
+ * until the process ends: a later call on the same stream with the same
+ * descriptors reuses it without an upload, and a call with other
+ * descriptors rewrites it once the stream has passed the copy's last use.
+ * Results are deterministic (fixed reduction order). */
 int cq_dequant_matvec_many(int n, const cq_matvec_desc* descs, int bits, int group_size,
                            const float* levels, int n_levels, int64_t batch, void* stream);
 
@@ -320,7 +325,7 @@ int cq_dequant_matvec_many(int n, const cq_matvec_desc* descs, int bits, int gro
  * bit), but the workspace lives in a fixed array of this library, 16 MiB
  * per GPU (held from the library's load until the process ends), and the
  * call allocates nothing.  The workspace a call needs is a descriptor table
- * of about 56 bytes per matrix plus sum(batch * k) * 4 bytes of rotated
+ * of about 80 bytes per matrix plus sum(batch * k) * 4 bytes of rotated
  * activations (4.6 MB for the 225 matrices of a 7B-parameter model at
  * batch 1); a call that needs more than 16 MiB returns CQ_ERR_UNSUPPORTED
  * before anything is enqueued (use cq_dequant_matvec_many then).  Every
