@@ -507,6 +507,7 @@ struct MatvecPlan {
   int rows_per_block;
   int pair_rows_per_wave;
   int mfma;  // 1: the matrix-core kernel (2 to 8 batch rows per launch)
+  int mfma_pass;  // its pass width: 4096 columns (one block per CU) or 2048 (two)
 };
 MatvecPlan matvec_plan(int sbits, int nb, const MatvecDesc* descs, int n);
 // Batch rows per product-kernel launch for a call of `batch` rows over the n
@@ -529,13 +530,14 @@ hipError_t launch_zero(float* y, int64_t count, hipStream_t stream);
 
 // The matrix-core product over many matrices (matvec_rot.hip): activations
 // rotated beforehand into xr, batch rows b0 .. b0 + nb - 1 (nb 1 .. 8), at
-// most mfma_rows_cap(sbits, nb) rows per block.  A matrix qualifies when
-// mfma_fits(k): k % 64 == 0 and k <= 2^26.
+// most mfma_rows_cap(sbits, nb) rows per block, passes of pass_cols (4096 or
+// 2048) columns.  A matrix qualifies when mfma_fits(k): k % 64 == 0 and
+// k <= 2^26.
 int mfma_rows_cap(int sbits, int nb);
 bool mfma_fits(int64_t k);
 hipError_t launch_mfma_many(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks, int sbits,
                             const LevelTable& lv, const float* xr, int64_t b0, int nb, int log2g,
-                            int rows_per_block, hipStream_t stream);
+                            int rows_per_block, int pass_cols, hipStream_t stream);
 
 // The multi-matrix product (cq_dequant_matvec_many) with a stream-ordered
 // workspace (fixed_ws == nullptr) or a fixed one of fixed_cap bytes whose

@@ -612,28 +612,24 @@ constexpr int log2_group(int g) { return g == 32 ? 5 : g == 64 ? 6 : g == 256 ? 
 }  // namespace km
 
 namespace {
-// Whether a launch of nb batch rows takes the matrix-core kernel.  It runs
-// one block of up to 48 rows per CU at a time (its LDS holds the chunk's
-// activations), so a block's load-products-reduction chain overlaps nothing
-// on its CU: over many row blocks that costs more than it saves at 2-4 rows.
-// Whole-call times on the 7B-shaped model's matrices (us), matrix cores /
-// before: batch 8: all 225 matrices 2645 / 3200 (per-row pairs), one layer
-// 108 / 152 (byte table); batch 4: all 2062 / 1666 (pairs), one layer 88 /
-// 111 (byte table); batch 2: all 2022 / 867, one layer 87 / 61 (pairs).
-// So: chunks of 5-8 rows, and of 3-4 rows where the byte table ran before.
-bool use_mfma(int sbits, int nb, const MatvecDesc* descs, int n) {
+// Whether a launch of nb batch rows takes the matrix-core kernel: 3 to 8
+// rows when every matrix qualifies.  Whole-call times on the 7B-shaped
+// model's matrices (us), matrix cores / the kernels before them: batch 8, all
+// 225 matrices 2316 / 3179 (per-row pairs), one layer 108 / 152 (byte
+// table); batch 4, all 1493 / 1670 (pairs), one layer 87 / 110 (byte table);
+// batch 2, all 1469 / 861 (pairs), one layer 87 / 61 (pairs).  With one or
+// two live batch rows of a 4-row chunk the matrix cores do 2-4 times the
+// useful work, so batch 2 keeps the pair and byte-table kernels.
+bool use_mfma(int nb, const MatvecDesc* descs, int n) {
   if (nb < 3) return false;
-  int64_t bytes = 0;
-  for (int i = 0; i < n; ++i) {
+  for (int i = 0; i < n; ++i)
     if (!mfma_fits(descs[i].k)) return false;
-    bytes += descs[i].n_out * (descs[i].k * sbits / 8);
-  }
-  return nb >= 5 || bytes < km::kPairMinBytes;
+  return true;
 }
 }  // namespace
 
 int matvec_chunk(int sbits, int64_t batch, const MatvecDesc* descs, int n) {
-  if (use_mfma(sbits, batch < 8 ? static_cast<int>(batch) : 8, descs, n)) return 8;
+  if (use_mfma(batch < 8 ? static_cast<int>(batch) : 8, descs, n)) return 8;
   int64_t max_k = 0;
   for (int i = 0; i < n; ++i) max_k = descs[i].k > max_k ? descs[i].k : max_k;
   if (sbits != 2 || max_k > km::kPairMaxK || batch > km::kPairMaxBatch) return 8;
@@ -644,7 +640,7 @@ int matvec_chunk(int sbits, int64_t batch, const MatvecDesc* descs, int n) {
 }
 
 MatvecPlan matvec_plan(int sbits, int nb, const MatvecDesc* descs, int n) {
-  if (use_mfma(sbits, nb, descs, n)) {
+  if (use_mfma(nb, descs, n)) {
     // Matrix-core kernel: one block of up to 48 rows per compute unit at a
     // time; fewer rows per block when the call has too few rows to give
     // every CU one.
@@ -654,7 +650,17 @@ MatvecPlan matvec_plan(int sbits, int nb, const MatvecDesc* descs, int n) {
     const int64_t cap = mfma_rows_cap(sbits, nb);
     int64_t rpb = (rows + cus - 1) / cus;
     rpb = rpb < 1 ? 1 : rpb > cap ? cap : rpb;
-    return MatvecPlan{static_cast<int>(rpb), 0, 1};
+    // Calls of at least 16 row blocks per CU take 2048-column passes: half
+    // the LDS, so two blocks share a CU and one's activation load and
+    // reduction overlap the other's products (all 225 matrices of the
+    // 7B-shaped model at batch 8: 2315 against 2659 us).  Smaller calls keep
+    // 4096-column passes (one layer: 109 against 122 us; one 11008x4096
+    // matrix: 41 against 45 us), whose single pass lets 4096-column rows
+    // scale each accumulator once.
+    int64_t blocks = 0;
+    for (int i = 0; i < n; ++i) blocks += (descs[i].n_out + rpb - 1) / rpb;
+    const int pass = blocks >= 16 * cus ? 2048 : 4096;
+    return MatvecPlan{static_cast<int>(rpb), 0, 1, pass};
   }
   int64_t max_k = 0;
   for (int i = 0; i < n; ++i) max_k = descs[i].k > max_k ? descs[i].k : max_k;
@@ -703,7 +709,8 @@ hipError_t launch_matvec(const MatvecDesc* table, const int64_t* bstart, int n, 
   const int log2g = km::log2_group(group_size);
   if ((1 << log2g) != group_size) return hipErrorInvalidValue;
   if (plan.mfma)
-    return launch_mfma_many(table, bstart, n, blocks, sbits, lv, xr, b0, nb, log2g, plan.rows_per_block, stream);
+    return launch_mfma_many(table, bstart, n, blocks, sbits, lv, xr, b0, nb, log2g, plan.rows_per_block,
+                            plan.mfma_pass, stream);
   if (plan.pair_rows_per_wave == km::kPairRowsPerWave) {
     hipLaunchKernelGGL((km::matvec_pair_kernel<km::kPairWaves, km::kPairRowsPerWave>),
                        dim3(static_cast<unsigned>(blocks)), dim3(km::kPairWaves * kWave), 0, stream, table, bstart,

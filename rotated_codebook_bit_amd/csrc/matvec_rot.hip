@@ -704,26 +704,37 @@ __device__ __forceinline__ int mf_find_desc(const int64_t* __restrict__ start, i
 // groups, whose norms scale either each decoded level (one multiply per
 // weight, shared by all batch rows) or, for rows of one pass with groups of
 // 64 or more columns, the lane's accumulator once at the end.
-template <int SB, int NH, bool MANY>
-__global__ void __launch_bounds__(kMfBlock, 1)
+template <int SB, int NH, bool MANY, int PC>
+__global__ void __launch_bounds__(PC / 8, 4096 / PC)
 matvec_mfma_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_block, MfMany many) {
+  // Block shape of a pass width PC (4096 or 2048 columns): PC / 512 waves,
+  // PC / 1024 slices of 1024 columns, two row subsets; one block per CU at
+  // 4096 columns, two at 2048 (half the LDS).
+  constexpr int WV = PC / 512;
+  constexpr int BLOCK = WV * kWave;
+  constexpr int SLICES = PC / 1024;
+  constexpr int SLICE = 1024;
+  constexpr int SUBSETS = WV / SLICES;
+  static_assert(SUBSETS == kMfSubsets, "the row caps assume two row subsets");
+  constexpr int RF4 = PC / 4 + PC / 64 + 2;  // float4 per LDS row: 2 mod 8
+  constexpr int NP = SLICES * 4;             // partial sums per output: slices x lane rows
   constexpr int NB = 4 * NH;                  // batch rows per block
-  constexpr int TPR = kMfBlock / NB;          // rotation threads per batch row
-  constexpr int V = kMfPass / TPR;            // columns per rotation thread: 32 or 64
+  constexpr int TPR = BLOCK / NB;          // rotation threads per batch row
+  constexpr int V = PC / TPR;            // columns per rotation thread: 32 or 64
   constexpr int MQ = mf_quads(SB, NH);        // row quads per wave
   static_assert(MQ % 2 == 0, "quads run in pairs");
   using LT = LaneTab<SB>;
   // One LDS array: the level table first, at address 0, so that its reads
   // take their offsets as immediates; then the activations.
   constexpr int kTabF = (LT::floats + 3) / 4 * 4;
-  __shared__ __attribute__((aligned(16))) float lds[kTabF + NB * kMfRowF4 * 4];
+  __shared__ __attribute__((aligned(16))) float lds[kTabF + NB * RF4 * 4];
   float* const tab = lds;
   float* const xs = lds + kTabF;
   if (threadIdx.x < kRotBlock) LT::fill(tab, lv, threadIdx.x);
 
   const int t = threadIdx.x, lane = t % kWave;
   const int w = __builtin_amdgcn_readfirstlane(t / kWave);
-  const int slice = w % kMfSlices, rsub = w / kMfSlices;
+  const int slice = w % SLICES, rsub = w / SLICES;
   const int bq = lane >> 2, q = lane & 3;
   int64_t b0, row_base;
   if constexpr (MANY) {
@@ -747,7 +758,7 @@ matvec_mfma_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_block, M
   const int64_t k = a.k, n_out = a.n_out;
   const int block_rows = static_cast<int>(n_out - row_base < rows_per_block ? n_out - row_base : rows_per_block);
   const int n_quads = (block_rows + 3) / 4;
-  const int nq = n_quads > rsub ? (n_quads - rsub + kMfSubsets - 1) / kMfSubsets : 0;  // this wave's quads
+  const int nq = n_quads > rsub ? (n_quads - rsub + SUBSETS - 1) / SUBSETS : 0;  // this wave's quads
   const int64_t row_bytes = k * SB / 8, ngr = k >> log2g;
   const int G = 1 << log2g;
   const char* tb = reinterpret_cast<const char*>(tab);
@@ -760,7 +771,7 @@ matvec_mfma_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_block, M
   int roff_c[MQ], roff_n[MQ];
 #pragma unroll
   for (int i = 0; i < MQ; ++i) {
-    int r = 4 * (rsub + kMfSubsets * i) + q;
+    int r = 4 * (rsub + SUBSETS * i) + q;
     r = r < block_rows ? r : block_rows - 1;
     roff_c[i] = static_cast<int>(r * row_bytes);
     roff_n[i] = static_cast<int>(r * ngr * 2);
@@ -780,12 +791,12 @@ matvec_mfma_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_block, M
   // scaled once at the end by its lane's norm (lane l's accumulator only
   // sums products with lane l's weights).  Otherwise every level is scaled
   // by its norm before its products.
-  const bool late = k <= kMfPass && G >= 64;
+  const bool late = k <= PC && G >= 64;
   float lnorm[MQ];
 #pragma unroll
   for (int i = 0; i < MQ; ++i) lnorm[i] = 0.0f;
 
-  for (int64_t p0 = 0; p0 < k; p0 += kMfPass) {
+  for (int64_t p0 = 0; p0 < k; p0 += PC) {
     // 1. The pass's activations, coalesced: thread (rr, cb) loads float4s
     //    cb + TPR s (s < V / 4) of batch row rr, zeros past k or past the
     //    batch (such a float4 is read at the start of x instead).
@@ -801,8 +812,8 @@ matvec_mfma_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_block, M
     //    lane 4 b + q takes columns 64 b .. 64 b + 63 of the slice of row
     //    4 quad + q.  Lanes whose columns lie past k get norm 0 (their
     //    activations are 0 too), so nothing they read contributes.
-    const int64_t c0 = p0 + static_cast<int64_t>(slice) * kMfSlice + 64 * bq;
-    const bool slice_live = p0 + static_cast<int64_t>(slice) * kMfSlice < k;  // the same for the wave
+    const int64_t c0 = p0 + static_cast<int64_t>(slice) * SLICE + 64 * bq;
+    const bool slice_live = p0 + static_cast<int64_t>(slice) * SLICE < k;  // the same for the wave
     MfCodes<SB> codes[MQ] = {};
     uint32_t nrm[MQ][2] = {};
     {
@@ -824,7 +835,7 @@ matvec_mfma_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_block, M
     //    many-matrix form loads activations rotated beforehand: it stops
     //    after the first write.
     {
-      float* dst = xs + rr * kMfRowF4 * 4;
+      float* dst = xs + rr * RF4 * 4;
 #pragma unroll
       for (int i = 0; i < V / 4; ++i) *reinterpret_cast<uint4*>(dst + 4 * mf_pad(cb + TPR * i)) = raw[i];
       hold_until_lds_written(raw);
@@ -833,7 +844,7 @@ matvec_mfma_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_block, M
     if constexpr (!MANY) {
     float xv[V];
     {
-      const float* src = xs + rr * kMfRowF4 * 4;
+      const float* src = xs + rr * RF4 * 4;
 #pragma unroll
       for (int i = 0; i < V / 4; ++i) {
         const float4 v = *reinterpret_cast<const float4*>(src + 4 * mf_pad((V / 4) * cb + i));
@@ -872,7 +883,7 @@ matvec_mfma_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_block, M
       for (int e = 0; e < V; ++e) xv[e] = dpp_stage<8>(xv[e], lane & 8);
     }
     {
-      float* dst = xs + rr * kMfRowF4 * 4;
+      float* dst = xs + rr * RF4 * 4;
       uint4 ch[V / 4];
 #pragma unroll
       for (int i = 0; i < V / 4; ++i) {
@@ -899,13 +910,13 @@ matvec_mfma_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_block, M
         lnorm[i] = nscale[i][0];
       }
       // Float4 16 b + 4 c + u of the slice sits at mf_pad(...) = 17 (f0 / 16) + 4 c + u.
-      const float* xbase = xs + q * kMfRowF4 * 4 + 4 * mf_pad((slice * kMfSlice) / 4 + 16 * bq);
+      const float* xbase = xs + q * RF4 * 4 + 4 * mf_pad((slice * SLICE) / 4 + 16 * bq);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         float xa[NH][16];
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
-          const float* src = xbase + 4 * h * kMfRowF4 * 4;
+          const float* src = xbase + 4 * h * RF4 * 4;
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const float4 v = *reinterpret_cast<const float4*>(src + 4 * (4 * c + u));
@@ -957,7 +968,7 @@ matvec_mfma_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_block, M
   //    thread per output adds its 16 partials in order.  The activations'
   //    LDS is free once every wave is past its last products.
   __syncthreads();
-  float* dump = xs;  // [kMfMaxRows][16][NB]
+  float* dump = xs;  // [kMfMaxRows][NP][NB]
 #pragma unroll
   for (int i = 0; i < MQ; ++i)
 #pragma unroll
@@ -971,10 +982,10 @@ matvec_mfma_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_block, M
     const int part = 4 * slice + (lane >> 4);
 #pragma unroll
     for (int i = 0; i < MQ; ++i) {
-      const int r = 4 * (rsub + kMfSubsets * i) + q;  // < 48
+      const int r = 4 * (rsub + SUBSETS * i) + q;  // < 48
 #pragma unroll
       for (int h = 0; h < NH; ++h)
-        *reinterpret_cast<float4*>(dump + (r * 16 + part) * NB + 4 * h) =
+        *reinterpret_cast<float4*>(dump + (r * NP + part) * NB + 4 * h) =
             make_float4(acc[i][h][0], acc[i][h][1], acc[i][h][2], acc[i][h][3]);
     }
     wait_lds_writes();  // the stored sums keep their registers until the LDS has them
@@ -985,13 +996,13 @@ matvec_mfma_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_block, M
   }
   __syncthreads();
   const float inv_g = 1.0f / static_cast<float>(G);  // exact: a power of two
-  for (int o = t; o < block_rows * NB; o += kMfBlock) {
+  for (int o = t; o < block_rows * NB; o += BLOCK) {
     const int r = o / NB, m = o % NB;
     if (b0 + m < a.batch) {
-      const float* src = dump + r * 16 * NB + m;
+      const float* src = dump + r * NP * NB + m;
       float sum = src[0];
 #pragma unroll
-      for (int p = 1; p < 16; ++p) sum += src[p * NB];
+      for (int p = 1; p < NP; ++p) sum += src[p * NB];
       a.y[(b0 + m) * n_out + row_base + r] = sum * inv_g;
     }
   }
@@ -1039,7 +1050,7 @@ hipError_t launch_mfma_rot(const MatvecArgs& a, const LevelTable& lv, int sbits,
     part.batch = a.batch - c0 * nb;
     const int64_t chunks = (part.batch + nb - 1) / nb;
     const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(chunks < kMaxGridY ? chunks : kMaxGridY));
-#define CQ_MF(SB, NH) hipLaunchKernelGGL((matvec_mfma_kernel<SB, NH, false>), grid, dim3(kMfBlock), 0, s, part, lv, log2g, rows_per_block, MfMany{})
+#define CQ_MF(SB, NH) hipLaunchKernelGGL((matvec_mfma_kernel<SB, NH, false, 4096>), grid, dim3(kMfBlock), 0, s, part, lv, log2g, rows_per_block, MfMany{})
     if (nh == 2) {
       if (sbits == 2) CQ_MF(2, 2); else if (sbits == 3) CQ_MF(3, 2); else CQ_MF(4, 2);
     } else {
@@ -1053,14 +1064,16 @@ hipError_t launch_mfma_rot(const MatvecArgs& a, const LevelTable& lv, int sbits,
 }
 
 // The many-matrix form: one launch per batch chunk of nb <= 8 rows over
-// blocks row blocks (the prefix bstart built with rows_per_block).
-hipError_t launch_mfma_many_kr(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks, int sbits,
+// blocks row blocks (the prefix bstart built with rows_per_block), in passes
+// of PC columns.
+template <int PC>
+hipError_t launch_mfma_many_pc(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks, int sbits,
                                const LevelTable& lv, const float* xr, int64_t b0, int nb, int log2g,
                                int rows_per_block, hipStream_t s) {
   const MfMany many{table, bstart, n, xr, b0, nb};
   MatvecArgs a{};
   const dim3 grid(static_cast<unsigned>(blocks));
-#define CQ_MFM(SB, NH) hipLaunchKernelGGL((matvec_mfma_kernel<SB, NH, true>), grid, dim3(kMfBlock), 0, s, a, lv, log2g, rows_per_block, many)
+#define CQ_MFM(SB, NH) hipLaunchKernelGGL((matvec_mfma_kernel<SB, NH, true, PC>), grid, dim3(PC / 8), 0, s, a, lv, log2g, rows_per_block, many)
   if (nb > 4) {
     if (sbits == 2) CQ_MFM(2, 2); else if (sbits == 3) CQ_MFM(3, 2); else CQ_MFM(4, 2);
   } else {
@@ -1158,11 +1171,15 @@ bool mfma_fits(int64_t k) { return k <= kPairMaxK && k % 64 == 0; }
 
 hipError_t launch_mfma_many(const MatvecDesc* table, const int64_t* bstart, int n, int64_t blocks, int sbits,
                             const LevelTable& lv, const float* xr, int64_t b0, int nb, int log2g,
-                            int rows_per_block, hipStream_t stream) {
+                            int rows_per_block, int pass_cols, hipStream_t stream) {
   if (blocks <= 0) return hipSuccess;
   if (nb < 1 || nb > 8 || sbits < 2 || sbits > 4 || rows_per_block < 1 || rows_per_block > mfma_rows_cap(sbits, nb))
     return hipErrorInvalidValue;
-  return kr::launch_mfma_many_kr(table, bstart, n, blocks, sbits, lv, xr, b0, nb, log2g, rows_per_block, stream);
+  if (pass_cols == 2048)
+    return kr::launch_mfma_many_pc<2048>(table, bstart, n, blocks, sbits, lv, xr, b0, nb, log2g, rows_per_block, stream);
+  if (pass_cols == 4096)
+    return kr::launch_mfma_many_pc<4096>(table, bstart, n, blocks, sbits, lv, xr, b0, nb, log2g, rows_per_block, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_matvec_one(const MatvecArgs& a, int sbits, const LevelTable& lv, int group_size,

@@ -516,16 +516,21 @@ def test_matvec_many_large_call(levels):
         check_matvec(host(it[5]), x.astype(np.float64) @ w_hat.T, x, w_hat)
 
 
-@pytest.mark.parametrize("batch,rows,n_mat", [(2, 4096, 4), (3, 16384, 8), (8, 16384, 8)])
-def test_matvec_pair_rows_large_call(batch, rows, n_mat, levels):
+@pytest.mark.parametrize("batch,rows,n_mat,k", [(2, 4096, 4, 16384), (3, 16384, 8, 16384), (8, 16384, 8, 16384),
+                                                  (8, 65536, 4, 16384), (4, 65536, 4, 16384),
+                                                  (5, 131072, 2, 2048)])
+def test_matvec_pair_rows_large_call(batch, rows, n_mat, k, levels):
     """Large 2-bit calls of several batch rows: at batch 2 (64 MiB of codes)
-    and 3 (512 MiB) the pair-table kernel runs once per row; at batch 8
-    (512 MiB, rows of four 4096-column passes) the matrix-core kernel takes
-    the whole chunk.  Random codes and norms (uniform codes, norms 0.5-2); 48
-    sampled rows per matrix, the first and last among them, are checked
-    against the oracle."""
+    the pair-table kernel runs once per row; at batch 3 (512 MiB, one padded
+    row in the chunk of four) and 8 (512 MiB, rows of four 4096-column passes)
+    the matrix-core kernel takes the whole chunk in 4096-column passes.  Calls
+    of 16 or more row blocks per CU run it in 2048-column passes, two blocks
+    per CU: 1 GiB at batch 8 and 4 (eight passes, levels scaled per element)
+    and batch 5 on rows of one pass (the norms applied once per accumulator;
+    three rows of the chunk past the batch).  Random codes and norms (uniform
+    codes, norms 0.5-2); 48 sampled rows per matrix, the first and last among
+    them, are checked against the oracle."""
     lv = levels[2]
-    k = 16384
     gen = torch.Generator(device=DEV).manual_seed(1000 * batch + n_mat)
     rng = np.random.default_rng(batch)
     items = []
