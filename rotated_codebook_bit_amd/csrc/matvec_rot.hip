@@ -718,10 +718,10 @@ matvec_mfma_kernel(MatvecArgs a, LevelTable lv, int log2g, int rows_per_block, M
   static_assert(SUBSETS == kMfSubsets, "the row caps assume two row subsets");
   constexpr int RF4 = PC / 4 + PC / 64 + 2;  // float4 per LDS row: 2 mod 8
   constexpr int NP = SLICES * 4;             // partial sums per output: slices x lane rows
-  constexpr int NB = 4 * NH;                  // batch rows per block
-  constexpr int TPR = BLOCK / NB;          // rotation threads per batch row
-  constexpr int V = PC / TPR;            // columns per rotation thread: 32 or 64
-  constexpr int MQ = mf_quads(SB, NH);        // row quads per wave
+  constexpr int NB = 4 * NH;                 // batch rows per block
+  constexpr int TPR = BLOCK / NB;            // rotation threads per batch row
+  constexpr int V = PC / TPR;                // columns per rotation thread: 32 or 64
+  constexpr int MQ = mf_quads(SB, NH);       // row quads per wave
   static_assert(MQ % 2 == 0, "quads run in pairs");
   using LT = LaneTab<SB>;
   // One LDS array: the level table first, at address 0, so that its reads
