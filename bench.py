@@ -376,8 +376,9 @@ def c2_phases(torch, cq, W, scrub) -> dict:
 
 
 def trace_summary(path: str) -> None:
-    """Per (kernel, grid) dispatch counts and durations from the kernel-trace
-    CSV files of a rocprofv3 output directory (one markdown table)."""
+    """Per (kernel, grid) dispatch counts and durations of the library's
+    kernels from the kernel-trace CSV files of a rocprofv3 output directory
+    (one markdown table)."""
     import csv
     import glob
     import statistics
@@ -386,6 +387,8 @@ def trace_summary(path: str) -> None:
         with open(f) as fh:
             for r in csv.DictReader(fh):
                 name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
+                if "cq::" not in name:  # the library's kernels only, not torch's input generation
+                    continue
                 key = (name, r.get("Grid_Size_X", r.get("Grid_Size", "")),
                        r.get("Grid_Size_Y", "1"), r.get("Workgroup_Size_X", r.get("Workgroup_Size", "")))
                 rows.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
@@ -399,7 +402,7 @@ def trace_summary(path: str) -> None:
 # Kernels of the traffic profile: phase -> kernel name (the largest dispatch
 # of that name is the whole-model launch).
 TRAFFIC_KERNELS = {"quantize": "cq::kq::quantize_contig<4, true, false, false>",
-                   "dequantize_f32": "cq::kd::dequantize_contig<2, false, false, false>",
+                   "dequantize_f32": "cq::kd::dequantize_quad_contig<2>",
                    "matvec_pass_b1": "cq::km::matvec_pair_kernel<",
                    "fake_quant_bf16_extra": "cq::kq::fakequant_contig<4, true, true>"}
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
@@ -829,7 +832,7 @@ def main():
     del scrub
 
     dom = "dequantize_f32" if tdq >= tq else "quantize"
-    dom_kernel = {"dequantize_f32": "dequantize_contig<2, false, false, false>",
+    dom_kernel = {"dequantize_f32": "dequantize_quad_contig<2>",
                   "quantize": "quantize_contig<4, true, false, false>"}
     ach = gbs(phases[dom]["bytes"], phases[dom]["ms"])
     traffic = None

@@ -175,12 +175,14 @@ constexpr int kQuadGroups = kWave / 4;  // groups per wave
 
 // Value of lane (lane ^ X) of the same quad, X = 1 or 2: DPP quad_perm
 // [1,0,3,2] (0xB1) or [2,3,0,1] (0x4E).  Every lane of the quad must be active.
+// bound_ctrl: a lane whose source is inactive would read 0, so the move needs
+// no old value (which would cost a register clear per exchange); within an
+// active quad every source lane exists.
 template <int X>
 __device__ __forceinline__ float quad_xor(float v) {
   static_assert(X == 1 || X == 2, "quad lanes differ in bit 0 or bit 1");
   constexpr int kCtrl = X == 1 ? 0xB1 : 0x4E;
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, true));
 }
 
 // Word held by lane K of the quad (quad_perm [K,K,K,K]).

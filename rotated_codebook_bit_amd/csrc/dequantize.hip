@@ -537,6 +537,118 @@ dequantize_ragged(const uint8_t* __restrict__ packed, const uint16_t* __restrict
   }
 }
 
+// Quad form for whole-group tensors (cols % 128 == 0), float32 output, 2- or
+// 4-bit fields.  A wave takes a step of 16 consecutive groups (8 KiB of
+// output): lane 4i + q holds elements 32q .. 32q+31 of the step's group i,
+// i.e. output line l = 4i + q (128 bytes) of the step.  Its codes are the
+// lane's 4 * SB bytes at offset 4 * SB * l of the step's packed bytes (one
+// coalesced load for the wave), stages 1-2 come from the byte table, the
+// remaining in-lane stages run in registers and stages 6-7 across the quad
+// (quad_butterfly_across).  These are the float32 operations of the one-lane
+// form in the same order, so the output bits are the same.
+//
+// The step's 8 KiB is transposed through a wave-private LDS buffer so that
+// store k writes bytes 1024k .. 1024k+1023 of the step: consecutive lanes,
+// consecutive 16 bytes, whole 128-byte lines.  (Each lane storing its own
+// line in eight 16-byte pieces leaves every instruction with 64 partial
+// lines, and under the streaming policy that ran 16 times slower.)  Chunk c
+// of line l sits at slot c ^ (l & 7) of the line's 128 bytes, so eight
+// consecutive lanes touch eight different 16-byte bank groups on both sides
+// of the transpose.
+//
+// Blocks of two waves, one step per wave: on the 7B-shaped model (26.4 GB of
+// float32 output) 4.65 ms against 4.76 for the one-lane kernel; blocks of 3
+// or 4 waves took 4.83-4.85 ms, two steps per wave 4.94, one-wave blocks
+// (3.2M of them) 5.7.  64 registers, so LDS (20 KiB per block) sets the
+// occupancy at 16 waves per CU.
+constexpr int kQuadStepOut = kQuadGroups * kGroup * 4;  // output bytes per step
+constexpr int kQuadContigWaves = 2;
+// Grid cap of the quad kernel; larger tensors loop (grid-stride).
+constexpr int64_t kMaxGridBlocks = int64_t{1} << 30;
+
+template <int SB>
+__global__ void __launch_bounds__(kQuadContigWaves * kWave)
+dequantize_quad_contig(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
+                       uint8_t* __restrict__ out, int64_t n_groups, LevelTable lv) {
+  static_assert(SB == 2 || SB == 4, "byte-table widths");
+#if defined(__HIP_DEVICE_COMPILE__)  // buffer builtins exist only for the GPU target
+  constexpr int E = ByteTable<SB>::E;
+  constexpr int QB = 4 * SB;  // packed bytes per lane
+  __shared__ __attribute__((aligned(16))) float tab[TableSize<SB>::floats];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kQuadContigWaves * kQuadStepOut];
+  for (int t = threadIdx.x; t < 256; t += blockDim.x) fill_table<SB>(tab, lv, t);
+  __syncthreads();
+  const int lane = threadIdx.x & (kWave - 1), q = lane & 3;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  uint8_t* const buf = stage + wave * kQuadStepOut;
+  const int64_t n_steps = (n_groups + kQuadGroups - 1) / kQuadGroups;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kQuadContigWaves;
+  for (int64_t step = static_cast<int64_t>(blockIdx.x) * kQuadContigWaves + wave; step < n_steps;
+       step += stride) {
+    const int64_t g0 = step * kQuadGroups;
+    const int64_t left = n_groups - g0;
+    const int nv = left < kQuadGroups ? static_cast<int>(left) : kQuadGroups;
+    // Lanes of groups past the end read zeros (outside the buffer resource)
+    // and their stores are dropped.
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    uint32_t words[SB];
+    const auto src = make_rsrc(packed + g0 * (16 * SB), nv * (16 * SB));
+    if constexpr (SB == 2) {
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(src, lane * QB, 0, 0);
+      words[0] = v.x;
+      words[1] = v.y;
+    } else {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(src, lane * QB, 0, 0);
+      words[0] = v.x;
+      words[1] = v.y;
+      words[2] = v.z;
+      words[3] = v.w;
+    }
+    const auto nsrc = make_rsrc(norms + g0, nv * 2);
+    const uint16_t n16 = __builtin_amdgcn_raw_buffer_load_b16(nsrc, (lane >> 2) * 2, 0, 0);
+    float y[kQuadElems];
+#pragma unroll
+    for (int k = 0; k < kQuadElems / E; ++k) {
+      const uint32_t b = (words[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+      if constexpr (E == 4) {
+        const float4 v = *reinterpret_cast<const float4*>(tab + 4 * b);
+        y[4 * k] = v.x;
+        y[4 * k + 1] = v.y;
+        y[4 * k + 2] = v.z;
+        y[4 * k + 3] = v.w;
+      } else {
+        const float2 v = *reinterpret_cast<const float2*>(tab + 2 * b);
+        y[2 * k] = v.x;
+        y[2 * k + 1] = v.y;
+      }
+    }
+    quad_butterfly_in_lane<E>(y);
+    quad_butterfly_across<1>(y, q);
+    quad_butterfly_across<2>(y, q);
+    const float sc = half_to_float(n16) * (1.0f / kGroup);
+    uint4 ch[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      ch[c] = make_uint4(__builtin_bit_cast(uint32_t, y[4 * c] * sc), __builtin_bit_cast(uint32_t, y[4 * c + 1] * sc),
+                         __builtin_bit_cast(uint32_t, y[4 * c + 2] * sc), __builtin_bit_cast(uint32_t, y[4 * c + 3] * sc));
+    const auto dst = make_rsrc(out + g0 * (kGroup * 4), nv * (kGroup * 4));
+#pragma unroll
+    for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(buf + lane * 128 + 16 * (c ^ (lane & 7))) = ch[c];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int sl = 8 * k + (lane >> 3), cl = lane & 7;  // source line and chunk
+      const uint4 v = *reinterpret_cast<const uint4*>(buf + sl * 128 + 16 * (cl ^ (sl & 7)));
+      store16<kStoreF32>(v, dst, static_cast<uint32_t>(16 * lane), static_cast<uint32_t>(1024 * k));
+    }
+    // The next step's LDS writes come after these reads in the wave's LDS
+    // order; the wait only keeps the written registers live (see
+    // hold_until_lds_written).
+    hold_until_lds_written(ch);
+  }
+#endif
+}
+
 // Grid: one batch per wave, a grid that covers the tensor (5-6% faster on
 // the 7B-shaped model than a resident grid for float32 output; 2 and 4
 // batches per wave were 4% and 8% slower), in blocks of W waves.  A call
@@ -554,6 +666,14 @@ hipError_t launch_sb(const uint8_t* packed, const uint16_t* norms, int64_t rows,
   uint8_t* ob = static_cast<uint8_t*>(out);
   if (cols % kGroup == 0) {
     const int64_t n_groups = rows * (cols / kGroup);
+    if constexpr (!BF16OUT && !TRITS && SB == 2) {
+      const int64_t n_steps = (n_groups + kQuadGroups - 1) / kQuadGroups;
+      const int64_t want = (n_steps + kQuadContigWaves - 1) / kQuadContigWaves;
+      const int blocks = static_cast<int>(want < kMaxGridBlocks ? want : kMaxGridBlocks);
+      hipLaunchKernelGGL((dequantize_quad_contig<SB>), dim3(blocks), dim3(kQuadContigWaves * kWave), 0, s, packed,
+                         norms, ob, n_groups, lv);
+      return hipGetLastError();
+    }
     const int64_t n_batches = (n_groups + kWave - 1) / kWave;
     const ContigGrid g = dequant_grid<BF16OUT>(n_batches);
     const DequantJob job{packed, norms, ob, n_groups, TensorTable<DequantDesc>{nullptr, nullptr, 0},

@@ -223,6 +223,33 @@ def test_bf16_output_is_rounded_f32_output(bits, levels):
 
 
 
+@pytest.mark.parametrize("rows,cols", [(1, 128), (21, 128), (17, 256), (3, 2048), (2049, 128), (5, 4096)])
+def test_dequantize_f32_steps(rows, cols, levels):
+    """Float32 dequantize of whole-group tensors runs in 16-group steps, two
+    waves per block: a single group, a partial last step (21, 2049 groups),
+    a block whose second wave has no step (17x256: 3 steps) and exact steps.
+    Arbitrary packed bytes and norms (zero, tiny, large) against the
+    oracle, element by element, and nothing is written past the output."""
+    lv = levels[2]
+    rs = np.random.default_rng(rows * 7919 + cols)
+    ng = rows * cols // O.GROUP
+    packed = rs.integers(0, 256, size=(rows, cols // O.GROUP, 32), dtype=np.uint8)
+    norms = (np.abs(rs.standard_normal(ng)) * 0.3).astype(np.float16)
+    norms[::5] = 0
+    norms[1::7] = np.float16(6e-5)
+    norms[2::11] = np.float16(3e4)
+    n16 = norms.view(np.uint16).reshape(rows, -1)
+    ref = O.dequantize(packed, n16, rows, cols, 2, lv)
+    say(f"dequantize f32 steps {rows}x{cols}")
+    pad = 4096
+    flat = torch.full((rows * cols + pad,), 7.0, dtype=torch.float32, device=DEV)
+    out = flat[:rows * cols].view(rows, cols)
+    cq.dequantize(torch.from_numpy(packed.reshape(rows, -1)).to(DEV), torch.from_numpy(norms.view(np.int16)).to(DEV)
+                  .view(torch.float16).view(rows, -1), rows, cols, 2, lv, out=out)
+    check_dequant(host(out), ref, n16, rows, cols)
+    assert bool((flat[rows * cols:] == 7.0).all())
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 # Between one and a few batches per CU: the contiguous kernels then launch
