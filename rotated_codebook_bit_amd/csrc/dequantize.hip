@@ -12,12 +12,18 @@
 // Sylvester matrix), i.e. x_hat = (norm / G) * H levels[idx]; 1/G = 2^-7 is
 // exact.
 //
-// Mapping: one lane owns one group (lookup, 7 butterfly stages and scaling in
-// registers).  The 512-byte (fp32) or 256-byte (bf16) output of a lane is
-// passed through a wave-private LDS buffer in four phases of 32 elements so
-// that the HBM stores are issued as full 128-byte lines by consecutive lanes.
-// Within a phase, 16-byte chunk c of group g sits in physical chunk slot
-// c ^ s(g) with s chosen so that 16 consecutive lanes never share a bank.
+// Kernels:
+//   dequantize_quad_contig  whole-group tensors with 2- or 4-bit fields (the
+//                           common case): a quad of lanes per group, 16-group
+//                           steps per wave, stores of whole kilobytes;
+//   dequantize_contig       whole-group tensors with 3-bit fields or trit
+//                           storage: one lane per group (lookup, 7 butterfly
+//                           stages and scaling in registers), the output of
+//                           a lane passed through a wave-private LDS buffer
+//                           in four phases of 32 elements so that the HBM
+//                           stores are issued as full 128-byte lines;
+//   dequantize_ragged       rows whose length is not a multiple of 128 (a
+//                           quad of lanes per group, padding dropped).
 
 #include "cq_internal.h"
 
@@ -269,7 +275,8 @@ __device__ __forceinline__ void store16(const uint4& v, __amdgpu_buffer_rsrc_t d
 #endif
 }
 
-// Fast path: cols % 128 == 0, so group g's output is 128 contiguous values.
+// One lane per group, for whole-group tensors (cols % 128 == 0, so group g's
+// output is 128 contiguous values) with 3-bit fields or trit storage.
 // The next batch's packed words and norm are loaded into registers while the
 // current batch is computed.  Stores go through a per-batch buffer resource
 // so the lanes past the end of the last batch are dropped by the hardware.
@@ -537,63 +544,87 @@ dequantize_ragged(const uint8_t* __restrict__ packed, const uint16_t* __restrict
   }
 }
 
-// Quad form for whole-group tensors (cols % 128 == 0), float32 output, 2- or
-// 4-bit fields.  A wave takes a step of 16 consecutive groups (8 KiB of
-// output): lane 4i + q holds elements 32q .. 32q+31 of the step's group i,
-// i.e. output line l = 4i + q (128 bytes) of the step.  Its codes are the
-// lane's 4 * SB bytes at offset 4 * SB * l of the step's packed bytes (one
-// coalesced load for the wave), stages 1-2 come from the byte table, the
-// remaining in-lane stages run in registers and stages 6-7 across the quad
+// Quad form for whole-group tensors (cols % 128 == 0), 2- or 4-bit fields,
+// float32 or bf16 output.  A wave takes a step of 16 consecutive groups of
+// one tensor: lane 4i + q holds elements 32q .. 32q+31 of the step's group i,
+// i.e. output bytes LB * lane .. LB * lane + LB - 1 of the step (LB = 128 for
+// float32, 64 for bf16).  Its codes are the lane's 4 * SB bytes at offset
+// 4 * SB * lane of the step's packed bytes (one coalesced load for the wave),
+// stages 1-2 (2-bit) or 1 (4-bit) come from the byte table, the remaining
+// in-lane stages run in registers and stages 6-7 across the quad
 // (quad_butterfly_across).  These are the float32 operations of the one-lane
 // form in the same order, so the output bits are the same.
 //
-// The step's 8 KiB is transposed through a wave-private LDS buffer so that
-// store k writes bytes 1024k .. 1024k+1023 of the step: consecutive lanes,
-// consecutive 16 bytes, whole 128-byte lines.  (Each lane storing its own
-// line in eight 16-byte pieces leaves every instruction with 64 partial
-// lines, and under the streaming policy that ran 16 times slower.)  Chunk c
-// of line l sits at slot c ^ (l & 7) of the line's 128 bytes, so eight
-// consecutive lanes touch eight different 16-byte bank groups on both sides
-// of the transpose.
+// The step's output (8 or 4 KiB) is transposed through a wave-private LDS
+// buffer so that store k writes bytes 1024k .. 1024k+1023 of the step:
+// consecutive lanes, consecutive 16 bytes, whole 128-byte lines.  (Each lane
+// storing its own bytes in 16-byte pieces leaves every instruction with 64
+// partial lines, and under the streaming policy of the float32 stores that
+// ran 16 times slower.)  Chunk c of lane l sits at slot c ^ swz(l) of the
+// lane's LB bytes, so eight consecutive lanes touch eight different 16-byte
+// bank groups on both sides of the transpose.
 //
 // Blocks of two waves, one step per wave: on the 7B-shaped model (26.4 GB of
-// float32 output) 4.65 ms against 4.76 for the one-lane kernel; blocks of 3
-// or 4 waves took 4.83-4.85 ms, two steps per wave 4.94, one-wave blocks
-// (3.2M of them) 5.7.  64 registers, so LDS (20 KiB per block) sets the
-// occupancy at 16 waves per CU.
-constexpr int kQuadStepOut = kQuadGroups * kGroup * 4;  // output bytes per step
+// float32 output) 4.60-4.65 ms against 4.76 for the one-lane kernel; blocks
+// of 3 or 4 waves took 4.83-4.85 ms, two steps per wave 4.94, one-wave blocks
+// 5.7, a capped grid looping over steps 5.65.  LDS (20 KiB per block for
+// float32) sets the occupancy at 16 waves per CU.
+//
+// MANY: a table of tensors whose 64-group batches are numbered consecutively
+// (the one-lane kernel's numbering); step s is quarter s % 4 of batch s / 4,
+// and quarters past a tensor's last group are skipped.
 constexpr int kQuadContigWaves = 2;
-// Grid cap of the quad kernel; larger tensors loop (grid-stride).
+// Grid cap of the quad kernel; larger calls loop (grid-stride).
 constexpr int64_t kMaxGridBlocks = int64_t{1} << 30;
 
-template <int SB>
+template <int SB, bool BF16OUT, bool MANY>
 __global__ void __launch_bounds__(kQuadContigWaves * kWave)
-dequantize_quad_contig(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
-                       uint8_t* __restrict__ out, int64_t n_groups, LevelTable lv) {
+dequantize_quad_contig(DequantJob job, LevelTable lv) {
   static_assert(SB == 2 || SB == 4, "byte-table widths");
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer builtins exist only for the GPU target
   constexpr int E = ByteTable<SB>::E;
-  constexpr int QB = 4 * SB;  // packed bytes per lane
+  constexpr int QB = 4 * SB;                 // packed bytes per lane
+  constexpr int OB = BF16OUT ? 2 : 4;        // output bytes per element
+  constexpr int LB = kQuadElems * OB;        // output bytes per lane
+  constexpr int CPL = LB / 16;               // 16-byte chunks per lane
+  constexpr int STEP = kWave * LB;           // output bytes per step
+  constexpr int NS = STEP / 1024;            // store instructions per step
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   __shared__ __attribute__((aligned(16))) float tab[TableSize<SB>::floats];
-  __shared__ __attribute__((aligned(16))) uint8_t stage[kQuadContigWaves * kQuadStepOut];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kQuadContigWaves * STEP];
   for (int t = threadIdx.x; t < 256; t += blockDim.x) fill_table<SB>(tab, lv, t);
   __syncthreads();
   const int lane = threadIdx.x & (kWave - 1), q = lane & 3;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  uint8_t* const buf = stage + wave * kQuadStepOut;
-  const int64_t n_steps = (n_groups + kQuadGroups - 1) / kQuadGroups;
+  uint8_t* const buf = stage + wave * STEP;
+  // Bank-group swizzle of a lane's chunks (see above).
+  auto swz = [](int l) __attribute__((always_inline)) { return BF16OUT ? (l >> 2) & 3 : l & 7; };
+  const int64_t n_steps = MANY ? 4 * job.n_batches : (job.n_groups + kQuadGroups - 1) / kQuadGroups;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kQuadContigWaves;
   for (int64_t step = static_cast<int64_t>(blockIdx.x) * kQuadContigWaves + wave; step < n_steps;
        step += stride) {
-    const int64_t g0 = step * kQuadGroups;
-    const int64_t left = n_groups - g0;
+    const uint8_t* pk = job.packed;
+    const uint16_t* nm = job.norms;
+    uint8_t* o = job.out;
+    int64_t g0 = step * kQuadGroups, ng = job.n_groups;
+    if constexpr (MANY) {
+      const int64_t b = step >> 2;
+      const int d = find_unit(job.t.start, 0, job.t.n, b);
+      const DequantDesc* qd = job.t.desc + d;  // field by field: scalar loads
+      pk = load_const(&qd->packed);
+      nm = load_const(&qd->norms);
+      o = load_const(&qd->out);
+      ng = load_const(&qd->rows) * (load_const(&qd->cols) / kGroup);
+      g0 = (b - load_const(job.t.start + d)) * kWave + (step & 3) * kQuadGroups;
+      if (g0 >= ng) continue;  // a quarter past the tensor's partial last batch
+    }
+    const int64_t left = ng - g0;
     const int nv = left < kQuadGroups ? static_cast<int>(left) : kQuadGroups;
     // Lanes of groups past the end read zeros (outside the buffer resource)
     // and their stores are dropped.
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     uint32_t words[SB];
-    const auto src = make_rsrc(packed + g0 * (16 * SB), nv * (16 * SB));
+    const auto src = make_rsrc(pk + g0 * (16 * SB), nv * (16 * SB));
     if constexpr (SB == 2) {
       const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(src, lane * QB, 0, 0);
       words[0] = v.x;
@@ -605,7 +636,7 @@ dequantize_quad_contig(const uint8_t* __restrict__ packed, const uint16_t* __res
       words[2] = v.z;
       words[3] = v.w;
     }
-    const auto nsrc = make_rsrc(norms + g0, nv * 2);
+    const auto nsrc = make_rsrc(nm + g0, nv * 2);
     const uint16_t n16 = __builtin_amdgcn_raw_buffer_load_b16(nsrc, (lane >> 2) * 2, 0, 0);
     float y[kQuadElems];
 #pragma unroll
@@ -627,19 +658,32 @@ dequantize_quad_contig(const uint8_t* __restrict__ packed, const uint16_t* __res
     quad_butterfly_across<1>(y, q);
     quad_butterfly_across<2>(y, q);
     const float sc = half_to_float(n16) * (1.0f / kGroup);
-    uint4 ch[8];
+    uint4 ch[CPL];
+    if constexpr (BF16OUT) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      ch[c] = make_uint4(__builtin_bit_cast(uint32_t, y[4 * c] * sc), __builtin_bit_cast(uint32_t, y[4 * c + 1] * sc),
-                         __builtin_bit_cast(uint32_t, y[4 * c + 2] * sc), __builtin_bit_cast(uint32_t, y[4 * c + 3] * sc));
-    const auto dst = make_rsrc(out + g0 * (kGroup * 4), nv * (kGroup * 4));
+      for (int c = 0; c < CPL; ++c) {
+        uint32_t w[4];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(buf + lane * 128 + 16 * (c ^ (lane & 7))) = ch[c];
+        for (int i = 0; i < 4; ++i)
+          w[i] = f32_to_bf16_rne(y[8 * c + 2 * i] * sc) | (f32_to_bf16_rne(y[8 * c + 2 * i + 1] * sc) << 16);
+        ch[c] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    } else {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int sl = 8 * k + (lane >> 3), cl = lane & 7;  // source line and chunk
-      const uint4 v = *reinterpret_cast<const uint4*>(buf + sl * 128 + 16 * (cl ^ (sl & 7)));
-      store16<kStoreF32>(v, dst, static_cast<uint32_t>(16 * lane), static_cast<uint32_t>(1024 * k));
+      for (int c = 0; c < CPL; ++c)
+        ch[c] = make_uint4(__builtin_bit_cast(uint32_t, y[4 * c] * sc), __builtin_bit_cast(uint32_t, y[4 * c + 1] * sc),
+                           __builtin_bit_cast(uint32_t, y[4 * c + 2] * sc),
+                           __builtin_bit_cast(uint32_t, y[4 * c + 3] * sc));
+    }
+    const auto dst = make_rsrc(o + g0 * (kGroup * OB), nv * (kGroup * OB));
+    const int sw = swz(lane);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) *reinterpret_cast<uint4*>(buf + lane * LB + 16 * (c ^ sw)) = ch[c];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const int sl = (1024 * k + 16 * lane) / LB, cl = lane % CPL;  // source lane and chunk
+      const uint4 v = *reinterpret_cast<const uint4*>(buf + sl * LB + 16 * (cl ^ swz(sl)));
+      store16<BF16OUT ? 0 : kStoreF32>(v, dst, static_cast<uint32_t>(16 * lane), static_cast<uint32_t>(1024 * k));
     }
     // The next step's LDS writes come after these reads in the wave's LDS
     // order; the wait only keeps the written registers live (see
@@ -660,26 +704,31 @@ ContigGrid dequant_grid(int64_t n_batches) {
   return contig_grid(n_batches, contig_waves(BF16OUT), 1, kBlocksPerCu);
 }
 
+// Blocks of the quad kernel for n_steps steps: one step per wave.
+inline int quad_grid(int64_t n_steps) {
+  const int64_t want = (n_steps + kQuadContigWaves - 1) / kQuadContigWaves;
+  return static_cast<int>(want < 1 ? 1 : want < kMaxGridBlocks ? want : kMaxGridBlocks);
+}
+
 template <int SB, bool BF16OUT, bool TRITS>
 hipError_t launch_sb(const uint8_t* packed, const uint16_t* norms, int64_t rows, int64_t cols,
                      const LevelTable& lv, void* out, hipStream_t s) {
   uint8_t* ob = static_cast<uint8_t*>(out);
   if (cols % kGroup == 0) {
     const int64_t n_groups = rows * (cols / kGroup);
-    if constexpr (!BF16OUT && !TRITS && SB == 2) {
+    if constexpr (!TRITS && SB != 3) {  // 2- and 4-bit fields: the quad kernel
       const int64_t n_steps = (n_groups + kQuadGroups - 1) / kQuadGroups;
-      const int64_t want = (n_steps + kQuadContigWaves - 1) / kQuadContigWaves;
-      const int blocks = static_cast<int>(want < kMaxGridBlocks ? want : kMaxGridBlocks);
-      hipLaunchKernelGGL((dequantize_quad_contig<SB>), dim3(blocks), dim3(kQuadContigWaves * kWave), 0, s, packed,
-                         norms, ob, n_groups, lv);
-      return hipGetLastError();
+      const DequantJob job{packed, norms, ob, n_groups, TensorTable<DequantDesc>{nullptr, nullptr, 0}, 0};
+      hipLaunchKernelGGL((dequantize_quad_contig<SB, BF16OUT, false>), dim3(quad_grid(n_steps)),
+                         dim3(kQuadContigWaves * kWave), 0, s, job, lv);
+    } else {  // 3-bit fields and trit storage: one lane per group
+      const int64_t n_batches = (n_groups + kWave - 1) / kWave;
+      const ContigGrid g = dequant_grid<BF16OUT>(n_batches);
+      const DequantJob job{packed, norms, ob, n_groups, TensorTable<DequantDesc>{nullptr, nullptr, 0},
+                           n_batches};
+      hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT, false, TRITS>), dim3(g.blocks), dim3(g.waves * kWave), 0,
+                         s, job, lv);
     }
-    const int64_t n_batches = (n_groups + kWave - 1) / kWave;
-    const ContigGrid g = dequant_grid<BF16OUT>(n_batches);
-    const DequantJob job{packed, norms, ob, n_groups, TensorTable<DequantDesc>{nullptr, nullptr, 0},
-                         n_batches};
-    hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT, false, TRITS>), dim3(g.blocks), dim3(g.waves * kWave), 0, s,
-                       job, lv);
   } else {
     const int blocks = quad_blocks(rows * ((cols + kGroup - 1) / kGroup));
     const TensorTable<DequantDesc> none{nullptr, nullptr, 0};
@@ -698,10 +747,15 @@ hipError_t launch_many_sb(const LevelTable& lv, TensorTable<DequantDesc> contig,
                           TensorTable<DequantDesc> ragged, int64_t ragged_groups, int64_t ragged_cols_gcd,
                           hipStream_t s) {
   if (contig_batches > 0) {
-    const ContigGrid g = dequant_grid<BF16OUT>(contig_batches);
     const DequantJob job{nullptr, nullptr, nullptr, 0, contig, contig_batches};
-    hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT, true, TRITS>), dim3(g.blocks), dim3(g.waves * kWave), 0, s,
-                       job, lv);
+    if constexpr (!TRITS && SB != 3) {
+      hipLaunchKernelGGL((dequantize_quad_contig<SB, BF16OUT, true>), dim3(quad_grid(4 * contig_batches)),
+                         dim3(kQuadContigWaves * kWave), 0, s, job, lv);
+    } else {
+      const ContigGrid g = dequant_grid<BF16OUT>(contig_batches);
+      hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT, true, TRITS>), dim3(g.blocks), dim3(g.waves * kWave), 0, s,
+                         job, lv);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

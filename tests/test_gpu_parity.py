@@ -223,31 +223,66 @@ def test_bf16_output_is_rounded_f32_output(bits, levels):
 
 
 
-@pytest.mark.parametrize("rows,cols", [(1, 128), (21, 128), (17, 256), (3, 2048), (2049, 128), (5, 4096)])
-def test_dequantize_f32_steps(rows, cols, levels):
-    """Float32 dequantize of whole-group tensors runs in 16-group steps, two
-    waves per block: a single group, a partial last step (21, 2049 groups),
-    a block whose second wave has no step (17x256: 3 steps) and exact steps.
-    Arbitrary packed bytes and norms (zero, tiny, large) against the
-    oracle, element by element, and nothing is written past the output."""
-    lv = levels[2]
-    rs = np.random.default_rng(rows * 7919 + cols)
+def random_codes(rows, cols, bits, seed):
+    """Arbitrary packed bytes and binary16 norms (zero, tiny, large)."""
+    rs = np.random.default_rng(seed)
     ng = rows * cols // O.GROUP
-    packed = rs.integers(0, 256, size=(rows, cols // O.GROUP, 32), dtype=np.uint8)
+    packed = rs.integers(0, 256, size=(rows, cols // O.GROUP, 16 * bits), dtype=np.uint8)
     norms = (np.abs(rs.standard_normal(ng)) * 0.3).astype(np.float16)
     norms[::5] = 0
     norms[1::7] = np.float16(6e-5)
     norms[2::11] = np.float16(3e4)
-    n16 = norms.view(np.uint16).reshape(rows, -1)
-    ref = O.dequantize(packed, n16, rows, cols, 2, lv)
-    say(f"dequantize f32 steps {rows}x{cols}")
+    return packed, norms.view(np.uint16).reshape(rows, -1)
+
+
+def codes_dev(packed, n16, rows):
+    return (torch.from_numpy(packed.reshape(rows, -1)).to(DEV),
+            torch.from_numpy(n16.view(np.int16)).to(DEV).view(torch.float16))
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("rows,cols", [(1, 128), (21, 128), (17, 256), (3, 2048), (2049, 128), (5, 4096)])
+def test_dequantize_steps(rows, cols, bits, levels):
+    """Dequantize of whole-group tensors with 2- and 4-bit fields runs in
+    16-group steps, two waves per block: a single group, a partial last step
+    (21, 2049 groups), a block whose second wave has no step (17x256: 3
+    steps) and exact steps.  Arbitrary codes and norms; float32 output
+    against the oracle element by element, bf16 output equal to the rounded
+    float32 output, and nothing written past either output."""
+    lv = levels[bits]
+    packed, n16 = random_codes(rows, cols, bits, rows * 7919 + cols + bits)
+    ref = O.dequantize(packed, n16, rows, cols, bits, lv)
+    p_dev, n_dev = codes_dev(packed, n16, rows)
+    say(f"dequantize steps {rows}x{cols} bits={bits}")
     pad = 4096
     flat = torch.full((rows * cols + pad,), 7.0, dtype=torch.float32, device=DEV)
     out = flat[:rows * cols].view(rows, cols)
-    cq.dequantize(torch.from_numpy(packed.reshape(rows, -1)).to(DEV), torch.from_numpy(norms.view(np.int16)).to(DEV)
-                  .view(torch.float16).view(rows, -1), rows, cols, 2, lv, out=out)
+    cq.dequantize(p_dev, n_dev, rows, cols, bits, lv, out=out)
     check_dequant(host(out), ref, n16, rows, cols)
     assert bool((flat[rows * cols:] == 7.0).all())
+    flat16 = torch.full((rows * cols + pad,), 7.0, dtype=torch.bfloat16, device=DEV)
+    out16 = flat16[:rows * cols].view(rows, cols)
+    cq.dequantize(p_dev, n_dev, rows, cols, bits, lv, out_dtype=torch.bfloat16, out=out16)
+    assert torch.equal(out16.view(torch.int16), out.to(torch.bfloat16).view(torch.int16))
+    assert bool((flat16[rows * cols:] == 7.0).all())
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_dequantize_many_steps(bits, levels):
+    """The multi-tensor dequantize takes 16-group quarters of each tensor's
+    64-group batches; quarters past a tensor's last group are skipped.
+    Tensors of 1, 6, 34, 50 and 130 groups in one call (float32 against the
+    oracle, bf16 against the rounded float32 output)."""
+    lv = levels[bits]
+    shapes = [(1, 128), (3, 256), (17, 256), (5, 1280), (13, 1280)]
+    codes = [random_codes(r, c, bits, 31 * i + bits) for i, (r, c) in enumerate(shapes)]
+    items = [(*codes_dev(pk, n16, r), r, c) for (r, c), (pk, n16) in zip(shapes, codes)]
+    say(f"dequantize_many steps bits={bits}")
+    outs = cq.dequantize_many(items, bits, lv)
+    outs16 = cq.dequantize_many(items, bits, lv, out_dtype=torch.bfloat16)
+    for (r, c), (pk, n16), o, o16 in zip(shapes, codes, outs, outs16):
+        check_dequant(host(o), O.dequantize(pk, n16, r, c, bits, lv), n16, r, c)
+        assert torch.equal(o16.view(torch.int16), o.to(torch.bfloat16).view(torch.int16)), (r, c)
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
