@@ -13,11 +13,11 @@
 // exact.
 //
 // Kernels:
-//   dequantize_quad_contig  whole-group tensors with 2- or 4-bit fields (the
-//                           common case): a quad of lanes per group, 16-group
-//                           steps per wave, stores of whole kilobytes;
-//   dequantize_contig       whole-group tensors with 3-bit fields or trit
-//                           storage: one lane per group (lookup, 7 butterfly
+//   dequantize_quad_contig  whole-group tensors with 2-, 3- or 4-bit fields:
+//                           a quad of lanes per group, 16-group steps per
+//                           wave, stores of whole kilobytes;
+//   dequantize_contig       whole-group tensors in trit storage: one lane
+//                           per group (lookup, 7 butterfly
 //                           stages and scaling in registers), the output of
 //                           a lane passed through a wave-private LDS buffer
 //                           in four phases of 32 elements so that the HBM
@@ -276,7 +276,8 @@ __device__ __forceinline__ void store16(const uint4& v, __amdgpu_buffer_rsrc_t d
 }
 
 // One lane per group, for whole-group tensors (cols % 128 == 0, so group g's
-// output is 128 contiguous values) with 3-bit fields or trit storage.
+// output is 128 contiguous values) in trit storage (and, as SB = 3, the
+// kernel that 3-bit fields used before the quad kernel).
 // The next batch's packed words and norm are loaded into registers while the
 // current batch is computed.  Stores go through a per-batch buffer resource
 // so the lanes past the end of the last batch are dropped by the hardware.
@@ -544,13 +545,15 @@ dequantize_ragged(const uint8_t* __restrict__ packed, const uint16_t* __restrict
   }
 }
 
-// Quad form for whole-group tensors (cols % 128 == 0), 2- or 4-bit fields,
-// float32 or bf16 output.  A wave takes a step of 16 consecutive groups of
-// one tensor: lane 4i + q holds elements 32q .. 32q+31 of the step's group i,
+// Quad form for whole-group tensors (cols % 128 == 0), 2-, 3- or 4-bit
+// fields, float32 or bf16 output.  A wave takes a step of 16 consecutive
+// groups of one tensor: lane 4i + q holds elements 32q .. 32q+31 of the
+// step's group i,
 // i.e. output bytes LB * lane .. LB * lane + LB - 1 of the step (LB = 128 for
 // float32, 64 for bf16).  Its codes are the lane's 4 * SB bytes at offset
 // 4 * SB * lane of the step's packed bytes (one coalesced load for the wave),
-// stages 1-2 (2-bit) or 1 (4-bit) come from the byte table, the remaining
+// stages 1-2 (2-bit) or 1 (4-bit) come from the byte table (3-bit fields:
+// one lookup per element in an 8-entry table, no stage), the remaining
 // in-lane stages run in registers and stages 6-7 across the quad
 // (quad_butterfly_across).  These are the float32 operations of the one-lane
 // form in the same order, so the output bits are the same.
@@ -580,9 +583,9 @@ constexpr int64_t kMaxGridBlocks = int64_t{1} << 30;
 template <int SB, bool BF16OUT, bool MANY>
 __global__ void __launch_bounds__(kQuadContigWaves * kWave)
 dequantize_quad_contig(DequantJob job, LevelTable lv) {
-  static_assert(SB == 2 || SB == 4, "byte-table widths");
+  static_assert(SB >= 2 && SB <= 4, "2-, 3- and 4-bit fields");
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer builtins exist only for the GPU target
-  constexpr int E = ByteTable<SB>::E;
+  constexpr int E = SB == 3 ? 1 : ByteTable<SB>::E;  // elements per table read
   constexpr int QB = 4 * SB;                 // packed bytes per lane
   constexpr int OB = BF16OUT ? 2 : 4;        // output bytes per element
   constexpr int LB = kQuadElems * OB;        // output bytes per lane
@@ -629,6 +632,12 @@ dequantize_quad_contig(DequantJob job, LevelTable lv) {
       const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(src, lane * QB, 0, 0);
       words[0] = v.x;
       words[1] = v.y;
+    } else if constexpr (SB == 3) {
+      typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+      const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(src, lane * QB, 0, 0);
+      words[0] = v.x;
+      words[1] = v.y;
+      words[2] = v.z;
     } else {
       const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(src, lane * QB, 0, 0);
       words[0] = v.x;
@@ -641,6 +650,13 @@ dequantize_quad_contig(DequantJob job, LevelTable lv) {
     float y[kQuadElems];
 #pragma unroll
     for (int k = 0; k < kQuadElems / E; ++k) {
+      if constexpr (SB == 3) {  // element k's field at bit 3k of the lane's 96 bits; an 8-entry table
+        const int pos = 3 * k, wd = pos >> 5, off = pos & 31;
+        uint32_t v = words[wd] >> off;
+        if (off > 29) v |= words[wd + 1] << (32 - off);
+        y[k] = tab[v & 7u];
+        continue;
+      }
       const uint32_t b = (words[k >> 2] >> (8 * (k & 3))) & 0xFFu;
       if constexpr (E == 4) {
         const float4 v = *reinterpret_cast<const float4*>(tab + 4 * b);
@@ -716,12 +732,12 @@ hipError_t launch_sb(const uint8_t* packed, const uint16_t* norms, int64_t rows,
   uint8_t* ob = static_cast<uint8_t*>(out);
   if (cols % kGroup == 0) {
     const int64_t n_groups = rows * (cols / kGroup);
-    if constexpr (!TRITS && SB != 3) {  // 2- and 4-bit fields: the quad kernel
+    if constexpr (!TRITS) {  // 2-, 3- and 4-bit fields: the quad kernel
       const int64_t n_steps = (n_groups + kQuadGroups - 1) / kQuadGroups;
       const DequantJob job{packed, norms, ob, n_groups, TensorTable<DequantDesc>{nullptr, nullptr, 0}, 0};
       hipLaunchKernelGGL((dequantize_quad_contig<SB, BF16OUT, false>), dim3(quad_grid(n_steps)),
                          dim3(kQuadContigWaves * kWave), 0, s, job, lv);
-    } else {  // 3-bit fields and trit storage: one lane per group
+    } else {  // trit storage: one lane per group
       const int64_t n_batches = (n_groups + kWave - 1) / kWave;
       const ContigGrid g = dequant_grid<BF16OUT>(n_batches);
       const DequantJob job{packed, norms, ob, n_groups, TensorTable<DequantDesc>{nullptr, nullptr, 0},
@@ -748,7 +764,7 @@ hipError_t launch_many_sb(const LevelTable& lv, TensorTable<DequantDesc> contig,
                           hipStream_t s) {
   if (contig_batches > 0) {
     const DequantJob job{nullptr, nullptr, nullptr, 0, contig, contig_batches};
-    if constexpr (!TRITS && SB != 3) {
+    if constexpr (!TRITS) {
       hipLaunchKernelGGL((dequantize_quad_contig<SB, BF16OUT, true>), dim3(quad_grid(4 * contig_batches)),
                          dim3(kQuadContigWaves * kWave), 0, s, job, lv);
     } else {
