@@ -13,15 +13,10 @@
 // exact.
 //
 // Kernels:
-//   dequantize_quad_contig  whole-group tensors with 2-, 3- or 4-bit fields:
-//                           a quad of lanes per group, 16-group steps per
-//                           wave, stores of whole kilobytes;
-//   dequantize_contig       whole-group tensors in trit storage: one lane
-//                           per group (lookup, 7 butterfly
-//                           stages and scaling in registers), the output of
-//                           a lane passed through a wave-private LDS buffer
-//                           in four phases of 32 elements so that the HBM
-//                           stores are issued as full 128-byte lines;
+//   dequantize_quad_contig  whole-group tensors (cols % 128 == 0): 2-, 3- or
+//                           4-bit fields or trit storage, a quad of lanes
+//                           per group, 16-group steps per wave, stores of
+//                           whole kilobytes;
 //   dequantize_ragged       rows whose length is not a multiple of 128 (a
 //                           quad of lanes per group, padding dropped).
 
@@ -30,53 +25,6 @@
 namespace cq {
 namespace kd {
 
-constexpr int kWaves = 4;
-constexpr int kBlock = kWaves * kWave;
-// Floor of the covering grid for mid-size tensors: one block per CU.
-constexpr int kBlocksPerCu = 1;
-// Waves per block of dequantize_contig: eight.  On the 7B-shaped model that
-// was 1.6% faster than four for float32 output (at about 200 VGPRs a CU holds
-// eight waves either way) and, with the covering grid, 6.6% faster than the
-// resident grid of 4-wave blocks that bf16 output used before.
-constexpr int contig_waves(bool) { return 2 * kWaves; }
-
-__device__ __forceinline__ void butterfly(float (&y)[kGroup]) {
-#pragma unroll
-  for (int h = 1; h < kGroup; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < kGroup; i += 2 * h) {
-#pragma unroll
-      for (int j = i; j < i + h; ++j) {
-        const float a = y[j], b = y[j + h];
-        y[j] = a + b;
-        y[j + h] = a - b;
-      }
-    }
-  }
-}
-
-template <int SB>
-__device__ __forceinline__ void load_indices(const uint8_t* __restrict__ packed, int64_t g,
-                                             uint32_t (&words)[4 * SB]) {
-  const uint4* src = reinterpret_cast<const uint4*>(packed + g * (16 * SB));
-#pragma unroll
-  for (int i = 0; i < SB; ++i) {
-    const uint4 v = src[i];
-    words[4 * i] = v.x;
-    words[4 * i + 1] = v.y;
-    words[4 * i + 2] = v.z;
-    words[4 * i + 3] = v.w;
-  }
-}
-
-template <int SB>
-__device__ __forceinline__ uint32_t index_at(const uint32_t (&words)[4 * SB], int j) {
-  const int pos = SB * j, wd = pos >> 5, off = pos & 31;
-  uint32_t v = words[wd] >> off;
-  if (off + SB > 32) v |= words[wd + 1] << (32 - off);
-  return v & ((1u << SB) - 1u);
-}
-
 __device__ __forceinline__ float half_to_float(uint16_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, h));
 }
@@ -84,36 +32,6 @@ __device__ __forceinline__ float half_to_float(uint16_t h) {
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   const uint32_t u = __builtin_bit_cast(uint32_t, f);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-// Reconstruct one group into y (float32, already scaled), generic form:
-// per-element level lookup, then the 7 butterfly stages.
-template <int SB>
-__device__ __forceinline__ void reconstruct(const uint32_t (&words)[4 * SB], uint16_t n16,
-                                            const float* lut, float (&y)[kGroup]) {
-#pragma unroll
-  for (int j = 0; j < kGroup; ++j) y[j] = lut[index_at<SB>(words, j)];
-  butterfly(y);
-  const float s = half_to_float(n16) * (1.0f / kGroup);
-#pragma unroll
-  for (int j = 0; j < kGroup; ++j) y[j] *= s;
-}
-
-// Butterfly stages with pair distance >= h0 (the earlier ones are done).
-template <int H0>
-__device__ __forceinline__ void butterfly_from(float (&y)[kGroup]) {
-#pragma unroll
-  for (int h = H0; h < kGroup; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < kGroup; i += 2 * h) {
-#pragma unroll
-      for (int j = i; j < i + h; ++j) {
-        const float a = y[j], b = y[j + h];
-        y[j] = a + b;
-        y[j + h] = a - b;
-      }
-    }
-  }
 }
 
 // Byte table: a packed byte holds E = 8 / SB consecutive indices (E = 4 at 2
@@ -150,28 +68,6 @@ struct ByteTable {
       hold_values(v0, v1);
     }
   }
-  // Byte k (0..G*SB/8-1) of the group's packed bits.
-  static __device__ __forceinline__ uint32_t byte_at(const uint32_t (&words)[4 * SB], int k) {
-    return (words[k >> 2] >> (8 * (k & 3))) & 0xFFu;
-  }
-  static __device__ __forceinline__ void decode(const uint32_t (&words)[4 * SB], const float* tab,
-                                                float (&y)[kGroup]) {
-#pragma unroll
-    for (int k = 0; k < kGroup / E; ++k) {
-      const uint32_t b = byte_at(words, k);
-      if constexpr (E == 4) {
-        const float4 v = *reinterpret_cast<const float4*>(tab + 4 * b);
-        y[4 * k] = v.x;
-        y[4 * k + 1] = v.y;
-        y[4 * k + 2] = v.z;
-        y[4 * k + 3] = v.w;
-      } else {
-        const float2 v = *reinterpret_cast<const float2*>(tab + 2 * b);
-        y[2 * k] = v.x;
-        y[2 * k + 1] = v.y;
-      }
-    }
-  }
 };
 
 template <int SB>
@@ -193,60 +89,8 @@ __device__ __forceinline__ void fill_table(float* tab, const LevelTable& lv, int
   }
 }
 
-template <int SB>
-__device__ __forceinline__ void reconstruct_fast(const uint32_t (&words)[4 * SB], uint16_t n16,
-                                                 const float* tab, float (&y)[kGroup]) {
-  if constexpr (SB == 3) {
-    reconstruct<SB>(words, n16, tab, y);
-  } else {
-    ByteTable<SB>::decode(words, tab, y);
-    butterfly_from<ByteTable<SB>::E>(y);
-    const float s = half_to_float(n16) * (1.0f / kGroup);
-#pragma unroll
-    for (int j = 0; j < kGroup; ++j) y[j] *= s;
-  }
-}
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-
-// Packed words and norm of every lane's group of batch bt (zeros past the
-// end: buffer loads outside the resource return 0).
-template <int SB>
-__device__ __forceinline__ void fetch_batch(const uint8_t* __restrict__ packed,
-                                            const uint16_t* __restrict__ norms, int64_t bt,
-                                            int nv, int lane, uint32_t (&words)[4 * SB],
-                                            uint16_t& n16) {
-#if defined(__HIP_DEVICE_COMPILE__)  // buffer builtins exist only for the GPU target
-  constexpr int PB = 16 * SB;  // packed bytes per group
-  const auto src = make_rsrc(packed + bt * kWave * PB, nv * PB);
-#pragma unroll
-  for (int i = 0; i < SB; ++i) {
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(src, lane * PB + 16 * i, 0, 0);
-    words[4 * i] = v.x;
-    words[4 * i + 1] = v.y;
-    words[4 * i + 2] = v.z;
-    words[4 * i + 3] = v.w;
-  }
-  const auto nsrc = make_rsrc(norms + bt * kWave, nv * 2);
-  n16 = __builtin_amdgcn_raw_buffer_load_b16(nsrc, lane * 2, 0, 0);
-#endif
-}
-
-// Trit storage (three-level code, 26 bytes per group at 2-byte alignment):
-// 13 16-bit loads per lane, one trit byte pair in each dword's low half.
-__device__ __forceinline__ void fetch_batch_trits(const uint8_t* __restrict__ packed,
-                                                  const uint16_t* __restrict__ norms, int64_t bt,
-                                                  int nv, int lane, uint32_t (&t)[13], uint16_t& n16) {
-#if defined(__HIP_DEVICE_COMPILE__)  // buffer builtins exist only for the GPU target
-  const auto src = make_rsrc(packed + bt * kWave * kTritBytes, nv * kTritBytes);
-#pragma unroll
-  for (int k = 0; k < 13; ++k) t[k] = __builtin_amdgcn_raw_buffer_load_b16(src, lane * kTritBytes + 2 * k, 0, 0);
-  const auto nsrc = make_rsrc(norms + bt * kWave, nv * 2);
-  n16 = __builtin_amdgcn_raw_buffer_load_b16(nsrc, lane * 2, 0, 0);
-#endif
 }
 
 __device__ __forceinline__ void fill_trit_table(uint16_t* ttab, int t) {
@@ -260,10 +104,12 @@ __device__ __forceinline__ void fill_trit_table(uint16_t* ttab, int t) {
 
 // Cache policy of the output stores (the buffer instruction's aux bits:
 // 2 = nt, 16 = sc1).  Float32 output is stored "nt sc1", streaming: on the
-// 7B-shaped model that took dequantize from 5.18 to 4.92 ms (nt or sc1 alone:
-// 5.05, sc0 sc1: 5.05).  Every policy bit made bf16 output slower (3.21 ms ->
-// 4.07-4.55 ms), so it keeps the default.
-constexpr int kStoreF32 = 2 | 16;
+// 7B-shaped model that took the one-lane-per-group kernel this library had
+// first from 5.18 to 4.92 ms (nt or sc1 alone: 5.05, sc0 sc1: 5.05), and with
+// the quad kernel nt alone, sc1 alone and the default policy were 1-3%
+// slower.  Every policy bit made bf16 output slower (3.21 ms -> 4.07-4.55
+// ms, one-lane kernel), so it keeps the default.
+[[maybe_unused]] constexpr int kStoreF32 = 2 | 16;  // used in device code only
 
 template <int AUX>
 __device__ __forceinline__ void store16(const uint4& v, __amdgpu_buffer_rsrc_t dst, uint32_t voff,
@@ -275,16 +121,10 @@ __device__ __forceinline__ void store16(const uint4& v, __amdgpu_buffer_rsrc_t d
 #endif
 }
 
-// One lane per group, for whole-group tensors (cols % 128 == 0, so group g's
-// output is 128 contiguous values) in trit storage (and, as SB = 3, the
-// kernel that 3-bit fields used before the quad kernel).
-// The next batch's packed words and norm are loaded into registers while the
-// current batch is computed.  Stores go through a per-batch buffer resource
-// so the lanes past the end of the last batch are dropped by the hardware.
-//
-// One launch covers one tensor (MANY = false) or a table of tensors whose
-// column counts are multiples of 128 (MANY = true, batches of each tensor
-// numbered consecutively).
+// One launch of the quad kernel: one tensor (MANY = false: packed, norms,
+// out, n_groups) or a table of tensors whose column counts are multiples of
+// 128 (MANY = true: t and the total of their 64-group batches, each tensor's
+// batches numbered consecutively).
 struct DequantJob {
   const uint8_t* packed;
   const uint16_t* norms;
@@ -293,147 +133,6 @@ struct DequantJob {
   TensorTable<DequantDesc> t;
   int64_t n_batches;
 };
-
-// Inputs and output of one 64-group batch: local batch bt of a tensor with
-// n_groups groups.
-struct DBatch {
-  const uint8_t* packed;
-  const uint16_t* norms;
-  uint8_t* out;
-  int64_t bt;
-  int64_t n_groups;
-  __device__ int nvalid() const {
-    const int64_t left = n_groups - bt * kWave;
-    return static_cast<int>(left < kWave ? left : kWave);
-  }
-};
-
-template <bool MANY>
-__device__ __forceinline__ DBatch resolve(const DequantJob& j, int64_t b, int& d) {
-  if constexpr (!MANY) {
-    return DBatch{j.packed, j.norms, j.out, b, j.n_groups};
-  } else {
-    d = find_unit(j.t.start, d, j.t.n, b);
-    const DequantDesc* q = j.t.desc + d;  // field by field: scalar loads
-    return DBatch{load_const(&q->packed), load_const(&q->norms), load_const(&q->out),
-                  b - load_const(j.t.start + d), load_const(&q->rows) * (load_const(&q->cols) / kGroup)};
-  }
-}
-
-// TRITS (with SB = 2): the packed input is trit storage, converted to 2-bit
-// fields in registers.
-template <int SB, bool BF16OUT, bool MANY, bool TRITS = false>
-__global__ void __launch_bounds__(contig_waves(BF16OUT) * kWave, 2)
-dequantize_contig(DequantJob job, LevelTable lv) {
-  constexpr int W = contig_waves(BF16OUT);
-  constexpr int OB = BF16OUT ? 2 : 4;        // output bytes per element
-  constexpr int GOB = kGroup * OB;           // output bytes per group
-  constexpr int PB = 32 * OB;                // bytes per group per phase
-  constexpr int CPP = PB / 16;               // 16-byte chunks per group per phase
-  constexpr int GPB = 256 / PB;              // groups per 256-byte LDS row
-  constexpr int GPI = kWave / CPP;           // groups per store instruction
-  constexpr int WAVE_BYTES = kWave * PB;
-  constexpr int NI = WAVE_BYTES / 1024;      // store instructions per phase
-  __shared__ __attribute__((aligned(16))) float tab[TableSize<SB>::floats];
-  __shared__ __attribute__((aligned(16))) uint8_t lds[W * WAVE_BYTES];
-  __shared__ uint16_t ttab[TRITS ? 256 : 1];
-  // Blocks have 1 to W waves (dequant_grid); the tables need 256 entries.
-  for (int t = threadIdx.x; t < 256; t += blockDim.x) {
-    if constexpr (TRITS) fill_trit_table(ttab, t);
-    fill_table<SB>(tab, lv, t);
-  }
-  __syncthreads();
-
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int waves = __builtin_amdgcn_readfirstlane(blockDim.x / kWave);
-  uint8_t* const buf = lds + wave * WAVE_BYTES;
-  const int64_t n_batches = job.n_batches;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * waves;
-  int64_t batch = static_cast<int64_t>(blockIdx.x) * waves + wave;
-  if (batch >= n_batches) return;
-  int d = 0;
-
-  // LDS write: this lane's chunk c of a phase goes to slot c ^ swz_w.
-  const int swz_w = (lane / GPB) & (CPP - 1);
-  // Store instruction i moves groups GPI*i + lane/CPP, chunk lane % CPP.
-  const int gq = lane / CPP, cc = lane % CPP;
-  const uint32_t st_lane = static_cast<uint32_t>(gq * GOB + 16 * cc);
-
-  constexpr int FW = TRITS ? 13 : 4 * SB;  // fetched dwords per lane
-  uint32_t nwords[FW];
-  uint16_t nn16 = 0;
-  auto fetch = [&](const DBatch& b_) __attribute__((always_inline)) {
-    if constexpr (TRITS)
-      fetch_batch_trits(b_.packed, b_.norms, b_.bt, b_.nvalid(), lane, nwords, nn16);
-    else
-      fetch_batch<SB>(b_.packed, b_.norms, b_.bt, b_.nvalid(), lane, nwords, nn16);
-  };
-  DBatch cur = resolve<MANY>(job, batch, d);
-  fetch(cur);
-  for (;;) {
-    uint32_t words[4 * SB];
-    if constexpr (TRITS) {
-      static_assert(SB == 2, "trit storage decodes to 2-bit fields");
-      trits_to_fields(nwords, ttab, words);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4 * SB; ++i) words[i] = nwords[i];
-    }
-    const uint16_t n16 = nn16;
-    const int64_t next = batch + stride;
-    const int nv = cur.nvalid();
-    DBatch nxt = cur;
-    if (next < n_batches) {
-      nxt = resolve<MANY>(job, next, d);
-      fetch(nxt);
-    }
-
-    float y[kGroup];
-    reconstruct_fast<SB>(words, n16, tab, y);
-
-    const auto dst = make_rsrc(cur.out + cur.bt * kWave * GOB, nv * GOB);
-    // bf16 output: all 128 values are rounded and packed before the first
-    // phase, so the phases only move finished registers.
-    uint32_t pk[BF16OUT ? kGroup / 2 : 1];
-    if constexpr (BF16OUT) {
-#pragma unroll
-      for (int i = 0; i < kGroup / 2; ++i) pk[i] = f32_to_bf16_rne(y[2 * i]) | (f32_to_bf16_rne(y[2 * i + 1]) << 16);
-    }
-#pragma unroll
-    for (int ph = 0; ph < 4; ++ph) {
-      // Scatter this lane's 32 values of the phase into the swizzled buffer.
-      uint4 ch[CPP];
-#pragma unroll
-      for (int c = 0; c < CPP; ++c) {
-        if constexpr (BF16OUT) {
-          const int q = 16 * ph + 4 * c;
-          ch[c] = make_uint4(pk[q], pk[q + 1], pk[q + 2], pk[q + 3]);
-        } else {
-          const int e = 32 * ph + 4 * c;
-          ch[c] = make_uint4(__builtin_bit_cast(uint32_t, y[e]), __builtin_bit_cast(uint32_t, y[e + 1]),
-                             __builtin_bit_cast(uint32_t, y[e + 2]), __builtin_bit_cast(uint32_t, y[e + 3]));
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < CPP; ++c) *reinterpret_cast<uint4*>(buf + lane * PB + 16 * (c ^ swz_w)) = ch[c];
-      // Gather 16-byte chunks so consecutive lanes write consecutive bytes.
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int gs = GPI * i + gq;
-        const int sw = (gs / GPB) & (CPP - 1);
-        const uint4 v = *reinterpret_cast<const uint4*>(buf + gs * PB + 16 * (cc ^ sw));
-        store16<BF16OUT ? 0 : kStoreF32>(v, dst, st_lane + ph * PB, static_cast<uint32_t>(GPI * i * GOB));
-      }
-      // After the gather reads (which complete after the writes), so the wait
-      // adds nothing to the phase.
-      hold_until_lds_written(ch);
-    }
-    cur = nxt;
-    batch = next;
-    if (batch >= n_batches) break;
-  }
-}
 
 // General path: rows whose length is not a multiple of 128, in quad form
 // (see quad_load / quad_butterfly_across): lane q of a quad reads the
@@ -555,8 +254,8 @@ dequantize_ragged(const uint8_t* __restrict__ packed, const uint16_t* __restrict
 // stages 1-2 (2-bit) or 1 (4-bit) come from the byte table (3-bit fields:
 // one lookup per element in an 8-entry table, no stage), the remaining
 // in-lane stages run in registers and stages 6-7 across the quad
-// (quad_butterfly_across).  These are the float32 operations of the one-lane
-// form in the same order, so the output bits are the same.
+// (quad_butterfly_across).  These are the float32 operations, in the same
+// order, of the seven butterfly stages run over one lane's 128 values.
 //
 // The step's output (8 or 4 KiB) is transposed through a wave-private LDS
 // buffer so that store k writes bytes 1024k .. 1024k+1023 of the step:
@@ -568,22 +267,24 @@ dequantize_ragged(const uint8_t* __restrict__ packed, const uint16_t* __restrict
 // bank groups on both sides of the transpose.
 //
 // Blocks of two waves, one step per wave: on the 7B-shaped model (26.4 GB of
-// float32 output) 4.60-4.65 ms against 4.76 for the one-lane kernel; blocks
-// of 3 or 4 waves took 4.83-4.85 ms, two steps per wave 4.94, one-wave blocks
-// 5.7, a capped grid looping over steps 5.65.  LDS (20 KiB per block for
+// float32 output) 4.60-4.65 ms against 4.76 for a kernel with one lane per
+// group and 32 KiB per wave; blocks of 3 or 4 waves took 4.83-4.85 ms, two
+// steps per wave 4.94, one-wave blocks 5.7, a capped grid looping over steps
+// 5.65.  LDS (20 KiB per block for
 // float32) sets the occupancy at 16 waves per CU.
 //
 // MANY: a table of tensors whose 64-group batches are numbered consecutively
-// (the one-lane kernel's numbering); step s is quarter s % 4 of batch s / 4,
-// and quarters past a tensor's last group are skipped.
+// (the numbering quantize's multi-tensor launch uses too); step s is quarter
+// s % 4 of batch s / 4, and quarters past a tensor's last group are skipped.
 constexpr int kQuadContigWaves = 2;
 // Grid cap of the quad kernel; larger calls loop (grid-stride).
 constexpr int64_t kMaxGridBlocks = int64_t{1} << 30;
 
-template <int SB, bool BF16OUT, bool MANY>
+template <int SB, bool BF16OUT, bool MANY, bool TRITS = false>
 __global__ void __launch_bounds__(kQuadContigWaves * kWave)
 dequantize_quad_contig(DequantJob job, LevelTable lv) {
   static_assert(SB >= 2 && SB <= 4, "2-, 3- and 4-bit fields");
+  static_assert(!TRITS || SB == 2, "trit storage decodes to 2-bit fields");
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer builtins exist only for the GPU target
   constexpr int E = SB == 3 ? 1 : ByteTable<SB>::E;  // elements per table read
   constexpr int QB = 4 * SB;                 // packed bytes per lane
@@ -596,7 +297,11 @@ dequantize_quad_contig(DequantJob job, LevelTable lv) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   __shared__ __attribute__((aligned(16))) float tab[TableSize<SB>::floats];
   __shared__ __attribute__((aligned(16))) uint8_t stage[kQuadContigWaves * STEP];
-  for (int t = threadIdx.x; t < 256; t += blockDim.x) fill_table<SB>(tab, lv, t);
+  __shared__ uint16_t ttab[TRITS ? 256 : 1];
+  for (int t = threadIdx.x; t < 256; t += blockDim.x) {
+    if constexpr (TRITS) fill_trit_table(ttab, t);
+    fill_table<SB>(tab, lv, t);
+  }
   __syncthreads();
   const int lane = threadIdx.x & (kWave - 1), q = lane & 3;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -627,18 +332,31 @@ dequantize_quad_contig(DequantJob job, LevelTable lv) {
     // Lanes of groups past the end read zeros (outside the buffer resource)
     // and their stores are dropped.
     uint32_t words[SB];
-    const auto src = make_rsrc(pk + g0 * (16 * SB), nv * (16 * SB));
-    if constexpr (SB == 2) {
+    if constexpr (TRITS) {
+      // Trit storage (26 bytes per group, 2-byte aligned): every lane of the
+      // quad converts its group's 26 bytes to the 256 bits of 2-bit fields
+      // and keeps the 64 bits of its quarter.
+      const auto src = make_rsrc(pk + g0 * kTritBytes, nv * kTritBytes);
+      uint32_t tr[13], all[8];
+#pragma unroll
+      for (int k = 0; k < 13; ++k) tr[k] = __builtin_amdgcn_raw_buffer_load_b16(src, (lane >> 2) * kTritBytes + 2 * k, 0, 0);
+      trits_to_fields(tr, ttab, all);
+      words[0] = q == 0 ? all[0] : q == 1 ? all[2] : q == 2 ? all[4] : all[6];
+      words[1] = q == 0 ? all[1] : q == 1 ? all[3] : q == 2 ? all[5] : all[7];
+    } else if constexpr (SB == 2) {
+      const auto src = make_rsrc(pk + g0 * (16 * SB), nv * (16 * SB));
       const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(src, lane * QB, 0, 0);
       words[0] = v.x;
       words[1] = v.y;
     } else if constexpr (SB == 3) {
+      const auto src = make_rsrc(pk + g0 * (16 * SB), nv * (16 * SB));
       typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
       const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(src, lane * QB, 0, 0);
       words[0] = v.x;
       words[1] = v.y;
       words[2] = v.z;
     } else {
+      const auto src = make_rsrc(pk + g0 * (16 * SB), nv * (16 * SB));
       const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(src, lane * QB, 0, 0);
       words[0] = v.x;
       words[1] = v.y;
@@ -709,17 +427,6 @@ dequantize_quad_contig(DequantJob job, LevelTable lv) {
 #endif
 }
 
-// Grid: one batch per wave, a grid that covers the tensor (5-6% faster on
-// the 7B-shaped model than a resident grid for float32 output; 2 and 4
-// batches per wave were 4% and 8% slower), in blocks of W waves.  A call
-// with fewer than W batches per CU takes smaller blocks, so its batches
-// spread over more CUs (256x512, 16 batches: 16 one-wave blocks instead of
-// two of eight).
-template <bool BF16OUT>
-ContigGrid dequant_grid(int64_t n_batches) {
-  return contig_grid(n_batches, contig_waves(BF16OUT), 1, kBlocksPerCu);
-}
-
 // Blocks of the quad kernel for n_steps steps: one step per wave.
 inline int quad_grid(int64_t n_steps) {
   const int64_t want = (n_steps + kQuadContigWaves - 1) / kQuadContigWaves;
@@ -732,19 +439,10 @@ hipError_t launch_sb(const uint8_t* packed, const uint16_t* norms, int64_t rows,
   uint8_t* ob = static_cast<uint8_t*>(out);
   if (cols % kGroup == 0) {
     const int64_t n_groups = rows * (cols / kGroup);
-    if constexpr (!TRITS) {  // 2-, 3- and 4-bit fields: the quad kernel
-      const int64_t n_steps = (n_groups + kQuadGroups - 1) / kQuadGroups;
-      const DequantJob job{packed, norms, ob, n_groups, TensorTable<DequantDesc>{nullptr, nullptr, 0}, 0};
-      hipLaunchKernelGGL((dequantize_quad_contig<SB, BF16OUT, false>), dim3(quad_grid(n_steps)),
-                         dim3(kQuadContigWaves * kWave), 0, s, job, lv);
-    } else {  // trit storage: one lane per group
-      const int64_t n_batches = (n_groups + kWave - 1) / kWave;
-      const ContigGrid g = dequant_grid<BF16OUT>(n_batches);
-      const DequantJob job{packed, norms, ob, n_groups, TensorTable<DequantDesc>{nullptr, nullptr, 0},
-                           n_batches};
-      hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT, false, TRITS>), dim3(g.blocks), dim3(g.waves * kWave), 0,
-                         s, job, lv);
-    }
+    const int64_t n_steps = (n_groups + kQuadGroups - 1) / kQuadGroups;
+    const DequantJob job{packed, norms, ob, n_groups, TensorTable<DequantDesc>{nullptr, nullptr, 0}, 0};
+    hipLaunchKernelGGL((dequantize_quad_contig<SB, BF16OUT, false, TRITS>), dim3(quad_grid(n_steps)),
+                       dim3(kQuadContigWaves * kWave), 0, s, job, lv);
   } else {
     const int blocks = quad_blocks(rows * ((cols + kGroup - 1) / kGroup));
     const TensorTable<DequantDesc> none{nullptr, nullptr, 0};
@@ -764,14 +462,8 @@ hipError_t launch_many_sb(const LevelTable& lv, TensorTable<DequantDesc> contig,
                           hipStream_t s) {
   if (contig_batches > 0) {
     const DequantJob job{nullptr, nullptr, nullptr, 0, contig, contig_batches};
-    if constexpr (!TRITS) {
-      hipLaunchKernelGGL((dequantize_quad_contig<SB, BF16OUT, true>), dim3(quad_grid(4 * contig_batches)),
-                         dim3(kQuadContigWaves * kWave), 0, s, job, lv);
-    } else {
-      const ContigGrid g = dequant_grid<BF16OUT>(contig_batches);
-      hipLaunchKernelGGL((dequantize_contig<SB, BF16OUT, true, TRITS>), dim3(g.blocks), dim3(g.waves * kWave), 0, s,
-                         job, lv);
-    }
+    hipLaunchKernelGGL((dequantize_quad_contig<SB, BF16OUT, true, TRITS>), dim3(quad_grid(4 * contig_batches)),
+                       dim3(kQuadContigWaves * kWave), 0, s, job, lv);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
