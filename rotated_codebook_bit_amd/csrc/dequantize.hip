@@ -103,13 +103,13 @@ __device__ __forceinline__ void fill_trit_table(uint16_t* ttab, int t) {
 }
 
 // Cache policy of the output stores (the buffer instruction's aux bits:
-// 2 = nt, 16 = sc1).  Float32 output is stored "nt sc1", streaming: on the
-// 7B-shaped model that took the one-lane-per-group kernel this library had
-// first from 5.18 to 4.92 ms (nt or sc1 alone: 5.05, sc0 sc1: 5.05), and with
-// the quad kernel nt alone, sc1 alone and the default policy were 1-3%
-// slower.  Every policy bit made bf16 output slower (3.21 ms -> 4.07-4.55
-// ms, one-lane kernel), so it keeps the default.
-[[maybe_unused]] constexpr int kStoreF32 = 2 | 16;  // used in device code only
+// 2 = nt, 16 = sc1): "nt sc1", streaming, for both output types.  On the
+// 7B-shaped model it took the one-lane-per-group kernel this library had
+// first from 5.18 to 4.92 ms for float32 output (nt or sc1 alone: 5.05, sc0
+// sc1: 5.05); with the quad kernel nt alone, sc1 alone and the default
+// policy were 1-3% slower for float32, and the default 3-9% slower for bf16
+// (3.03 against 2.78-2.80 ms in 4-wave blocks).
+[[maybe_unused]] constexpr int kStoreStream = 2 | 16;  // used in device code only
 
 template <int AUX>
 __device__ __forceinline__ void store16(const uint4& v, __amdgpu_buffer_rsrc_t dst, uint32_t voff,
@@ -261,27 +261,30 @@ dequantize_ragged(const uint8_t* __restrict__ packed, const uint16_t* __restrict
 // buffer so that store k writes bytes 1024k .. 1024k+1023 of the step:
 // consecutive lanes, consecutive 16 bytes, whole 128-byte lines.  (Each lane
 // storing its own bytes in 16-byte pieces leaves every instruction with 64
-// partial lines, and under the streaming policy of the float32 stores that
+// partial lines, and under the streaming policy of these stores that
 // ran 16 times slower.)  Chunk c of lane l sits at slot c ^ swz(l) of the
 // lane's LB bytes, so eight consecutive lanes touch eight different 16-byte
 // bank groups on both sides of the transpose.
 //
-// Blocks of two waves, one step per wave: on the 7B-shaped model (26.4 GB of
-// float32 output) 4.60-4.65 ms against 4.76 for a kernel with one lane per
-// group and 32 KiB per wave; blocks of 3 or 4 waves took 4.83-4.85 ms, two
-// steps per wave 4.94, one-wave blocks 5.7, a capped grid looping over steps
-// 5.65.  LDS (20 KiB per block for
-// float32) sets the occupancy at 16 waves per CU.
+// One step per wave, in blocks of 16 KiB of output: two waves for float32,
+// four for bf16.  On the 7B-shaped model (26.4 GB of float32 output)
+// 4.60-4.65 ms against 4.76 for a kernel with one lane per group and 32 KiB
+// per wave; blocks of 3 or 4 waves took 4.83-4.88 ms, two steps per wave
+// 4.94, one-wave blocks 5.7, a capped grid looping over steps 5.65.  bf16
+// output: 2.78-2.80 ms in 4-wave blocks, 2.95-2.97 in 2-wave ones.  For
+// float32 the LDS (20 KiB per block) sets the occupancy at 16 waves per CU.
 //
 // MANY: a table of tensors whose 64-group batches are numbered consecutively
 // (the numbering quantize's multi-tensor launch uses too); step s is quarter
 // s % 4 of batch s / 4, and quarters past a tensor's last group are skipped.
-constexpr int kQuadContigWaves = 2;
+// Waves per block: 16 KiB of output per block (two 8 KiB float32 steps or
+// four 4 KiB bf16 steps) was the fastest shape for both output types.
+constexpr int quad_waves(bool bf16out) { return bf16out ? 4 : 2; }
 // Grid cap of the quad kernel; larger calls loop (grid-stride).
 constexpr int64_t kMaxGridBlocks = int64_t{1} << 30;
 
 template <int SB, bool BF16OUT, bool MANY, bool TRITS = false>
-__global__ void __launch_bounds__(kQuadContigWaves * kWave)
+__global__ void __launch_bounds__(quad_waves(BF16OUT) * kWave)
 dequantize_quad_contig(DequantJob job, LevelTable lv) {
   static_assert(SB >= 2 && SB <= 4, "2-, 3- and 4-bit fields");
   static_assert(!TRITS || SB == 2, "trit storage decodes to 2-bit fields");
@@ -296,7 +299,8 @@ dequantize_quad_contig(DequantJob job, LevelTable lv) {
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   __shared__ __attribute__((aligned(16))) float tab[TableSize<SB>::floats];
-  __shared__ __attribute__((aligned(16))) uint8_t stage[kQuadContigWaves * STEP];
+  constexpr int W = quad_waves(BF16OUT);
+  __shared__ __attribute__((aligned(16))) uint8_t stage[W * STEP];
   __shared__ uint16_t ttab[TRITS ? 256 : 1];
   for (int t = threadIdx.x; t < 256; t += blockDim.x) {
     if constexpr (TRITS) fill_trit_table(ttab, t);
@@ -309,8 +313,8 @@ dequantize_quad_contig(DequantJob job, LevelTable lv) {
   // Bank-group swizzle of a lane's chunks (see above).
   auto swz = [](int l) __attribute__((always_inline)) { return BF16OUT ? (l >> 2) & 3 : l & 7; };
   const int64_t n_steps = MANY ? 4 * job.n_batches : (job.n_groups + kQuadGroups - 1) / kQuadGroups;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kQuadContigWaves;
-  for (int64_t step = static_cast<int64_t>(blockIdx.x) * kQuadContigWaves + wave; step < n_steps;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * W;
+  for (int64_t step = static_cast<int64_t>(blockIdx.x) * W + wave; step < n_steps;
        step += stride) {
     const uint8_t* pk = job.packed;
     const uint16_t* nm = job.norms;
@@ -417,7 +421,7 @@ dequantize_quad_contig(DequantJob job, LevelTable lv) {
     for (int k = 0; k < NS; ++k) {
       const int sl = (1024 * k + 16 * lane) / LB, cl = lane % CPL;  // source lane and chunk
       const uint4 v = *reinterpret_cast<const uint4*>(buf + sl * LB + 16 * (cl ^ swz(sl)));
-      store16<BF16OUT ? 0 : kStoreF32>(v, dst, static_cast<uint32_t>(16 * lane), static_cast<uint32_t>(1024 * k));
+      store16<kStoreStream>(v, dst, static_cast<uint32_t>(16 * lane), static_cast<uint32_t>(1024 * k));
     }
     // The next step's LDS writes come after these reads in the wave's LDS
     // order; the wait only keeps the written registers live (see
@@ -428,8 +432,9 @@ dequantize_quad_contig(DequantJob job, LevelTable lv) {
 }
 
 // Blocks of the quad kernel for n_steps steps: one step per wave.
-inline int quad_grid(int64_t n_steps) {
-  const int64_t want = (n_steps + kQuadContigWaves - 1) / kQuadContigWaves;
+inline int quad_grid(int64_t n_steps, bool bf16out) {
+  const int w = quad_waves(bf16out);
+  const int64_t want = (n_steps + w - 1) / w;
   return static_cast<int>(want < 1 ? 1 : want < kMaxGridBlocks ? want : kMaxGridBlocks);
 }
 
@@ -441,8 +446,8 @@ hipError_t launch_sb(const uint8_t* packed, const uint16_t* norms, int64_t rows,
     const int64_t n_groups = rows * (cols / kGroup);
     const int64_t n_steps = (n_groups + kQuadGroups - 1) / kQuadGroups;
     const DequantJob job{packed, norms, ob, n_groups, TensorTable<DequantDesc>{nullptr, nullptr, 0}, 0};
-    hipLaunchKernelGGL((dequantize_quad_contig<SB, BF16OUT, false, TRITS>), dim3(quad_grid(n_steps)),
-                       dim3(kQuadContigWaves * kWave), 0, s, job, lv);
+    hipLaunchKernelGGL((dequantize_quad_contig<SB, BF16OUT, false, TRITS>), dim3(quad_grid(n_steps, BF16OUT)),
+                       dim3(quad_waves(BF16OUT) * kWave), 0, s, job, lv);
   } else {
     const int blocks = quad_blocks(rows * ((cols + kGroup - 1) / kGroup));
     const TensorTable<DequantDesc> none{nullptr, nullptr, 0};
@@ -462,8 +467,8 @@ hipError_t launch_many_sb(const LevelTable& lv, TensorTable<DequantDesc> contig,
                           hipStream_t s) {
   if (contig_batches > 0) {
     const DequantJob job{nullptr, nullptr, nullptr, 0, contig, contig_batches};
-    hipLaunchKernelGGL((dequantize_quad_contig<SB, BF16OUT, true, TRITS>), dim3(quad_grid(4 * contig_batches)),
-                       dim3(kQuadContigWaves * kWave), 0, s, job, lv);
+    hipLaunchKernelGGL((dequantize_quad_contig<SB, BF16OUT, true, TRITS>), dim3(quad_grid(4 * contig_batches, BF16OUT)),
+                       dim3(quad_waves(BF16OUT) * kWave), 0, s, job, lv);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
