@@ -402,7 +402,7 @@ def trace_summary(path: str) -> None:
 # Kernels of the traffic profile: phase -> kernel name (the largest dispatch
 # of that name is the whole-model launch).
 TRAFFIC_KERNELS = {"quantize": "cq::kq::quantize_contig<4, true, false, false>",
-                   "dequantize_f32": "cq::kd::dequantize_quad_contig<2, false, false>",
+                   "dequantize_f32": "cq::kd::dequantize_quad_contig<2, false, false, false>",
                    "matvec_pass_b1": "cq::km::matvec_pair_kernel<",
                    "fake_quant_bf16_extra": "cq::kq::fakequant_contig<4, true, true>"}
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
@@ -832,7 +832,7 @@ def main():
     del scrub
 
     dom = "dequantize_f32" if tdq >= tq else "quantize"
-    dom_kernel = {"dequantize_f32": "dequantize_quad_contig<2, false, false>",
+    dom_kernel = {"dequantize_f32": "dequantize_quad_contig<2, false, false, false>",
                   "quantize": "quantize_contig<4, true, false, false>"}
     ach = gbs(phases[dom]["bytes"], phases[dom]["ms"])
     traffic = None
