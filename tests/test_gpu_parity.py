@@ -285,6 +285,61 @@ def test_dequantize_many_steps(bits, levels):
         assert torch.equal(o16.view(torch.int16), o.to(torch.bfloat16).view(torch.int16)), (r, c)
 
 
+RANDOM_WIDTHS = [O.TERNARY, 2, 3, 4, O.TERNARY_TRITS]
+
+
+def random_indexed_codes(rs, rows, cols, bits):
+    """Packed storage of uniform random indices (valid for the width: 0..2
+    for the ternary codes) and binary16 norms with zeros and extremes."""
+    ngr = -(-cols // O.GROUP)
+    idx = rs.integers(0, O.n_levels(bits), size=(rows, ngr, O.GROUP))
+    packed = O.pack_indices(idx, bits)
+    norms = (np.abs(rs.standard_normal(rows * ngr)) * 0.3).astype(np.float16)
+    norms[rs.random(norms.size) < 0.05] = 0
+    norms[rs.random(norms.size) < 0.02] = np.float16(5e4)
+    return packed, norms.view(np.uint16).reshape(rows, ngr)
+
+
+@pytest.mark.parametrize("case", range(25))
+def test_dequantize_random_shapes(case, levels):
+    """A seeded sweep of whole-group shapes over every storage form (ternary
+    and 2/3/4-bit fields, trits) and both output types: float32 against the
+    oracle element by element, bf16 equal to the rounded float32 output."""
+    rs = np.random.default_rng(9000 + case)
+    bits = RANDOM_WIDTHS[case % len(RANDOM_WIDTHS)]
+    lv = levels[O.TERNARY if bits == O.TERNARY_TRITS else bits]
+    rows, cols = int(rs.integers(1, 400)), 128 * int(rs.integers(1, 48))
+    packed, n16 = random_indexed_codes(rs, rows, cols, bits)
+    ref = O.dequantize(packed, n16, rows, cols, bits, lv)
+    p_dev, n_dev = codes_dev(packed, n16, rows)
+    say(f"dequantize random {rows}x{cols} bits={bits}")
+    out = cq.dequantize(p_dev, n_dev, rows, cols, bits, lv)
+    check_dequant(host(out), ref, n16, rows, cols)
+    out16 = cq.dequantize(p_dev, n_dev, rows, cols, bits, lv, out_dtype=torch.bfloat16)
+    assert torch.equal(out16.view(torch.int16), out.to(torch.bfloat16).view(torch.int16))
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_dequantize_many_random(case, levels):
+    """Seeded multi-tensor calls: 1-7 tensors of random shapes, whole-group
+    and ragged mixed, one storage form per call, float32 against the oracle
+    element by element."""
+    rs = np.random.default_rng(9500 + case)
+    bits = RANDOM_WIDTHS[case % len(RANDOM_WIDTHS)]
+    lv = levels[O.TERNARY if bits == O.TERNARY_TRITS else bits]
+    shapes = []
+    for _ in range(int(rs.integers(1, 8))):
+        rows = int(rs.integers(1, 200))
+        cols = 128 * int(rs.integers(1, 24)) if rs.random() < 0.7 else int(rs.integers(1, 1500))
+        shapes.append((rows, cols))
+    codes = [random_indexed_codes(rs, r, c, bits) for r, c in shapes]
+    items = [(*codes_dev(pk, n16, r), r, c) for (r, c), (pk, n16) in zip(shapes, codes)]
+    say(f"dequantize_many random {shapes} bits={bits}")
+    outs = cq.dequantize_many(items, bits, lv)
+    for (r, c), (pk, n16), o in zip(shapes, codes, outs):
+        check_dequant(host(o), O.dequantize(pk, n16, r, c, bits, lv), n16, r, c)
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 # Between one and a few batches per CU: the contiguous kernels then launch
